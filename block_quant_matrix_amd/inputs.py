@@ -1,0 +1,98 @@
+"""Seeded synthetic inputs for the block-quantized DMMV path.
+
+This module only draws random numbers and lays them out as the raw input bytes
+the path consumes (GGML-style blocks: little-endian fp16 scale first, then the
+quants).  It does none of the method's arithmetic: no quantization, no dot
+products, no scaling.  Both the CPU oracle's tests and the GPU path take their
+inputs from here, so both sides see identical bytes.
+
+Value distributions (the workloads' recipe):
+  * Q8_0 weights: int8 values uniform in [-127, 127]; scales |N(0,1)|*0.01
+    rounded once to fp16.
+  * Q4_0 weights: nibbles uniform in 0..15 (so each packed byte is uniform in
+    0..255); scales |N(0,1)|*0.02 rounded once to fp16.
+  * activations: fp32 N(0,1).
+  * MoE router logits: fp32 N(0,1); shared-expert gate scalar: fp32 N(0,1).
+Seeds: workload i (1-based, in the order below) uses 1000*i + s.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+Q4_0 = 4
+Q8_0 = 8
+BLOCK_BYTES = {Q4_0: 18, Q8_0: 34}
+SCALE_C = {Q8_0: 0.01, Q4_0: 0.02}
+
+
+def seed_for(workload: int, s: int = 0) -> int:
+    return 1000 * workload + s
+
+
+def fp16_scales(rng: np.random.Generator, n: int, c: float) -> np.ndarray:
+    """|N(0,1)| * c in fp64, rounded once (RNE) to fp16."""
+    return (np.abs(rng.standard_normal(n, dtype=np.float64)) * c).astype(np.float16)
+
+
+def layout_blocks(scales_f16: np.ndarray, quant_bytes: np.ndarray) -> np.ndarray:
+    """Interleave per-block fp16 scales and quant bytes into one byte stream.
+
+    scales_f16: [n] float16; quant_bytes: [n][q] uint8 -> [n*(2+q)] uint8.
+    """
+    n = scales_f16.size
+    q = quant_bytes.reshape(n, -1)
+    out = np.empty((n, 2 + q.shape[1]), np.uint8)
+    out[:, :2] = np.ascontiguousarray(scales_f16.astype("<f2")).view(np.uint8).reshape(n, 2)
+    out[:, 2:] = q
+    return out.reshape(-1)
+
+
+def gen_weights(wtype: int, rows: int, k: int, seed: int, scale_c: float | None = None) -> np.ndarray:
+    """Random weight matrix [rows][k/32 blocks] as raw bytes (uint8)."""
+    assert k % 32 == 0
+    n = rows * (k // 32)
+    rng = np.random.default_rng(seed)
+    c = SCALE_C[wtype] if scale_c is None else scale_c
+    d = fp16_scales(rng, n, c)
+    if wtype == Q8_0:
+        q = rng.integers(-127, 128, size=(n, 32), dtype=np.int8).view(np.uint8)
+    elif wtype == Q4_0:
+        q = rng.integers(0, 256, size=(n, 16), dtype=np.uint8)
+    else:
+        raise ValueError("unknown weight type %r" % wtype)
+    return layout_blocks(d, q)
+
+
+def gen_activation(n_tok: int, k: int, seed: int) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n_tok, k), dtype=np.float32)
+    return x[0] if n_tok == 1 else x
+
+
+def gen_router(n_routed: int, seed: int):
+    """Router logits N(0,1)[n_routed] and the shared-expert gate scalar g ~ N(0,1)."""
+    rng = np.random.default_rng(seed)
+    logits = rng.standard_normal(n_routed, dtype=np.float32)
+    g = np.float32(rng.standard_normal(dtype=np.float32))
+    return logits, g
+
+
+# The five workloads (shapes from the pages; distributions as above).
+WORKLOADS = {
+    1: dict(name="q8_0_dmmv_64x2048", wtype=Q8_0, rows=64, k=2048),
+    2: dict(name="q4_0_dmmv_4096x4096", wtype=Q4_0, rows=4096, k=4096),
+    3: dict(name="q4_0_lmhead_248320x2048_argmax", wtype=Q4_0, rows=248320, k=2048),
+    4: dict(name="q4_0_moe_128e_top8_shared_2048x512", wtype=Q4_0, n_routed=128, top_k=8,
+            d_model=2048, d_ff=512),
+    5: dict(name="q4_0_prefill_gemm_m512_n5120_k5120", wtype=Q4_0, m=512, n=5120, k=5120),
+}
+
+
+def moe_banks(seed: int, n_experts: int, d_model: int, d_ff: int, wtype: int = Q4_0):
+    """Gate||up bank [E][2*d_ff rows][d_model] (rows 0..d_ff-1 gate, d_ff..2*d_ff-1 up)
+    and down bank [E][d_model rows][d_ff], as contiguous byte streams."""
+    gu = gen_weights(wtype, n_experts * 2 * d_ff, d_model, seed)
+    down = gen_weights(wtype, n_experts * d_model, d_ff, seed + 500)
+    gu_stride = 2 * d_ff * (d_model // 32) * BLOCK_BYTES[wtype]
+    down_stride = d_model * (d_ff // 32) * BLOCK_BYTES[wtype]
+    return gu, gu_stride, down, down_stride

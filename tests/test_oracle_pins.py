@@ -1,0 +1,470 @@
+"""Pins for the CPU oracle: closed forms, exhaustive decodes, brute force and
+invariants that fix its arithmetic independently of the oracle itself.
+
+Each test names the oracle step it pins.  A plausible slip anywhere in the
+oracle (a dropped term, a wrong sign, a swapped nibble, a wrong rounding mode,
+a transposed operand) fails at least one of these.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+from block_quant_matrix_amd import inputs
+
+Q4, Q8 = 4, 8
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------- helpers --
+
+def f16_bytes(v: float) -> bytes:
+    return np.array([v], "<f2").tobytes()
+
+
+def q8_block(d: float, q) -> np.ndarray:
+    q = np.asarray(q, np.int8)
+    assert q.size == 32
+    return np.frombuffer(f16_bytes(d) + q.tobytes(), np.uint8).copy()
+
+
+def q4_block_from_elements(d: float, nib) -> np.ndarray:
+    """nib[0..31] unsigned nibbles in element order -> 18-byte block
+    (element j<16 in the low nibble of qs[j], element j+16 in the high nibble)."""
+    nib = np.asarray(nib, np.uint8)
+    assert nib.size == 32 and nib.max() < 16
+    qs = (nib[:16] | (nib[16:] << 4)).astype(np.uint8)
+    return np.frombuffer(f16_bytes(d) + qs.tobytes(), np.uint8).copy()
+
+
+def lossless_activation(rng, k, e=7):
+    """x = kint * 2^-e per block with some |kint| = 127 in every block, so that
+    quantization is exact: d = 2^-e, q = kint."""
+    kint = rng.integers(-127, 128, size=k).astype(np.int64)
+    for b in range(k // 32):
+        j = b * 32 + int(rng.integers(0, 32))
+        kint[j] = 127 if rng.integers(0, 2) else -127
+    return (kint * 2.0 ** -e).astype(np.float32), kint
+
+
+# ----------------------------------------------- P1: the dot primitive -----
+
+def test_p1_golden_dp4a_70(ref):
+    """The pages' own worked example: 1*5+2*6+3*7+4*8 = 70 (tests/golden/dp4a_70.txt)."""
+    with open(os.path.join(GOLDEN, "dp4a_70.txt")) as f:
+        rows = [l for l in f if l.strip() and not l.startswith("#")]
+    assert rows
+    for line in rows:
+        a, b, want = line.split("|")
+        a = [int(v) for v in a.split()]
+        b = [int(v) for v in b.split()]
+        want = int(want)
+        qa = np.zeros(32, np.int8)
+        qb = np.zeros(32, np.int8)
+        qa[:4] = a
+        qb[:4] = b
+        assert ref.block_isum(Q8, q8_block(1.0, qa), qb) == want
+        # the same four products through the Q4_0 encoding (value = nib - 8)
+        nib = np.full(32, 8, np.uint8)
+        nib[:4] = np.array(a) + 8
+        assert ref.block_isum(Q4, q4_block_from_elements(1.0, nib), qb) == want
+
+
+def test_p1_dot_extremes(ref):
+    qa = np.zeros(32, np.int8)
+    qb = np.zeros(32, np.int8)
+    qa[:4] = -128
+    qb[:4] = -128
+    assert ref.block_isum(Q8, q8_block(1.0, qa), qb) == 65536
+    qa[:4] = 127
+    assert ref.block_isum(Q8, q8_block(1.0, qa), qb) == -65024
+    # the largest possible |isum| of a whole block still fits int32
+    qa[:] = -128
+    qb[:] = -128
+    assert ref.block_isum(Q8, q8_block(1.0, qa), qb) == 32 * 128 * 128
+
+
+# ---------------------------------------------------- P2: fp16 decode ------
+
+def test_p2_fp16_decode_exhaustive(ref):
+    """All 65536 binary16 patterns against numpy's own float16 conversion."""
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = ref.fp16_to_f64(h)
+    want = h.view(np.float16).astype(np.float64)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    # signed zero is kept
+    assert math.copysign(1.0, ref.fp16_to_f64(np.array([0x8000], np.uint16))[0]) == -1.0
+
+
+def test_p2_block_decode_layout(ref):
+    """Scale is the first two bytes, little-endian; then the quants."""
+    d, vals = ref.decode_block(Q8, q8_block(-0.375, np.arange(-16, 16)))
+    assert d == -0.375
+    assert list(vals) == list(range(-16, 16))
+    d, vals = ref.decode_block(Q4, q4_block_from_elements(2.0 ** -20, np.arange(32) % 16))
+    assert d == 2.0 ** -20  # an fp16 subnormal
+    assert list(vals) == [(j % 16) - 8 for j in range(32)]
+
+
+# --------------------------------------------- P3: activation quantizer ----
+
+def quant_block(ref, x):
+    q, d, s = ref.quantize_act(np.asarray(x, np.float32))
+    return q, float(d[0]), int(s[0])
+
+
+def test_p3a_zero_block(ref):
+    q, d, s = quant_block(ref, np.zeros(32))
+    assert d == 0.0 and s == 0 and not q.any()
+    q, d, s = quant_block(ref, -np.zeros(32))
+    assert d == 0.0 and s == 0 and not q.any()
+
+
+@pytest.mark.parametrize("e", [0, 3, 7, 20, 100])
+def test_p3b_lossless(ref, e):
+    rng = np.random.default_rng(e)
+    x, kint = lossless_activation(rng, 32, e)
+    q, d, s = quant_block(ref, x)
+    assert d == 2.0 ** -e
+    assert np.array_equal(q.astype(np.int64), kint)
+    assert s == kint.sum()
+
+
+@pytest.mark.parametrize("c", [1.0, 0.3, 1e-3, 7.5, 1e30])
+def test_p3c_constant_block(ref, c):
+    q, d, s = quant_block(ref, np.full(32, c))
+    assert (q == 127).all() and s == 32 * 127
+    assert d == np.float32(np.float32(c) / np.float32(127.0))
+    q, d, s = quant_block(ref, np.full(32, -c))
+    assert (q == -127).all() and s == -32 * 127
+
+
+def test_p3d_half_way_rounds_away_from_zero(ref):
+    """amax = 127 * 2^-e; elements at +-2.5, +-0.5, +-1.5 units of 2^-e.
+    Half away from zero gives +-3, +-1, +-2 (half to even would give 2, 0, 2)."""
+    e = 5
+    u = 2.0 ** -e
+    x = np.zeros(32)
+    x[0] = 127 * u
+    x[1], x[2] = 2.5 * u, -2.5 * u
+    x[3], x[4] = 0.5 * u, -0.5 * u
+    x[5], x[6] = 1.5 * u, -1.5 * u
+    q, d, s = quant_block(ref, x)
+    assert d == u
+    assert list(q[:7]) == [127, 3, -3, 1, -1, 2, -2]
+    assert s == 127
+
+
+def test_p3e_invariants(ref):
+    rng = np.random.default_rng(33)
+    x = rng.standard_normal((64, 32 * 16)).astype(np.float32)
+    x[3] *= 1e-30
+    x[4] *= 1e30
+    qx, dx, sx = ref.quantize_act(x)
+    assert np.abs(qx.astype(np.int32)).max() <= 127
+    xb = x.reshape(64, 16, 32).astype(np.float64)
+    qb = qx.reshape(64, 16, 32).astype(np.int64)
+    assert np.array_equal(qb.sum(-1), sx)
+    amax_pos = np.abs(xb).argmax(-1)
+    assert (np.abs(np.take_along_axis(qb, amax_pos[..., None], -1)) == 127).all()
+    err = np.abs(xb - dx[..., None].astype(np.float64) * qb)
+    assert (err <= dx[..., None] / 2 * (1 + 1e-6)).all()
+    # sign symmetry: -x quantizes to -q with the same scale (used again in P9)
+    qn, dn, sn = ref.quantize_act(-x)
+    assert np.array_equal(qn, -qx) and np.array_equal(dn, dx) and np.array_equal(sn, -sx)
+
+
+def test_p3_rejects_non_finite(ref):
+    x = np.zeros(32, np.float32)
+    x[7] = np.inf
+    with pytest.raises(RuntimeError):
+        ref.quantize_act(x)
+    x[7] = np.nan
+    with pytest.raises(RuntimeError):
+        ref.quantize_act(x)
+
+
+# --------------------------------------------------- P4: all ones ----------
+
+@pytest.mark.parametrize("wtype", [Q8, Q4])
+def test_p4_all_ones(ref, wtype):
+    """q = 1 everywhere (Q4_0 nibble 9), d_w = 1.0, x = 127/128 -> d_x = 1/128,
+    q_x = 127, isum = 4064, t_b = 31.75 and y = K*127/128 = 2032 exactly."""
+    k, rows = 2048, 4
+    blk = q8_block(1.0, np.ones(32)) if wtype == Q8 else q4_block_from_elements(1.0, np.full(32, 9))
+    w = np.tile(blk, rows * (k // 32))
+    x = np.full(k, 127 / 128, np.float32)
+    qx, dx, sx = ref.quantize_act(x)
+    assert (qx == 127).all() and (dx == 1 / 128).all() and (sx == 32 * 127).all()
+    y, S, isums = ref.dmmv(wtype, w, rows, k, qx, dx, want_isums=True)
+    assert (isums == 4064).all()
+    assert (y == 2032.0).all() and (S == 2032.0).all()
+
+
+# -------------------------------------------- P5: single nonzero block -----
+
+@pytest.mark.parametrize("wtype", [Q8, Q4])
+def test_p5_single_nonzero_block(ref, wtype):
+    rows, k = 130, 32 * 66
+    nb = k // 32
+    rng = np.random.default_rng(5)
+    x, kint = lossless_activation(rng, k, e=6)
+    qx, dx, _ = ref.quantize_act(x)
+    assert np.array_equal(qx.astype(np.int64), kint) and (dx == 2.0 ** -6).all()
+    base = inputs.gen_weights(wtype, rows, k, 77)
+    bb = inputs.BLOCK_BYTES[wtype]
+    for rstar, bstar in [(0, 0), (0, nb - 1), (rows - 1, 0), (rows - 1, nb - 1), (63, 31),
+                         (64, 32), (65, 64), (127, 1), (128, 65)]:
+        w = base.copy().reshape(rows * nb, bb)
+        w[:, 0:2] = np.frombuffer(f16_bytes(0.0), np.uint8)
+        w[rstar * nb + bstar, 0:2] = np.frombuffer(f16_bytes(0.125), np.uint8)
+        blk = w[rstar * nb + bstar]
+        if wtype == Q8:
+            vals = blk[2:].view(np.int8).astype(np.int64)
+        else:
+            qs = blk[2:].astype(np.int64)
+            vals = np.concatenate([qs & 15, qs >> 4]) - 8
+        isum = int(np.dot(vals, kint[bstar * 32:(bstar + 1) * 32]))
+        y, S = ref.dmmv(wtype, w.reshape(-1), rows, k, qx, dx)
+        want = np.zeros(rows)
+        want[rstar] = 0.125 * 2.0 ** -6 * isum
+        assert np.array_equal(y, want), (rstar, bstar)
+
+
+# ------------------------------------------------ P6: Q4_0 identity -------
+
+def test_p6_q4_identity_random_blocks(ref):
+    """The oracle evaluates sum (nib-8)*q and sum nib*q - 8*sum q and fails on a
+    mismatch; run it over many random blocks and activations."""
+    rng = np.random.default_rng(6)
+    w = inputs.gen_weights(Q4, 64, 32 * 64, 606)
+    x = rng.standard_normal(32 * 64).astype(np.float32)
+    qx, dx, _ = ref.quantize_act(x)
+    ref.dmmv(Q4, w, 64, 32 * 64, qx, dx)  # raises on an identity failure
+
+
+# ---------------------------------------------------- P7: nibble order ----
+
+def test_p7_nibble_order(ref):
+    """qs[0] = 0x0F, all other nibbles 8: element 0 = 15-8 = 7, element 16 = 0-8 = -8."""
+    qs = np.full(16, 0x88, np.uint8)
+    qs[0] = 0x0F
+    blk = np.frombuffer(f16_bytes(1.0) + qs.tobytes(), np.uint8).copy()
+    e0 = np.zeros(32, np.int8)
+    e0[0] = 127
+    e16 = np.zeros(32, np.int8)
+    e16[16] = 127
+    assert ref.block_isum(Q4, blk, e0) == 889
+    assert ref.block_isum(Q4, blk, e16) == -1016
+    e1 = np.zeros(32, np.int8)
+    e1[1] = 127
+    assert ref.block_isum(Q4, blk, e1) == 0
+
+
+# --------------------------------------------------- P8: brute force ------
+
+@pytest.mark.parametrize("wtype", [Q8, Q4])
+@pytest.mark.parametrize("k", [32, 64, 256])
+def test_p8_bruteforce_tiny(ref, wtype, k):
+    rows = 8
+    w = inputs.gen_weights(wtype, rows, k, 800 + k)
+    x = inputs.gen_activation(1, k, 900 + k)
+    qx, dx, _ = ref.quantize_act(x)
+    y, S = ref.dmmv(wtype, w, rows, k, qx, dx)
+    ybf = ref.dmmv_bruteforce(wtype, w, rows, k, qx, dx)
+    assert (np.abs(y - ybf) <= 1e-12 * S).all()
+
+
+@pytest.mark.parametrize("wl", [1, 2, 3])
+def test_p8_bruteforce_sampled_workloads(ref, wl):
+    cfg = inputs.WORKLOADS[wl]
+    w = inputs.gen_weights(cfg["wtype"], cfg["rows"], cfg["k"], inputs.seed_for(wl))
+    x = inputs.gen_activation(1, cfg["k"], inputs.seed_for(wl) + 1)
+    qx, dx, _ = ref.quantize_act(x)
+    rng = np.random.default_rng(wl)
+    rows = np.unique(np.concatenate([[0, cfg["rows"] - 1],
+                                     rng.integers(0, cfg["rows"], 254)])).astype(np.int64)
+    y, S = ref.dmmv(cfg["wtype"], w, cfg["rows"], cfg["k"], qx, dx, rows_eval=rows)
+    ybf = ref.dmmv_bruteforce(cfg["wtype"], w, cfg["rows"], cfg["k"], qx, dx, rows_eval=rows)
+    assert (np.abs(y - ybf) <= 1e-12 * S).all()
+
+
+def test_p8_bruteforce_gemm_entries(ref):
+    n, k, m = 40, 32 * 10, 6
+    w = inputs.gen_weights(Q4, n, k, 81)
+    x = inputs.gen_activation(m, k, 82)
+    qx, dx, _ = ref.quantize_act(x)
+    mi, ni = np.meshgrid(np.arange(m), np.arange(n), indexing="ij")
+    y, S = ref.gemm_entries(Q4, w, n, k, qx, dx, m, mi.ravel(), ni.ravel())
+    for t in range(m):
+        ybf = ref.dmmv_bruteforce(Q4, w, n, k, qx[t], dx[t])
+        assert (np.abs(y.reshape(m, n)[t] - ybf) <= 1e-12 * S.reshape(m, n)[t]).all()
+
+
+# ------------------------------------------------------ P9: linearity -----
+
+@pytest.mark.parametrize("wtype", [Q8, Q4])
+def test_p9_linearity(ref, wtype):
+    rows, k = 33, 32 * 12
+    nb = k // 32
+    bb = inputs.BLOCK_BYTES[wtype]
+    w = inputs.gen_weights(wtype, rows, k, 91)
+    x = inputs.gen_activation(1, k, 92)
+    qx, dx, sx = ref.quantize_act(x)
+    y, S, isums = ref.dmmv(wtype, w, rows, k, qx, dx, want_isums=True)
+    # doubling every weight scale doubles y exactly
+    w2 = w.copy().reshape(rows * nb, bb)
+    d = w2[:, 0:2].copy().view("<f2").astype(np.float64).ravel()
+    w2[:, 0:2] = (d * 2).astype("<f2").view(np.uint8).reshape(-1, 2)
+    y2, _ = ref.dmmv(wtype, w2.reshape(-1), rows, k, qx, dx)
+    assert np.array_equal(y2, 2 * y)
+    # negating x negates qx, sx and every isum; y flips sign exactly
+    qn, dn, sn = ref.quantize_act(-x)
+    assert np.array_equal(qn, -qx) and np.array_equal(dn, dx) and np.array_equal(sn, -sx)
+    yn, _, isn = ref.dmmv(wtype, w, rows, k, qn, dn, want_isums=True)
+    assert np.array_equal(isn, -isums) and np.array_equal(yn, -y)
+    # permuting rows permutes y
+    perm = np.random.default_rng(9).permutation(rows)
+    wp = w.reshape(rows, nb * bb)[perm].reshape(-1)
+    yp, _ = ref.dmmv(wtype, wp, rows, k, qx, dx)
+    assert np.array_equal(yp, y[perm])
+
+
+def test_p9_accumulate_adds_previous(ref):
+    rows, k = 16, 64
+    w = inputs.gen_weights(Q4, rows, k, 95)
+    qx, dx, _ = ref.quantize_act(inputs.gen_activation(1, k, 96))
+    y, S = ref.dmmv(Q4, w, rows, k, qx, dx)
+    prev = np.linspace(-3, 3, rows).astype(np.float32)
+    ya, Sa = ref.dmmv(Q4, w, rows, k, qx, dx, y_prev=prev)
+    assert np.array_equal(ya, y + prev.astype(np.float64))
+    assert np.array_equal(Sa, S + np.abs(prev.astype(np.float64)))
+
+
+# ---------------------------------------------------------- P11: MoE ------
+
+def test_p11_route_against_full_sort(ref):
+    for seed in range(20):
+        logits, g = inputs.gen_router(128, seed)
+        if seed == 3:
+            logits[10] = logits[20] = logits[30] = 5.0  # a three-way tie at the top
+        ids, wts = ref.moe_route(logits, 8, g)
+        order = np.lexsort((np.arange(128), -logits.astype(np.float64)))  # by -logit, then id
+        assert list(ids[:8]) == list(order[:8])
+        assert ids[8] == 128
+        assert abs(wts[:8].sum() - 1.0) < 1e-15
+        sel = logits[order[:8]].astype(np.float64)
+        want = np.exp(sel - sel.max()) / np.exp(sel - sel.max()).sum()
+        assert np.allclose(wts[:8], want, rtol=1e-14, atol=0)
+        assert wts[8] == pytest.approx(1 / (1 + math.exp(-float(g))), rel=1e-15)
+        assert (np.diff(wts[:8]) <= 0).all()
+    ids, wts = ref.moe_route(np.zeros(128, np.float32), 8, np.float32(0.0))
+    assert list(ids) == list(range(8)) + [128]
+    assert (wts[:8] == 0.125).all() and wts[8] == 0.5
+    ids, wts = ref.moe_route(np.zeros(128, np.float32), 8, None)
+    assert ids.size == 8
+
+
+def test_p11_swiglu_closed_forms(ref):
+    gu = np.array([[0.0, 1.0, -30.0, 3.0, 5.0, 2.0, 7.0, 1.0]], np.float32)  # f = 4
+    h = ref.swiglu(gu, 4)[0]
+    assert h[0] == 0.0
+    assert h[1] == np.float32(1.0 / (1.0 + math.exp(-1.0)) * 2.0)
+    assert h[2] == np.float32(-30.0 / (1.0 + math.exp(30.0)) * 7.0) and abs(h[2]) < 1e-10
+    assert h[3] == np.float32(3.0 / (1.0 + math.exp(-3.0)))
+    # silu(z) - silu(-z) = z
+    z = np.linspace(-8, 8, 64).astype(np.float32)
+    gu = np.concatenate([z, -z, np.ones(64), np.ones(64)]).astype(np.float32).reshape(1, -1)
+    h = ref.swiglu(gu, 128)[0]
+    assert np.allclose(h[:64].astype(np.float64) - h[64:].astype(np.float64), z, rtol=0, atol=4e-6)
+
+
+def test_p11_moe_identical_and_one_hot_experts(ref):
+    d_model, d_ff, E = 256, 64, 5
+    bank_gu, gs, bank_d, ds = inputs.moe_banks(1100, E, d_model, d_ff)
+    # make every expert a copy of expert 0
+    bank_gu = np.tile(bank_gu[:gs], E)
+    bank_d = np.tile(bank_d[:ds], E)
+    x = inputs.gen_activation(1, d_model, 1101)
+    ids = np.array([0, 1, 2, 3, 4], np.int32)
+    wts = np.array([0.1, 0.2, 0.3, 0.25, 0.15])
+    y, S = ref.moe_ffn(Q4, bank_gu, gs, bank_d, ds, d_model, d_ff, ids, wts, x)
+    y1, S1 = ref.moe_ffn(Q4, bank_gu, gs, bank_d, ds, d_model, d_ff, ids[:1], np.ones(1), x)
+    assert (np.abs(y - y1) <= 1e-12 * S1).all()
+    # one-hot weights pick that expert alone; permuting (id, w) pairs changes nothing
+    bank_gu, gs, bank_d, ds = inputs.moe_banks(1200, E, d_model, d_ff)
+    y3, S3 = ref.moe_ffn(Q4, bank_gu, gs, bank_d, ds, d_model, d_ff, ids, np.eye(5)[3], x)
+    y3b, _ = ref.moe_ffn(Q4, bank_gu, gs, bank_d, ds, d_model, d_ff, ids[3:4], np.ones(1), x)
+    assert (np.abs(y3 - y3b) <= 1e-12 * S3).all()
+    ya, Sa = ref.moe_ffn(Q4, bank_gu, gs, bank_d, ds, d_model, d_ff, ids, wts, x)
+    p = np.array([4, 2, 0, 3, 1])
+    yb, _ = ref.moe_ffn(Q4, bank_gu, gs, bank_d, ds, d_model, d_ff, ids[p], wts[p], x)
+    assert (np.abs(ya - yb) <= 1e-12 * Sa).all()
+
+
+# -------------------------------------------------------- P12: argmax -----
+
+def test_p12_argmax_cases(ref):
+    y = np.zeros(100, np.float32)
+    y[5] = y[7] = 3.0
+    assert ref.argmax_f32(y) == 5
+    y = -np.arange(1, 130, dtype=np.float32)
+    assert ref.argmax_f32(y) == 0
+    y = np.arange(67, dtype=np.float32)
+    assert ref.argmax_f32(y) == 66
+    y = np.full(1, -7.0, np.float32)
+    assert ref.argmax_f32(y) == 0
+    y = np.random.default_rng(12).standard_normal(1000).astype(np.float32)
+    assert ref.argmax_f32(y) == int(np.argmax(y))
+    assert ref.argmax_f32(np.zeros(0, np.float32)) == -1
+
+
+# ---------------------------------------------------- P13: determinism ----
+
+def test_p13_deterministic(ref):
+    w = inputs.gen_weights(Q4, 64, 512, 131)
+    x = inputs.gen_activation(1, 512, 132)
+    a = ref.quantize_act(x)
+    b = ref.quantize_act(x)
+    assert all(np.array_equal(u, v) for u, v in zip(a, b))
+    y1, S1 = ref.dmmv(Q4, w, 64, 512, a[0], a[1])
+    y2, S2 = ref.dmmv(Q4, w, 64, 512, b[0], b[1])
+    assert np.array_equal(y1, y2) and np.array_equal(S1, S2)
+    # the generators are seeded
+    assert np.array_equal(inputs.gen_weights(Q8, 4, 64, 7), inputs.gen_weights(Q8, 4, 64, 7))
+
+
+# ------------------------------------------- P14: quantization error ------
+
+@pytest.mark.parametrize("wtype", [Q8, Q4])
+def test_p14_quantization_error_bound(ref, wtype):
+    rows, k = 64, 2048
+    w = inputs.gen_weights(wtype, rows, k, 141)
+    x = inputs.gen_activation(1, k, 142)
+    qx, dx, _ = ref.quantize_act(x)
+    y, _ = ref.dmmv(wtype, w, rows, k, qx, dx)
+    yt = ref.dmmv_true(wtype, w, rows, k, x)
+    bound = ref.quant_error_bound(wtype, w, rows, k, dx)
+    assert (np.abs(y - yt) <= bound * (1 + 1e-6)).all()
+    # and the bound is not vacuous: the typical error is well inside it
+    assert np.median(np.abs(y - yt) / bound) < 0.2
+
+
+# ----------------------------------------------- generators' recipe -------
+
+def test_generator_distributions():
+    w = inputs.gen_weights(Q4, 512, 2048, 1).reshape(-1, 18)
+    d = w[:, :2].copy().view("<f2").astype(np.float64).ravel()
+    assert (d >= 0).all() and abs(d.mean() - 0.02 * math.sqrt(2 / math.pi)) < 2e-4
+    nib = np.concatenate([w[:, 2:] & 15, w[:, 2:] >> 4]).ravel()
+    assert abs(nib.mean() - 7.5) < 0.05 and nib.min() == 0 and nib.max() == 15
+    w = inputs.gen_weights(Q8, 512, 2048, 1).reshape(-1, 34)
+    q = w[:, 2:].view(np.int8)
+    assert q.min() == -127 and q.max() == 127
+    d = w[:, :2].copy().view("<f2").astype(np.float64).ravel()
+    assert abs(d.mean() - 0.01 * math.sqrt(2 / math.pi)) < 1e-4
+    # some scales are fp16 subnormals; they must be kept as such
+    assert (d < 2.0 ** -14).any()
