@@ -1,0 +1,462 @@
+#!/usr/bin/env python3
+"""Throughput of the block-quantized decode path on one MI355X.
+
+Default (workload 2): one step = quantize one fp32 activation of 4096 to int8
+blocks, then the Q4_0 DMMV of a 4096 x 4096 weight matrix.  Weights rotate
+over distinct copies whose total is more than twice the 256 MB MALL, so every
+step streams its weights from HBM.  Prints ONE JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1..5]
+
+Timing: a GPU-side spin kernel is queued ahead of the timed region so that the
+K steps are enqueued before the GPU reaches them and run back to back (host
+launch cost is not what is measured); HIP events on the launch stream bracket
+exactly the K steps.  A second pass times the dominant kernel alone with an
+event pair around each launch (roofline.achieved).  The CPU oracle is timed on
+a bounded sample of the same workload (cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA, TOP/s
+MALL_BYTES = 256 << 20
+
+METRIC = "DMMV achieved HBM GB/s (% of MI355X peak) + rows/s, Q4_0 4096x4096"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one 256 MiB device copy (counter calibration)")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------- workloads --
+
+class Workload:
+    name = ""
+    dominant = ""            # name of the dominant kernel
+    bound = "hbm"
+    steps = 2000
+    warmup = 50
+
+    def setup(self, torch, zq, inputs):
+        raise NotImplementedError
+
+    def step(self, i):
+        raise NotImplementedError
+
+    def dominant_launch(self, i, ev_start, ev_end):
+        """Run step i with ev_start/ev_end recorded around the dominant kernel."""
+        raise NotImplementedError
+
+    def value(self, ms_per_step):
+        """(value, unit) of the whole step."""
+        raise NotImplementedError
+
+    def achieved(self, ms_per_launch):
+        raise NotImplementedError
+
+    def cpu_baseline(self, seconds):
+        raise NotImplementedError
+
+
+def copies_for(nbytes, lo=2):
+    return max(lo, int(np.ceil(2 * MALL_BYTES / nbytes)) + 1)
+
+
+class DmmvWorkload(Workload):
+    """Quantize + DMMV (+ argmax for the LM head)."""
+
+    def __init__(self, wl):
+        from block_quant_matrix_amd import inputs
+        cfg = inputs.WORKLOADS[wl]
+        self.wl = wl
+        self.name = cfg["name"]
+        self.wtype, self.rows, self.k = cfg["wtype"], cfg["rows"], cfg["k"]
+        self.argmax = wl == 3
+        self.bb = inputs.BLOCK_BYTES[self.wtype]
+        self.nb = self.k // 32
+        self.wbytes = self.rows * self.nb * self.bb
+        self.dmmv_bytes = (self.wbytes + self.k + 4 * self.nb + 4 * self.rows +
+                           (4 * self.nb if self.wtype == inputs.Q4_0 else 0))
+        self.step_bytes = self.dmmv_bytes  # bytes the step's DMMV must move
+        self.dominant = "dmmv_q4_0" if self.wtype == inputs.Q4_0 else "dmmv_q8_0"
+        self.steps = {1: 20000, 2: 4000, 3: 200}[wl]
+        self.warmup = {1: 500, 2: 200, 3: 10}[wl]
+
+    def setup(self, torch, zq, inputs):
+        self.torch, self.zq = torch, zq
+        self.ncopy = copies_for(self.wbytes)
+        host = [inputs.gen_weights(self.wtype, self.rows, self.k, inputs.seed_for(self.wl, c))
+                for c in range(self.ncopy)]
+        self.w = [torch.from_numpy(h).to("cuda") for h in host]
+        self.w_host0 = host[0]
+        del host
+        self.x_host = inputs.gen_activation(1, self.k, inputs.seed_for(self.wl) + 1)
+        self.x = torch.from_numpy(self.x_host).to("cuda")
+        self.qx = torch.empty(self.k, dtype=torch.int8, device="cuda")
+        self.dx = torch.empty(self.nb, dtype=torch.float32, device="cuda")
+        self.sx = torch.empty(self.nb, dtype=torch.int32, device="cuda")
+        self.y = torch.empty(self.rows, dtype=torch.float32, device="cuda")
+        if self.argmax:
+            self.ws_bytes = zq.zq_argmax_workspace_bytes(self.rows)
+            self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
+            self.idx = torch.empty(1, dtype=torch.int32, device="cuda")
+
+    def _dmmv(self, w):
+        if self.wtype == 4:
+            self.zq.zq_dmmv_q4_0(w, self.rows, self.k, self.qx, self.dx, self.sx, self.y)
+        else:
+            self.zq.zq_dmmv_q8_0(w, self.rows, self.k, self.qx, self.dx, self.y)
+
+    def step(self, i):
+        self.zq.zq_quantize_act(self.x, 1, self.k, self.k, self.qx, self.dx, self.sx)
+        self._dmmv(self.w[i % self.ncopy])
+        if self.argmax:
+            self.zq.zq_argmax_f32(self.y, self.rows, self.idx, self.ws, self.ws_bytes)
+
+    def dominant_launch(self, i, e0, e1):
+        self.zq.zq_quantize_act(self.x, 1, self.k, self.k, self.qx, self.dx, self.sx)
+        e0.record()
+        self._dmmv(self.w[i % self.ncopy])
+        e1.record()
+        if self.argmax:
+            self.zq.zq_argmax_f32(self.y, self.rows, self.idx, self.ws, self.ws_bytes)
+
+    def value(self, ms):
+        return self.step_bytes / (ms * 1e-3) / 1e9, "GB/s"
+
+    def achieved(self, ms):
+        return self.dmmv_bytes / (ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s", self.dmmv_bytes
+
+    def extra(self, ms):
+        return {"rows_per_s": self.rows / (ms * 1e-3)}
+
+    def cpu_baseline(self, seconds):
+        import oracle
+        n, t0 = 0, time.perf_counter()
+        while True:
+            qx, dx, sx = oracle.quantize_act(self.x_host)
+            oracle.dmmv(self.wtype, self.w_host0, self.rows, self.k, qx, dx)
+            if self.argmax:
+                pass  # the oracle's argmax is negligible next to the rows
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+        per = el / n
+        return dict(value=self.step_bytes / per / 1e9, unit="GB/s", cores=1, kind="oracle",
+                    sample="%d full steps (quantize + %d-row DMMV) of this workload on one "
+                           "host thread, %.1f s" % (n, self.rows, el))
+
+
+class MoeWorkload(Workload):
+    """Router + one token through 8 routed + 1 shared Q4_0 experts."""
+    dominant = "dmmv_moe_gather"
+    steps = 2000
+    warmup = 100
+
+    def __init__(self):
+        from block_quant_matrix_amd import inputs
+        cfg = inputs.WORKLOADS[4]
+        self.name = cfg["name"]
+        self.E, self.top_k, self.dm, self.dff = cfg["n_routed"], cfg["top_k"], cfg["d_model"], cfg["d_ff"]
+        self.n_sel = self.top_k + 1
+        bb = 18
+        self.gu_w = self.n_sel * 2 * self.dff * (self.dm // 32) * bb
+        self.down_w = self.n_sel * self.dm * (self.dff // 32) * bb
+        self.step_bytes = self.gu_w + self.down_w + 4 * self.dm + 4 * self.dm
+        self.gather_bytes = self.gu_w + self.dm + 8 * (self.dm // 32) + 4 * self.n_sel * 2 * self.dff
+
+    def setup(self, torch, zq, inputs):
+        self.torch, self.zq = torch, zq
+        bank_bytes = (self.E + 1) * (2 * self.dff * (self.dm // 32) + self.dm * (self.dff // 32)) * 18
+        self.ncopy = copies_for(bank_bytes)
+        self.banks = []
+        for c in range(self.ncopy):
+            gu, gs, down, ds = inputs.moe_banks(inputs.seed_for(4, c), self.E + 1, self.dm, self.dff)
+            self.banks.append((torch.from_numpy(gu).to("cuda"), torch.from_numpy(down).to("cuda")))
+            if c == 0:
+                self.host_bank = (gu, gs, down, ds)
+        self.gs, self.ds = gs, ds
+        nlog = 64
+        lg = [inputs.gen_router(self.E, inputs.seed_for(4, 100 + i)) for i in range(nlog)]
+        self.logits = torch.from_numpy(np.stack([l for l, _ in lg])).to("cuda")
+        self.gates = torch.from_numpy(np.array([g for _, g in lg], np.float32)).to("cuda")
+        self.host_router = lg[0]
+        self.x_host = inputs.gen_activation(1, self.dm, inputs.seed_for(4) + 7)
+        self.x = torch.from_numpy(self.x_host).to("cuda")
+        self.ids = torch.empty(self.n_sel, dtype=torch.int32, device="cuda")
+        self.wts = torch.empty(self.n_sel, dtype=torch.float32, device="cuda")
+        self.ws_bytes = zq.zq_moe_ffn_workspace_bytes(self.dm, self.dff, self.n_sel)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
+        self.y = torch.empty(self.dm, dtype=torch.float32, device="cuda")
+        # stage buffers for the instrumented pass
+        self.qx = torch.empty(self.dm, dtype=torch.int8, device="cuda")
+        self.dxv = torch.empty(self.dm // 32, dtype=torch.float32, device="cuda")
+        self.sxv = torch.empty(self.dm // 32, dtype=torch.int32, device="cuda")
+        self.gu = torch.empty((self.n_sel, 2 * self.dff), dtype=torch.float32, device="cuda")
+        self.qh = torch.empty((self.n_sel, self.dff), dtype=torch.int8, device="cuda")
+        self.dh = torch.empty((self.n_sel, self.dff // 32), dtype=torch.float32, device="cuda")
+        self.sh = torch.empty((self.n_sel, self.dff // 32), dtype=torch.int32, device="cuda")
+
+    def _route(self, i):
+        j = i % self.logits.shape[0]
+        self.zq.zq_moe_route(self.logits[j], self.E, self.top_k, self.gates[j:j + 1], self.ids,
+                             self.wts)
+
+    def step(self, i):
+        gu, down = self.banks[i % self.ncopy]
+        self._route(i)
+        self.zq.zq_moe_ffn(4, gu, self.gs, down, self.ds, self.E + 1, self.dm, self.dff, self.ids,
+                           self.wts, self.n_sel, self.x, self.ws, self.ws_bytes, self.y)
+
+    def dominant_launch(self, i, e0, e1):
+        zq = self.zq
+        gu, down = self.banks[i % self.ncopy]
+        self._route(i)
+        zq.zq_quantize_act(self.x, 1, self.dm, self.dm, self.qx, self.dxv, self.sxv)
+        e0.record()
+        zq.zq_dmmv_moe(4, gu, self.E + 1, self.gs, 2 * self.dff, self.dm, self.ids, None, self.n_sel,
+                       self.qx, self.dxv, self.sxv, 0, 0, self.gu)
+        e1.record()
+        zq.zq_swiglu_quantize(self.gu, self.n_sel, self.dff, self.qh, self.dh, self.sh)
+        zq.zq_dmmv_moe(4, down, self.E + 1, self.ds, self.dm, self.dff, self.ids, self.wts,
+                       self.n_sel, self.qh, self.dh, self.sh, self.dff, 1, self.y)
+
+    def value(self, ms):
+        return self.step_bytes / (ms * 1e-3) / 1e9, "GB/s"
+
+    def achieved(self, ms):
+        return self.gather_bytes / (ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s", self.gather_bytes
+
+    def extra(self, ms):
+        return {"tokens_per_s": 1.0 / (ms * 1e-3)}
+
+    def cpu_baseline(self, seconds):
+        import oracle
+        gu, gs, down, ds = self.host_bank
+        logits, g = self.host_router
+        n, t0 = 0, time.perf_counter()
+        while True:
+            ids, wts = oracle.moe_route(logits, self.top_k, g)
+            oracle.moe_ffn(4, gu, gs, down, ds, self.dm, self.dff, ids, wts, self.x_host)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+        per = el / n
+        return dict(value=self.step_bytes / per / 1e9, unit="GB/s", cores=1, kind="oracle",
+                    sample="%d full MoE tokens (route + 9 experts) on one host thread, %.1f s"
+                           % (n, el))
+
+
+class GemmWorkload(Workload):
+    dominant = "gemm_prefill"
+    bound = "mfma"
+    steps = 100
+    warmup = 10
+
+    def __init__(self):
+        from block_quant_matrix_amd import inputs
+        cfg = inputs.WORKLOADS[5]
+        self.name = cfg["name"]
+        self.m, self.n, self.k = cfg["m"], cfg["n"], cfg["k"]
+        self.ops = 2 * self.m * self.n * self.k
+
+    def setup(self, torch, zq, inputs):
+        self.torch, self.zq = torch, zq
+        wbytes = self.n * (self.k // 32) * 18
+        self.ncopy = copies_for(wbytes)
+        host = [inputs.gen_weights(4, self.n, self.k, inputs.seed_for(5, c)) for c in range(self.ncopy)]
+        self.w = [torch.from_numpy(h).to("cuda") for h in host]
+        self.w_host0 = host[0]
+        del host
+        self.x_host = inputs.gen_activation(self.m, self.k, inputs.seed_for(5) + 1)
+        self.x = torch.from_numpy(self.x_host).to("cuda")
+        self.qx = torch.empty((self.m, self.k), dtype=torch.int8, device="cuda")
+        self.dx = torch.empty((self.m, self.k // 32), dtype=torch.float32, device="cuda")
+        self.y = torch.empty((self.m, self.n), dtype=torch.float32, device="cuda")
+
+    def step(self, i):
+        self.zq.zq_quantize_act(self.x, self.m, self.k, self.k, self.qx, self.dx, None)
+        self.zq.zq_gemm_prefill(4, self.w[i % self.ncopy], self.n, self.k, self.qx, self.dx, None,
+                                self.m, self.y)
+
+    def dominant_launch(self, i, e0, e1):
+        self.zq.zq_quantize_act(self.x, self.m, self.k, self.k, self.qx, self.dx, None)
+        e0.record()
+        self.zq.zq_gemm_prefill(4, self.w[i % self.ncopy], self.n, self.k, self.qx, self.dx, None,
+                                self.m, self.y)
+        e1.record()
+
+    def value(self, ms):
+        return self.ops / (ms * 1e-3) / 1e12, "TOP/s"
+
+    def achieved(self, ms):
+        return self.ops / (ms * 1e-3) / 1e12, INT8_PEAK_TOPS, "TOP/s", self.ops
+
+    def extra(self, ms):
+        return {"tokens_per_s": self.m / (ms * 1e-3)}
+
+    def cpu_baseline(self, seconds):
+        import oracle
+        rng = np.random.default_rng(0)
+        qx, dx, _ = oracle.quantize_act(self.x_host)
+        n_pairs, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            mi = rng.integers(0, self.m, 256)
+            ni = rng.integers(0, self.n, 256)
+            oracle.gemm_entries(4, self.w_host0, self.n, self.k, qx, dx, self.m, mi, ni)
+            n_pairs += 256
+        el = time.perf_counter() - t0
+        ops_per_s = n_pairs * 2 * self.k / el
+        return dict(value=ops_per_s / 1e12, unit="TOP/s", cores=1, kind="oracle",
+                    sample="%d output entries (of %d) of this GEMM on one host thread, %.1f s"
+                           % (n_pairs, self.m * self.n, el))
+
+
+def make_workload(wl):
+    if wl in (1, 2, 3):
+        return DmmvWorkload(wl)
+    if wl == 4:
+        return MoeWorkload()
+    return GemmWorkload()
+
+
+# ----------------------------------------------------------------- timing --
+
+_SLEEP_CYCLES_PER_MS = None
+
+
+def gpu_blocker(torch, ms):
+    """Queue about `ms` of GPU work (torch's spin kernel) so the launches that
+    follow are all enqueued before the GPU reaches them."""
+    global _SLEEP_CYCLES_PER_MS
+    if _SLEEP_CYCLES_PER_MS is None:  # calibrate the spin kernel's clock once
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        torch.cuda._sleep(10_000_000)
+        e1.record()
+        torch.cuda.synchronize()
+        _SLEEP_CYCLES_PER_MS = 10_000_000 / max(e0.elapsed_time(e1), 1e-3)
+    ms = min(max(ms, 1.0), 2000.0)
+    torch.cuda._sleep(int(ms * _SLEEP_CYCLES_PER_MS))
+
+
+def host_launch_ms(w, torch, n=50):
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n):
+        w.step(i)
+    el = (time.perf_counter() - t0) * 1e3 / n
+    torch.cuda.synchronize()
+    return el
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(got --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from block_quant_matrix_amd import inputs, zq
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    if zq.zq_device_check(0) != 0:
+        print("device 0 is not gfx950", file=sys.stderr)
+        sys.exit(1)
+
+    w = make_workload(args.workload)
+    K = args.steps if args.steps is not None else w.steps
+    W = args.warmup if args.warmup is not None else w.warmup
+    w.setup(torch, zq, inputs)
+
+    if args.calibrate_copy:  # a plain copy of known size, for counter scaling
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        del src, dst
+
+    for i in range(W):
+        w.step(i)
+    torch.cuda.synchronize()
+    h_ms = host_launch_ms(w, torch)
+
+    # --- timed region: exactly K steps between two events ---
+    t_ev0 = torch.cuda.Event(enable_timing=True)
+    t_ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    gpu_blocker(torch, 1.5 * h_ms * K + 5)
+    t_ev0.record()
+    for i in range(K):
+        w.step(i)
+    t_ev1.record()
+    torch.cuda.synchronize()
+    ms_per_step = t_ev0.elapsed_time(t_ev1) / K
+
+    # --- dominant kernel: an event pair around every launch ---
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    torch.cuda.synchronize()
+    gpu_blocker(torch, 1.5 * h_ms * K + 5)
+    for i in range(K):
+        w.dominant_launch(i, *evs[i])
+    torch.cuda.synchronize()
+    ms_kernel = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    value, unit = w.value(ms_per_step)
+    ach, peak, runit, per_launch = w.achieved(ms_kernel)
+    out = {
+        "metric": METRIC if args.workload == 2 else "%s throughput (%s)" % (w.name, unit),
+        "value": round(value, 3),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": w.name, "weight_copies": w.ncopy, "parallelism": "none"},
+        "pct_of_peak": round(100.0 * value / (HBM_PEAK_GBS if unit == "GB/s" else INT8_PEAK_TOPS), 2),
+    }
+    out.update({k: round(v, 1) for k, v in w.extra(ms_per_step).items()})
+    out["roofline"] = {"bound": w.bound, "kernel": w.dominant, "achieved": round(ach, 3),
+                       "peak": peak, "unit": runit, "frac": round(ach / peak, 4),
+                       "per_launch": per_launch, "ms_per_launch": round(ms_kernel, 6),
+                       "traffic": None}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = w.cpu_baseline(args.cpu_seconds)
+        out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 4)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

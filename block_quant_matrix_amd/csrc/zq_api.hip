@@ -1,0 +1,338 @@
+// zq_api.hip -- the extern "C" boundary of libzq: argument checks, then
+// launches on the caller's stream.  Every check runs before any launch, so a
+// rejected call writes nothing.
+#include <atomic>
+#include <cstring>
+
+#include "zq_common.h"
+#include "zq_internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// Per-device capability cache: 0 unknown, 1 gfx950, -1 other.
+std::atomic<int> g_dev_ok[kMaxDevices];
+
+int check_device(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return ZQ_EDEVICE;
+  int v = g_dev_ok[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ZQ_EDEVICE;
+    v = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+    g_dev_ok[dev].store(v, std::memory_order_relaxed);
+  }
+  return v == 1 ? ZQ_OK : ZQ_EDEVICE;
+}
+
+int check_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return ZQ_EDEVICE;
+  return check_device(dev);
+}
+
+inline bool al(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+inline bool k_ok(int64_t k) { return k > 0 && k % 32 == 0 && k / 32 <= (int64_t(1) << 30); }
+inline hipStream_t S(void *s) { return static_cast<hipStream_t>(s); }
+inline int64_t block_bytes(int wtype) { return wtype == ZQ_Q4_0 ? 18 : (wtype == ZQ_Q8_0 ? 34 : -1); }
+
+#define ZQ_REQUIRE(cond, code) \
+  do {                         \
+    if (!(cond)) return (code); \
+  } while (0)
+
+constexpr size_t kAlign = 256;
+inline size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct MoeWorkspace {
+  size_t qx, dx, sx, gu, qh, dh, sh, total;
+};
+
+MoeWorkspace moe_layout(int64_t d_model, int64_t d_ff, int32_t n_sel) {
+  MoeWorkspace w;
+  size_t off = 0;
+  w.qx = off; off += round_up(static_cast<size_t>(d_model));
+  w.dx = off; off += round_up(static_cast<size_t>(d_model / 32) * 4);
+  w.sx = off; off += round_up(static_cast<size_t>(d_model / 32) * 4);
+  w.gu = off; off += round_up(static_cast<size_t>(n_sel) * 2 * d_ff * 4);
+  w.qh = off; off += round_up(static_cast<size_t>(n_sel) * d_ff);
+  w.dh = off; off += round_up(static_cast<size_t>(n_sel) * (d_ff / 32) * 4);
+  w.sh = off; off += round_up(static_cast<size_t>(n_sel) * (d_ff / 32) * 4);
+  w.total = off;
+  return w;
+}
+
+int dmmv_common(int wtype, const void *w, int64_t rows, int64_t k, const int8_t *qx,
+                const float *dx, const int32_t *sx, float *y, uint32_t flags, void *stream) {
+  ZQ_REQUIRE(w && qx && dx && y, ZQ_ENULL);
+  ZQ_REQUIRE(rows >= 0 && k_ok(k), ZQ_EINVAL);
+  ZQ_REQUIRE((flags & ~uint32_t(ZQ_ACCUMULATE)) == 0, ZQ_EINVAL);
+  ZQ_REQUIRE(al(w, 4) && al(qx, 16) && al(dx, 4) && al(y, 4) && al(sx, 4), ZQ_EALIGN);
+  const int dc = check_current_device();
+  if (dc != ZQ_OK) return dc;
+  zq::DmmvArgs a{};
+  a.w = static_cast<const uint8_t *>(w);
+  a.qx = qx;
+  a.dx = dx;
+  a.sx = wtype == ZQ_Q4_0 ? sx : nullptr;
+  a.y = y;
+  a.rows = rows;
+  a.nb = static_cast<int32_t>(k / 32);
+  a.flags = flags;
+  return zq::launch_dmmv(wtype, zq::MODE_PLAIN, a, S(stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int zq_version(void) { return 1; }
+
+const char *zq_strerror(int status) {
+  switch (status) {
+    case ZQ_OK: return "ok";
+    case ZQ_EINVAL: return "invalid argument (size, k % 32, flags, type, mode or range)";
+    case ZQ_ENULL: return "a required pointer is NULL";
+    case ZQ_EALIGN: return "misaligned pointer or stride";
+    case ZQ_ERANGE: return "expert id out of range";
+    case ZQ_EDEVICE: return "current device is not a gfx950 GPU";
+    case ZQ_ELAUNCH: return "kernel launch failed";
+    default: return "unknown zq status";
+  }
+}
+
+int zq_device_check(int device) { return check_device(device); }
+
+int zq_quantize_act(const float *x, int64_t n_tok, int64_t k, int64_t x_stride, int8_t *qx,
+                    float *dx, int32_t *sx, void *stream) {
+  ZQ_REQUIRE(x && qx && dx, ZQ_ENULL);
+  ZQ_REQUIRE(n_tok >= 0 && k_ok(k) && x_stride >= k, ZQ_EINVAL);
+  ZQ_REQUIRE(n_tok * (k / 32) <= (int64_t(1) << 31), ZQ_EINVAL);
+  ZQ_REQUIRE(al(x, 16) && x_stride % 4 == 0 && al(qx, 16) && al(dx, 4) && al(sx, 4), ZQ_EALIGN);
+  const int dc = check_current_device();
+  if (dc != ZQ_OK) return dc;
+  return zq::launch_quantize_act(x, n_tok, k, x_stride, qx, dx, sx, S(stream));
+}
+
+int zq_dmmv_q8_0(const void *w, int64_t rows, int64_t k, const int8_t *qx, const float *dx,
+                 float *y, uint32_t flags, void *stream) {
+  return dmmv_common(ZQ_Q8_0, w, rows, k, qx, dx, nullptr, y, flags, stream);
+}
+
+int zq_dmmv_q4_0(const void *w, int64_t rows, int64_t k, const int8_t *qx, const float *dx,
+                 const int32_t *sx, float *y, uint32_t flags, void *stream) {
+  return dmmv_common(ZQ_Q4_0, w, rows, k, qx, dx, sx, y, flags, stream);
+}
+
+int zq_dmmv_isums(int wtype, const void *w, int64_t rows, int64_t k, const int8_t *qx,
+                  const int32_t *sx, int32_t *isums, void *stream) {
+  ZQ_REQUIRE(block_bytes(wtype) > 0, ZQ_EINVAL);
+  ZQ_REQUIRE(w && qx && isums, ZQ_ENULL);
+  ZQ_REQUIRE(rows >= 0 && k_ok(k), ZQ_EINVAL);
+  ZQ_REQUIRE(al(w, 4) && al(qx, 16) && al(sx, 4) && al(isums, 4), ZQ_EALIGN);
+  const int dc = check_current_device();
+  if (dc != ZQ_OK) return dc;
+  zq::DmmvArgs a{};
+  a.w = static_cast<const uint8_t *>(w);
+  a.qx = qx;
+  a.sx = wtype == ZQ_Q4_0 ? sx : nullptr;
+  a.isums = isums;
+  a.rows = rows;
+  a.nb = static_cast<int32_t>(k / 32);
+  // dx must be readable by the shared inner loop: point it at qx's bytes,
+  // which span k bytes >= (k/32)*4 bytes; the value only feeds the unused
+  // fp32 partial.
+  a.dx = reinterpret_cast<const float *>(qx);
+  return zq::launch_dmmv(wtype, zq::MODE_ISUMS, a, S(stream));
+}
+
+size_t zq_argmax_workspace_bytes(int64_t n) { return zq::argmax_workspace(n); }
+
+int zq_argmax_f32(const float *y, int64_t n, int32_t *out_idx, void *workspace,
+                  size_t workspace_bytes, void *stream) {
+  ZQ_REQUIRE(y && out_idx && workspace, ZQ_ENULL);
+  ZQ_REQUIRE(n >= 1 && n <= INT32_MAX, ZQ_EINVAL);
+  ZQ_REQUIRE(workspace_bytes >= zq::argmax_workspace(n), ZQ_EINVAL);
+  ZQ_REQUIRE(al(y, 4) && al(out_idx, 4) && al(workspace, 8), ZQ_EALIGN);
+  const int dc = check_current_device();
+  if (dc != ZQ_OK) return dc;
+  return zq::launch_argmax(y, n, out_idx, workspace, S(stream));
+}
+
+int zq_moe_route(const float *logits, int32_t n_routed, int32_t top_k, const float *shared_gate,
+                 int32_t *ids, float *wts, void *stream) {
+  ZQ_REQUIRE(logits && ids && wts, ZQ_ENULL);
+  ZQ_REQUIRE(top_k >= 1 && top_k <= 64 && n_routed >= top_k && n_routed <= 1024, ZQ_EINVAL);
+  ZQ_REQUIRE(al(logits, 4) && al(ids, 4) && al(wts, 4) && al(shared_gate, 4), ZQ_EALIGN);
+  const int dc = check_current_device();
+  if (dc != ZQ_OK) return dc;
+  return zq::launch_moe_route(logits, n_routed, top_k, shared_gate, ids, wts, S(stream));
+}
+
+int zq_dmmv_moe(int wtype, const void *bank, int64_t n_experts, int64_t expert_stride_bytes,
+                int64_t rows, int64_t k, const int32_t *ids, const float *wts, int32_t n_sel,
+                const int8_t *qx, const float *dx, const int32_t *sx, int64_t x_stride, int mode,
+                float *y, uint32_t flags, int32_t *dev_status, void *stream) {
+  const int64_t bb = block_bytes(wtype);
+  ZQ_REQUIRE(bb > 0, ZQ_EINVAL);
+  ZQ_REQUIRE(mode == ZQ_MOE_GATHER || mode == ZQ_MOE_WEIGHTED_SUM, ZQ_EINVAL);
+  ZQ_REQUIRE(bank && ids && qx && dx && y, ZQ_ENULL);
+  ZQ_REQUIRE(mode == ZQ_MOE_GATHER || wts, ZQ_ENULL);
+  ZQ_REQUIRE(n_experts >= 1 && n_experts <= INT32_MAX && rows >= 0 && k_ok(k), ZQ_EINVAL);
+  ZQ_REQUIRE(n_sel >= 0 && n_sel <= 65535, ZQ_EINVAL);
+  ZQ_REQUIRE(x_stride >= 0 && x_stride % 32 == 0 && (x_stride == 0 || x_stride >= k), ZQ_EINVAL);
+  ZQ_REQUIRE(expert_stride_bytes >= rows * (k / 32) * bb && expert_stride_bytes % 2 == 0,
+             ZQ_EINVAL);
+  if (mode == ZQ_MOE_GATHER) {
+    ZQ_REQUIRE(flags == 0, ZQ_EINVAL);
+  } else {
+    ZQ_REQUIRE((flags & ~uint32_t(ZQ_ACCUMULATE)) == 0, ZQ_EINVAL);
+  }
+  ZQ_REQUIRE(al(bank, 4) && al(ids, 4) && al(wts, 4) && al(qx, 16) && al(dx, 4) && al(sx, 4) &&
+                 al(y, 4) && al(dev_status, 4),
+             ZQ_EALIGN);
+  const int dc = check_current_device();
+  if (dc != ZQ_OK) return dc;
+  zq::DmmvArgs a{};
+  a.w = static_cast<const uint8_t *>(bank);
+  a.qx = qx;
+  a.dx = dx;
+  a.sx = wtype == ZQ_Q4_0 ? sx : nullptr;
+  a.y = y;
+  a.ids = ids;
+  a.wts = wts;
+  a.status = dev_status;
+  a.rows = rows;
+  a.expert_stride = expert_stride_bytes;
+  a.x_stride = x_stride;
+  a.nb = static_cast<int32_t>(k / 32);
+  a.n_experts = static_cast<int32_t>(n_experts);
+  a.n_sel = n_sel;
+  a.flags = flags;
+  return zq::launch_dmmv(wtype, mode == ZQ_MOE_GATHER ? zq::MODE_GATHER : zq::MODE_WEIGHTED, a,
+                         S(stream));
+}
+
+int zq_swiglu_quantize(const float *gu, int64_t n, int64_t f, int8_t *qh, float *dh, int32_t *sh,
+                       float *h_out, void *stream) {
+  ZQ_REQUIRE(gu && qh && dh, ZQ_ENULL);
+  ZQ_REQUIRE(n >= 0 && k_ok(f) && n * (f / 32) <= (int64_t(1) << 31), ZQ_EINVAL);
+  ZQ_REQUIRE(al(gu, 16) && al(qh, 16) && al(dh, 4) && al(sh, 4) && al(h_out, 16), ZQ_EALIGN);
+  const int dc = check_current_device();
+  if (dc != ZQ_OK) return dc;
+  return zq::launch_swiglu_quantize(gu, n, f, qh, dh, sh, h_out, S(stream));
+}
+
+size_t zq_moe_ffn_workspace_bytes(int64_t d_model, int64_t d_ff, int32_t n_sel) {
+  if (d_model <= 0 || d_ff <= 0 || n_sel < 0) return 0;
+  return moe_layout(d_model, d_ff, n_sel).total;
+}
+
+int zq_moe_ffn(int wtype, const void *gu_bank, int64_t gu_stride_bytes, const void *down_bank,
+               int64_t down_stride_bytes, int64_t n_experts, int64_t d_model, int64_t d_ff,
+               const int32_t *ids, const float *wts, int32_t n_sel, const float *x,
+               void *workspace, size_t workspace_bytes, float *y, uint32_t flags,
+               int32_t *dev_status, void *stream) {
+  const int64_t bb = block_bytes(wtype);
+  ZQ_REQUIRE(bb > 0, ZQ_EINVAL);
+  ZQ_REQUIRE(gu_bank && down_bank && ids && wts && x && workspace && y, ZQ_ENULL);
+  ZQ_REQUIRE(n_experts >= 1 && n_experts <= INT32_MAX && k_ok(d_model) && k_ok(d_ff), ZQ_EINVAL);
+  ZQ_REQUIRE(n_sel >= 0 && n_sel <= 65535, ZQ_EINVAL);
+  ZQ_REQUIRE(gu_stride_bytes >= 2 * d_ff * (d_model / 32) * bb && gu_stride_bytes % 2 == 0,
+             ZQ_EINVAL);
+  ZQ_REQUIRE(down_stride_bytes >= d_model * (d_ff / 32) * bb && down_stride_bytes % 2 == 0,
+             ZQ_EINVAL);
+  ZQ_REQUIRE((flags & ~uint32_t(ZQ_ACCUMULATE)) == 0, ZQ_EINVAL);
+  const MoeWorkspace L = moe_layout(d_model, d_ff, n_sel);
+  ZQ_REQUIRE(workspace_bytes >= L.total, ZQ_EINVAL);
+  ZQ_REQUIRE(al(gu_bank, 4) && al(down_bank, 4) && al(ids, 4) && al(wts, 4) && al(x, 16) &&
+                 al(workspace, kAlign) && al(y, 4) && al(dev_status, 4),
+             ZQ_EALIGN);
+  const int dc = check_current_device();
+  if (dc != ZQ_OK) return dc;
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
+  int8_t *qx = reinterpret_cast<int8_t *>(ws + L.qx);
+  float *dx = reinterpret_cast<float *>(ws + L.dx);
+  int32_t *sx = reinterpret_cast<int32_t *>(ws + L.sx);
+  float *gu = reinterpret_cast<float *>(ws + L.gu);
+  int8_t *qh = reinterpret_cast<int8_t *>(ws + L.qh);
+  float *dh = reinterpret_cast<float *>(ws + L.dh);
+  int32_t *sh = reinterpret_cast<int32_t *>(ws + L.sh);
+  hipStream_t s = S(stream);
+  int rc;
+  if (n_sel > 0) {
+  rc = zq::launch_quantize_act(x, 1, d_model, d_model, qx, dx, sx, s);
+  if (rc != ZQ_OK) return rc;
+  zq::DmmvArgs a{};
+  a.w = static_cast<const uint8_t *>(gu_bank);
+  a.qx = qx;
+  a.dx = dx;
+  a.sx = wtype == ZQ_Q4_0 ? sx : nullptr;
+  a.y = gu;
+  a.ids = ids;
+  a.status = dev_status;
+  a.rows = 2 * d_ff;
+  a.expert_stride = gu_stride_bytes;
+  a.x_stride = 0;
+  a.nb = static_cast<int32_t>(d_model / 32);
+  a.n_experts = static_cast<int32_t>(n_experts);
+  a.n_sel = n_sel;
+  rc = zq::launch_dmmv(wtype, zq::MODE_GATHER, a, s);
+  if (rc != ZQ_OK) return rc;
+  rc = zq::launch_swiglu_quantize(gu, n_sel, d_ff, qh, dh, sh, nullptr, s);
+  if (rc != ZQ_OK) return rc;
+  }
+  // With no selected expert the weighted pass writes y = 0 (or leaves y as
+  // it is with ZQ_ACCUMULATE) and reads no activation.
+  zq::DmmvArgs b{};
+  b.w = static_cast<const uint8_t *>(down_bank);
+  b.qx = qh;
+  b.dx = dh;
+  b.sx = wtype == ZQ_Q4_0 ? sh : nullptr;
+  b.y = y;
+  b.ids = ids;
+  b.wts = wts;
+  b.status = dev_status;
+  b.rows = d_model;
+  b.expert_stride = down_stride_bytes;
+  b.x_stride = d_ff;
+  b.nb = static_cast<int32_t>(d_ff / 32);
+  b.n_experts = static_cast<int32_t>(n_experts);
+  b.n_sel = n_sel;
+  b.flags = flags;
+  return zq::launch_dmmv(wtype, zq::MODE_WEIGHTED, b, s);
+}
+
+int zq_gemm_prefill(int wtype, const void *w, int64_t n, int64_t k, const int8_t *qx,
+                    const float *dx, const int32_t *sx, int64_t m, float *y, uint32_t flags,
+                    void *stream) {
+  (void)sx;  // the kernel unpacks Q4_0 nibbles to signed values; no block sums needed
+  ZQ_REQUIRE(block_bytes(wtype) > 0, ZQ_EINVAL);
+  ZQ_REQUIRE(w && qx && dx && y, ZQ_ENULL);
+  ZQ_REQUIRE(n >= 0 && m >= 0 && k_ok(k), ZQ_EINVAL);
+  ZQ_REQUIRE(((n + 63) / 64) * ((m + 63) / 64) <= INT32_MAX, ZQ_EINVAL);
+  ZQ_REQUIRE((flags & ~uint32_t(ZQ_ACCUMULATE)) == 0, ZQ_EINVAL);
+  ZQ_REQUIRE(al(w, 4) && al(qx, 16) && al(dx, 4) && al(y, 4) && al(sx, 4), ZQ_EALIGN);
+  const int dc = check_current_device();
+  if (dc != ZQ_OK) return dc;
+  return zq::launch_gemm(wtype, w, n, k, qx, dx, m, y, flags, nullptr, 0, m, 0, n, S(stream));
+}
+
+int zq_gemm_isums(int wtype, const void *w, int64_t n, int64_t k, const int8_t *qx,
+                  const int32_t *sx, int64_t m, int64_t m0, int64_t m1, int64_t n0, int64_t n1,
+                  int32_t *isums, void *stream) {
+  (void)sx;
+  ZQ_REQUIRE(block_bytes(wtype) > 0, ZQ_EINVAL);
+  ZQ_REQUIRE(w && qx && isums, ZQ_ENULL);
+  ZQ_REQUIRE(n >= 0 && m >= 0 && k_ok(k), ZQ_EINVAL);
+  ZQ_REQUIRE(0 <= m0 && m0 <= m1 && m1 <= m && 0 <= n0 && n0 <= n1 && n1 <= n, ZQ_EINVAL);
+  ZQ_REQUIRE(al(w, 4) && al(qx, 16) && al(isums, 4) && al(sx, 4), ZQ_EALIGN);
+  const int dc = check_current_device();
+  if (dc != ZQ_OK) return dc;
+  // dx is not read by the isums variant's result; the scale loads use qx's
+  // bytes as a readable stand-in (k >= 32 bytes per token >= k/32 floats).
+  return zq::launch_gemm(wtype, w, n, k, qx, reinterpret_cast<const float *>(qx), m, nullptr, 0,
+                         isums, m0, m1, n0, n1, S(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,248 @@
+// zq_common.h -- device helpers shared by the libzq HIP kernels (gfx950 only).
+//
+// Wave64 throughout.  Nothing here is shared with the CPU oracle.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/zq.h"
+
+namespace zq {
+
+// ------------------------------------------------------------ block types --
+
+template <int WT> struct Blk;
+// Q4_0: fp16 d + 16 bytes of nibbles = 18 bytes.  A 4-byte-aligned window of
+// 5 dwords starting at (block address rounded down to 4) covers the block.
+template <> struct Blk<ZQ_Q4_0> { static constexpr int BYTES = 18; static constexpr int NW = 5; };
+// Q8_0: fp16 d + 32 int8 = 34 bytes; a 9-dword window covers it.
+template <> struct Blk<ZQ_Q8_0> { static constexpr int BYTES = 34; static constexpr int NW = 9; };
+
+typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Load the NW-dword window holding the block at byte address p (p is 2-byte
+// aligned; the window starts at p rounded down to 4).  Returns the byte
+// offset o in {0, 2} of the block inside the window.
+template <int WT>
+__device__ __forceinline__ uint32_t load_window(const uint8_t *p, uint32_t (&w)[Blk<WT>::NW]) {
+  const uintptr_t addr = reinterpret_cast<uintptr_t>(p);
+  const uint32_t o = static_cast<uint32_t>(addr & 3u);
+  const uint32_t *pw = reinterpret_cast<const uint32_t *>(addr - o);
+  const u32x4a4 v0 = *reinterpret_cast<const u32x4a4 *>(pw);
+  w[0] = v0.x; w[1] = v0.y; w[2] = v0.z; w[3] = v0.w;
+  if constexpr (WT == ZQ_Q4_0) {
+    w[4] = pw[4];
+  } else {
+    const u32x4a4 v1 = *reinterpret_cast<const u32x4a4 *>(pw + 4);
+    w[4] = v1.x; w[5] = v1.y; w[6] = v1.z; w[7] = v1.w;
+    w[8] = pw[8];
+  }
+  return o;
+}
+
+// fp16 bits (low 16 bits of h) -> fp32, exact for every finite value
+// including subnormals.
+__device__ __forceinline__ float f16_to_f32(uint32_t h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
+}
+
+// The block's fp16 scale, at byte o of the window.
+__device__ __forceinline__ float window_scale(uint32_t w0, uint32_t o) {
+  return f16_to_f32(__builtin_amdgcn_ubfe(w0, o * 8u, 16u));
+}
+
+// Byte selector that extracts window bytes [o+2, o+6) from the dword pair
+// (w[k+1]:w[k]) with v_perm_b32.
+__device__ __forceinline__ uint32_t quant_selector(uint32_t o) {
+  return 0x05040302u + o * 0x01010101u;
+}
+
+// sum_i nib_i * xq_i over one Q4_0 block (nibbles 0..15 taken as they are):
+// the caller subtracts 8 * sum(xq) to get sum (nib-8)*xq.  xq[0..3] hold
+// activation elements 0..15, xq[4..7] elements 16..31 (4 int8 per dword).
+__device__ __forceinline__ int32_t q4_raw_dot(const uint32_t (&w)[5], uint32_t sel,
+                                              const uint32_t (&xq)[8]) {
+  int32_t s = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t q = __builtin_amdgcn_perm(w[k + 1], w[k], sel);
+    const uint32_t lo = q & 0x0F0F0F0Fu;
+    const uint32_t hi = (q >> 4) & 0x0F0F0F0Fu;
+    s = __builtin_amdgcn_sdot4(static_cast<int>(lo), static_cast<int>(xq[k]), s, false);
+    s = __builtin_amdgcn_sdot4(static_cast<int>(hi), static_cast<int>(xq[4 + k]), s, false);
+  }
+  return s;
+}
+
+// sum_i q_i * xq_i over one Q8_0 block.
+__device__ __forceinline__ int32_t q8_dot(const uint32_t (&w)[9], uint32_t sel,
+                                          const uint32_t (&xq)[8]) {
+  int32_t s = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t q = __builtin_amdgcn_perm(w[k + 1], w[k], sel);
+    s = __builtin_amdgcn_sdot4(static_cast<int>(q), static_cast<int>(xq[k]), s, false);
+  }
+  return s;
+}
+
+// ----------------------------------------------------------- reductions ---
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+// DPP controls (gfx9 encoding).
+constexpr int DPP_QUAD_XOR1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+constexpr int DPP_ROW_MIRROR = 0x140;
+
+// Sum over each aligned group of G lanes (G in {1,2,4,8,16}); every lane of
+// the group receives the total.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (G >= 2) v += dpp<DPP_QUAD_XOR1>(v);
+  if constexpr (G >= 4) v += dpp<DPP_QUAD_XOR2>(v);
+  if constexpr (G >= 8) v += dpp<DPP_ROW_HALF_MIRROR>(v);
+  if constexpr (G >= 16) v += dpp<DPP_ROW_MIRROR>(v);
+  return v;
+}
+
+// v_permlane32_swap / v_permlane16_swap: exchange the odd 32-lane (16-lane)
+// rows of a with the even rows of b.
+__device__ __forceinline__ void swap32(float &a, float &b) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, a),
+                                            __builtin_bit_cast(uint32_t, b), false, false);
+  a = __builtin_bit_cast(float, static_cast<uint32_t>(r[0]));
+  b = __builtin_bit_cast(float, static_cast<uint32_t>(r[1]));
+}
+__device__ __forceinline__ void swap16(float &a, float &b) {
+  auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, a),
+                                            __builtin_bit_cast(uint32_t, b), false, false);
+  a = __builtin_bit_cast(float, static_cast<uint32_t>(r[0]));
+  b = __builtin_bit_cast(float, static_cast<uint32_t>(r[1]));
+}
+
+// Row reduction of a wave holding RB partial sums per lane, where each row
+// slot is LPR consecutive lanes (LPR in {8,16,32,64}).  Halving steps with
+// the permlane swaps fold pairs of partials while summing across 32- and
+// 16-lane halves; the rest is a DPP sum inside 16 (or 8) lanes.
+// On return, out[m] (m < RB >> halvings()) holds in every lane of its
+// sub-group the full sum of row-step rowstep(m, lane).
+template <int LPR, int RB>
+struct RowReduce {
+  static constexpr bool H32 = (LPR == 64) && (RB >= 2);
+  static constexpr bool H16 = (LPR >= 32) && ((H32 ? RB / 2 : RB) >= 2);
+  static constexpr int NH = (H32 ? 1 : 0) + (H16 ? 1 : 0);
+  static constexpr int NOUT = RB >> NH;
+  static constexpr int G = LPR < 16 ? LPR : 16;
+
+  __device__ __forceinline__ static void run(float (&v)[RB], float (&out)[NOUT]) {
+    constexpr int N1 = H32 ? RB / 2 : RB;
+    float u[N1];
+    if constexpr (H32) {
+#pragma unroll
+      for (int m = 0; m < N1; ++m) {
+        float a = v[2 * m], b = v[2 * m + 1];
+        swap32(a, b);
+        u[m] = a + b;
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < N1; ++m) u[m] = v[m];
+    }
+    if constexpr (H16) {
+#pragma unroll
+      for (int m = 0; m < NOUT; ++m) {
+        float a = u[2 * m], b = u[2 * m + 1];
+        swap16(a, b);
+        out[m] = a + b;
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < NOUT; ++m) out[m] = u[m];
+    }
+#pragma unroll
+    for (int m = 0; m < NOUT; ++m) {
+      float t = group_sum<G>(out[m]);
+      if constexpr (LPR >= 32 && !H16) {
+        float a = t, b = t;
+        swap16(a, b);
+        t = a + b;
+      }
+      if constexpr (LPR == 64 && !H32) {
+        float a = t, b = t;
+        swap32(a, b);
+        t = a + b;
+      }
+      out[m] = t;
+    }
+  }
+  // Row step of output m held by `lane`.
+  __device__ __forceinline__ static int rowstep(int m, int lane) {
+    const int A = (lane >> 5) & 1;
+    const int B = (lane >> 4) & 1;
+    int t = m << NH;
+    if constexpr (H16) t |= B << (H32 ? 1 : 0);
+    if constexpr (H32) t |= A;
+    return t;
+  }
+  // Exactly one lane per (output, row slot) writes it: the outputs repeat
+  // with a period of LPR >> NH lanes inside a slot.
+  __device__ __forceinline__ static bool writer(int lane) {
+    return (lane & ((LPR >> NH) - 1)) == 0;
+  }
+};
+
+// --------------------------------------------------------- quantization ---
+
+// Round half away from zero, for |v| < 2^23.
+__device__ __forceinline__ float round_half_away(float v) {
+  const float t = __builtin_truncf(v);
+  const float f = v - t;  // exact
+  return (__builtin_fabsf(f) >= 0.5f) ? t + __builtin_copysignf(1.0f, v) : t;
+}
+
+// Quantize one 32-element block held by 8 consecutive lanes (4 elements per
+// lane, lane g of the group holding elements 4g..4g+3).  Returns the 4 codes
+// packed little-endian; d and s are the block scale and code sum (valid in
+// every lane of the group).
+__device__ __forceinline__ uint32_t quantize_block8(const float (&x)[4], float &d_out,
+                                                   int32_t &s_out) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[i]));
+  amax = __builtin_fmaxf(amax, dpp<DPP_QUAD_XOR1>(amax));
+  amax = __builtin_fmaxf(amax, dpp<DPP_QUAD_XOR2>(amax));
+  amax = __builtin_fmaxf(amax, dpp<DPP_ROW_HALF_MIRROR>(amax));
+  const float d = amax / 127.0f;              // IEEE division (no fast-math)
+  const float id = (d != 0.0f) ? 1.0f / d : 0.0f;
+  uint32_t packed = 0;
+  int32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int q = static_cast<int>(round_half_away(x[i] * id));
+    q = q > 127 ? 127 : (q < -127 ? -127 : q);
+    s += q;
+    packed |= (static_cast<uint32_t>(q) & 0xFFu) << (8 * i);
+  }
+  float sf = static_cast<float>(s);  // |s| <= 508: exact in fp32
+  sf += dpp<DPP_QUAD_XOR1>(sf);
+  sf += dpp<DPP_QUAD_XOR2>(sf);
+  sf += dpp<DPP_ROW_HALF_MIRROR>(sf);
+  d_out = d;
+  s_out = static_cast<int32_t>(sf);
+  return packed;
+}
+
+}  // namespace zq
+
+// Host-side launch helpers.
+#define ZQ_LAUNCH_CHECK()                                   \
+  do {                                                      \
+    if (hipGetLastError() != hipSuccess) return ZQ_ELAUNCH; \
+  } while (0)

@@ -1,0 +1,48 @@
+// zq_internal.h -- host-side launchers shared between the libzq translation
+// units (argument checking lives in zq_api.hip; these assume valid input).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace zq {
+
+enum DmmvMode { MODE_PLAIN = 0, MODE_ISUMS = 1, MODE_GATHER = 2, MODE_WEIGHTED = 3 };
+
+// Everything one DMMV-family launch needs, passed by value.
+struct DmmvArgs {
+  const uint8_t *w;     // matrix, or bank of matrices (MoE)
+  const int8_t *qx;     // activation codes (slot s at qx + s * x_stride)
+  const float *dx;      // activation scales (slot s at dx + s * x_stride / 32)
+  const int32_t *sx;    // activation block sums, may be null (Q4_0 then sums qx)
+  float *y;             // output rows
+  int32_t *isums;       // MODE_ISUMS output [rows][nb]
+  const int32_t *ids;   // MoE: selected expert ids [n_sel]
+  const float *wts;     // MoE weighted sum: weights [n_sel]
+  int32_t *status;      // MoE: receives ZQ_ERANGE on a bad id (may be null)
+  int64_t rows;
+  int64_t row_bytes;
+  int64_t expert_stride;
+  int64_t x_stride;
+  int64_t n_groups;     // row groups per slot
+  int32_t nb;           // blocks per row
+  int32_t n_experts;
+  int32_t n_sel;
+  uint32_t flags;
+};
+
+int launch_quantize_act(const float *x, int64_t n_tok, int64_t k, int64_t x_stride, int8_t *qx,
+                        float *dx, int32_t *sx, hipStream_t stream);
+int launch_swiglu_quantize(const float *gu, int64_t n, int64_t f, int8_t *qh, float *dh,
+                           int32_t *sh, float *h_out, hipStream_t stream);
+// mode: DmmvMode; a.n_groups and a.row_bytes are filled in by the launcher.
+int launch_dmmv(int wtype, int mode, DmmvArgs a, hipStream_t stream);
+int launch_argmax(const float *y, int64_t n, int32_t *out_idx, void *ws, hipStream_t stream);
+size_t argmax_workspace(int64_t n);
+int launch_moe_route(const float *logits, int32_t n_routed, int32_t top_k, const float *shared_gate,
+                     int32_t *ids, float *wts, hipStream_t stream);
+int launch_gemm(int wtype, const void *w, int64_t n, int64_t k, const int8_t *qx, const float *dx,
+                int64_t m, float *y, uint32_t flags, int32_t *isums, int64_t m0, int64_t m1,
+                int64_t n0, int64_t n1, hipStream_t stream);
+
+}  // namespace zq

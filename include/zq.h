@@ -1,0 +1,179 @@
+/*
+ * zq.h -- C ABI of libzq, block-quantized decode-path kernels for AMD MI355X
+ * (gfx950).
+ *
+ * The path: GGML-style Q8_0 / Q4_0 weight blocks, an activation quantized to
+ * int8 blocks of 32 with one fp32 scale each, and per-block int8 x int8 ->
+ * int32 dot products scaled by d_w * d_x and summed into fp32 rows.
+ *
+ *   Q8_0 block (34 bytes): fp16 d (little-endian) then int8 q[32]; value q*d.
+ *   Q4_0 block (18 bytes): fp16 d then uint8 qs[16]; element j (j < 16) is the
+ *       low nibble of qs[j], element j+16 the high nibble; value (nib-8)*d.
+ *   Both are the GGML layouts, which the pages state are identical bit for bit
+ *   across ZINC's backends ("Bringing ZINC to NVIDIA: a CUDA backend ...",
+ *   section "The reassuring result: ZINC's matmuls are __dp4a, not tensor
+ *   cores"; "CUDA backend for ZINC", section 4 "Kernel port strategy").
+ *   A weight matrix of `rows` x `k` is rows*(k/32) blocks, row-major, no
+ *   padding; its row b-th block starts at byte (r*(k/32)+b)*block_bytes.
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer is a DEVICE pointer owned by the caller; the library never
+ *     allocates, frees or retains memory.  `stream` is a hipStream_t passed as
+ *     void* (NULL = the default stream).  Calls are asynchronous on `stream`;
+ *     the caller keeps every buffer alive until that work completes.
+ *   - Arguments are checked before anything is launched.  On any error the
+ *     call returns a negative zq_status and writes nothing.  0 = launched.
+ *   - Alignment: weights 4-byte aligned; qx 16-byte aligned; x 16-byte aligned
+ *     with a row stride that is a multiple of 4 elements; every other array
+ *     4-byte aligned.  A Q4_0/Q8_0 kernel may read the two bytes that follow
+ *     the last block of a weight buffer when they share that block's aligned
+ *     4-byte word (never beyond it).
+ *   - k must be a positive multiple of 32; sizes are element counts.
+ *   - Only gfx950 devices are accepted (ZQ_EDEVICE otherwise).
+ *   - The library keeps no mutable global state apart from a per-device
+ *     capability cache filled once; calls are thread-safe.
+ */
+#ifndef ZQ_H
+#define ZQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum zq_status {
+    ZQ_OK = 0,
+    ZQ_EINVAL = -1,  /* bad size, k % 32 != 0, unknown flag/type/mode, ranges    */
+    ZQ_ENULL = -2,   /* a required pointer is NULL                              */
+    ZQ_EALIGN = -3,  /* a pointer or stride violates the alignment rules above  */
+    ZQ_ERANGE = -4,  /* an expert id outside [0, n_experts), found on the GPU   */
+    ZQ_EDEVICE = -5, /* current device is not gfx950 / no device                */
+    ZQ_ELAUNCH = -6  /* the HIP runtime refused the launch                      */
+};
+
+enum zq_flags { ZQ_ACCUMULATE = 1 /* y += W.x instead of y = W.x */ };
+enum zq_wtype { ZQ_Q4_0 = 4, ZQ_Q8_0 = 8 };
+enum zq_moe_mode { ZQ_MOE_GATHER = 0, ZQ_MOE_WEIGHTED_SUM = 1 };
+
+int zq_version(void);
+const char *zq_strerror(int status);
+/* ZQ_OK when `device` is a gfx950 GPU, else ZQ_EDEVICE. */
+int zq_device_check(int device);
+
+/* Activation block quantization (the "quantize" shader family named in
+ * "Bringing ZINC to NVIDIA", section "Porting the kernels"; formula: the
+ * reading documented with the library).  For each token t and block b:
+ *   amax = max|x|, d = amax/127 (IEEE fp32 division), id = d ? 1/d : 0,
+ *   q = round_half_away_from_zero(x*id) clamped to [-127,127], s = sum q.
+ * x:  [n_tok][x_stride] fp32 (first k used);  qx: [n_tok][k] int8;
+ * dx: [n_tok][k/32] fp32;  sx: [n_tok][k/32] int32, may be NULL.
+ * x must be finite (not checked). */
+int zq_quantize_act(const float *x, int64_t n_tok, int64_t k, int64_t x_stride,
+                    int8_t *qx, float *dx, int32_t *sx, void *stream);
+
+/* Dequantizing matrix-vector product (habr "Как мы запустили 35B LLM ...",
+ * section "Что такое DMMV": read the quantized weights, dequantize in
+ * registers, multiply by the input vector, write the row):
+ *   y[r] (+)= sum_b fp32(d_w[r][b]) * dx[b] * isum[r][b],
+ *   isum[r][b] = sum_i w[r][b][i] * qx[32b+i]   (exact int32).
+ * w: rows*(k/32) blocks; qx [k]; dx [k/32]; y [rows] fp32.
+ * flags: 0 or ZQ_ACCUMULATE. */
+int zq_dmmv_q8_0(const void *w, int64_t rows, int64_t k, const int8_t *qx, const float *dx,
+                 float *y, uint32_t flags, void *stream);
+/* As zq_dmmv_q8_0 for Q4_0 weights.  sx [k/32] (block sums of qx) may be NULL,
+ * in which case the kernel sums qx itself. */
+int zq_dmmv_q4_0(const void *w, int64_t rows, int64_t k, const int8_t *qx, const float *dx,
+                 const int32_t *sx, float *y, uint32_t flags, void *stream);
+
+/* Test hook: the per-block integer sums of the same DMMV inner loop,
+ * isums[r][b] for every row r and block b (int32 [rows][k/32]). */
+int zq_dmmv_isums(int wtype, const void *w, int64_t rows, int64_t k, const int8_t *qx,
+                  const int32_t *sx, int32_t *isums, void *stream);
+
+/* Index of the largest logit, ties to the lowest index ("argmax (exact)",
+ * "CUDA backend for ZINC", section 5, M1 kernel library).  y [n] fp32 finite;
+ * out_idx: one int32.  workspace: device scratch of at least
+ * zq_argmax_workspace_bytes(n) bytes, 8-byte aligned. */
+size_t zq_argmax_workspace_bytes(int64_t n);
+int zq_argmax_f32(const float *y, int64_t n, int32_t *out_idx, void *workspace,
+                  size_t workspace_bytes, void *stream);
+
+/* MoE router ("softmax_topk", "Bringing ZINC to NVIDIA", section "The roadmap:
+ * from 70 to a coherent token"; "CUDA backend for ZINC", section 5): the
+ * top_k largest of n_routed logits, largest first, ties to the lower id;
+ * wts = softmax over the selected logits.  If shared_gate (one device fp32)
+ * is non-NULL, a shared expert with id n_routed and weight sigmoid(g) is
+ * appended ("one sigmoid-gated shared expert", same page, section "The target
+ * model").  ids/wts: top_k (+1) entries.  1 <= top_k <= 64,
+ * top_k <= n_routed <= 1024. */
+int zq_moe_route(const float *logits, int32_t n_routed, int32_t top_k,
+                 const float *shared_gate, int32_t *ids, float *wts, void *stream);
+
+/* Expert-indexed DMMV over a list of selected experts (dmmv_*_moe and
+ * moe_weighted_acc, "CUDA backend for ZINC", section 5; the selected experts
+ * come from a GPU-resident work list, "RTX 5090: Batched Prefill & CUDA
+ * Graphs in ZINC", section "Prefill -- a correction, and a better GEMM").
+ * bank: n_experts matrices of rows x k, expert e at bank + e*expert_stride_bytes
+ * (stride even).  ids [n_sel] int32, wts [n_sel] fp32 (device).  Activation
+ * of slot s: qx + s*x_stride, dx/sx + s*(x_stride/32) (x_stride = 0 broadcasts
+ * one activation; otherwise a multiple of 32).
+ *   ZQ_MOE_GATHER:       y[s][r]   = (W[ids[s]] . x_s)[r]        y [n_sel][rows]
+ *                        (wts unused, may be NULL; flags must be 0)
+ *   ZQ_MOE_WEIGHTED_SUM: y[r]    (+)= sum_s wts[s]*(W[ids[s]] . x_s)[r]   y [rows]
+ * An id outside [0, n_experts) is skipped (contributes nothing; in GATHER its
+ * output row block is left untouched) and, if dev_status is non-NULL,
+ * ZQ_ERANGE is stored to *dev_status (which is otherwise not written). */
+int zq_dmmv_moe(int wtype, const void *bank, int64_t n_experts, int64_t expert_stride_bytes,
+                int64_t rows, int64_t k, const int32_t *ids, const float *wts, int32_t n_sel,
+                const int8_t *qx, const float *dx, const int32_t *sx, int64_t x_stride,
+                int mode, float *y, uint32_t flags, int32_t *dev_status, void *stream);
+
+/* SwiGLU then activation quantization ("swiglu", "CUDA backend for ZINC",
+ * section 5): gu [n][2f] (gate in [.][0:f], up in [.][f:2f]);
+ * h = silu(g)*u with silu(z) = z/(1+exp(-z)), evaluated in fp64 and rounded
+ * once to fp32, then quantized exactly as zq_quantize_act:
+ * qh [n][f] int8, dh [n][f/32] fp32, sh [n][f/32] int32 (may be NULL);
+ * h_out [n][f] fp32 receives h when non-NULL.  f % 32 == 0. */
+int zq_swiglu_quantize(const float *gu, int64_t n, int64_t f, int8_t *qh, float *dh,
+                       int32_t *sh, float *h_out, void *stream);
+
+/* One token through the selected experts: quantize x, gate||up DMMV of every
+ * selected expert (one launch), swiglu + re-quantize, down DMMV with the
+ * weighted sum fused (one launch).  gu_bank: experts of [2*d_ff][d_model]
+ * (rows 0..d_ff-1 gate, d_ff..2*d_ff-1 up); down_bank: [d_model][d_ff].
+ * workspace: at least zq_moe_ffn_workspace_bytes(d_model, d_ff, n_sel) bytes,
+ * 256-byte aligned.  y [d_model] (+)= sum_s wts[s] * down_s.
+ * flags: 0 or ZQ_ACCUMULATE. */
+size_t zq_moe_ffn_workspace_bytes(int64_t d_model, int64_t d_ff, int32_t n_sel);
+int zq_moe_ffn(int wtype, const void *gu_bank, int64_t gu_stride_bytes, const void *down_bank,
+               int64_t down_stride_bytes, int64_t n_experts, int64_t d_model, int64_t d_ff,
+               const int32_t *ids, const float *wts, int32_t n_sel, const float *x,
+               void *workspace, size_t workspace_bytes, float *y, uint32_t flags,
+               int32_t *dev_status, void *stream);
+
+/* Batched prefill GEMM ("one register-tiled GEMM over all prompt tokens at
+ * once", "RTX 5090: Batched Prefill & CUDA Graphs in ZINC", opening answer
+ * and section "Prefill -- a correction, and a better GEMM"; the dequant is
+ * fused into the GEMM as the same page's closing paragraph recommends):
+ *   Y[m][n] (+)= sum_b dx[m][b] * d_w[n][b] * isum(m, n, b),
+ * with each block's integer sum taken on int8 matrix cores.
+ * w: n x k weight matrix; qx [m][k] int8; dx [m][k/32]; sx [m][k/32] (may be
+ * NULL); y [m][n] fp32 row-major.  flags: 0 or ZQ_ACCUMULATE. */
+int zq_gemm_prefill(int wtype, const void *w, int64_t n, int64_t k, const int8_t *qx,
+                    const float *dx, const int32_t *sx, int64_t m, float *y, uint32_t flags,
+                    void *stream);
+
+/* Test hook: the per-block integer sums of the same GEMM tile loop for
+ * tokens [m0, m1) and weight rows [n0, n1): isums[(mm-m0)][(nn-n0)][b],
+ * int32 [(m1-m0)][(n1-n0)][k/32]. */
+int zq_gemm_isums(int wtype, const void *w, int64_t n, int64_t k, const int8_t *qx,
+                  const int32_t *sx, int64_t m, int64_t m0, int64_t m1, int64_t n0, int64_t n1,
+                  int32_t *isums, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZQ_H */

@@ -1,0 +1,141 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol
+include/zq.h declares, the binding mirrors the header, and argument errors
+come back as the documented codes before anything touches a device.
+
+Pointers here are fake non-zero addresses: every check below fails (or, for
+valid arguments, reaches the device check) before any launch, so nothing is
+ever dereferenced.
+"""
+import os
+import re
+import subprocess
+
+import pytest
+
+from block_quant_matrix_amd import zq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "zq.h")
+
+A = 0x10000   # 64 KiB-aligned fake device addresses
+B = 0x20000
+C = 0x30000
+D = 0x40000
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(zq_\w+)\s*\(", src)))
+
+
+def test_header_symbols_exported():
+    names = header_functions()
+    assert len(names) >= 15
+    L = zq.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", zq.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (zq_\w+)", out))
+    assert set(names) <= exported
+    # nothing exported beyond the header's zq_ functions
+    assert exported <= set(names)
+
+
+def test_binding_mirrors_header():
+    assert set(zq.SIGNATURES) == set(header_functions())
+    for n in zq.SIGNATURES:
+        if n.startswith("zq_") and n not in ("zq_strerror",):
+            assert callable(getattr(zq, n)), n
+
+
+def test_version_and_strerror():
+    L = zq.lib()
+    assert L.zq_version() == 1
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert zq.strerror(code)
+    assert "unknown" in zq.strerror(-99)
+
+
+def test_workspace_sizes():
+    L = zq.lib()
+    assert L.zq_argmax_workspace_bytes(1) >= 8
+    assert L.zq_argmax_workspace_bytes(248320) >= 8 * 243
+    ws = L.zq_moe_ffn_workspace_bytes(2048, 512, 9)
+    assert ws >= 2048 + 9 * 1024 * 4 + 9 * 512 and ws % 256 == 0
+    assert L.zq_moe_ffn_workspace_bytes(0, 512, 9) == 0
+
+
+def rc_dmmv_q4(**kw):
+    a = dict(w=A, rows=4, k=64, qx=B, dx=C, sx=None, y=D, flags=0)
+    a.update(kw)
+    return zq.lib().zq_dmmv_q4_0(a["w"], a["rows"], a["k"], a["qx"], a["dx"], a["sx"], a["y"],
+                                 a["flags"], None)
+
+
+def test_dmmv_argument_errors():
+    assert rc_dmmv_q4(k=33) == zq.ZQ_EINVAL
+    assert rc_dmmv_q4(k=0) == zq.ZQ_EINVAL
+    assert rc_dmmv_q4(rows=-1) == zq.ZQ_EINVAL
+    assert rc_dmmv_q4(flags=2) == zq.ZQ_EINVAL
+    assert rc_dmmv_q4(w=None) == zq.ZQ_ENULL
+    assert rc_dmmv_q4(qx=None) == zq.ZQ_ENULL
+    assert rc_dmmv_q4(y=None) == zq.ZQ_ENULL
+    assert rc_dmmv_q4(w=A + 2) == zq.ZQ_EALIGN
+    assert rc_dmmv_q4(qx=B + 8) == zq.ZQ_EALIGN
+    assert rc_dmmv_q4(y=D + 1) == zq.ZQ_EALIGN
+    assert rc_dmmv_q4(sx=C + 2) == zq.ZQ_EALIGN
+    L = zq.lib()
+    assert L.zq_dmmv_q8_0(A, 4, 48, B, C, D, 0, None) == zq.ZQ_EINVAL
+    assert L.zq_dmmv_isums(5, A, 4, 64, B, None, D, None) == zq.ZQ_EINVAL
+    assert L.zq_dmmv_isums(4, A, 4, 64, B, None, None, None) == zq.ZQ_ENULL
+
+
+def test_other_argument_errors():
+    L = zq.lib()
+    # quantize: stride < k, misaligned x, stride not a multiple of 4
+    assert L.zq_quantize_act(A, 1, 64, 32, B, C, None, None) == zq.ZQ_EINVAL
+    assert L.zq_quantize_act(A + 4, 1, 64, 64, B, C, None, None) == zq.ZQ_EALIGN
+    assert L.zq_quantize_act(A, 2, 64, 66, B, C, None, None) == zq.ZQ_EALIGN
+    assert L.zq_quantize_act(None, 1, 64, 64, B, C, None, None) == zq.ZQ_ENULL
+    # argmax: n = 0, workspace too small
+    assert L.zq_argmax_f32(A, 0, B, C, 4096, None) == zq.ZQ_EINVAL
+    assert L.zq_argmax_f32(A, 248320, B, C, 8, None) == zq.ZQ_EINVAL
+    # router: top_k > n_routed, top_k > 64
+    assert L.zq_moe_route(A, 4, 8, None, B, C, None) == zq.ZQ_EINVAL
+    assert L.zq_moe_route(A, 128, 65, None, B, C, None) == zq.ZQ_EINVAL
+    # moe: bad mode, gather with flags, weighted without weights, short stride
+    args = dict(wtype=4, bank=A, n_experts=129, stride=1024 * 64 * 18, rows=1024, k=2048, ids=B,
+                wts=C, n_sel=9, qx=D, dx=D + 4096, sx=None, x_stride=0, mode=0, y=D + 8192,
+                flags=0, status=None)
+
+    def moe(**kw):
+        a = dict(args)
+        a.update(kw)
+        return L.zq_dmmv_moe(a["wtype"], a["bank"], a["n_experts"], a["stride"], a["rows"], a["k"],
+                             a["ids"], a["wts"], a["n_sel"], a["qx"], a["dx"], a["sx"],
+                             a["x_stride"], a["mode"], a["y"], a["flags"], a["status"], None)
+
+    assert moe(mode=2) == zq.ZQ_EINVAL
+    assert moe(flags=1) == zq.ZQ_EINVAL
+    assert moe(mode=1, wts=None) == zq.ZQ_ENULL
+    assert moe(stride=100) == zq.ZQ_EINVAL
+    assert moe(x_stride=48) == zq.ZQ_EINVAL
+    assert moe(n_sel=-1) == zq.ZQ_EINVAL
+    # swiglu: f not a multiple of 32
+    assert L.zq_swiglu_quantize(A, 9, 48, B, C, None, None, None) == zq.ZQ_EINVAL
+    # moe_ffn: workspace too small
+    assert L.zq_moe_ffn(4, A, 1024 * 64 * 18, B, 2048 * 16 * 18, 129, 2048, 512, C, C + 64, 9, D,
+                        D + 65536, 16, D + 1 << 20, 0, None, None) == zq.ZQ_EINVAL
+    # gemm: bad ranges
+    assert L.zq_gemm_isums(4, A, 64, 64, B, None, 8, 4, 2, 0, 64, C, None) == zq.ZQ_EINVAL
+    assert L.zq_gemm_isums(4, A, 64, 64, B, None, 8, 0, 8, 0, 65, C, None) == zq.ZQ_EINVAL
+    assert L.zq_gemm_prefill(3, A, 64, 64, B, C, None, 8, D, 0, None) == zq.ZQ_EINVAL
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="a GPU is present")
+def test_valid_arguments_without_gpu_report_no_device():
+    """With every argument valid, the last check is the device: no GPU here."""
+    assert rc_dmmv_q4() == zq.ZQ_EDEVICE
+    assert zq.lib().zq_device_check(0) == zq.ZQ_EDEVICE

@@ -1,0 +1,286 @@
+"""GPU parity of the activation quantizer, the Q4_0/Q8_0 DMMV and argmax
+against the CPU oracle, through the C ABI.
+
+Bar: bit-exact qx / dx / sx and per-block int32 sums; fp32 rows within 1e-4 of
+the fp64 reference (normwise against S, elementwise on well-conditioned rows);
+argmax exact on the GPU's own logits.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from block_quant_matrix_amd import inputs
+from gpuhelp import check_rows, dev, host, nan_f32, quantize_gpu, sentinel_i32, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+Q4, Q8 = 4, 8
+
+
+@pytest.fixture(scope="module")
+def zq():
+    torch_cuda()
+    from block_quant_matrix_amd import zq as _zq
+    assert _zq.zq_device_check(0) == 0, "not a gfx950 device"
+    return _zq
+
+
+# --------------------------------------------------------------- quantize --
+
+def special_activation(k, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal(k).astype(np.float32)
+    nb = k // 32
+    if nb >= 1:
+        x[0:32] = 0.0                                    # zero block -> d = 0
+    if nb >= 2:                                          # half-way cases
+        u = 2.0 ** -5
+        blk = np.zeros(32)
+        blk[0] = 127 * u
+        blk[1:7] = np.array([2.5, -2.5, 0.5, -0.5, 1.5, -1.5]) * u
+        x[32:64] = blk
+    if nb >= 3:
+        x[64:96] = np.float32(3.3)                       # constant block
+    if nb >= 4:
+        x[96:128] *= np.float32(1e-30)                   # tiny magnitudes
+    if nb >= 5:
+        x[128:160] *= np.float32(1e30)                   # huge magnitudes
+    return x
+
+
+@pytest.mark.parametrize("t,k", [(1, 32), (1, 2048), (1, 4096), (3, 96), (7, 5120), (512, 5120),
+                                 (1, 512)])
+def test_quantize_bitexact(zq, t, k):
+    x = inputs.gen_activation(t, k, 7000 + t + k).reshape(t, k)
+    x[0] = special_activation(k, 1)
+    qx, dx, sx = quantize_gpu(zq, x)
+    rq, rd, rs = oracle.quantize_act(x)
+    assert np.array_equal(host(qx), rq)
+    assert np.array_equal(host(dx).view(np.uint32), rd.view(np.uint32))
+    assert np.array_equal(host(sx), rs)
+
+
+def test_quantize_strided_rows_and_null_sums(zq):
+    torch = torch_cuda()
+    t, k, stride = 5, 256, 260
+    x = np.random.default_rng(3).standard_normal((t, stride)).astype(np.float32)
+    qx = torch.zeros((t, k), dtype=torch.int8, device="cuda")
+    dx = nan_f32(t, k // 32)
+    zq.zq_quantize_act(dev(x), t, k, stride, qx, dx, None)
+    rq, rd, _ = oracle.quantize_act(x[:, :k])
+    assert np.array_equal(host(qx), rq)
+    assert np.array_equal(host(dx), rd)
+
+
+# ------------------------------------------------------------------ dmmv ---
+
+SHAPES = [(1, 32), (7, 64), (64, 2048), (130, 96), (33, 512), (257, 4096), (70, 5120),
+          (19, 32 * 200), (5, 32 * 9), (1000, 32 * 3)]
+
+
+def run_dmmv(zq, wtype, w_np, rows, k, qx, dx, sx, y=None, flags=0):
+    y = nan_f32(rows) if y is None else y
+    wd = dev(w_np)
+    if wtype == Q4:
+        zq.zq_dmmv_q4_0(wd, rows, k, qx, dx, sx, y, flags)
+    else:
+        zq.zq_dmmv_q8_0(wd, rows, k, qx, dx, y, flags)
+    return y
+
+
+@pytest.mark.parametrize("wtype", [Q4, Q8])
+@pytest.mark.parametrize("rows,k", SHAPES)
+def test_dmmv_isums_and_rows(zq, wtype, rows, k):
+    seed = 100 * rows + k + wtype
+    w = inputs.gen_weights(wtype, rows, k, seed)
+    x = inputs.gen_activation(1, k, seed + 1)
+    qx, dx, sx = quantize_gpu(zq, x)
+    rq, rd, rs = oracle.quantize_act(x)
+    assert np.array_equal(host(qx)[0], rq)
+    y_ref, S, isums_ref = oracle.dmmv(wtype, w, rows, k, rq, rd, want_isums=True)
+    isums = sentinel_i32(rows, k // 32)
+    zq.zq_dmmv_isums(wtype, dev(w), rows, k, qx, sx, isums)
+    assert np.array_equal(host(isums), isums_ref)
+    y = run_dmmv(zq, wtype, w, rows, k, qx, dx, sx)
+    check_rows(host(y), y_ref, S, "dmmv wtype=%d %dx%d" % (wtype, rows, k))
+    if wtype == Q4:  # the kernel's own block sums when sx is not given
+        isums2 = sentinel_i32(rows, k // 32)
+        zq.zq_dmmv_isums(wtype, dev(w), rows, k, qx, None, isums2)
+        assert np.array_equal(host(isums2), isums_ref)
+        y2 = run_dmmv(zq, wtype, w, rows, k, qx, dx, None)
+        assert np.array_equal(host(y2), host(y))
+
+
+@pytest.mark.parametrize("wtype", [Q4, Q8])
+def test_dmmv_accumulate(zq, wtype):
+    rows, k = 300, 2048
+    w = inputs.gen_weights(wtype, rows, k, 31)
+    x = inputs.gen_activation(1, k, 32)
+    qx, dx, sx = quantize_gpu(zq, x)
+    rq, rd, _ = oracle.quantize_act(x)
+    prev = np.random.default_rng(33).standard_normal(rows).astype(np.float32)
+    y = dev(prev.copy())
+    run_dmmv(zq, wtype, w, rows, k, qx, dx, sx, y=y, flags=1)
+    y_ref, S = oracle.dmmv(wtype, w, rows, k, rq, rd, y_prev=prev)
+    check_rows(host(y), y_ref, S, "accumulate")
+
+
+@pytest.mark.parametrize("wtype", [Q4, Q8])
+def test_dmmv_all_ones_exact(zq, wtype):
+    """Every row must come back as exactly 2032.0 (= K * 127/128)."""
+    rows, k = 200, 2048
+    if wtype == Q8:
+        blk = np.frombuffer(np.array([1.0], "<f2").tobytes() + bytes([1] * 32), np.uint8)
+    else:
+        blk = np.frombuffer(np.array([1.0], "<f2").tobytes() + bytes([0x99] * 16), np.uint8)
+    w = np.tile(blk, rows * (k // 32))
+    x = np.full(k, 127 / 128, np.float32)
+    qx, dx, sx = quantize_gpu(zq, x)
+    y = run_dmmv(zq, wtype, w, rows, k, qx, dx, sx)
+    assert (host(y) == 2032.0).all()
+
+
+@pytest.mark.parametrize("wtype", [Q4, Q8])
+def test_dmmv_single_nonzero_block(zq, wtype):
+    """All scales zero except (r*, b*) = 2^-3 with a lossless activation:
+    exactly one non-zero row with the exact value 2^-3 * 2^-6 * isum."""
+    rows, k = 130, 32 * 66
+    nb = k // 32
+    bb = inputs.BLOCK_BYTES[wtype]
+    rng = np.random.default_rng(5)
+    kint = rng.integers(-127, 128, size=k)
+    kint[::32] = 127
+    x = (kint * 2.0 ** -6).astype(np.float32)
+    qx, dx, sx = quantize_gpu(zq, x)
+    base = inputs.gen_weights(wtype, rows, k, 77).reshape(rows * nb, bb)
+    base[:, 0:2] = 0
+    for rstar, bstar in [(0, 0), (rows - 1, nb - 1), (63, 31), (64, 32), (65, 64), (128, 65)]:
+        w = base.copy()
+        w[rstar * nb + bstar, 0:2] = np.frombuffer(np.array([0.125], "<f2").tobytes(), np.uint8)
+        y = host(run_dmmv(zq, wtype, w.reshape(-1), rows, k, qx, dx, sx))
+        blk = w[rstar * nb + bstar]
+        vals = (blk[2:].view(np.int8).astype(np.int64) if wtype == Q8 else
+                np.concatenate([blk[2:] & 15, blk[2:] >> 4]).astype(np.int64) - 8)
+        want = np.zeros(rows)
+        want[rstar] = 0.125 * 2.0 ** -6 * int(np.dot(vals, kint[bstar * 32:(bstar + 1) * 32]))
+        assert np.array_equal(y.astype(np.float64), want), (rstar, bstar)
+
+
+def test_dmmv_every_fp16_scale(zq):
+    """Scales run through every finite fp16 bit pattern (subnormals included):
+    the GPU must decode each exactly (integer sums unaffected; rows within
+    tolerance of the fp64 reference)."""
+    rows, k = 1024, 2048
+    nb = k // 32
+    w = inputs.gen_weights(Q4, rows, k, 55).reshape(rows * nb, 18)
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    finite = np.isfinite(pats.view(np.float16))
+    pats = np.where(finite, pats, 0).astype("<u2")
+    w[:, 0:2] = pats.view(np.uint8).reshape(-1, 2)
+    w = w.reshape(-1)
+    x = inputs.gen_activation(1, k, 56)
+    qx, dx, sx = quantize_gpu(zq, x)
+    rq, rd, _ = oracle.quantize_act(x)
+    y_ref, S = oracle.dmmv(Q4, w, rows, k, rq, rd)
+    y = run_dmmv(zq, Q4, w, rows, k, qx, dx, sx)
+    check_rows(host(y), y_ref, S, "every fp16 scale")
+
+
+@pytest.mark.parametrize("wtype", [Q4, Q8])
+def test_dmmv_deterministic(zq, wtype):
+    rows, k = 4096, 4096
+    w = inputs.gen_weights(wtype, rows, k, 9)
+    x = inputs.gen_activation(1, k, 10)
+    qx, dx, sx = quantize_gpu(zq, x)
+    y1 = host(run_dmmv(zq, wtype, w, rows, k, qx, dx, sx))
+    y2 = host(run_dmmv(zq, wtype, w, rows, k, qx, dx, sx))
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+
+
+def test_dmmv_empty_rows(zq):
+    torch = torch_cuda()
+    qx, dx, sx = quantize_gpu(zq, inputs.gen_activation(1, 64, 1))
+    y = nan_f32(1)
+    zq.zq_dmmv_q4_0(dev(np.zeros(64, np.uint8)), 0, 64, qx, dx, sx, y)
+    torch.cuda.synchronize()
+    assert np.isnan(host(y)).all()  # nothing written
+
+
+# -------------------------------------------------------------- argmax -----
+
+def gpu_argmax(zq, y_np):
+    torch = torch_cuda()
+    n = y_np.size
+    yd = dev(y_np.astype(np.float32))
+    ws_bytes = zq.zq_argmax_workspace_bytes(n)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    out = sentinel_i32(1)
+    zq.zq_argmax_f32(yd, n, out, ws, ws_bytes)
+    return int(host(out)[0])
+
+
+def test_argmax_cases(zq):
+    y = np.zeros(100, np.float32)
+    y[5] = y[7] = 3.0
+    assert gpu_argmax(zq, y) == 5
+    assert gpu_argmax(zq, -np.arange(1, 130, dtype=np.float32)) == 0
+    assert gpu_argmax(zq, np.arange(67, dtype=np.float32)) == 66
+    assert gpu_argmax(zq, np.full(1, -7.0, np.float32)) == 0
+    for n in (63, 64, 65, 1023, 1025, 248320, 1 << 20):
+        y = np.random.default_rng(n).standard_normal(n).astype(np.float32)
+        assert gpu_argmax(zq, y) == oracle.argmax_f32(y), n
+    y = np.zeros(248320, np.float32)
+    y[[1000, 200000, 248319]] = 1.0  # ties across partial blocks -> lowest
+    assert gpu_argmax(zq, y) == 1000
+
+
+# ---------------------------------------------- workloads at full size -----
+
+@pytest.mark.parametrize("wl", [1, 2])
+@pytest.mark.parametrize("s", [0, 1, 2])
+def test_workload_dmmv_full(zq, wl, s):
+    cfg = inputs.WORKLOADS[wl]
+    wt, rows, k = cfg["wtype"], cfg["rows"], cfg["k"]
+    w = inputs.gen_weights(wt, rows, k, inputs.seed_for(wl, s))
+    x = inputs.gen_activation(1, k, inputs.seed_for(wl, s) + 1)
+    qx, dx, sx = quantize_gpu(zq, x)
+    rq, rd, rs = oracle.quantize_act(x)
+    assert np.array_equal(host(qx)[0], rq) and np.array_equal(host(dx)[0], rd)
+    assert np.array_equal(host(sx)[0], rs)
+    y_ref, S, isums_ref = oracle.dmmv(wt, w, rows, k, rq, rd, want_isums=True)
+    isums = sentinel_i32(rows, k // 32)
+    zq.zq_dmmv_isums(wt, dev(w), rows, k, qx, sx, isums)
+    assert np.array_equal(host(isums), isums_ref)
+    y = run_dmmv(zq, wt, w, rows, k, qx, dx, sx)
+    check_rows(host(y), y_ref, S, cfg["name"])
+
+
+def test_workload_lmhead_full_and_argmax(zq):
+    """248320 x 2048 Q4_0 logits, every row against the oracle, then argmax."""
+    torch = torch_cuda()
+    cfg = inputs.WORKLOADS[3]
+    wt, rows, k = cfg["wtype"], cfg["rows"], cfg["k"]
+    w = inputs.gen_weights(wt, rows, k, inputs.seed_for(3))
+    x = inputs.gen_activation(1, k, inputs.seed_for(3) + 1)
+    qx, dx, sx = quantize_gpu(zq, x)
+    rq, rd, _ = oracle.quantize_act(x)
+    assert np.array_equal(host(qx)[0], rq)
+    y = run_dmmv(zq, wt, w, rows, k, qx, dx, sx)
+    y_ref, S = oracle.dmmv(wt, w, rows, k, rq, rd)
+    y_h = host(y)
+    check_rows(y_h, y_ref, S, cfg["name"])
+    ws_bytes = zq.zq_argmax_workspace_bytes(rows)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    out = sentinel_i32(1)
+    zq.zq_argmax_f32(y, rows, out, ws, ws_bytes)
+    idx = int(host(out)[0])
+    # exact on the GPU's own logits
+    assert idx == oracle.argmax_f32(y_h)
+    # against the oracle's logits: equal unless its top two are within the
+    # fp32 error bound of each other
+    order = np.argsort(-y_ref, kind="stable")
+    i1, i2 = int(order[0]), int(order[1])
+    if y_ref[i1] - y_ref[i2] >= 1e-4 * (S[i1] + S[i2]):
+        assert idx == i1
+    else:
+        assert y_ref[i1] - y_ref[idx] <= 1e-4 * (S[i1] + S[idx])
