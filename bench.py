@@ -11,8 +11,8 @@ step streams its weights from HBM.  Prints ONE JSON line.
 Timing: a GPU-side spin kernel is queued ahead of the timed region so that the
 K steps are enqueued before the GPU reaches them and run back to back (host
 launch cost is not what is measured); HIP events on the launch stream bracket
-exactly the K steps.  A second pass times the dominant kernel alone with an
-event pair around each launch (roofline.achieved).  The CPU oracle is timed on
+exactly the K steps.  A second pass times K back-to-back launches of the
+dominant kernel alone the same way (roofline.achieved).  The CPU oracle is timed on
 a bounded sample of the same workload (cpu_baseline).
 """
 from __future__ import annotations
@@ -52,7 +52,7 @@ def parse():
 
 class Workload:
     name = ""
-    dominant = ""            # name of the dominant kernel
+    dominant_name = ""       # name of the dominant kernel
     bound = "hbm"
     steps = 2000
     warmup = 50
@@ -63,8 +63,12 @@ class Workload:
     def step(self, i):
         raise NotImplementedError
 
-    def dominant_launch(self, i, ev_start, ev_end):
-        """Run step i with ev_start/ev_end recorded around the dominant kernel."""
+    def prepare_dominant(self):
+        """Produce the inputs the dominant kernel reads (outside any timing)."""
+        raise NotImplementedError
+
+    def dominant(self, i):
+        """Launch only the dominant kernel, on the inputs of step i."""
         raise NotImplementedError
 
     def value(self, ms_per_step):
@@ -95,10 +99,19 @@ class DmmvWorkload(Workload):
         self.bb = inputs.BLOCK_BYTES[self.wtype]
         self.nb = self.k // 32
         self.wbytes = self.rows * self.nb * self.bb
-        self.dmmv_bytes = (self.wbytes + self.k + 4 * self.nb + 4 * self.rows +
-                           (4 * self.nb if self.wtype == inputs.Q4_0 else 0))
-        self.step_bytes = self.dmmv_bytes  # bytes the step's DMMV must move
-        self.dominant = "dmmv_q4_0" if self.wtype == inputs.Q4_0 else "dmmv_q8_0"
+        # small (decode) matrices: one fused launch quantizes x and runs the
+        # DMMV; the LM head: quantize, DMMV, argmax
+        self.fused = wl in (1, 2)
+        if self.fused:
+            # weights + fp32 activation in + fp32 rows out
+            self.dmmv_bytes = self.wbytes + 4 * self.k + 4 * self.rows
+            self.dominant_name = "dmmv_f32x_kernel (quantize + DMMV)"
+        else:
+            # weights + int8 codes + scales + block sums + fp32 rows
+            self.dmmv_bytes = (self.wbytes + self.k + 4 * self.nb + 4 * self.rows +
+                               (4 * self.nb if self.wtype == inputs.Q4_0 else 0))
+            self.dominant_name = "dmmv_kernel"
+        self.step_bytes = self.dmmv_bytes
         self.steps = {1: 20000, 2: 4000, 3: 200}[wl]
         self.warmup = {1: 500, 2: 200, 3: 10}[wl]
 
@@ -128,18 +141,24 @@ class DmmvWorkload(Workload):
             self.zq.zq_dmmv_q8_0(w, self.rows, self.k, self.qx, self.dx, self.y)
 
     def step(self, i):
+        if self.fused:
+            self.zq.zq_dmmv_f32(self.wtype, self.w[i % self.ncopy], self.rows, self.k, self.x,
+                                self.y)
+            return
         self.zq.zq_quantize_act(self.x, 1, self.k, self.k, self.qx, self.dx, self.sx)
         self._dmmv(self.w[i % self.ncopy])
         if self.argmax:
             self.zq.zq_argmax_f32(self.y, self.rows, self.idx, self.ws, self.ws_bytes)
 
-    def dominant_launch(self, i, e0, e1):
-        self.zq.zq_quantize_act(self.x, 1, self.k, self.k, self.qx, self.dx, self.sx)
-        e0.record()
-        self._dmmv(self.w[i % self.ncopy])
-        e1.record()
-        if self.argmax:
-            self.zq.zq_argmax_f32(self.y, self.rows, self.idx, self.ws, self.ws_bytes)
+    def prepare_dominant(self):
+        if not self.fused:
+            self.zq.zq_quantize_act(self.x, 1, self.k, self.k, self.qx, self.dx, self.sx)
+
+    def dominant(self, i):
+        if self.fused:
+            self.step(i)
+        else:
+            self._dmmv(self.w[i % self.ncopy])
 
     def value(self, ms):
         return self.step_bytes / (ms * 1e-3) / 1e9, "GB/s"
@@ -170,7 +189,7 @@ class DmmvWorkload(Workload):
 
 class MoeWorkload(Workload):
     """Router + one token through 8 routed + 1 shared Q4_0 experts."""
-    dominant = "dmmv_moe_gather"
+    dominant_name = "dmmv_kernel (MoE gather)"
     steps = 2000
     warmup = 100
 
@@ -229,18 +248,14 @@ class MoeWorkload(Workload):
         self.zq.zq_moe_ffn(4, gu, self.gs, down, self.ds, self.E + 1, self.dm, self.dff, self.ids,
                            self.wts, self.n_sel, self.x, self.ws, self.ws_bytes, self.y)
 
-    def dominant_launch(self, i, e0, e1):
-        zq = self.zq
-        gu, down = self.banks[i % self.ncopy]
-        self._route(i)
-        zq.zq_quantize_act(self.x, 1, self.dm, self.dm, self.qx, self.dxv, self.sxv)
-        e0.record()
-        zq.zq_dmmv_moe(4, gu, self.E + 1, self.gs, 2 * self.dff, self.dm, self.ids, None, self.n_sel,
-                       self.qx, self.dxv, self.sxv, 0, 0, self.gu)
-        e1.record()
-        zq.zq_swiglu_quantize(self.gu, self.n_sel, self.dff, self.qh, self.dh, self.sh)
-        zq.zq_dmmv_moe(4, down, self.E + 1, self.ds, self.dm, self.dff, self.ids, self.wts,
-                       self.n_sel, self.qh, self.dh, self.sh, self.dff, 1, self.y)
+    def prepare_dominant(self):
+        self._route(0)
+        self.zq.zq_quantize_act(self.x, 1, self.dm, self.dm, self.qx, self.dxv, self.sxv)
+
+    def dominant(self, i):
+        gu, _ = self.banks[i % self.ncopy]
+        self.zq.zq_dmmv_moe(4, gu, self.E + 1, self.gs, 2 * self.dff, self.dm, self.ids, None,
+                            self.n_sel, self.qx, self.dxv, self.sxv, 0, 0, self.gu)
 
     def value(self, ms):
         return self.step_bytes / (ms * 1e-3) / 1e9, "GB/s"
@@ -270,7 +285,7 @@ class MoeWorkload(Workload):
 
 
 class GemmWorkload(Workload):
-    dominant = "gemm_prefill"
+    dominant_name = "gemm_kernel"
     bound = "mfma"
     steps = 100
     warmup = 10
@@ -301,12 +316,12 @@ class GemmWorkload(Workload):
         self.zq.zq_gemm_prefill(4, self.w[i % self.ncopy], self.n, self.k, self.qx, self.dx, None,
                                 self.m, self.y)
 
-    def dominant_launch(self, i, e0, e1):
+    def prepare_dominant(self):
         self.zq.zq_quantize_act(self.x, self.m, self.k, self.k, self.qx, self.dx, None)
-        e0.record()
+
+    def dominant(self, i):
         self.zq.zq_gemm_prefill(4, self.w[i % self.ncopy], self.n, self.k, self.qx, self.dx, None,
                                 self.m, self.y)
-        e1.record()
 
     def value(self, ms):
         return self.ops / (ms * 1e-3) / 1e12, "TOP/s"
@@ -332,6 +347,26 @@ class GemmWorkload(Workload):
         return dict(value=ops_per_s / 1e12, unit="TOP/s", cores=1, kind="oracle",
                     sample="%d output entries (of %d) of this GEMM on one host thread, %.1f s"
                            % (n_pairs, self.m * self.n, el))
+
+
+def counted_traffic(kernel_name):
+    """HBM bytes per launch from the committed counter runs (profiles/traffic.json),
+    or None when the kernel's sources have changed since they were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path)).get(kernel_name)
+    except (OSError, ValueError):
+        return None
+    if not rec:
+        return None
+    h = hashlib.sha256()
+    for src in rec["sources"]:
+        try:
+            h.update(open(os.path.join(ROOT, src), "rb").read())
+        except OSError:
+            return None
+    return rec["traffic_bytes_per_launch"] if h.hexdigest() == rec["sha256"] else None
 
 
 def make_workload(wl):
@@ -419,15 +454,21 @@ def main():
     torch.cuda.synchronize()
     ms_per_step = t_ev0.elapsed_time(t_ev1) / K
 
-    # --- dominant kernel: an event pair around every launch ---
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(K)]
+    # --- dominant kernel alone: K back-to-back launches between two events.
+    # (An event pair around each launch adds several microseconds of marker
+    # processing to a microsecond-scale kernel; back-to-back launches include
+    # only the dispatch gap, which the kernel-trace durations also carry.)
+    w.prepare_dominant()
+    d_ev0 = torch.cuda.Event(enable_timing=True)
+    d_ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     gpu_blocker(torch, 1.5 * h_ms * K + 5)
+    d_ev0.record()
     for i in range(K):
-        w.dominant_launch(i, *evs[i])
+        w.dominant(i)
+    d_ev1.record()
     torch.cuda.synchronize()
-    ms_kernel = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    ms_kernel = d_ev0.elapsed_time(d_ev1) / K
 
     value, unit = w.value(ms_per_step)
     ach, peak, runit, per_launch = w.achieved(ms_kernel)
@@ -448,10 +489,10 @@ def main():
         "pct_of_peak": round(100.0 * value / (HBM_PEAK_GBS if unit == "GB/s" else INT8_PEAK_TOPS), 2),
     }
     out.update({k: round(v, 1) for k, v in w.extra(ms_per_step).items()})
-    out["roofline"] = {"bound": w.bound, "kernel": w.dominant, "achieved": round(ach, 3),
+    out["roofline"] = {"bound": w.bound, "kernel": w.dominant_name, "achieved": round(ach, 3),
                        "peak": peak, "unit": runit, "frac": round(ach / peak, 4),
                        "per_launch": per_launch, "ms_per_launch": round(ms_kernel, 6),
-                       "traffic": None}
+                       "traffic": counted_traffic(w.dominant_name)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = w.cpu_baseline(args.cpu_seconds)
         out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 4)

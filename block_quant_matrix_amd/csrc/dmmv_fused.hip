@@ -1,0 +1,213 @@
+// dmmv_fused.hip -- activation quantization fused into the DMMV (gfx950).
+//
+//   y (+)= W . Q(x)      Q = the activation block quantizer of quantize.hip
+//
+// One launch per matrix-vector product.  Each workgroup (WPB waves) owns
+// WPB*RB*(64/LPR) consecutive rows.  Order of work inside a workgroup:
+//   1. every thread issues its load of the fp32 activation (one float4 of a
+//      32-element block; 8 lanes per block),
+//   2. every lane issues all of its weight-block windows (the DMMV mapping of
+//      dmmv.hip: one lane per block, RB row steps x BPL blocks),
+//   3. the activation (which returns first) is quantized by 8-lane groups
+//      into LDS -- codes, scale and 8*sum -- while the weights stream in,
+//   4. barrier; each lane reads its blocks' codes from LDS (the activation is
+//      staged in LDS once per workgroup and shared by all its waves),
+//   5. packed int8 dots per block, fp32 scaling, lane reduction, store.
+// The quantized activation can also be written out (by workgroup 0) so that
+// later products against the same input need not quantize again.
+#include "zq_common.h"
+#include "zq_internal.h"
+
+namespace zq {
+
+template <int WT, int LPR, int BPL, int RB, int WPB>
+__global__ __launch_bounds__(64 * WPB) void dmmv_f32x_kernel(const DmmvF32Args a) {
+  constexpr int S = 64 / LPR;
+  constexpr int NW = Blk<WT>::NW;
+  constexpr int BB = Blk<WT>::BYTES;
+  constexpr int T = 64 * WPB;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  int8_t *lq = reinterpret_cast<int8_t *>(smem);                   // [k]
+  float *ld = reinterpret_cast<float *>(smem + a.k);               // [nb]
+  int32_t *ls8 = reinterpret_cast<int32_t *>(smem + a.k + 4 * a.nb);  // [nb]
+
+  const int tid = static_cast<int>(threadIdx.x);
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int j = lane & (LPR - 1);
+  const int slot = lane / LPR;
+  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * WPB + wv) * (RB * S);
+
+  // 1. activation loads for this thread's first block
+  const int g = tid & 7;
+  int qb = tid >> 3;
+  float xv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (qb < a.nb) {
+    const float4 v = *reinterpret_cast<const float4 *>(a.x + qb * 32 + g * 4);
+    xv[0] = v.x; xv[1] = v.y; xv[2] = v.z; xv[3] = v.w;
+  }
+
+  // 2. weight windows
+  uint32_t win[RB][BPL][NW];
+  uint32_t off[RB][BPL];
+#pragma unroll
+  for (int t = 0; t < RB; ++t) {
+    int64_t row = row0 + t * S + slot;
+    row = row < a.rows ? row : a.rows - 1;
+#pragma unroll
+    for (int i = 0; i < BPL; ++i) {
+      int b = j + LPR * i;
+      b = b < a.nb ? b : a.nb - 1;
+      off[t][i] = load_window<WT>(a.w + row * a.row_bytes + static_cast<int64_t>(b) * BB, win[t][i]);
+    }
+  }
+
+  // 3. quantize the activation into LDS (8 lanes per block)
+  const bool out = (blockIdx.x == 0) && (a.qx_out != nullptr);
+  for (; qb < a.nb; qb += T / 8) {
+    if (qb != (tid >> 3)) {  // further blocks when k > 4*T (rare)
+      const float4 v = *reinterpret_cast<const float4 *>(a.x + qb * 32 + g * 4);
+      xv[0] = v.x; xv[1] = v.y; xv[2] = v.z; xv[3] = v.w;
+    }
+    float d;
+    int32_t s;
+    const uint32_t packed = quantize_block8(xv, d, s);
+    *reinterpret_cast<uint32_t *>(lq + qb * 32 + g * 4) = packed;
+    if (g == 0) {
+      ld[qb] = d;
+      ls8[qb] = 8 * s;
+    }
+    if (out) {
+      *reinterpret_cast<uint32_t *>(a.qx_out + qb * 32 + g * 4) = packed;
+      if (g == 0) {
+        if (a.dx_out) a.dx_out[qb] = d;
+        if (a.sx_out) a.sx_out[qb] = s;
+      }
+    }
+  }
+  __syncthreads();
+
+  // 4. this lane's activation blocks from LDS
+  uint32_t xq[BPL][8];
+  float xd[BPL];
+  int32_t xs8[BPL];
+#pragma unroll
+  for (int i = 0; i < BPL; ++i) {
+    const int b = j + LPR * i;
+    if (b < a.nb) {
+      const u32x4 v0 = *reinterpret_cast<const u32x4 *>(lq + 32 * b);
+      const u32x4 v1 = *reinterpret_cast<const u32x4 *>(lq + 32 * b + 16);
+      xq[i][0] = v0.x; xq[i][1] = v0.y; xq[i][2] = v0.z; xq[i][3] = v0.w;
+      xq[i][4] = v1.x; xq[i][5] = v1.y; xq[i][6] = v1.z; xq[i][7] = v1.w;
+      xd[i] = ld[b];
+      xs8[i] = WT == ZQ_Q4_0 ? ls8[b] : 0;
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) xq[i][k] = 0;
+      xd[i] = 0.0f;
+      xs8[i] = 0;
+    }
+  }
+
+  // 5. dots, scaling, reduction, store
+  float acc[RB];
+#pragma unroll
+  for (int t = 0; t < RB; ++t) {
+    float p = 0.0f;
+#pragma unroll
+    for (int i = 0; i < BPL; ++i) {
+      const float dw = window_scale(win[t][i][0], off[t][i]);
+      const uint32_t sel = quant_selector(off[t][i]);
+      int32_t isum;
+      if constexpr (WT == ZQ_Q4_0) {
+        isum = q4_raw_dot(win[t][i], sel, xq[i]) - xs8[i];
+      } else {
+        isum = q8_dot(win[t][i], sel, xq[i]);
+      }
+      p = __builtin_fmaf(dw * xd[i], static_cast<float>(isum), p);
+    }
+    acc[t] = p;
+  }
+  using R = RowReduce<LPR, RB>;
+  float res[R::NOUT];
+  R::run(acc, res);
+  if (R::writer(lane)) {
+#pragma unroll
+    for (int m = 0; m < R::NOUT; ++m) {
+      const int64_t row = row0 + static_cast<int64_t>(R::rowstep(m, lane)) * S + slot;
+      if (row < a.rows) {
+        float *yp = a.y + row;
+        *yp = (a.flags & ZQ_ACCUMULATE) ? *yp + res[m] : res[m];
+      }
+    }
+  }
+}
+
+namespace {
+
+struct FShape {
+  int lpr, bpl;
+};
+// Single-pass layouts: nb <= LPR * BPL.
+constexpr FShape kFShapes[] = {{8, 1}, {16, 1}, {32, 1}, {64, 1}, {64, 2}, {32, 5}, {64, 4}, {64, 8}};
+
+template <int WT, int LPR, int BPL, int RB, int WPB>
+int launch_f(const DmmvF32Args &a, hipStream_t stream) {
+  constexpr int S = 64 / LPR;
+  const int64_t rows_per_wg = static_cast<int64_t>(WPB) * RB * S;
+  const int64_t grid = (a.rows + rows_per_wg - 1) / rows_per_wg;
+  const size_t lds = static_cast<size_t>(a.k) + 8 * static_cast<size_t>(a.nb);
+  hipLaunchKernelGGL((dmmv_f32x_kernel<WT, LPR, BPL, RB, WPB>), dim3(static_cast<unsigned>(grid)),
+                     dim3(64 * WPB), lds, stream, a);
+  ZQ_LAUNCH_CHECK();
+  return ZQ_OK;
+}
+
+// Small matrices (decode): 16 waves per workgroup, one row step per wave, so
+// the activation is quantized once per 16*S rows and every SIMD holds four
+// waves.  Large matrices: four waves per workgroup, several row steps each.
+template <int WT, int LPR, int BPL>
+int launch_fs(const DmmvF32Args &a, hipStream_t stream) {
+  constexpr int S = 64 / LPR;
+  // 1024-thread groups leave 128 VGPRs per wave: wide layouts use 8 waves.
+  constexpr int WPB = BPL <= 2 ? 16 : 8;
+  if (a.rows <= static_cast<int64_t>(256) * WPB * S) return launch_f<WT, LPR, BPL, 1, WPB>(a, stream);
+  if constexpr (BPL <= 2) return launch_f<WT, LPR, BPL, 4, 4>(a, stream);
+  return launch_f<WT, LPR, BPL, 2, 4>(a, stream);
+}
+
+template <int WT>
+int launch_fw(const FShape &s, const DmmvF32Args &a, hipStream_t stream) {
+  if (s.lpr == 8) return launch_fs<WT, 8, 1>(a, stream);
+  if (s.lpr == 16) return launch_fs<WT, 16, 1>(a, stream);
+  if (s.lpr == 32 && s.bpl == 1) return launch_fs<WT, 32, 1>(a, stream);
+  if (s.lpr == 32 && s.bpl == 5) return launch_fs<WT, 32, 5>(a, stream);
+  if (s.lpr == 64 && s.bpl == 1) return launch_fs<WT, 64, 1>(a, stream);
+  if (s.lpr == 64 && s.bpl == 2) return launch_fs<WT, 64, 2>(a, stream);
+  if (s.lpr == 64 && s.bpl == 4) return launch_fs<WT, 64, 4>(a, stream);
+  return launch_fs<WT, 64, 8>(a, stream);
+}
+
+}  // namespace
+
+int launch_dmmv_f32x(int wtype, DmmvF32Args a, hipStream_t stream) {
+  if (a.rows == 0) return ZQ_OK;
+  a.row_bytes = static_cast<int64_t>(a.nb) * (wtype == ZQ_Q4_0 ? 18 : 34);
+  // the single-pass layout with the least idle lanes
+  FShape best = kFShapes[0];
+  int64_t waste = -1;
+  for (const FShape &s : kFShapes) {
+    const int64_t cap = static_cast<int64_t>(s.lpr) * s.bpl;
+    if (cap < a.nb) continue;
+    const int64_t w = cap - a.nb;
+    if (waste < 0 || w < waste || (w == waste && s.lpr > best.lpr)) {
+      best = s;
+      waste = w;
+    }
+  }
+  if (waste < 0) return ZQ_EINVAL;
+  if (wtype == ZQ_Q4_0) return launch_fw<ZQ_Q4_0>(best, a, stream);
+  return launch_fw<ZQ_Q8_0>(best, a, stream);
+}
+
+}  // namespace zq

@@ -124,6 +124,30 @@ int zq_dmmv_q4_0(const void *w, int64_t rows, int64_t k, const int8_t *qx, const
   return dmmv_common(ZQ_Q4_0, w, rows, k, qx, dx, sx, y, flags, stream);
 }
 
+int zq_dmmv_f32(int wtype, const void *w, int64_t rows, int64_t k, const float *x, float *y,
+                uint32_t flags, int8_t *qx_out, float *dx_out, int32_t *sx_out, void *stream) {
+  ZQ_REQUIRE(block_bytes(wtype) > 0, ZQ_EINVAL);
+  ZQ_REQUIRE(w && x && y, ZQ_ENULL);
+  ZQ_REQUIRE(rows >= 0 && k_ok(k) && k <= 16384, ZQ_EINVAL);
+  ZQ_REQUIRE((flags & ~uint32_t(ZQ_ACCUMULATE)) == 0, ZQ_EINVAL);
+  ZQ_REQUIRE(al(w, 4) && al(x, 16) && al(y, 4) && al(qx_out, 4) && al(dx_out, 4) && al(sx_out, 4),
+             ZQ_EALIGN);
+  const int dc = check_current_device();
+  if (dc != ZQ_OK) return dc;
+  zq::DmmvF32Args a{};
+  a.w = static_cast<const uint8_t *>(w);
+  a.x = x;
+  a.y = y;
+  a.qx_out = qx_out;
+  a.dx_out = dx_out;
+  a.sx_out = sx_out;
+  a.rows = rows;
+  a.k = static_cast<int32_t>(k);
+  a.nb = static_cast<int32_t>(k / 32);
+  a.flags = flags;
+  return zq::launch_dmmv_f32x(wtype, a, S(stream));
+}
+
 int zq_dmmv_isums(int wtype, const void *w, int64_t rows, int64_t k, const int8_t *qx,
                   const int32_t *sx, int32_t *isums, void *stream) {
   ZQ_REQUIRE(block_bytes(wtype) > 0, ZQ_EINVAL);

@@ -200,8 +200,11 @@ struct RowReduce {
 
 // --------------------------------------------------------- quantization ---
 
-// Round half away from zero, for |v| < 2^23.
+// Round half away from zero, for |v| < 2^23.  v must already be a rounded
+// fp32 value: the callers keep FMA contraction off so that v - trunc(v) is
+// not fused with the multiply that produced v.
 __device__ __forceinline__ float round_half_away(float v) {
+#pragma clang fp contract(off)
   const float t = __builtin_truncf(v);
   const float f = v - t;  // exact
   return (__builtin_fabsf(f) >= 0.5f) ? t + __builtin_copysignf(1.0f, v) : t;
@@ -213,6 +216,9 @@ __device__ __forceinline__ float round_half_away(float v) {
 // every lane of the group).
 __device__ __forceinline__ uint32_t quantize_block8(const float (&x)[4], float &d_out,
                                                    int32_t &s_out) {
+  // Every step below is one IEEE fp32 operation, rounded on its own: x*id
+  // must be rounded before its fractional part decides the code.
+#pragma clang fp contract(off)
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[i]));

@@ -31,6 +31,22 @@ struct DmmvArgs {
   uint32_t flags;
 };
 
+// The fused quantize + DMMV launch.
+struct DmmvF32Args {
+  const uint8_t *w;
+  const float *x;       // fp32 activation [k]
+  float *y;
+  int8_t *qx_out;       // optional copy of the quantized activation
+  float *dx_out;
+  int32_t *sx_out;
+  int64_t rows;
+  int64_t row_bytes;    // filled in by the launcher
+  int32_t k;
+  int32_t nb;
+  uint32_t flags;
+};
+
+int launch_dmmv_f32x(int wtype, DmmvF32Args a, hipStream_t stream);
 int launch_quantize_act(const float *x, int64_t n_tok, int64_t k, int64_t x_stride, int8_t *qx,
                         float *dx, int32_t *sx, hipStream_t stream);
 int launch_swiglu_quantize(const float *gu, int64_t n, int64_t f, int8_t *qh, float *dh,

@@ -33,6 +33,7 @@ SIGNATURES = {
     "zq_quantize_act": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "zq_dmmv_q8_0": (_INT, [_P, _I64, _I64, _P, _P, _P, _U32, _P]),
     "zq_dmmv_q4_0": (_INT, [_P, _I64, _I64, _P, _P, _P, _P, _U32, _P]),
+    "zq_dmmv_f32": (_INT, [_INT, _P, _I64, _I64, _P, _P, _U32, _P, _P, _P, _P]),
     "zq_dmmv_isums": (_INT, [_INT, _P, _I64, _I64, _P, _P, _P, _P]),
     "zq_argmax_workspace_bytes": (_SZ, [_I64]),
     "zq_argmax_f32": (_INT, [_P, _I64, _P, _P, _SZ, _P]),
@@ -122,6 +123,12 @@ def zq_dmmv_q8_0(w, rows, k, qx, dx, y, flags=0, stream=None):
 def zq_dmmv_q4_0(w, rows, k, qx, dx, sx, y, flags=0, stream=None):
     return _call("zq_dmmv_q4_0", ptr(w), rows, k, ptr(qx), ptr(dx), ptr(sx), ptr(y), flags,
                  _stream(stream))
+
+
+def zq_dmmv_f32(wtype, w, rows, k, x, y, flags=0, qx_out=None, dx_out=None, sx_out=None,
+                stream=None):
+    return _call("zq_dmmv_f32", wtype, ptr(w), rows, k, ptr(x), ptr(y), flags, ptr(qx_out),
+                 ptr(dx_out), ptr(sx_out), _stream(stream))
 
 
 def zq_dmmv_isums(wtype, w, rows, k, qx, sx, isums, stream=None):

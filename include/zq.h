@@ -87,6 +87,21 @@ int zq_dmmv_q8_0(const void *w, int64_t rows, int64_t k, const int8_t *qx, const
 int zq_dmmv_q4_0(const void *w, int64_t rows, int64_t k, const int8_t *qx, const float *dx,
                  const int32_t *sx, float *y, uint32_t flags, void *stream);
 
+/* DMMV from the fp32 activation in one launch: y (+)= W . Q(x), where Q is
+ * exactly the quantization of zq_quantize_act (same codes, scales, sums).
+ * The input is the fp32 vector, as in the direct row-range DMMV slice of
+ * "The first ZINC_RT model slices that actually count", section "The
+ * one-wave workaround" (input fp32 vector, output fp32 rows, weight rows,
+ * cols a multiple of 32, rows); each workgroup quantizes x into LDS while its
+ * weight loads are in flight.
+ * wtype: ZQ_Q4_0 or ZQ_Q8_0; w: rows x k blocks; x [k] fp32 (16-byte aligned,
+ * finite); y [rows] fp32; flags: 0 or ZQ_ACCUMULATE; 32 <= k <= 16384.
+ * qx_out [k] int8 (4-byte aligned), dx_out [k/32], sx_out [k/32]: when
+ * qx_out is non-NULL the quantized activation is also stored there (dx_out
+ * and sx_out may each be NULL); all three may be NULL. */
+int zq_dmmv_f32(int wtype, const void *w, int64_t rows, int64_t k, const float *x, float *y,
+                uint32_t flags, int8_t *qx_out, float *dx_out, int32_t *sx_out, void *stream);
+
 /* Test hook: the per-block integer sums of the same DMMV inner loop,
  * isums[r][b] for every row r and block b (int32 [rows][k/32]). */
 int zq_dmmv_isums(int wtype, const void *w, int64_t rows, int64_t k, const int8_t *qx,

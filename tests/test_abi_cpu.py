@@ -92,6 +92,16 @@ def test_dmmv_argument_errors():
     assert L.zq_dmmv_isums(4, A, 4, 64, B, None, None, None) == zq.ZQ_ENULL
 
 
+def test_fused_dmmv_argument_errors():
+    L = zq.lib()
+    assert L.zq_dmmv_f32(4, A, 4, 16416, B, C, 0, None, None, None, None) == zq.ZQ_EINVAL
+    assert L.zq_dmmv_f32(6, A, 4, 64, B, C, 0, None, None, None, None) == zq.ZQ_EINVAL
+    assert L.zq_dmmv_f32(4, A, 4, 64, B + 4, C, 0, None, None, None, None) == zq.ZQ_EALIGN
+    assert L.zq_dmmv_f32(4, A, 4, 64, B, C, 0, D + 2, None, None, None) == zq.ZQ_EALIGN
+    assert L.zq_dmmv_f32(4, A, 4, 64, None, C, 0, None, None, None, None) == zq.ZQ_ENULL
+    assert L.zq_dmmv_f32(8, A, 4, 64, B, C, 4, None, None, None, None) == zq.ZQ_EINVAL
+
+
 def test_other_argument_errors():
     L = zq.lib()
     # quantize: stride < k, misaligned x, stride not a multiple of 4

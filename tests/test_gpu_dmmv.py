@@ -60,6 +60,20 @@ def test_quantize_bitexact(zq, t, k):
     assert np.array_equal(host(sx), rs)
 
 
+def test_quantize_halfway_after_rounding(zq):
+    """fp32 products that round to exactly c + 1/2: the GPU must round the
+    product before deciding, as the oracle does (no fused multiply-add)."""
+    from cases import halfway_after_rounding
+    for seed in (1, 2, 3):
+        x, hits = halfway_after_rounding(seed)
+        qx, dx, sx = quantize_gpu(zq, x)
+        rq, rd, rs = oracle.quantize_act(x)
+        q = host(qx)[0]
+        assert all(int(rq[i]) == want for i, want in hits)
+        assert np.array_equal(q, rq), int((q != rq).sum())
+        assert np.array_equal(host(dx)[0], rd) and np.array_equal(host(sx)[0], rs)
+
+
 def test_quantize_strided_rows_and_null_sums(zq):
     torch = torch_cuda()
     t, k, stride = 5, 256, 260
@@ -109,6 +123,35 @@ def test_dmmv_isums_and_rows(zq, wtype, rows, k):
         assert np.array_equal(host(isums2), isums_ref)
         y2 = run_dmmv(zq, wtype, w, rows, k, qx, dx, None)
         assert np.array_equal(host(y2), host(y))
+
+
+@pytest.mark.parametrize("wtype", [Q4, Q8])
+@pytest.mark.parametrize("rows,k", SHAPES + [(4096, 4096), (5000, 2048), (20000, 512)])
+def test_dmmv_f32_fused(zq, wtype, rows, k):
+    """Quantize + DMMV in one launch: the quantized activation it writes out is
+    bit-exact with the oracle, the rows are within tolerance."""
+    torch = torch_cuda()
+    seed = 300 * rows + k + wtype
+    w = inputs.gen_weights(wtype, rows, k, seed)
+    x = inputs.gen_activation(1, k, seed + 1)
+    if k >= 64:
+        x[:64] = special_activation(64, 2)
+    y = nan_f32(rows)
+    qxo = torch.full((k,), 0x55, dtype=torch.int8, device="cuda")
+    dxo = nan_f32(k // 32)
+    sxo = sentinel_i32(k // 32)
+    wd = dev(w)
+    zq.zq_dmmv_f32(wtype, wd, rows, k, dev(x), y, 0, qxo, dxo, sxo)
+    rq, rd, rs = oracle.quantize_act(x)
+    assert np.array_equal(host(qxo), rq)
+    assert np.array_equal(host(dxo).view(np.uint32), rd.view(np.uint32))
+    assert np.array_equal(host(sxo), rs)
+    y_ref, S = oracle.dmmv(wtype, w, rows, k, rq, rd)
+    check_rows(host(y), y_ref, S, "fused wtype=%d %dx%d" % (wtype, rows, k))
+    # accumulate, and no quantized-activation output
+    y2 = y.clone()
+    zq.zq_dmmv_f32(wtype, wd, rows, k, dev(x), y2, 1)
+    assert np.allclose(host(y2), 2 * host(y), rtol=1e-6, atol=0)
 
 
 @pytest.mark.parametrize("wtype", [Q4, Q8])
@@ -253,6 +296,9 @@ def test_workload_dmmv_full(zq, wl, s):
     assert np.array_equal(host(isums), isums_ref)
     y = run_dmmv(zq, wt, w, rows, k, qx, dx, sx)
     check_rows(host(y), y_ref, S, cfg["name"])
+    yf = nan_f32(rows)
+    zq.zq_dmmv_f32(wt, dev(w), rows, k, dev(x), yf)
+    check_rows(host(yf), y_ref, S, cfg["name"] + " fused")
 
 
 def test_workload_lmhead_full_and_argmax(zq):

@@ -468,3 +468,15 @@ def test_generator_distributions():
     assert abs(d.mean() - 0.01 * math.sqrt(2 / math.pi)) < 1e-4
     # some scales are fp16 subnormals; they must be kept as such
     assert (d < 2.0 ** -14).any()
+
+
+def test_p3f_halfway_after_rounding(ref):
+    """Elements whose fp32 product x*id rounds to exactly c + 1/2 (the exact
+    product lies below it) must quantize to c + 1: the product is rounded to
+    fp32 before the half-away-from-zero decision."""
+    from cases import halfway_after_rounding
+    x, hits = halfway_after_rounding(11)
+    assert len(hits) > 1000
+    q, d, s = ref.quantize_act(x)
+    for i, want in hits:
+        assert int(q[i]) == want, (i, want, int(q[i]))
