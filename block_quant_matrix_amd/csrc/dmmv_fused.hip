@@ -4,11 +4,11 @@
 //
 // One launch per matrix-vector product.  Each workgroup (WPB waves) owns
 // WPB*RB*(64/LPR) consecutive rows.  Order of work inside a workgroup:
-//   1. every thread issues its load of the fp32 activation (one float4 of a
-//      32-element block; 8 lanes per block),
+//   1. every thread issues its load of the fp32 activation (two lanes per
+//      32-element block, four float4 each),
 //   2. every lane issues all of its weight-block windows (the DMMV mapping of
 //      dmmv.hip: one lane per block, RB row steps x BPL blocks),
-//   3. the activation (which returns first) is quantized by 8-lane groups
+//   3. the activation (which returns first) is quantized by 2-lane groups
 //      into LDS -- codes, scale and 8*sum -- while the weights stream in,
 //   4. barrier; each lane reads its blocks' codes from LDS (the activation is
 //      staged in LDS once per workgroup and shared by all its waves),
@@ -38,13 +38,17 @@ __global__ __launch_bounds__(64 * WPB) void dmmv_f32x_kernel(const DmmvF32Args a
   const int slot = lane / LPR;
   const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * WPB + wv) * (RB * S);
 
-  // 1. activation loads for this thread's first block
-  const int g = tid & 7;
-  int qb = tid >> 3;
-  float xv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  // 1. activation loads for this thread's first block: two lanes per block,
+  //    16 elements (four float4) each
+  const int g = tid & 1;
+  int qb = tid >> 1;
+  float xv[16];
   if (qb < a.nb) {
-    const float4 v = *reinterpret_cast<const float4 *>(a.x + qb * 32 + g * 4);
-    xv[0] = v.x; xv[1] = v.y; xv[2] = v.z; xv[3] = v.w;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float4 v = *reinterpret_cast<const float4 *>(a.x + qb * 32 + g * 16 + 4 * u);
+      xv[4 * u] = v.x; xv[4 * u + 1] = v.y; xv[4 * u + 2] = v.z; xv[4 * u + 3] = v.w;
+    }
   }
 
   // 2. weight windows
@@ -62,23 +66,29 @@ __global__ __launch_bounds__(64 * WPB) void dmmv_f32x_kernel(const DmmvF32Args a
     }
   }
 
-  // 3. quantize the activation into LDS (8 lanes per block)
+  // 3. quantize the activation into LDS.  Two lanes per block keep the
+  //    per-block work (the two IEEE divisions) on as few waves as possible.
   const bool out = (blockIdx.x == 0) && (a.qx_out != nullptr);
-  for (; qb < a.nb; qb += T / 8) {
-    if (qb != (tid >> 3)) {  // further blocks when k > 4*T (rare)
-      const float4 v = *reinterpret_cast<const float4 *>(a.x + qb * 32 + g * 4);
-      xv[0] = v.x; xv[1] = v.y; xv[2] = v.z; xv[3] = v.w;
+  for (; qb < a.nb; qb += T / 2) {
+    if (qb != (tid >> 1)) {  // further blocks when k > 16*T (not for k <= 16384)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float4 v = *reinterpret_cast<const float4 *>(a.x + qb * 32 + g * 16 + 4 * u);
+        xv[4 * u] = v.x; xv[4 * u + 1] = v.y; xv[4 * u + 2] = v.z; xv[4 * u + 3] = v.w;
+      }
     }
+    uint32_t pk[4];
     float d;
     int32_t s;
-    const uint32_t packed = quantize_block8(xv, d, s);
-    *reinterpret_cast<uint32_t *>(lq + qb * 32 + g * 4) = packed;
+    quantize_block<2>(xv, pk, d, s);
+    *reinterpret_cast<u32x4 *>(lq + qb * 32 + g * 16) = u32x4{pk[0], pk[1], pk[2], pk[3]};
     if (g == 0) {
       ld[qb] = d;
       ls8[qb] = 8 * s;
     }
     if (out) {
-      *reinterpret_cast<uint32_t *>(a.qx_out + qb * 32 + g * 4) = packed;
+      uint32_t *qo = reinterpret_cast<uint32_t *>(a.qx_out + qb * 32 + g * 16);
+      qo[0] = pk[0]; qo[1] = pk[1]; qo[2] = pk[2]; qo[3] = pk[3];
       if (g == 0) {
         if (a.dx_out) a.dx_out[qb] = d;
         if (a.sx_out) a.sx_out[qb] = s;

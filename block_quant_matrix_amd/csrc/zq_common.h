@@ -21,21 +21,25 @@ template <> struct Blk<ZQ_Q8_0> { static constexpr int BYTES = 34; static conste
 
 typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// Global-address-space views: loads through these are global_load (vmcnt
+// only).  A generic pointer would become flat_load, which also counts in
+// lgkmcnt and makes the compiler wait for every load before touching LDS.
+typedef __attribute__((address_space(1))) const uint32_t g_u32;
+typedef __attribute__((address_space(1))) const u32x4a4 g_u32x4a4;
 
 // Load the NW-dword window holding the block at byte address p (p is 2-byte
 // aligned; the window starts at p rounded down to 4).  Returns the byte
 // offset o in {0, 2} of the block inside the window.
 template <int WT>
 __device__ __forceinline__ uint32_t load_window(const uint8_t *p, uint32_t (&w)[Blk<WT>::NW]) {
-  const uintptr_t addr = reinterpret_cast<uintptr_t>(p);
-  const uint32_t o = static_cast<uint32_t>(addr & 3u);
-  const uint32_t *pw = reinterpret_cast<const uint32_t *>(addr - o);
-  const u32x4a4 v0 = *reinterpret_cast<const u32x4a4 *>(pw);
+  const uint32_t o = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p) & 3u);
+  const g_u32 *pw = (const g_u32 *)(p - o);
+  const u32x4a4 v0 = *(const g_u32x4a4 *)pw;
   w[0] = v0.x; w[1] = v0.y; w[2] = v0.z; w[3] = v0.w;
   if constexpr (WT == ZQ_Q4_0) {
     w[4] = pw[4];
   } else {
-    const u32x4a4 v1 = *reinterpret_cast<const u32x4a4 *>(pw + 4);
+    const u32x4a4 v1 = *(const g_u32x4a4 *)(pw + 4);
     w[4] = v1.x; w[5] = v1.y; w[6] = v1.z; w[7] = v1.w;
     w[8] = pw[8];
   }
@@ -210,39 +214,54 @@ __device__ __forceinline__ float round_half_away(float v) {
   return (__builtin_fabsf(f) >= 0.5f) ? t + __builtin_copysignf(1.0f, v) : t;
 }
 
-// Quantize one 32-element block held by 8 consecutive lanes (4 elements per
-// lane, lane g of the group holding elements 4g..4g+3).  Returns the 4 codes
-// packed little-endian; d and s are the block scale and code sum (valid in
-// every lane of the group).
-__device__ __forceinline__ uint32_t quantize_block8(const float (&x)[4], float &d_out,
-                                                   int32_t &s_out) {
+// Quantize one 32-element block held by G consecutive lanes (G in {2,4,8}),
+// lane g of the group holding elements g*E .. g*E+E-1 with E = 32/G.  The
+// codes come back packed little-endian, four per dword; d and s (the block
+// scale and code sum) are valid in every lane of the group.  The result does
+// not depend on G: max is exact, the scale is one IEEE division, and every
+// element is rounded on its own.
+template <int G>
+__device__ __forceinline__ void quantize_block(const float (&x)[32 / G], uint32_t (&packed)[8 / G],
+                                               float &d_out, int32_t &s_out) {
   // Every step below is one IEEE fp32 operation, rounded on its own: x*id
   // must be rounded before its fractional part decides the code.
 #pragma clang fp contract(off)
+  constexpr int E = 32 / G;
   float amax = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[i]));
-  amax = __builtin_fmaxf(amax, dpp<DPP_QUAD_XOR1>(amax));
-  amax = __builtin_fmaxf(amax, dpp<DPP_QUAD_XOR2>(amax));
-  amax = __builtin_fmaxf(amax, dpp<DPP_ROW_HALF_MIRROR>(amax));
+  for (int i = 0; i < E; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[i]));
+  if constexpr (G >= 2) amax = __builtin_fmaxf(amax, dpp<DPP_QUAD_XOR1>(amax));
+  if constexpr (G >= 4) amax = __builtin_fmaxf(amax, dpp<DPP_QUAD_XOR2>(amax));
+  if constexpr (G >= 8) amax = __builtin_fmaxf(amax, dpp<DPP_ROW_HALF_MIRROR>(amax));
   const float d = amax / 127.0f;              // IEEE division (no fast-math)
   const float id = (d != 0.0f) ? 1.0f / d : 0.0f;
-  uint32_t packed = 0;
   int32_t s = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int q = static_cast<int>(round_half_away(x[i] * id));
-    q = q > 127 ? 127 : (q < -127 ? -127 : q);
-    s += q;
-    packed |= (static_cast<uint32_t>(q) & 0xFFu) << (8 * i);
+  for (int w = 0; w < E / 4; ++w) {
+    uint32_t p = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int q = static_cast<int>(round_half_away(x[4 * w + i] * id));
+      q = q > 127 ? 127 : (q < -127 ? -127 : q);
+      s += q;
+      p |= (static_cast<uint32_t>(q) & 0xFFu) << (8 * i);
+    }
+    packed[w] = p;
   }
-  float sf = static_cast<float>(s);  // |s| <= 508: exact in fp32
-  sf += dpp<DPP_QUAD_XOR1>(sf);
-  sf += dpp<DPP_QUAD_XOR2>(sf);
-  sf += dpp<DPP_ROW_HALF_MIRROR>(sf);
+  float sf = static_cast<float>(s);  // |s| <= 32*127: exact in fp32
+  if constexpr (G >= 2) sf += dpp<DPP_QUAD_XOR1>(sf);
+  if constexpr (G >= 4) sf += dpp<DPP_QUAD_XOR2>(sf);
+  if constexpr (G >= 8) sf += dpp<DPP_ROW_HALF_MIRROR>(sf);
   d_out = d;
   s_out = static_cast<int32_t>(sf);
-  return packed;
+}
+
+// The 8-lane form (four elements per lane) used by the standalone kernels.
+__device__ __forceinline__ uint32_t quantize_block8(const float (&x)[4], float &d_out,
+                                                   int32_t &s_out) {
+  uint32_t packed[1];
+  quantize_block<8>(x, packed, d_out, s_out);
+  return packed[0];
 }
 
 }  // namespace zq
