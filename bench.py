@@ -189,7 +189,7 @@ class DmmvWorkload(Workload):
 
 class MoeWorkload(Workload):
     """Router + one token through 8 routed + 1 shared Q4_0 experts."""
-    dominant_name = "dmmv_kernel (MoE gather)"
+    dominant_name = "moe_gate_up_kernel"
     steps = 2000
     warmup = 100
 
@@ -203,7 +203,9 @@ class MoeWorkload(Workload):
         self.gu_w = self.n_sel * 2 * self.dff * (self.dm // 32) * bb
         self.down_w = self.n_sel * self.dm * (self.dff // 32) * bb
         self.step_bytes = self.gu_w + self.down_w + 4 * self.dm + 4 * self.dm
-        self.gather_bytes = self.gu_w + self.dm + 8 * (self.dm // 32) + 4 * self.n_sel * 2 * self.dff
+        # fused gate/up pass: weights + fp32 x in + quantized h out (codes, scales, sums)
+        self.gate_up_bytes = (self.gu_w + 4 * self.dm + self.n_sel * self.dff +
+                              8 * self.n_sel * (self.dff // 32))
 
     def setup(self, torch, zq, inputs):
         self.torch, self.zq = torch, zq
@@ -228,11 +230,7 @@ class MoeWorkload(Workload):
         self.ws_bytes = zq.zq_moe_ffn_workspace_bytes(self.dm, self.dff, self.n_sel)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
         self.y = torch.empty(self.dm, dtype=torch.float32, device="cuda")
-        # stage buffers for the instrumented pass
-        self.qx = torch.empty(self.dm, dtype=torch.int8, device="cuda")
-        self.dxv = torch.empty(self.dm // 32, dtype=torch.float32, device="cuda")
-        self.sxv = torch.empty(self.dm // 32, dtype=torch.int32, device="cuda")
-        self.gu = torch.empty((self.n_sel, 2 * self.dff), dtype=torch.float32, device="cuda")
+        # outputs of the gate/up pass when it is timed alone
         self.qh = torch.empty((self.n_sel, self.dff), dtype=torch.int8, device="cuda")
         self.dh = torch.empty((self.n_sel, self.dff // 32), dtype=torch.float32, device="cuda")
         self.sh = torch.empty((self.n_sel, self.dff // 32), dtype=torch.int32, device="cuda")
@@ -250,18 +248,17 @@ class MoeWorkload(Workload):
 
     def prepare_dominant(self):
         self._route(0)
-        self.zq.zq_quantize_act(self.x, 1, self.dm, self.dm, self.qx, self.dxv, self.sxv)
 
     def dominant(self, i):
         gu, _ = self.banks[i % self.ncopy]
-        self.zq.zq_dmmv_moe(4, gu, self.E + 1, self.gs, 2 * self.dff, self.dm, self.ids, None,
-                            self.n_sel, self.qx, self.dxv, self.sxv, 0, 0, self.gu)
+        self.zq.zq_moe_gate_up(4, gu, self.gs, self.E + 1, self.dm, self.dff, self.ids, self.n_sel,
+                               self.x, self.qh, self.dh, self.sh)
 
     def value(self, ms):
         return self.step_bytes / (ms * 1e-3) / 1e9, "GB/s"
 
     def achieved(self, ms):
-        return self.gather_bytes / (ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s", self.gather_bytes
+        return self.gate_up_bytes / (ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s", self.gate_up_bytes
 
     def extra(self, ms):
         return {"tokens_per_s": 1.0 / (ms * 1e-3)}

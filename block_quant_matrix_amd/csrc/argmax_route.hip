@@ -113,67 +113,76 @@ int launch_argmax(const float *y, int64_t n, int32_t *out_idx, void *ws, hipStre
 
 // ------------------------------------------------------------- router -----
 
-// One wave.  Lane l holds logits l, l+64, ... (up to 16 per lane).  top_k
-// rounds of a wave-wide (value, id) maximum pick the experts largest first,
-// ties to the lower id.  The softmax over the selected logits and the
-// shared-expert sigmoid are evaluated in fp64 by lane 0, in selection order.
-__global__ __launch_bounds__(64) void moe_route_kernel(const float *__restrict__ logits,
-                                                       int32_t n_routed, int32_t top_k,
-                                                       const float *__restrict__ shared_gate,
-                                                       int32_t *__restrict__ ids,
-                                                       float *__restrict__ wts) {
-  constexpr int PER = 16;
-  const int lane = static_cast<int>(threadIdx.x);
-  float v[PER];
-  bool taken[PER];
-#pragma unroll
-  for (int r = 0; r < PER; ++r) {
-    const int e = lane + 64 * r;
-    v[r] = e < n_routed ? logits[e] : -__builtin_inff();
-    taken[r] = e >= n_routed;
-  }
+// Rank selection.  Each logit's rank is the number of logits that beat it
+// (larger, or equal at a lower id); the top_k experts are the logits of rank
+// < top_k, stored at their rank, so they come out largest first with ties
+// to the lower id.  P threads share one logit's comparisons (logits staged
+// in LDS and read as broadcasts) and add their partial counts with DPP.  The
+// softmax over the selected logits is evaluated in fp64 (each of the top_k
+// exponentials by its own thread, the normalizer summed in rank order), as
+// is the shared expert's sigmoid.
+template <int P>
+__global__ __launch_bounds__(1024) void moe_route_kernel(const float *__restrict__ logits,
+                                                         int32_t n_routed, int32_t top_k,
+                                                         const float *__restrict__ shared_gate,
+                                                         int32_t *__restrict__ ids,
+                                                         float *__restrict__ wts) {
+  __shared__ float lv[1024];
   __shared__ int32_t sel_id[64];
   __shared__ float sel_v[64];
-  for (int s = 0; s < top_k; ++s) {
-    float bv = -__builtin_inff();
-    int32_t bi = 0x7fffffff;
-#pragma unroll
-    for (int r = 0; r < PER; ++r) {
-      const int e = lane + 64 * r;
-      if (!taken[r] && beats(v[r], e, bv, bi)) {
-        bv = v[r];
-        bi = e;
+  __shared__ double sel_e[64];
+  const int t = static_cast<int>(threadIdx.x);
+  for (int i = t; i < n_routed; i += static_cast<int>(blockDim.x)) lv[i] = logits[i];
+  __syncthreads();
+  const int n_groups = static_cast<int>(blockDim.x) / P;
+  const int part = t & (P - 1);
+  for (int e0 = 0; e0 < n_routed; e0 += n_groups) {  // uniform trip count
+    const int e = e0 + t / P;
+    const bool ok = e < n_routed;
+    const float v = ok ? lv[e] : 0.0f;
+    float cnt = 0.0f;  // exact small integers
+    if (ok) {
+      for (int j = part; j < n_routed; j += P) {
+        const float u = lv[j];
+        cnt += (u > v || (u == v && j < e)) ? 1.0f : 0.0f;
       }
     }
-    wave_best(bv, bi);
-#pragma unroll
-    for (int r = 0; r < PER; ++r)
-      if (lane + 64 * r == bi) taken[r] = true;
-    if (lane == 0) {
-      sel_id[s] = bi;
-      sel_v[s] = bv;
+    cnt = group_sum<P>(cnt);
+    if (ok && part == 0) {
+      const int rank = static_cast<int>(cnt);
+      if (rank < top_k) {
+        sel_id[rank] = e;
+        sel_v[rank] = v;
+      }
     }
   }
   __syncthreads();
-  if (lane == 0) {
-    const double m = static_cast<double>(sel_v[0]);
+  if (t < top_k) sel_e[t] = exp(static_cast<double>(sel_v[t]) - static_cast<double>(sel_v[0]));
+  __syncthreads();
+  if (t < top_k) {
     double z = 0.0;
-    for (int s = 0; s < top_k; ++s) z += exp(static_cast<double>(sel_v[s]) - m);
-    for (int s = 0; s < top_k; ++s) {
-      ids[s] = sel_id[s];
-      wts[s] = static_cast<float>(exp(static_cast<double>(sel_v[s]) - m) / z);
-    }
-    if (shared_gate) {
-      ids[top_k] = n_routed;
-      wts[top_k] = static_cast<float>(1.0 / (1.0 + exp(-static_cast<double>(*shared_gate))));
-    }
+    for (int s = 0; s < top_k; ++s) z += sel_e[s];
+    ids[t] = sel_id[t];
+    wts[t] = static_cast<float>(sel_e[t] / z);
+  }
+  if (t == top_k && shared_gate) {
+    ids[top_k] = n_routed;
+    wts[top_k] = static_cast<float>(1.0 / (1.0 + exp(-static_cast<double>(*shared_gate))));
   }
 }
 
 int launch_moe_route(const float *logits, int32_t n_routed, int32_t top_k, const float *shared_gate,
                      int32_t *ids, float *wts, hipStream_t stream) {
-  hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(64), 0, stream, logits, n_routed, top_k,
-                     shared_gate, ids, wts);
+  // 1024 threads; P threads per logit while n_routed * P fits (P <= 16)
+  int p = 1;
+  while (p < 16 && n_routed * (p * 2) <= 1024) p *= 2;
+  switch (p) {
+    case 16: hipLaunchKernelGGL(moe_route_kernel<16>, dim3(1), dim3(1024), 0, stream, logits, n_routed, top_k, shared_gate, ids, wts); break;
+    case 8: hipLaunchKernelGGL(moe_route_kernel<8>, dim3(1), dim3(1024), 0, stream, logits, n_routed, top_k, shared_gate, ids, wts); break;
+    case 4: hipLaunchKernelGGL(moe_route_kernel<4>, dim3(1), dim3(1024), 0, stream, logits, n_routed, top_k, shared_gate, ids, wts); break;
+    case 2: hipLaunchKernelGGL(moe_route_kernel<2>, dim3(1), dim3(1024), 0, stream, logits, n_routed, top_k, shared_gate, ids, wts); break;
+    default: hipLaunchKernelGGL(moe_route_kernel<1>, dim3(1), dim3(1024), 0, stream, logits, n_routed, top_k, shared_gate, ids, wts); break;
+  }
   ZQ_LAUNCH_CHECK();
   return ZQ_OK;
 }

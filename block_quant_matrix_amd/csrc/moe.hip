@@ -1,0 +1,392 @@
+// moe.hip -- the MoE expert FFN of one token in two launches (gfx950).
+//
+// gate/up pass (moe_gate_up_kernel): one workgroup of 16 waves per
+// (selected expert, 32-wide block of the FFN width).  It quantizes the fp32
+// activation into LDS (two lanes per 32-element block), computes the 32 gate
+// rows and the 32 matching up rows of that expert with the lane-per-block
+// DMMV mapping, and finishes in its epilogue with SwiGLU
+// h = silu(g) * u (fp64, one rounding to fp32) and the re-quantization of
+// that 32-element block of h: codes, scale and block sum go straight to the
+// down pass's input.  The swiglu + quantize step never round-trips through
+// a separate launch.
+//
+// down pass (moe_down_kernel): every lane owns one (row, block) of the down
+// matrices and issues the windows of ALL selected experts before any
+// arithmetic (up to 16 per chunk), with the selected experts' quantized
+// activations staged in LDS.  The per-expert weight multiplies each expert's
+// partial before the single lane reduction, so the weighted accumulate costs
+// one FMA per expert and lane.
+#include "zq_common.h"
+#include "zq_internal.h"
+
+namespace zq {
+
+// ------------------------------------------------------------- gate/up ----
+
+template <int WT, int LPR, int BPL, int RB>
+__global__ __launch_bounds__(1024) void moe_gate_up_kernel(const MoeGateUpArgs a) {
+  constexpr int WPB = 16;
+  constexpr int S = 64 / LPR;
+  constexpr int NW = Blk<WT>::NW;
+  constexpr int BB = Blk<WT>::BYTES;
+  constexpr int T = 64 * WPB;
+  static_assert(RB * S * WPB == 64, "a workgroup computes 32 gate + 32 up rows");
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  int8_t *lq = reinterpret_cast<int8_t *>(smem);                     // [k]
+  float *ld = reinterpret_cast<float *>(smem + a.k);                 // [nb]
+  int32_t *ls8 = reinterpret_cast<int32_t *>(smem + a.k + 4 * a.nb);  // [nb]
+  float *lrow = reinterpret_cast<float *>(smem + a.k + 8 * a.nb);     // [64] gate | up
+
+  const int tid = static_cast<int>(threadIdx.x);
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int j = lane & (LPR - 1);
+  const int slot = lane / LPR;
+  const int hb = static_cast<int>(blockIdx.x);  // 32-wide block of the FFN width
+  const int s = static_cast<int>(blockIdx.y);   // selected-expert slot
+
+  // activation loads (two lanes per block), issued before the expert id so
+  // that they share its round trip
+  const int g = tid & 1;
+  int qb = tid >> 1;
+  float xv[16];
+  if (qb < a.nb) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float4 v = *reinterpret_cast<const float4 *>(a.x + qb * 32 + g * 16 + 4 * u);
+      xv[4 * u] = v.x; xv[4 * u + 1] = v.y; xv[4 * u + 2] = v.z; xv[4 * u + 3] = v.w;
+    }
+  }
+  const int e = a.ids[s];
+  if (e < 0 || e >= a.n_experts) {  // uniform over the workgroup
+    if (a.status && tid == 0) *a.status = ZQ_ERANGE;
+    return;
+  }
+  const uint8_t *wb = a.bank + static_cast<int64_t>(e) * a.expert_stride;
+
+  // weight windows: local rows 0..31 -> gate rows 32*hb.., 32..63 -> up rows
+  uint32_t win[RB][BPL][NW];
+  uint32_t off[RB][BPL];
+#pragma unroll
+  for (int t = 0; t < RB; ++t) {
+    const int lr = wv * (RB * S) + t * S + slot;  // 0..63
+    const int64_t row = (lr < 32) ? (32 * hb + lr) : (a.d_ff + 32 * hb + (lr - 32));
+#pragma unroll
+    for (int i = 0; i < BPL; ++i) {
+      int b = j + LPR * i;
+      b = b < a.nb ? b : a.nb - 1;
+      off[t][i] = load_window<WT>(wb + row * a.row_bytes + static_cast<int64_t>(b) * BB, win[t][i]);
+    }
+  }
+
+  // quantize x into LDS
+  for (; qb < a.nb; qb += T / 2) {
+    if (qb != (tid >> 1)) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float4 v = *reinterpret_cast<const float4 *>(a.x + qb * 32 + g * 16 + 4 * u);
+        xv[4 * u] = v.x; xv[4 * u + 1] = v.y; xv[4 * u + 2] = v.z; xv[4 * u + 3] = v.w;
+      }
+    }
+    uint32_t pk[4];
+    float d;
+    int32_t sum;
+    quantize_block<2>(xv, pk, d, sum);
+    *reinterpret_cast<u32x4 *>(lq + qb * 32 + g * 16) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+    if (g == 0) {
+      ld[qb] = d;
+      ls8[qb] = 8 * sum;
+    }
+  }
+  __syncthreads();
+
+  uint32_t xq[BPL][8];
+  float xd[BPL];
+  int32_t xs8[BPL];
+#pragma unroll
+  for (int i = 0; i < BPL; ++i) {
+    const int b = j + LPR * i;
+    if (b < a.nb) {
+      const u32x4 v0 = *reinterpret_cast<const u32x4 *>(lq + 32 * b);
+      const u32x4 v1 = *reinterpret_cast<const u32x4 *>(lq + 32 * b + 16);
+      xq[i][0] = v0.x; xq[i][1] = v0.y; xq[i][2] = v0.z; xq[i][3] = v0.w;
+      xq[i][4] = v1.x; xq[i][5] = v1.y; xq[i][6] = v1.z; xq[i][7] = v1.w;
+      xd[i] = ld[b];
+      xs8[i] = WT == ZQ_Q4_0 ? ls8[b] : 0;
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) xq[i][k] = 0;
+      xd[i] = 0.0f;
+      xs8[i] = 0;
+    }
+  }
+  float acc[RB];
+#pragma unroll
+  for (int t = 0; t < RB; ++t) {
+    float p = 0.0f;
+#pragma unroll
+    for (int i = 0; i < BPL; ++i) {
+      const float dw = window_scale(win[t][i][0], off[t][i]);
+      const uint32_t sel = quant_selector(off[t][i]);
+      int32_t isum;
+      if constexpr (WT == ZQ_Q4_0) {
+        isum = q4_raw_dot(win[t][i], sel, xq[i]) - xs8[i];
+      } else {
+        isum = q8_dot(win[t][i], sel, xq[i]);
+      }
+      p = __builtin_fmaf(dw * xd[i], static_cast<float>(isum), p);
+    }
+    acc[t] = p;
+  }
+  using R = RowReduce<LPR, RB>;
+  float res[R::NOUT];
+  R::run(acc, res);
+  if (R::writer(lane)) {
+#pragma unroll
+    for (int m = 0; m < R::NOUT; ++m) {
+      const int lr = wv * (RB * S) + R::rowstep(m, lane) * S + slot;
+      lrow[lr] = res[m];
+    }
+  }
+  __syncthreads();
+
+  // epilogue: SwiGLU over the 32 outputs and their quantization (8 lanes,
+  // four elements each)
+  if (tid < 8) {
+    const int i0 = 4 * tid;
+    float hv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const double gd = static_cast<double>(lrow[i0 + q]);
+      const double silu = gd / (1.0 + exp(-gd));
+      hv[q] = static_cast<float>(silu * static_cast<double>(lrow[32 + i0 + q]));
+    }
+    uint32_t packed[1];
+    float d;
+    int32_t sum;
+    quantize_block<8>(hv, packed, d, sum);
+    const int64_t hoff = static_cast<int64_t>(s) * a.d_ff + 32 * hb + i0;
+    *reinterpret_cast<uint32_t *>(a.qh + hoff) = packed[0];
+    if (tid == 0) {
+      a.dh[static_cast<int64_t>(s) * (a.d_ff / 32) + hb] = d;
+      if (a.sh) a.sh[static_cast<int64_t>(s) * (a.d_ff / 32) + hb] = sum;
+    }
+    if (a.h_out) *reinterpret_cast<float4 *>(a.h_out + hoff) = make_float4(hv[0], hv[1], hv[2], hv[3]);
+    if (a.gu_out) {
+      float *gp = a.gu_out + static_cast<int64_t>(s) * 2 * a.d_ff;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        gp[32 * hb + i0 + q] = lrow[i0 + q];
+        gp[a.d_ff + 32 * hb + i0 + q] = lrow[32 + i0 + q];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- down -----
+
+constexpr int kDownMaxSel = 16;  // experts whose windows are in flight at once
+
+template <int WT, int LPR, int BPL, int WPB>
+__global__ __launch_bounds__(64 * WPB) void moe_down_kernel(const MoeDownArgs a) {
+  constexpr int S = 64 / LPR;
+  constexpr int NW = Blk<WT>::NW;
+  constexpr int BB = Blk<WT>::BYTES;
+  constexpr int T = 64 * WPB;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  // per slot: codes [k], then scales [nb] and 8*sums [nb] after all codes
+  int8_t *lq = reinterpret_cast<int8_t *>(smem);
+  float *ld = reinterpret_cast<float *>(smem + static_cast<int64_t>(a.n_sel) * a.k);
+  int32_t *ls8 = reinterpret_cast<int32_t *>(ld + static_cast<int64_t>(a.n_sel) * a.nb);
+
+  const int tid = static_cast<int>(threadIdx.x);
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int j = lane & (LPR - 1);
+  const int slot = lane / LPR;
+  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * WPB + wv) * S;
+  int64_t row = row0 + slot;
+  const bool row_ok = row < a.rows;
+  row = row_ok ? row : a.rows - 1;
+
+  float acc = 0.0f;
+  bool first = true;
+  for (int s0 = 0; s0 < a.n_sel; s0 += kDownMaxSel) {
+    // All of the chunk's expert ids first: a window address depends on its
+    // id, and the loads' counter is in order, so waiting for an id issued
+    // after other windows would wait for those windows too.
+    // One vector load brings the chunk's ids (lane c holds id c), then
+    // v_readlane makes each one uniform; the weights come the same way.
+    const int cl = lane & (kDownMaxSel - 1);
+    const bool cok = s0 + cl < a.n_sel;
+    const int my_id = cok ? a.ids[s0 + cl] : -1;
+    const float my_w = cok ? a.wts[s0 + cl] : 0.0f;
+    int eid[kDownMaxSel];
+#pragma unroll
+    for (int c = 0; c < kDownMaxSel; ++c) eid[c] = __builtin_amdgcn_readlane(my_id, c);
+    uint32_t win[kDownMaxSel][BPL][NW];
+    uint32_t off[kDownMaxSel][BPL];
+#pragma unroll
+    for (int c = 0; c < kDownMaxSel; ++c) {
+      const int s = s0 + c;
+      if (s < a.n_sel) {
+        const int e = eid[c];
+        const bool eok = e >= 0 && e < a.n_experts;
+        const uint8_t *wb = a.bank + static_cast<int64_t>(eok ? e : 0) * a.expert_stride;
+#pragma unroll
+        for (int i = 0; i < BPL; ++i) {
+          int b = j + LPR * i;
+          b = b < a.nb ? b : a.nb - 1;
+          off[c][i] = load_window<WT>(wb + row * a.row_bytes + static_cast<int64_t>(b) * BB, win[c][i]);
+        }
+      }
+    }
+    if (first) {
+      // The first chunk's windows are in flight: stage every slot's
+      // activation (codes in 16-byte pieces, scales, 8*sums) in LDS meanwhile.
+      const int64_t nq = static_cast<int64_t>(a.n_sel) * a.k / 16;
+      for (int64_t q = tid; q < nq; q += T) {
+        const int64_t sl = q * 16 / a.k, in = q * 16 - sl * a.k;
+        *reinterpret_cast<u32x4 *>(lq + q * 16) =
+            *reinterpret_cast<const u32x4 *>(a.qx + sl * a.x_stride + in);
+      }
+      const int64_t nsc = static_cast<int64_t>(a.n_sel) * a.nb;
+      for (int64_t q = tid; q < nsc; q += T) {
+        const int64_t sl = q / a.nb, b = q - sl * a.nb;
+        ld[q] = a.dx[sl * (a.x_stride / 32) + b];
+        if constexpr (WT == ZQ_Q4_0) {
+          int32_t sum;
+          if (a.sx) {
+            sum = a.sx[sl * (a.x_stride / 32) + b];
+          } else {
+            sum = 0;
+            const uint32_t *cq = reinterpret_cast<const uint32_t *>(a.qx + sl * a.x_stride + 32 * b);
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+              sum = __builtin_amdgcn_sdot4(static_cast<int>(cq[k]), 0x01010101, sum, false);
+          }
+          ls8[q] = 8 * sum;
+        }
+      }
+      __syncthreads();  // the staged activations are visible
+      first = false;
+    }
+#pragma unroll
+    for (int c = 0; c < kDownMaxSel; ++c) {
+      const int s = s0 + c;
+      if (s < a.n_sel) {
+        const int e = eid[c];
+        if (e < 0 || e >= a.n_experts) {
+          if (a.status) *a.status = ZQ_ERANGE;
+          continue;
+        }
+        const float ws = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_w), c));
+        float p = 0.0f;
+#pragma unroll
+        for (int i = 0; i < BPL; ++i) {
+          const int b = j + LPR * i;
+          const bool bok = b < a.nb;
+          const int bc = bok ? b : 0;
+          const int8_t *cq = lq + static_cast<int64_t>(s) * a.k + 32 * bc;
+          const u32x4 v0 = *reinterpret_cast<const u32x4 *>(cq);
+          const u32x4 v1 = *reinterpret_cast<const u32x4 *>(cq + 16);
+          const uint32_t xq[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+          const float xd = bok ? ld[static_cast<int64_t>(s) * a.nb + bc] : 0.0f;
+          const float dw = window_scale(win[c][i][0], off[c][i]);
+          const uint32_t sel = quant_selector(off[c][i]);
+          int32_t isum;
+          if constexpr (WT == ZQ_Q4_0) {
+            isum = q4_raw_dot(win[c][i], sel, xq) - ls8[static_cast<int64_t>(s) * a.nb + bc];
+          } else {
+            isum = q8_dot(win[c][i], sel, xq);
+          }
+          p = __builtin_fmaf(dw * xd, static_cast<float>(isum), p);
+        }
+        acc = __builtin_fmaf(ws, p, acc);
+      }
+    }
+  }
+  if (first) __syncthreads();  // (n_sel == 0) keep the barrier count uniform
+
+  using R = RowReduce<LPR, 1>;
+  float v[1] = {acc};
+  float res[1];
+  R::run(v, res);
+  if (R::writer(lane) && row_ok) {
+    float *yp = a.y + row0 + slot;
+    *yp = (a.flags & ZQ_ACCUMULATE) ? *yp + res[0] : res[0];
+  }
+}
+
+// ------------------------------------------------------------ dispatch -----
+
+namespace {
+
+template <int WT, int LPR, int BPL, int RB>
+int launch_gu(const MoeGateUpArgs &a, hipStream_t stream) {
+  const size_t lds = static_cast<size_t>(a.k) + 8 * static_cast<size_t>(a.nb) + 64 * 4;
+  hipLaunchKernelGGL((moe_gate_up_kernel<WT, LPR, BPL, RB>),
+                     dim3(static_cast<unsigned>(a.d_ff / 32), static_cast<unsigned>(a.n_sel)),
+                     dim3(1024), lds, stream, a);
+  ZQ_LAUNCH_CHECK();
+  return ZQ_OK;
+}
+
+template <int WT>
+int launch_gu_w(const MoeGateUpArgs &a, hipStream_t stream) {
+  // single-pass layouts with 64 rows per 16-wave workgroup
+  if (a.nb <= 16) return launch_gu<WT, 16, 1, 1>(a, stream);
+  if (a.nb <= 32) return launch_gu<WT, 32, 1, 2>(a, stream);
+  if (a.nb <= 64) return launch_gu<WT, 64, 1, 4>(a, stream);
+  return launch_gu<WT, 64, 2, 4>(a, stream);  // nb <= 128 (moe_gate_up_fits)
+}
+
+template <int WT, int LPR, int BPL>
+int launch_dn(const MoeDownArgs &a, hipStream_t stream) {
+  constexpr int WPB = 2;
+  constexpr int S = 64 / LPR;
+  const int64_t rows_per_wg = WPB * S;
+  const unsigned grid = static_cast<unsigned>((a.rows + rows_per_wg - 1) / rows_per_wg);
+  hipLaunchKernelGGL((moe_down_kernel<WT, LPR, BPL, WPB>), dim3(grid), dim3(64 * WPB),
+                     moe_down_lds_bytes(a.n_sel, a.k), stream, a);
+  ZQ_LAUNCH_CHECK();
+  return ZQ_OK;
+}
+
+template <int WT>
+int launch_dn_w(const MoeDownArgs &a, hipStream_t stream) {
+  if (a.nb <= 8) return launch_dn<WT, 8, 1>(a, stream);
+  if (a.nb <= 16) return launch_dn<WT, 16, 1>(a, stream);
+  if (a.nb <= 32) return launch_dn<WT, 32, 1>(a, stream);
+  if (a.nb <= 64) return launch_dn<WT, 64, 1>(a, stream);
+  return launch_dn<WT, 64, 2>(a, stream);
+}
+
+}  // namespace
+
+size_t moe_down_lds_bytes(int64_t n_sel, int64_t k) {
+  return static_cast<size_t>(n_sel) * (static_cast<size_t>(k) + 8 * static_cast<size_t>(k / 32));
+}
+
+// 1024-thread workgroups leave 128 VGPRs per wave: two blocks per lane at most.
+bool moe_gate_up_fits(int64_t d_model) { return d_model <= 4096; }
+bool moe_down_fits(int64_t n_sel, int64_t k) {
+  return k <= 4096 && moe_down_lds_bytes(n_sel, k) <= 64 * 1024;
+}
+
+int launch_moe_gate_up(int wtype, MoeGateUpArgs a, hipStream_t stream) {
+  if (a.n_sel == 0 || a.d_ff == 0) return ZQ_OK;
+  a.nb = static_cast<int32_t>(a.k / 32);
+  a.row_bytes = static_cast<int64_t>(a.nb) * (wtype == ZQ_Q4_0 ? 18 : 34);
+  return wtype == ZQ_Q4_0 ? launch_gu_w<ZQ_Q4_0>(a, stream) : launch_gu_w<ZQ_Q8_0>(a, stream);
+}
+
+int launch_moe_down(int wtype, MoeDownArgs a, hipStream_t stream) {
+  if (a.rows == 0) return ZQ_OK;
+  a.nb = static_cast<int32_t>(a.k / 32);
+  a.row_bytes = static_cast<int64_t>(a.nb) * (wtype == ZQ_Q4_0 ? 18 : 34);
+  return wtype == ZQ_Q4_0 ? launch_dn_w<ZQ_Q4_0>(a, stream) : launch_dn_w<ZQ_Q8_0>(a, stream);
+}
+
+}  // namespace zq

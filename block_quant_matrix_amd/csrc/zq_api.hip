@@ -233,8 +233,62 @@ int zq_dmmv_moe(int wtype, const void *bank, int64_t n_experts, int64_t expert_s
   a.n_experts = static_cast<int32_t>(n_experts);
   a.n_sel = n_sel;
   a.flags = flags;
+  if (mode == ZQ_MOE_WEIGHTED_SUM && x_stride % 32 == 0 && zq::moe_down_fits(n_sel, k)) {
+    zq::MoeDownArgs b{};
+    b.bank = static_cast<const uint8_t *>(bank);
+    b.expert_stride = expert_stride_bytes;
+    b.n_experts = static_cast<int32_t>(n_experts);
+    b.ids = ids;
+    b.wts = wts;
+    b.n_sel = n_sel;
+    b.qx = qx;
+    b.dx = dx;
+    b.sx = wtype == ZQ_Q4_0 ? sx : nullptr;
+    b.x_stride = x_stride;
+    b.k = static_cast<int32_t>(k);
+    b.rows = rows;
+    b.y = y;
+    b.flags = flags;
+    b.status = dev_status;
+    return zq::launch_moe_down(wtype, b, S(stream));
+  }
   return zq::launch_dmmv(wtype, mode == ZQ_MOE_GATHER ? zq::MODE_GATHER : zq::MODE_WEIGHTED, a,
                          S(stream));
+}
+
+int zq_moe_gate_up(int wtype, const void *gu_bank, int64_t gu_stride_bytes, int64_t n_experts,
+                   int64_t d_model, int64_t d_ff, const int32_t *ids, int32_t n_sel,
+                   const float *x, int8_t *qh, float *dh, int32_t *sh, float *h_out,
+                   float *gu_out, int32_t *dev_status, void *stream) {
+  const int64_t bb = block_bytes(wtype);
+  ZQ_REQUIRE(bb > 0, ZQ_EINVAL);
+  ZQ_REQUIRE(gu_bank && ids && x && qh && dh, ZQ_ENULL);
+  ZQ_REQUIRE(n_experts >= 1 && n_experts <= INT32_MAX && k_ok(d_model) && k_ok(d_ff), ZQ_EINVAL);
+  ZQ_REQUIRE(zq::moe_gate_up_fits(d_model) && d_ff <= (int64_t(1) << 30), ZQ_EINVAL);
+  ZQ_REQUIRE(n_sel >= 0 && n_sel <= 65535, ZQ_EINVAL);
+  ZQ_REQUIRE(gu_stride_bytes >= 2 * d_ff * (d_model / 32) * bb && gu_stride_bytes % 2 == 0,
+             ZQ_EINVAL);
+  ZQ_REQUIRE(al(gu_bank, 4) && al(ids, 4) && al(x, 16) && al(qh, 16) && al(dh, 4) && al(sh, 4) &&
+                 al(h_out, 16) && al(gu_out, 4) && al(dev_status, 4),
+             ZQ_EALIGN);
+  const int dc = check_current_device();
+  if (dc != ZQ_OK) return dc;
+  zq::MoeGateUpArgs a{};
+  a.bank = static_cast<const uint8_t *>(gu_bank);
+  a.expert_stride = gu_stride_bytes;
+  a.n_experts = static_cast<int32_t>(n_experts);
+  a.ids = ids;
+  a.n_sel = n_sel;
+  a.x = x;
+  a.k = static_cast<int32_t>(d_model);
+  a.d_ff = static_cast<int32_t>(d_ff);
+  a.qh = qh;
+  a.dh = dh;
+  a.sh = sh;
+  a.h_out = h_out;
+  a.gu_out = gu_out;
+  a.status = dev_status;
+  return zq::launch_moe_gate_up(wtype, a, S(stream));
 }
 
 int zq_swiglu_quantize(const float *gu, int64_t n, int64_t f, int8_t *qh, float *dh, int32_t *sh,
@@ -275,39 +329,75 @@ int zq_moe_ffn(int wtype, const void *gu_bank, int64_t gu_stride_bytes, const vo
   const int dc = check_current_device();
   if (dc != ZQ_OK) return dc;
   uint8_t *ws = static_cast<uint8_t *>(workspace);
-  int8_t *qx = reinterpret_cast<int8_t *>(ws + L.qx);
-  float *dx = reinterpret_cast<float *>(ws + L.dx);
-  int32_t *sx = reinterpret_cast<int32_t *>(ws + L.sx);
-  float *gu = reinterpret_cast<float *>(ws + L.gu);
   int8_t *qh = reinterpret_cast<int8_t *>(ws + L.qh);
   float *dh = reinterpret_cast<float *>(ws + L.dh);
   int32_t *sh = reinterpret_cast<int32_t *>(ws + L.sh);
   hipStream_t s = S(stream);
   int rc;
-  if (n_sel > 0) {
-  rc = zq::launch_quantize_act(x, 1, d_model, d_model, qx, dx, sx, s);
-  if (rc != ZQ_OK) return rc;
-  zq::DmmvArgs a{};
-  a.w = static_cast<const uint8_t *>(gu_bank);
-  a.qx = qx;
-  a.dx = dx;
-  a.sx = wtype == ZQ_Q4_0 ? sx : nullptr;
-  a.y = gu;
-  a.ids = ids;
-  a.status = dev_status;
-  a.rows = 2 * d_ff;
-  a.expert_stride = gu_stride_bytes;
-  a.x_stride = 0;
-  a.nb = static_cast<int32_t>(d_model / 32);
-  a.n_experts = static_cast<int32_t>(n_experts);
-  a.n_sel = n_sel;
-  rc = zq::launch_dmmv(wtype, zq::MODE_GATHER, a, s);
-  if (rc != ZQ_OK) return rc;
-  rc = zq::launch_swiglu_quantize(gu, n_sel, d_ff, qh, dh, sh, nullptr, s);
-  if (rc != ZQ_OK) return rc;
+  if (zq::moe_gate_up_fits(d_model)) {
+    zq::MoeGateUpArgs a{};
+    a.bank = static_cast<const uint8_t *>(gu_bank);
+    a.expert_stride = gu_stride_bytes;
+    a.n_experts = static_cast<int32_t>(n_experts);
+    a.ids = ids;
+    a.n_sel = n_sel;
+    a.x = x;
+    a.k = static_cast<int32_t>(d_model);
+    a.d_ff = static_cast<int32_t>(d_ff);
+    a.qh = qh;
+    a.dh = dh;
+    a.sh = sh;
+    a.status = dev_status;
+    rc = zq::launch_moe_gate_up(wtype, a, s);
+    if (rc != ZQ_OK) return rc;
+  } else if (n_sel > 0) {
+    // wide models: quantize x, gather gate||up rows, then swiglu + quantize
+    int8_t *qx = reinterpret_cast<int8_t *>(ws + L.qx);
+    float *dx = reinterpret_cast<float *>(ws + L.dx);
+    int32_t *sx = reinterpret_cast<int32_t *>(ws + L.sx);
+    float *gu = reinterpret_cast<float *>(ws + L.gu);
+    rc = zq::launch_quantize_act(x, 1, d_model, d_model, qx, dx, sx, s);
+    if (rc != ZQ_OK) return rc;
+    zq::DmmvArgs a{};
+    a.w = static_cast<const uint8_t *>(gu_bank);
+    a.qx = qx;
+    a.dx = dx;
+    a.sx = wtype == ZQ_Q4_0 ? sx : nullptr;
+    a.y = gu;
+    a.ids = ids;
+    a.status = dev_status;
+    a.rows = 2 * d_ff;
+    a.expert_stride = gu_stride_bytes;
+    a.x_stride = 0;
+    a.nb = static_cast<int32_t>(d_model / 32);
+    a.n_experts = static_cast<int32_t>(n_experts);
+    a.n_sel = n_sel;
+    rc = zq::launch_dmmv(wtype, zq::MODE_GATHER, a, s);
+    if (rc != ZQ_OK) return rc;
+    rc = zq::launch_swiglu_quantize(gu, n_sel, d_ff, qh, dh, sh, nullptr, s);
+    if (rc != ZQ_OK) return rc;
   }
-  // With no selected expert the weighted pass writes y = 0 (or leaves y as
-  // it is with ZQ_ACCUMULATE) and reads no activation.
+  // With no selected expert the down pass writes y = 0 (or leaves y as it
+  // is with ZQ_ACCUMULATE) and reads no activation.
+  if (zq::moe_down_fits(n_sel, d_ff)) {
+    zq::MoeDownArgs b{};
+    b.bank = static_cast<const uint8_t *>(down_bank);
+    b.expert_stride = down_stride_bytes;
+    b.n_experts = static_cast<int32_t>(n_experts);
+    b.ids = ids;
+    b.wts = wts;
+    b.n_sel = n_sel;
+    b.qx = qh;
+    b.dx = dh;
+    b.sx = wtype == ZQ_Q4_0 ? sh : nullptr;
+    b.x_stride = d_ff;
+    b.k = static_cast<int32_t>(d_ff);
+    b.rows = d_model;
+    b.y = y;
+    b.flags = flags;
+    b.status = dev_status;
+    return zq::launch_moe_down(wtype, b, s);
+  }
   zq::DmmvArgs b{};
   b.w = static_cast<const uint8_t *>(down_bank);
   b.qx = qh;

@@ -47,6 +47,53 @@ struct DmmvF32Args {
 };
 
 int launch_dmmv_f32x(int wtype, DmmvF32Args a, hipStream_t stream);
+
+// MoE gate/up pass fused with swiglu + re-quantization.
+struct MoeGateUpArgs {
+  const uint8_t *bank;  // experts of [2*d_ff rows][k]
+  int64_t expert_stride;
+  int32_t n_experts;
+  const int32_t *ids;
+  int32_t n_sel;
+  const float *x;       // fp32 activation [k]
+  int32_t k;
+  int32_t nb;           // filled in by the launcher
+  int64_t row_bytes;    // filled in by the launcher
+  int32_t d_ff;
+  int8_t *qh;           // [n_sel][d_ff]
+  float *dh;            // [n_sel][d_ff/32]
+  int32_t *sh;          // [n_sel][d_ff/32] or null
+  float *h_out;         // [n_sel][d_ff] or null
+  float *gu_out;        // [n_sel][2*d_ff] or null
+  int32_t *status;
+};
+
+// MoE down pass with the weighted sum over the selected experts fused in.
+struct MoeDownArgs {
+  const uint8_t *bank;  // experts of [rows][k]
+  int64_t expert_stride;
+  int32_t n_experts;
+  const int32_t *ids;
+  const float *wts;
+  int32_t n_sel;
+  const int8_t *qx;     // slot s at qx + s * x_stride
+  const float *dx;
+  const int32_t *sx;
+  int64_t x_stride;
+  int32_t k;
+  int32_t nb;           // filled in by the launcher
+  int64_t rows;
+  int64_t row_bytes;    // filled in by the launcher
+  float *y;
+  uint32_t flags;
+  int32_t *status;
+};
+
+int launch_moe_gate_up(int wtype, MoeGateUpArgs a, hipStream_t stream);
+int launch_moe_down(int wtype, MoeDownArgs a, hipStream_t stream);
+size_t moe_down_lds_bytes(int64_t n_sel, int64_t k);
+bool moe_gate_up_fits(int64_t d_model);
+bool moe_down_fits(int64_t n_sel, int64_t k);
 int launch_quantize_act(const float *x, int64_t n_tok, int64_t k, int64_t x_stride, int8_t *qx,
                         float *dx, int32_t *sx, hipStream_t stream);
 int launch_swiglu_quantize(const float *gu, int64_t n, int64_t f, int8_t *qh, float *dh,

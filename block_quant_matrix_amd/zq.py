@@ -41,6 +41,8 @@ SIGNATURES = {
     "zq_dmmv_moe": (_INT, [_INT, _P, _I64, _I64, _I64, _I64, _P, _P, _I32, _P, _P, _P, _I64,
                            _INT, _P, _U32, _P, _P]),
     "zq_swiglu_quantize": (_INT, [_P, _I64, _I64, _P, _P, _P, _P, _P]),
+    "zq_moe_gate_up": (_INT, [_INT, _P, _I64, _I64, _I64, _I64, _P, _I32, _P, _P, _P, _P, _P, _P,
+                              _P, _P]),
     "zq_moe_ffn_workspace_bytes": (_SZ, [_I64, _I64, _I32]),
     "zq_moe_ffn": (_INT, [_INT, _P, _I64, _P, _I64, _I64, _I64, _I64, _P, _P, _I32, _P, _P, _SZ,
                           _P, _U32, _P, _P]),
@@ -160,6 +162,13 @@ def zq_dmmv_moe(wtype, bank, n_experts, expert_stride_bytes, rows, k, ids, wts, 
 def zq_swiglu_quantize(gu, n, f, qh, dh, sh=None, h_out=None, stream=None):
     return _call("zq_swiglu_quantize", ptr(gu), n, f, ptr(qh), ptr(dh), ptr(sh), ptr(h_out),
                  _stream(stream))
+
+
+def zq_moe_gate_up(wtype, gu_bank, gu_stride_bytes, n_experts, d_model, d_ff, ids, n_sel, x, qh,
+                   dh, sh=None, h_out=None, gu_out=None, dev_status=None, stream=None):
+    return _call("zq_moe_gate_up", wtype, ptr(gu_bank), gu_stride_bytes, n_experts, d_model, d_ff,
+                 ptr(ids), n_sel, ptr(x), ptr(qh), ptr(dh), ptr(sh), ptr(h_out), ptr(gu_out),
+                 ptr(dev_status), _stream(stream))
 
 
 def zq_moe_ffn_workspace_bytes(d_model, d_ff, n_sel) -> int:

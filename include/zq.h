@@ -154,9 +154,29 @@ int zq_dmmv_moe(int wtype, const void *bank, int64_t n_experts, int64_t expert_s
 int zq_swiglu_quantize(const float *gu, int64_t n, int64_t f, int8_t *qh, float *dh,
                        int32_t *sh, float *h_out, void *stream);
 
-/* One token through the selected experts: quantize x, gate||up DMMV of every
- * selected expert (one launch), swiglu + re-quantize, down DMMV with the
- * weighted sum fused (one launch).  gu_bank: experts of [2*d_ff][d_model]
+/* The gate||up stage of the expert FFN with SwiGLU and the re-quantization
+ * fused in (one launch): for every selected slot s and every 32-wide block
+ * of the FFN width, the 32 gate rows and 32 up rows of expert ids[s] against
+ * Q(x) (the quantization of zq_quantize_act), then h = silu(g)*u in fp64
+ * rounded once to fp32, then h quantized exactly as zq_quantize_act.
+ * ("dmmv_q4k_moe (gate/up)" and "swiglu", "CUDA backend for ZINC",
+ * section 5; the fusion is that page's M3 "fused_gate_up" item.)
+ * gu_bank: experts of [2*d_ff][d_model] (rows 0..d_ff-1 gate, d_ff.. up),
+ * expert e at gu_bank + e*gu_stride_bytes; ids [n_sel]; x [d_model] fp32
+ * (16-byte aligned); outputs qh [n_sel][d_ff] int8 (16-byte aligned),
+ * dh [n_sel][d_ff/32] fp32, sh [n_sel][d_ff/32] int32 (may be NULL).
+ * Optional (may be NULL) debug outputs: h_out [n_sel][d_ff] fp32 (16-byte
+ * aligned) and gu_out [n_sel][2*d_ff] fp32, the gate||up rows.
+ * d_model <= 4096, d_ff % 32 == 0.  A bad id is skipped (its outputs are
+ * left untouched) and reported through dev_status as in zq_dmmv_moe. */
+int zq_moe_gate_up(int wtype, const void *gu_bank, int64_t gu_stride_bytes, int64_t n_experts,
+                   int64_t d_model, int64_t d_ff, const int32_t *ids, int32_t n_sel,
+                   const float *x, int8_t *qh, float *dh, int32_t *sh, float *h_out,
+                   float *gu_out, int32_t *dev_status, void *stream);
+
+/* One token through the selected experts in two launches: zq_moe_gate_up
+ * (quantize x, gate||up rows, swiglu, re-quantize), then the down DMMV with
+ * the weighted sum over the selected experts fused in.  gu_bank: experts of [2*d_ff][d_model]
  * (rows 0..d_ff-1 gate, d_ff..2*d_ff-1 up); down_bank: [d_model][d_ff].
  * workspace: at least zq_moe_ffn_workspace_bytes(d_model, d_ff, n_sel) bytes,
  * 256-byte aligned.  y [d_model] (+)= sum_s wts[s] * down_s.

@@ -133,6 +133,13 @@ def test_other_argument_errors():
     assert moe(stride=100) == zq.ZQ_EINVAL
     assert moe(x_stride=48) == zq.ZQ_EINVAL
     assert moe(n_sel=-1) == zq.ZQ_EINVAL
+    # fused gate/up: model wider than 4096, missing outputs
+    assert L.zq_moe_gate_up(4, A, 8192 * 256 * 18 * 2, 9, 8192, 256, B, 9, C, D, D + 65536, None,
+                            None, None, None, None) == zq.ZQ_EINVAL
+    assert L.zq_moe_gate_up(4, A, 1024 * 64 * 18, 9, 2048, 512, B, 9, C, None, D, None, None,
+                            None, None, None) == zq.ZQ_ENULL
+    assert L.zq_moe_gate_up(4, A, 1024 * 64 * 18, 9, 2048, 512, B, 9, C, D + 4, D + 65536, None,
+                            None, None, None, None) == zq.ZQ_EALIGN
     # swiglu: f not a multiple of 32
     assert L.zq_swiglu_quantize(A, 9, 48, B, C, None, None, None) == zq.ZQ_EINVAL
     # moe_ffn: workspace too small

@@ -65,7 +65,7 @@ def test_route_against_oracle(zq):
 
 
 def run_chain(zq, banks, seed):
-    """Route -> quantize -> gather -> swiglu+quantize -> weighted down, each
+    """Route -> fused gate/up (+ swiglu + re-quantize) -> weighted down, each
     stage checked against the oracle on the GPU's previous output."""
     torch = torch_cuda()
     logits, g = inputs.gen_router(E_ROUTED, seed)
@@ -75,24 +75,19 @@ def run_chain(zq, banks, seed):
     assert np.array_equal(ids, rids)
     n_sel = ids.size
     ids_d, wts_d = dev(ids), dev(wts)
-
-    qx, dx, sx = quantize_gpu(zq, x)
-    rq, rd, rs = oracle.quantize_act(x)
-    assert np.array_equal(host(qx)[0], rq) and np.array_equal(host(dx)[0], rd)
-
-    gu = nan_f32(n_sel, 2 * D_FF)
-    status = sentinel_i32(1, value=0)
-    zq.zq_dmmv_moe(Q4, banks["gu_d"], N_EXPERTS, banks["gs"], 2 * D_FF, D_MODEL, ids_d, None,
-                   n_sel, qx, dx, sx, 0, 0, gu, 0, status)
-    gu_h = host(gu)
-    gu_ref, gu_S = oracle.moe_gate_up(Q4, banks["gu"], banks["gs"], D_MODEL, D_FF, ids, rq, rd)
-    check_rows(gu_h, gu_ref, gu_S, "moe gate/up gather")
+    rq, rd, _ = oracle.quantize_act(x)
 
     qh = torch.zeros((n_sel, D_FF), dtype=torch.int8, device="cuda")
     dh = nan_f32(n_sel, D_FF // 32)
     sh = sentinel_i32(n_sel, D_FF // 32)
     h = nan_f32(n_sel, D_FF)
-    zq.zq_swiglu_quantize(gu, n_sel, D_FF, qh, dh, sh, h)
+    gu = nan_f32(n_sel, 2 * D_FF)
+    status = sentinel_i32(1, value=0)
+    zq.zq_moe_gate_up(Q4, banks["gu_d"], banks["gs"], N_EXPERTS, D_MODEL, D_FF, ids_d, n_sel,
+                      dev(x), qh, dh, sh, h, gu, status)
+    gu_h = host(gu)
+    gu_ref, gu_S = oracle.moe_gate_up(Q4, banks["gu"], banks["gs"], D_MODEL, D_FF, ids, rq, rd)
+    check_rows(gu_h, gu_ref, gu_S, "moe fused gate/up rows")
     h_h = host(h)
     h_ref = oracle.swiglu(gu_h, D_FF)  # on the GPU's own gate/up rows
     assert np.allclose(h_h, h_ref, rtol=1e-6, atol=0)
@@ -110,6 +105,33 @@ def run_chain(zq, banks, seed):
     check_rows(y_h, y_ref, S, "moe weighted down")
     assert int(host(status)[0]) == 0
     return dict(x=x, ids=ids, wts=wts, ids_d=ids_d, wts_d=wts_d, y=y_h, rw=rw)
+
+
+def test_moe_gather_and_swiglu_kernels(zq, banks):
+    """The standalone expert gather DMMV and swiglu + quantize kernels."""
+    torch = torch_cuda()
+    logits, g = inputs.gen_router(E_ROUTED, 4321)
+    ids, _ = oracle.moe_route(logits, TOP_K, g)
+    n_sel = ids.size
+    x = inputs.gen_activation(1, D_MODEL, 4322)
+    qx, dx, sx = quantize_gpu(zq, x)
+    rq, rd, _ = oracle.quantize_act(x)
+    gu = nan_f32(n_sel, 2 * D_FF)
+    zq.zq_dmmv_moe(Q4, banks["gu_d"], N_EXPERTS, banks["gs"], 2 * D_FF, D_MODEL, dev(ids), None,
+                   n_sel, qx, dx, sx, 0, 0, gu)
+    gu_h = host(gu)
+    gu_ref, gu_S = oracle.moe_gate_up(Q4, banks["gu"], banks["gs"], D_MODEL, D_FF, ids, rq, rd)
+    check_rows(gu_h, gu_ref, gu_S, "moe gather")
+    qh = torch.zeros((n_sel, D_FF), dtype=torch.int8, device="cuda")
+    dh = nan_f32(n_sel, D_FF // 32)
+    sh = sentinel_i32(n_sel, D_FF // 32)
+    h = nan_f32(n_sel, D_FF)
+    zq.zq_swiglu_quantize(gu, n_sel, D_FF, qh, dh, sh, h)
+    h_h = host(h)
+    assert np.allclose(h_h, oracle.swiglu(gu_h, D_FF), rtol=1e-6, atol=0)
+    rqh, rdh, rsh = oracle.quantize_act(h_h)
+    assert np.array_equal(host(qh), rqh) and np.array_equal(host(dh), rdh)
+    assert np.array_equal(host(sh), rsh)
 
 
 @pytest.mark.parametrize("s", [0, 1, 2])
@@ -133,6 +155,26 @@ def test_moe_chain_and_composite(zq, banks, s):
     zq.zq_moe_ffn(Q4, banks["gu_d"], banks["gs"], banks["down_d"], banks["ds"], N_EXPERTS, D_MODEL,
                   D_FF, c["ids_d"], c["wts_d"], n_sel, dev(c["x"]), ws, ws_bytes, y, 1)
     assert np.allclose(host(y), 2 * prev, rtol=1e-6, atol=0)
+
+
+@pytest.mark.parametrize("d_model,d_ff,n_sel", [(5120, 64, 3), (256, 96, 17), (64, 32, 1)])
+def test_moe_ffn_other_shapes(zq, d_model, d_ff, n_sel):
+    """A model wider than the fused gate/up kernel takes (the separate
+    quantize / gather / swiglu path), more than 16 selected experts (two
+    chunks of down windows), and the smallest shapes."""
+    torch = torch_cuda()
+    E = n_sel + 2
+    gu, gs, down, ds = inputs.moe_banks(777 + d_model, E, d_model, d_ff)
+    ids = np.random.default_rng(d_ff).permutation(E)[:n_sel].astype(np.int32)
+    wts = np.random.default_rng(d_ff + 1).uniform(0.1, 1.0, n_sel).astype(np.float32)
+    x = inputs.gen_activation(1, d_model, 778)
+    ws_bytes = zq.zq_moe_ffn_workspace_bytes(d_model, d_ff, n_sel)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    y = nan_f32(d_model)
+    zq.zq_moe_ffn(Q4, dev(gu), gs, dev(down), ds, E, d_model, d_ff, dev(ids), dev(wts), n_sel,
+                  dev(x), ws, ws_bytes, y)
+    y_ref, S = oracle.moe_ffn(Q4, gu, gs, down, ds, d_model, d_ff, ids, wts.astype(np.float64), x)
+    check_rows(host(y), y_ref, S, "moe %dx%d n_sel=%d" % (d_model, d_ff, n_sel), tol=1e-3)
 
 
 def test_moe_bad_expert_id_is_skipped_and_reported(zq, banks):
