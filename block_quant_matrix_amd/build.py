@@ -31,10 +31,16 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 
+# Per-source extra flags.  The GEMM's MFMA results feed VALU code right away;
+# the VGPR form of the MFMA saves one v_accvgpr_read per result element.
+EXTRA = {
+    "gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)

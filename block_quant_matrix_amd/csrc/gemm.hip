@@ -3,19 +3,30 @@
 //
 //   Y[m][n] (+)= sum_b dx[m][b] * d_w[n][b] * isum(m, n, b)
 //
-// Each workgroup (4 waves) owns a 64 (tokens) x 64 (weight rows) tile; each
-// wave a 32 x 32 quarter = 2 x 2 tiles of v_mfma_i32_16x16x32_i8.  The K
-// step of that instruction is exactly one 32-element block, so every block's
-// integer sum comes out of the matrix core on its own and is rescaled in fp32
-// (convert, d_x*d_w, FMA) before the next block: a K=64 form would add two
-// blocks with different scales.
+// One v_mfma_i32_16x16x32_i8 covers exactly one 32-element block of one
+// 16 (tokens) x 16 (weight rows) tile, so every block's integer sum leaves
+// the matrix core on its own and is rescaled in fp32 (convert, d_x*d_w,
+// FMA) before the next block; a K=64 form would add two blocks with
+// different scales.  The matrix cores finish a tile's block in about 20
+// cycles, the 12 VALU operations of its rescale take longer: the epilogue,
+// not the MFMA, bounds this kernel, so the layout below is chosen to keep
+// every other cost (LDS traffic, staging, idle CUs) under it.
 //
-// K is staged through LDS four blocks at a time, double-buffered: activation
+// Workgroup tile: 128 tokens x 80 weight rows, 8 waves.  For the prefill
+// shape (512 x 5120) that is 4 x 64 = 256 tiles, one per CU of the chip, so
+// no CU runs a second tile while others idle.  The waves split K: waves 0-3
+// take blocks 0-1 of every 4-block stage, waves 4-7 blocks 2-3; each wave
+// owns 32 tokens x 80 rows (2 x 5 MFMA tiles).  The two K halves are added
+// through LDS at the end.
+//
+// Staging: every stage (4 blocks) is loaded from global memory into
+// registers one stage ahead and written to LDS double-buffered.  Activation
 // codes are copied as they are; weight blocks are unpacked once per tile to
-// signed int8 (Q4_0: nib - 8 via (nib + 0x78) ^ 0x80 per byte) so the unpack
-// is amortized over the 64 tokens of the tile.  Tiles are assigned so that
-// consecutive workgroups on one XCD walk all token tiles of the same weight
-// rows (L2 reuse of the weight slice).
+// signed int8 (Q4_0: nib - 8 via (nib + 0x78) ^ 0x80 per byte).  In LDS a
+// row is laid out [lane group g][block][8 bytes], so one 16-byte read gives
+// a lane its MFMA fragment (k = 8g..8g+7) for two consecutive blocks.
+// Tiles are ordered so that each XCD walks all token tiles of a contiguous
+// range of weight rows (L2 reuse of that weight slice).
 #include "zq_common.h"
 #include "zq_internal.h"
 
@@ -23,14 +34,33 @@ namespace zq {
 
 namespace {
 
-constexpr int BM = 64;
-constexpr int BN = 64;
-constexpr int KB = 4;                       // blocks per stage
-constexpr int ROWB = KB * 32 + 16;          // LDS row stride (bytes), padded
-constexpr int A_BYTES = BM * ROWB;
-constexpr int B_BYTES = BN * ROWB;
+constexpr int BM = 128;                 // tokens per tile
+constexpr int BN = 80;                  // weight rows per tile
+constexpr int KB = 4;                   // blocks per stage
+constexpr int NT = 512;                 // threads (8 waves)
+constexpr int MS = 2;                   // 16-token subtiles per wave
+constexpr int NS = BN / 16;             // 16-row subtiles per wave (5)
+constexpr int ROWB = KB * 32 + 16;      // LDS bytes per row: [g][kb][8] + pad
+constexpr int A_OFF = 0;
+constexpr int B_OFF = A_OFF + BM * ROWB;
+// The weight region has BM rows although only BN are read: threads of rows
+// BN..BM-1 store their (clamped, unused) copy there, which keeps the staging
+// code free of divergent branches.
+constexpr int DX_OFF = B_OFF + BM * ROWB;      // float [KB][BM]
+constexpr int DW_OFF = DX_OFF + KB * BM * 4;   // float [BM][KB]
+constexpr int STAGE_BYTES = DW_OFF + BM * KB * 4;
+static_assert(BM * KB == NT, "one activation (row, block) per thread");
+static_assert(BN <= BM, "weight rows fit the staging grid");
+constexpr int RING = 2;                 // stages of global loads in flight
+constexpr bool kInterleave = false;     // MFMA / rescale interleaving hints
+static_assert(RING % 2 == 0, "the LDS double buffer alternates with the unrolled ring");
+// More than half of the CU's 160 KB, so a CU never holds two tiles while
+// another CU idles.
+constexpr int LDS_BYTES = 2 * STAGE_BYTES > 82 * 1024 ? 2 * STAGE_BYTES : 82 * 1024;
+static_assert(4 * MS * NS * 4 * 64 * 4 <= 2 * STAGE_BYTES, "K-split exchange fits in LDS");
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 struct GemmArgs {
   const uint8_t *w;
@@ -46,79 +76,151 @@ struct GemmArgs {
   uint32_t flags;
 };
 
+template <int WT>
 struct StageRegs {
-  u32x4 a0, a1;     // 32 activation bytes
-  float dxv;        // activation scale of (row, block)
-  uint32_t wq[8];   // 32 unpacked weight bytes (signed int8)
-  float dwv;        // weight scale of (row, block)
+  u32x4 a0, a1;                // 32 activation bytes of (row, block)
+  float dxv;                   // its scale
+  uint32_t w[Blk<WT>::NW];     // weight window of (row, block), raw
+  uint32_t o;                  // byte offset of the block inside the window
+  bool a_ok, b_ok;             // block index < nb
 };
 
+// Every thread issues the same loads for every stage (rows and blocks past
+// the end are clamped to valid addresses and zeroed at the LDS store), so the
+// number of loads in flight is the same on every path and the compiler can
+// wait for the oldest stage only.
 template <int WT>
 __device__ __forceinline__ void load_stage(const GemmArgs &g, int64_t m0, int64_t n0, int kb0,
-                                           StageRegs &r) {
+                                           StageRegs<WT> &r) {
   const int t = static_cast<int>(threadIdx.x);
-  const int row = t >> 2;     // 0..63
-  const int blk = t & 3;      // 0..3
+  const int row = t >> 2;
+  const int blk = t & 3;
   const int b = kb0 + blk;
   const bool bok = b < g.nb;
   const int bc = bok ? b : g.nb - 1;
-  // activation: token row m0+row, block b
   int64_t mr = m0 + row;
   mr = mr < g.m_end ? mr : g.m_end - 1;
   const int8_t *ap = g.qx + mr * g.k + static_cast<int64_t>(bc) * 32;
   r.a0 = *reinterpret_cast<const u32x4 *>(ap);
   r.a1 = *reinterpret_cast<const u32x4 *>(ap + 16);
-  r.dxv = bok ? g.dx[mr * g.nb + bc] : 0.0f;
-  // weight: row n0+row, block b
-  int64_t nr = n0 + row;
+  r.dxv = g.dx[mr * g.nb + bc];
+  r.a_ok = bok;
+  int64_t nr = n0 + (row < BN ? row : BN - 1);
   nr = nr < g.n_end ? nr : g.n_end - 1;
-  uint32_t w[Blk<WT>::NW];
-  const uint32_t o = load_window<WT>(g.w + nr * g.row_bytes + static_cast<int64_t>(bc) * Blk<WT>::BYTES, w);
-  const uint32_t sel = quant_selector(o);
-  r.dwv = bok ? window_scale(w[0], o) : 0.0f;
-  if constexpr (WT == ZQ_Q4_0) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t p = __builtin_amdgcn_perm(w[q + 1], w[q], sel);
-      r.wq[q] = ((p & 0x0F0F0F0Fu) + 0x78787878u) ^ 0x80808080u;
-      r.wq[4 + q] = (((p >> 4) & 0x0F0F0F0Fu) + 0x78787878u) ^ 0x80808080u;
-    }
-  } else {
-#pragma unroll
-    for (int q = 0; q < 8; ++q) r.wq[q] = __builtin_amdgcn_perm(w[q + 1], w[q], sel);
-  }
-  if (!bok) {
-    r.a0 = u32x4{0, 0, 0, 0};
-    r.a1 = u32x4{0, 0, 0, 0};
-#pragma unroll
-    for (int q = 0; q < 8; ++q) r.wq[q] = 0;
-  }
+  r.o = load_window<WT>(g.w + nr * g.row_bytes + static_cast<int64_t>(bc) * Blk<WT>::BYTES, r.w);
+  r.b_ok = bok;
 }
 
-__device__ __forceinline__ void store_stage(uint8_t *lds, const StageRegs &r) {
+// Blocks past nb (ragged K, padded stages) keep the clamped codes that were
+// loaded and get zero scales: d_x * d_w = 0 times a finite integer sum adds
+// an exact zero, so their codes need not be cleared.
+template <int WT>
+__device__ __forceinline__ void store_stage(uint8_t *lds, const StageRegs<WT> &r) {
   const int t = static_cast<int>(threadIdx.x);
   const int row = t >> 2;
   const int blk = t & 3;
-  uint8_t *A = lds;
-  uint8_t *B = lds + A_BYTES;
-  float *DX = reinterpret_cast<float *>(lds + A_BYTES + B_BYTES);
-  float *DW = DX + KB * BM;
-  *reinterpret_cast<u32x4 *>(A + row * ROWB + blk * 32) = r.a0;
-  *reinterpret_cast<u32x4 *>(A + row * ROWB + blk * 32 + 16) = r.a1;
-  *reinterpret_cast<u32x4 *>(B + row * ROWB + blk * 32) = u32x4{r.wq[0], r.wq[1], r.wq[2], r.wq[3]};
-  *reinterpret_cast<u32x4 *>(B + row * ROWB + blk * 32 + 16) =
-      u32x4{r.wq[4], r.wq[5], r.wq[6], r.wq[7]};
-  DX[blk * BM + row] = r.dxv;
-  DW[blk * BN + row] = r.dwv;
+  {
+    uint8_t *p = lds + A_OFF + row * ROWB + blk * 8;
+    *reinterpret_cast<u32x2 *>(p + 0) = u32x2{r.a0.x, r.a0.y};
+    *reinterpret_cast<u32x2 *>(p + 32) = u32x2{r.a0.z, r.a0.w};
+    *reinterpret_cast<u32x2 *>(p + 64) = u32x2{r.a1.x, r.a1.y};
+    *reinterpret_cast<u32x2 *>(p + 96) = u32x2{r.a1.z, r.a1.w};
+    reinterpret_cast<float *>(lds + DX_OFF)[blk * BM + row] = r.a_ok ? r.dxv : 0.0f;
+  }
+  {
+    uint32_t wq[8];
+    const uint32_t sel = quant_selector(r.o);
+    if constexpr (WT == ZQ_Q4_0) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t p = __builtin_amdgcn_perm(r.w[q + 1], r.w[q], sel);
+        wq[q] = ((p & 0x0F0F0F0Fu) + 0x78787878u) ^ 0x80808080u;
+        wq[4 + q] = (((p >> 4) & 0x0F0F0F0Fu) + 0x78787878u) ^ 0x80808080u;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) wq[q] = __builtin_amdgcn_perm(r.w[q + 1], r.w[q], sel);
+    }
+    uint8_t *p = lds + B_OFF + row * ROWB + blk * 8;
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi)
+      *reinterpret_cast<u32x2 *>(p + 32 * gi) = u32x2{wq[2 * gi], wq[2 * gi + 1]};
+    reinterpret_cast<float *>(lds + DW_OFF)[row * KB + blk] =
+        r.b_ok ? window_scale(r.w[0], r.o) : 0.0f;
+  }
 }
 
-constexpr int STAGE_BYTES = A_BYTES + B_BYTES + 2 * KB * 64 * 4;
+__device__ __forceinline__ int64_t as_i64(uint32_t lo, uint32_t hi) {
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
 
 template <int WT, bool ISUMS>
-__global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][STAGE_BYTES];
-  // XCD-aware tile order: workgroup ids go round-robin over the 8 XCDs; give
-  // each XCD a contiguous run of tiles that share weight rows.
+__device__ __forceinline__ void compute_stage(const GemmArgs &g, const uint8_t *S, int st, int64_t m0,
+                                              int64_t n0, int mp, int kb0, int lane,
+                                              float (&acc)[MS][NS][4]) {
+  const int l16 = lane & 15, lg = lane >> 4;
+  u32x4 af[MS], bf[NS];
+  float4 dxa[MS][2];
+  float2 dwb[NS];
+#pragma unroll
+  for (int ms = 0; ms < MS; ++ms) {
+    const int row = mp * 32 + ms * 16;
+    af[ms] = *reinterpret_cast<const u32x4 *>(S + A_OFF + (row + l16) * ROWB + lg * 32 + kb0 * 8);
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      dxa[ms][q] = *reinterpret_cast<const float4 *>(S + DX_OFF + ((kb0 + q) * BM + row + 4 * lg) * 4);
+  }
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    bf[j] = *reinterpret_cast<const u32x4 *>(S + B_OFF + (j * 16 + l16) * ROWB + lg * 32 + kb0 * 8);
+    dwb[j] = *reinterpret_cast<const float2 *>(S + DW_OFF + ((j * 16 + l16) * KB + kb0) * 4);
+  }
+  constexpr int NTILE = 2 * MS * NS;   // (block, token subtile, row subtile)
+  i32x4 is[NTILE];
+#pragma unroll
+  for (int t = 0; t < NTILE; ++t) {
+    const int q = t / (MS * NS), ms = (t / NS) % MS, j = t % NS;
+    const int64_t a = q == 0 ? as_i64(af[ms].x, af[ms].y) : as_i64(af[ms].z, af[ms].w);
+    const int64_t b = q == 0 ? as_i64(bf[j].x, bf[j].y) : as_i64(bf[j].z, bf[j].w);
+    const i32x4 z = {0, 0, 0, 0};
+    is[t] = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, b, z, 0, 0, 0);
+  }
+#pragma unroll
+  for (int t = 0; t < NTILE; ++t) {
+    const int q = t / (MS * NS), ms = (t / NS) % MS, j = t % NS;
+    if constexpr (ISUMS) {
+      const int blk = st * KB + kb0 + q;
+      const int64_t n = n0 + j * 16 + l16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t m = m0 + mp * 32 + ms * 16 + lg * 4 + r;
+        if (blk < g.nb && m < g.m_end && n < g.n_end)
+          g.isums[((m - g.m_begin) * (g.n_end - g.n_begin) + (n - g.n_begin)) * g.nb + blk] = is[t][r];
+      }
+    } else {
+      const float dxs[4] = {dxa[ms][q].x, dxa[ms][q].y, dxa[ms][q].z, dxa[ms][q].w};
+      const float dw = q == 0 ? dwb[j].x : dwb[j].y;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        acc[ms][j][r] = __builtin_fmaf(dxs[r] * dw, static_cast<float>(is[t][r]), acc[ms][j][r]);
+    }
+  }
+  if constexpr (!ISUMS && kInterleave) {
+    // Keep the matrix pipe busy while the VALU rescales older tiles: two
+    // MFMAs ahead, then one MFMA per tile's 12-op rescale.
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+#pragma unroll
+    for (int t = 0; t < NTILE - 2; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);
+  }
+}
+
+template <int WT, bool ISUMS>
+__global__ __launch_bounds__(NT) void gemm_kernel(const GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
   const int64_t tiles = static_cast<int64_t>(g.tiles_m) * g.tiles_n;
   int64_t id = blockIdx.x;
   if (tiles % 8 == 0) id = (id % 8) * (tiles / 8) + id / 8;
@@ -129,89 +231,73 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs g) {
 
   const int lane = static_cast<int>(threadIdx.x & 63);
   const int wv = static_cast<int>(threadIdx.x >> 6);
-  const int wm = wv & 1, wn = wv >> 1;
+  const int kh = wv >> 2;           // K half: blocks 2kh, 2kh+1 of each stage
+  const int mp = wv & 3;            // tokens mp*32 .. mp*32+31 of the tile
   const int l16 = lane & 15, lg = lane >> 4;
+  const int kb0 = 2 * kh;
 
-  float acc[2][2][4];
+  float acc[MS][NS][4];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < MS; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < NS; ++b)
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[a][b][r] = 0.0f;
 
+  // Stage s is loaded into register slot s % RING, RING stages ahead of the
+  // compute that consumes it, so RING stages of compute cover the latency of
+  // its global loads.
+  // The stage count is padded to a multiple of RING so that the unrolled
+  // loop body has no branch.  A stage past the end has all its blocks past
+  // nb: its loads are clamped to valid addresses and store_stage zeroes its
+  // codes and scales, so computing it adds exact zeros.
   const int n_stages = (g.nb + KB - 1) / KB;
-  StageRegs sr;
-  load_stage<WT>(g, m0, n0, 0, sr);
-  store_stage(lds[0], sr);
+  const int n_pad = (n_stages + RING - 1) / RING * RING;
+  StageRegs<WT> sr[RING];
+#pragma unroll
+  for (int p = 0; p < RING; ++p) load_stage<WT>(g, m0, n0, p * KB, sr[p]);
+  store_stage<WT>(lds, sr[0]);
+  load_stage<WT>(g, m0, n0, RING * KB, sr[0]);
   __syncthreads();
 
-  for (int st = 0; st < n_stages; ++st) {
-    const int cur = st & 1;
-    if (st + 1 < n_stages) load_stage<WT>(g, m0, n0, (st + 1) * KB, sr);
-    const uint8_t *A = lds[cur];
-    const uint8_t *B = lds[cur] + A_BYTES;
-    const float *DX = reinterpret_cast<const float *>(lds[cur] + A_BYTES + B_BYTES);
-    const float *DW = DX + KB * BM;
+  for (int st0 = 0; st0 < n_pad; st0 += RING) {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      int64_t af[2], bf[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        af[t] = *reinterpret_cast<const int64_t *>(A + (wm * 32 + t * 16 + l16) * ROWB + kb * 32 + lg * 8);
-        bf[t] = *reinterpret_cast<const int64_t *>(B + (wn * 32 + t * 16 + l16) * ROWB + kb * 32 + lg * 8);
-      }
-      float4 dxa[2];
-      float dwb[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        dxa[t] = *reinterpret_cast<const float4 *>(DX + kb * BM + wm * 32 + t * 16 + lg * 4);
-        dwb[t] = DW[kb * BN + wn * 32 + t * 16 + l16];
-      }
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          const i32x4 z = {0, 0, 0, 0};
-          const i32x4 is = __builtin_amdgcn_mfma_i32_16x16x32_i8(af[mt], bf[nt], z, 0, 0, 0);
-          if constexpr (ISUMS) {
-            const int b = st * KB + kb;
-            const int64_t n = n0 + wn * 32 + nt * 16 + l16;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int64_t m = m0 + wm * 32 + mt * 16 + lg * 4 + r;
-              if (b < g.nb && m < g.m_end && n < g.n_end)
-                g.isums[((m - g.m_begin) * (g.n_end - g.n_begin) + (n - g.n_begin)) * g.nb + b] = is[r];
-            }
-          } else {
-            const float dxs[4] = {dxa[mt].x, dxa[mt].y, dxa[mt].z, dxa[mt].w};
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              acc[mt][nt][r] =
-                  __builtin_fmaf(dxs[r] * dwb[nt], static_cast<float>(is[r]), acc[mt][nt][r]);
-          }
-        }
-      }
+    for (int p = 0; p < RING; ++p) {
+      const int st = st0 + p;
+      compute_stage<WT, ISUMS>(g, lds + (p & 1) * STAGE_BYTES, st, m0, n0, mp, kb0, lane, acc);
+      const int slot = (p + 1) % RING;
+      store_stage<WT>(lds + ((p + 1) & 1) * STAGE_BYTES, sr[slot]);
+      load_stage<WT>(g, m0, n0, (st + 1 + RING) * KB, sr[slot]);
+      __syncthreads();
     }
-    if (st + 1 < n_stages) store_stage(lds[cur ^ 1], sr);
-    __syncthreads();
   }
 
   if constexpr (!ISUMS) {
+    // Add the two K halves: the wave of half kh keeps token subtile ms = kh
+    // and hands the other one to its partner through LDS.
+    float *red = reinterpret_cast<float *>(lds);   // [mp][ms][NS*4][64]
+    auto slot = [&](int ms, int v) { return ((mp * MS + ms) * (NS * 4) + v) * 64 + lane; };
+    const int give = 1 - kh;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int j = 0; j < NS; ++j)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const int64_t n = n0 + wn * 32 + nt * 16 + l16;
+      for (int r = 0; r < 4; ++r) red[slot(give, j * 4 + r)] = give == 0 ? acc[0][j][r] : acc[1][j][r];
+    __syncthreads();
+    const int keep = kh;
+    const int64_t mbase = m0 + mp * 32 + keep * 16 + lg * 4;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int64_t m = m0 + wm * 32 + mt * 16 + lg * 4 + r;
-          if (m < g.m_end && n < g.n_end) {
-            float *yp = g.y + m * g.n + n;
-            *yp = (g.flags & ZQ_ACCUMULATE) ? *yp + acc[mt][nt][r] : acc[mt][nt][r];
-          }
+    for (int j = 0; j < NS; ++j) {
+      const int64_t n = n0 + j * 16 + l16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = (keep == 0 ? acc[0][j][r] : acc[1][j][r]) + red[slot(keep, j * 4 + r)];
+        const int64_t m = mbase + r;
+        if (m < g.m_end && n < g.n_end) {
+          float *yp = g.y + m * g.n + n;
+          *yp = (g.flags & ZQ_ACCUMULATE) ? *yp + v : v;
         }
       }
+    }
   }
 }
 
@@ -242,14 +328,14 @@ int launch_gemm(int wtype, const void *w, int64_t n, int64_t k, const int8_t *qx
   const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(g.tiles_m) * g.tiles_n);
   if (wtype == ZQ_Q4_0) {
     if (isums)
-      hipLaunchKernelGGL((gemm_kernel<ZQ_Q4_0, true>), dim3(grid), dim3(256), 0, stream, g);
+      hipLaunchKernelGGL((gemm_kernel<ZQ_Q4_0, true>), dim3(grid), dim3(NT), 0, stream, g);
     else
-      hipLaunchKernelGGL((gemm_kernel<ZQ_Q4_0, false>), dim3(grid), dim3(256), 0, stream, g);
+      hipLaunchKernelGGL((gemm_kernel<ZQ_Q4_0, false>), dim3(grid), dim3(NT), 0, stream, g);
   } else {
     if (isums)
-      hipLaunchKernelGGL((gemm_kernel<ZQ_Q8_0, true>), dim3(grid), dim3(256), 0, stream, g);
+      hipLaunchKernelGGL((gemm_kernel<ZQ_Q8_0, true>), dim3(grid), dim3(NT), 0, stream, g);
     else
-      hipLaunchKernelGGL((gemm_kernel<ZQ_Q8_0, false>), dim3(grid), dim3(256), 0, stream, g);
+      hipLaunchKernelGGL((gemm_kernel<ZQ_Q8_0, false>), dim3(grid), dim3(NT), 0, stream, g);
   }
   ZQ_LAUNCH_CHECK();
   return ZQ_OK;
