@@ -9,48 +9,6 @@ namespace {
 constexpr int kArgmaxThreads = 256;
 constexpr int kArgmaxMaxBlocks = 1024;
 
-struct ValIdx {
-  float v;
-  int32_t i;
-};
-
-// a beats b: larger value, or equal value at a lower index.
-__device__ __forceinline__ bool beats(float av, int32_t ai, float bv, int32_t bi) {
-  return av > bv || (av == bv && ai < bi);
-}
-
-__device__ __forceinline__ void wave_best(float &v, int32_t &i) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const float ov = __shfl_xor(v, m);
-    const int32_t oi = __shfl_xor(i, m);
-    if (beats(ov, oi, v, i)) {
-      v = ov;
-      i = oi;
-    }
-  }
-}
-
-// Best (value, index) of the 256-thread block, valid in thread 0.
-__device__ __forceinline__ void block_best(float &v, int32_t &i) {
-  __shared__ float sv[kArgmaxThreads / 64];
-  __shared__ int32_t si[kArgmaxThreads / 64];
-  wave_best(v, i);
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) {
-    sv[w] = v;
-    si[w] = i;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int k = 1; k < kArgmaxThreads / 64; ++k)
-      if (beats(sv[k], si[k], v, i)) {
-        v = sv[k];
-        i = si[k];
-      }
-  }
-}
-
 }  // namespace
 
 // Stage 1: each block scans a contiguous chunk and writes its best pair.
@@ -68,24 +26,35 @@ __global__ __launch_bounds__(kArgmaxThreads) void argmax_partial_kernel(const fl
       i = static_cast<int32_t>(k);
     }
   }
-  block_best(v, i);
+  block_best<kArgmaxThreads / 64>(v, i);
   if (threadIdx.x == 0) part[blockIdx.x] = ValIdx{v, i};
 }
 
-// Stage 2: one block reduces the partial pairs.
+// Stage 2: one block reduces the partial pairs.  Each thread issues the
+// loads of up to kFinalPer pairs before comparing any, so the pass costs one
+// memory latency rather than one per pair.
+constexpr int kFinalPer = 8;
+
 __global__ __launch_bounds__(kArgmaxThreads) void argmax_final_kernel(const ValIdx *__restrict__ part,
                                                                       int nparts,
                                                                       int32_t *__restrict__ out) {
   float v = -__builtin_inff();
   int32_t i = 0x7fffffff;
-  for (int k = threadIdx.x; k < nparts; k += kArgmaxThreads) {
-    const ValIdx p = part[k];
-    if (beats(p.v, p.i, v, i)) {
-      v = p.v;
-      i = p.i;
+  for (int base = 0; base < nparts; base += kArgmaxThreads * kFinalPer) {
+    ValIdx p[kFinalPer];
+#pragma unroll
+    for (int u = 0; u < kFinalPer; ++u) {
+      const int k = base + u * kArgmaxThreads + static_cast<int>(threadIdx.x);
+      p[u] = k < nparts ? part[k] : ValIdx{-__builtin_inff(), 0x7fffffff};
     }
+#pragma unroll
+    for (int u = 0; u < kFinalPer; ++u)
+      if (beats(p[u].v, p[u].i, v, i)) {
+        v = p[u].v;
+        i = p[u].i;
+      }
   }
-  block_best(v, i);
+  block_best<kArgmaxThreads / 64>(v, i);
   if (threadIdx.x == 0) *out = i;
 }
 
@@ -97,6 +66,13 @@ static int argmax_blocks(int64_t n) {
 }
 
 size_t argmax_workspace(int64_t n) { return sizeof(ValIdx) * static_cast<size_t>(argmax_blocks(n)); }
+
+int launch_argmax_final(const void *part, int nparts, int32_t *out_idx, hipStream_t stream) {
+  hipLaunchKernelGGL(argmax_final_kernel, dim3(1), dim3(kArgmaxThreads), 0, stream,
+                     static_cast<const ValIdx *>(part), nparts, out_idx);
+  ZQ_LAUNCH_CHECK();
+  return ZQ_OK;
+}
 
 int launch_argmax(const float *y, int64_t n, int32_t *out_idx, void *ws, hipStream_t stream) {
   const int nb = argmax_blocks(n);

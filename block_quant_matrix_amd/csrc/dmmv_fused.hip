@@ -15,12 +15,19 @@
 //   5. packed int8 dots per block, fp32 scaling, lane reduction, store.
 // The quantized activation can also be written out (by workgroup 0) so that
 // later products against the same input need not quantize again.
+//
+// Each wave walks row groups with a grid stride.  The decode shapes launch
+// one group per wave; the LM head (hundreds of thousands of rows) launches a
+// bounded grid so that every workgroup quantizes the activation once and then
+// streams several groups, and with ARGMAX every workgroup also keeps the best
+// (logit, row) pair of the rows it wrote and leaves it for the one-block
+// final argmax.
 #include "zq_common.h"
 #include "zq_internal.h"
 
 namespace zq {
 
-template <int WT, int LPR, int BPL, int RB, int WPB>
+template <int WT, int LPR, int BPL, int RB, int WPB, bool ARGMAX>
 __global__ __launch_bounds__(64 * WPB) void dmmv_f32x_kernel(const DmmvF32Args a) {
   constexpr int S = 64 / LPR;
   constexpr int NW = Blk<WT>::NW;
@@ -36,7 +43,10 @@ __global__ __launch_bounds__(64 * WPB) void dmmv_f32x_kernel(const DmmvF32Args a
   const int wv = tid >> 6;
   const int j = lane & (LPR - 1);
   const int slot = lane / LPR;
-  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * WPB + wv) * (RB * S);
+  const int64_t n_groups = (a.rows + RB * S - 1) / (RB * S);
+  const int64_t gstride = static_cast<int64_t>(gridDim.x) * WPB;
+  int64_t grp = static_cast<int64_t>(blockIdx.x) * WPB + wv;   // first row group of this wave
+  int64_t row0 = grp * (RB * S);
 
   // 1. activation loads for this thread's first block: two lanes per block,
   //    16 elements (four float4) each
@@ -119,37 +129,66 @@ __global__ __launch_bounds__(64 * WPB) void dmmv_f32x_kernel(const DmmvF32Args a
     }
   }
 
-  // 5. dots, scaling, reduction, store
-  float acc[RB];
+  // 5. dots, scaling, reduction, store; then the next row group
+  float best_v = -__builtin_inff();
+  int32_t best_i = 0x7fffffff;
+  for (;;) {
+    float acc[RB];
 #pragma unroll
-  for (int t = 0; t < RB; ++t) {
-    float p = 0.0f;
+    for (int t = 0; t < RB; ++t) {
+      float p = 0.0f;
 #pragma unroll
-    for (int i = 0; i < BPL; ++i) {
-      const float dw = window_scale(win[t][i][0], off[t][i]);
-      const uint32_t sel = quant_selector(off[t][i]);
-      int32_t isum;
-      if constexpr (WT == ZQ_Q4_0) {
-        isum = q4_raw_dot(win[t][i], sel, xq[i]) - xs8[i];
-      } else {
-        isum = q8_dot(win[t][i], sel, xq[i]);
+      for (int i = 0; i < BPL; ++i) {
+        const float dw = window_scale(win[t][i][0], off[t][i]);
+        const uint32_t sel = quant_selector(off[t][i]);
+        int32_t isum;
+        if constexpr (WT == ZQ_Q4_0) {
+          isum = q4_raw_dot(win[t][i], sel, xq[i]) - xs8[i];
+        } else {
+          isum = q8_dot(win[t][i], sel, xq[i]);
+        }
+        p = __builtin_fmaf(dw * xd[i], static_cast<float>(isum), p);
       }
-      p = __builtin_fmaf(dw * xd[i], static_cast<float>(isum), p);
+      acc[t] = p;
     }
-    acc[t] = p;
+    using R = RowReduce<LPR, RB>;
+    float res[R::NOUT];
+    R::run(acc, res);
+    if (R::writer(lane)) {
+#pragma unroll
+      for (int m = 0; m < R::NOUT; ++m) {
+        const int64_t row = row0 + static_cast<int64_t>(R::rowstep(m, lane)) * S + slot;
+        if (row < a.rows) {
+          float *yp = a.y + row;
+          const float v = (a.flags & ZQ_ACCUMULATE) ? *yp + res[m] : res[m];
+          *yp = v;
+          if constexpr (ARGMAX) {
+            if (beats(v, static_cast<int32_t>(row), best_v, best_i)) {
+              best_v = v;
+              best_i = static_cast<int32_t>(row);
+            }
+          }
+        }
+      }
+    }
+    grp += gstride;
+    if (grp >= n_groups) break;
+    row0 = grp * (RB * S);
+#pragma unroll
+    for (int t = 0; t < RB; ++t) {
+      int64_t row = row0 + t * S + slot;
+      row = row < a.rows ? row : a.rows - 1;
+#pragma unroll
+      for (int i = 0; i < BPL; ++i) {
+        int b = j + LPR * i;
+        b = b < a.nb ? b : a.nb - 1;
+        off[t][i] = load_window<WT>(a.w + row * a.row_bytes + static_cast<int64_t>(b) * BB, win[t][i]);
+      }
+    }
   }
-  using R = RowReduce<LPR, RB>;
-  float res[R::NOUT];
-  R::run(acc, res);
-  if (R::writer(lane)) {
-#pragma unroll
-    for (int m = 0; m < R::NOUT; ++m) {
-      const int64_t row = row0 + static_cast<int64_t>(R::rowstep(m, lane)) * S + slot;
-      if (row < a.rows) {
-        float *yp = a.y + row;
-        *yp = (a.flags & ZQ_ACCUMULATE) ? *yp + res[m] : res[m];
-      }
-    }
+  if constexpr (ARGMAX) {
+    block_best<WPB>(best_v, best_i);
+    if (threadIdx.x == 0) static_cast<ValIdx *>(a.part)[blockIdx.x] = ValIdx{best_v, best_i};
   }
 }
 
@@ -165,10 +204,18 @@ template <int WT, int LPR, int BPL, int RB, int WPB>
 int launch_f(const DmmvF32Args &a, hipStream_t stream) {
   constexpr int S = 64 / LPR;
   const int64_t rows_per_wg = static_cast<int64_t>(WPB) * RB * S;
-  const int64_t grid = (a.rows + rows_per_wg - 1) / rows_per_wg;
+  int64_t grid = (a.rows + rows_per_wg - 1) / rows_per_wg;
   const size_t lds = static_cast<size_t>(a.k) + 8 * static_cast<size_t>(a.nb);
-  hipLaunchKernelGGL((dmmv_f32x_kernel<WT, LPR, BPL, RB, WPB>), dim3(static_cast<unsigned>(grid)),
-                     dim3(64 * WPB), lds, stream, a);
+  if (a.part) {
+    if (grid > kArgmaxMaxParts) grid = kArgmaxMaxParts;
+    hipLaunchKernelGGL((dmmv_f32x_kernel<WT, LPR, BPL, RB, WPB, true>),
+                       dim3(static_cast<unsigned>(grid)), dim3(64 * WPB), lds, stream, a);
+    ZQ_LAUNCH_CHECK();
+    if (a.out_idx) return launch_argmax_final(a.part, static_cast<int>(grid), a.out_idx, stream);
+    return ZQ_OK;
+  }
+  hipLaunchKernelGGL((dmmv_f32x_kernel<WT, LPR, BPL, RB, WPB, false>),
+                     dim3(static_cast<unsigned>(grid)), dim3(64 * WPB), lds, stream, a);
   ZQ_LAUNCH_CHECK();
   return ZQ_OK;
 }
@@ -182,7 +229,9 @@ int launch_fs(const DmmvF32Args &a, hipStream_t stream) {
   // 1024-thread groups leave 128 VGPRs per wave: wide layouts use 8 waves.
   constexpr int WPB = BPL <= 2 ? 16 : 8;
   if (a.rows <= static_cast<int64_t>(256) * WPB * S) return launch_f<WT, LPR, BPL, 1, WPB>(a, stream);
-  if constexpr (BPL <= 2) return launch_f<WT, LPR, BPL, 4, 4>(a, stream);
+  // windows held per lane: RB * BPL
+  if constexpr (BPL == 1) return launch_f<WT, LPR, BPL, 8, 4>(a, stream);
+  if constexpr (BPL == 2) return launch_f<WT, LPR, BPL, 4, 4>(a, stream);
   return launch_f<WT, LPR, BPL, 2, 4>(a, stream);
 }
 

@@ -183,6 +183,31 @@ int zq_argmax_f32(const float *y, int64_t n, int32_t *out_idx, void *workspace,
   return zq::launch_argmax(y, n, out_idx, workspace, S(stream));
 }
 
+size_t zq_dmmv_f32_argmax_workspace_bytes(void) {
+  return sizeof(zq::ValIdx) * static_cast<size_t>(zq::kArgmaxMaxParts);
+}
+
+int zq_dmmv_f32_argmax(int wtype, const void *w, int64_t rows, int64_t k, const float *x, float *y,
+                       int32_t *out_idx, void *workspace, size_t workspace_bytes, void *stream) {
+  ZQ_REQUIRE(block_bytes(wtype) > 0, ZQ_EINVAL);
+  ZQ_REQUIRE(w && x && y && workspace, ZQ_ENULL);
+  ZQ_REQUIRE(rows >= 1 && rows <= INT32_MAX && k_ok(k) && k <= 16384, ZQ_EINVAL);
+  ZQ_REQUIRE(workspace_bytes >= zq_dmmv_f32_argmax_workspace_bytes(), ZQ_EINVAL);
+  ZQ_REQUIRE(al(w, 4) && al(x, 16) && al(y, 4) && al(out_idx, 4) && al(workspace, 8), ZQ_EALIGN);
+  const int dc = check_current_device();
+  if (dc != ZQ_OK) return dc;
+  zq::DmmvF32Args a{};
+  a.w = static_cast<const uint8_t *>(w);
+  a.x = x;
+  a.y = y;
+  a.part = workspace;
+  a.out_idx = out_idx;
+  a.rows = rows;
+  a.k = static_cast<int32_t>(k);
+  a.nb = static_cast<int32_t>(k / 32);
+  return zq::launch_dmmv_f32x(wtype, a, S(stream));
+}
+
 int zq_moe_route(const float *logits, int32_t n_routed, int32_t top_k, const float *shared_gate,
                  int32_t *ids, float *wts, void *stream) {
   ZQ_REQUIRE(logits && ids && wts, ZQ_ENULL);

@@ -264,6 +264,54 @@ __device__ __forceinline__ uint32_t quantize_block8(const float (&x)[4], float &
   return packed[0];
 }
 
+
+// ---------------------------------------------------------------- argmax --
+// A (value, index) pair; a beats b when its value is larger, or equal at a
+// lower index (ties go to the lowest index).
+struct ValIdx {
+  float v;
+  int32_t i;
+};
+
+__device__ __forceinline__ bool beats(float av, int32_t ai, float bv, int32_t bi) {
+  return av > bv || (av == bv && ai < bi);
+}
+
+// Best pair of the wave, valid in every lane.
+__device__ __forceinline__ void wave_best(float &v, int32_t &i) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const float ov = __shfl_xor(v, m);
+    const int32_t oi = __shfl_xor(i, m);
+    if (beats(ov, oi, v, i)) {
+      v = ov;
+      i = oi;
+    }
+  }
+}
+
+// Best pair of a workgroup of NWAVES waves, valid in thread 0.  Every thread
+// of the workgroup must call it.
+template <int NWAVES>
+__device__ __forceinline__ void block_best(float &v, int32_t &i) {
+  __shared__ float sv[NWAVES];
+  __shared__ int32_t si[NWAVES];
+  wave_best(v, i);
+  const int w = static_cast<int>(threadIdx.x >> 6);
+  if ((threadIdx.x & 63) == 0) {
+    sv[w] = v;
+    si[w] = i;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int k = 1; k < NWAVES; ++k)
+      if (beats(sv[k], si[k], v, i)) {
+        v = sv[k];
+        i = si[k];
+      }
+  }
+}
+
 }  // namespace zq
 
 // Host-side launch helpers.

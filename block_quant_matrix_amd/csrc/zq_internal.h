@@ -39,6 +39,8 @@ struct DmmvF32Args {
   int8_t *qx_out;       // optional copy of the quantized activation
   float *dx_out;
   int32_t *sx_out;
+  void *part;           // argmax partials, one (value, index) per workgroup, or null
+  int32_t *out_idx;     // argmax of y (needs part), or null
   int64_t rows;
   int64_t row_bytes;    // filled in by the launcher
   int32_t k;
@@ -46,7 +48,13 @@ struct DmmvF32Args {
   uint32_t flags;
 };
 
+// With a.part set, the launch is persistent (at most kArgmaxMaxParts
+// workgroups walk the row groups) and leaves one argmax partial per
+// workgroup; with a.out_idx also set, the final argmax follows.
+constexpr int kArgmaxMaxParts = 2048;
 int launch_dmmv_f32x(int wtype, DmmvF32Args a, hipStream_t stream);
+// Reduce nparts (value, index) partials to the argmax index.
+int launch_argmax_final(const void *part, int nparts, int32_t *out_idx, hipStream_t stream);
 
 // MoE gate/up pass fused with swiglu + re-quantization.
 struct MoeGateUpArgs {

@@ -37,6 +37,8 @@ SIGNATURES = {
     "zq_dmmv_isums": (_INT, [_INT, _P, _I64, _I64, _P, _P, _P, _P]),
     "zq_argmax_workspace_bytes": (_SZ, [_I64]),
     "zq_argmax_f32": (_INT, [_P, _I64, _P, _P, _SZ, _P]),
+    "zq_dmmv_f32_argmax_workspace_bytes": (_SZ, []),
+    "zq_dmmv_f32_argmax": (_INT, [_INT, _P, _I64, _I64, _P, _P, _P, _P, _SZ, _P]),
     "zq_moe_route": (_INT, [_P, _I32, _I32, _P, _P, _P, _P]),
     "zq_dmmv_moe": (_INT, [_INT, _P, _I64, _I64, _I64, _I64, _P, _P, _I32, _P, _P, _P, _I64,
                            _INT, _P, _U32, _P, _P]),
@@ -145,6 +147,15 @@ def zq_argmax_workspace_bytes(n: int) -> int:
 def zq_argmax_f32(y, n, out_idx, workspace, workspace_bytes, stream=None):
     return _call("zq_argmax_f32", ptr(y), n, ptr(out_idx), ptr(workspace), workspace_bytes,
                  _stream(stream))
+
+
+def zq_dmmv_f32_argmax_workspace_bytes() -> int:
+    return lib().zq_dmmv_f32_argmax_workspace_bytes()
+
+
+def zq_dmmv_f32_argmax(wtype, w, rows, k, x, y, out_idx, workspace, workspace_bytes, stream=None):
+    return _call("zq_dmmv_f32_argmax", wtype, ptr(w), rows, k, ptr(x), ptr(y), ptr(out_idx),
+                 ptr(workspace), workspace_bytes, _stream(stream))
 
 
 def zq_moe_route(logits, n_routed, top_k, shared_gate, ids, wts, stream=None):

@@ -115,6 +115,25 @@ size_t zq_argmax_workspace_bytes(int64_t n);
 int zq_argmax_f32(const float *y, int64_t n, int32_t *out_idx, void *workspace,
                   size_t workspace_bytes, void *stream);
 
+/* The LM-head step in two launches: y = W . Q(x) over all rows, exactly as
+ * zq_dmmv_f32 computes it (same codes, same rows, bit for bit), and out_idx
+ * = the argmax of y with ties to the lowest row ("argmax (exact)", "CUDA
+ * backend for ZINC", section 5; the vocab-output DMMV, "Как мы запустили
+ * 35B LLM на видеокарте за $500", section "Утилизация полосы памяти по
+ * операциям").  The DMMV launch is persistent: each workgroup quantizes the
+ * activation once, walks several row groups and leaves the best (logit,
+ * row) pair it wrote; one block then reduces those pairs.  k <= 16384 as
+ * for zq_dmmv_f32.  x [k] fp32 16-byte aligned; y [rows] fp32 (written,
+ * never accumulated); out_idx: one int32, or NULL to produce y only (one
+ * launch; the partials are still written to the workspace).  workspace:
+ * device scratch of at least zq_dmmv_f32_argmax_workspace_bytes() bytes,
+ * 8-byte aligned, owned by the caller; its contents are undefined
+ * afterwards.  1 <= rows <= INT32_MAX.  ZQ_EINVAL for k out of range or a
+ * small workspace; nothing is launched then. */
+size_t zq_dmmv_f32_argmax_workspace_bytes(void);
+int zq_dmmv_f32_argmax(int wtype, const void *w, int64_t rows, int64_t k, const float *x, float *y,
+                       int32_t *out_idx, void *workspace, size_t workspace_bytes, void *stream);
+
 /* MoE router ("softmax_topk", "Bringing ZINC to NVIDIA", section "The roadmap:
  * from 70 to a coherent token"; "CUDA backend for ZINC", section 5): the
  * top_k largest of n_routed logits, largest first, ties to the lower id;

@@ -65,6 +65,28 @@ def test_workspace_sizes():
     ws = L.zq_moe_ffn_workspace_bytes(2048, 512, 9)
     assert ws >= 2048 + 9 * 1024 * 4 + 9 * 512 and ws % 256 == 0
     assert L.zq_moe_ffn_workspace_bytes(0, 512, 9) == 0
+    assert L.zq_dmmv_f32_argmax_workspace_bytes() == 8 * 2048
+
+
+def test_lmhead_argument_errors():
+    L = zq.lib()
+    ws = L.zq_dmmv_f32_argmax_workspace_bytes()
+
+    def rc(wtype=4, w=A, rows=248320, k=2048, x=B, y=C, out=D, work=A + 0x8000, wsb=ws):
+        return L.zq_dmmv_f32_argmax(wtype, w, rows, k, x, y, out, work, wsb, None)
+
+    assert rc(wtype=5) == zq.ZQ_EINVAL
+    assert rc(rows=0) == zq.ZQ_EINVAL
+    assert rc(rows=1 << 31) == zq.ZQ_EINVAL
+    assert rc(k=2047) == zq.ZQ_EINVAL
+    assert rc(k=16384 + 32) == zq.ZQ_EINVAL
+    assert rc(wsb=ws - 8) == zq.ZQ_EINVAL
+    assert rc(x=None) == zq.ZQ_ENULL
+    assert rc(y=None) == zq.ZQ_ENULL
+    assert rc(work=None) == zq.ZQ_ENULL
+    assert rc(x=B + 4) == zq.ZQ_EALIGN
+    assert rc(work=A + 0x8004) == zq.ZQ_EALIGN
+    assert rc(y=C + 2) == zq.ZQ_EALIGN
 
 
 def rc_dmmv_q4(**kw):
@@ -155,4 +177,11 @@ def test_other_argument_errors():
 def test_valid_arguments_without_gpu_report_no_device():
     """With every argument valid, the last check is the device: no GPU here."""
     assert rc_dmmv_q4() == zq.ZQ_EDEVICE
+    L = zq.lib()
+    assert L.zq_dmmv_f32_argmax(4, A, 248320, 2048, B, C, D, A + 0x8000,
+                                L.zq_dmmv_f32_argmax_workspace_bytes(), None) == zq.ZQ_EDEVICE
+    assert L.zq_dmmv_f32_argmax(8, A, 7, 8192, B, C, D, A + 0x8000,
+                                L.zq_dmmv_f32_argmax_workspace_bytes(), None) == zq.ZQ_EDEVICE
+    assert L.zq_dmmv_f32_argmax(4, A, 7, 64, B, C, None, A + 0x8000,
+                                L.zq_dmmv_f32_argmax_workspace_bytes(), None) == zq.ZQ_EDEVICE
     assert zq.lib().zq_device_check(0) == zq.ZQ_EDEVICE

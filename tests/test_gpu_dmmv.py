@@ -330,3 +330,100 @@ def test_workload_lmhead_full_and_argmax(zq):
         assert idx == i1
     else:
         assert y_ref[i1] - y_ref[idx] <= 1e-4 * (S[i1] + S[idx])
+
+
+# ------------------------------------------- LM head in two launches -------
+
+def lmhead_gpu(zq, wt, w_dev, rows, k, x_np):
+    """zq_dmmv_f32_argmax on one activation: (y, idx) on the host."""
+    torch = torch_cuda()
+    ws_bytes = zq.zq_dmmv_f32_argmax_workspace_bytes()
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    y = nan_f32(rows)
+    out = sentinel_i32(1)
+    zq.zq_dmmv_f32_argmax(wt, w_dev, rows, k, dev(x_np.astype(np.float32).ravel()), y, out, ws,
+                          ws_bytes)
+    return host(y), int(host(out)[0])
+
+
+def fused_rows(zq, wt, w_dev, rows, k, x_np):
+    y = nan_f32(rows)
+    zq.zq_dmmv_f32(wt, w_dev, rows, k, dev(x_np.astype(np.float32).ravel()), y)
+    return host(y)
+
+
+@pytest.mark.parametrize("wtype", [Q4, Q8])
+@pytest.mark.parametrize("rows,k", [(1, 32), (7, 96), (1000, 2048), (4097, 2080), (300, 8192),
+                                    (70000, 256), (5000, 16384)])
+def test_lmhead_fused_small(zq, wtype, rows, k):
+    """y equals zq_dmmv_f32's rows bit for bit (the same kernel, whose
+    workgroups here walk several row groups) and the oracle's within the
+    bar; the index is the exact argmax of those logits."""
+    seed = 77 + rows + k + wtype
+    w = inputs.gen_weights(wtype, rows, k, seed)
+    x = inputs.gen_activation(1, k, seed + 1)
+    wd = dev(w)
+    y, idx = lmhead_gpu(zq, wtype, wd, rows, k, x)
+    y_f = fused_rows(zq, wtype, wd, rows, k, x)
+    assert np.array_equal(y.view(np.uint32), y_f.view(np.uint32))
+    rq, rd, _ = oracle.quantize_act(x)
+    y_ref, S = oracle.dmmv(wtype, w, rows, k, rq, rd)
+    check_rows(y, y_ref, S, "lmhead %d x %d" % (rows, k))
+    assert idx == oracle.argmax_f32(y)
+
+
+def test_lmhead_fused_ties_and_ends(zq):
+    """Equal logits resolve to the lowest row, across workgroups too; the
+    maximum at the first and at the last row is found."""
+    rows, k = 9000, 64
+    base = inputs.gen_weights(Q4, 1, k, 5).ravel()  # one 36-byte row
+    x = inputs.gen_activation(1, k, 6)
+    rq, rd, _ = oracle.quantize_act(x)
+    # every row identical -> all logits equal -> row 0
+    w = np.tile(base, rows)
+    y, idx = lmhead_gpu(zq, Q4, dev(w), rows, k, x)
+    assert np.all(y == y[0]) and idx == 0
+    # rows with all-zero scales give 0; one row copies base with a positive
+    # logit: place it (and a tie) at chosen rows
+    y1, _ = oracle.dmmv(Q4, base, 1, k, rq, rd)
+    sign = 1.0 if y1[0] > 0 else -1.0
+    zero_row = base.copy().reshape(2, 18)
+    zero_row[:, 0:2] = 0                           # fp16 scale 0 in both blocks
+    neg = base.copy().reshape(2, 18)
+    if sign < 0:                                   # flip to a positive logit: negate scales
+        for b in range(2):
+            d = np.frombuffer(neg[b, 0:2].tobytes(), np.float16)[0]
+            neg[b, 0:2] = np.frombuffer(np.float16(-d).tobytes(), np.uint8)
+    pos = neg.ravel()
+    for rows_at in ([0], [rows - 1], [4500, 8999], [123, 124, 8000]):
+        w = np.tile(zero_row.ravel(), rows)
+        for r in rows_at:
+            w[r * 36:(r + 1) * 36] = pos
+        y, idx = lmhead_gpu(zq, Q4, dev(w), rows, k, x)
+        assert y[rows_at[0]] > 0
+        assert idx == min(rows_at), rows_at
+
+
+def test_workload_lmhead_two_launch_full(zq):
+    """248320 x 2048 Q4_0 through zq_dmmv_f32_argmax: the same logits as
+    zq_dmmv_f32, bit for bit, the oracle's within the bar, and the exact
+    argmax of them."""
+    cfg = inputs.WORKLOADS[3]
+    wt, rows, k = cfg["wtype"], cfg["rows"], cfg["k"]
+    w = inputs.gen_weights(wt, rows, k, inputs.seed_for(3))
+    x = inputs.gen_activation(1, k, inputs.seed_for(3) + 1)
+    wd = dev(w)
+    y, idx = lmhead_gpu(zq, wt, wd, rows, k, x)
+    y_f = fused_rows(zq, wt, wd, rows, k, x)
+    assert np.array_equal(y.view(np.uint32), y_f.view(np.uint32))
+    rq, rd, _ = oracle.quantize_act(x)
+    y_ref, S = oracle.dmmv(wt, w, rows, k, rq, rd)
+    check_rows(y, y_ref, S, cfg["name"] + " two-launch")
+    assert idx == oracle.argmax_f32(y)
+    # out_idx = NULL: the logits alone, identical
+    torch = torch_cuda()
+    ws_bytes = zq.zq_dmmv_f32_argmax_workspace_bytes()
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    y2 = nan_f32(rows)
+    zq.zq_dmmv_f32_argmax(wt, wd, rows, k, dev(x.ravel()), y2, None, ws, ws_bytes)
+    assert np.array_equal(host(y2).view(np.uint32), y.view(np.uint32))
