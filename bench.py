@@ -178,8 +178,9 @@ class DmmvWorkload(Workload):
 
 
 class MoeWorkload(Workload):
-    """Router + one token through 8 routed + 1 shared Q4_0 experts."""
-    dominant_name = "moe_gate_up_kernel"
+    """Router + one token through 8 routed + 1 shared Q4_0 experts, in two
+    launches: gate/up with the router folded in, then down."""
+    dominant_name = "moe_gate_up_kernel (router folded in)"
     steps = 2000
     warmup = 100
 
@@ -193,9 +194,10 @@ class MoeWorkload(Workload):
         self.gu_w = self.n_sel * 2 * self.dff * (self.dm // 32) * bb
         self.down_w = self.n_sel * self.dm * (self.dff // 32) * bb
         self.step_bytes = self.gu_w + self.down_w + 4 * self.dm + 4 * self.dm
-        # fused gate/up pass: weights + fp32 x in + quantized h out (codes, scales, sums)
-        self.gate_up_bytes = (self.gu_w + 4 * self.dm + self.n_sel * self.dff +
-                              8 * self.n_sel * (self.dff // 32))
+        # fused gate/up pass: weights + fp32 x + router logits in, quantized h
+        # out (codes, scales, sums) + the expert list and weights
+        self.gate_up_bytes = (self.gu_w + 4 * self.dm + 4 * self.E + self.n_sel * self.dff +
+                              8 * self.n_sel * (self.dff // 32) + 8 * self.n_sel)
 
     def setup(self, torch, zq, inputs):
         self.torch, self.zq = torch, zq
@@ -225,24 +227,22 @@ class MoeWorkload(Workload):
         self.dh = torch.empty((self.n_sel, self.dff // 32), dtype=torch.float32, device="cuda")
         self.sh = torch.empty((self.n_sel, self.dff // 32), dtype=torch.int32, device="cuda")
 
-    def _route(self, i):
-        j = i % self.logits.shape[0]
-        self.zq.zq_moe_route(self.logits[j], self.E, self.top_k, self.gates[j:j + 1], self.ids,
-                             self.wts)
-
     def step(self, i):
         gu, down = self.banks[i % self.ncopy]
-        self._route(i)
-        self.zq.zq_moe_ffn(4, gu, self.gs, down, self.ds, self.E + 1, self.dm, self.dff, self.ids,
-                           self.wts, self.n_sel, self.x, self.ws, self.ws_bytes, self.y)
+        j = i % self.logits.shape[0]
+        self.zq.zq_moe_ffn_route(4, gu, self.gs, down, self.ds, self.E + 1, self.dm, self.dff,
+                                 self.logits[j], self.E, self.top_k, self.gates[j:j + 1], self.x,
+                                 self.ids, self.wts, self.ws, self.ws_bytes, self.y)
 
     def prepare_dominant(self):
-        self._route(0)
+        pass
 
     def dominant(self, i):
         gu, _ = self.banks[i % self.ncopy]
-        self.zq.zq_moe_gate_up(4, gu, self.gs, self.E + 1, self.dm, self.dff, self.ids, self.n_sel,
-                               self.x, self.qh, self.dh, self.sh)
+        j = i % self.logits.shape[0]
+        self.zq.zq_moe_gate_up_route(4, gu, self.gs, self.E + 1, self.dm, self.dff, self.logits[j],
+                                     self.E, self.top_k, self.gates[j:j + 1], self.x, self.ids,
+                                     self.wts, self.qh, self.dh, self.sh)
 
     def value(self, ms):
         return self.step_bytes / (ms * 1e-3) / 1e9, "GB/s"

@@ -89,14 +89,8 @@ int launch_argmax(const float *y, int64_t n, int32_t *out_idx, void *ws, hipStre
 
 // ------------------------------------------------------------- router -----
 
-// Rank selection.  Each logit's rank is the number of logits that beat it
-// (larger, or equal at a lower id); the top_k experts are the logits of rank
-// < top_k, stored at their rank, so they come out largest first with ties
-// to the lower id.  P threads share one logit's comparisons (logits staged
-// in LDS and read as broadcasts) and add their partial counts with DPP.  The
-// softmax over the selected logits is evaluated in fp64 (each of the top_k
-// exponentials by its own thread, the normalizer summed in rank order), as
-// is the shared expert's sigmoid.
+// The router: rank selection and fp64 softmax (route_rank, route_weights in
+// zq_common.h) in one workgroup.
 template <int P>
 __global__ __launch_bounds__(1024) void moe_route_kernel(const float *__restrict__ logits,
                                                          int32_t n_routed, int32_t top_k,
@@ -110,41 +104,9 @@ __global__ __launch_bounds__(1024) void moe_route_kernel(const float *__restrict
   const int t = static_cast<int>(threadIdx.x);
   for (int i = t; i < n_routed; i += static_cast<int>(blockDim.x)) lv[i] = logits[i];
   __syncthreads();
-  const int n_groups = static_cast<int>(blockDim.x) / P;
-  const int part = t & (P - 1);
-  for (int e0 = 0; e0 < n_routed; e0 += n_groups) {  // uniform trip count
-    const int e = e0 + t / P;
-    const bool ok = e < n_routed;
-    const float v = ok ? lv[e] : 0.0f;
-    float cnt = 0.0f;  // exact small integers
-    if (ok) {
-      for (int j = part; j < n_routed; j += P) {
-        const float u = lv[j];
-        cnt += (u > v || (u == v && j < e)) ? 1.0f : 0.0f;
-      }
-    }
-    cnt = group_sum<P>(cnt);
-    if (ok && part == 0) {
-      const int rank = static_cast<int>(cnt);
-      if (rank < top_k) {
-        sel_id[rank] = e;
-        sel_v[rank] = v;
-      }
-    }
-  }
+  route_rank<P>(lv, n_routed, top_k, sel_id, sel_v);
   __syncthreads();
-  if (t < top_k) sel_e[t] = exp(static_cast<double>(sel_v[t]) - static_cast<double>(sel_v[0]));
-  __syncthreads();
-  if (t < top_k) {
-    double z = 0.0;
-    for (int s = 0; s < top_k; ++s) z += sel_e[s];
-    ids[t] = sel_id[t];
-    wts[t] = static_cast<float>(sel_e[t] / z);
-  }
-  if (t == top_k && shared_gate) {
-    ids[top_k] = n_routed;
-    wts[top_k] = static_cast<float>(1.0 / (1.0 + exp(-static_cast<double>(*shared_gate))));
-  }
+  route_weights(sel_id, sel_v, sel_e, n_routed, top_k, shared_gate, ids, wts);
 }
 
 int launch_moe_route(const float *logits, int32_t n_routed, int32_t top_k, const float *shared_gate,

@@ -23,7 +23,7 @@ namespace zq {
 
 // ------------------------------------------------------------- gate/up ----
 
-template <int WT, int LPR, int BPL, int RB>
+template <int WT, int LPR, int BPL, int RB, bool ROUTED>
 __global__ __launch_bounds__(1024) void moe_gate_up_kernel(const MoeGateUpArgs a) {
   constexpr int WPB = 16;
   constexpr int S = 64 / LPR;
@@ -57,10 +57,23 @@ __global__ __launch_bounds__(1024) void moe_gate_up_kernel(const MoeGateUpArgs a
       xv[4 * u] = v.x; xv[4 * u + 1] = v.y; xv[4 * u + 2] = v.z; xv[4 * u + 3] = v.w;
     }
   }
-  const int e = a.ids[s];
-  if (e < 0 || e >= a.n_experts) {  // uniform over the workgroup
-    if (a.status && tid == 0) *a.status = ZQ_ERANGE;
-    return;
+  int e;
+  __shared__ int32_t rsel[64];
+  __shared__ float rselv[64];
+  if constexpr (ROUTED) {
+    // the router, in every workgroup: rank the logits, take slot s's expert
+    __shared__ float rlv[1024];
+    for (int i = tid; i < a.n_routed; i += T) rlv[i] = a.logits[i];
+    __syncthreads();
+    route_rank<8>(rlv, a.n_routed, a.top_k, rsel, rselv);
+    __syncthreads();
+    e = s < a.top_k ? rsel[s] : a.n_routed;
+  } else {
+    e = a.ids[s];
+    if (e < 0 || e >= a.n_experts) {  // uniform over the workgroup
+      if (a.status && tid == 0) *a.status = ZQ_ERANGE;
+      return;
+    }
   }
   const uint8_t *wb = a.bank + static_cast<int64_t>(e) * a.expert_stride;
 
@@ -179,6 +192,14 @@ __global__ __launch_bounds__(1024) void moe_gate_up_kernel(const MoeGateUpArgs a
         gp[32 * hb + i0 + q] = lrow[i0 + q];
         gp[a.d_ff + 32 * hb + i0 + q] = lrow[32 + i0 + q];
       }
+    }
+  }
+  // one workgroup publishes the expert list and weights for the down pass,
+  // last, so that the fp64 softmax delays none of its loads
+  if constexpr (ROUTED) {
+    if (blockIdx.x == 0 && blockIdx.y == 0) {  // uniform over the workgroup
+      __shared__ double rsele[64];
+      route_weights(rsel, rselv, rsele, a.n_routed, a.top_k, a.shared_gate, a.ids_out, a.wts_out);
     }
   }
 }
@@ -326,9 +347,11 @@ namespace {
 template <int WT, int LPR, int BPL, int RB>
 int launch_gu(const MoeGateUpArgs &a, hipStream_t stream) {
   const size_t lds = static_cast<size_t>(a.k) + 8 * static_cast<size_t>(a.nb) + 64 * 4;
-  hipLaunchKernelGGL((moe_gate_up_kernel<WT, LPR, BPL, RB>),
-                     dim3(static_cast<unsigned>(a.d_ff / 32), static_cast<unsigned>(a.n_sel)),
-                     dim3(1024), lds, stream, a);
+  const dim3 grid(static_cast<unsigned>(a.d_ff / 32), static_cast<unsigned>(a.n_sel));
+  if (a.logits)
+    hipLaunchKernelGGL((moe_gate_up_kernel<WT, LPR, BPL, RB, true>), grid, dim3(1024), lds, stream, a);
+  else
+    hipLaunchKernelGGL((moe_gate_up_kernel<WT, LPR, BPL, RB, false>), grid, dim3(1024), lds, stream, a);
   ZQ_LAUNCH_CHECK();
   return ZQ_OK;
 }

@@ -316,6 +316,51 @@ int zq_moe_gate_up(int wtype, const void *gu_bank, int64_t gu_stride_bytes, int6
   return zq::launch_moe_gate_up(wtype, a, S(stream));
 }
 
+int zq_moe_gate_up_route(int wtype, const void *gu_bank, int64_t gu_stride_bytes,
+                         int64_t n_experts, int64_t d_model, int64_t d_ff, const float *logits,
+                         int32_t n_routed, int32_t top_k, const float *shared_gate,
+                         const float *x, int32_t *ids, float *wts, int8_t *qh, float *dh,
+                         int32_t *sh, float *h_out, float *gu_out, void *stream) {
+  const int64_t bb = block_bytes(wtype);
+  ZQ_REQUIRE(bb > 0, ZQ_EINVAL);
+  ZQ_REQUIRE(gu_bank && logits && ids && wts && x && qh && dh, ZQ_ENULL);
+  ZQ_REQUIRE(top_k >= 1 && top_k <= 64 && n_routed >= top_k && n_routed <= 1024, ZQ_EINVAL);
+  const int32_t n_sel = top_k + (shared_gate ? 1 : 0);
+  ZQ_REQUIRE(n_experts >= n_sel - top_k + n_routed && n_experts <= INT32_MAX && k_ok(d_model) &&
+                 k_ok(d_ff),
+             ZQ_EINVAL);
+  ZQ_REQUIRE(zq::moe_gate_up_fits(d_model) && d_ff <= (int64_t(1) << 30), ZQ_EINVAL);
+  ZQ_REQUIRE(gu_stride_bytes >= 2 * d_ff * (d_model / 32) * bb && gu_stride_bytes % 2 == 0,
+             ZQ_EINVAL);
+  ZQ_REQUIRE(al(gu_bank, 4) && al(logits, 4) && al(shared_gate, 4) && al(ids, 4) && al(wts, 4) &&
+                 al(x, 16) && al(qh, 16) && al(dh, 4) && al(sh, 4) && al(h_out, 16) &&
+                 al(gu_out, 4),
+             ZQ_EALIGN);
+  const int dc = check_current_device();
+  if (dc != ZQ_OK) return dc;
+  zq::MoeGateUpArgs a{};
+  a.bank = static_cast<const uint8_t *>(gu_bank);
+  a.expert_stride = gu_stride_bytes;
+  a.n_experts = static_cast<int32_t>(n_experts);
+  a.ids = ids;
+  a.n_sel = n_sel;
+  a.x = x;
+  a.k = static_cast<int32_t>(d_model);
+  a.d_ff = static_cast<int32_t>(d_ff);
+  a.qh = qh;
+  a.dh = dh;
+  a.sh = sh;
+  a.h_out = h_out;
+  a.gu_out = gu_out;
+  a.logits = logits;
+  a.n_routed = n_routed;
+  a.top_k = top_k;
+  a.shared_gate = shared_gate;
+  a.ids_out = ids;
+  a.wts_out = wts;
+  return zq::launch_moe_gate_up(wtype, a, S(stream));
+}
+
 int zq_swiglu_quantize(const float *gu, int64_t n, int64_t f, int8_t *qh, float *dh, int32_t *sh,
                        float *h_out, void *stream) {
   ZQ_REQUIRE(gu && qh && dh, ZQ_ENULL);
@@ -331,33 +376,29 @@ size_t zq_moe_ffn_workspace_bytes(int64_t d_model, int64_t d_ff, int32_t n_sel) 
   return moe_layout(d_model, d_ff, n_sel).total;
 }
 
-int zq_moe_ffn(int wtype, const void *gu_bank, int64_t gu_stride_bytes, const void *down_bank,
-               int64_t down_stride_bytes, int64_t n_experts, int64_t d_model, int64_t d_ff,
-               const int32_t *ids, const float *wts, int32_t n_sel, const float *x,
-               void *workspace, size_t workspace_bytes, float *y, uint32_t flags,
-               int32_t *dev_status, void *stream) {
-  const int64_t bb = block_bytes(wtype);
-  ZQ_REQUIRE(bb > 0, ZQ_EINVAL);
-  ZQ_REQUIRE(gu_bank && down_bank && ids && wts && x && workspace && y, ZQ_ENULL);
-  ZQ_REQUIRE(n_experts >= 1 && n_experts <= INT32_MAX && k_ok(d_model) && k_ok(d_ff), ZQ_EINVAL);
-  ZQ_REQUIRE(n_sel >= 0 && n_sel <= 65535, ZQ_EINVAL);
-  ZQ_REQUIRE(gu_stride_bytes >= 2 * d_ff * (d_model / 32) * bb && gu_stride_bytes % 2 == 0,
-             ZQ_EINVAL);
-  ZQ_REQUIRE(down_stride_bytes >= d_model * (d_ff / 32) * bb && down_stride_bytes % 2 == 0,
-             ZQ_EINVAL);
-  ZQ_REQUIRE((flags & ~uint32_t(ZQ_ACCUMULATE)) == 0, ZQ_EINVAL);
+namespace {
+
+// The router's arguments when the expert list is computed on the GPU.
+struct MoeRoute {
+  const float *logits;
+  int32_t n_routed;
+  int32_t top_k;
+  const float *shared_gate;
+};
+
+// One token through the selected experts, arguments already checked.  With
+// route set, ids / wts are written (by the gate/up pass, or by the router
+// launch on the wide-model path) before the down pass reads them.
+int moe_ffn_run(int wtype, const void *gu_bank, int64_t gu_stride_bytes, const void *down_bank,
+                int64_t down_stride_bytes, int64_t n_experts, int64_t d_model, int64_t d_ff,
+                int32_t *ids, float *wts, int32_t n_sel, const float *x, void *workspace,
+                float *y, uint32_t flags, int32_t *dev_status, const MoeRoute *route,
+                hipStream_t s) {
   const MoeWorkspace L = moe_layout(d_model, d_ff, n_sel);
-  ZQ_REQUIRE(workspace_bytes >= L.total, ZQ_EINVAL);
-  ZQ_REQUIRE(al(gu_bank, 4) && al(down_bank, 4) && al(ids, 4) && al(wts, 4) && al(x, 16) &&
-                 al(workspace, kAlign) && al(y, 4) && al(dev_status, 4),
-             ZQ_EALIGN);
-  const int dc = check_current_device();
-  if (dc != ZQ_OK) return dc;
   uint8_t *ws = static_cast<uint8_t *>(workspace);
   int8_t *qh = reinterpret_cast<int8_t *>(ws + L.qh);
   float *dh = reinterpret_cast<float *>(ws + L.dh);
   int32_t *sh = reinterpret_cast<int32_t *>(ws + L.sh);
-  hipStream_t s = S(stream);
   int rc;
   if (zq::moe_gate_up_fits(d_model)) {
     zq::MoeGateUpArgs a{};
@@ -365,6 +406,14 @@ int zq_moe_ffn(int wtype, const void *gu_bank, int64_t gu_stride_bytes, const vo
     a.expert_stride = gu_stride_bytes;
     a.n_experts = static_cast<int32_t>(n_experts);
     a.ids = ids;
+    if (route) {
+      a.logits = route->logits;
+      a.n_routed = route->n_routed;
+      a.top_k = route->top_k;
+      a.shared_gate = route->shared_gate;
+      a.ids_out = ids;
+      a.wts_out = wts;
+    }
     a.n_sel = n_sel;
     a.x = x;
     a.k = static_cast<int32_t>(d_model);
@@ -376,7 +425,13 @@ int zq_moe_ffn(int wtype, const void *gu_bank, int64_t gu_stride_bytes, const vo
     rc = zq::launch_moe_gate_up(wtype, a, s);
     if (rc != ZQ_OK) return rc;
   } else if (n_sel > 0) {
-    // wide models: quantize x, gather gate||up rows, then swiglu + quantize
+    // wide models: the router (if asked), quantize x, gather gate||up rows,
+    // then swiglu + quantize
+    if (route) {
+      rc = zq::launch_moe_route(route->logits, route->n_routed, route->top_k, route->shared_gate,
+                                ids, wts, s);
+      if (rc != ZQ_OK) return rc;
+    }
     int8_t *qx = reinterpret_cast<int8_t *>(ws + L.qx);
     float *dx = reinterpret_cast<float *>(ws + L.dx);
     int32_t *sx = reinterpret_cast<int32_t *>(ws + L.sx);
@@ -440,6 +495,67 @@ int zq_moe_ffn(int wtype, const void *gu_bank, int64_t gu_stride_bytes, const vo
   b.n_sel = n_sel;
   b.flags = flags;
   return zq::launch_dmmv(wtype, zq::MODE_WEIGHTED, b, s);
+}
+
+
+}  // namespace
+
+int zq_moe_ffn(int wtype, const void *gu_bank, int64_t gu_stride_bytes, const void *down_bank,
+               int64_t down_stride_bytes, int64_t n_experts, int64_t d_model, int64_t d_ff,
+               const int32_t *ids, const float *wts, int32_t n_sel, const float *x,
+               void *workspace, size_t workspace_bytes, float *y, uint32_t flags,
+               int32_t *dev_status, void *stream) {
+  const int64_t bb = block_bytes(wtype);
+  ZQ_REQUIRE(bb > 0, ZQ_EINVAL);
+  ZQ_REQUIRE(gu_bank && down_bank && ids && wts && x && workspace && y, ZQ_ENULL);
+  ZQ_REQUIRE(n_experts >= 1 && n_experts <= INT32_MAX && k_ok(d_model) && k_ok(d_ff), ZQ_EINVAL);
+  ZQ_REQUIRE(n_sel >= 0 && n_sel <= 65535, ZQ_EINVAL);
+  ZQ_REQUIRE(gu_stride_bytes >= 2 * d_ff * (d_model / 32) * bb && gu_stride_bytes % 2 == 0,
+             ZQ_EINVAL);
+  ZQ_REQUIRE(down_stride_bytes >= d_model * (d_ff / 32) * bb && down_stride_bytes % 2 == 0,
+             ZQ_EINVAL);
+  ZQ_REQUIRE((flags & ~uint32_t(ZQ_ACCUMULATE)) == 0, ZQ_EINVAL);
+  const MoeWorkspace L = moe_layout(d_model, d_ff, n_sel);
+  ZQ_REQUIRE(workspace_bytes >= L.total, ZQ_EINVAL);
+  ZQ_REQUIRE(al(gu_bank, 4) && al(down_bank, 4) && al(ids, 4) && al(wts, 4) && al(x, 16) &&
+                 al(workspace, kAlign) && al(y, 4) && al(dev_status, 4),
+             ZQ_EALIGN);
+  const int dc = check_current_device();
+  if (dc != ZQ_OK) return dc;
+  return moe_ffn_run(wtype, gu_bank, gu_stride_bytes, down_bank, down_stride_bytes, n_experts,
+                     d_model, d_ff, const_cast<int32_t *>(ids), const_cast<float *>(wts), n_sel, x,
+                     workspace, y, flags, dev_status, nullptr, S(stream));
+}
+
+int zq_moe_ffn_route(int wtype, const void *gu_bank, int64_t gu_stride_bytes,
+                     const void *down_bank, int64_t down_stride_bytes, int64_t n_experts,
+                     int64_t d_model, int64_t d_ff, const float *logits, int32_t n_routed,
+                     int32_t top_k, const float *shared_gate, const float *x, int32_t *ids,
+                     float *wts, void *workspace, size_t workspace_bytes, float *y,
+                     uint32_t flags, void *stream) {
+  const int64_t bb = block_bytes(wtype);
+  ZQ_REQUIRE(bb > 0, ZQ_EINVAL);
+  ZQ_REQUIRE(gu_bank && down_bank && logits && ids && wts && x && workspace && y, ZQ_ENULL);
+  ZQ_REQUIRE(top_k >= 1 && top_k <= 64 && n_routed >= top_k && n_routed <= 1024, ZQ_EINVAL);
+  const int32_t n_sel = top_k + (shared_gate ? 1 : 0);
+  ZQ_REQUIRE(n_experts >= n_sel - top_k + n_routed && n_experts <= INT32_MAX && k_ok(d_model) &&
+                 k_ok(d_ff),
+             ZQ_EINVAL);
+  ZQ_REQUIRE(gu_stride_bytes >= 2 * d_ff * (d_model / 32) * bb && gu_stride_bytes % 2 == 0,
+             ZQ_EINVAL);
+  ZQ_REQUIRE(down_stride_bytes >= d_model * (d_ff / 32) * bb && down_stride_bytes % 2 == 0,
+             ZQ_EINVAL);
+  ZQ_REQUIRE((flags & ~uint32_t(ZQ_ACCUMULATE)) == 0, ZQ_EINVAL);
+  ZQ_REQUIRE(workspace_bytes >= moe_layout(d_model, d_ff, n_sel).total, ZQ_EINVAL);
+  ZQ_REQUIRE(al(gu_bank, 4) && al(down_bank, 4) && al(logits, 4) && al(shared_gate, 4) &&
+                 al(ids, 4) && al(wts, 4) && al(x, 16) && al(workspace, kAlign) && al(y, 4),
+             ZQ_EALIGN);
+  const int dc = check_current_device();
+  if (dc != ZQ_OK) return dc;
+  const MoeRoute route{logits, n_routed, top_k, shared_gate};
+  return moe_ffn_run(wtype, gu_bank, gu_stride_bytes, down_bank, down_stride_bytes, n_experts,
+                     d_model, d_ff, ids, wts, n_sel, x, workspace, y, flags, nullptr, &route,
+                     S(stream));
 }
 
 int zq_gemm_prefill(int wtype, const void *w, int64_t n, int64_t k, const int8_t *qx,

@@ -312,6 +312,74 @@ __device__ __forceinline__ void block_best(float &v, int32_t &i) {
   }
 }
 
+
+// ---------------------------------------------------------------- router --
+// Rank selection over n logits staged in LDS (lv) by the whole workgroup, P
+// threads per logit: a logit's rank is the number of logits that beat it
+// (larger, or equal at a lower id), and the logits of rank < top_k are
+// stored at their rank (sel_id, sel_v), largest first with ties to the
+// lower id.  Counts are small integers, exact in fp32.  Every thread of the
+// workgroup must call it; the caller synchronizes before reading sel_*.
+template <int P>
+__device__ __forceinline__ void route_rank(const float *lv, int n, int top_k, int32_t *sel_id,
+                                           float *sel_v) {
+  const int t = static_cast<int>(threadIdx.x);
+  const int n_groups = static_cast<int>(blockDim.x) / P;
+  const int part = t & (P - 1);
+  for (int e0 = 0; e0 < n; e0 += n_groups) {  // uniform trip count
+    const int e = e0 + t / P;
+    const bool ok = e < n;
+    const float v = ok ? lv[e] : 0.0f;
+    float cnt = 0.0f;
+    if (ok) {
+      // eight comparisons per step, their LDS reads issued together
+      for (int j0 = part; j0 < n; j0 += 8 * P) {
+#pragma unroll
+        for (int u8 = 0; u8 < 8; ++u8) {
+          const int j = j0 + u8 * P;
+          if (j < n) {
+            const float u = lv[j];
+            cnt += (u > v || (u == v && j < e)) ? 1.0f : 0.0f;
+          }
+        }
+      }
+    }
+    cnt = group_sum<P>(cnt);
+    if (ok && part == 0) {
+      const int rank = static_cast<int>(cnt);
+      if (rank < top_k) {
+        sel_id[rank] = e;
+        sel_v[rank] = v;
+      }
+    }
+  }
+}
+
+// Expert list and weights from the ranked selection: ids[r] = sel_id[r] and
+// wts = softmax over the selected logits, each exponential evaluated in fp64
+// by its own thread and the normalizer summed in rank order; with a shared
+// gate, the shared expert (id n) follows with weight sigmoid(g) in fp64.
+// sel_e: LDS scratch of top_k doubles.  Every thread of the workgroup must
+// call it (it synchronizes).
+__device__ __forceinline__ void route_weights(const int32_t *sel_id, const float *sel_v,
+                                              double *sel_e, int n, int top_k,
+                                              const float *shared_gate, int32_t *ids,
+                                              float *wts) {
+  const int t = static_cast<int>(threadIdx.x);
+  if (t < top_k) sel_e[t] = exp(static_cast<double>(sel_v[t]) - static_cast<double>(sel_v[0]));
+  __syncthreads();
+  if (t < top_k) {
+    double z = 0.0;
+    for (int r = 0; r < top_k; ++r) z += sel_e[r];
+    ids[t] = sel_id[t];
+    wts[t] = static_cast<float>(sel_e[t] / z);
+  }
+  if (t == top_k && shared_gate) {
+    ids[top_k] = n;
+    wts[top_k] = static_cast<float>(1.0 / (1.0 + exp(-static_cast<double>(*shared_gate))));
+  }
+}
+
 }  // namespace zq
 
 // Host-side launch helpers.

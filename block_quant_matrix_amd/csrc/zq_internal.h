@@ -74,6 +74,16 @@ struct MoeGateUpArgs {
   float *h_out;         // [n_sel][d_ff] or null
   float *gu_out;        // [n_sel][2*d_ff] or null
   int32_t *status;
+  // With logits set, the workgroups select the experts themselves (the
+  // router of zq_moe_route) instead of reading ids: slot s < top_k takes the
+  // expert of rank s, slot top_k the shared expert (id n_routed); the
+  // workgroup of slot 0, block 0 also writes ids_out / wts_out.
+  const float *logits;  // [n_routed] or null
+  int32_t n_routed;
+  int32_t top_k;
+  const float *shared_gate;
+  int32_t *ids_out;
+  float *wts_out;
 };
 
 // MoE down pass with the weighted sum over the selected experts fused in.

@@ -48,6 +48,10 @@ SIGNATURES = {
     "zq_moe_ffn_workspace_bytes": (_SZ, [_I64, _I64, _I32]),
     "zq_moe_ffn": (_INT, [_INT, _P, _I64, _P, _I64, _I64, _I64, _I64, _P, _P, _I32, _P, _P, _SZ,
                           _P, _U32, _P, _P]),
+    "zq_moe_gate_up_route": (_INT, [_INT, _P, _I64, _I64, _I64, _I64, _P, _I32, _I32, _P, _P, _P,
+                                    _P, _P, _P, _P, _P, _P, _P]),
+    "zq_moe_ffn_route": (_INT, [_INT, _P, _I64, _P, _I64, _I64, _I64, _I64, _P, _I32, _I32, _P, _P,
+                                _P, _P, _P, _SZ, _P, _U32, _P]),
     "zq_gemm_prefill": (_INT, [_INT, _P, _I64, _I64, _P, _P, _P, _I64, _P, _U32, _P]),
     "zq_gemm_isums": (_INT, [_INT, _P, _I64, _I64, _P, _P, _I64, _I64, _I64, _I64, _I64, _P, _P]),
 }
@@ -192,6 +196,23 @@ def zq_moe_ffn(wtype, gu_bank, gu_stride_bytes, down_bank, down_stride_bytes, n_
     return _call("zq_moe_ffn", wtype, ptr(gu_bank), gu_stride_bytes, ptr(down_bank),
                  down_stride_bytes, n_experts, d_model, d_ff, ptr(ids), ptr(wts), n_sel, ptr(x),
                  ptr(workspace), workspace_bytes, ptr(y), flags, ptr(dev_status), _stream(stream))
+
+
+def zq_moe_gate_up_route(wtype, gu_bank, gu_stride, n_experts, d_model, d_ff, logits, n_routed,
+                         top_k, shared_gate, x, ids, wts, qh, dh, sh=None, h_out=None, gu_out=None,
+                         stream=None):
+    return _call("zq_moe_gate_up_route", wtype, ptr(gu_bank), gu_stride, n_experts, d_model, d_ff,
+                 ptr(logits), n_routed, top_k, ptr(shared_gate), ptr(x), ptr(ids), ptr(wts),
+                 ptr(qh), ptr(dh), ptr(sh), ptr(h_out), ptr(gu_out), _stream(stream))
+
+
+def zq_moe_ffn_route(wtype, gu_bank, gu_stride, down_bank, down_stride, n_experts, d_model, d_ff,
+                     logits, n_routed, top_k, shared_gate, x, ids, wts, workspace,
+                     workspace_bytes, y, flags=0, stream=None):
+    return _call("zq_moe_ffn_route", wtype, ptr(gu_bank), gu_stride, ptr(down_bank), down_stride,
+                 n_experts, d_model, d_ff, ptr(logits), n_routed, top_k, ptr(shared_gate), ptr(x),
+                 ptr(ids), ptr(wts), ptr(workspace), workspace_bytes, ptr(y), flags,
+                 _stream(stream))
 
 
 def zq_gemm_prefill(wtype, w, n, k, qx, dx, sx, m, y, flags=0, stream=None):

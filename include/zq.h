@@ -193,6 +193,19 @@ int zq_moe_gate_up(int wtype, const void *gu_bank, int64_t gu_stride_bytes, int6
                    const float *x, int8_t *qh, float *dh, int32_t *sh, float *h_out,
                    float *gu_out, int32_t *dev_status, void *stream);
 
+/* The same stage with the router folded in (the router of zq_moe_route, in
+ * every workgroup): slot s < top_k takes the expert of rank s among the
+ * n_routed logits, slot top_k the shared expert (id n_routed) when
+ * shared_gate is non-NULL; ids / wts (top_k (+1) entries) receive the
+ * router's output, bit for bit, for the down pass.  Outputs as
+ * zq_moe_gate_up with n_sel = top_k (+1).  1 <= top_k <= 64,
+ * top_k <= n_routed <= 1024, n_experts >= n_routed (+1), d_model <= 4096. */
+int zq_moe_gate_up_route(int wtype, const void *gu_bank, int64_t gu_stride_bytes,
+                         int64_t n_experts, int64_t d_model, int64_t d_ff, const float *logits,
+                         int32_t n_routed, int32_t top_k, const float *shared_gate,
+                         const float *x, int32_t *ids, float *wts, int8_t *qh, float *dh,
+                         int32_t *sh, float *h_out, float *gu_out, void *stream);
+
 /* One token through the selected experts in two launches: zq_moe_gate_up
  * (quantize x, gate||up rows, swiglu, re-quantize), then the down DMMV with
  * the weighted sum over the selected experts fused in.  gu_bank: experts of [2*d_ff][d_model]
@@ -206,6 +219,27 @@ int zq_moe_ffn(int wtype, const void *gu_bank, int64_t gu_stride_bytes, const vo
                const int32_t *ids, const float *wts, int32_t n_sel, const float *x,
                void *workspace, size_t workspace_bytes, float *y, uint32_t flags,
                int32_t *dev_status, void *stream);
+
+/* zq_moe_route followed by zq_moe_ffn, with the router folded into the
+ * gate/up pass: the whole MoE block of one token in two launches, the expert
+ * list never leaving the GPU ("RTX 5090: Batched Prefill & CUDA Graphs in
+ * ZINC", sections "Prefill -- a correction, and a better GEMM" and "What's
+ * next": GPU-side expert routing with no router round-trip).  Every gate/up
+ * workgroup ranks the n_routed logits itself; the selection and weights are
+ * those of zq_moe_route, bit for bit, and are written to ids / wts
+ * (top_k + 1 entries with a shared gate, else top_k), which the down pass
+ * then reads.  n_sel = top_k (+ 1): the workspace is
+ * zq_moe_ffn_workspace_bytes(d_model, d_ff, n_sel).  n_experts >= n_routed
+ * (+ 1 for the shared expert, id n_routed).  1 <= top_k <= 64,
+ * top_k <= n_routed <= 1024.  Wide models (d_model > 4096) run the router,
+ * quantize, gather and swiglu launches instead, with the same results.
+ * flags: 0 or ZQ_ACCUMULATE. */
+int zq_moe_ffn_route(int wtype, const void *gu_bank, int64_t gu_stride_bytes,
+                     const void *down_bank, int64_t down_stride_bytes, int64_t n_experts,
+                     int64_t d_model, int64_t d_ff, const float *logits, int32_t n_routed,
+                     int32_t top_k, const float *shared_gate, const float *x, int32_t *ids,
+                     float *wts, void *workspace, size_t workspace_bytes, float *y,
+                     uint32_t flags, void *stream);
 
 /* Batched prefill GEMM ("one register-tiled GEMM over all prompt tokens at
  * once", "RTX 5090: Batched Prefill & CUDA Graphs in ZINC", opening answer

@@ -68,6 +68,47 @@ def test_workspace_sizes():
     assert L.zq_dmmv_f32_argmax_workspace_bytes() == 8 * 2048
 
 
+def test_moe_ffn_route_argument_errors():
+    L = zq.lib()
+    ws = L.zq_moe_ffn_workspace_bytes(2048, 512, 9)
+    gs, ds = 2 * 512 * 64 * 18, 2048 * 16 * 18
+
+    def rc(wtype=4, n_experts=129, d_model=2048, d_ff=512, logits=B, n_routed=128, top_k=8,
+           g=C, x=D, ids=A + 0x1000, wts=A + 0x2000, work=A + 0x4000, wsb=ws, y=A + 0x8000,
+           flags=0):
+        return L.zq_moe_ffn_route(wtype, A, gs, B, ds, n_experts, d_model, d_ff, logits, n_routed,
+                                  top_k, g, x, ids, wts, work, wsb, y, flags, None)
+
+    assert rc(wtype=3) == zq.ZQ_EINVAL
+    assert rc(top_k=0) == zq.ZQ_EINVAL
+    assert rc(top_k=65, n_routed=128) == zq.ZQ_EINVAL
+    assert rc(n_routed=1025) == zq.ZQ_EINVAL
+    assert rc(n_routed=7) == zq.ZQ_EINVAL              # fewer than top_k
+    assert rc(n_experts=128) == zq.ZQ_EINVAL           # no room for the shared expert
+    assert rc(d_model=2047) == zq.ZQ_EINVAL
+    assert rc(flags=2) == zq.ZQ_EINVAL
+    assert rc(wsb=ws - 1) == zq.ZQ_EINVAL
+    assert rc(logits=None) == zq.ZQ_ENULL
+    assert rc(ids=None) == zq.ZQ_ENULL
+    assert rc(x=D + 4) == zq.ZQ_EALIGN
+    assert rc(work=A + 0x4010) == zq.ZQ_EALIGN
+
+
+def test_moe_gate_up_route_argument_errors():
+    L = zq.lib()
+    gs = 2 * 512 * 64 * 18
+
+    def rc(d_model=2048, n_routed=128, top_k=8, g=C, logits=B, qh=A + 0x1000):
+        return L.zq_moe_gate_up_route(4, A, gs, 129, d_model, 512, logits, n_routed, top_k, g, D,
+                                      A + 0x2000, A + 0x3000, qh, A + 0x4000, None, None, None,
+                                      None)
+
+    assert rc(d_model=8192) == zq.ZQ_EINVAL     # wider than the fused stage takes
+    assert rc(top_k=9, n_routed=8) == zq.ZQ_EINVAL
+    assert rc(logits=None) == zq.ZQ_ENULL
+    assert rc(qh=A + 0x1004) == zq.ZQ_EALIGN
+
+
 def test_lmhead_argument_errors():
     L = zq.lib()
     ws = L.zq_dmmv_f32_argmax_workspace_bytes()
@@ -184,4 +225,8 @@ def test_valid_arguments_without_gpu_report_no_device():
                                 L.zq_dmmv_f32_argmax_workspace_bytes(), None) == zq.ZQ_EDEVICE
     assert L.zq_dmmv_f32_argmax(4, A, 7, 64, B, C, None, A + 0x8000,
                                 L.zq_dmmv_f32_argmax_workspace_bytes(), None) == zq.ZQ_EDEVICE
+    ws = L.zq_moe_ffn_workspace_bytes(2048, 512, 8)
+    assert L.zq_moe_ffn_route(4, A, 2 * 512 * 64 * 18, B, 2048 * 16 * 18, 128, 2048, 512, B, 128,
+                              8, None, D, A + 0x1000, A + 0x2000, A + 0x4000, ws, A + 0x8000, 0,
+                              None) == zq.ZQ_EDEVICE
     assert zq.lib().zq_device_check(0) == zq.ZQ_EDEVICE

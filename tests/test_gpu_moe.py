@@ -213,3 +213,113 @@ def test_moe_no_selected_expert(zq, banks):
     zq.zq_moe_ffn(Q4, banks["gu_d"], banks["gs"], banks["down_d"], banks["ds"], N_EXPERTS, D_MODEL,
                   D_FF, ids, wts, 0, dev(np.zeros(D_MODEL, np.float32)), ws, ws_bytes, y)
     assert (host(y) == 0).all()
+
+
+# ------------------------------------------------ router folded in ---------
+
+def routed_ffn(zq, gu_d, gs, down_d, ds, n_experts, d_model, d_ff, logits, top_k, g, x, y=None,
+               flags=0):
+    torch = torch_cuda()
+    n_routed = logits.size
+    n_sel = top_k + (1 if g is not None else 0)
+    ws_bytes = zq.zq_moe_ffn_workspace_bytes(d_model, d_ff, n_sel)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    ids = sentinel_i32(n_sel)
+    wts = nan_f32(n_sel)
+    y = nan_f32(d_model) if y is None else y
+    gd = None if g is None else dev(np.array([g], np.float32))
+    zq.zq_moe_ffn_route(Q4, gu_d, gs, down_d, ds, n_experts, d_model, d_ff, dev(logits), n_routed,
+                        top_k, gd, dev(x), ids, wts, ws, ws_bytes, y, flags)
+    return host(ids), host(wts), y
+
+
+def unfused_ffn(zq, gu_d, gs, down_d, ds, n_experts, d_model, d_ff, logits, top_k, g, x):
+    torch = torch_cuda()
+    ids, wts = gpu_route(zq, logits, g, top_k=top_k)
+    n_sel = ids.size
+    ws_bytes = zq.zq_moe_ffn_workspace_bytes(d_model, d_ff, n_sel)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    y = nan_f32(d_model)
+    zq.zq_moe_ffn(Q4, gu_d, gs, down_d, ds, n_experts, d_model, d_ff, dev(ids), dev(wts), n_sel,
+                  dev(x), ws, ws_bytes, y)
+    return ids, wts, host(y)
+
+
+@pytest.mark.parametrize("s", [0, 1, 2, 3])
+def test_moe_ffn_route_equals_route_then_ffn(zq, banks, s):
+    """Two launches give the router's ids and weights and the composite's
+    rows, bit for bit; seed 3 puts a three-way tie at the top."""
+    logits, g = inputs.gen_router(E_ROUTED, inputs.seed_for(4, 10 + s))
+    if s == 3:
+        logits[[3, 9, 70]] = logits.max() + 1.0
+    x = inputs.gen_activation(1, D_MODEL, inputs.seed_for(4, 10 + s) + 7)
+    args = (banks["gu_d"], banks["gs"], banks["down_d"], banks["ds"], N_EXPERTS, D_MODEL, D_FF,
+            logits, TOP_K, g, x)
+    ids, wts, y = routed_ffn(zq, *args)
+    rids, rwts, ry = unfused_ffn(zq, *args)
+    assert np.array_equal(ids, rids)
+    assert np.array_equal(wts.view(np.uint32), rwts.view(np.uint32))
+    assert np.array_equal(host(y).view(np.uint32), ry.view(np.uint32))
+    oids, _ = oracle.moe_route(logits, TOP_K, g)
+    assert np.array_equal(ids, oids)
+    # accumulate
+    prev = host(y).copy()
+    routed_ffn(zq, *args, y=y, flags=1)
+    assert np.allclose(host(y), 2 * prev, rtol=1e-6, atol=0)
+
+
+@pytest.mark.parametrize("d_model,d_ff,n_routed,top_k,shared", [
+    (64, 32, 200, 17, True),      # 18 selected: two chunks of down windows
+    (256, 96, 1024, 64, False),   # the router's limits, no shared expert
+    (5120, 64, 40, 3, True),      # wider than the fused gate/up: router launch + unfused path
+])
+def test_moe_ffn_route_other_shapes(zq, d_model, d_ff, n_routed, top_k, shared):
+    E = n_routed + (1 if shared else 0)
+    gu, gs, down, ds = inputs.moe_banks(4242 + d_model + top_k, E, d_model, d_ff)
+    rng = np.random.default_rng(n_routed + top_k)
+    logits = rng.standard_normal(n_routed).astype(np.float32)
+    g = np.float32(rng.standard_normal()) if shared else None
+    x = inputs.gen_activation(1, d_model, 4243 + d_ff)
+    args = (dev(gu), gs, dev(down), ds, E, d_model, d_ff, logits, top_k, g, x)
+    ids, wts, y = routed_ffn(zq, *args)
+    rids, rwts, ry = unfused_ffn(zq, *args)
+    assert np.array_equal(ids, rids)
+    assert np.array_equal(wts.view(np.uint32), rwts.view(np.uint32))
+    assert np.array_equal(host(y).view(np.uint32), ry.view(np.uint32))
+    oids, ow = oracle.moe_route(logits, top_k, g)
+    assert np.array_equal(ids, oids)
+    y_ref, S = oracle.moe_ffn(Q4, gu, gs, down, ds, d_model, d_ff, ids, ow, x)
+    check_rows(host(y), y_ref, S, "routed moe %dx%d" % (d_model, d_ff), tol=1e-3)
+
+
+def test_moe_gate_up_route_stage(zq, banks):
+    """The routed gate/up stage equals route + zq_moe_gate_up, output by
+    output and bit for bit (ids, weights, gate||up rows, h, codes, scales,
+    sums)."""
+    torch = torch_cuda()
+    for s in range(3):
+        logits, g = inputs.gen_router(E_ROUTED, inputs.seed_for(4, 20 + s))
+        x = inputs.gen_activation(1, D_MODEL, inputs.seed_for(4, 20 + s) + 7)
+        n_sel = TOP_K + 1
+        outs = []
+        for routed in (True, False):
+            qh = torch.zeros((n_sel, D_FF), dtype=torch.int8, device="cuda")
+            dh = nan_f32(n_sel, D_FF // 32)
+            sh = sentinel_i32(n_sel, D_FF // 32)
+            h = nan_f32(n_sel, D_FF)
+            gu = nan_f32(n_sel, 2 * D_FF)
+            if routed:
+                ids = sentinel_i32(n_sel)
+                wts = nan_f32(n_sel)
+                zq.zq_moe_gate_up_route(Q4, banks["gu_d"], banks["gs"], N_EXPERTS, D_MODEL, D_FF,
+                                        dev(logits), E_ROUTED, TOP_K, dev(np.array([g], np.float32)),
+                                        dev(x), ids, wts, qh, dh, sh, h, gu)
+                ids, wts = host(ids), host(wts)
+            else:
+                ids, wts = gpu_route(zq, logits, g)
+                zq.zq_moe_gate_up(Q4, banks["gu_d"], banks["gs"], N_EXPERTS, D_MODEL, D_FF,
+                                  dev(ids), n_sel, dev(x), qh, dh, sh, h, gu)
+            outs.append([ids, wts.view(np.uint32)] +
+                        [host(t).view(np.uint8) for t in (qh, dh, sh, h, gu)])
+        for a, b in zip(*outs):
+            assert np.array_equal(a, b)
