@@ -11,6 +11,10 @@ Value distributions (the workloads' recipe):
     rounded once to fp16.
   * Q4_0 weights: nibbles uniform in 0..15 (so each packed byte is uniform in
     0..255); scales |N(0,1)|*0.02 rounded once to fp16.
+  * K-quant weights (256-element super-blocks): every packed byte of codes,
+    fifth bits, 6-bit sub-block scales/mins (Q4_K, Q5_K) uniform in 0..255;
+    Q6_K sub-block scales int8 uniform in [-128, 127]; the super-block d and
+    dmin |N(0,1)|*0.001 rounded once to fp16.
   * activations: fp32 N(0,1).
   * MoE router logits: fp32 N(0,1); shared-expert gate scalar: fp32 N(0,1).
 Seeds: workload i (1-based, in the order below) uses 1000*i + s.
@@ -21,8 +25,13 @@ import numpy as np
 
 Q4_0 = 4
 Q8_0 = 8
+Q4_K = 12
+Q5_K = 13
+Q6_K = 14
 BLOCK_BYTES = {Q4_0: 18, Q8_0: 34}
-SCALE_C = {Q8_0: 0.01, Q4_0: 0.02}
+SCALE_C = {Q8_0: 0.01, Q4_0: 0.02, Q4_K: 0.001, Q5_K: 0.001, Q6_K: 0.001}
+# K-quant super-blocks: bytes per 256 elements
+K_BLOCK_BYTES = {Q4_K: 144, Q5_K: 176, Q6_K: 210}
 
 
 def seed_for(workload: int, s: int = 0) -> int:
@@ -61,6 +70,34 @@ def gen_weights(wtype: int, rows: int, k: int, seed: int, scale_c: float | None 
     else:
         raise ValueError("unknown weight type %r" % wtype)
     return layout_blocks(d, q)
+
+
+def gen_weights_k(wtype: int, rows: int, k: int, seed: int) -> np.ndarray:
+    """Random K-quant weight matrix [rows][k/256 super-blocks] as raw bytes.
+
+    Q4_K / Q5_K: fp16 d, fp16 dmin, then the rest of the super-block as
+    uniform random bytes (12 bytes of packed 6-bit scales and mins, the fifth
+    bits of Q5_K, the nibbles).  Q6_K: 208 uniform random bytes (low nibbles,
+    2-bit highs, int8 sub-block scales) then fp16 d."""
+    assert k % 256 == 0
+    n = rows * (k // 256)
+    bb = K_BLOCK_BYTES[wtype]
+    rng = np.random.default_rng(seed)
+    c = SCALE_C[wtype]
+    out = np.empty((n, bb), np.uint8)
+    if wtype in (Q4_K, Q5_K):
+        d = fp16_scales(rng, n, c)
+        dmin = fp16_scales(rng, n, c)
+        out[:, 0:2] = np.ascontiguousarray(d.astype("<f2")).view(np.uint8).reshape(n, 2)
+        out[:, 2:4] = np.ascontiguousarray(dmin.astype("<f2")).view(np.uint8).reshape(n, 2)
+        out[:, 4:] = rng.integers(0, 256, size=(n, bb - 4), dtype=np.uint8)
+    elif wtype == Q6_K:
+        d = fp16_scales(rng, n, c)
+        out[:, :208] = rng.integers(0, 256, size=(n, 208), dtype=np.uint8)
+        out[:, 208:] = np.ascontiguousarray(d.astype("<f2")).view(np.uint8).reshape(n, 2)
+    else:
+        raise ValueError("not a K-quant type %r" % wtype)
+    return out.reshape(-1)
 
 
 def gen_activation(n_tok: int, k: int, seed: int) -> np.ndarray:

@@ -26,7 +26,11 @@ _LIB = os.path.join(_HERE, "libzqref.so")
 
 Q4_0 = 4
 Q8_0 = 8
+Q4_K = 12
+Q5_K = 13
+Q6_K = 14
 BLOCK_BYTES = {Q4_0: 18, Q8_0: 34}
+K_BLOCK_BYTES = {Q4_K: 144, Q5_K: 176, Q6_K: 210}
 
 _ERR = {0: "ok", -1: "invalid argument", -2: "non-finite input",
         -3: "int32 overflow", -4: "Q4_0 identity failed"}
@@ -73,6 +77,11 @@ def lib() -> ctypes.CDLL:
         L.zqref_moe_route.argtypes = [P, I, I, P, P, P]
         L.zqref_swiglu.argtypes = [P, I64, I64, P]
         L.zqref_gemm_entries.argtypes = [I, P, I64, I64, P, P, I64, P, P, I64, P, P]
+        L.zqref_k_block_bytes.restype = I64
+        L.zqref_k_block_bytes.argtypes = [I]
+        L.zqref_k_decode.argtypes = [I, P, P, P, P, P, P]
+        L.zqref_k_dmmv_rows.argtypes = [I, P, I64, I64, P, P, P, P, I64, P, P, P]
+        L.zqref_k_bruteforce.argtypes = [I, P, I64, I64, P, P, P, I64, P]
         _lib = L
     return _lib
 
@@ -179,6 +188,50 @@ def quant_error_bound(wtype, w, rows, k, dx, rows_eval=None):
     _check(lib().zqref_quant_error_bound(wtype, _p(w), rows, k, _p(dx), _p(idx), n, _p(out)),
            "quant_error_bound")
     return out
+
+
+def k_decode(wtype: int, sb: np.ndarray):
+    """One K-quant super-block -> (d, dmin, scales, mins, codes[256])."""
+    b = _c(sb, np.uint8)
+    d, dmin = ctypes.c_double(), ctypes.c_double()
+    sc = np.zeros(16, np.int32)
+    mn = np.zeros(16, np.int32)
+    q = np.empty(256, np.int32)
+    _check(lib().zqref_k_decode(wtype, _p(b), ctypes.byref(d), ctypes.byref(dmin), _p(sc), _p(mn),
+                                _p(q)), "k_decode")
+    n = 16 if wtype == Q6_K else 8
+    return d.value, dmin.value, sc[:n], mn[:n], q
+
+
+def k_dmmv(wtype: int, w: np.ndarray, rows: int, k: int, qx, dx, rows_eval=None, y_prev=None,
+           want_isums: bool = False):
+    """fp64 reference rows over K-quant weights: (y_ref, S) or
+    (y_ref, S, isums[n_eval][K/32])."""
+    w = _c(w, np.uint8)
+    assert w.size >= rows * (k // 256) * K_BLOCK_BYTES[wtype]
+    qx = _c(qx, np.int8)
+    dx = _c(dx, np.float32)
+    idx = None if rows_eval is None else _c(rows_eval, np.int64)
+    n = rows if idx is None else idx.size
+    y = np.empty(n, np.float64)
+    S = np.empty(n, np.float64)
+    yp = None if y_prev is None else _c(y_prev, np.float32)
+    isums = np.empty((n, k // 32), np.int32) if want_isums else None
+    _check(lib().zqref_k_dmmv_rows(wtype, _p(w), rows, k, _p(qx), _p(dx), _p(yp), _p(idx), n,
+                                   _p(y), _p(S), _p(isums)), "k_dmmv_rows")
+    return (y, S, isums) if want_isums else (y, S)
+
+
+def k_bruteforce(wtype, w, rows, k, qx, dx, rows_eval=None):
+    w = _c(w, np.uint8)
+    qx = _c(qx, np.int8)
+    dx = _c(dx, np.float32)
+    idx = None if rows_eval is None else _c(rows_eval, np.int64)
+    n = rows if idx is None else idx.size
+    y = np.empty(n, np.float64)
+    _check(lib().zqref_k_bruteforce(wtype, _p(w), rows, k, _p(qx), _p(dx), _p(idx), n, _p(y)),
+           "k_bruteforce")
+    return y
 
 
 def argmax_f32(y: np.ndarray) -> int:

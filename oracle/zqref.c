@@ -29,6 +29,23 @@
  *     "Bringing ZINC to NVIDIA", section "The roadmap: from 70 to a coherent
  *     token", and "CUDA backend for ZINC", section 5 (milestone M1).
  *   - argmax "exact": "CUDA backend for ZINC", section 5 (M1 kernel library).
+ *   - the K-quant super-blocks Q4_K / Q5_K / Q6_K (256 elements), also GGML's
+ *     layouts bit for bit: "Bringing ZINC to NVIDIA", section "The reassuring
+ *     result" ("Q4_K/Q5_K/Q6_K 256-element super-blocks"), and "CUDA backend
+ *     for ZINC", section 5 ("canonical GGML Q4_K dequant + matvec,
+ *     cross-checked vs llama.cpp get_scale_min_k4").  Layouts, as published
+ *     with GGML:
+ *       Q4_K (144 B): fp16 d, fp16 dmin, 12 bytes of 6-bit sub-block scales
+ *         and mins, 128 bytes of nibbles.  Eight sub-blocks of 32; element e
+ *         of 64-group g (e < 32: low nibble, else high nibble of byte
+ *         16 + 32g + e%32) belongs to sub-block 2g + e/32; value
+ *         d*sc*q - dmin*m with q in 0..15.
+ *       Q5_K (176 B): as Q4_K, plus 32 bytes of fifth bits after the scales
+ *         (bit 2g for the low-nibble element, 2g+1 for the high-nibble one,
+ *         in byte e%32), the nibbles following; q in 0..31.
+ *       Q6_K (210 B): 128 bytes of low nibbles, 64 bytes of 2-bit highs, 16
+ *         int8 sub-block scales, fp16 d last.  Sixteen sub-blocks of 16
+ *         (element index / 16); value d*scale*(q - 32), q in 0..63.
  *
  * Readings taken where the pages are silent (each is listed with its reason
  * in the design notes of the repository):
@@ -56,6 +73,9 @@
 
 #define ZQREF_Q4_0 4
 #define ZQREF_Q8_0 8
+#define ZQREF_Q4_K 12
+#define ZQREF_Q5_K 13
+#define ZQREF_Q6_K 14
 
 int zqref_version(void) { return 1; }
 
@@ -301,6 +321,168 @@ int zqref_quant_error_bound(int wtype, const uint8_t *w, int64_t rows, int64_t k
             e += fabs(block_scale(blk)) * ((double)dx[b] / 2.0) * sw;
         }
         bound[i] = e;
+    }
+    return ZQREF_OK;
+}
+
+/* ------------------------------------------------- K-quant super-blocks -- */
+
+int64_t zqref_k_block_bytes(int wtype)
+{
+    if (wtype == ZQREF_Q4_K) return 144;
+    if (wtype == ZQREF_Q5_K) return 176;
+    if (wtype == ZQREF_Q6_K) return 210;
+    return ZQREF_EINVAL;
+}
+
+static uint16_t le16(const uint8_t *p) { return (uint16_t)(p[0] | (p[1] << 8)); }
+
+/* The 6-bit scale and min of sub-block j (0..7) from the 12 packed bytes s:
+ * sub-blocks 0-3 keep their scale in the low 6 bits of s[j] and their min in
+ * the low 6 bits of s[j+4]; sub-blocks 4-7 keep the low 4 bits of scale and
+ * min in the two nibbles of s[j+4] and their top 2 bits in the top 2 bits of
+ * s[j-4] (scale) and s[j] (min). */
+static void k_scale_min(const uint8_t *s, int j, int32_t *sc, int32_t *m)
+{
+    if (j < 4) {
+        *sc = s[j] & 63;
+        *m = s[j + 4] & 63;
+    } else {
+        *sc = (s[j + 4] & 15) | ((s[j - 4] >> 6) << 4);
+        *m = (s[j + 4] >> 4) | ((s[j] >> 6) << 4);
+    }
+}
+
+/* Decode one super-block: d, dmin (0 for Q6_K), the sub-block scales and
+ * mins (8 of each for Q4_K / Q5_K, 16 scales for Q6_K with mins 0), and the
+ * 256 unsigned codes q in element order. */
+int zqref_k_decode(int wtype, const uint8_t *sb, double *d, double *dmin, int32_t *sc,
+                   int32_t *mn, int32_t *q)
+{
+    if (wtype == ZQREF_Q4_K || wtype == ZQREF_Q5_K) {
+        *d = zqref_fp16_to_f64(le16(sb));
+        *dmin = zqref_fp16_to_f64(le16(sb + 2));
+        for (int j = 0; j < 8; j++) k_scale_min(sb + 4, j, &sc[j], &mn[j]);
+        const uint8_t *qh = sb + 16;
+        const uint8_t *qs = sb + (wtype == ZQREF_Q4_K ? 16 : 48);
+        for (int e = 0; e < 256; e++) {
+            int g = e / 64, l = e % 32, hi = (e % 64) >= 32;
+            int v = hi ? (qs[32 * g + l] >> 4) : (qs[32 * g + l] & 15);
+            if (wtype == ZQREF_Q5_K) v |= ((qh[l] >> (2 * g + hi)) & 1) << 4;
+            q[e] = v;
+        }
+        return ZQREF_OK;
+    }
+    if (wtype == ZQREF_Q6_K) {
+        const uint8_t *ql = sb, *qh = sb + 128;
+        const int8_t *scales = (const int8_t *)(sb + 192);
+        *d = zqref_fp16_to_f64(le16(sb + 208));
+        *dmin = 0.0;
+        for (int j = 0; j < 16; j++) {
+            sc[j] = scales[j];
+            mn[j] = 0;
+        }
+        for (int e = 0; e < 256; e++) {
+            int h = e / 128, c = (e % 128) / 32, l = e % 32;
+            int lo = ql[64 * h + 32 * (c & 1) + l];
+            lo = (c < 2) ? (lo & 15) : (lo >> 4);
+            int top = (qh[32 * h + l] >> (2 * c)) & 3;
+            q[e] = lo | (top << 4);
+        }
+        return ZQREF_OK;
+    }
+    return ZQREF_EINVAL;
+}
+
+/* Row references over K-quant weights against the int8 activation blocks of
+ * 32.  Each activation block b lines up with one 32-element sub-block of
+ * Q4_K / Q5_K, or with two 16-element sub-blocks of Q6_K.  Per block:
+ *   Q4_K / Q5_K: isum_b = sum q*qx, s_b = sum qx (exact integers),
+ *     t_b = dx_b * (d*sc*isum_b - dmin*m*s_b),
+ *     S += |dx_b| * (|d*sc*isum_b| + |dmin*m*s_b|);
+ *   Q6_K: isum_b = sum sc(e) * (q - 32) * qx (the scale of each element's
+ *     16-element sub-block; an exact integer), t_b = dx_b * d * isum_b,
+ *     S += |t_b|.
+ * y_ref = sum_b t_b in fp64, sequentially; y_prev / row_idx / isums as in
+ * zqref_dmmv_rows. */
+int zqref_k_dmmv_rows(int wtype, const uint8_t *w, int64_t rows, int64_t k, const int8_t *qx,
+                      const float *dx, const float *y_prev, const int64_t *row_idx,
+                      int64_t n_eval, double *y_ref, double *S, int32_t *isums)
+{
+    int64_t bb = zqref_k_block_bytes(wtype);
+    if (bb < 0 || k <= 0 || k % 256 != 0 || rows < 0 || n_eval < 0) return ZQREF_EINVAL;
+    int64_t nsb = k / 256, nb = k / 32;
+    for (int64_t i = 0; i < n_eval; i++) {
+        int64_t r = row_idx ? row_idx[i] : i;
+        if (r < 0 || r >= rows) return ZQREF_EINVAL;
+        double y = 0.0, sabs = 0.0;
+        for (int64_t u = 0; u < nsb; u++) {
+            double d, dmin;
+            int32_t sc[16], mn[16], q[256];
+            int rc = zqref_k_decode(wtype, w + (r * nsb + u) * bb, &d, &dmin, sc, mn, q);
+            if (rc != ZQREF_OK) return rc;
+            for (int j = 0; j < 8; j++) {
+                int64_t b = u * 8 + j;
+                const int8_t *xb = qx + b * 32;
+                int64_t is = 0, sx = 0;
+                for (int e = 0; e < 32; e++) {
+                    int64_t code = q[32 * j + e];
+                    if (wtype == ZQREF_Q6_K) is += (int64_t)sc[(32 * j + e) / 16] * (code - 32) * xb[e];
+                    else is += code * xb[e];
+                    sx += xb[e];
+                }
+                if (is > INT32_MAX || is < INT32_MIN) return ZQREF_EOVERFLOW;
+                if (isums) isums[i * nb + b] = (int32_t)is;
+                double t, tabs;
+                if (wtype == ZQREF_Q6_K) {
+                    t = (double)dx[b] * d * (double)is;
+                    tabs = fabs(t);
+                } else {
+                    double a1 = d * (double)sc[j] * (double)is;
+                    double a2 = dmin * (double)mn[j] * (double)sx;
+                    t = (double)dx[b] * (a1 - a2);
+                    tabs = fabs((double)dx[b]) * (fabs(a1) + fabs(a2));
+                }
+                y += t;
+                sabs += tabs;
+            }
+        }
+        if (y_prev) {
+            y += (double)y_prev[r];
+            sabs += fabs((double)y_prev[r]);
+        }
+        y_ref[i] = y;
+        if (S) S[i] = sabs;
+    }
+    return ZQREF_OK;
+}
+
+/* Brute force: every weight dequantized to fp64 on its own (d*sc*q - dmin*m,
+ * or d*sc*(q-32)), every activation element dx*qx, plain dot product. */
+int zqref_k_bruteforce(int wtype, const uint8_t *w, int64_t rows, int64_t k, const int8_t *qx,
+                       const float *dx, const int64_t *row_idx, int64_t n_eval, double *y_bf)
+{
+    int64_t bb = zqref_k_block_bytes(wtype);
+    if (bb < 0 || k <= 0 || k % 256 != 0) return ZQREF_EINVAL;
+    int64_t nsb = k / 256;
+    for (int64_t i = 0; i < n_eval; i++) {
+        int64_t r = row_idx ? row_idx[i] : i;
+        if (r < 0 || r >= rows) return ZQREF_EINVAL;
+        double y = 0.0;
+        for (int64_t u = 0; u < nsb; u++) {
+            double d, dmin;
+            int32_t sc[16], mn[16], q[256];
+            int rc = zqref_k_decode(wtype, w + (r * nsb + u) * bb, &d, &dmin, sc, mn, q);
+            if (rc != ZQREF_OK) return rc;
+            for (int e = 0; e < 256; e++) {
+                double wv;
+                if (wtype == ZQREF_Q6_K) wv = d * (double)sc[e / 16] * (double)(q[e] - 32);
+                else wv = d * (double)sc[e / 32] * (double)q[e] - dmin * (double)mn[e / 32];
+                int64_t j = u * 256 + e;
+                y += wv * ((double)dx[j / 32] * (double)qx[j]);
+            }
+        }
+        y_bf[i] = y;
     }
     return ZQREF_OK;
 }

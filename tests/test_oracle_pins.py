@@ -480,3 +480,214 @@ def test_p3f_halfway_after_rounding(ref):
     q, d, s = ref.quantize_act(x)
     for i, want in hits:
         assert int(q[i]) == want, (i, want, int(q[i]))
+
+
+# ------------------------------------------------------- K-quants (P15) ----
+# An encoder written here from the byte and bit positions of the published
+# layouts (element index -> byte, nibble, bit), independent of the oracle's
+# decoder, which walks the other way.
+
+Q4_K, Q5_K, Q6_K = 12, 13, 14
+KBB = {Q4_K: 144, Q5_K: 176, Q6_K: 210}
+
+
+def k_encode(wtype, d, dmin, sc, mn, q):
+    """Pack one super-block.  sc/mn: 8 values in 0..63 (Q4_K, Q5_K) or 16
+    int8 scales (Q6_K); q: 256 codes (0..15, 0..31 or 0..63)."""
+    out = np.zeros(KBB[wtype], np.uint8)
+    if wtype in (Q4_K, Q5_K):
+        out[0:2] = np.frombuffer(np.float16(d).astype("<f2").tobytes(), np.uint8)
+        out[2:4] = np.frombuffer(np.float16(dmin).astype("<f2").tobytes(), np.uint8)
+        s = np.zeros(12, np.int64)
+        for j in range(4):
+            s[j] = sc[j] | ((sc[j + 4] >> 4) << 6)
+            s[j + 4] = mn[j] | ((mn[j + 4] >> 4) << 6)
+            s[j + 8] = (sc[j + 4] & 15) | ((mn[j + 4] & 15) << 4)
+        out[4:16] = s
+        code0 = 16 if wtype == Q4_K else 48
+        for e in range(256):
+            g, w = divmod(e, 64)
+            hi, l = divmod(w, 32)
+            out[code0 + 32 * g + l] |= (q[e] & 15) << (4 * hi)
+            if wtype == Q5_K:
+                out[16 + l] |= ((q[e] >> 4) & 1) << (2 * g + hi)
+    else:
+        for e in range(256):
+            h, rest = divmod(e, 128)
+            c, l = divmod(rest, 32)
+            out[64 * h + 32 * (c % 2) + l] |= (q[e] & 15) << (4 * (c // 2))
+            out[128 + 32 * h + l] |= ((q[e] >> 4) & 3) << (2 * c)
+        out[192:208] = np.asarray(sc, np.int64).astype(np.int8).view(np.uint8)
+        out[208:210] = np.frombuffer(np.float16(d).astype("<f2").tobytes(), np.uint8)
+    return out
+
+
+def golden_kquant():
+    rows = []
+    for line in open(os.path.join(GOLDEN, "kquant_superblocks.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        typ, head, code, high, vals = [f.strip() for f in line.split("|")]
+        wt = {"Q4_K": Q4_K, "Q5_K": Q5_K, "Q6_K": Q6_K}[typ]
+        hb = []
+        for tok in head.split():
+            hb += list(bytes.fromhex(tok))   # 4-digit tokens: little-endian fp16 bytes as written
+        sb = np.zeros(KBB[wt], np.uint8)
+        if wt == Q4_K:
+            sb[0:16] = hb
+            sb[16:] = int(code, 16)
+        elif wt == Q5_K:
+            sb[0:16] = hb
+            sb[16:48] = int(high, 16)
+            sb[48:] = int(code, 16)
+        else:
+            sb[0:128] = int(code, 16)
+            sb[128:192] = int(high, 16)
+            sb[192:210] = hb
+        exp = {int(a): float(b) for a, b in (t.split(":") for t in vals.split())}
+        rows.append((wt, sb, exp))
+    return rows
+
+
+def dequant_one(ref, wt, sb, e):
+    """Element e of super-block sb through the oracle's brute-force path:
+    activation one-hot at e with code 1 and scale 1."""
+    qx = np.zeros(256, np.int8)
+    qx[e] = 1
+    dx = np.ones(8, np.float32)
+    return float(ref.k_bruteforce(wt, sb, 1, 256, qx, dx)[0])
+
+
+def test_p15_golden_superblocks(ref):
+    """Hand-worked super-blocks (tests/golden/kquant_superblocks.txt): the
+    decoder and the brute-force path give the values derived by hand."""
+    g = golden_kquant()
+    assert [w for w, _, _ in g] == [Q4_K, Q5_K, Q6_K]
+    for wt, sb, exp in g:
+        d, dmin, sc, mn, q = ref.k_decode(wt, sb)
+        for e, v in exp.items():
+            if wt == Q6_K:
+                assert d * sc[e // 16] * (q[e] - 32) == v, (wt, e)
+            else:
+                assert d * sc[e // 32] * q[e] - dmin * mn[e // 32] == v, (wt, e)
+            assert dequant_one(ref, wt, sb, e) == v, (wt, e)
+    # the scales of the Q4_K example, spelled out in the fixture
+    d, dmin, sc, mn, _ = ref.k_decode(Q4_K, g[0][1])
+    assert (d, dmin) == (1.0, 0.5)
+    assert list(sc) == [1, 2, 3, 4, 17, 35, 53, 7] and list(mn) == [5, 6, 7, 8, 18, 36, 54, 8]
+
+
+@pytest.mark.parametrize("wt", [Q4_K, Q5_K, Q6_K])
+def test_p15_encode_decode_round_trip(ref, wt):
+    rng = np.random.default_rng(wt)
+    for _ in range(50):
+        d, dmin = float(np.float16(rng.uniform(0.01, 2))), float(np.float16(rng.uniform(0, 2)))
+        if wt == Q6_K:
+            sc = rng.integers(-128, 128, 16)
+            mn = np.zeros(16, np.int64)
+            q = rng.integers(0, 64, 256)
+            dmin = 0.0
+        else:
+            sc = rng.integers(0, 64, 8)
+            mn = rng.integers(0, 64, 8)
+            q = rng.integers(0, 32 if wt == Q5_K else 16, 256)
+        dd, dm, s2, m2, q2 = ref.k_decode(wt, k_encode(wt, d, dmin, sc, mn, q))
+        assert dd == d and dm == dmin
+        assert np.array_equal(s2, sc) and np.array_equal(m2, mn) and np.array_equal(q2, q)
+
+
+def test_p15_scale_min_exhaustive(ref):
+    """Every 6-bit (scale, min) pair at every sub-block position."""
+    for j in range(8):
+        for v in range(64):
+            sc = np.zeros(8, np.int64)
+            mn = np.zeros(8, np.int64)
+            sc[j] = v
+            mn[j] = 63 - v
+            _, _, s2, m2, _ = ref.k_decode(Q4_K, k_encode(Q4_K, 1.0, 1.0, sc, mn, np.zeros(256, np.int64)))
+            assert np.array_equal(s2, sc) and np.array_equal(m2, mn), (j, v)
+
+
+@pytest.mark.parametrize("wt", [Q4_K, Q5_K, Q6_K])
+def test_p15_single_element_positions(ref, wt):
+    """A lone code at each of the 256 positions lands at that element (and
+    nowhere else) with the scale of its sub-block."""
+    top = {Q4_K: 15, Q5_K: 31, Q6_K: 63}[wt]
+    base = 32 if wt == Q6_K else 0
+    sc = np.arange(1, 17) if wt == Q6_K else np.arange(1, 9)
+    for e in range(256):
+        q = np.full(256, base, np.int64)
+        q[e] = top
+        sb = k_encode(wt, 0.5, 0.0, sc, np.zeros(len(sc), np.int64), q)
+        _, _, _, _, q2 = ref.k_decode(wt, sb)
+        assert np.array_equal(q2, q), (wt, e)
+        sub = e // 16 if wt == Q6_K else e // 32
+        assert dequant_one(ref, wt, sb, e) == 0.5 * sc[sub] * (top - base)
+
+
+@pytest.mark.parametrize("wt", [Q4_K, Q5_K, Q6_K])
+def test_p15_closed_form_rows(ref, wt):
+    """Unit scales and a constant code: every weight equals one number c, so
+    each row is c * sum_b dx_b * s_b, exactly."""
+    rows, k = 3, 512
+    if wt == Q6_K:
+        sb = k_encode(wt, 1.0, 0.0, np.ones(16, np.int64), np.zeros(16, np.int64),
+                      np.full(256, 33, np.int64))            # value 1*1*(33-32) = 1
+        c = 1.0
+    else:
+        sb = k_encode(wt, 1.0, 0.5, np.ones(8, np.int64), np.full(8, 2, np.int64),
+                      np.full(256, 3, np.int64))             # value 3 - 1 = 2
+        c = 2.0
+    w = np.tile(sb, rows * (k // 256))
+    x = inputs.gen_activation(1, k, 31)
+    qx, dx, sx = ref.quantize_act(x)
+    y, S = ref.k_dmmv(wt, w, rows, k, qx, dx)
+    expect = c * sum(float(dx[b]) * int(sx[b]) for b in range(k // 32))
+    assert np.all(np.abs(y - expect) <= 1e-12 * S)
+
+
+@pytest.mark.parametrize("wt", [Q4_K, Q5_K, Q6_K])
+def test_p15_bruteforce_and_isums(ref, wt):
+    """Random super-blocks: the per-block references equal the element-wise
+    brute force, and the integer sums equal numpy's on the encoder's codes."""
+    rng = np.random.default_rng(100 + wt)
+    rows, k = 4, 768
+    sbs, codes, scs = [], [], []
+    for _ in range(rows * k // 256):
+        if wt == Q6_K:
+            sc, mn, q = rng.integers(-128, 128, 16), np.zeros(16, np.int64), rng.integers(0, 64, 256)
+        else:
+            sc, mn = rng.integers(0, 64, 8), rng.integers(0, 64, 8)
+            q = rng.integers(0, 32 if wt == Q5_K else 16, 256)
+        sbs.append(k_encode(wt, float(np.float16(rng.uniform(0.001, 0.01))),
+                            float(np.float16(rng.uniform(0, 0.01))), sc, mn, q))
+        codes.append(q)
+        scs.append(sc)
+    w = np.concatenate(sbs)
+    x = inputs.gen_activation(1, k, 32)
+    qx, dx, sx = ref.quantize_act(x)
+    y, S, isums = ref.k_dmmv(wt, w, rows, k, qx, dx, want_isums=True)
+    yb = ref.k_bruteforce(wt, w, rows, k, qx, dx)
+    assert np.all(np.abs(y - yb) <= 1e-12 * S)
+    nsb = k // 256
+    for r in range(rows):
+        for b in range(k // 32):
+            u, j = divmod(b, 8)
+            q = codes[r * nsb + u][32 * j:32 * j + 32].astype(np.int64)
+            xb = qx[32 * b:32 * b + 32].astype(np.int64)
+            if wt == Q6_K:
+                s16 = scs[r * nsb + u][np.arange(32 * j, 32 * j + 32) // 16].astype(np.int64)
+                expect = int(np.sum(s16 * (q - 32) * xb))
+            else:
+                expect = int(np.sum(q * xb))
+            assert isums[r, b] == expect, (r, b)
+
+
+def test_p15_generator_layout():
+    """gen_weights_k: the fp16 super-block scales sit where the layouts put
+    them, with the stated distribution."""
+    for wt in (Q4_K, Q5_K, Q6_K):
+        w = inputs.gen_weights_k(wt, 64, 1024, 5).reshape(-1, KBB[wt])
+        off = 208 if wt == Q6_K else 0
+        d = w[:, off:off + 2].copy().view("<f2").astype(np.float64).ravel()
+        assert np.all(d >= 0) and 0.0004 < d.mean() < 0.0012
