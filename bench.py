@@ -6,7 +6,7 @@ blocks, then the Q4_0 DMMV of a 4096 x 4096 weight matrix.  Weights rotate
 over distinct copies whose total is more than twice the 256 MB MALL, so every
 step streams its weights from HBM.  Prints ONE JSON line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1..5]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1..6]
 
 Timing: a GPU-side spin kernel is queued ahead of the timed region so that the
 K steps are enqueued before the GPU reaches them and run back to back (host
@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -175,6 +175,79 @@ class DmmvWorkload(Workload):
                     sample="%d full steps (quantize + %d-row DMMV%s) of this workload on one "
                            "host thread, %.1f s" % (n, self.rows, " + argmax" if self.argmax else "",
                                                     el))
+
+
+class DmmvKWorkload(Workload):
+    """Quantize + DMMV over Q4_K super-blocks (two launches)."""
+    dominant_name = "dmmv_q4k_kernel"
+
+    def __init__(self, wl):
+        from block_quant_matrix_amd import inputs
+        cfg = inputs.WORKLOADS[wl]
+        self.wl = wl
+        self.name = cfg["name"]
+        self.wtype, self.rows, self.k = cfg["wtype"], cfg["rows"], cfg["k"]
+        self.nb = self.k // 32
+        self.wbytes = self.rows * (self.k // 256) * inputs.K_BLOCK_BYTES[self.wtype]
+        # the DMMV reads the weights, the int8 codes, scales and block sums,
+        # and writes fp32 rows; the step adds the fp32 activation the
+        # quantizer reads and the codes, scales and sums it writes
+        self.dmmv_bytes = self.wbytes + self.k + 8 * self.nb + 4 * self.rows
+        self.step_bytes = self.dmmv_bytes + 4 * self.k + self.k + 8 * self.nb
+        # two launches per step: 2000 steps keep the timed region's launches
+        # within one hardware queue, so all of them are enqueued ahead of the GPU
+        self.steps, self.warmup = 2000, 100
+
+    def setup(self, torch, zq, inputs):
+        self.torch, self.zq = torch, zq
+        self.ncopy = copies_for(self.wbytes)
+        host = [inputs.gen_weights_k(self.wtype, self.rows, self.k, inputs.seed_for(self.wl, c))
+                for c in range(self.ncopy)]
+        self.w = [torch.from_numpy(h).to("cuda") for h in host]
+        self.w_host0 = host[0]
+        del host
+        self.x_host = inputs.gen_activation(1, self.k, inputs.seed_for(self.wl) + 1)
+        self.x = torch.from_numpy(self.x_host).to("cuda")
+        self.qx = torch.empty(self.k, dtype=torch.int8, device="cuda")
+        self.dx = torch.empty(self.nb, dtype=torch.float32, device="cuda")
+        self.sx = torch.empty(self.nb, dtype=torch.int32, device="cuda")
+        self.y = torch.empty(self.rows, dtype=torch.float32, device="cuda")
+
+    def step(self, i):
+        self.zq.zq_quantize_act(self.x, 1, self.k, self.k, self.qx, self.dx, self.sx)
+        self.zq.zq_dmmv_q4_k(self.w[i % self.ncopy], self.rows, self.k, self.qx, self.dx, self.sx,
+                             self.y)
+
+    def prepare_dominant(self):
+        self.zq.zq_quantize_act(self.x, 1, self.k, self.k, self.qx, self.dx, self.sx)
+
+    def dominant(self, i):
+        self.zq.zq_dmmv_q4_k(self.w[i % self.ncopy], self.rows, self.k, self.qx, self.dx, self.sx,
+                             self.y)
+
+    def value(self, ms):
+        return self.step_bytes / (ms * 1e-3) / 1e9, "GB/s"
+
+    def achieved(self, ms):
+        return self.dmmv_bytes / (ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s", self.dmmv_bytes
+
+    def extra(self, ms):
+        return {"rows_per_s": self.rows / (ms * 1e-3)}
+
+    def cpu_baseline(self, seconds):
+        import oracle
+        n, t0 = 0, time.perf_counter()
+        while True:
+            qx, dx, sx = oracle.quantize_act(self.x_host)
+            oracle.k_dmmv(self.wtype, self.w_host0, self.rows, self.k, qx, dx)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+        per = el / n
+        return dict(value=self.step_bytes / per / 1e9, unit="GB/s", cores=1, kind="oracle",
+                    sample="%d full steps (quantize + %d-row Q4_K DMMV) of this workload on one "
+                           "host thread, %.1f s" % (n, self.rows, el))
 
 
 class MoeWorkload(Workload):
@@ -361,6 +434,8 @@ def make_workload(wl):
         return DmmvWorkload(wl)
     if wl == 4:
         return MoeWorkload()
+    if wl == 6:
+        return DmmvKWorkload(wl)
     return GemmWorkload()
 
 

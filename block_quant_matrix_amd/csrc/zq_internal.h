@@ -53,6 +53,10 @@ struct DmmvF32Args {
 // workgroup; with a.out_idx also set, the final argmax follows.
 constexpr int kArgmaxMaxParts = 2048;
 int launch_dmmv_f32x(int wtype, DmmvF32Args a, hipStream_t stream);
+
+// DMMV over Q4_K super-blocks (a.nb = k/32, k a multiple of 256); isums
+// selects the per-block integer sums instead of rows.
+int launch_dmmv_q4k(DmmvArgs a, bool isums, hipStream_t stream);
 // Reduce nparts (value, index) partials to the argmax index.
 int launch_argmax_final(const void *part, int nparts, int32_t *out_idx, hipStream_t stream);
 

@@ -122,6 +122,8 @@ WORKLOADS = {
     4: dict(name="q4_0_moe_128e_top8_shared_2048x512", wtype=Q4_0, n_routed=128, top_k=8,
             d_model=2048, d_ff=512),
     5: dict(name="q4_0_prefill_gemm_m512_n5120_k5120", wtype=Q4_0, m=512, n=5120, k=5120),
+    # K-quant DMMV: the headline shape over the format the pages' experts use
+    6: dict(name="q4_k_dmmv_4096x4096", wtype=Q4_K, rows=4096, k=4096),
 }
 
 

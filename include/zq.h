@@ -54,7 +54,7 @@ enum zq_status {
 };
 
 enum zq_flags { ZQ_ACCUMULATE = 1 /* y += W.x instead of y = W.x */ };
-enum zq_wtype { ZQ_Q4_0 = 4, ZQ_Q8_0 = 8 };
+enum zq_wtype { ZQ_Q4_0 = 4, ZQ_Q8_0 = 8, ZQ_Q4_K = 12 };
 enum zq_moe_mode { ZQ_MOE_GATHER = 0, ZQ_MOE_WEIGHTED_SUM = 1 };
 
 int zq_version(void);
@@ -85,6 +85,20 @@ int zq_dmmv_q8_0(const void *w, int64_t rows, int64_t k, const int8_t *qx, const
 /* As zq_dmmv_q8_0 for Q4_0 weights.  sx [k/32] (block sums of qx) may be NULL,
  * in which case the kernel sums qx itself. */
 int zq_dmmv_q4_0(const void *w, int64_t rows, int64_t k, const int8_t *qx, const float *dx,
+                 const int32_t *sx, float *y, uint32_t flags, void *stream);
+
+/* The same DMMV over GGML Q4_K super-blocks (256 elements, 144 bytes, bit
+ * for bit: "Bringing ZINC to NVIDIA", section "The reassuring result";
+ * "CUDA backend for ZINC", section 5, dmmv_q4k): d, dmin, 6-bit sub-block
+ * scales and mins, nibbles; an element is d*sc*q - dmin*m.  With the int8
+ * activation blocks of 32 (zq_quantize_act), which line up with the
+ * 32-element sub-blocks:
+ *   y[r] (+)= sum_b dx[b] * (d*sc_b * isum[r][b] - dmin*m_b * sx[b]),
+ *   isum = sum q * qx (exact int32).
+ * k a multiple of 256; w 16-byte aligned, rows of k/256 super-blocks; sx may
+ * be NULL (the kernel then sums the codes).  zq_dmmv_isums with ZQ_Q4_K
+ * returns the isum of every 32-element sub-block. */
+int zq_dmmv_q4_k(const void *w, int64_t rows, int64_t k, const int8_t *qx, const float *dx,
                  const int32_t *sx, float *y, uint32_t flags, void *stream);
 
 /* DMMV from the fp32 activation in one launch: y (+)= W . Q(x), where Q is

@@ -109,6 +109,22 @@ def test_moe_gate_up_route_argument_errors():
     assert rc(qh=A + 0x1004) == zq.ZQ_EALIGN
 
 
+def test_q4k_argument_errors():
+    L = zq.lib()
+
+    def rc(w=A, rows=4, k=512, qx=B, dx=C, sx=None, y=D, flags=0):
+        return L.zq_dmmv_q4_k(w, rows, k, qx, dx, sx, y, flags, None)
+
+    assert rc(k=288) == zq.ZQ_EINVAL           # not a whole super-block
+    assert rc(rows=-1) == zq.ZQ_EINVAL
+    assert rc(flags=4) == zq.ZQ_EINVAL
+    assert rc(w=A + 8) == zq.ZQ_EALIGN         # super-blocks are read 16 bytes at a time
+    assert rc(qx=B + 4) == zq.ZQ_EALIGN
+    assert rc(y=None) == zq.ZQ_ENULL
+    assert L.zq_dmmv_isums(12, A, 4, 288, B, None, C, None) == zq.ZQ_EINVAL
+    assert L.zq_dmmv_isums(12, A + 4, 4, 512, B, None, C, None) == zq.ZQ_EALIGN
+
+
 def test_lmhead_argument_errors():
     L = zq.lib()
     ws = L.zq_dmmv_f32_argmax_workspace_bytes()
@@ -218,6 +234,7 @@ def test_other_argument_errors():
 def test_valid_arguments_without_gpu_report_no_device():
     """With every argument valid, the last check is the device: no GPU here."""
     assert rc_dmmv_q4() == zq.ZQ_EDEVICE
+    assert zq.lib().zq_dmmv_q4_k(A, 4, 512, B, C, None, D, 0, None) == zq.ZQ_EDEVICE
     L = zq.lib()
     assert L.zq_dmmv_f32_argmax(4, A, 248320, 2048, B, C, D, A + 0x8000,
                                 L.zq_dmmv_f32_argmax_workspace_bytes(), None) == zq.ZQ_EDEVICE
