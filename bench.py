@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6])
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7, 8])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -178,8 +178,9 @@ class DmmvWorkload(Workload):
 
 
 class DmmvKWorkload(Workload):
-    """Quantize + DMMV over Q4_K super-blocks (two launches)."""
-    dominant_name = "dmmv_q4k_kernel"
+    """Quantize + DMMV over K-quant super-blocks (Q4_K / Q5_K / Q6_K; two
+    launches)."""
+    dominant_name = "dmmv_k_kernel"
 
     def __init__(self, wl):
         from block_quant_matrix_amd import inputs
@@ -187,16 +188,24 @@ class DmmvKWorkload(Workload):
         self.wl = wl
         self.name = cfg["name"]
         self.wtype, self.rows, self.k = cfg["wtype"], cfg["rows"], cfg["k"]
+        self.tname = {inputs.Q4_K: "Q4_K", inputs.Q5_K: "Q5_K", inputs.Q6_K: "Q6_K"}[self.wtype]
+        self.dominant_name = "dmmv_k_kernel (%s)" % self.tname
         self.nb = self.k // 32
         self.wbytes = self.rows * (self.k // 256) * inputs.K_BLOCK_BYTES[self.wtype]
-        # the DMMV reads the weights, the int8 codes, scales and block sums,
-        # and writes fp32 rows; the step adds the fp32 activation the
-        # quantizer reads and the codes, scales and sums it writes
-        self.dmmv_bytes = self.wbytes + self.k + 8 * self.nb + 4 * self.rows
+        # the DMMV reads the weights, the int8 codes, scales (and for Q4_K /
+        # Q5_K the block sums), and writes fp32 rows; the step adds the fp32
+        # activation the quantizer reads and the codes, scales and sums it
+        # writes
+        sums = 4 * self.nb if self.wtype != inputs.Q6_K else 0
+        self.dmmv_bytes = self.wbytes + self.k + 4 * self.nb + sums + 4 * self.rows
         self.step_bytes = self.dmmv_bytes + 4 * self.k + self.k + 8 * self.nb
-        # two launches per step: 2000 steps keep the timed region's launches
-        # within one hardware queue, so all of them are enqueued ahead of the GPU
-        self.steps, self.warmup = 2000, 100
+        # two launches per step: at most 2000 steps keep the timed region's
+        # launches within one hardware queue, so all of them are enqueued
+        # ahead of the GPU
+        if self.wbytes > (64 << 20):
+            self.steps, self.warmup = 300, 20
+        else:
+            self.steps, self.warmup = 2000, 100
 
     def setup(self, torch, zq, inputs):
         self.torch, self.zq = torch, zq
@@ -213,17 +222,24 @@ class DmmvKWorkload(Workload):
         self.sx = torch.empty(self.nb, dtype=torch.int32, device="cuda")
         self.y = torch.empty(self.rows, dtype=torch.float32, device="cuda")
 
+    def _dmmv(self, i):
+        w = self.w[i % self.ncopy]
+        if self.tname == "Q4_K":
+            self.zq.zq_dmmv_q4_k(w, self.rows, self.k, self.qx, self.dx, self.sx, self.y)
+        elif self.tname == "Q5_K":
+            self.zq.zq_dmmv_q5_k(w, self.rows, self.k, self.qx, self.dx, self.sx, self.y)
+        else:
+            self.zq.zq_dmmv_q6_k(w, self.rows, self.k, self.qx, self.dx, self.y)
+
     def step(self, i):
         self.zq.zq_quantize_act(self.x, 1, self.k, self.k, self.qx, self.dx, self.sx)
-        self.zq.zq_dmmv_q4_k(self.w[i % self.ncopy], self.rows, self.k, self.qx, self.dx, self.sx,
-                             self.y)
+        self._dmmv(i)
 
     def prepare_dominant(self):
         self.zq.zq_quantize_act(self.x, 1, self.k, self.k, self.qx, self.dx, self.sx)
 
     def dominant(self, i):
-        self.zq.zq_dmmv_q4_k(self.w[i % self.ncopy], self.rows, self.k, self.qx, self.dx, self.sx,
-                             self.y)
+        self._dmmv(i)
 
     def value(self, ms):
         return self.step_bytes / (ms * 1e-3) / 1e9, "GB/s"
@@ -246,8 +262,8 @@ class DmmvKWorkload(Workload):
                 break
         per = el / n
         return dict(value=self.step_bytes / per / 1e9, unit="GB/s", cores=1, kind="oracle",
-                    sample="%d full steps (quantize + %d-row Q4_K DMMV) of this workload on one "
-                           "host thread, %.1f s" % (n, self.rows, el))
+                    sample="%d full steps (quantize + %d-row %s DMMV) of this workload on one "
+                           "host thread, %.1f s" % (n, self.rows, self.tname, el))
 
 
 class MoeWorkload(Workload):
@@ -434,7 +450,7 @@ def make_workload(wl):
         return DmmvWorkload(wl)
     if wl == 4:
         return MoeWorkload()
-    if wl == 6:
+    if wl in (6, 7, 8):
         return DmmvKWorkload(wl)
     return GemmWorkload()
 

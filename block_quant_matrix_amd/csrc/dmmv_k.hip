@@ -1,25 +1,43 @@
-// dmmv_k.hip -- DMMV over Q4_K super-blocks (gfx950, wave64).
+// dmmv_k.hip -- DMMV over GGML K-quant super-blocks: Q4_K, Q5_K, Q6_K
+// (gfx950, wave64).
 //
-// Q4_K is GGML's 256-element super-block, bit for bit (144 bytes): fp16 d,
-// fp16 dmin, twelve bytes of 6-bit sub-block scales and mins, and 128 bytes
-// of nibbles in four 64-element groups; within group g, byte l holds element
-// l of sub-block 2g in its low nibble and element l of sub-block 2g+1 in its
-// high nibble.  An element is d*sc*q - dmin*m with q in 0..15.
+// The three formats hold 256 elements per super-block, bit for bit as GGML
+// stores them:
+//   Q4_K (144 B): fp16 d, fp16 dmin, twelve bytes of 6-bit sub-block scales
+//     and mins, then 128 bytes of nibbles in four 64-element groups; within
+//     group g, byte l holds element l of sub-block 2g in its low nibble and
+//     element l of sub-block 2g+1 in its high nibble.  Element: d*sc*q -
+//     dmin*m, q in 0..15.
+//   Q5_K (176 B): as Q4_K with 32 bytes of fifth bits between the scales and
+//     the nibbles: bit 2g (2g+1) of byte l is the fifth bit of element l of
+//     sub-block 2g (2g+1).  q in 0..31.
+//   Q6_K (210 B): 128 bytes of low nibbles, 64 bytes of 2-bit highs, sixteen
+//     int8 scales of 16-element sub-blocks, fp16 d last.  In half h (128
+//     elements), element 32c+l (c = 0..3, l = 0..31) takes its low 4 bits
+//     from byte 64h+32(c&1)+l (low nibble for c < 2, high for c >= 2) and its
+//     top 2 bits from bits 2c..2c+1 of high byte 32h+l.  Element:
+//     d*sc*(q-32), q in 0..63.
 //
-// Against the int8 activation blocks of 32 (which line up with the 32-element
-// sub-blocks), a sub-block j with activation block b contributes
-//   dx_b * (d*sc_j * isum - dmin*m_j * s_b),   isum = sum q*qx,  s_b = sum qx,
-// two exact integers and the block's sum of codes.
+// Against the int8 activation blocks of 32 (aligned with the sub-blocks):
+//   Q4_K / Q5_K: block b (sub-block j) adds dx_b*(d*sc_j*isum - dmin*m_j*s_b),
+//     isum = sum q*qx and s_b = sum qx, both exact integers;
+//   Q6_K: block b (two 16-element sub-blocks) adds dx_b*d*isum_b with
+//     isum_b = sum sc*(q-32)*qx over its 32 elements, an exact integer.
 //
-// Mapping: one lane per 64-element group (a "unit", two sub-blocks and two
-// activation blocks).  The lane loads the 16-byte super-block header (d, dmin,
-// scales: one 16-byte load, shared by the four lanes of the super-block
-// through the cache) and its 32 bytes of nibbles (two 16-byte loads; every
-// super-block is 16-byte aligned because 144 = 9*16).  A row slot of LPR
-// lanes walks the row as in the Q4_0/Q8_0 DMMV (dmmv.hip): the lane keeps its
-// units' activation codes, scales and sums in registers, issues the loads of
-// RB row steps before any arithmetic, and the row partials are folded across
-// lanes by RowReduce.
+// Mapping: one lane per "unit" of 64 elements, four units per super-block;
+// a lane's position p = 0..3 inside its super-blocks is fixed (LPR is a
+// multiple of 4).  Q4_K / Q5_K unit p is group p (sub-blocks 2p, 2p+1: one
+// 16-byte header load shared by the super-block's four lanes through the
+// cache, 32 bytes of nibbles, and for Q5_K the 32 bytes of fifth bits).
+// Q6_K unit p is half h = p>>1, elements l in [16t, 16t+16) with t = p&1, of
+// all four quarters c: its low bits are two 16-byte runs, its high bits one,
+// all disjoint between the four lanes; since 210-byte super-blocks are only
+// 2-byte aligned, each run is read as a 5-dword window and realigned with
+// v_perm_b32, and no window reaches past its super-block's own 210 bytes.
+// A row slot of LPR lanes walks the row as in the Q4_0 / Q8_0 DMMV
+// (dmmv.hip): activation codes, scales and sums of the lane's units stay in
+// registers, the loads of RB row steps are issued before any arithmetic, and
+// row partials are folded across lanes by RowReduce.
 #include "zq_common.h"
 #include "zq_internal.h"
 
@@ -27,46 +45,111 @@ namespace zq {
 
 namespace {
 
-constexpr int K4_BYTES = 144;
+template <int WT> struct KQ;
+// NWD: dwords of one unit's weights held between load and arithmetic
+template <> struct KQ<ZQ_Q4_K> { static constexpr int BYTES = 144; static constexpr int NWD = 12; };
+template <> struct KQ<ZQ_Q5_K> { static constexpr int BYTES = 176; static constexpr int NWD = 20; };
+// Q6_K: three 5-dword windows, a 3-dword scale window, d, the window offset
+template <> struct KQ<ZQ_Q6_K> { static constexpr int BYTES = 210; static constexpr int NWD = 20; };
 
-// activation of one unit: codes of blocks 2u and 2u+1, their scales and sums
+// Activation of one unit.  Q4_K / Q5_K: codes of blocks 2u (q[0..7]) and
+// 2u+1 (q[8..15]), their scales d[0..1] and code sums fs[0..1].  Q6_K: for
+// c = 0..3 the 16 codes q[4c..4c+3] of the unit's run in quarter c, that
+// block's scale d[c] and the run's code sum is[c].
 struct KUnitAct {
-  uint32_t q[2][8];
-  float d[2];
-  float s[2];
+  uint32_t q[16];
+  float d[4];
+  float fs[4];
+  int32_t is[4];
 };
 
-template <int LPR, int BPL>
+__device__ __forceinline__ int32_t code_sum(const uint32_t *q, int n) {
+  int32_t s = 0;
+  for (int k = 0; k < n; ++k) s = __builtin_amdgcn_sdot4(static_cast<int>(q[k]), 0x01010101, s, false);
+  return s;
+}
+
+template <int WT, int LPR, int BPL>
 __device__ __forceinline__ void load_unit_act(KUnitAct (&act)[BPL], const DmmvArgs &a, int pass,
                                               int j, int nu) {
 #pragma unroll
   for (int i = 0; i < BPL; ++i) {
     const int u = pass * LPR * BPL + j + LPR * i;
+    KUnitAct &A = act[i];
+    if (u < nu) {
+      if constexpr (WT == ZQ_Q6_K) {
+        const int base = 256 * (u >> 2) + 128 * ((u >> 1) & 1) + 16 * (u & 1);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      if (u < nu) {
-        const int b = 2 * u + h;
-        const u32x4 v0 = *reinterpret_cast<const u32x4 *>(a.qx + 32 * b);
-        const u32x4 v1 = *reinterpret_cast<const u32x4 *>(a.qx + 32 * b + 16);
-        act[i].q[h][0] = v0.x; act[i].q[h][1] = v0.y; act[i].q[h][2] = v0.z; act[i].q[h][3] = v0.w;
-        act[i].q[h][4] = v1.x; act[i].q[h][5] = v1.y; act[i].q[h][6] = v1.z; act[i].q[h][7] = v1.w;
-        act[i].d[h] = a.dx[b];
-        int32_t sum;
-        if (a.sx) {
-          sum = a.sx[b];
-        } else {
-          sum = 0;
-#pragma unroll
-          for (int k = 0; k < 8; ++k)
-            sum = __builtin_amdgcn_sdot4(static_cast<int>(act[i].q[h][k]), 0x01010101, sum, false);
+        for (int c = 0; c < 4; ++c) {
+          const int e0 = base + 32 * c;
+          const u32x4 v = *reinterpret_cast<const u32x4 *>(a.qx + e0);
+          A.q[4 * c] = v.x; A.q[4 * c + 1] = v.y; A.q[4 * c + 2] = v.z; A.q[4 * c + 3] = v.w;
+          A.d[c] = a.dx[e0 >> 5];
+          A.is[c] = code_sum(&A.q[4 * c], 4);
         }
-        act[i].s[h] = static_cast<float>(sum);  // |sum| <= 32*127: exact
       } else {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) act[i].q[h][k] = 0;
-        act[i].d[h] = 0.0f;
-        act[i].s[h] = 0.0f;
+        for (int h = 0; h < 2; ++h) {
+          const int b = 2 * u + h;
+          const u32x4 v0 = *reinterpret_cast<const u32x4 *>(a.qx + 32 * b);
+          const u32x4 v1 = *reinterpret_cast<const u32x4 *>(a.qx + 32 * b + 16);
+          uint32_t *q = &A.q[8 * h];
+          q[0] = v0.x; q[1] = v0.y; q[2] = v0.z; q[3] = v0.w;
+          q[4] = v1.x; q[5] = v1.y; q[6] = v1.z; q[7] = v1.w;
+          A.d[h] = a.dx[b];
+          const int32_t sum = a.sx ? a.sx[b] : code_sum(q, 8);
+          A.fs[h] = static_cast<float>(sum);  // |sum| <= 32*127: exact
+        }
       }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) A.q[k] = 0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        A.d[c] = 0.0f;
+        A.fs[c] = 0.0f;
+        A.is[c] = 0;
+      }
+    }
+  }
+}
+
+// 5 dwords starting at p rounded down to 4 (p is 2-byte aligned).
+__device__ __forceinline__ void load5(const uint8_t *p, uint32_t *w) {
+  const g_u32 *pw = (const g_u32 *)(reinterpret_cast<uintptr_t>(p) & ~uintptr_t(3));
+  const u32x4a4 v = *(const g_u32x4a4 *)pw;
+  w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  w[4] = pw[4];
+}
+
+// Issue the loads of one unit of super-block sb for a lane at position p.
+template <int WT>
+__device__ __forceinline__ void load_unit_w(const uint8_t *sb, int p, uint32_t (&v)[KQ<WT>::NWD]) {
+  if constexpr (WT == ZQ_Q6_K) {
+    const int h = p >> 1, t = p & 1;
+    const uint8_t *ql = sb + 64 * h + 16 * t;
+    load5(ql, &v[0]);                           // low bits, quarters 0 and 2
+    load5(ql + 32, &v[5]);                      // low bits, quarters 1 and 3
+    load5(sb + 128 + 32 * h + 16 * t, &v[10]);  // high bits
+    // scales 8h..8h+7 live at sb+192+8h; the 3-dword window from
+    // (sb+190+8h) rounded down to 4 ends at or before sb+210
+    const g_u32 *ps = (const g_u32 *)(reinterpret_cast<uintptr_t>(sb + 190 + 8 * h) & ~uintptr_t(3));
+    v[15] = ps[0]; v[16] = ps[1]; v[17] = ps[2];
+    v[18] = *(const __attribute__((address_space(1))) uint16_t *)(sb + 208);
+    v[19] = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(sb) & 3u);  // 0 or 2
+  } else {
+    constexpr int QS = WT == ZQ_Q4_K ? 16 : 48;
+    const u32x4 h = *reinterpret_cast<const u32x4 *>(sb);
+    const u32x4 q0 = *reinterpret_cast<const u32x4 *>(sb + QS + 32 * p);
+    const u32x4 q1 = *reinterpret_cast<const u32x4 *>(sb + QS + 16 + 32 * p);
+    v[0] = h.x; v[1] = h.y; v[2] = h.z; v[3] = h.w;
+    v[4] = q0.x; v[5] = q0.y; v[6] = q0.z; v[7] = q0.w;
+    v[8] = q1.x; v[9] = q1.y; v[10] = q1.z; v[11] = q1.w;
+    if constexpr (WT == ZQ_Q5_K) {
+      const u32x4 e0 = *reinterpret_cast<const u32x4 *>(sb + 16);
+      const u32x4 e1 = *reinterpret_cast<const u32x4 *>(sb + 32);
+      v[12] = e0.x; v[13] = e0.y; v[14] = e0.z; v[15] = e0.w;
+      v[16] = e1.x; v[17] = e1.y; v[18] = e1.z; v[19] = e1.w;
     }
   }
 }
@@ -94,9 +177,76 @@ __device__ __forceinline__ void k4_scale_min(uint32_t s0, uint32_t s1, uint32_t 
   mn = static_cast<float>(m);
 }
 
-template <int LPR, int BPL, int RB, bool ISUMS>
-__global__ __launch_bounds__(256) void dmmv_q4k_kernel(const DmmvArgs a) {
+// The unit's contribution to its row, and its integer sums: Q4_K / Q5_K
+// is[0..1] = isum of blocks 2u, 2u+1; Q6_K is[c] = sc*sum (q-32)*qx over the
+// lane's 16 elements of quarter c.
+template <int WT>
+__device__ __forceinline__ float unit_dot(const uint32_t (&v)[KQ<WT>::NWD], int p,
+                                          const KUnitAct &A, int32_t (&is)[4]) {
+  if constexpr (WT == ZQ_Q6_K) {
+    const uint32_t o = v[19];
+    const uint32_t sel = 0x03020100u + o * 0x01010101u;         // bytes o..o+3
+    const uint32_t sels = 0x03020100u + (4u - o) * 0x01010101u;  // scale window offset 4-o
+    uint32_t l0[4], l1[4], hb[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      l0[k] = __builtin_amdgcn_perm(v[k + 1], v[k], sel);
+      l1[k] = __builtin_amdgcn_perm(v[k + 6], v[k + 5], sel);
+      hb[k] = __builtin_amdgcn_perm(v[k + 11], v[k + 10], sel);
+    }
+    const uint32_t s01 = __builtin_amdgcn_perm(v[16], v[15], sels);  // scales 8h..8h+3
+    const uint32_t s23 = __builtin_amdgcn_perm(v[17], v[16], sels);  // scales 8h+4..8h+7
+    const int t8 = 8 * (p & 1);
+    const int sc[4] = {static_cast<int8_t>(s01 >> t8), static_cast<int8_t>(s01 >> (t8 + 16)),
+                       static_cast<int8_t>(s23 >> t8), static_cast<int8_t>(s23 >> (t8 + 16))};
+    float part = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      int32_t s = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t lw = (c & 1) ? l1[k] : l0[k];
+        const uint32_t lo = (c < 2 ? lw : lw >> 4) & 0x0F0F0F0Fu;
+        const uint32_t hi = c < 3 ? (hb[k] << (4 - 2 * c)) & 0x30303030u : (hb[k] >> 2) & 0x30303030u;
+        s = __builtin_amdgcn_sdot4(static_cast<int>(lo | hi), static_cast<int>(A.q[4 * c + k]), s, false);
+      }
+      is[c] = sc[c] * (s - 32 * A.is[c]);  // |.| <= 128*32*127*16 < 2^24
+      part = __builtin_fmaf(A.d[c], static_cast<float>(is[c]), part);
+    }
+    return f16_to_f32(v[18]) * part;
+  } else {
+    const float d = f16_to_f32(v[0] & 0xFFFFu);
+    const float dmin = f16_to_f32(v[0] >> 16);
+    float sc0, mn0, sc1, mn1;
+    k4_scale_min(v[1], v[2], v[3], 2 * p, sc0, mn0);
+    k4_scale_min(v[1], v[2], v[3], 2 * p + 1, sc1, mn1);
+    int32_t is0 = 0, is1 = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      uint32_t lo = v[4 + k] & 0x0F0F0F0Fu;
+      uint32_t hi = (v[4 + k] >> 4) & 0x0F0F0F0Fu;
+      if constexpr (WT == ZQ_Q5_K) {
+        const uint32_t e = v[12 + k] >> (2 * p);
+        lo |= (e << 4) & 0x10101010u;
+        hi |= (e << 3) & 0x10101010u;
+      }
+      is0 = __builtin_amdgcn_sdot4(static_cast<int>(lo), static_cast<int>(A.q[k]), is0, false);
+      is1 = __builtin_amdgcn_sdot4(static_cast<int>(hi), static_cast<int>(A.q[8 + k]), is1, false);
+    }
+    is[0] = is0;
+    is[1] = is1;
+    const float a0 = (d * sc0) * static_cast<float>(is0);
+    const float b0 = (dmin * mn0) * A.fs[0];
+    const float a1 = (d * sc1) * static_cast<float>(is1);
+    const float b1 = (dmin * mn1) * A.fs[1];
+    return __builtin_fmaf(A.d[1], a1 - b1, A.d[0] * (a0 - b0));
+  }
+}
+
+template <int WT, int LPR, int BPL, int RB, bool ISUMS>
+__global__ __launch_bounds__(256) void dmmv_k_kernel(const DmmvArgs a) {
   constexpr int S = 64 / LPR;
+  constexpr int NWD = KQ<WT>::NWD;
   const int lane = static_cast<int>(threadIdx.x & 63);
   const int j = lane & (LPR - 1);
   const int slot = lane / LPR;
@@ -104,11 +254,10 @@ __global__ __launch_bounds__(256) void dmmv_q4k_kernel(const DmmvArgs a) {
   const int64_t n_waves = (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 6;
   const int nu = a.nb / 2;  // 64-element units per row
   const int n_pass = (nu + LPR * BPL - 1) / (LPR * BPL);
-  // every unit of this lane has the same group inside its super-block
-  const int grp = j & 3;
+  const int p = j & 3;      // the lane's unit position in every super-block it visits
 
   KUnitAct act[BPL];
-  if (n_pass == 1) load_unit_act<LPR, BPL>(act, a, 0, j, nu);
+  if (n_pass == 1) load_unit_act<WT, LPR, BPL>(act, a, 0, j, nu);
 
   for (int64_t gi = wave; gi < a.n_groups; gi += n_waves) {
     const int64_t row0 = gi * (RB * S);
@@ -116,8 +265,8 @@ __global__ __launch_bounds__(256) void dmmv_q4k_kernel(const DmmvArgs a) {
 #pragma unroll
     for (int t = 0; t < RB; ++t) acc[t] = 0.0f;
     for (int pass = 0; pass < n_pass; ++pass) {
-      if (n_pass > 1) load_unit_act<LPR, BPL>(act, a, pass, j, nu);
-      u32x4 hdr[RB][BPL], qa[RB][BPL], qb[RB][BPL];
+      if (n_pass > 1) load_unit_act<WT, LPR, BPL>(act, a, pass, j, nu);
+      uint32_t v[RB][BPL][NWD];
 #pragma unroll
       for (int t = 0; t < RB; ++t) {
         int64_t row = row0 + t * S + slot;
@@ -126,49 +275,39 @@ __global__ __launch_bounds__(256) void dmmv_q4k_kernel(const DmmvArgs a) {
         for (int i = 0; i < BPL; ++i) {
           int u = pass * LPR * BPL + j + LPR * i;
           u = u < nu ? u : nu - 1;
-          const uint8_t *sb = a.w + row * a.row_bytes + static_cast<int64_t>(u >> 2) * K4_BYTES;
-          hdr[t][i] = *reinterpret_cast<const u32x4 *>(sb);
-          qa[t][i] = *reinterpret_cast<const u32x4 *>(sb + 16 + 32 * (u & 3));
-          qb[t][i] = *reinterpret_cast<const u32x4 *>(sb + 32 + 32 * (u & 3));
+          const uint8_t *sb = a.w + row * a.row_bytes + static_cast<int64_t>(u >> 2) * KQ<WT>::BYTES;
+          load_unit_w<WT>(sb, p, v[t][i]);
         }
       }
 #pragma unroll
       for (int t = 0; t < RB; ++t) {
-        float p = 0.0f;
+        float part = 0.0f;
 #pragma unroll
         for (int i = 0; i < BPL; ++i) {
-          const u32x4 h = hdr[t][i];
-          const float d = f16_to_f32(h.x & 0xFFFFu);
-          const float dmin = f16_to_f32(h.x >> 16);
-          float sc0, mn0, sc1, mn1;
-          k4_scale_min(h.y, h.z, h.w, 2 * grp, sc0, mn0);
-          k4_scale_min(h.y, h.z, h.w, 2 * grp + 1, sc1, mn1);
-          const uint32_t w[8] = {qa[t][i].x, qa[t][i].y, qa[t][i].z, qa[t][i].w,
-                                 qb[t][i].x, qb[t][i].y, qb[t][i].z, qb[t][i].w};
-          int32_t is0 = 0, is1 = 0;
-#pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            const uint32_t lo = w[k] & 0x0F0F0F0Fu;
-            const uint32_t hi = (w[k] >> 4) & 0x0F0F0F0Fu;
-            is0 = __builtin_amdgcn_sdot4(static_cast<int>(lo), static_cast<int>(act[i].q[0][k]), is0, false);
-            is1 = __builtin_amdgcn_sdot4(static_cast<int>(hi), static_cast<int>(act[i].q[1][k]), is1, false);
-          }
+          int32_t is[4];
+          part += unit_dot<WT>(v[t][i], p, act[i], is);
           if constexpr (ISUMS) {
             const int64_t row = row0 + t * S + slot;
             const int u = pass * LPR * BPL + j + LPR * i;
-            if (row < a.rows && u < nu) {
-              a.isums[row * a.nb + 2 * u] = is0;
-              a.isums[row * a.nb + 2 * u + 1] = is1;
+            if constexpr (WT == ZQ_Q6_K) {
+              // a block's two 16-element runs sit in lanes p and p^1
+              int32_t blk[4];
+#pragma unroll
+              for (int c = 0; c < 4; ++c) blk[c] = is[c] + __shfl_xor(is[c], 1);
+              if (row < a.rows && u < nu && (p & 1) == 0) {
+                int32_t *dst = a.isums + row * a.nb + 8 * (u >> 2) + 4 * (p >> 1);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) dst[c] = blk[c];
+              }
+            } else {
+              if (row < a.rows && u < nu) {
+                a.isums[row * a.nb + 2 * u] = is[0];
+                a.isums[row * a.nb + 2 * u + 1] = is[1];
+              }
             }
           }
-          const float a0 = (d * sc0) * static_cast<float>(is0);
-          const float b0 = (dmin * mn0) * act[i].s[0];
-          const float a1 = (d * sc1) * static_cast<float>(is1);
-          const float b1 = (dmin * mn1) * act[i].s[1];
-          p = __builtin_fmaf(act[i].d[0], a0 - b0, p);
-          p = __builtin_fmaf(act[i].d[1], a1 - b1, p);
         }
-        acc[t] += p;
+        acc[t] += part;
       }
     }
     if constexpr (!ISUMS) {
@@ -194,7 +333,7 @@ struct KShape {
 };
 // (LPR, BPL) layouts over units; any row length is served, further passes
 // take the units beyond LPR*BPL.  LPR is a multiple of 4, so a lane's units
-// all sit at the same group of their super-blocks.
+// all sit at the same position of their super-blocks.
 constexpr KShape kKShapes[] = {{8, 1}, {16, 1}, {32, 1}, {64, 1}, {64, 2}, {64, 4}, {16, 5}};
 
 KShape choose_kshape(int nu) {
@@ -216,63 +355,82 @@ KShape choose_kshape(int nu) {
   return best;
 }
 
-// Rows per wave group = RB * (64/LPR): the largest RB (three 16-byte loads
-// per unit held per lane, RB*BPL <= 8) that still leaves >= 2048 waves.
+// Largest row steps per group RB whose weight registers (RB*BPL units of
+// NWD dwords) stay within 96 dwords and that still leaves >= 2048 waves.
+template <int WT>
 int choose_krb(const KShape &sh, int64_t rows, bool isums) {
   if (isums) return 1;
   const int S = 64 / sh.lpr;
-  const int cap = 8 / sh.bpl;
+  const int cap = 96 / (KQ<WT>::NWD * sh.bpl);
   for (int rb : {8, 4, 2, 1}) {
-    if (rb > cap) continue;
-    if ((rows + rb * S - 1) / (rb * S) >= 2048) return rb;
+    if (rb > cap && rb > 1) continue;
+    if (rb == 1 || (rows + rb * S - 1) / (rb * S) >= 2048) return rb;
   }
   return 1;
 }
 
-template <int LPR, int BPL, int RB, bool ISUMS>
+template <int WT, int LPR, int BPL, int RB, bool ISUMS>
 int launch_k1(DmmvArgs a, hipStream_t stream) {
   constexpr int S = 64 / LPR;
   a.n_groups = (a.rows + RB * S - 1) / (RB * S);
   const int64_t blocks = (a.n_groups + 3) / 4;
   const unsigned grid = static_cast<unsigned>(blocks < 1048576 ? blocks : 1048576);
-  hipLaunchKernelGGL((dmmv_q4k_kernel<LPR, BPL, RB, ISUMS>), dim3(grid), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((dmmv_k_kernel<WT, LPR, BPL, RB, ISUMS>), dim3(grid), dim3(256), 0, stream,
+                     a);
   ZQ_LAUNCH_CHECK();
   return ZQ_OK;
 }
 
-template <int LPR, int BPL, bool ISUMS>
+// RB values instantiated per (type, BPL): those choose_krb can return.
+template <int WT, int LPR, int BPL, bool ISUMS>
 int launch_krb(int rb, const DmmvArgs &a, hipStream_t stream) {
-  if constexpr (ISUMS) return launch_k1<LPR, BPL, 1, true>(a, stream);
-  switch (rb) {
-    case 1: return launch_k1<LPR, BPL, 1, ISUMS>(a, stream);
-    case 2: return launch_k1<LPR, BPL, 2, ISUMS>(a, stream);
-    case 4: return launch_k1<LPR, BPL, 4, ISUMS>(a, stream);
-    default:
-      if constexpr (BPL == 1) return launch_k1<LPR, BPL, 8, ISUMS>(a, stream);
-      return launch_k1<LPR, BPL, 4, ISUMS>(a, stream);
+  constexpr int CAP = 96 / (KQ<WT>::NWD * BPL);
+  if constexpr (ISUMS) {
+    return launch_k1<WT, LPR, BPL, 1, true>(a, stream);
+  } else {
+    if constexpr (CAP >= 8) {
+      if (rb >= 8) return launch_k1<WT, LPR, BPL, 8, false>(a, stream);
+    }
+    if constexpr (CAP >= 4) {
+      if (rb >= 4) return launch_k1<WT, LPR, BPL, 4, false>(a, stream);
+    }
+    if constexpr (CAP >= 2) {
+      if (rb >= 2) return launch_k1<WT, LPR, BPL, 2, false>(a, stream);
+    }
+    return launch_k1<WT, LPR, BPL, 1, false>(a, stream);
   }
 }
 
-template <bool ISUMS>
+template <int WT, bool ISUMS>
 int launch_kshape(const KShape &sh, int rb, const DmmvArgs &a, hipStream_t stream) {
-  if (sh.lpr == 8) return launch_krb<8, 1, ISUMS>(rb, a, stream);
-  if (sh.lpr == 16 && sh.bpl == 1) return launch_krb<16, 1, ISUMS>(rb, a, stream);
-  if (sh.lpr == 16) return launch_krb<16, 5, ISUMS>(rb, a, stream);
-  if (sh.lpr == 32) return launch_krb<32, 1, ISUMS>(rb, a, stream);
-  if (sh.bpl == 1) return launch_krb<64, 1, ISUMS>(rb, a, stream);
-  if (sh.bpl == 2) return launch_krb<64, 2, ISUMS>(rb, a, stream);
-  return launch_krb<64, 4, ISUMS>(rb, a, stream);
+  if (sh.lpr == 8) return launch_krb<WT, 8, 1, ISUMS>(rb, a, stream);
+  if (sh.lpr == 16 && sh.bpl == 1) return launch_krb<WT, 16, 1, ISUMS>(rb, a, stream);
+  if (sh.lpr == 16) return launch_krb<WT, 16, 5, ISUMS>(rb, a, stream);
+  if (sh.lpr == 32) return launch_krb<WT, 32, 1, ISUMS>(rb, a, stream);
+  if (sh.bpl == 1) return launch_krb<WT, 64, 1, ISUMS>(rb, a, stream);
+  if (sh.bpl == 2) return launch_krb<WT, 64, 2, ISUMS>(rb, a, stream);
+  return launch_krb<WT, 64, 4, ISUMS>(rb, a, stream);
+}
+
+template <int WT>
+int launch_type(DmmvArgs a, bool isums, hipStream_t stream) {
+  a.row_bytes = static_cast<int64_t>(a.nb / 8) * KQ<WT>::BYTES;
+  const KShape sh = choose_kshape(a.nb / 2);
+  const int rb = choose_krb<WT>(sh, a.rows, isums);
+  if (isums) return launch_kshape<WT, true>(sh, rb, a, stream);
+  return launch_kshape<WT, false>(sh, rb, a, stream);
 }
 
 }  // namespace
 
-int launch_dmmv_q4k(DmmvArgs a, bool isums, hipStream_t stream) {
+int launch_dmmv_k(int wtype, DmmvArgs a, bool isums, hipStream_t stream) {
   if (a.rows == 0) return ZQ_OK;
-  a.row_bytes = static_cast<int64_t>(a.nb / 8) * K4_BYTES;
-  const KShape sh = choose_kshape(a.nb / 2);
-  const int rb = choose_krb(sh, a.rows, isums);
-  if (isums) return launch_kshape<true>(sh, rb, a, stream);
-  return launch_kshape<false>(sh, rb, a, stream);
+  switch (wtype) {
+    case ZQ_Q4_K: return launch_type<ZQ_Q4_K>(a, isums, stream);
+    case ZQ_Q5_K: return launch_type<ZQ_Q5_K>(a, isums, stream);
+    case ZQ_Q6_K: return launch_type<ZQ_Q6_K>(a, isums, stream);
+    default: return ZQ_EINVAL;
+  }
 }
 
 }  // namespace zq

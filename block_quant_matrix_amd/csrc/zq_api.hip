@@ -82,6 +82,35 @@ int dmmv_common(int wtype, const void *w, int64_t rows, int64_t k, const int8_t 
   return zq::launch_dmmv(wtype, zq::MODE_PLAIN, a, S(stream));
 }
 
+// The K-quant DMMV and its isums hook share the checks: k a multiple of
+// 256, w 16-byte aligned (super-blocks of 144 and 176 bytes stay 16-byte
+// aligned; the 210-byte Q6_K ones are read through dword windows).
+int dmmv_k_common(int wtype, const void *w, int64_t rows, int64_t k, const int8_t *qx,
+                  const float *dx, const int32_t *sx, float *y, int32_t *isums, uint32_t flags,
+                  void *stream) {
+  ZQ_REQUIRE(wtype == ZQ_Q4_K || wtype == ZQ_Q5_K || wtype == ZQ_Q6_K, ZQ_EINVAL);
+  ZQ_REQUIRE(w && qx && (isums || (dx && y)), ZQ_ENULL);
+  ZQ_REQUIRE(rows >= 0 && k_ok(k) && k % 256 == 0, ZQ_EINVAL);
+  ZQ_REQUIRE((flags & ~uint32_t(ZQ_ACCUMULATE)) == 0, ZQ_EINVAL);
+  ZQ_REQUIRE(al(w, 16) && al(qx, 16) && al(dx, 4) && al(y, 4) && al(sx, 4) && al(isums, 4),
+             ZQ_EALIGN);
+  const int dc = check_current_device();
+  if (dc != ZQ_OK) return dc;
+  zq::DmmvArgs a{};
+  a.w = static_cast<const uint8_t *>(w);
+  a.qx = qx;
+  // the isums hook has no scales: qx's bytes stand in for dx (k bytes cover
+  // the k/32 fp32 values), their values only feed the unused row partials
+  a.dx = isums ? reinterpret_cast<const float *>(qx) : dx;
+  a.sx = wtype == ZQ_Q6_K ? nullptr : sx;
+  a.y = y;
+  a.isums = isums;
+  a.rows = rows;
+  a.nb = static_cast<int32_t>(k / 32);
+  a.flags = flags;
+  return zq::launch_dmmv_k(wtype, a, isums != nullptr, S(stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -126,22 +155,17 @@ int zq_dmmv_q4_0(const void *w, int64_t rows, int64_t k, const int8_t *qx, const
 
 int zq_dmmv_q4_k(const void *w, int64_t rows, int64_t k, const int8_t *qx, const float *dx,
                  const int32_t *sx, float *y, uint32_t flags, void *stream) {
-  ZQ_REQUIRE(w && qx && dx && y, ZQ_ENULL);
-  ZQ_REQUIRE(rows >= 0 && k_ok(k) && k % 256 == 0, ZQ_EINVAL);
-  ZQ_REQUIRE((flags & ~uint32_t(ZQ_ACCUMULATE)) == 0, ZQ_EINVAL);
-  ZQ_REQUIRE(al(w, 16) && al(qx, 16) && al(dx, 4) && al(y, 4) && al(sx, 4), ZQ_EALIGN);
-  const int dc = check_current_device();
-  if (dc != ZQ_OK) return dc;
-  zq::DmmvArgs a{};
-  a.w = static_cast<const uint8_t *>(w);
-  a.qx = qx;
-  a.dx = dx;
-  a.sx = sx;
-  a.y = y;
-  a.rows = rows;
-  a.nb = static_cast<int32_t>(k / 32);
-  a.flags = flags;
-  return zq::launch_dmmv_q4k(a, false, S(stream));
+  return dmmv_k_common(ZQ_Q4_K, w, rows, k, qx, dx, sx, y, nullptr, flags, stream);
+}
+
+int zq_dmmv_q5_k(const void *w, int64_t rows, int64_t k, const int8_t *qx, const float *dx,
+                 const int32_t *sx, float *y, uint32_t flags, void *stream) {
+  return dmmv_k_common(ZQ_Q5_K, w, rows, k, qx, dx, sx, y, nullptr, flags, stream);
+}
+
+int zq_dmmv_q6_k(const void *w, int64_t rows, int64_t k, const int8_t *qx, const float *dx,
+                 float *y, uint32_t flags, void *stream) {
+  return dmmv_k_common(ZQ_Q6_K, w, rows, k, qx, dx, nullptr, y, nullptr, flags, stream);
 }
 
 int zq_dmmv_f32(int wtype, const void *w, int64_t rows, int64_t k, const float *x, float *y,
@@ -170,24 +194,8 @@ int zq_dmmv_f32(int wtype, const void *w, int64_t rows, int64_t k, const float *
 
 int zq_dmmv_isums(int wtype, const void *w, int64_t rows, int64_t k, const int8_t *qx,
                   const int32_t *sx, int32_t *isums, void *stream) {
-  if (wtype == ZQ_Q4_K) {
-    ZQ_REQUIRE(w && qx && isums, ZQ_ENULL);
-    ZQ_REQUIRE(rows >= 0 && k_ok(k) && k % 256 == 0, ZQ_EINVAL);
-    ZQ_REQUIRE(al(w, 16) && al(qx, 16) && al(sx, 4) && al(isums, 4), ZQ_EALIGN);
-    const int dc = check_current_device();
-    if (dc != ZQ_OK) return dc;
-    zq::DmmvArgs a{};
-    a.w = static_cast<const uint8_t *>(w);
-    a.qx = qx;
-    a.sx = sx;
-    a.isums = isums;
-    a.rows = rows;
-    a.nb = static_cast<int32_t>(k / 32);
-    // dx is read by the shared activation loader; qx's bytes stand in (k bytes
-    // cover the k/32 fp32 values), their values only feed the unused rows
-    a.dx = reinterpret_cast<const float *>(qx);
-    return zq::launch_dmmv_q4k(a, true, S(stream));
-  }
+  if (wtype == ZQ_Q4_K || wtype == ZQ_Q5_K || wtype == ZQ_Q6_K)
+    return dmmv_k_common(wtype, w, rows, k, qx, nullptr, sx, nullptr, isums, 0, stream);
   ZQ_REQUIRE(block_bytes(wtype) > 0, ZQ_EINVAL);
   ZQ_REQUIRE(w && qx && isums, ZQ_ENULL);
   ZQ_REQUIRE(rows >= 0 && k_ok(k), ZQ_EINVAL);

@@ -54,9 +54,10 @@ struct DmmvF32Args {
 constexpr int kArgmaxMaxParts = 2048;
 int launch_dmmv_f32x(int wtype, DmmvF32Args a, hipStream_t stream);
 
-// DMMV over Q4_K super-blocks (a.nb = k/32, k a multiple of 256); isums
-// selects the per-block integer sums instead of rows.
-int launch_dmmv_q4k(DmmvArgs a, bool isums, hipStream_t stream);
+// DMMV over K-quant super-blocks, wtype ZQ_Q4_K / ZQ_Q5_K / ZQ_Q6_K
+// (a.nb = k/32, k a multiple of 256); isums selects the per-32-block integer
+// sums instead of rows.
+int launch_dmmv_k(int wtype, DmmvArgs a, bool isums, hipStream_t stream);
 // Reduce nparts (value, index) partials to the argmax index.
 int launch_argmax_final(const void *part, int nparts, int32_t *out_idx, hipStream_t stream);
 

@@ -114,7 +114,7 @@ def gen_router(n_routed: int, seed: int):
     return logits, g
 
 
-# The five workloads (shapes from the pages; distributions as above).
+# The workloads (shapes from the pages; distributions as above).
 WORKLOADS = {
     1: dict(name="q8_0_dmmv_64x2048", wtype=Q8_0, rows=64, k=2048),
     2: dict(name="q4_0_dmmv_4096x4096", wtype=Q4_0, rows=4096, k=4096),
@@ -124,6 +124,9 @@ WORKLOADS = {
     5: dict(name="q4_0_prefill_gemm_m512_n5120_k5120", wtype=Q4_0, m=512, n=5120, k=5120),
     # K-quant DMMV: the headline shape over the format the pages' experts use
     6: dict(name="q4_k_dmmv_4096x4096", wtype=Q4_K, rows=4096, k=4096),
+    # the LM head of the pages' model is Q6_K at the vocabulary shape
+    7: dict(name="q6_k_lmhead_dmmv_248320x2048", wtype=Q6_K, rows=248320, k=2048),
+    8: dict(name="q5_k_dmmv_4096x4096", wtype=Q5_K, rows=4096, k=4096),
 }
 
 

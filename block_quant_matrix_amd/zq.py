@@ -15,8 +15,7 @@ LIB_PATH = os.path.join(HERE, "libzq.so")
 
 ZQ_OK, ZQ_EINVAL, ZQ_ENULL, ZQ_EALIGN, ZQ_ERANGE, ZQ_EDEVICE, ZQ_ELAUNCH = 0, -1, -2, -3, -4, -5, -6
 ZQ_ACCUMULATE = 1
-ZQ_Q4_0, ZQ_Q8_0, ZQ_Q4_K = 4, 8, 12
-ZQ_Q4_0, ZQ_Q8_0 = 4, 8
+ZQ_Q4_0, ZQ_Q8_0, ZQ_Q4_K, ZQ_Q5_K, ZQ_Q6_K = 4, 8, 12, 13, 14
 ZQ_MOE_GATHER, ZQ_MOE_WEIGHTED_SUM = 0, 1
 
 _P = ctypes.c_void_p
@@ -35,6 +34,8 @@ SIGNATURES = {
     "zq_dmmv_q8_0": (_INT, [_P, _I64, _I64, _P, _P, _P, _U32, _P]),
     "zq_dmmv_q4_0": (_INT, [_P, _I64, _I64, _P, _P, _P, _P, _U32, _P]),
     "zq_dmmv_q4_k": (_INT, [_P, _I64, _I64, _P, _P, _P, _P, _U32, _P]),
+    "zq_dmmv_q5_k": (_INT, [_P, _I64, _I64, _P, _P, _P, _P, _U32, _P]),
+    "zq_dmmv_q6_k": (_INT, [_P, _I64, _I64, _P, _P, _P, _U32, _P]),
     "zq_dmmv_f32": (_INT, [_INT, _P, _I64, _I64, _P, _P, _U32, _P, _P, _P, _P]),
     "zq_dmmv_isums": (_INT, [_INT, _P, _I64, _I64, _P, _P, _P, _P]),
     "zq_argmax_workspace_bytes": (_SZ, [_I64]),
@@ -137,6 +138,16 @@ def zq_dmmv_q4_0(w, rows, k, qx, dx, sx, y, flags=0, stream=None):
 
 def zq_dmmv_q4_k(w, rows, k, qx, dx, sx, y, flags=0, stream=None):
     return _call("zq_dmmv_q4_k", ptr(w), rows, k, ptr(qx), ptr(dx), ptr(sx), ptr(y), flags,
+                 _stream(stream))
+
+
+def zq_dmmv_q5_k(w, rows, k, qx, dx, sx, y, flags=0, stream=None):
+    return _call("zq_dmmv_q5_k", ptr(w), rows, k, ptr(qx), ptr(dx), ptr(sx), ptr(y), flags,
+                 _stream(stream))
+
+
+def zq_dmmv_q6_k(w, rows, k, qx, dx, y, flags=0, stream=None):
+    return _call("zq_dmmv_q6_k", ptr(w), rows, k, ptr(qx), ptr(dx), ptr(y), flags,
                  _stream(stream))
 
 

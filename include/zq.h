@@ -54,7 +54,7 @@ enum zq_status {
 };
 
 enum zq_flags { ZQ_ACCUMULATE = 1 /* y += W.x instead of y = W.x */ };
-enum zq_wtype { ZQ_Q4_0 = 4, ZQ_Q8_0 = 8, ZQ_Q4_K = 12 };
+enum zq_wtype { ZQ_Q4_0 = 4, ZQ_Q8_0 = 8, ZQ_Q4_K = 12, ZQ_Q5_K = 13, ZQ_Q6_K = 14 };
 enum zq_moe_mode { ZQ_MOE_GATHER = 0, ZQ_MOE_WEIGHTED_SUM = 1 };
 
 int zq_version(void);
@@ -87,19 +87,32 @@ int zq_dmmv_q8_0(const void *w, int64_t rows, int64_t k, const int8_t *qx, const
 int zq_dmmv_q4_0(const void *w, int64_t rows, int64_t k, const int8_t *qx, const float *dx,
                  const int32_t *sx, float *y, uint32_t flags, void *stream);
 
-/* The same DMMV over GGML Q4_K super-blocks (256 elements, 144 bytes, bit
- * for bit: "Bringing ZINC to NVIDIA", section "The reassuring result";
- * "CUDA backend for ZINC", section 5, dmmv_q4k): d, dmin, 6-bit sub-block
- * scales and mins, nibbles; an element is d*sc*q - dmin*m.  With the int8
- * activation blocks of 32 (zq_quantize_act), which line up with the
- * 32-element sub-blocks:
- *   y[r] (+)= sum_b dx[b] * (d*sc_b * isum[r][b] - dmin*m_b * sx[b]),
- *   isum = sum q * qx (exact int32).
- * k a multiple of 256; w 16-byte aligned, rows of k/256 super-blocks; sx may
- * be NULL (the kernel then sums the codes).  zq_dmmv_isums with ZQ_Q4_K
- * returns the isum of every 32-element sub-block. */
+/* The same DMMV over GGML's K-quant super-blocks of 256 elements, bit for
+ * bit ("Bringing ZINC to NVIDIA", section "The reassuring result"; "CUDA
+ * backend for ZINC", section 5, dmmv_q4k / dmmv_q5k / dmmv_q6k; the pages'
+ * model keeps its experts in Q4_K / Q5_K and its LM head in Q6_K):
+ *   Q4_K, 144 bytes: fp16 d, fp16 dmin, 12 bytes of 6-bit sub-block scales
+ *     and mins, 128 bytes of nibbles; element d*sc*q - dmin*m, q in 0..15;
+ *   Q5_K, 176 bytes: as Q4_K with 32 bytes of fifth bits after the scales;
+ *     q in 0..31;
+ *   Q6_K, 210 bytes: 128 bytes of low nibbles, 64 bytes of 2-bit highs, 16
+ *     int8 scales of 16-element sub-blocks, fp16 d; element d*sc*(q - 32).
+ * With the int8 activation blocks of 32 (zq_quantize_act), which line up
+ * with the sub-blocks:
+ *   Q4_K / Q5_K: y[r] (+)= sum_b dx[b]*(d*sc_b*isum[r][b] - dmin*m_b*sx[b]),
+ *     isum = sum q*qx;
+ *   Q6_K: y[r] (+)= sum_b dx[b]*d*isum[r][b], isum = sum sc*(q-32)*qx over
+ *     the block's two 16-element sub-blocks;
+ * every isum an exact int32.  k a multiple of 256; w 16-byte aligned, rows
+ * of k/256 super-blocks back to back; sx may be NULL (the kernel then sums
+ * the codes).  zq_dmmv_isums with ZQ_Q4_K / ZQ_Q5_K / ZQ_Q6_K returns the
+ * isum of every 32-element block. */
 int zq_dmmv_q4_k(const void *w, int64_t rows, int64_t k, const int8_t *qx, const float *dx,
                  const int32_t *sx, float *y, uint32_t flags, void *stream);
+int zq_dmmv_q5_k(const void *w, int64_t rows, int64_t k, const int8_t *qx, const float *dx,
+                 const int32_t *sx, float *y, uint32_t flags, void *stream);
+int zq_dmmv_q6_k(const void *w, int64_t rows, int64_t k, const int8_t *qx, const float *dx,
+                 float *y, uint32_t flags, void *stream);
 
 /* DMMV from the fp32 activation in one launch: y (+)= W . Q(x), where Q is
  * exactly the quantization of zq_quantize_act (same codes, scales, sums).

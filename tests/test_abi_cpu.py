@@ -125,6 +125,31 @@ def test_q4k_argument_errors():
     assert L.zq_dmmv_isums(12, A + 4, 4, 512, B, None, C, None) == zq.ZQ_EALIGN
 
 
+def test_q5k_q6k_argument_errors():
+    L = zq.lib()
+
+    def rc5(w=A, rows=4, k=512, qx=B, dx=C, sx=None, y=D, flags=0):
+        return L.zq_dmmv_q5_k(w, rows, k, qx, dx, sx, y, flags, None)
+
+    def rc6(w=A, rows=4, k=512, qx=B, dx=C, y=D, flags=0):
+        return L.zq_dmmv_q6_k(w, rows, k, qx, dx, y, flags, None)
+
+    for rc in (rc5, rc6):
+        assert rc(k=480) == zq.ZQ_EINVAL        # not a whole super-block
+        assert rc(rows=-1) == zq.ZQ_EINVAL
+        assert rc(flags=2) == zq.ZQ_EINVAL
+        assert rc(w=A + 2) == zq.ZQ_EALIGN
+        assert rc(qx=B + 8) == zq.ZQ_EALIGN
+        assert rc(dx=None) == zq.ZQ_ENULL
+        assert rc(w=None) == zq.ZQ_ENULL
+    assert rc5(sx=C + 2) == zq.ZQ_EALIGN
+    for wt in (13, 14):
+        assert L.zq_dmmv_isums(wt, A, 4, 480, B, None, C, None) == zq.ZQ_EINVAL
+        assert L.zq_dmmv_isums(wt, A + 4, 4, 512, B, None, C, None) == zq.ZQ_EALIGN
+        assert L.zq_dmmv_isums(wt, A, 4, 512, B, None, None, None) == zq.ZQ_ENULL
+    assert L.zq_dmmv_isums(15, A, 4, 512, B, None, C, None) == zq.ZQ_EINVAL
+
+
 def test_lmhead_argument_errors():
     L = zq.lib()
     ws = L.zq_dmmv_f32_argmax_workspace_bytes()
@@ -235,6 +260,8 @@ def test_valid_arguments_without_gpu_report_no_device():
     """With every argument valid, the last check is the device: no GPU here."""
     assert rc_dmmv_q4() == zq.ZQ_EDEVICE
     assert zq.lib().zq_dmmv_q4_k(A, 4, 512, B, C, None, D, 0, None) == zq.ZQ_EDEVICE
+    assert zq.lib().zq_dmmv_q5_k(A, 4, 512, B, C, None, D, 0, None) == zq.ZQ_EDEVICE
+    assert zq.lib().zq_dmmv_q6_k(A, 4, 512, B, C, D, 0, None) == zq.ZQ_EDEVICE
     L = zq.lib()
     assert L.zq_dmmv_f32_argmax(4, A, 248320, 2048, B, C, D, A + 0x8000,
                                 L.zq_dmmv_f32_argmax_workspace_bytes(), None) == zq.ZQ_EDEVICE
