@@ -30,42 +30,54 @@ namespace zq {
 template <int BPL> struct ActRegs {
   uint32_t q[BPL][8];
   float d[BPL];
+  int32_t sraw[BPL];
   int32_t s8[BPL];
 };
 
+// Issue the loads of the lane's activation blocks (codes, scale, block sum
+// when sx is given).  Blocks past the row end load the last block; finish_act
+// zeroes their scales.  No arithmetic on the loaded values here, so the wave
+// requests its weight windows before it waits on any of them.
 template <int WT, int LPR, int BPL>
 __device__ __forceinline__ void load_act(ActRegs<BPL> &act, const DmmvArgs &a, int s, int pass,
                                          int j) {
   const int8_t *qx = a.qx + static_cast<int64_t>(s) * a.x_stride;
   const float *dx = a.dx + static_cast<int64_t>(s) * (a.x_stride / 32);
-  const int32_t *sx = a.sx ? a.sx + static_cast<int64_t>(s) * (a.x_stride / 32) : nullptr;
+  // with no sx the sum loads read dx (a valid address) and are not used
+  const int32_t *sx = a.sx ? a.sx + static_cast<int64_t>(s) * (a.x_stride / 32)
+                           : reinterpret_cast<const int32_t *>(dx);
 #pragma unroll
   for (int i = 0; i < BPL; ++i) {
-    const int b = pass * LPR * BPL + j + LPR * i;
-    if (b < a.nb) {
-      const u32x4 v0 = *reinterpret_cast<const u32x4 *>(qx + 32 * b);
-      const u32x4 v1 = *reinterpret_cast<const u32x4 *>(qx + 32 * b + 16);
-      act.q[i][0] = v0.x; act.q[i][1] = v0.y; act.q[i][2] = v0.z; act.q[i][3] = v0.w;
-      act.q[i][4] = v1.x; act.q[i][5] = v1.y; act.q[i][6] = v1.z; act.q[i][7] = v1.w;
-      act.d[i] = dx[b];
-      if constexpr (WT == ZQ_Q4_0) {
-        int32_t sum;
-        if (sx) {
-          sum = sx[b];
-        } else {
-          sum = 0;
+    int b = pass * LPR * BPL + j + LPR * i;
+    b = b < a.nb ? b : a.nb - 1;
+    const u32x4 v0 = *reinterpret_cast<const u32x4 *>(qx + 32 * b);
+    const u32x4 v1 = *reinterpret_cast<const u32x4 *>(qx + 32 * b + 16);
+    act.q[i][0] = v0.x; act.q[i][1] = v0.y; act.q[i][2] = v0.z; act.q[i][3] = v0.w;
+    act.q[i][4] = v1.x; act.q[i][5] = v1.y; act.q[i][6] = v1.z; act.q[i][7] = v1.w;
+    act.d[i] = dx[b];
+    if constexpr (WT == ZQ_Q4_0) act.sraw[i] = sx[b];
+  }
+}
+
+// The arithmetic half: 8 * block sum for the Q4_0 offset, and zero scales
+// for the blocks past the row end.  No loads, so the outstanding-load
+// counters agree on every path.
+template <int WT, int LPR, int BPL>
+__device__ __forceinline__ void finish_act(ActRegs<BPL> &act, const DmmvArgs &a, int pass, int j) {
 #pragma unroll
-          for (int k = 0; k < 8; ++k)
-            sum = __builtin_amdgcn_sdot4(static_cast<int>(act.q[i][k]), 0x01010101, sum, false);
-        }
-        act.s8[i] = 8 * sum;
-      } else {
-        act.s8[i] = 0;
+  for (int i = 0; i < BPL; ++i) {
+    const bool ok = pass * LPR * BPL + j + LPR * i < a.nb;
+    act.d[i] = ok ? act.d[i] : 0.0f;
+    if constexpr (WT == ZQ_Q4_0) {
+      int32_t sum = act.sraw[i];
+      if (!a.sx) {
+        sum = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          sum = __builtin_amdgcn_sdot4(static_cast<int>(act.q[i][k]), 0x01010101, sum, false);
       }
+      act.s8[i] = 8 * sum;
     } else {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) act.q[i][k] = 0;
-      act.d[i] = 0.0f;
       act.s8[i] = 0;
     }
   }
@@ -74,7 +86,7 @@ __device__ __forceinline__ void load_act(ActRegs<BPL> &act, const DmmvArgs &a, i
 // Load and reduce one pass (BPL blocks per lane) of RB row steps.
 template <int WT, int LPR, int BPL, int RB, int MODE>
 __device__ __forceinline__ void block_pass(const DmmvArgs &a, const uint8_t *wb, int64_t row0,
-                                           int pass, int j, int slot, const ActRegs<BPL> &act,
+                                           int pass, int j, int slot, ActRegs<BPL> &act,
                                            float (&part)[RB]) {
   constexpr int NW = Blk<WT>::NW;
   constexpr int BB = Blk<WT>::BYTES;
@@ -92,6 +104,8 @@ __device__ __forceinline__ void block_pass(const DmmvArgs &a, const uint8_t *wb,
       off[t][i] = load_window<WT>(wb + row * a.row_bytes + static_cast<int64_t>(b) * BB, win[t][i]);
     }
   }
+  // re-derived on every pass: one multiply (or 8 dot4) per block, no loads
+  finish_act<WT, LPR, BPL>(act, a, pass, j);
 #pragma unroll
   for (int t = 0; t < RB; ++t) {
     float p = 0.0f;

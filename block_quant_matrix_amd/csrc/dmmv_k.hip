@@ -55,12 +55,16 @@ template <> struct KQ<ZQ_Q6_K> { static constexpr int BYTES = 210; static conste
 // Activation of one unit.  Q4_K / Q5_K: codes of blocks 2u (q[0..7]) and
 // 2u+1 (q[8..15]), their scales d[0..1] and code sums fs[0..1].  Q6_K: for
 // c = 0..3 the 16 codes q[4c..4c+3] of the unit's run in quarter c, that
-// block's scale d[c] and the run's code sum is[c].
+// block's scale d[c] and minus 32 times the run's code sum, m32[c].
+// load_unit_act only issues the loads (raw block sums in sraw); finish_act
+// derives the sums once the wave's weight loads are in flight, so a wave
+// never waits on the activation before its weights are requested.
 struct KUnitAct {
   uint32_t q[16];
   float d[4];
-  float fs[4];
-  int32_t is[4];
+  int32_t sraw[2];
+  float fs[2];
+  int32_t m32[4];
 };
 
 __device__ __forceinline__ int32_t code_sum(const uint32_t *q, int n) {
@@ -69,46 +73,65 @@ __device__ __forceinline__ int32_t code_sum(const uint32_t *q, int n) {
   return s;
 }
 
+// Loads only.  Units past the row end load the row's last unit; their
+// scales are zeroed in finish_act.
 template <int WT, int LPR, int BPL>
 __device__ __forceinline__ void load_unit_act(KUnitAct (&act)[BPL], const DmmvArgs &a, int pass,
                                               int j, int nu) {
+  // block sums come from sx when given; otherwise the loads read dx (any
+  // valid address) and finish_act sums the codes
+  const int32_t *sxp = a.sx ? a.sx : reinterpret_cast<const int32_t *>(a.dx);
 #pragma unroll
   for (int i = 0; i < BPL; ++i) {
-    const int u = pass * LPR * BPL + j + LPR * i;
+    int u = pass * LPR * BPL + j + LPR * i;
+    u = u < nu ? u : nu - 1;
     KUnitAct &A = act[i];
-    if (u < nu) {
-      if constexpr (WT == ZQ_Q6_K) {
-        const int base = 256 * (u >> 2) + 128 * ((u >> 1) & 1) + 16 * (u & 1);
+    if constexpr (WT == ZQ_Q6_K) {
+      const int base = 256 * (u >> 2) + 128 * ((u >> 1) & 1) + 16 * (u & 1);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int e0 = base + 32 * c;
-          const u32x4 v = *reinterpret_cast<const u32x4 *>(a.qx + e0);
-          A.q[4 * c] = v.x; A.q[4 * c + 1] = v.y; A.q[4 * c + 2] = v.z; A.q[4 * c + 3] = v.w;
-          A.d[c] = a.dx[e0 >> 5];
-          A.is[c] = code_sum(&A.q[4 * c], 4);
-        }
-      } else {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int b = 2 * u + h;
-          const u32x4 v0 = *reinterpret_cast<const u32x4 *>(a.qx + 32 * b);
-          const u32x4 v1 = *reinterpret_cast<const u32x4 *>(a.qx + 32 * b + 16);
-          uint32_t *q = &A.q[8 * h];
-          q[0] = v0.x; q[1] = v0.y; q[2] = v0.z; q[3] = v0.w;
-          q[4] = v1.x; q[5] = v1.y; q[6] = v1.z; q[7] = v1.w;
-          A.d[h] = a.dx[b];
-          const int32_t sum = a.sx ? a.sx[b] : code_sum(q, 8);
-          A.fs[h] = static_cast<float>(sum);  // |sum| <= 32*127: exact
-        }
+      for (int c = 0; c < 4; ++c) {
+        const int e0 = base + 32 * c;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(a.qx + e0);
+        A.q[4 * c] = v.x; A.q[4 * c + 1] = v.y; A.q[4 * c + 2] = v.z; A.q[4 * c + 3] = v.w;
+        A.d[c] = a.dx[e0 >> 5];
       }
     } else {
 #pragma unroll
-      for (int k = 0; k < 16; ++k) A.q[k] = 0;
+      for (int h = 0; h < 2; ++h) {
+        const int b = 2 * u + h;
+        const u32x4 v0 = *reinterpret_cast<const u32x4 *>(a.qx + 32 * b);
+        const u32x4 v1 = *reinterpret_cast<const u32x4 *>(a.qx + 32 * b + 16);
+        uint32_t *q = &A.q[8 * h];
+        q[0] = v0.x; q[1] = v0.y; q[2] = v0.z; q[3] = v0.w;
+        q[4] = v1.x; q[5] = v1.y; q[6] = v1.z; q[7] = v1.w;
+        A.d[h] = a.dx[b];
+        A.sraw[h] = sxp[b];
+      }
+    }
+  }
+}
+
+// The arithmetic half of the activation set-up (no loads, so the counters
+// of outstanding loads are the same on every path).
+template <int WT, int LPR, int BPL>
+__device__ __forceinline__ void finish_act(KUnitAct (&act)[BPL], const DmmvArgs &a, int pass,
+                                           int j, int nu) {
+#pragma unroll
+  for (int i = 0; i < BPL; ++i) {
+    const bool ok = pass * LPR * BPL + j + LPR * i < nu;
+    KUnitAct &A = act[i];
+    if constexpr (WT == ZQ_Q6_K) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        A.d[c] = 0.0f;
-        A.fs[c] = 0.0f;
-        A.is[c] = 0;
+        A.m32[c] = -32 * code_sum(&A.q[4 * c], 4);
+        A.d[c] = ok ? A.d[c] : 0.0f;
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int32_t sum = a.sx ? A.sraw[h] : code_sum(&A.q[8 * h], 8);
+        A.fs[h] = static_cast<float>(sum);  // |sum| <= 32*127: exact
+        A.d[h] = ok ? A.d[h] : 0.0f;
       }
     }
   }
@@ -202,7 +225,8 @@ __device__ __forceinline__ float unit_dot(const uint32_t (&v)[KQ<WT>::NWD], int 
     float part = 0.0f;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      int32_t s = 0;
+      // sum (q - 32) * qx over the run: the dot chain starts at -32 * sum qx
+      int32_t s = A.m32[c];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const uint32_t lw = (c & 1) ? l1[k] : l0[k];
@@ -210,7 +234,7 @@ __device__ __forceinline__ float unit_dot(const uint32_t (&v)[KQ<WT>::NWD], int 
         const uint32_t hi = c < 3 ? (hb[k] << (4 - 2 * c)) & 0x30303030u : (hb[k] >> 2) & 0x30303030u;
         s = __builtin_amdgcn_sdot4(static_cast<int>(lo | hi), static_cast<int>(A.q[4 * c + k]), s, false);
       }
-      is[c] = sc[c] * (s - 32 * A.is[c]);  // |.| <= 128*32*127*16 < 2^24
+      is[c] = __mul24(sc[c], s);  // |.| <= 128*32*127*16 < 2^24: exact in 24-bit
       part = __builtin_fmaf(A.d[c], static_cast<float>(is[c]), part);
     }
     return f16_to_f32(v[18]) * part;
@@ -243,8 +267,12 @@ __device__ __forceinline__ float unit_dot(const uint32_t (&v)[KQ<WT>::NWD], int 
   }
 }
 
+// The occupancy target is capped at 2 waves per SIMD: aiming higher, the
+// scheduler trades the loads of later row steps (issued together, so a wave
+// has all its bytes in flight at once) for registers and serialises them.
 template <int WT, int LPR, int BPL, int RB, bool ISUMS>
-__global__ __launch_bounds__(256) void dmmv_k_kernel(const DmmvArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void dmmv_k_kernel(
+    const DmmvArgs a) {
   constexpr int S = 64 / LPR;
   constexpr int NWD = KQ<WT>::NWD;
   const int lane = static_cast<int>(threadIdx.x & 63);
@@ -279,6 +307,8 @@ __global__ __launch_bounds__(256) void dmmv_k_kernel(const DmmvArgs a) {
           load_unit_w<WT>(sb, p, v[t][i]);
         }
       }
+      // re-derived every group: a few dot4 per unit, no loads
+      finish_act<WT, LPR, BPL>(act, a, pass, j, nu);
 #pragma unroll
       for (int t = 0; t < RB; ++t) {
         float part = 0.0f;
