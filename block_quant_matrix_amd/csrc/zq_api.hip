@@ -168,6 +168,31 @@ int zq_dmmv_q6_k(const void *w, int64_t rows, int64_t k, const int8_t *qx, const
   return dmmv_k_common(ZQ_Q6_K, w, rows, k, qx, dx, nullptr, y, nullptr, flags, stream);
 }
 
+int zq_dmmv_tokens(int wtype, const void *w, int64_t rows, int64_t k, const int8_t *qx,
+                   const float *dx, const int32_t *sx, int32_t n_tok, float *y, uint32_t flags,
+                   void *stream) {
+  ZQ_REQUIRE(block_bytes(wtype) > 0, ZQ_EINVAL);
+  ZQ_REQUIRE(w && qx && dx && y, ZQ_ENULL);
+  ZQ_REQUIRE(rows >= 0 && k_ok(k) && k <= (int64_t(1) << 30), ZQ_EINVAL);
+  ZQ_REQUIRE(n_tok >= 1 && n_tok <= 8, ZQ_EINVAL);
+  ZQ_REQUIRE((flags & ~uint32_t(ZQ_ACCUMULATE)) == 0, ZQ_EINVAL);
+  ZQ_REQUIRE(al(w, 4) && al(qx, 16) && al(dx, 4) && al(y, 4) && al(sx, 4), ZQ_EALIGN);
+  const int dc = check_current_device();
+  if (dc != ZQ_OK) return dc;
+  zq::DmmvTokArgs a{};
+  a.w = static_cast<const uint8_t *>(w);
+  a.qx = qx;
+  a.dx = dx;
+  a.sx = wtype == ZQ_Q4_0 ? sx : nullptr;
+  a.y = y;
+  a.rows = rows;
+  a.k = static_cast<int32_t>(k);
+  a.nb = static_cast<int32_t>(k / 32);
+  a.n_tok = n_tok;
+  a.flags = flags;
+  return zq::launch_dmmv_tok(wtype, a, S(stream));
+}
+
 int zq_dmmv_f32(int wtype, const void *w, int64_t rows, int64_t k, const float *x, float *y,
                 uint32_t flags, int8_t *qx_out, float *dx_out, int32_t *sx_out, void *stream) {
   ZQ_REQUIRE(block_bytes(wtype) > 0, ZQ_EINVAL);

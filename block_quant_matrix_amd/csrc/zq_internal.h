@@ -31,6 +31,24 @@ struct DmmvArgs {
   uint32_t flags;
 };
 
+// The multi-token DMMV: T <= 8 activations, token t at qx + t*k,
+// dx / sx + t*nb, output rows at y + t*rows.
+struct DmmvTokArgs {
+  const uint8_t *w;
+  const int8_t *qx;
+  const float *dx;
+  const int32_t *sx;    // may be null (the kernel then sums the codes)
+  float *y;
+  int64_t rows;
+  int64_t row_bytes;    // filled in by the launcher
+  int64_t n_groups;     // filled in by the launcher
+  int32_t k;
+  int32_t nb;
+  int32_t n_tok;
+  uint32_t flags;
+};
+int launch_dmmv_tok(int wtype, DmmvTokArgs a, hipStream_t stream);
+
 // The fused quantize + DMMV launch.
 struct DmmvF32Args {
   const uint8_t *w;

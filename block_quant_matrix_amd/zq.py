@@ -36,6 +36,7 @@ SIGNATURES = {
     "zq_dmmv_q4_k": (_INT, [_P, _I64, _I64, _P, _P, _P, _P, _U32, _P]),
     "zq_dmmv_q5_k": (_INT, [_P, _I64, _I64, _P, _P, _P, _P, _U32, _P]),
     "zq_dmmv_q6_k": (_INT, [_P, _I64, _I64, _P, _P, _P, _U32, _P]),
+    "zq_dmmv_tokens": (_INT, [_INT, _P, _I64, _I64, _P, _P, _P, _I32, _P, _U32, _P]),
     "zq_dmmv_f32": (_INT, [_INT, _P, _I64, _I64, _P, _P, _U32, _P, _P, _P, _P]),
     "zq_dmmv_isums": (_INT, [_INT, _P, _I64, _I64, _P, _P, _P, _P]),
     "zq_argmax_workspace_bytes": (_SZ, [_I64]),
@@ -149,6 +150,11 @@ def zq_dmmv_q5_k(w, rows, k, qx, dx, sx, y, flags=0, stream=None):
 def zq_dmmv_q6_k(w, rows, k, qx, dx, y, flags=0, stream=None):
     return _call("zq_dmmv_q6_k", ptr(w), rows, k, ptr(qx), ptr(dx), ptr(y), flags,
                  _stream(stream))
+
+
+def zq_dmmv_tokens(wtype, w, rows, k, qx, dx, sx, n_tok, y, flags=0, stream=None):
+    return _call("zq_dmmv_tokens", wtype, ptr(w), rows, k, ptr(qx), ptr(dx), ptr(sx), n_tok, ptr(y),
+                 flags, _stream(stream))
 
 
 def zq_dmmv_f32(wtype, w, rows, k, x, y, flags=0, qx_out=None, dx_out=None, sx_out=None,

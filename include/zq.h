@@ -114,6 +114,20 @@ int zq_dmmv_q5_k(const void *w, int64_t rows, int64_t k, const int8_t *qx, const
 int zq_dmmv_q6_k(const void *w, int64_t rows, int64_t k, const int8_t *qx, const float *dx,
                  float *y, uint32_t flags, void *stream);
 
+/* Multi-token DMMV: the DMMV above for n_tok = 1..8 activations sharing one
+ * pass over the weights: the small-M matvec ("RTX 5090: Batched Prefill &
+ * CUDA Graphs in ZINC", section "What's next", names a multi-row kernel for
+ * the small-M expert matvecs; section "Prefill - a correction, and a better
+ * GEMM" takes all tokens through one weight pass instead of one matvec per
+ * token):
+ *   y[t][r] (+)= sum_b fp32(d_w[r][b]) * dx[t][b] * isum_t[r][b].
+ * wtype ZQ_Q4_0 or ZQ_Q8_0; qx [n_tok][k] int8 (16-byte aligned); dx
+ * [n_tok][k/32]; sx [n_tok][k/32] for Q4_0, may be NULL (ignored for Q8_0);
+ * y [n_tok][rows] fp32. */
+int zq_dmmv_tokens(int wtype, const void *w, int64_t rows, int64_t k, const int8_t *qx,
+                   const float *dx, const int32_t *sx, int32_t n_tok, float *y, uint32_t flags,
+                   void *stream);
+
 /* DMMV from the fp32 activation in one launch: y (+)= W . Q(x), where Q is
  * exactly the quantization of zq_quantize_act (same codes, scales, sums).
  * The input is the fp32 vector, as in the direct row-range DMMV slice of

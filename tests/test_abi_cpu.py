@@ -150,6 +150,25 @@ def test_q5k_q6k_argument_errors():
     assert L.zq_dmmv_isums(15, A, 4, 512, B, None, C, None) == zq.ZQ_EINVAL
 
 
+def test_tokens_argument_errors():
+    L = zq.lib()
+
+    def rc(wt=4, w=A, rows=4, k=512, qx=B, dx=C, sx=None, n_tok=2, y=D, flags=0):
+        return L.zq_dmmv_tokens(wt, w, rows, k, qx, dx, sx, n_tok, y, flags, None)
+
+    assert rc(n_tok=0) == zq.ZQ_EINVAL
+    assert rc(n_tok=9) == zq.ZQ_EINVAL
+    assert rc(wt=12) == zq.ZQ_EINVAL          # K-quants have their own entry points
+    assert rc(k=48) == zq.ZQ_EINVAL
+    assert rc(rows=-1) == zq.ZQ_EINVAL
+    assert rc(flags=2) == zq.ZQ_EINVAL
+    assert rc(qx=B + 4) == zq.ZQ_EALIGN
+    assert rc(w=A + 2) == zq.ZQ_EALIGN
+    assert rc(sx=C + 1) == zq.ZQ_EALIGN
+    assert rc(dx=None) == zq.ZQ_ENULL
+    assert rc(y=None) == zq.ZQ_ENULL
+
+
 def test_lmhead_argument_errors():
     L = zq.lib()
     ws = L.zq_dmmv_f32_argmax_workspace_bytes()
@@ -262,6 +281,7 @@ def test_valid_arguments_without_gpu_report_no_device():
     assert zq.lib().zq_dmmv_q4_k(A, 4, 512, B, C, None, D, 0, None) == zq.ZQ_EDEVICE
     assert zq.lib().zq_dmmv_q5_k(A, 4, 512, B, C, None, D, 0, None) == zq.ZQ_EDEVICE
     assert zq.lib().zq_dmmv_q6_k(A, 4, 512, B, C, D, 0, None) == zq.ZQ_EDEVICE
+    assert zq.lib().zq_dmmv_tokens(4, A, 4, 512, B, C, None, 2, D, 0, None) == zq.ZQ_EDEVICE
     L = zq.lib()
     assert L.zq_dmmv_f32_argmax(4, A, 248320, 2048, B, C, D, A + 0x8000,
                                 L.zq_dmmv_f32_argmax_workspace_bytes(), None) == zq.ZQ_EDEVICE
