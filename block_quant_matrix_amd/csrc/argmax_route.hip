@@ -102,7 +102,7 @@ __global__ __launch_bounds__(1024) void moe_route_kernel(const float *__restrict
   __shared__ float sel_v[64];
   __shared__ double sel_e[64];
   const int t = static_cast<int>(threadIdx.x);
-  for (int i = t; i < n_routed; i += static_cast<int>(blockDim.x)) lv[i] = logits[i];
+  for (int i = t; i < n_routed; i += static_cast<int>(blockDim.x)) lv[i] = route_key(logits[i]);
   __syncthreads();
   route_rank<P>(lv, n_routed, top_k, sel_id, sel_v);
   __syncthreads();

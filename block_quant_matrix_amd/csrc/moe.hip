@@ -63,17 +63,17 @@ __global__ __launch_bounds__(1024) void moe_gate_up_kernel(const MoeGateUpArgs a
   if constexpr (ROUTED) {
     // the router, in every workgroup: rank the logits, take slot s's expert
     __shared__ float rlv[1024];
-    for (int i = tid; i < a.n_routed; i += T) rlv[i] = a.logits[i];
+    for (int i = tid; i < a.n_routed; i += T) rlv[i] = route_key(a.logits[i]);
     __syncthreads();
     route_rank<8>(rlv, a.n_routed, a.top_k, rsel, rselv);
     __syncthreads();
     e = s < a.top_k ? rsel[s] : a.n_routed;
   } else {
     e = a.ids[s];
-    if (e < 0 || e >= a.n_experts) {  // uniform over the workgroup
-      if (a.status && tid == 0) *a.status = ZQ_ERANGE;
-      return;
-    }
+  }
+  if (e < 0 || e >= a.n_experts) {  // uniform over the workgroup
+    if (a.status && tid == 0) *a.status = ZQ_ERANGE;
+    return;
   }
   const uint8_t *wb = a.bank + static_cast<int64_t>(e) * a.expert_stride;
 

@@ -314,7 +314,12 @@ __device__ __forceinline__ void block_best(float &v, int32_t &i) {
 
 
 // ---------------------------------------------------------------- router --
-// Rank selection over n logits staged in LDS (lv) by the whole workgroup, P
+// A logit as staged for ranking: NaN becomes -inf, so that "beats" is a total
+// order on the staged values and every rank 0..n-1 is taken exactly once (a
+// NaN logit could otherwise leave a rank, and with it an expert slot, empty).
+__device__ __forceinline__ float route_key(float v) { return v != v ? -__builtin_inff() : v; }
+
+// Rank selection over n logits staged in LDS (lv, through route_key) by the whole workgroup, P
 // threads per logit: a logit's rank is the number of logits that beat it
 // (larger, or equal at a lower id), and the logits of rank < top_k are
 // stored at their rank (sel_id, sel_v), largest first with ties to the

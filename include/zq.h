@@ -253,7 +253,8 @@ int zq_moe_gate_up_route(int wtype, const void *gu_bank, int64_t gu_stride_bytes
  * (rows 0..d_ff-1 gate, d_ff..2*d_ff-1 up); down_bank: [d_model][d_ff].
  * workspace: at least zq_moe_ffn_workspace_bytes(d_model, d_ff, n_sel) bytes,
  * 256-byte aligned.  y [d_model] (+)= sum_s wts[s] * down_s.
- * flags: 0 or ZQ_ACCUMULATE. */
+ * flags: 0 or ZQ_ACCUMULATE.  y may be x itself (the residual add of a
+ * decode step): x is read only by the launches before y is written. */
 size_t zq_moe_ffn_workspace_bytes(int64_t d_model, int64_t d_ff, int32_t n_sel);
 int zq_moe_ffn(int wtype, const void *gu_bank, int64_t gu_stride_bytes, const void *down_bank,
                int64_t down_stride_bytes, int64_t n_experts, int64_t d_model, int64_t d_ff,

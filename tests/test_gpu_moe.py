@@ -323,3 +323,27 @@ def test_moe_gate_up_route_stage(zq, banks):
                         [host(t).view(np.uint8) for t in (qh, dh, sh, h, gu)])
         for a, b in zip(*outs):
             assert np.array_equal(a, b)
+
+
+def test_router_nan_logits_fill_every_slot(zq, banks):
+    """NaN logits rank below every number (ties by id), so every slot gets a
+    distinct expert in range, both in the router launch and inside the
+    routed gate/up pass: the selection the oracle makes when every NaN is
+    replaced by a number below all the others (the oracle takes finite
+    logits only)."""
+    logits, g = inputs.gen_router(E_ROUTED, inputs.seed_for(4, 40))
+    logits[[0, 5, int(np.argmax(logits)), 77]] = np.nan
+    low = np.float32(np.nanmin(logits) - 1000.0)
+    clean = np.where(np.isnan(logits), low, logits).astype(np.float32)
+    rids, _ = oracle.moe_route(clean, TOP_K, g)
+    ids, _ = gpu_route(zq, logits, g)
+    assert np.array_equal(ids, rids)
+    x = inputs.gen_activation(1, D_MODEL, 41)
+    ids2, wts2, y = routed_ffn(zq, banks["gu_d"], banks["gs"], banks["down_d"], banks["ds"],
+                               N_EXPERTS, D_MODEL, D_FF, logits, TOP_K, g, x)
+    assert np.array_equal(ids2, rids)
+    assert np.isfinite(host(y)).all()
+    # all logits NaN: still TOP_K distinct experts (ids 0..TOP_K-1) and the
+    # shared one; the weights are then undefined
+    ids3, _ = gpu_route(zq, np.full(E_ROUTED, np.nan, np.float32), g)
+    assert list(ids3) == list(range(TOP_K)) + [E_ROUTED]
