@@ -76,6 +76,7 @@ def lib() -> ctypes.CDLL:
         L.zqref_argmax_f32.argtypes = [P, I64]
         L.zqref_moe_route.argtypes = [P, I, I, P, P, P]
         L.zqref_swiglu.argtypes = [P, I64, I64, P]
+        L.zqref_rms_norm.argtypes = [P, P, ctypes.c_double, I64, I64, I64, P]
         L.zqref_gemm_entries.argtypes = [I, P, I64, I64, P, P, I64, P, P, I64, P, P]
         L.zqref_k_block_bytes.restype = I64
         L.zqref_k_block_bytes.argtypes = [I]
@@ -248,6 +249,20 @@ def moe_route(logits: np.ndarray, top_k: int, shared_gate: float | None):
     g = None if shared_gate is None else np.array([shared_gate], np.float32)
     _check(lib().zqref_moe_route(_p(logits), n, top_k, _p(g), _p(ids), _p(wts)), "moe_route")
     return ids, wts
+
+
+def rms_norm(x: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
+    """xn = x / sqrt(mean(x^2) + eps) * w per token, in fp64: x [T][K] or [K]
+    fp32, w [K] fp32 -> fp64 of x's shape."""
+    x = _c(x, np.float32)
+    squeeze = x.ndim == 1
+    x2 = x.reshape(1, -1) if squeeze else x
+    t, k = x2.shape
+    w = _c(w, np.float32)
+    assert w.size == k
+    xn = np.empty((t, k), np.float64)
+    _check(lib().zqref_rms_norm(_p(x2), _p(w), float(eps), t, k, k, _p(xn)), "rms_norm")
+    return xn[0] if squeeze else xn
 
 
 def swiglu(gu: np.ndarray, f: int) -> np.ndarray:

@@ -56,7 +56,12 @@
  *   - routing: top-k by logit (ties to the lower id), weights = softmax over
  *     the selected k; shared expert weight = sigmoid(g);
  *   - swiglu h = silu(g)*u with silu(z) = z/(1+exp(-z)), evaluated in fp64
- *     and rounded once to fp32.
+ *     and rounded once to fp32;
+ *   - rms_norm_mul ("Bringing ZINC to NVIDIA", section "The roadmap: from 70
+ *     to a coherent token"; fused rms_norm_dmmv kernels in "CUDA backend for
+ *     ZINC", section 5, milestone M3): xn_i = x_i / sqrt(mean_j x_j^2 + eps)
+ *     * w_i, the root-mean-square normalization with an elementwise weight,
+ *     eps an argument; evaluated in fp64.
  *
  * Every fp32 row output of the path is compared against the fp64 reference
  * y_ref computed here together with its error scale S = sum_b |t_b|.
@@ -549,6 +554,31 @@ int zqref_swiglu(const float *gu, int64_t n, int64_t f, float *h)
             double silu = g / (1.0 + exp(-g));
             h[s * f + i] = (float)(silu * u);
         }
+    }
+    return ZQREF_OK;
+}
+
+/* RMS normalization with an elementwise weight, per token t:
+ *   xn[t][i] = x[t][i] / sqrt((sum_j x[t][j]^2) / k + eps) * w[i],
+ * every step in fp64 (the sum sequential), the result kept in fp64.
+ * x: [n_tok][x_stride] (first k used); w: [k]; eps >= 0. */
+int zqref_rms_norm(const float *x, const float *w, double eps, int64_t n_tok, int64_t k,
+                   int64_t x_stride, double *xn)
+{
+    if (n_tok < 0 || k <= 0 || x_stride < k || !(eps >= 0.0) || !isfinite(eps)) return ZQREF_EINVAL;
+    for (int64_t i = 0; i < k; i++)
+        if (!isfinite(w[i])) return ZQREF_ENONFINITE;
+    for (int64_t t = 0; t < n_tok; t++) {
+        const float *xt = x + t * x_stride;
+        double ss = 0.0;
+        for (int64_t i = 0; i < k; i++) {
+            if (!isfinite(xt[i])) return ZQREF_ENONFINITE;
+            ss += (double)xt[i] * (double)xt[i];
+        }
+        double ms = ss / (double)k + eps;
+        if (!(ms > 0.0)) return ZQREF_EINVAL;  /* all-zero x with eps = 0 */
+        double r = sqrt(ms);
+        for (int64_t i = 0; i < k; i++) xn[t * k + i] = (double)xt[i] / r * (double)w[i];
     }
     return ZQREF_OK;
 }

@@ -691,3 +691,52 @@ def test_p15_generator_layout():
         off = 208 if wt == Q6_K else 0
         d = w[:, off:off + 2].copy().view("<f2").astype(np.float64).ravel()
         assert np.all(d >= 0) and 0.0004 < d.mean() < 0.0012
+
+
+# ------------------------------------------------------- P16: rms_norm ----
+
+def test_p16_rms_norm_golden(ref):
+    """Hand-derived values (tests/golden/rms_norm.txt)."""
+    n = 0
+    for line in open(os.path.join(GOLDEN, "rms_norm.txt")):
+        if not line.strip() or line.startswith("#"):
+            continue
+        xs, ws, eps, exp = [p.split() for p in line.split("|")]
+        x = np.array([float(v) for v in xs], np.float32)
+        w = np.array([float(v) for v in ws], np.float32)
+        got = ref.rms_norm(x, w, float(eps[0]))
+        assert np.allclose(got, [float(v) for v in exp], rtol=1e-15, atol=0), line
+        n += 1
+    assert n == 4
+
+
+def test_p16_rms_norm_invariants(ref):
+    rng = np.random.default_rng(16)
+    k = 2048
+    x = rng.standard_normal(k).astype(np.float32)
+    one = np.ones(k, np.float32)
+    xn = ref.rms_norm(x, one, 0.0)
+    # unit root mean square: sum of squares = k
+    assert abs(float(np.sum(xn * xn)) - k) <= 1e-9 * k
+    # scale invariance (eps = 0): a power of two scales x and the root mean
+    # square alike, exactly
+    assert np.array_equal(ref.rms_norm(4 * x, one, 0.0), xn)
+    assert np.array_equal(ref.rms_norm(0.5 * x, one, 0.0), xn)
+    # the weight multiplies elementwise, at its own index
+    w = rng.standard_normal(k).astype(np.float32)
+    assert np.allclose(ref.rms_norm(x, w, 0.0), xn * w.astype(np.float64), rtol=1e-15, atol=0)
+    # eps enters under the root: a constant vector c gives c / sqrt(c^2 + eps)
+    c = np.full(k, 0.75, np.float32)
+    assert np.allclose(ref.rms_norm(c, one, 0.4375), 0.75 / math.sqrt(0.5625 + 0.4375),
+                       rtol=1e-15, atol=0)
+    # a constant vector with eps = 0 normalizes to its sign
+    assert np.array_equal(ref.rms_norm(-c, one, 0.0), -np.ones(k))
+    # zero input: zero output with eps > 0, refused with eps = 0
+    assert np.array_equal(ref.rms_norm(np.zeros(k, np.float32), one, 1e-6), np.zeros(k))
+    with pytest.raises(RuntimeError):
+        ref.rms_norm(np.zeros(k, np.float32), one, 0.0)
+    # tokens are independent
+    x2 = rng.standard_normal((3, 64)).astype(np.float32)
+    xn2 = ref.rms_norm(x2, np.ones(64, np.float32), 1e-6)
+    for t in range(3):
+        assert np.array_equal(xn2[t], ref.rms_norm(x2[t], np.ones(64, np.float32), 1e-6))
