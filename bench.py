@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7, 8])
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7, 8, 9, 10])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -70,6 +70,10 @@ class Workload:
     def dominant(self, i):
         """Launch only the dominant kernel, on the inputs of step i."""
         raise NotImplementedError
+
+    def pct_of_peak(self, value, unit):
+        """The step's rate as a percentage of the chip's peak for its unit."""
+        return 100.0 * value / (HBM_PEAK_GBS if unit == "GB/s" else INT8_PEAK_TOPS)
 
     def value(self, ms_per_step):
         """(value, unit) of the whole step."""
@@ -266,6 +270,229 @@ class DmmvKWorkload(Workload):
                            "host thread, %.1f s" % (n, self.rows, self.tname, el))
 
 
+class DmmvTokWorkload(Workload):
+    """Quantize 8 tokens + one multi-token DMMV over Q4_0 4096 x 4096 (two
+    launches): the small-M decode shape."""
+    dominant_name = "dmmv_tok_kernel"
+
+    def __init__(self, wl):
+        from block_quant_matrix_amd import inputs
+        cfg = inputs.WORKLOADS[wl]
+        self.wl = wl
+        self.name = cfg["name"]
+        self.wtype, self.rows, self.k, self.T = cfg["wtype"], cfg["rows"], cfg["k"], cfg["n_tok"]
+        self.nb = self.k // 32
+        self.wbytes = self.rows * self.nb * inputs.BLOCK_BYTES[self.wtype]
+        # the DMMV reads the weights once and every token's codes, scales and
+        # sums, and writes T rows of fp32; the step adds the quantizer's fp32
+        # reads and its writes
+        self.dmmv_bytes = self.wbytes + self.T * (self.k + 8 * self.nb) + 4 * self.T * self.rows
+        self.step_bytes = self.dmmv_bytes + self.T * (4 * self.k + self.k + 8 * self.nb)
+        self.steps, self.warmup = 2000, 100
+
+    def setup(self, torch, zq, inputs):
+        self.torch, self.zq = torch, zq
+        self.ncopy = copies_for(self.wbytes)
+        host = [inputs.gen_weights(self.wtype, self.rows, self.k, inputs.seed_for(self.wl, c))
+                for c in range(self.ncopy)]
+        self.w = [torch.from_numpy(h).to("cuda") for h in host]
+        self.w_host0 = host[0]
+        del host
+        self.x_host = inputs.gen_activation(self.T, self.k, inputs.seed_for(self.wl) + 1)
+        self.x = torch.from_numpy(self.x_host).to("cuda")
+        self.qx = torch.empty((self.T, self.k), dtype=torch.int8, device="cuda")
+        self.dx = torch.empty((self.T, self.nb), dtype=torch.float32, device="cuda")
+        self.sx = torch.empty((self.T, self.nb), dtype=torch.int32, device="cuda")
+        self.y = torch.empty((self.T, self.rows), dtype=torch.float32, device="cuda")
+
+    def step(self, i):
+        self.zq.zq_quantize_act(self.x, self.T, self.k, self.k, self.qx, self.dx, self.sx)
+        self.dominant(i)
+
+    def prepare_dominant(self):
+        self.zq.zq_quantize_act(self.x, self.T, self.k, self.k, self.qx, self.dx, self.sx)
+
+    def dominant(self, i):
+        self.zq.zq_dmmv_tokens(self.wtype, self.w[i % self.ncopy], self.rows, self.k, self.qx,
+                               self.dx, self.sx, self.T, self.y)
+
+    def value(self, ms):
+        return self.step_bytes / (ms * 1e-3) / 1e9, "GB/s"
+
+    def achieved(self, ms):
+        return self.dmmv_bytes / (ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s", self.dmmv_bytes
+
+    def extra(self, ms):
+        return {"token_rows_per_s": self.T * self.rows / (ms * 1e-3), "us_per_token": ms * 1e3 / self.T}
+
+    def cpu_baseline(self, seconds):
+        import oracle
+        n, t0 = 0, time.perf_counter()
+        while True:
+            qx, dx, _ = oracle.quantize_act(self.x_host)
+            for t in range(self.T):
+                oracle.dmmv(self.wtype, self.w_host0, self.rows, self.k, qx[t], dx[t])
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+        per = el / n
+        return dict(value=self.step_bytes / per / 1e9, unit="GB/s", cores=1, kind="oracle",
+                    sample="%d full steps (quantize %d tokens + %d-row DMMV per token) on one "
+                           "host thread, %.1f s" % (n, self.T, self.rows, el))
+
+
+class DecodeChainWorkload(Workload):
+    """One token through 40 layers (RMS norm + Q8_0 router DMMV, routed MoE
+    block of 128 + 1 Q4_0 experts added onto the state) and the LM head with
+    its final norm and argmax: 122 launches, replayed as one HIP graph.  The
+    eager time of the same chain is reported beside it."""
+    dominant_name = "moe_gate_up_kernel (router folded in)"
+    bound = "hbm"
+
+    def __init__(self, wl):
+        from block_quant_matrix_amd import inputs
+        cfg = inputs.WORKLOADS[wl]
+        self.wl = wl
+        self.name = cfg["name"]
+        self.layers, self.nbanks = cfg["layers"], cfg["moe_banks"]
+        self.E, self.top_k, self.dm, self.dff = cfg["n_routed"], cfg["top_k"], cfg["d_model"], cfg["d_ff"]
+        self.vocab = cfg["vocab"]
+        self.n_sel = self.top_k + 1
+        bb = 18
+        gu_w = self.n_sel * 2 * self.dff * (self.dm // 32) * bb
+        down_w = self.n_sel * self.dm * (self.dff // 32) * bb
+        router_w = self.E * (self.dm // 32) * 34
+        lm_w = self.vocab * (self.dm // 32) * bb
+        # bytes a token must read at least: every layer's router and selected
+        # experts, the LM head; plus the fp32 state and logits traffic
+        self.token_bytes = self.layers * (router_w + gu_w + down_w) + lm_w + 4 * self.vocab
+        self.gate_up_bytes = (gu_w + 4 * self.dm + 4 * self.E + self.n_sel * self.dff +
+                              8 * self.n_sel * (self.dff // 32) + 8 * self.n_sel)
+        # each replay enqueues every kernel: 24 steps keep the timed region's
+        # launches within one hardware queue
+        self.steps, self.warmup = 24, 3
+
+    def setup(self, torch, zq, inputs):
+        from block_quant_matrix_amd.chain import DecodeChain
+        self.torch, self.zq = torch, zq
+        rng = np.random.default_rng(inputs.seed_for(self.wl, 9))
+        banks, self.host_banks = [], []
+        for c in range(self.nbanks):
+            gu, gs, down, ds = inputs.moe_banks(inputs.seed_for(self.wl, c), self.E + 1, self.dm,
+                                                self.dff)
+            banks.append((torch.from_numpy(gu).to("cuda"), gs, torch.from_numpy(down).to("cuda"),
+                          ds, self.E + 1))
+            self.host_banks.append((gu, gs, down, ds))
+        self.ncopy = self.nbanks
+        routers = [inputs.gen_weights(inputs.Q8_0, self.E, self.dm, inputs.seed_for(self.wl, 20 + l))
+                   for l in range(self.layers)]
+        norms = [(1 + 0.1 * rng.standard_normal(self.dm)).astype(np.float32)
+                 for _ in range(self.layers + 1)]
+        gates = rng.standard_normal(self.layers).astype(np.float32)
+        lm = inputs.gen_weights(inputs.Q4_0, self.vocab, self.dm, inputs.seed_for(self.wl, 30))
+        self.host = dict(routers=routers, norms=norms, gates=gates, lm=lm)
+        dev = lambda a: torch.from_numpy(a).to("cuda")
+        self.chain = DecodeChain(torch, [dev(r) for r in routers], [banks[l % self.nbanks]
+                                 for l in range(self.layers)], dev(lm),
+                                 [dev(n) for n in norms[:-1]], dev(norms[-1]), d_model=self.dm,
+                                 n_routed=self.E, top_k=self.top_k, d_ff=self.dff,
+                                 vocab=self.vocab,
+                                 shared_gate=[dev(gates[l:l + 1]) for l in range(self.layers)])
+        self.x0_host = inputs.gen_activation(1, self.dm, inputs.seed_for(self.wl) + 1)
+        self.x0 = dev(self.x0_host)
+        self.chain.x.copy_(self.x0)
+        self.chain.step()  # eager warm-up, then capture
+        torch.cuda.synchronize()
+        self.chain.x.copy_(self.x0)
+        self.chain.capture()
+        torch.cuda.synchronize()
+        # dominant kernel alone: the gate/up pass of one layer's MoE
+        self.qh = torch.empty((self.n_sel, self.dff), dtype=torch.int8, device="cuda")
+        self.dh = torch.empty((self.n_sel, self.dff // 32), dtype=torch.float32, device="cuda")
+        self.sh = torch.empty((self.n_sel, self.dff // 32), dtype=torch.int32, device="cuda")
+        self.banks = banks
+
+    def step(self, i):
+        self.chain.replay()
+
+    def prepare_dominant(self):
+        pass
+
+    def dominant(self, i):
+        gu, gs, _, _, ne = self.banks[i % self.nbanks]
+        c = self.chain
+        self.zq.zq_moe_gate_up_route(4, gu, gs, ne, self.dm, self.dff, c.logits, self.E,
+                                     self.top_k, c.shared_gate[0], c.xn, c.ids, c.wts, self.qh,
+                                     self.dh, self.sh)
+
+    def value(self, ms):
+        return 1.0 / (ms * 1e-3), "tok/s"
+
+    def pct_of_peak(self, value, unit):
+        # the bytes one token must read, at that token rate, against HBM peak
+        return 100.0 * self.token_bytes * value / 1e9 / HBM_PEAK_GBS
+
+    def achieved(self, ms):
+        return self.gate_up_bytes / (ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s", self.gate_up_bytes
+
+    def extra(self, ms):
+        torch = self.torch
+        K = self.steps
+        # the same chain launched eagerly, timed the same way
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            self.chain.step()
+        host_eager = (time.perf_counter() - t0) * 1e3 / K
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            self.chain.replay()
+        host_graph = (time.perf_counter() - t0) * 1e3 / K
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        gpu_blocker(torch, 1.5 * host_eager * K + 5)
+        e0.record()
+        for i in range(K):
+            self.chain.step()
+        e1.record()
+        torch.cuda.synchronize()
+        eager_ms = e0.elapsed_time(e1) / K
+        return {"launches_per_token": self.chain.launches_per_step(),
+                "graph_us_per_token": ms * 1e3, "eager_us_per_token": eager_ms * 1e3,
+                "host_submit_us_graph": host_graph * 1e3, "host_submit_us_eager": host_eager * 1e3,
+                "token_GB_per_s": self.token_bytes / (ms * 1e-3) / 1e9}
+
+    def cpu_baseline(self, seconds):
+        import oracle
+        h = self.host
+        n, t0 = 0, time.perf_counter()
+        while True:
+            x = self.x0_host.astype(np.float32).copy()
+            for l in range(self.layers):
+                xn = oracle.rms_norm(x, h["norms"][l], 1e-6).astype(np.float32)
+                qx, dx, _ = oracle.quantize_act(xn)
+                logits, _ = oracle.dmmv(8, h["routers"][l], self.E, self.dm, qx, dx)
+                ids, wts = oracle.moe_route(logits.astype(np.float32), self.top_k, h["gates"][l])
+                gu, gs, down, ds = self.host_banks[l % self.nbanks]
+                y, _ = oracle.moe_ffn(4, gu, gs, down, ds, self.dm, self.dff, ids, wts, xn)
+                x = (x + y).astype(np.float32)
+            xn = oracle.rms_norm(x, h["norms"][-1], 1e-6).astype(np.float32)
+            qx, dx, _ = oracle.quantize_act(xn)
+            yl, _ = oracle.dmmv(4, h["lm"], self.vocab, self.dm, qx, dx)
+            int(np.argmax(yl))
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+        per = el / n
+        return dict(value=1.0 / per, unit="tok/s", cores=1, kind="oracle",
+                    sample="%d tokens through the %d-layer chain and the LM head on one host "
+                           "thread, %.1f s" % (n, self.layers, el))
+
+
 class MoeWorkload(Workload):
     """Router + one token through 8 routed + 1 shared Q4_0 experts, in two
     launches: gate/up with the router folded in, then down."""
@@ -452,6 +679,10 @@ def make_workload(wl):
         return MoeWorkload()
     if wl in (6, 7, 8):
         return DmmvKWorkload(wl)
+    if wl == 9:
+        return DmmvTokWorkload(wl)
+    if wl == 10:
+        return DecodeChainWorkload(wl)
     return GemmWorkload()
 
 
@@ -564,7 +795,7 @@ def main():
         "dtype": "int8",
         "data": "synthetic",
         "config": {"workload": w.name, "weight_copies": w.ncopy, "parallelism": "none"},
-        "pct_of_peak": round(100.0 * value / (HBM_PEAK_GBS if unit == "GB/s" else INT8_PEAK_TOPS), 2),
+        "pct_of_peak": round(w.pct_of_peak(value, unit), 2),
     }
     out.update({k: round(v, 1) for k, v in w.extra(ms_per_step).items()})
     out["roofline"] = {"bound": w.bound, "kernel": w.dominant_name, "achieved": round(ach, 3),

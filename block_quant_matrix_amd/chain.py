@@ -2,17 +2,18 @@
 replay.
 
 One token passes through `layers` copies of the hot path and the LM head:
-  per layer: router logits = Q8_0 DMMV of the fp32 state (one launch, the
-    activation quantized inside), then the routed MoE block (router top-k +
-    softmax folded into the gate/up pass, SwiGLU + requantize, down with the
+  per layer: RMS-normalize the fp32 state and take the router logits as a
+    Q8_0 DMMV of it (one launch; the normalized state xn is published for
+    the experts), then the routed MoE block on xn (router top-k + softmax
+    folded into the gate/up pass, SwiGLU + requantize, down with the
     weighted sum) added onto the state (two launches, ZQ_ACCUMULATE);
-  then the LM head: Q4_0 DMMV of the state + argmax (two launches).
+  then the LM head: final RMS norm, Q4_0 DMMV + argmax (two launches).
 The layer order and the residual add follow the decode forward order of
 "Bringing ZINC to NVIDIA: a CUDA backend, because WSL2 only speaks CUDA",
 section "The roadmap: from 70 to a coherent token" (router DMMV,
 softmax_topk, expert gate/up, swiglu, expert down with the weighted
-accumulate, residual accumulate, LM head, argmax), without the attention,
-SSM and norm stages that lie outside this path.  Replaying the whole
+accumulate, residual accumulate, rms_norm_mul, LM head, argmax), without
+the attention and SSM stages that lie outside this path.  Replaying the whole
 per-token chain as one graph is "RTX 5090: Batched Prefill & CUDA Graphs in
 ZINC", section "CUDA graphs - the structural answer to launch latency";
 here torch.cuda.CUDAGraph records the same launches through HIP stream
@@ -29,16 +30,19 @@ from . import zq as _zq
 
 
 class DecodeChain:
-    def __init__(self, torch, router_w, moe_banks, lm_w, *, d_model, n_routed, top_k, d_ff,
-                 vocab, shared_gate):
+    def __init__(self, torch, router_w, moe_banks, lm_w, norm_w, final_norm_w, *, d_model,
+                 n_routed, top_k, d_ff, vocab, shared_gate, eps=1e-6):
         """router_w: per-layer Q8_0 [n_routed][d_model] device byte tensors;
         moe_banks: per-layer (gu_bank, gu_stride, down_bank, down_stride, n_experts);
-        lm_w: Q4_0 [vocab][d_model] device bytes; shared_gate: per-layer fp32
-        device scalars (the shared expert's gate g) or None."""
+        lm_w: Q4_0 [vocab][d_model] device bytes; norm_w: per-layer fp32
+        [d_model] RMS-norm weights, final_norm_w the one before the LM head;
+        shared_gate: per-layer fp32 device scalars (the shared expert's gate
+        g) or None."""
         self.torch = torch
         self.layers = len(router_w)
-        assert len(moe_banks) == self.layers
+        assert len(moe_banks) == self.layers and len(norm_w) == self.layers
         self.router_w, self.moe_banks, self.lm_w = router_w, moe_banks, lm_w
+        self.norm_w, self.final_norm_w, self.eps = norm_w, final_norm_w, eps
         self.d_model, self.n_routed, self.top_k, self.d_ff = d_model, n_routed, top_k, d_ff
         self.vocab = vocab
         self.shared_gate = shared_gate
@@ -46,6 +50,7 @@ class DecodeChain:
         n_sel = top_k + (1 if shared_gate is not None else 0)
         self.n_sel = n_sel
         self.x = torch.zeros(d_model, dtype=torch.float32, device=dev)  # the state
+        self.xn = torch.zeros(d_model, dtype=torch.float32, device=dev)  # normalized state
         self.logits = torch.empty(n_routed, dtype=torch.float32, device=dev)
         self.ids = torch.empty(n_sel, dtype=torch.int32, device=dev)
         self.wts = torch.empty(n_sel, dtype=torch.float32, device=dev)
@@ -61,15 +66,17 @@ class DecodeChain:
         """Enqueue one token: every layer, then the LM head and argmax."""
         d, f = self.d_model, self.d_ff
         for layer in range(self.layers):
-            _zq.zq_dmmv_f32(_zq.ZQ_Q8_0, self.router_w[layer], self.n_routed, d, self.x,
-                            self.logits, stream=stream)
+            _zq.zq_rms_norm_dmmv_f32(_zq.ZQ_Q8_0, self.router_w[layer], self.n_routed, d, self.x,
+                                     self.norm_w[layer], self.eps, self.logits,
+                                     xn_out=self.xn, stream=stream)
             gu, gs, dn, ds, ne = self.moe_banks[layer]
             g = None if self.shared_gate is None else self.shared_gate[layer]
             _zq.zq_moe_ffn_route(_zq.ZQ_Q4_0, gu, gs, dn, ds, ne, d, f, self.logits, self.n_routed,
-                                 self.top_k, g, self.x, self.ids, self.wts, self.ws, self.ws_bytes,
+                                 self.top_k, g, self.xn, self.ids, self.wts, self.ws, self.ws_bytes,
                                  self.x, _zq.ZQ_ACCUMULATE, stream=stream)
-        _zq.zq_dmmv_f32_argmax(_zq.ZQ_Q4_0, self.lm_w, self.vocab, d, self.x, self.y_lm, self.idx,
-                               self.lm_ws, self.lm_ws_bytes, stream=stream)
+        _zq.zq_rms_norm_dmmv_f32_argmax(_zq.ZQ_Q4_0, self.lm_w, self.vocab, d, self.x,
+                                        self.final_norm_w, self.eps, self.y_lm, self.idx,
+                                        self.lm_ws, self.lm_ws_bytes, stream=stream)
 
     def launches_per_step(self) -> int:
         return 3 * self.layers + 2

@@ -27,7 +27,7 @@
 
 namespace zq {
 
-template <int WT, int LPR, int BPL, int RB, int WPB, bool ARGMAX>
+template <int WT, int LPR, int BPL, int RB, int WPB, bool ARGMAX, bool NORM>
 __global__ __launch_bounds__(64 * WPB) void dmmv_f32x_kernel(const DmmvF32Args a) {
   constexpr int S = 64 / LPR;
   constexpr int NW = Blk<WT>::NW;
@@ -53,11 +53,16 @@ __global__ __launch_bounds__(64 * WPB) void dmmv_f32x_kernel(const DmmvF32Args a
   const int g = tid & 1;
   int qb = tid >> 1;
   float xv[16];
+  float nw[16];  // the norm weights of the same elements (NORM)
   if (qb < a.nb) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const float4 v = *reinterpret_cast<const float4 *>(a.x + qb * 32 + g * 16 + 4 * u);
       xv[4 * u] = v.x; xv[4 * u + 1] = v.y; xv[4 * u + 2] = v.z; xv[4 * u + 3] = v.w;
+      if constexpr (NORM) {
+        const float4 q = *reinterpret_cast<const float4 *>(a.norm_w + qb * 32 + g * 16 + 4 * u);
+        nw[4 * u] = q.x; nw[4 * u + 1] = q.y; nw[4 * u + 2] = q.z; nw[4 * u + 3] = q.w;
+      }
     }
   }
 
@@ -76,15 +81,55 @@ __global__ __launch_bounds__(64 * WPB) void dmmv_f32x_kernel(const DmmvF32Args a
     }
   }
 
+  // 2b. NORM: the sum of squares of x over the workgroup (fused
+  //     multiply-adds per thread, then block_sum_all), and the factor
+  float inv = 1.0f;
+  if constexpr (NORM) {
+    float ss = 0.0f;
+    for (int b = tid >> 1; b < a.nb; b += T / 2) {
+      if (b == (tid >> 1)) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) ss = __builtin_fmaf(xv[e], xv[e], ss);
+      } else {  // further blocks when k > 16*T
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float4 v = *reinterpret_cast<const float4 *>(a.x + b * 32 + g * 16 + 4 * u);
+          ss = __builtin_fmaf(v.x, v.x, ss);
+          ss = __builtin_fmaf(v.y, v.y, ss);
+          ss = __builtin_fmaf(v.z, v.z, ss);
+          ss = __builtin_fmaf(v.w, v.w, ss);
+        }
+      }
+    }
+    ss = block_sum_all<WPB>(ss);
+    inv = rms_inv(ss, a.k, a.eps);
+  }
+
   // 3. quantize the activation into LDS.  Two lanes per block keep the
   //    per-block work (the two IEEE divisions) on as few waves as possible.
   const bool out = (blockIdx.x == 0) && (a.qx_out != nullptr);
+  const bool xn_out = NORM && (blockIdx.x == 0) && (a.xn_out != nullptr);
   for (; qb < a.nb; qb += T / 2) {
     if (qb != (tid >> 1)) {  // further blocks when k > 16*T (not for k <= 16384)
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const float4 v = *reinterpret_cast<const float4 *>(a.x + qb * 32 + g * 16 + 4 * u);
         xv[4 * u] = v.x; xv[4 * u + 1] = v.y; xv[4 * u + 2] = v.z; xv[4 * u + 3] = v.w;
+        if constexpr (NORM) {
+          const float4 q = *reinterpret_cast<const float4 *>(a.norm_w + qb * 32 + g * 16 + 4 * u);
+          nw[4 * u] = q.x; nw[4 * u + 1] = q.y; nw[4 * u + 2] = q.z; nw[4 * u + 3] = q.w;
+        }
+      }
+    }
+    if constexpr (NORM) {
+#pragma clang fp contract(off)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) xv[e] = (xv[e] * inv) * nw[e];
+      if (xn_out) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          *reinterpret_cast<float4 *>(a.xn_out + qb * 32 + g * 16 + 4 * u) =
+              make_float4(xv[4 * u], xv[4 * u + 1], xv[4 * u + 2], xv[4 * u + 3]);
       }
     }
     uint32_t pk[4];
@@ -206,16 +251,24 @@ int launch_f(const DmmvF32Args &a, hipStream_t stream) {
   const int64_t rows_per_wg = static_cast<int64_t>(WPB) * RB * S;
   int64_t grid = (a.rows + rows_per_wg - 1) / rows_per_wg;
   const size_t lds = static_cast<size_t>(a.k) + 8 * static_cast<size_t>(a.nb);
+  const dim3 gd(static_cast<unsigned>(a.part && grid > kArgmaxMaxParts ? kArgmaxMaxParts : grid));
   if (a.part) {
-    if (grid > kArgmaxMaxParts) grid = kArgmaxMaxParts;
-    hipLaunchKernelGGL((dmmv_f32x_kernel<WT, LPR, BPL, RB, WPB, true>),
-                       dim3(static_cast<unsigned>(grid)), dim3(64 * WPB), lds, stream, a);
+    if (a.norm_w)
+      hipLaunchKernelGGL((dmmv_f32x_kernel<WT, LPR, BPL, RB, WPB, true, true>), gd, dim3(64 * WPB),
+                         lds, stream, a);
+    else
+      hipLaunchKernelGGL((dmmv_f32x_kernel<WT, LPR, BPL, RB, WPB, true, false>), gd, dim3(64 * WPB),
+                         lds, stream, a);
     ZQ_LAUNCH_CHECK();
-    if (a.out_idx) return launch_argmax_final(a.part, static_cast<int>(grid), a.out_idx, stream);
+    if (a.out_idx) return launch_argmax_final(a.part, static_cast<int>(gd.x), a.out_idx, stream);
     return ZQ_OK;
   }
-  hipLaunchKernelGGL((dmmv_f32x_kernel<WT, LPR, BPL, RB, WPB, false>),
-                     dim3(static_cast<unsigned>(grid)), dim3(64 * WPB), lds, stream, a);
+  if (a.norm_w)
+    hipLaunchKernelGGL((dmmv_f32x_kernel<WT, LPR, BPL, RB, WPB, false, true>), gd, dim3(64 * WPB),
+                       lds, stream, a);
+  else
+    hipLaunchKernelGGL((dmmv_f32x_kernel<WT, LPR, BPL, RB, WPB, false, false>), gd, dim3(64 * WPB),
+                       lds, stream, a);
   ZQ_LAUNCH_CHECK();
   return ZQ_OK;
 }

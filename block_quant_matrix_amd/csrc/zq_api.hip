@@ -279,6 +279,89 @@ int zq_dmmv_f32_argmax(int wtype, const void *w, int64_t rows, int64_t k, const 
   return zq::launch_dmmv_f32x(wtype, a, S(stream));
 }
 
+inline bool eps_ok(float eps) { return eps >= 0.0f && eps <= 3.0e38f; }  // finite, not NaN
+
+int zq_rms_norm_quantize(const float *x, const float *norm_w, float eps, int64_t n_tok, int64_t k,
+                         int64_t x_stride, int8_t *qx, float *dx, int32_t *sx, float *xn_out,
+                         void *stream) {
+  ZQ_REQUIRE(x && norm_w && qx && dx, ZQ_ENULL);
+  ZQ_REQUIRE(n_tok >= 0 && n_tok <= INT32_MAX && k_ok(k) && k <= (int64_t(1) << 30) &&
+                 x_stride >= k && eps_ok(eps),
+             ZQ_EINVAL);
+  ZQ_REQUIRE(al(x, 16) && x_stride % 4 == 0 && al(norm_w, 16) && al(qx, 16) && al(dx, 4) &&
+                 al(sx, 4) && al(xn_out, 16),
+             ZQ_EALIGN);
+  const int dc = check_current_device();
+  if (dc != ZQ_OK) return dc;
+  zq::RmsNormArgs a{};
+  a.x = x;
+  a.w = norm_w;
+  a.qx = qx;
+  a.dx = dx;
+  a.sx = sx;
+  a.xn_out = xn_out;
+  a.n_tok = n_tok;
+  a.x_stride = x_stride;
+  a.k = static_cast<int32_t>(k);
+  a.eps = eps;
+  return zq::launch_rms_norm_quantize(a, S(stream));
+}
+
+int zq_rms_norm_dmmv_f32(int wtype, const void *w, int64_t rows, int64_t k, const float *x,
+                         const float *norm_w, float eps, float *y, uint32_t flags, int8_t *qx_out,
+                         float *dx_out, int32_t *sx_out, float *xn_out, void *stream) {
+  ZQ_REQUIRE(block_bytes(wtype) > 0, ZQ_EINVAL);
+  ZQ_REQUIRE(w && x && norm_w && y, ZQ_ENULL);
+  ZQ_REQUIRE(rows >= 0 && k_ok(k) && k <= 16384 && eps_ok(eps), ZQ_EINVAL);
+  ZQ_REQUIRE((flags & ~uint32_t(ZQ_ACCUMULATE)) == 0, ZQ_EINVAL);
+  ZQ_REQUIRE(al(w, 4) && al(x, 16) && al(norm_w, 16) && al(y, 4) && al(qx_out, 4) &&
+                 al(dx_out, 4) && al(sx_out, 4) && al(xn_out, 16),
+             ZQ_EALIGN);
+  const int dc = check_current_device();
+  if (dc != ZQ_OK) return dc;
+  zq::DmmvF32Args a{};
+  a.w = static_cast<const uint8_t *>(w);
+  a.x = x;
+  a.y = y;
+  a.qx_out = qx_out;
+  a.dx_out = dx_out;
+  a.sx_out = sx_out;
+  a.norm_w = norm_w;
+  a.eps = eps;
+  a.xn_out = xn_out;
+  a.rows = rows;
+  a.k = static_cast<int32_t>(k);
+  a.nb = static_cast<int32_t>(k / 32);
+  a.flags = flags;
+  return zq::launch_dmmv_f32x(wtype, a, S(stream));
+}
+
+int zq_rms_norm_dmmv_f32_argmax(int wtype, const void *w, int64_t rows, int64_t k, const float *x,
+                                const float *norm_w, float eps, float *y, int32_t *out_idx,
+                                void *workspace, size_t workspace_bytes, void *stream) {
+  ZQ_REQUIRE(block_bytes(wtype) > 0, ZQ_EINVAL);
+  ZQ_REQUIRE(w && x && norm_w && y && workspace, ZQ_ENULL);
+  ZQ_REQUIRE(rows >= 1 && rows <= INT32_MAX && k_ok(k) && k <= 16384 && eps_ok(eps), ZQ_EINVAL);
+  ZQ_REQUIRE(workspace_bytes >= zq_dmmv_f32_argmax_workspace_bytes(), ZQ_EINVAL);
+  ZQ_REQUIRE(al(w, 4) && al(x, 16) && al(norm_w, 16) && al(y, 4) && al(out_idx, 4) &&
+                 al(workspace, 8),
+             ZQ_EALIGN);
+  const int dc = check_current_device();
+  if (dc != ZQ_OK) return dc;
+  zq::DmmvF32Args a{};
+  a.w = static_cast<const uint8_t *>(w);
+  a.x = x;
+  a.y = y;
+  a.part = workspace;
+  a.out_idx = out_idx;
+  a.norm_w = norm_w;
+  a.eps = eps;
+  a.rows = rows;
+  a.k = static_cast<int32_t>(k);
+  a.nb = static_cast<int32_t>(k / 32);
+  return zq::launch_dmmv_f32x(wtype, a, S(stream));
+}
+
 int zq_moe_route(const float *logits, int32_t n_routed, int32_t top_k, const float *shared_gate,
                  int32_t *ids, float *wts, void *stream) {
   ZQ_REQUIRE(logits && ids && wts, ZQ_ENULL);

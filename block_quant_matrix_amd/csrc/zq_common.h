@@ -265,6 +265,33 @@ __device__ __forceinline__ uint32_t quantize_block8(const float (&x)[4], float &
 }
 
 
+// ------------------------------------------------------------- rms norm --
+// 1 / sqrt(ss / k + eps), the RMS normalization factor: the mean is one IEEE
+// division, and the root and the reciprocal are correctly rounded (no
+// fast-math), each step rounded on its own.
+__device__ __forceinline__ float rms_inv(float ss, int k, float eps) {
+#pragma clang fp contract(off)
+  const float ms = ss / static_cast<float>(k) + eps;
+  return 1.0f / __builtin_sqrtf(ms);
+}
+
+// Sum of v over a workgroup of NWAVES waves, returned to every thread.
+// Every thread must call it (it synchronizes twice).
+template <int NWAVES>
+__device__ __forceinline__ float block_sum_all(float v) {
+  __shared__ float part[NWAVES];
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  const int w = static_cast<int>(threadIdx.x >> 6);
+  if ((threadIdx.x & 63) == 0) part[w] = v;
+  __syncthreads();
+  float t = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NWAVES; ++i) t += part[i];
+  __syncthreads();
+  return t;
+}
+
 // ---------------------------------------------------------------- argmax --
 // A (value, index) pair; a beats b when its value is larger, or equal at a
 // lower index (ties go to the lowest index).

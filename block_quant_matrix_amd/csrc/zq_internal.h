@@ -49,6 +49,21 @@ struct DmmvTokArgs {
 };
 int launch_dmmv_tok(int wtype, DmmvTokArgs a, hipStream_t stream);
 
+// RMS normalization + quantization, one workgroup per token.
+struct RmsNormArgs {
+  const float *x;       // [n_tok][x_stride]
+  const float *w;       // [k]
+  int8_t *qx;           // [n_tok][k]
+  float *dx;            // [n_tok][k/32]
+  int32_t *sx;          // may be null
+  float *xn_out;        // [n_tok][k], may be null
+  int64_t n_tok;
+  int64_t x_stride;
+  int32_t k;
+  float eps;
+};
+int launch_rms_norm_quantize(RmsNormArgs a, hipStream_t stream);
+
 // The fused quantize + DMMV launch.
 struct DmmvF32Args {
   const uint8_t *w;
@@ -64,6 +79,10 @@ struct DmmvF32Args {
   int32_t k;
   int32_t nb;
   uint32_t flags;
+  // last, so that the fields above keep their offsets in the kernel arguments
+  const float *norm_w;  // RMS-norm weight [k]: x is normalized before quantizing, or null
+  float *xn_out;        // optional copy of the normalized activation (with norm_w)
+  float eps;
 };
 
 // With a.part set, the launch is persistent (at most kArgmaxMaxParts

@@ -127,6 +127,12 @@ WORKLOADS = {
     # the LM head of the pages' model is Q6_K at the vocabulary shape
     7: dict(name="q6_k_lmhead_dmmv_248320x2048", wtype=Q6_K, rows=248320, k=2048),
     8: dict(name="q5_k_dmmv_4096x4096", wtype=Q5_K, rows=4096, k=4096),
+    # small-M decode: eight tokens through one pass over the weights
+    9: dict(name="q4_0_dmmv_8tok_4096x4096", wtype=Q4_0, rows=4096, k=4096, n_tok=8),
+    # one token through 40 layers of the path (norm + router + routed MoE)
+    # and the LM head, replayed as one graph; 4 distinct expert banks
+    10: dict(name="decode_chain_40l_moe128e_top8_lmhead248320", layers=40, moe_banks=4,
+             n_routed=128, top_k=8, d_model=2048, d_ff=512, vocab=248320),
 }
 
 

@@ -36,6 +36,11 @@ SIGNATURES = {
     "zq_dmmv_q4_k": (_INT, [_P, _I64, _I64, _P, _P, _P, _P, _U32, _P]),
     "zq_dmmv_q5_k": (_INT, [_P, _I64, _I64, _P, _P, _P, _P, _U32, _P]),
     "zq_dmmv_q6_k": (_INT, [_P, _I64, _I64, _P, _P, _P, _U32, _P]),
+    "zq_rms_norm_quantize": (_INT, [_P, _P, ctypes.c_float, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
+    "zq_rms_norm_dmmv_f32": (_INT, [_INT, _P, _I64, _I64, _P, _P, ctypes.c_float, _P, _U32, _P, _P,
+                                    _P, _P, _P]),
+    "zq_rms_norm_dmmv_f32_argmax": (_INT, [_INT, _P, _I64, _I64, _P, _P, ctypes.c_float, _P, _P, _P,
+                                           _SZ, _P]),
     "zq_dmmv_tokens": (_INT, [_INT, _P, _I64, _I64, _P, _P, _P, _I32, _P, _U32, _P]),
     "zq_dmmv_f32": (_INT, [_INT, _P, _I64, _I64, _P, _P, _U32, _P, _P, _P, _P]),
     "zq_dmmv_isums": (_INT, [_INT, _P, _I64, _I64, _P, _P, _P, _P]),
@@ -150,6 +155,24 @@ def zq_dmmv_q5_k(w, rows, k, qx, dx, sx, y, flags=0, stream=None):
 def zq_dmmv_q6_k(w, rows, k, qx, dx, y, flags=0, stream=None):
     return _call("zq_dmmv_q6_k", ptr(w), rows, k, ptr(qx), ptr(dx), ptr(y), flags,
                  _stream(stream))
+
+
+def zq_rms_norm_quantize(x, norm_w, eps, n_tok, k, x_stride, qx, dx, sx=None, xn_out=None,
+                         stream=None):
+    return _call("zq_rms_norm_quantize", ptr(x), ptr(norm_w), eps, n_tok, k, x_stride, ptr(qx),
+                 ptr(dx), ptr(sx), ptr(xn_out), _stream(stream))
+
+
+def zq_rms_norm_dmmv_f32(wtype, w, rows, k, x, norm_w, eps, y, flags=0, qx_out=None, dx_out=None,
+                         sx_out=None, xn_out=None, stream=None):
+    return _call("zq_rms_norm_dmmv_f32", wtype, ptr(w), rows, k, ptr(x), ptr(norm_w), eps, ptr(y),
+                 flags, ptr(qx_out), ptr(dx_out), ptr(sx_out), ptr(xn_out), _stream(stream))
+
+
+def zq_rms_norm_dmmv_f32_argmax(wtype, w, rows, k, x, norm_w, eps, y, out_idx, workspace,
+                                workspace_bytes, stream=None):
+    return _call("zq_rms_norm_dmmv_f32_argmax", wtype, ptr(w), rows, k, ptr(x), ptr(norm_w), eps,
+                 ptr(y), ptr(out_idx), ptr(workspace), workspace_bytes, _stream(stream))
 
 
 def zq_dmmv_tokens(wtype, w, rows, k, qx, dx, sx, n_tok, y, flags=0, stream=None):

@@ -143,6 +143,36 @@ int zq_dmmv_tokens(int wtype, const void *w, int64_t rows, int64_t k, const int8
 int zq_dmmv_f32(int wtype, const void *w, int64_t rows, int64_t k, const float *x, float *y,
                 uint32_t flags, int8_t *qx_out, float *dx_out, int32_t *sx_out, void *stream);
 
+/* RMS normalization fused with the activation quantization (the
+ * rms_norm_mul stage of "Bringing ZINC to NVIDIA: a CUDA backend, because
+ * WSL2 only speaks CUDA", section "The roadmap: from 70 to a coherent
+ * token", and the fused rms_norm_dmmv kernels of "CUDA backend for ZINC",
+ * section 5, milestone M3; the formula is the reading documented with the
+ * library).  Per token t, in fp32:
+ *   ss = sum_i x[t][i]^2 (fused multiply-adds, order the kernel's),
+ *   inv = 1 / sqrt(ss / k + eps)  (IEEE division and root),
+ *   xn[t][i] = (x[t][i] * inv) * norm_w[i],
+ * then qx/dx/sx = the zq_quantize_act quantization of xn.  norm_w [k] and
+ * x (row stride x_stride, a multiple of 4) 16-byte aligned; eps finite and
+ * >= 0; xn_out [n_tok][k] (16-byte aligned) receives xn when non-NULL; sx
+ * may be NULL.  x must be finite and not all zero when eps = 0. */
+int zq_rms_norm_quantize(const float *x, const float *norm_w, float eps, int64_t n_tok, int64_t k,
+                         int64_t x_stride, int8_t *qx, float *dx, int32_t *sx, float *xn_out,
+                         void *stream);
+/* zq_dmmv_f32 with the RMS normalization in front: y (+)= W . Q(xn), xn as
+ * in zq_rms_norm_quantize, in one launch (every workgroup reduces the sum of
+ * squares of x while its weight loads are in flight).  xn_out [k] (16-byte
+ * aligned, may be NULL) receives xn; qx_out / dx_out / sx_out as in
+ * zq_dmmv_f32.  32 <= k <= 16384. */
+int zq_rms_norm_dmmv_f32(int wtype, const void *w, int64_t rows, int64_t k, const float *x,
+                         const float *norm_w, float eps, float *y, uint32_t flags, int8_t *qx_out,
+                         float *dx_out, int32_t *sx_out, float *xn_out, void *stream);
+/* The LM-head step with the final RMS normalization in front: as
+ * zq_dmmv_f32_argmax on xn. */
+int zq_rms_norm_dmmv_f32_argmax(int wtype, const void *w, int64_t rows, int64_t k, const float *x,
+                                const float *norm_w, float eps, float *y, int32_t *out_idx,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
 /* Test hook: the per-block integer sums of the same DMMV inner loop,
  * isums[r][b] for every row r and block b (int32 [rows][k/32]). */
 int zq_dmmv_isums(int wtype, const void *w, int64_t rows, int64_t k, const int8_t *qx,

@@ -169,6 +169,43 @@ def test_tokens_argument_errors():
     assert rc(y=None) == zq.ZQ_ENULL
 
 
+def test_rms_norm_argument_errors():
+    L = zq.lib()
+
+    def rq(x=A, nw=B, eps=1e-6, n_tok=2, k=512, stride=512, qx=C, dx=D, sx=None, xn=None):
+        return L.zq_rms_norm_quantize(x, nw, eps, n_tok, k, stride, qx, dx, sx, xn, None)
+
+    assert rq(eps=-1.0) == zq.ZQ_EINVAL
+    assert rq(eps=float("nan")) == zq.ZQ_EINVAL
+    assert rq(eps=float("inf")) == zq.ZQ_EINVAL
+    assert rq(k=48) == zq.ZQ_EINVAL
+    assert rq(stride=256) == zq.ZQ_EINVAL       # shorter than k
+    assert rq(n_tok=-1) == zq.ZQ_EINVAL
+    assert rq(nw=None) == zq.ZQ_ENULL
+    assert rq(nw=B + 4) == zq.ZQ_EALIGN        # read 16 bytes at a time
+    assert rq(stride=514) == zq.ZQ_EALIGN
+    assert rq(xn=D + 8) == zq.ZQ_EALIGN
+
+    def rd(wt=4, w=A, rows=4, k=512, x=B, nw=C, eps=1e-6, y=D, flags=0, xn=None):
+        return L.zq_rms_norm_dmmv_f32(wt, w, rows, k, x, nw, eps, y, flags, None, None, None, xn,
+                                      None)
+
+    assert rd(wt=12) == zq.ZQ_EINVAL
+    assert rd(k=16416) == zq.ZQ_EINVAL
+    assert rd(eps=-0.5) == zq.ZQ_EINVAL
+    assert rd(flags=2) == zq.ZQ_EINVAL
+    assert rd(nw=None) == zq.ZQ_ENULL
+    assert rd(nw=C + 4) == zq.ZQ_EALIGN
+    assert rd(xn=D + 4) == zq.ZQ_EALIGN
+    ws = L.zq_dmmv_f32_argmax_workspace_bytes()
+    assert L.zq_rms_norm_dmmv_f32_argmax(4, A, 4, 512, B, None, 1e-6, D, None, C, ws,
+                                         None) == zq.ZQ_ENULL
+    assert L.zq_rms_norm_dmmv_f32_argmax(4, A, 4, 512, B, C, 1e-6, D, None, C, ws - 8,
+                                         None) == zq.ZQ_EINVAL
+    assert L.zq_rms_norm_dmmv_f32_argmax(4, A, 0, 512, B, C, 1e-6, D, None, C, ws,
+                                         None) == zq.ZQ_EINVAL
+
+
 def test_lmhead_argument_errors():
     L = zq.lib()
     ws = L.zq_dmmv_f32_argmax_workspace_bytes()
@@ -282,6 +319,10 @@ def test_valid_arguments_without_gpu_report_no_device():
     assert zq.lib().zq_dmmv_q5_k(A, 4, 512, B, C, None, D, 0, None) == zq.ZQ_EDEVICE
     assert zq.lib().zq_dmmv_q6_k(A, 4, 512, B, C, D, 0, None) == zq.ZQ_EDEVICE
     assert zq.lib().zq_dmmv_tokens(4, A, 4, 512, B, C, None, 2, D, 0, None) == zq.ZQ_EDEVICE
+    assert zq.lib().zq_rms_norm_quantize(A, B, 1e-6, 2, 512, 512, C, D, None, None,
+                                         None) == zq.ZQ_EDEVICE
+    assert zq.lib().zq_rms_norm_dmmv_f32(4, A, 4, 512, B, C, 1e-6, D, 0, None, None, None, None,
+                                         None) == zq.ZQ_EDEVICE
     L = zq.lib()
     assert L.zq_dmmv_f32_argmax(4, A, 248320, 2048, B, C, D, A + 0x8000,
                                 L.zq_dmmv_f32_argmax_workspace_bytes(), None) == zq.ZQ_EDEVICE

@@ -18,15 +18,18 @@ def chain():
     from block_quant_matrix_amd import zq
     from block_quant_matrix_amd.chain import DecodeChain
     assert zq.zq_device_check(0) == 0
-    router, banks, gates = [], [], []
+    router, banks, gates, norms = [], [], [], []
+    rng = np.random.default_rng(45)
     for layer in range(LAYERS):
         router.append(dev(inputs.gen_weights(inputs.Q8_0, N_ROUTED, D_MODEL, 40 + layer)))
         gu, gs, dn, ds = inputs.moe_banks(50 + layer, N_ROUTED + 1, D_MODEL, D_FF)
         banks.append((dev(gu), gs, dev(dn), ds, N_ROUTED + 1))
         gates.append(dev(np.array([0.3 * (layer - 1)], np.float32)))
+        norms.append(dev((1 + 0.1 * rng.standard_normal(D_MODEL)).astype(np.float32)))
     lm = dev(inputs.gen_weights(inputs.Q4_0, VOCAB, D_MODEL, 60))
-    return DecodeChain(torch, router, banks, lm, d_model=D_MODEL, n_routed=N_ROUTED, top_k=TOP_K,
-                       d_ff=D_FF, vocab=VOCAB, shared_gate=gates)
+    final = dev((1 + 0.1 * rng.standard_normal(D_MODEL)).astype(np.float32))
+    return DecodeChain(torch, router, banks, lm, norms, final, d_model=D_MODEL, n_routed=N_ROUTED,
+                       top_k=TOP_K, d_ff=D_FF, vocab=VOCAB, shared_gate=gates)
 
 
 def outputs(c):
