@@ -265,28 +265,48 @@ __global__ __launch_bounds__(64 * WPB) void moe_down_kernel(const MoeDownArgs a)
     if (first) {
       // The first chunk's windows are in flight: stage every slot's
       // activation (codes in 16-byte pieces, scales, 8*sums) in LDS meanwhile.
+      // Each thread issues up to kStage loads of each kind before it stores
+      // any, so a pass costs one cache latency rather than one per item.
+      constexpr int kStage = 4;
       const int64_t nq = static_cast<int64_t>(a.n_sel) * a.k / 16;
-      for (int64_t q = tid; q < nq; q += T) {
-        const int64_t sl = q * 16 / a.k, in = q * 16 - sl * a.k;
-        *reinterpret_cast<u32x4 *>(lq + q * 16) =
-            *reinterpret_cast<const u32x4 *>(a.qx + sl * a.x_stride + in);
-      }
       const int64_t nsc = static_cast<int64_t>(a.n_sel) * a.nb;
-      for (int64_t q = tid; q < nsc; q += T) {
-        const int64_t sl = q / a.nb, b = q - sl * a.nb;
-        ld[q] = a.dx[sl * (a.x_stride / 32) + b];
-        if constexpr (WT == ZQ_Q4_0) {
-          int32_t sum;
-          if (a.sx) {
-            sum = a.sx[sl * (a.x_stride / 32) + b];
-          } else {
-            sum = 0;
-            const uint32_t *cq = reinterpret_cast<const uint32_t *>(a.qx + sl * a.x_stride + 32 * b);
+      const int64_t nmax = nq > nsc ? nq : nsc;
+      for (int64_t base = tid; base < nmax; base += kStage * T) {
+        u32x4 cv[kStage];
+        float dv[kStage];
+        int32_t sv[kStage];
 #pragma unroll
-            for (int k = 0; k < 8; ++k)
-              sum = __builtin_amdgcn_sdot4(static_cast<int>(cq[k]), 0x01010101, sum, false);
+        for (int u = 0; u < kStage; ++u) {
+          const int64_t q = base + u * T;
+          if (q < nq) {
+            const int64_t sl = q * 16 / a.k, in = q * 16 - sl * a.k;
+            cv[u] = *reinterpret_cast<const u32x4 *>(a.qx + sl * a.x_stride + in);
           }
-          ls8[q] = 8 * sum;
+          if (q < nsc) {
+            const int64_t sl = q / a.nb, b = q - sl * a.nb;
+            dv[u] = a.dx[sl * (a.x_stride / 32) + b];
+            if constexpr (WT == ZQ_Q4_0) {
+              if (a.sx) {
+                sv[u] = a.sx[sl * (a.x_stride / 32) + b];
+              } else {
+                int32_t sum = 0;
+                const uint32_t *cq = reinterpret_cast<const uint32_t *>(a.qx + sl * a.x_stride + 32 * b);
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                  sum = __builtin_amdgcn_sdot4(static_cast<int>(cq[k]), 0x01010101, sum, false);
+                sv[u] = sum;
+              }
+            }
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kStage; ++u) {
+          const int64_t q = base + u * T;
+          if (q < nq) *reinterpret_cast<u32x4 *>(lq + q * 16) = cv[u];
+          if (q < nsc) {
+            ld[q] = dv[u];
+            if constexpr (WT == ZQ_Q4_0) ls8[q] = 8 * sv[u];
+          }
         }
       }
       __syncthreads();  // the staged activations are visible
