@@ -144,7 +144,7 @@ __global__ __launch_bounds__(256) void dmmv_kernel(const DmmvArgs a) {
   if constexpr (MODE == MODE_GATHER) {
     s0 = static_cast<int>(blockIdx.y);
     s1 = s0 + 1;
-    const int e = a.ids[s0];
+    const int e = a.ids[s0] - a.id_base;
     if (e < 0 || e >= a.n_experts) {  // uniform over the block
       if (a.status) *a.status = ZQ_ERANGE;
       return;
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(256) void dmmv_kernel(const DmmvArgs a) {
       const uint8_t *wb = a.w;
       float ws = 1.0f;
       if constexpr (MODE == MODE_GATHER || MODE == MODE_WEIGHTED) {
-        const int e = a.ids[s];
+        const int e = a.ids[s] - a.id_base;
         if (e < 0 || e >= a.n_experts) {
           if (a.status) *a.status = ZQ_ERANGE;
           continue;

@@ -76,11 +76,14 @@ __device__ __forceinline__ int32_t code_sum(const uint32_t *q, int n) {
 // Loads only.  Units past the row end load the row's last unit; their
 // scales are zeroed in finish_act.
 template <int WT, int LPR, int BPL>
-__device__ __forceinline__ void load_unit_act(KUnitAct (&act)[BPL], const DmmvArgs &a, int pass,
-                                              int j, int nu) {
-  // block sums come from sx when given; otherwise the loads read dx (any
-  // valid address) and finish_act sums the codes
-  const int32_t *sxp = a.sx ? a.sx : reinterpret_cast<const int32_t *>(a.dx);
+__device__ __forceinline__ void load_unit_act(KUnitAct (&act)[BPL], const DmmvArgs &a, int s,
+                                              int pass, int j, int nu) {
+  // slot s's activation; block sums come from sx when given, otherwise the
+  // loads read dx (any valid address) and finish_act sums the codes
+  const int8_t *qx = a.qx + static_cast<int64_t>(s) * a.x_stride;
+  const float *dx = a.dx + static_cast<int64_t>(s) * (a.x_stride / 32);
+  const int32_t *sxp = a.sx ? a.sx + static_cast<int64_t>(s) * (a.x_stride / 32)
+                            : reinterpret_cast<const int32_t *>(dx);
 #pragma unroll
   for (int i = 0; i < BPL; ++i) {
     int u = pass * LPR * BPL + j + LPR * i;
@@ -91,20 +94,20 @@ __device__ __forceinline__ void load_unit_act(KUnitAct (&act)[BPL], const DmmvAr
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int e0 = base + 32 * c;
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(a.qx + e0);
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(qx + e0);
         A.q[4 * c] = v.x; A.q[4 * c + 1] = v.y; A.q[4 * c + 2] = v.z; A.q[4 * c + 3] = v.w;
-        A.d[c] = a.dx[e0 >> 5];
+        A.d[c] = dx[e0 >> 5];
       }
     } else {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int b = 2 * u + h;
-        const u32x4 v0 = *reinterpret_cast<const u32x4 *>(a.qx + 32 * b);
-        const u32x4 v1 = *reinterpret_cast<const u32x4 *>(a.qx + 32 * b + 16);
+        const u32x4 v0 = *reinterpret_cast<const u32x4 *>(qx + 32 * b);
+        const u32x4 v1 = *reinterpret_cast<const u32x4 *>(qx + 32 * b + 16);
         uint32_t *q = &A.q[8 * h];
         q[0] = v0.x; q[1] = v0.y; q[2] = v0.z; q[3] = v0.w;
         q[4] = v1.x; q[5] = v1.y; q[6] = v1.z; q[7] = v1.w;
-        A.d[h] = a.dx[b];
+        A.d[h] = dx[b];
         A.sraw[h] = sxp[b];
       }
     }
@@ -270,9 +273,15 @@ __device__ __forceinline__ float unit_dot(const uint32_t (&v)[KQ<WT>::NWD], int 
 // The occupancy target is capped at 2 waves per SIMD: aiming higher, the
 // scheduler trades the loads of later row steps (issued together, so a wave
 // has all its bytes in flight at once) for registers and serialises them.
-template <int WT, int LPR, int BPL, int RB, bool ISUMS>
+//
+// MODE: MODE_PLAIN / MODE_ISUMS (one matrix), MODE_GATHER (grid.y = slot s:
+// y[s] = W[e_s] . x_s), MODE_WEIGHTED (every slot: y = sum_s wts[s] W[e_s]
+// . x_s, folded into the row partials before the lane reduction); expert
+// e_s = ids[s] - id_base, skipped (and reported) outside [0, n_experts).
+template <int WT, int LPR, int BPL, int RB, int MODE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void dmmv_k_kernel(
     const DmmvArgs a) {
+  constexpr bool ISUMS = MODE == MODE_ISUMS;
   constexpr int S = 64 / LPR;
   constexpr int NWD = KQ<WT>::NWD;
   const int lane = static_cast<int>(threadIdx.x & 63);
@@ -284,60 +293,91 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   const int n_pass = (nu + LPR * BPL - 1) / (LPR * BPL);
   const int p = j & 3;      // the lane's unit position in every super-block it visits
 
+  int s0 = 0, s1 = 1;
+  if constexpr (MODE == MODE_GATHER) {
+    s0 = static_cast<int>(blockIdx.y);
+    s1 = s0 + 1;
+    const int e = a.ids[s0] - a.id_base;
+    if (e < 0 || e >= a.n_experts) {  // uniform over the workgroup
+      if (a.status) *a.status = ZQ_ERANGE;
+      return;
+    }
+  } else if constexpr (MODE == MODE_WEIGHTED) {
+    s1 = a.n_sel;
+  }
+
   KUnitAct act[BPL];
-  if (n_pass == 1) load_unit_act<WT, LPR, BPL>(act, a, 0, j, nu);
+  const bool hoist = (n_pass == 1) && (MODE != MODE_WEIGHTED);
+  if (hoist) load_unit_act<WT, LPR, BPL>(act, a, s0, 0, j, nu);
 
   for (int64_t gi = wave; gi < a.n_groups; gi += n_waves) {
     const int64_t row0 = gi * (RB * S);
     float acc[RB];
 #pragma unroll
     for (int t = 0; t < RB; ++t) acc[t] = 0.0f;
-    for (int pass = 0; pass < n_pass; ++pass) {
-      if (n_pass > 1) load_unit_act<WT, LPR, BPL>(act, a, pass, j, nu);
-      uint32_t v[RB][BPL][NWD];
-#pragma unroll
-      for (int t = 0; t < RB; ++t) {
-        int64_t row = row0 + t * S + slot;
-        row = row < a.rows ? row : a.rows - 1;
-#pragma unroll
-        for (int i = 0; i < BPL; ++i) {
-          int u = pass * LPR * BPL + j + LPR * i;
-          u = u < nu ? u : nu - 1;
-          const uint8_t *sb = a.w + row * a.row_bytes + static_cast<int64_t>(u >> 2) * KQ<WT>::BYTES;
-          load_unit_w<WT>(sb, p, v[t][i]);
+    for (int s = s0; s < s1; ++s) {
+      const uint8_t *wb = a.w;
+      float ws = 1.0f;
+      if constexpr (MODE == MODE_GATHER || MODE == MODE_WEIGHTED) {
+        const int e = a.ids[s] - a.id_base;
+        if (e < 0 || e >= a.n_experts) {
+          if (a.status) *a.status = ZQ_ERANGE;
+          continue;
         }
+        wb = a.w + static_cast<int64_t>(e) * a.expert_stride;
+        if constexpr (MODE == MODE_WEIGHTED) ws = a.wts[s];
       }
-      // re-derived every group: a few dot4 per unit, no loads
-      finish_act<WT, LPR, BPL>(act, a, pass, j, nu);
+      for (int pass = 0; pass < n_pass; ++pass) {
+        if (!hoist) load_unit_act<WT, LPR, BPL>(act, a, s, pass, j, nu);
+        uint32_t v[RB][BPL][NWD];
 #pragma unroll
-      for (int t = 0; t < RB; ++t) {
-        float part = 0.0f;
+        for (int t = 0; t < RB; ++t) {
+          int64_t row = row0 + t * S + slot;
+          row = row < a.rows ? row : a.rows - 1;
 #pragma unroll
-        for (int i = 0; i < BPL; ++i) {
-          int32_t is[4];
-          part += unit_dot<WT>(v[t][i], p, act[i], is);
-          if constexpr (ISUMS) {
-            const int64_t row = row0 + t * S + slot;
-            const int u = pass * LPR * BPL + j + LPR * i;
-            if constexpr (WT == ZQ_Q6_K) {
-              // a block's two 16-element runs sit in lanes p and p^1
-              int32_t blk[4];
+          for (int i = 0; i < BPL; ++i) {
+            int u = pass * LPR * BPL + j + LPR * i;
+            u = u < nu ? u : nu - 1;
+            const uint8_t *sb = wb + row * a.row_bytes + static_cast<int64_t>(u >> 2) * KQ<WT>::BYTES;
+            load_unit_w<WT>(sb, p, v[t][i]);
+          }
+        }
+        // re-derived every group: a few dot4 per unit, no loads
+        finish_act<WT, LPR, BPL>(act, a, pass, j, nu);
 #pragma unroll
-              for (int c = 0; c < 4; ++c) blk[c] = is[c] + __shfl_xor(is[c], 1);
-              if (row < a.rows && u < nu && (p & 1) == 0) {
-                int32_t *dst = a.isums + row * a.nb + 8 * (u >> 2) + 4 * (p >> 1);
+        for (int t = 0; t < RB; ++t) {
+          float part = 0.0f;
 #pragma unroll
-                for (int c = 0; c < 4; ++c) dst[c] = blk[c];
-              }
-            } else {
-              if (row < a.rows && u < nu) {
-                a.isums[row * a.nb + 2 * u] = is[0];
-                a.isums[row * a.nb + 2 * u + 1] = is[1];
+          for (int i = 0; i < BPL; ++i) {
+            int32_t is[4];
+            part += unit_dot<WT>(v[t][i], p, act[i], is);
+            if constexpr (ISUMS) {
+              const int64_t row = row0 + t * S + slot;
+              const int u = pass * LPR * BPL + j + LPR * i;
+              if constexpr (WT == ZQ_Q6_K) {
+                // a block's two 16-element runs sit in lanes p and p^1
+                int32_t blk[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) blk[c] = is[c] + __shfl_xor(is[c], 1);
+                if (row < a.rows && u < nu && (p & 1) == 0) {
+                  int32_t *dst = a.isums + row * a.nb + 8 * (u >> 2) + 4 * (p >> 1);
+#pragma unroll
+                  for (int c = 0; c < 4; ++c) dst[c] = blk[c];
+                }
+              } else {
+                if (row < a.rows && u < nu) {
+                  a.isums[row * a.nb + 2 * u] = is[0];
+                  a.isums[row * a.nb + 2 * u + 1] = is[1];
+                }
               }
             }
           }
+          if constexpr (MODE == MODE_WEIGHTED) {
+            acc[t] = __builtin_fmaf(ws, part, acc[t]);
+          } else {
+            acc[t] += part;
+          }
         }
-        acc[t] += part;
       }
     }
     if constexpr (!ISUMS) {
@@ -350,6 +390,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
           const int64_t row = row0 + static_cast<int64_t>(R::rowstep(m, lane)) * S + slot;
           if (row < a.rows) {
             float *yp = a.y + row;
+            if constexpr (MODE == MODE_GATHER) yp += static_cast<int64_t>(s0) * a.rows;
             *yp = (a.flags & ZQ_ACCUMULATE) ? *yp + out[m] : out[m];
           }
         }
@@ -386,79 +427,89 @@ KShape choose_kshape(int nu) {
 }
 
 // Largest row steps per group RB whose weight registers (RB*BPL units of
-// NWD dwords) stay within 96 dwords and that still leaves >= 2048 waves.
+// NWD dwords) stay within 96 dwords and that still leaves >= 2048 waves
+// (counting every gathered slot); the MoE modes keep RB <= 4.
 template <int WT>
-int choose_krb(const KShape &sh, int64_t rows, bool isums) {
-  if (isums) return 1;
+int choose_krb(const KShape &sh, int64_t rows, int mode, int64_t slots) {
+  if (mode == MODE_ISUMS) return 1;
   const int S = 64 / sh.lpr;
   const int cap = 96 / (KQ<WT>::NWD * sh.bpl);
   for (int rb : {8, 4, 2, 1}) {
     if (rb > cap && rb > 1) continue;
-    if (rb == 1 || (rows + rb * S - 1) / (rb * S) >= 2048) return rb;
+    if (rb > 4 && mode != MODE_PLAIN) continue;
+    if (rb == 1 || (rows + rb * S - 1) / (rb * S) * slots >= 2048) return rb;
   }
   return 1;
 }
 
-template <int WT, int LPR, int BPL, int RB, bool ISUMS>
+template <int WT, int LPR, int BPL, int RB, int MODE>
 int launch_k1(DmmvArgs a, hipStream_t stream) {
   constexpr int S = 64 / LPR;
   a.n_groups = (a.rows + RB * S - 1) / (RB * S);
   const int64_t blocks = (a.n_groups + 3) / 4;
   const unsigned grid = static_cast<unsigned>(blocks < 1048576 ? blocks : 1048576);
-  hipLaunchKernelGGL((dmmv_k_kernel<WT, LPR, BPL, RB, ISUMS>), dim3(grid), dim3(256), 0, stream,
+  const unsigned gy = MODE == MODE_GATHER ? static_cast<unsigned>(a.n_sel) : 1u;
+  hipLaunchKernelGGL((dmmv_k_kernel<WT, LPR, BPL, RB, MODE>), dim3(grid, gy), dim3(256), 0, stream,
                      a);
   ZQ_LAUNCH_CHECK();
   return ZQ_OK;
 }
 
-// RB values instantiated per (type, BPL): those choose_krb can return.
-template <int WT, int LPR, int BPL, bool ISUMS>
+// RB values instantiated per (type, BPL, mode): those choose_krb can return.
+template <int WT, int LPR, int BPL, int MODE>
 int launch_krb(int rb, const DmmvArgs &a, hipStream_t stream) {
-  constexpr int CAP = 96 / (KQ<WT>::NWD * BPL);
-  if constexpr (ISUMS) {
-    return launch_k1<WT, LPR, BPL, 1, true>(a, stream);
+  constexpr int CAP0 = 96 / (KQ<WT>::NWD * BPL);
+  constexpr int CAP = MODE == MODE_PLAIN ? CAP0 : (CAP0 < 4 ? CAP0 : 4);
+  if constexpr (MODE == MODE_ISUMS) {
+    return launch_k1<WT, LPR, BPL, 1, MODE>(a, stream);
   } else {
     if constexpr (CAP >= 8) {
-      if (rb >= 8) return launch_k1<WT, LPR, BPL, 8, false>(a, stream);
+      if (rb >= 8) return launch_k1<WT, LPR, BPL, 8, MODE>(a, stream);
     }
     if constexpr (CAP >= 4) {
-      if (rb >= 4) return launch_k1<WT, LPR, BPL, 4, false>(a, stream);
+      if (rb >= 4) return launch_k1<WT, LPR, BPL, 4, MODE>(a, stream);
     }
     if constexpr (CAP >= 2) {
-      if (rb >= 2) return launch_k1<WT, LPR, BPL, 2, false>(a, stream);
+      if (rb >= 2) return launch_k1<WT, LPR, BPL, 2, MODE>(a, stream);
     }
-    return launch_k1<WT, LPR, BPL, 1, false>(a, stream);
+    return launch_k1<WT, LPR, BPL, 1, MODE>(a, stream);
   }
 }
 
-template <int WT, bool ISUMS>
+template <int WT, int MODE>
 int launch_kshape(const KShape &sh, int rb, const DmmvArgs &a, hipStream_t stream) {
-  if (sh.lpr == 8) return launch_krb<WT, 8, 1, ISUMS>(rb, a, stream);
-  if (sh.lpr == 16 && sh.bpl == 1) return launch_krb<WT, 16, 1, ISUMS>(rb, a, stream);
-  if (sh.lpr == 16) return launch_krb<WT, 16, 5, ISUMS>(rb, a, stream);
-  if (sh.lpr == 32) return launch_krb<WT, 32, 1, ISUMS>(rb, a, stream);
-  if (sh.bpl == 1) return launch_krb<WT, 64, 1, ISUMS>(rb, a, stream);
-  if (sh.bpl == 2) return launch_krb<WT, 64, 2, ISUMS>(rb, a, stream);
-  return launch_krb<WT, 64, 4, ISUMS>(rb, a, stream);
+  if (sh.lpr == 8) return launch_krb<WT, 8, 1, MODE>(rb, a, stream);
+  if (sh.lpr == 16 && sh.bpl == 1) return launch_krb<WT, 16, 1, MODE>(rb, a, stream);
+  if (sh.lpr == 16) return launch_krb<WT, 16, 5, MODE>(rb, a, stream);
+  if (sh.lpr == 32) return launch_krb<WT, 32, 1, MODE>(rb, a, stream);
+  if (sh.bpl == 1) return launch_krb<WT, 64, 1, MODE>(rb, a, stream);
+  if (sh.bpl == 2) return launch_krb<WT, 64, 2, MODE>(rb, a, stream);
+  return launch_krb<WT, 64, 4, MODE>(rb, a, stream);
 }
 
 template <int WT>
-int launch_type(DmmvArgs a, bool isums, hipStream_t stream) {
+int launch_type(int mode, DmmvArgs a, hipStream_t stream) {
   a.row_bytes = static_cast<int64_t>(a.nb / 8) * KQ<WT>::BYTES;
   const KShape sh = choose_kshape(a.nb / 2);
-  const int rb = choose_krb<WT>(sh, a.rows, isums);
-  if (isums) return launch_kshape<WT, true>(sh, rb, a, stream);
-  return launch_kshape<WT, false>(sh, rb, a, stream);
+  const int64_t slots = mode == MODE_GATHER ? a.n_sel : 1;
+  const int rb = choose_krb<WT>(sh, a.rows, mode, slots);
+  switch (mode) {
+    case MODE_PLAIN: return launch_kshape<WT, MODE_PLAIN>(sh, rb, a, stream);
+    case MODE_ISUMS: return launch_kshape<WT, MODE_ISUMS>(sh, rb, a, stream);
+    case MODE_GATHER: return launch_kshape<WT, MODE_GATHER>(sh, rb, a, stream);
+    default: return launch_kshape<WT, MODE_WEIGHTED>(sh, rb, a, stream);
+  }
 }
 
 }  // namespace
 
-int launch_dmmv_k(int wtype, DmmvArgs a, bool isums, hipStream_t stream) {
+int launch_dmmv_k(int wtype, int mode, DmmvArgs a, hipStream_t stream) {
   if (a.rows == 0) return ZQ_OK;
+  if (mode == MODE_GATHER && a.n_sel == 0) return ZQ_OK;
   switch (wtype) {
-    case ZQ_Q4_K: return launch_type<ZQ_Q4_K>(a, isums, stream);
-    case ZQ_Q5_K: return launch_type<ZQ_Q5_K>(a, isums, stream);
-    case ZQ_Q6_K: return launch_type<ZQ_Q6_K>(a, isums, stream);
+    case ZQ_Q4_K: return launch_type<ZQ_Q4_K>(mode, a, stream);
+    case ZQ_Q5_K: return launch_type<ZQ_Q5_K>(mode, a, stream);
+    case ZQ_Q6_K: return launch_type<ZQ_Q6_K>(mode, a, stream);
     default: return ZQ_EINVAL;
   }
 }

@@ -240,7 +240,7 @@ __global__ __launch_bounds__(64 * WPB) void moe_down_kernel(const MoeDownArgs a)
     // v_readlane makes each one uniform; the weights come the same way.
     const int cl = lane & (kDownMaxSel - 1);
     const bool cok = s0 + cl < a.n_sel;
-    const int my_id = cok ? a.ids[s0 + cl] : -1;
+    const int my_id = cok ? a.ids[s0 + cl] - a.id_base : -1;
     const float my_w = cok ? a.wts[s0 + cl] : 0.0f;
     int eid[kDownMaxSel];
 #pragma unroll

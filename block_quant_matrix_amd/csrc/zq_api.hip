@@ -108,7 +108,53 @@ int dmmv_k_common(int wtype, const void *w, int64_t rows, int64_t k, const int8_
   a.rows = rows;
   a.nb = static_cast<int32_t>(k / 32);
   a.flags = flags;
-  return zq::launch_dmmv_k(wtype, a, isums != nullptr, S(stream));
+  return zq::launch_dmmv_k(wtype, isums ? zq::MODE_ISUMS : zq::MODE_PLAIN, a, S(stream));
+}
+
+// Expert-indexed K-quant DMMV (gather / weighted sum); id_base is
+// subtracted from every id (a bank that holds experts id_base.. only).
+int dmmv_moe_k(int wtype, const void *bank, int64_t n_experts, int64_t expert_stride_bytes,
+               int64_t rows, int64_t k, const int32_t *ids, const float *wts, int32_t n_sel,
+               const int8_t *qx, const float *dx, const int32_t *sx, int64_t x_stride, int mode,
+               float *y, uint32_t flags, int32_t *dev_status, int32_t id_base, hipStream_t stream) {
+  const int64_t sbb = wtype == ZQ_Q4_K ? 144 : (wtype == ZQ_Q5_K ? 176 : 210);
+  ZQ_REQUIRE(mode == ZQ_MOE_GATHER || mode == ZQ_MOE_WEIGHTED_SUM, ZQ_EINVAL);
+  ZQ_REQUIRE(bank && ids && qx && dx && y, ZQ_ENULL);
+  ZQ_REQUIRE(mode == ZQ_MOE_GATHER || wts, ZQ_ENULL);
+  ZQ_REQUIRE(n_experts >= 1 && n_experts <= INT32_MAX && rows >= 0 && k_ok(k) && k % 256 == 0,
+             ZQ_EINVAL);
+  ZQ_REQUIRE(n_sel >= 0 && n_sel <= 65535, ZQ_EINVAL);
+  ZQ_REQUIRE(x_stride >= 0 && x_stride % 32 == 0 && (x_stride == 0 || x_stride >= k), ZQ_EINVAL);
+  ZQ_REQUIRE(expert_stride_bytes >= rows * (k / 256) * sbb, ZQ_EINVAL);
+  if (mode == ZQ_MOE_GATHER) {
+    ZQ_REQUIRE(flags == 0, ZQ_EINVAL);
+  } else {
+    ZQ_REQUIRE((flags & ~uint32_t(ZQ_ACCUMULATE)) == 0, ZQ_EINVAL);
+  }
+  ZQ_REQUIRE(al(bank, 16) && expert_stride_bytes % 16 == 0 && al(ids, 4) && al(wts, 4) &&
+                 al(qx, 16) && al(dx, 4) && al(sx, 4) && al(y, 4) && al(dev_status, 4),
+             ZQ_EALIGN);
+  const int dc = check_current_device();
+  if (dc != ZQ_OK) return dc;
+  zq::DmmvArgs a{};
+  a.w = static_cast<const uint8_t *>(bank);
+  a.qx = qx;
+  a.dx = dx;
+  a.sx = wtype == ZQ_Q6_K ? nullptr : sx;
+  a.y = y;
+  a.ids = ids;
+  a.wts = wts;
+  a.status = dev_status;
+  a.rows = rows;
+  a.expert_stride = expert_stride_bytes;
+  a.x_stride = x_stride;
+  a.nb = static_cast<int32_t>(k / 32);
+  a.n_experts = static_cast<int32_t>(n_experts);
+  a.n_sel = n_sel;
+  a.flags = flags;
+  a.id_base = id_base;
+  return zq::launch_dmmv_k(wtype, mode == ZQ_MOE_GATHER ? zq::MODE_GATHER : zq::MODE_WEIGHTED, a,
+                           stream);
 }
 
 }  // namespace
@@ -376,6 +422,9 @@ int zq_dmmv_moe(int wtype, const void *bank, int64_t n_experts, int64_t expert_s
                 int64_t rows, int64_t k, const int32_t *ids, const float *wts, int32_t n_sel,
                 const int8_t *qx, const float *dx, const int32_t *sx, int64_t x_stride, int mode,
                 float *y, uint32_t flags, int32_t *dev_status, void *stream) {
+  if (wtype == ZQ_Q4_K || wtype == ZQ_Q5_K || wtype == ZQ_Q6_K)
+    return dmmv_moe_k(wtype, bank, n_experts, expert_stride_bytes, rows, k, ids, wts, n_sel, qx,
+                      dx, sx, x_stride, mode, y, flags, dev_status, 0, S(stream));
   const int64_t bb = block_bytes(wtype);
   ZQ_REQUIRE(bb > 0, ZQ_EINVAL);
   ZQ_REQUIRE(mode == ZQ_MOE_GATHER || mode == ZQ_MOE_WEIGHTED_SUM, ZQ_EINVAL);
@@ -742,6 +791,143 @@ int zq_gemm_isums(int wtype, const void *w, int64_t n, int64_t k, const int8_t *
   // bytes as a readable stand-in (k >= 32 bytes per token >= k/32 floats).
   return zq::launch_gemm(wtype, w, n, k, qx, reinterpret_cast<const float *>(qx), m, nullptr, 0,
                          isums, m0, m1, n0, n1, S(stream));
+}
+
+namespace {
+
+// Launch one expert-indexed DMMV stage in whichever kernel serves wtype
+// (arguments already checked by the caller).
+int moe_stage(int wtype, int mode, const void *bank, int64_t stride, int64_t n_experts,
+              int32_t id_base, int64_t rows, int64_t k, const int32_t *ids, const float *wts,
+              int32_t n_sel, const int8_t *qx, const float *dx, const int32_t *sx,
+              int64_t x_stride, float *y, uint32_t flags, hipStream_t s) {
+  zq::DmmvArgs a{};
+  a.w = static_cast<const uint8_t *>(bank);
+  a.qx = qx;
+  a.dx = dx;
+  a.sx = (wtype == ZQ_Q4_0 || wtype == ZQ_Q4_K || wtype == ZQ_Q5_K) ? sx : nullptr;
+  a.y = y;
+  a.ids = ids;
+  a.wts = wts;
+  a.rows = rows;
+  a.expert_stride = stride;
+  a.x_stride = x_stride;
+  a.nb = static_cast<int32_t>(k / 32);
+  a.n_experts = static_cast<int32_t>(n_experts);
+  a.n_sel = n_sel;
+  a.flags = flags;
+  a.id_base = id_base;
+  if (wtype == ZQ_Q4_K || wtype == ZQ_Q5_K || wtype == ZQ_Q6_K) return zq::launch_dmmv_k(wtype, mode, a, s);
+  // the same dispatch as zq_dmmv_moe: the weighted sum over Q4_0 / Q8_0
+  // experts takes the dedicated down kernel when it fits
+  if (mode == zq::MODE_WEIGHTED && x_stride % 32 == 0 && zq::moe_down_fits(n_sel, k)) {
+    zq::MoeDownArgs b{};
+    b.bank = static_cast<const uint8_t *>(bank);
+    b.expert_stride = stride;
+    b.n_experts = static_cast<int32_t>(n_experts);
+    b.ids = ids;
+    b.wts = wts;
+    b.n_sel = n_sel;
+    b.qx = qx;
+    b.dx = dx;
+    b.sx = wtype == ZQ_Q4_0 ? sx : nullptr;
+    b.x_stride = x_stride;
+    b.k = static_cast<int32_t>(k);
+    b.rows = rows;
+    b.y = y;
+    b.flags = flags;
+    b.id_base = id_base;
+    return zq::launch_moe_down(wtype, b, s);
+  }
+  return zq::launch_dmmv(wtype, mode, a, s);
+}
+
+bool is_k(int wtype) { return wtype == ZQ_Q4_K || wtype == ZQ_Q5_K || wtype == ZQ_Q6_K; }
+
+// Bytes of one rows x k matrix in wtype, or -1 for an unknown type.
+int64_t matrix_bytes(int wtype, int64_t rows, int64_t k) {
+  if (wtype == ZQ_Q4_0 || wtype == ZQ_Q8_0) return rows * (k / 32) * block_bytes(wtype);
+  if (!is_k(wtype)) return -1;
+  const int64_t sbb = wtype == ZQ_Q4_K ? 144 : (wtype == ZQ_Q5_K ? 176 : 210);
+  return rows * (k / 256) * sbb;
+}
+
+}  // namespace
+
+int zq_moe_ffn_mixed(int gu_wtype, const void *gu_bank, int64_t gu_stride_bytes, int down_wtype,
+                     const void *down_bank, int64_t down_stride_bytes, int sh_wtype,
+                     const void *sh_gu, const void *sh_down, int64_t d_model, int64_t d_ff,
+                     const float *logits, int32_t n_routed, int32_t top_k,
+                     const float *shared_gate, const float *x, int32_t *ids, float *wts,
+                     void *workspace, size_t workspace_bytes, float *y, uint32_t flags,
+                     void *stream) {
+  const bool shared = shared_gate != nullptr;
+  ZQ_REQUIRE(matrix_bytes(gu_wtype, 1, 256) > 0 && matrix_bytes(down_wtype, 1, 256) > 0 &&
+                 (!shared || matrix_bytes(sh_wtype, 1, 256) > 0),
+             ZQ_EINVAL);
+  ZQ_REQUIRE(gu_bank && down_bank && logits && x && ids && wts && workspace && y, ZQ_ENULL);
+  ZQ_REQUIRE(!shared || (sh_gu && sh_down), ZQ_ENULL);
+  ZQ_REQUIRE(k_ok(d_model) && k_ok(d_ff) && d_model <= (int64_t(1) << 24) &&
+                 d_ff <= (int64_t(1) << 24) && top_k >= 1 && top_k <= 64 && n_routed >= top_k &&
+                 n_routed <= 1024,
+             ZQ_EINVAL);
+  // K-quant matrices take whole 256-element super-blocks along k
+  ZQ_REQUIRE(!is_k(gu_wtype) || d_model % 256 == 0, ZQ_EINVAL);
+  ZQ_REQUIRE(!is_k(down_wtype) || d_ff % 256 == 0, ZQ_EINVAL);
+  ZQ_REQUIRE(!shared || !is_k(sh_wtype) || (d_model % 256 == 0 && d_ff % 256 == 0), ZQ_EINVAL);
+  ZQ_REQUIRE(gu_stride_bytes >= matrix_bytes(gu_wtype, 2 * d_ff, d_model) &&
+                 down_stride_bytes >= matrix_bytes(down_wtype, d_model, d_ff),
+             ZQ_EINVAL);
+  ZQ_REQUIRE((flags & ~uint32_t(ZQ_ACCUMULATE)) == 0, ZQ_EINVAL);
+  const int32_t n_sel = top_k + (shared ? 1 : 0);
+  ZQ_REQUIRE(workspace_bytes >= zq_moe_ffn_workspace_bytes(d_model, d_ff, n_sel), ZQ_EINVAL);
+  const auto bank_al = [](int wt, const void *p, int64_t stride) {
+    return is_k(wt) ? (al(p, 16) && stride % 16 == 0) : (al(p, 4) && stride % 2 == 0);
+  };
+  ZQ_REQUIRE(bank_al(gu_wtype, gu_bank, gu_stride_bytes) &&
+                 bank_al(down_wtype, down_bank, down_stride_bytes) &&
+                 (!shared || (bank_al(sh_wtype, sh_gu, 0) && bank_al(sh_wtype, sh_down, 0))) &&
+                 al(logits, 4) && al(shared_gate, 4) && al(x, 16) && al(ids, 4) && al(wts, 4) &&
+                 al(workspace, 256) && al(y, 4),
+             ZQ_EALIGN);
+  const int dc = check_current_device();
+  if (dc != ZQ_OK) return dc;
+  hipStream_t s = S(stream);
+  const MoeWorkspace L = moe_layout(d_model, d_ff, n_sel);
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
+  int8_t *qx = reinterpret_cast<int8_t *>(ws + L.qx);
+  float *dx = reinterpret_cast<float *>(ws + L.dx);
+  int32_t *sx = reinterpret_cast<int32_t *>(ws + L.sx);
+  float *gu = reinterpret_cast<float *>(ws + L.gu);
+  int8_t *qh = reinterpret_cast<int8_t *>(ws + L.qh);
+  float *dh = reinterpret_cast<float *>(ws + L.dh);
+  int32_t *sh = reinterpret_cast<int32_t *>(ws + L.sh);
+  int rc = zq::launch_moe_route(logits, n_routed, top_k, shared_gate, ids, wts, s);
+  if (rc != ZQ_OK) return rc;
+  rc = zq::launch_quantize_act(x, 1, d_model, d_model, qx, dx, sx, s);
+  if (rc != ZQ_OK) return rc;
+  // gate||up rows of every selected expert; the shared one (id n_routed) from
+  // its own matrix
+  rc = moe_stage(gu_wtype, zq::MODE_GATHER, gu_bank, gu_stride_bytes, n_routed, 0, 2 * d_ff,
+                 d_model, ids, nullptr, top_k, qx, dx, sx, 0, gu, 0, s);
+  if (rc != ZQ_OK) return rc;
+  if (shared) {
+    rc = moe_stage(sh_wtype, zq::MODE_GATHER, sh_gu, 0, 1, n_routed, 2 * d_ff, d_model,
+                   ids + top_k, nullptr, 1, qx, dx, sx, 0,
+                   gu + static_cast<int64_t>(top_k) * 2 * d_ff, 0, s);
+    if (rc != ZQ_OK) return rc;
+  }
+  rc = zq::launch_swiglu_quantize(gu, n_sel, d_ff, qh, dh, sh, nullptr, s);
+  if (rc != ZQ_OK) return rc;
+  // down rows: the weighted sum over the routed experts, then the shared one
+  // added onto it
+  rc = moe_stage(down_wtype, zq::MODE_WEIGHTED, down_bank, down_stride_bytes, n_routed, 0,
+                 d_model, d_ff, ids, wts, top_k, qh, dh, sh, d_ff, y, flags, s);
+  if (rc != ZQ_OK || !shared) return rc;
+  const int64_t h0 = static_cast<int64_t>(top_k) * d_ff;
+  return moe_stage(sh_wtype, zq::MODE_WEIGHTED, sh_down, 0, 1, n_routed, d_model, d_ff,
+                   ids + top_k, wts + top_k, 1, qh + h0, dh + h0 / 32, sh + h0 / 32, d_ff, y,
+                   ZQ_ACCUMULATE, s);
 }
 
 }  // extern "C"

@@ -29,6 +29,8 @@ struct DmmvArgs {
   int32_t n_experts;
   int32_t n_sel;
   uint32_t flags;
+  // last, so that the fields above keep their kernel-argument offsets
+  int32_t id_base;      // MoE: expert e = ids[s] - id_base (a bank holding experts id_base..)
 };
 
 // The multi-token DMMV: T <= 8 activations, token t at qx + t*k,
@@ -94,7 +96,7 @@ int launch_dmmv_f32x(int wtype, DmmvF32Args a, hipStream_t stream);
 // DMMV over K-quant super-blocks, wtype ZQ_Q4_K / ZQ_Q5_K / ZQ_Q6_K
 // (a.nb = k/32, k a multiple of 256); isums selects the per-32-block integer
 // sums instead of rows.
-int launch_dmmv_k(int wtype, DmmvArgs a, bool isums, hipStream_t stream);
+int launch_dmmv_k(int wtype, int mode, DmmvArgs a, hipStream_t stream);
 // Reduce nparts (value, index) partials to the argmax index.
 int launch_argmax_final(const void *part, int nparts, int32_t *out_idx, hipStream_t stream);
 
@@ -147,6 +149,8 @@ struct MoeDownArgs {
   float *y;
   uint32_t flags;
   int32_t *status;
+  // last, so that the fields above keep their kernel-argument offsets
+  int32_t id_base;      // expert e = ids[s] - id_base
 };
 
 int launch_moe_gate_up(int wtype, MoeGateUpArgs a, hipStream_t stream);

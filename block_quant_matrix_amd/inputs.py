@@ -136,6 +136,17 @@ WORKLOADS = {
 }
 
 
+def moe_banks_k(seed: int, n_experts: int, d_model: int, d_ff: int, gu_wtype: int,
+                down_wtype: int):
+    """As moe_banks for K-quant experts (gate||up and down may differ in
+    type, as in the pages' model: Q4_K gate/up, Q5_K down)."""
+    gu = gen_weights_k(gu_wtype, n_experts * 2 * d_ff, d_model, seed)
+    down = gen_weights_k(down_wtype, n_experts * d_model, d_ff, seed + 500)
+    gu_stride = 2 * d_ff * (d_model // 256) * K_BLOCK_BYTES[gu_wtype]
+    down_stride = d_model * (d_ff // 256) * K_BLOCK_BYTES[down_wtype]
+    return gu, gu_stride, down, down_stride
+
+
 def moe_banks(seed: int, n_experts: int, d_model: int, d_ff: int, wtype: int = Q4_0):
     """Gate||up bank [E][2*d_ff rows][d_model] (rows 0..d_ff-1 gate, d_ff..2*d_ff-1 up)
     and down bank [E][d_model rows][d_ff], as contiguous byte streams."""

@@ -61,6 +61,8 @@ SIGNATURES = {
                                     _P, _P, _P, _P, _P, _P, _P]),
     "zq_moe_ffn_route": (_INT, [_INT, _P, _I64, _P, _I64, _I64, _I64, _I64, _P, _I32, _I32, _P, _P,
                                 _P, _P, _P, _SZ, _P, _U32, _P]),
+    "zq_moe_ffn_mixed": (_INT, [_INT, _P, _I64, _INT, _P, _I64, _INT, _P, _P, _I64, _I64, _P, _I32,
+                                _I32, _P, _P, _P, _P, _P, _SZ, _P, _U32, _P]),
     "zq_gemm_prefill": (_INT, [_INT, _P, _I64, _I64, _P, _P, _P, _I64, _P, _U32, _P]),
     "zq_gemm_isums": (_INT, [_INT, _P, _I64, _I64, _P, _P, _I64, _I64, _I64, _I64, _I64, _P, _P]),
 }
@@ -270,3 +272,12 @@ def zq_gemm_prefill(wtype, w, n, k, qx, dx, sx, m, y, flags=0, stream=None):
 def zq_gemm_isums(wtype, w, n, k, qx, sx, m, m0, m1, n0, n1, isums, stream=None):
     return _call("zq_gemm_isums", wtype, ptr(w), n, k, ptr(qx), ptr(sx), m, m0, m1, n0, n1,
                  ptr(isums), _stream(stream))
+
+
+def zq_moe_ffn_mixed(gu_wtype, gu_bank, gu_stride, down_wtype, down_bank, down_stride, sh_wtype,
+                     sh_gu, sh_down, d_model, d_ff, logits, n_routed, top_k, shared_gate, x, ids,
+                     wts, workspace, workspace_bytes, y, flags=0, stream=None):
+    return _call("zq_moe_ffn_mixed", gu_wtype, ptr(gu_bank), gu_stride, down_wtype, ptr(down_bank),
+                 down_stride, sh_wtype, ptr(sh_gu), ptr(sh_down), d_model, d_ff, ptr(logits),
+                 n_routed, top_k, ptr(shared_gate), ptr(x), ptr(ids), ptr(wts), ptr(workspace),
+                 workspace_bytes, ptr(y), flags, _stream(stream))

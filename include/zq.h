@@ -220,8 +220,10 @@ int zq_moe_route(const float *logits, int32_t n_routed, int32_t top_k,
  * moe_weighted_acc, "CUDA backend for ZINC", section 5; the selected experts
  * come from a GPU-resident work list, "RTX 5090: Batched Prefill & CUDA
  * Graphs in ZINC", section "Prefill -- a correction, and a better GEMM").
- * bank: n_experts matrices of rows x k, expert e at bank + e*expert_stride_bytes
- * (stride even).  ids [n_sel] int32, wts [n_sel] fp32 (device).  Activation
+ * wtype: ZQ_Q4_0 / ZQ_Q8_0 (stride even), or ZQ_Q4_K / ZQ_Q5_K / ZQ_Q6_K (k a
+ * multiple of 256, bank 16-byte aligned, stride a multiple of 16; the pages'
+ * experts are Q4_K / Q5_K, "CUDA backend for ZINC", section 5).
+ * bank: n_experts matrices of rows x k, expert e at bank + e*expert_stride_bytes.  ids [n_sel] int32, wts [n_sel] fp32 (device).  Activation
  * of slot s: qx + s*x_stride, dx/sx + s*(x_stride/32) (x_stride = 0 broadcasts
  * one activation; otherwise a multiple of 32).
  *   ZQ_MOE_GATHER:       y[s][r]   = (W[ids[s]] . x_s)[r]        y [n_sel][rows]
@@ -312,6 +314,31 @@ int zq_moe_ffn_route(int wtype, const void *gu_bank, int64_t gu_stride_bytes,
                      int32_t top_k, const float *shared_gate, const float *x, int32_t *ids,
                      float *wts, void *workspace, size_t workspace_bytes, float *y,
                      uint32_t flags, void *stream);
+
+/* One token through routed experts and a shared expert stored in different
+ * formats, as the pages' model keeps them: routed gate/up Q4_K, routed down
+ * Q5_K, shared expert Q8_0 ("CUDA backend for ZINC", section 5, "The target
+ * model & milestone ordering": dmmv_q4k_moe gate/up, dmmv_q5k_moe down, the
+ * Q8_0 shared expert with sigmoid_scale_acc).  gu_wtype / down_wtype /
+ * sh_wtype: any of ZQ_Q4_0, ZQ_Q8_0, ZQ_Q4_K, ZQ_Q5_K, ZQ_Q6_K (K-quant
+ * matrices need d_model resp. d_ff a multiple of 256; banks and matrices
+ * 16-byte aligned for K-quants, 4 otherwise).  gu_bank: n_routed experts of
+ * [2*d_ff][d_model] (rows 0..d_ff-1 gate) at gu_stride_bytes; down_bank:
+ * n_routed experts of [d_model][d_ff]; sh_gu / sh_down: the shared expert's
+ * two matrices (used when shared_gate is non-NULL).  The router is
+ * zq_moe_route's (ids / wts receive top_k (+1) entries, the shared one with
+ * id n_routed); then, one launch each: quantize x, gather the routed
+ * gate||up rows, the shared gate||up rows, SwiGLU + re-quantize, the routed
+ * weighted down sum, the shared down term added on.  y [d_model] (+)= the
+ * weighted sum; workspace >= zq_moe_ffn_workspace_bytes(d_model, d_ff,
+ * top_k (+1)) bytes, 256-byte aligned.  y may be x itself. */
+int zq_moe_ffn_mixed(int gu_wtype, const void *gu_bank, int64_t gu_stride_bytes, int down_wtype,
+                     const void *down_bank, int64_t down_stride_bytes, int sh_wtype,
+                     const void *sh_gu, const void *sh_down, int64_t d_model, int64_t d_ff,
+                     const float *logits, int32_t n_routed, int32_t top_k,
+                     const float *shared_gate, const float *x, int32_t *ids, float *wts,
+                     void *workspace, size_t workspace_bytes, float *y, uint32_t flags,
+                     void *stream);
 
 /* Batched prefill GEMM ("one register-tiled GEMM over all prompt tokens at
  * once", "RTX 5090: Batched Prefill & CUDA Graphs in ZINC", opening answer

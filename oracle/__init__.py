@@ -319,6 +319,46 @@ def moe_down_weighted(wtype, down_bank, down_stride, d_model, d_ff, ids, wts, qh
     return y, S
 
 
+def expert_rows_any(wtype, bank: np.ndarray, expert_stride: int, rows: int, k: int, eid: int,
+                    qx, dx, rows_eval=None):
+    """Reference rows of expert ``eid`` of a bank in any weight type (Q4_0 /
+    Q8_0 blocks or K-quant super-blocks)."""
+    if wtype in K_BLOCK_BYTES:
+        nbytes = rows * (k // 256) * K_BLOCK_BYTES[wtype]
+        w = bank[eid * expert_stride: eid * expert_stride + nbytes]
+        return k_dmmv(wtype, w, rows, k, qx, dx, rows_eval=rows_eval)
+    return moe_expert_rows(wtype, bank, expert_stride, rows, k, eid, qx, dx, rows_eval=rows_eval)
+
+
+def moe_ffn_mixed(gu_wtype, gu_bank, gu_stride, down_wtype, down_bank, down_stride, sh_wtype,
+                  sh_gu, sh_down, n_routed, d_model, d_ff, ids, wts, x):
+    """Unchained end-to-end reference of one token through routed experts of
+    one format pair and a shared expert (id n_routed) of its own format, in
+    its own matrices: quantize x, gate||up rows per selected expert, swiglu,
+    quantize h, weighted sum of the down rows.  Returns (y, S)."""
+    qx, dx, _ = quantize_act(x)
+    gus = []
+    for e in ids:
+        if int(e) == n_routed:
+            ye, _ = expert_rows_any(sh_wtype, sh_gu, 0, 2 * d_ff, d_model, 0, qx, dx)
+        else:
+            ye, _ = expert_rows_any(gu_wtype, gu_bank, gu_stride, 2 * d_ff, d_model, int(e), qx, dx)
+        gus.append(ye)
+    h = swiglu(np.stack(gus).astype(np.float32), d_ff)
+    qh, dh, _ = quantize_act(h)
+    y = np.zeros(d_model, np.float64)
+    S = np.zeros(d_model, np.float64)
+    for s, e in enumerate(ids):
+        if int(e) == n_routed:
+            ye, Se = expert_rows_any(sh_wtype, sh_down, 0, d_model, d_ff, 0, qh[s], dh[s])
+        else:
+            ye, Se = expert_rows_any(down_wtype, down_bank, down_stride, d_model, d_ff, int(e),
+                                     qh[s], dh[s])
+        y += float(wts[s]) * ye
+        S += abs(float(wts[s])) * Se
+    return y, S
+
+
 def moe_ffn(wtype, gu_bank, gu_stride, down_bank, down_stride, d_model, d_ff, ids, wts, x):
     """Unchained end-to-end reference of one token through the selected experts."""
     qx, dx, _ = quantize_act(x)

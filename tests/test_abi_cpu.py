@@ -206,6 +206,40 @@ def test_rms_norm_argument_errors():
                                          None) == zq.ZQ_EINVAL
 
 
+def test_moe_mixed_argument_errors():
+    L = zq.lib()
+    ws = L.zq_moe_ffn_workspace_bytes(512, 256, 5)
+
+    def rc(gwt=12, gb=A, gs=2 * 256 * 2 * 144, dwt=13, db=B, ds=512 * 1 * 176, swt=8, sg=C,
+           sd=D, dm=512, dff=256, logits=A + 0x100000, nr=16, k=4, g=B + 0x100000,
+           x=C + 0x100000, wsb=ws, flags=0, wsp=D + 0x100000):
+        return L.zq_moe_ffn_mixed(gwt, gb, gs, dwt, db, ds, swt, sg, sd, dm, dff, logits, nr, k, g,
+                                  x, A + 0x200000, B + 0x200000, wsp, wsb, C + 0x200000, flags,
+                                  None)
+
+    assert rc(gwt=7) == zq.ZQ_EINVAL
+    assert rc(swt=99) == zq.ZQ_EINVAL
+    assert rc(dff=288) == zq.ZQ_EINVAL          # Q5_K down needs d_ff % 256 == 0
+    assert rc(dm=288) == zq.ZQ_EINVAL           # Q4_K gate/up needs d_model % 256 == 0
+    assert rc(gs=1000) == zq.ZQ_EINVAL          # stride shorter than an expert
+    assert rc(k=0) == zq.ZQ_EINVAL
+    assert rc(nr=3) == zq.ZQ_EINVAL             # fewer experts than top_k
+    assert rc(wsb=ws - 1) == zq.ZQ_EINVAL
+    assert rc(flags=2) == zq.ZQ_EINVAL
+    assert rc(sg=None) == zq.ZQ_ENULL           # shared gate given, shared matrix missing
+    assert rc(gb=A + 4) == zq.ZQ_EALIGN         # K-quant banks are 16-byte aligned
+    assert rc(wsp=D + 0x100004) == zq.ZQ_EALIGN
+    # no shared expert: its matrices may be NULL and its type is not checked
+    assert rc(g=None, sg=None, sd=None, swt=99) == zq.ZQ_EDEVICE
+    # the K-quant expert-indexed DMMV
+    assert L.zq_dmmv_moe(12, A, 4, 144 * 64, 64, 288, B, None, 2, C, D, None, 0, 0, D, 0, None,
+                         None) == zq.ZQ_EINVAL    # k not a multiple of 256
+    assert L.zq_dmmv_moe(12, A + 8, 4, 144 * 64, 64, 256, B, None, 2, C, D, None, 0, 0, D, 0,
+                         None, None) == zq.ZQ_EALIGN
+    assert L.zq_dmmv_moe(12, A, 4, 144 * 63, 64, 256, B, None, 2, C, D, None, 0, 0, D, 0, None,
+                         None) == zq.ZQ_EINVAL    # stride shorter than an expert
+
+
 def test_lmhead_argument_errors():
     L = zq.lib()
     ws = L.zq_dmmv_f32_argmax_workspace_bytes()

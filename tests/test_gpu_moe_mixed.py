@@ -1,0 +1,174 @@
+"""GPU parity of the expert-indexed K-quant DMMV and of the MoE block with
+experts in the pages' own formats (routed gate/up Q4_K, down Q5_K, shared
+expert Q8_0), against the oracle."""
+import numpy as np
+import pytest
+
+import oracle
+from block_quant_matrix_amd import inputs
+from gpuhelp import check_rows, dev, host, nan_f32, quantize_gpu, sentinel_i32, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+Q4_0, Q8_0, Q4_K, Q5_K, Q6_K = 4, 8, 12, 13, 14
+NAME = {Q4_0: "q4_0", Q8_0: "q8_0", Q4_K: "q4_k", Q5_K: "q5_k", Q6_K: "q6_k"}
+
+
+@pytest.fixture(scope="module")
+def zq():
+    torch_cuda()
+    from block_quant_matrix_amd import zq as _zq
+    assert _zq.zq_device_check(0) == 0
+    return _zq
+
+
+def gen_bank(wt, n_experts, rows, k, seed):
+    if wt in (Q4_K, Q5_K, Q6_K):
+        w = inputs.gen_weights_k(wt, n_experts * rows, k, seed)
+        return w, rows * (k // 256) * inputs.K_BLOCK_BYTES[wt]
+    w = inputs.gen_weights(wt, n_experts * rows, k, seed)
+    return w, rows * (k // 32) * inputs.BLOCK_BYTES[wt]
+
+
+@pytest.mark.parametrize("wt", [Q4_K, Q5_K, Q6_K], ids=lambda t: NAME[t])
+def test_dmmv_moe_kquant_gather_and_weighted(zq, wt):
+    E, rows, k = 6, 96, 512
+    bank, stride = gen_bank(wt, E, rows, k, 810 + wt)
+    bank_d = dev(bank)
+    ids_h = np.array([3, 0, 5, 3], np.int32)
+    n = ids_h.size
+    wts_h = np.array([0.5, -1.25, 0.125, 2.0], np.float32)
+    # gather over one broadcast activation
+    x = inputs.gen_activation(1, k, 811)
+    qx, dx, sx = quantize_gpu(zq, x)
+    rq, rd, _ = oracle.quantize_act(x)
+    y = nan_f32(n, rows)
+    zq.zq_dmmv_moe(wt, bank_d, E, stride, rows, k, dev(ids_h), None, n, qx, dx, sx, 0,
+                   zq.ZQ_MOE_GATHER, y)
+    yh = host(y)
+    for s, e in enumerate(ids_h):
+        y_ref, S = oracle.expert_rows_any(wt, bank, stride, rows, k, int(e), rq, rd)
+        check_rows(yh[s], y_ref, S, "%s gather slot %d" % (NAME[wt], s))
+    # weighted sum over per-slot activations
+    xs = inputs.gen_activation(n, k, 812)
+    qxs, dxs, sxs = quantize_gpu(zq, xs)
+    rqs, rds, _ = oracle.quantize_act(xs)
+    y2 = nan_f32(rows)
+    zq.zq_dmmv_moe(wt, bank_d, E, stride, rows, k, dev(ids_h), dev(wts_h), n, qxs, dxs, sxs, k,
+                   zq.ZQ_MOE_WEIGHTED_SUM, y2)
+    y_ref = np.zeros(rows)
+    S = np.zeros(rows)
+    for s, e in enumerate(ids_h):
+        ye, Se = oracle.expert_rows_any(wt, bank, stride, rows, k, int(e), rqs[s], rds[s])
+        y_ref += float(wts_h[s]) * ye
+        S += abs(float(wts_h[s])) * Se
+    check_rows(host(y2), y_ref, S, "%s weighted" % NAME[wt])
+    # an id out of range is skipped and reported
+    status = sentinel_i32(1, value=0)
+    bad = dev(np.array([3, 9, 0], np.int32))
+    y3 = nan_f32(3, rows)
+    zq.zq_dmmv_moe(wt, bank_d, E, stride, rows, k, bad, None, 3, qx, dx, sx, 0, zq.ZQ_MOE_GATHER,
+                   y3, 0, status)
+    y3h = host(y3)
+    assert int(host(status)[0]) == zq.ZQ_ERANGE
+    assert np.isnan(y3h[1]).all() and not np.isnan(y3h[0]).any() and not np.isnan(y3h[2]).any()
+
+
+def run_mixed(zq, fmt, banks, d_model, d_ff, n_routed, top_k, logits, g, x, y=None, flags=0):
+    torch = torch_cuda()
+    (gwt, gu_d, gs), (dwt, dn_d, ds), (swt, sgu_d, sdn_d) = banks
+    n_sel = top_k + (1 if g is not None else 0)
+    ws_bytes = zq.zq_moe_ffn_workspace_bytes(d_model, d_ff, n_sel)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    ids, wts = sentinel_i32(n_sel), nan_f32(n_sel)
+    y = nan_f32(d_model) if y is None else y
+    gd = None if g is None else dev(np.array([g], np.float32))
+    zq.zq_moe_ffn_mixed(gwt, gu_d, gs, dwt, dn_d, ds, swt, sgu_d, sdn_d, d_model, d_ff, dev(logits),
+                        n_routed, top_k, gd, dev(x), ids, wts, ws, ws_bytes, y, flags)
+    return host(ids), host(wts), y
+
+
+def make_banks(fmt, n_routed, d_model, d_ff, seed):
+    gwt, dwt, swt = fmt
+    gu, gs = gen_bank(gwt, n_routed, 2 * d_ff, d_model, seed)
+    dn, ds = gen_bank(dwt, n_routed, d_model, d_ff, seed + 1)
+    sgu, _ = gen_bank(swt, 1, 2 * d_ff, d_model, seed + 2)
+    sdn, _ = gen_bank(swt, 1, d_model, d_ff, seed + 3)
+    host_b = ((gwt, gu, gs), (dwt, dn, ds), (swt, sgu, sdn))
+    dev_b = ((gwt, dev(gu), gs), (dwt, dev(dn), ds), (swt, dev(sgu), dev(sdn)))
+    return host_b, dev_b
+
+
+def oracle_mixed(host_b, n_routed, d_model, d_ff, ids, wts, x):
+    (gwt, gu, gs), (dwt, dn, ds), (swt, sgu, sdn) = host_b
+    return oracle.moe_ffn_mixed(gwt, gu, gs, dwt, dn, ds, swt, sgu, sdn, n_routed, d_model, d_ff,
+                                ids, wts, x)
+
+
+PAGES = (Q4_K, Q5_K, Q8_0)
+
+
+@pytest.mark.parametrize("fmt", [PAGES, (Q4_0, Q4_0, Q8_0), (Q6_K, Q4_K, Q4_0)],
+                         ids=lambda f: "-".join(NAME[t] for t in f))
+def test_moe_ffn_mixed_small(zq, fmt):
+    d_model, d_ff, n_routed, top_k = 512, 256, 16, 4
+    host_b, dev_b = make_banks(fmt, n_routed, d_model, d_ff, 830 + sum(fmt))
+    logits, g = inputs.gen_router(n_routed, 831)
+    x = inputs.gen_activation(1, d_model, 832)
+    ids, wts, y = run_mixed(zq, fmt, dev_b, d_model, d_ff, n_routed, top_k, logits, g, x)
+    rids, _ = oracle.moe_route(logits, top_k, g)
+    assert np.array_equal(ids, rids)
+    y_ref, S = oracle_mixed(host_b, n_routed, d_model, d_ff, ids, wts, x)
+    check_rows(host(y), y_ref, S, "mixed moe %s" % (fmt,), tol=1e-3)
+    # accumulate onto y
+    prev = host(y).copy()
+    run_mixed(zq, fmt, dev_b, d_model, d_ff, n_routed, top_k, logits, g, x, y=y, flags=1)
+    assert np.allclose(host(y), 2 * prev, rtol=1e-6, atol=0)
+
+
+def test_moe_ffn_mixed_equals_its_stages(zq):
+    """The composite gives the bits of the same stages run through the
+    public entry points one by one (router, quantize, routed and shared
+    gate||up gathers, SwiGLU + re-quantize, routed and shared down)."""
+    torch = torch_cuda()
+    d_model, d_ff, n_routed, top_k = 512, 256, 16, 4
+    host_b, dev_b = make_banks(PAGES, n_routed, d_model, d_ff, 840)
+    (gwt, gu_d, gs), (dwt, dn_d, ds), (swt, sgu_d, sdn_d) = dev_b
+    logits, g = inputs.gen_router(n_routed, 841)
+    x = inputs.gen_activation(1, d_model, 842)
+    ids, wts, y = run_mixed(zq, PAGES, dev_b, d_model, d_ff, n_routed, top_k, logits, g, x)
+    n_sel = top_k + 1
+    ids_d, wts_d = sentinel_i32(n_sel), nan_f32(n_sel)
+    zq.zq_moe_route(dev(logits), n_routed, top_k, dev(np.array([g], np.float32)), ids_d, wts_d)
+    qx, dx, sx = quantize_gpu(zq, x)
+    gu = nan_f32(n_sel, 2 * d_ff)
+    zq.zq_dmmv_moe(gwt, gu_d, n_routed, gs, 2 * d_ff, d_model, ids_d, None, top_k, qx, dx, sx, 0,
+                   zq.ZQ_MOE_GATHER, gu)
+    zero = dev(np.zeros(1, np.int32))
+    sgu_bytes, sdn_bytes = sgu_d.numel(), sdn_d.numel()   # one expert: stride = its size
+    zq.zq_dmmv_moe(swt, sgu_d, 1, sgu_bytes, 2 * d_ff, d_model, zero, None, 1, qx, dx, sx, 0,
+                   zq.ZQ_MOE_GATHER, gu[top_k:])
+    qh = torch.empty((n_sel, d_ff), dtype=torch.int8, device="cuda")
+    dh, sh = nan_f32(n_sel, d_ff // 32), sentinel_i32(n_sel, d_ff // 32)
+    zq.zq_swiglu_quantize(gu, n_sel, d_ff, qh, dh, sh)
+    y2 = nan_f32(d_model)
+    zq.zq_dmmv_moe(dwt, dn_d, n_routed, ds, d_model, d_ff, ids_d, wts_d, top_k, qh, dh, sh, d_ff,
+                   zq.ZQ_MOE_WEIGHTED_SUM, y2)
+    zq.zq_dmmv_moe(swt, sdn_d, 1, sdn_bytes, d_model, d_ff, zero, wts_d[top_k:], 1, qh[top_k:],
+                   dh[top_k:], sh[top_k:], d_ff, zq.ZQ_MOE_WEIGHTED_SUM, y2, zq.ZQ_ACCUMULATE)
+    assert np.array_equal(host(ids_d), ids)
+    assert np.array_equal(host(y2).view(np.uint32), host(y).view(np.uint32))
+
+
+def test_moe_ffn_mixed_pages_shape(zq):
+    """The pages' expert shapes: 128 routed experts of 2048 -> 512 -> 2048 in
+    Q4_K / Q5_K, top-8, a Q8_0 shared expert."""
+    d_model, d_ff, n_routed, top_k = 2048, 512, 128, 8
+    host_b, dev_b = make_banks(PAGES, n_routed, d_model, d_ff, 850)
+    for s in range(2):
+        logits, g = inputs.gen_router(n_routed, 851 + s)
+        x = inputs.gen_activation(1, d_model, 853 + s)
+        ids, wts, y = run_mixed(zq, PAGES, dev_b, d_model, d_ff, n_routed, top_k, logits, g, x)
+        assert np.array_equal(ids, oracle.moe_route(logits, top_k, g)[0])
+        y_ref, S = oracle_mixed(host_b, n_routed, d_model, d_ff, ids, wts, x)
+        check_rows(host(y), y_ref, S, "pages-format moe", tol=1e-3)
