@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7, 8, 9, 10])
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -340,6 +340,113 @@ class DmmvTokWorkload(Workload):
         return dict(value=self.step_bytes / per / 1e9, unit="GB/s", cores=1, kind="oracle",
                     sample="%d full steps (quantize %d tokens + %d-row DMMV per token) on one "
                            "host thread, %.1f s" % (n, self.T, self.rows, el))
+
+
+class MoeMixedWorkload(Workload):
+    """Router + one token through 8 routed experts stored as the pages' model
+    stores them (gate/up Q4_K, down Q5_K) and a Q8_0 shared expert, through
+    zq_moe_ffn_mixed (seven launches)."""
+    dominant_name = "dmmv_k_kernel (Q4_K gather)"
+
+    def __init__(self, wl):
+        from block_quant_matrix_amd import inputs
+        cfg = inputs.WORKLOADS[wl]
+        self.wl = wl
+        self.name = cfg["name"]
+        self.E, self.top_k, self.dm, self.dff = cfg["n_routed"], cfg["top_k"], cfg["d_model"], cfg["d_ff"]
+        self.gwt, self.dwt, self.swt = cfg["gu_wtype"], cfg["down_wtype"], cfg["sh_wtype"]
+        self.n_sel = self.top_k + 1
+        kb = inputs.K_BLOCK_BYTES
+        self.gu_m = 2 * self.dff * (self.dm // 256) * kb[self.gwt]
+        self.dn_m = self.dm * (self.dff // 256) * kb[self.dwt]
+        self.sgu_m = 2 * self.dff * (self.dm // 32) * inputs.BLOCK_BYTES[self.swt]
+        self.sdn_m = self.dm * (self.dff // 32) * inputs.BLOCK_BYTES[self.swt]
+        # weights a token reads: 8 routed experts' gate/up and down, the
+        # shared expert's two matrices; plus the fp32 activation, logits, y
+        self.step_bytes = (self.top_k * (self.gu_m + self.dn_m) + self.sgu_m + self.sdn_m +
+                           4 * self.dm + 4 * self.E + 4 * self.dm)
+        # the routed gate/up gather: 8 experts' rows, the quantized x, gu out
+        nb = self.dm // 32
+        self.gather_bytes = self.top_k * self.gu_m + self.dm + 8 * nb + 4 * self.top_k * 2 * self.dff
+        self.steps, self.warmup = 500, 50     # seven launches per step
+
+    def setup(self, torch, zq, inputs):
+        self.torch, self.zq = torch, zq
+        self.ncopy = copies_for(self.E * (self.gu_m + self.dn_m))
+        self.banks = []
+        for c in range(self.ncopy):
+            gu, gs, dn, ds = inputs.moe_banks_k(inputs.seed_for(self.wl, c), self.E, self.dm,
+                                                self.dff, self.gwt, self.dwt)
+            self.banks.append((torch.from_numpy(gu).to("cuda"), torch.from_numpy(dn).to("cuda")))
+            if c == 0:
+                self.host_bank = (gu, gs, dn, ds)
+            del gu, dn
+        self.gs, self.ds = gs, ds
+        sgu = inputs.gen_weights(self.swt, 2 * self.dff, self.dm, inputs.seed_for(self.wl, 40))
+        sdn = inputs.gen_weights(self.swt, self.dm, self.dff, inputs.seed_for(self.wl, 41))
+        self.host_shared = (sgu, sdn)
+        self.sgu, self.sdn = torch.from_numpy(sgu).to("cuda"), torch.from_numpy(sdn).to("cuda")
+        lg = [inputs.gen_router(self.E, inputs.seed_for(self.wl, 100 + i)) for i in range(64)]
+        self.logits = torch.from_numpy(np.stack([l for l, _ in lg])).to("cuda")
+        self.gates = torch.from_numpy(np.array([g for _, g in lg], np.float32)).to("cuda")
+        self.host_router = lg[0]
+        self.x_host = inputs.gen_activation(1, self.dm, inputs.seed_for(self.wl) + 7)
+        self.x = torch.from_numpy(self.x_host).to("cuda")
+        self.ids = torch.empty(self.n_sel, dtype=torch.int32, device="cuda")
+        self.wts = torch.empty(self.n_sel, dtype=torch.float32, device="cuda")
+        self.ws_bytes = zq.zq_moe_ffn_workspace_bytes(self.dm, self.dff, self.n_sel)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
+        self.y = torch.empty(self.dm, dtype=torch.float32, device="cuda")
+        self.qx = torch.empty(self.dm, dtype=torch.int8, device="cuda")
+        self.dx = torch.empty(self.dm // 32, dtype=torch.float32, device="cuda")
+        self.sx = torch.empty(self.dm // 32, dtype=torch.int32, device="cuda")
+        self.gu_out = torch.empty((self.top_k, 2 * self.dff), dtype=torch.float32, device="cuda")
+
+    def step(self, i):
+        gu, dn = self.banks[i % self.ncopy]
+        j = i % self.logits.shape[0]
+        self.zq.zq_moe_ffn_mixed(self.gwt, gu, self.gs, self.dwt, dn, self.ds, self.swt, self.sgu,
+                                 self.sdn, self.dm, self.dff, self.logits[j], self.E, self.top_k,
+                                 self.gates[j:j + 1], self.x, self.ids, self.wts, self.ws,
+                                 self.ws_bytes, self.y)
+
+    def prepare_dominant(self):
+        self.zq.zq_moe_route(self.logits[0], self.E, self.top_k, self.gates[0:1], self.ids, self.wts)
+        self.zq.zq_quantize_act(self.x, 1, self.dm, self.dm, self.qx, self.dx, self.sx)
+
+    def dominant(self, i):
+        gu, _ = self.banks[i % self.ncopy]
+        self.zq.zq_dmmv_moe(self.gwt, gu, self.E, self.gs, 2 * self.dff, self.dm, self.ids, None,
+                            self.top_k, self.qx, self.dx, self.sx, 0, self.zq.ZQ_MOE_GATHER,
+                            self.gu_out)
+
+    def value(self, ms):
+        return self.step_bytes / (ms * 1e-3) / 1e9, "GB/s"
+
+    def achieved(self, ms):
+        return self.gather_bytes / (ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s", self.gather_bytes
+
+    def extra(self, ms):
+        return {"tokens_per_s": 1.0 / (ms * 1e-3)}
+
+    def cpu_baseline(self, seconds):
+        import oracle
+        gu, gs, dn, ds = self.host_bank
+        sgu, sdn = self.host_shared
+        logits, g = self.host_router
+        n, t0 = 0, time.perf_counter()
+        while True:
+            ids, wts = oracle.moe_route(logits, self.top_k, g)
+            oracle.moe_ffn_mixed(self.gwt, gu, gs, self.dwt, dn, ds, self.swt, sgu, sdn, self.E,
+                                 self.dm, self.dff, ids, wts, self.x_host)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+        per = el / n
+        return dict(value=self.step_bytes / per / 1e9, unit="GB/s", cores=1, kind="oracle",
+                    sample="%d full MoE tokens (route + 8 K-quant experts + Q8_0 shared) on one "
+                           "host thread, %.1f s" % (n, el))
 
 
 class DecodeChainWorkload(Workload):
@@ -683,6 +790,8 @@ def make_workload(wl):
         return DmmvTokWorkload(wl)
     if wl == 10:
         return DecodeChainWorkload(wl)
+    if wl == 11:
+        return MoeMixedWorkload(wl)
     return GemmWorkload()
 
 

@@ -133,6 +133,10 @@ WORKLOADS = {
     # and the LM head, replayed as one graph; 4 distinct expert banks
     10: dict(name="decode_chain_40l_moe128e_top8_lmhead248320", layers=40, moe_banks=4,
              n_routed=128, top_k=8, d_model=2048, d_ff=512, vocab=248320),
+    # the MoE block in the pages' model formats: routed gate/up Q4_K, down
+    # Q5_K, shared expert Q8_0
+    11: dict(name="moe_128e_top8_q4k_q5k_shared_q8_0_2048x512", n_routed=128, top_k=8,
+             d_model=2048, d_ff=512, gu_wtype=Q4_K, down_wtype=Q5_K, sh_wtype=Q8_0),
 }
 
 
