@@ -345,8 +345,10 @@ class DmmvTokWorkload(Workload):
 class MoeMixedWorkload(Workload):
     """Router + one token through 8 routed experts stored as the pages' model
     stores them (gate/up Q4_K, down Q5_K) and a Q8_0 shared expert, through
-    zq_moe_ffn_mixed (seven launches)."""
-    dominant_name = "dmmv_k_kernel (Q4_K gather)"
+    zq_moe_ffn_mixed (four launches: the routed Q4_K gate/up pass with the
+    router folded in, the shared Q8_0 gate/up pass, the routed Q5_K weighted
+    down sum, the shared down term)."""
+    dominant_name = "moe_gate_up_k_kernel (Q4_K, router folded in)"
 
     def __init__(self, wl):
         from block_quant_matrix_amd import inputs
@@ -365,10 +367,13 @@ class MoeMixedWorkload(Workload):
         # shared expert's two matrices; plus the fp32 activation, logits, y
         self.step_bytes = (self.top_k * (self.gu_m + self.dn_m) + self.sgu_m + self.sdn_m +
                            4 * self.dm + 4 * self.E + 4 * self.dm)
-        # the routed gate/up gather: 8 experts' rows, the quantized x, gu out
-        nb = self.dm // 32
-        self.gather_bytes = self.top_k * self.gu_m + self.dm + 8 * nb + 4 * self.top_k * 2 * self.dff
-        self.steps, self.warmup = 500, 50     # seven launches per step
+        # the routed gate/up pass: 8 experts' gate||up rows, the fp32 x and
+        # the logits in; the quantized h (codes, scales, sums) and the
+        # expert list out
+        self.gather_bytes = (self.top_k * self.gu_m + 4 * self.dm + 4 * self.E +
+                             self.top_k * self.dff + 8 * self.top_k * (self.dff // 32) +
+                             8 * self.top_k)
+        self.steps, self.warmup = 1000, 100     # four launches per step
 
     def setup(self, torch, zq, inputs):
         self.torch, self.zq = torch, zq
@@ -397,10 +402,9 @@ class MoeMixedWorkload(Workload):
         self.ws_bytes = zq.zq_moe_ffn_workspace_bytes(self.dm, self.dff, self.n_sel)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
         self.y = torch.empty(self.dm, dtype=torch.float32, device="cuda")
-        self.qx = torch.empty(self.dm, dtype=torch.int8, device="cuda")
-        self.dx = torch.empty(self.dm // 32, dtype=torch.float32, device="cuda")
-        self.sx = torch.empty(self.dm // 32, dtype=torch.int32, device="cuda")
-        self.gu_out = torch.empty((self.top_k, 2 * self.dff), dtype=torch.float32, device="cuda")
+        self.qh = torch.empty((self.top_k, self.dff), dtype=torch.int8, device="cuda")
+        self.dh = torch.empty((self.top_k, self.dff // 32), dtype=torch.float32, device="cuda")
+        self.sh = torch.empty((self.top_k, self.dff // 32), dtype=torch.int32, device="cuda")
 
     def step(self, i):
         gu, dn = self.banks[i % self.ncopy]
@@ -411,14 +415,16 @@ class MoeMixedWorkload(Workload):
                                  self.ws_bytes, self.y)
 
     def prepare_dominant(self):
-        self.zq.zq_moe_route(self.logits[0], self.E, self.top_k, self.gates[0:1], self.ids, self.wts)
-        self.zq.zq_quantize_act(self.x, 1, self.dm, self.dm, self.qx, self.dx, self.sx)
+        pass
 
     def dominant(self, i):
+        # the routed launch of the step, alone (the shared slot is the next
+        # launch's)
         gu, _ = self.banks[i % self.ncopy]
-        self.zq.zq_dmmv_moe(self.gwt, gu, self.E, self.gs, 2 * self.dff, self.dm, self.ids, None,
-                            self.top_k, self.qx, self.dx, self.sx, 0, self.zq.ZQ_MOE_GATHER,
-                            self.gu_out)
+        j = i % self.logits.shape[0]
+        self.zq.zq_moe_gate_up_route(self.gwt, gu, self.gs, self.E, self.dm, self.dff,
+                                     self.logits[j], self.E, self.top_k, None, self.x, self.ids,
+                                     self.wts, self.qh, self.dh, self.sh)
 
     def value(self, ms):
         return self.step_bytes / (ms * 1e-3) / 1e9, "GB/s"

@@ -18,10 +18,124 @@
 // one FMA per expert and lane.
 #include "zq_common.h"
 #include "zq_internal.h"
+#include "zq_kquant.h"
 
 namespace zq {
 
 // ------------------------------------------------------------- gate/up ----
+// Pieces shared by the block-format and K-quant gate/up kernels: one
+// workgroup of T threads per (selected expert, 32-wide block of the FFN
+// width), computing 32 gate rows and the 32 matching up rows.
+
+// Loads of the fp32 activation for this thread's first 32-element block (two
+// lanes per block, 16 elements each); issued before anything is waited on.
+__device__ __forceinline__ void gu_load_x(const MoeGateUpArgs &a, int tid, float (&xv)[16]) {
+  const int g = tid & 1;
+  const int qb = tid >> 1;
+  if (qb < a.nb) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float4 v = *reinterpret_cast<const float4 *>(a.x + qb * 32 + g * 16 + 4 * u);
+      xv[4 * u] = v.x; xv[4 * u + 1] = v.y; xv[4 * u + 2] = v.z; xv[4 * u + 3] = v.w;
+    }
+  }
+}
+
+// The expert of slot s: ranked from the logits by the workgroup itself
+// (ROUTED: slot s < top_k takes rank s, slot top_k the shared expert, id
+// n_routed) or read from ids, less id_base.  rsel / rselv (LDS, 64) keep the
+// ranked selection for the publication at the end.  Every thread calls it.
+template <bool ROUTED, int T>
+__device__ __forceinline__ int gu_expert(const MoeGateUpArgs &a, int tid, int s, int32_t *rsel,
+                                         float *rselv) {
+  if constexpr (ROUTED) {
+    __shared__ float rlv[1024];
+    for (int i = tid; i < a.n_routed; i += T) rlv[i] = route_key(a.logits[i]);
+    __syncthreads();
+    route_rank<8>(rlv, a.n_routed, a.top_k, rsel, rselv);
+    __syncthreads();
+    return s < a.top_k ? rsel[s] : a.n_routed;
+  } else {
+    return a.ids[s] - a.id_base;
+  }
+}
+
+// Quantize x into LDS (two lanes per block, the first block already in xv):
+// codes, scales and the block sums times SUMX.
+template <int T, int SUMX>
+__device__ __forceinline__ void gu_quantize_x(const MoeGateUpArgs &a, int tid, float (&xv)[16],
+                                              int8_t *lq, float *ld, int32_t *ls) {
+  const int g = tid & 1;
+  for (int qb = tid >> 1; qb < a.nb; qb += T / 2) {
+    if (qb != (tid >> 1)) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float4 v = *reinterpret_cast<const float4 *>(a.x + qb * 32 + g * 16 + 4 * u);
+        xv[4 * u] = v.x; xv[4 * u + 1] = v.y; xv[4 * u + 2] = v.z; xv[4 * u + 3] = v.w;
+      }
+    }
+    uint32_t pk[4];
+    float d;
+    int32_t sum;
+    quantize_block<2>(xv, pk, d, sum);
+    *reinterpret_cast<u32x4 *>(lq + qb * 32 + g * 16) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+    if (g == 0) {
+      ld[qb] = d;
+      ls[qb] = SUMX * sum;
+    }
+  }
+}
+
+// Gate row lr (0..31) or up row lr (32..63) of FFN block hb, as a matrix row.
+__device__ __forceinline__ int64_t gu_row(const MoeGateUpArgs &a, int hb, int lr) {
+  return (lr < 32) ? (32 * hb + lr) : (a.d_ff + 32 * hb + (lr - 32));
+}
+
+// Epilogue, after the 64 row results are in lrow: SwiGLU over the 32
+// outputs (fp64, one rounding) and their quantization (8 lanes, four
+// elements each), then the router's publication (ROUTED, one workgroup).
+template <bool ROUTED>
+__device__ __forceinline__ void gu_epilogue(const MoeGateUpArgs &a, int tid, int s, int hb,
+                                            const float *lrow, const int32_t *rsel,
+                                            const float *rselv) {
+  if (tid < 8) {
+    const int i0 = 4 * tid;
+    float hv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const double gd = static_cast<double>(lrow[i0 + q]);
+      const double silu = gd / (1.0 + exp(-gd));
+      hv[q] = static_cast<float>(silu * static_cast<double>(lrow[32 + i0 + q]));
+    }
+    uint32_t packed[1];
+    float d;
+    int32_t sum;
+    quantize_block<8>(hv, packed, d, sum);
+    const int64_t hoff = static_cast<int64_t>(s) * a.d_ff + 32 * hb + i0;
+    *reinterpret_cast<uint32_t *>(a.qh + hoff) = packed[0];
+    if (tid == 0) {
+      a.dh[static_cast<int64_t>(s) * (a.d_ff / 32) + hb] = d;
+      if (a.sh) a.sh[static_cast<int64_t>(s) * (a.d_ff / 32) + hb] = sum;
+    }
+    if (a.h_out) *reinterpret_cast<float4 *>(a.h_out + hoff) = make_float4(hv[0], hv[1], hv[2], hv[3]);
+    if (a.gu_out) {
+      float *gp = a.gu_out + static_cast<int64_t>(s) * 2 * a.d_ff;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        gp[32 * hb + i0 + q] = lrow[i0 + q];
+        gp[a.d_ff + 32 * hb + i0 + q] = lrow[32 + i0 + q];
+      }
+    }
+  }
+  // one workgroup publishes the expert list and weights for the down pass,
+  // last, so that the fp64 softmax delays none of its loads
+  if constexpr (ROUTED) {
+    if (blockIdx.x == 0 && blockIdx.y == 0) {  // uniform over the workgroup
+      __shared__ double rsele[64];
+      route_weights(rsel, rselv, rsele, a.n_routed, a.top_k, a.shared_gate, a.ids_out, a.wts_out);
+    }
+  }
+}
 
 template <int WT, int LPR, int BPL, int RB, bool ROUTED>
 __global__ __launch_bounds__(1024) void moe_gate_up_kernel(const MoeGateUpArgs a) {
@@ -45,32 +159,13 @@ __global__ __launch_bounds__(1024) void moe_gate_up_kernel(const MoeGateUpArgs a
   const int hb = static_cast<int>(blockIdx.x);  // 32-wide block of the FFN width
   const int s = static_cast<int>(blockIdx.y);   // selected-expert slot
 
-  // activation loads (two lanes per block), issued before the expert id so
-  // that they share its round trip
-  const int g = tid & 1;
-  int qb = tid >> 1;
+  // activation loads, issued before the expert id so that they share its
+  // round trip
   float xv[16];
-  if (qb < a.nb) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float4 v = *reinterpret_cast<const float4 *>(a.x + qb * 32 + g * 16 + 4 * u);
-      xv[4 * u] = v.x; xv[4 * u + 1] = v.y; xv[4 * u + 2] = v.z; xv[4 * u + 3] = v.w;
-    }
-  }
-  int e;
+  gu_load_x(a, tid, xv);
   __shared__ int32_t rsel[64];
   __shared__ float rselv[64];
-  if constexpr (ROUTED) {
-    // the router, in every workgroup: rank the logits, take slot s's expert
-    __shared__ float rlv[1024];
-    for (int i = tid; i < a.n_routed; i += T) rlv[i] = route_key(a.logits[i]);
-    __syncthreads();
-    route_rank<8>(rlv, a.n_routed, a.top_k, rsel, rselv);
-    __syncthreads();
-    e = s < a.top_k ? rsel[s] : a.n_routed;
-  } else {
-    e = a.ids[s];
-  }
+  const int e = gu_expert<ROUTED, T>(a, tid, s, rsel, rselv);
   if (e < 0 || e >= a.n_experts) {  // uniform over the workgroup
     if (a.status && tid == 0) *a.status = ZQ_ERANGE;
     return;
@@ -82,8 +177,7 @@ __global__ __launch_bounds__(1024) void moe_gate_up_kernel(const MoeGateUpArgs a
   uint32_t off[RB][BPL];
 #pragma unroll
   for (int t = 0; t < RB; ++t) {
-    const int lr = wv * (RB * S) + t * S + slot;  // 0..63
-    const int64_t row = (lr < 32) ? (32 * hb + lr) : (a.d_ff + 32 * hb + (lr - 32));
+    const int64_t row = gu_row(a, hb, wv * (RB * S) + t * S + slot);
 #pragma unroll
     for (int i = 0; i < BPL; ++i) {
       int b = j + LPR * i;
@@ -92,25 +186,7 @@ __global__ __launch_bounds__(1024) void moe_gate_up_kernel(const MoeGateUpArgs a
     }
   }
 
-  // quantize x into LDS
-  for (; qb < a.nb; qb += T / 2) {
-    if (qb != (tid >> 1)) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float4 v = *reinterpret_cast<const float4 *>(a.x + qb * 32 + g * 16 + 4 * u);
-        xv[4 * u] = v.x; xv[4 * u + 1] = v.y; xv[4 * u + 2] = v.z; xv[4 * u + 3] = v.w;
-      }
-    }
-    uint32_t pk[4];
-    float d;
-    int32_t sum;
-    quantize_block<2>(xv, pk, d, sum);
-    *reinterpret_cast<u32x4 *>(lq + qb * 32 + g * 16) = u32x4{pk[0], pk[1], pk[2], pk[3]};
-    if (g == 0) {
-      ld[qb] = d;
-      ls8[qb] = 8 * sum;
-    }
-  }
+  gu_quantize_x<T, 8>(a, tid, xv, lq, ld, ls8);
   __syncthreads();
 
   uint32_t xq[BPL][8];
@@ -162,46 +238,96 @@ __global__ __launch_bounds__(1024) void moe_gate_up_kernel(const MoeGateUpArgs a
     }
   }
   __syncthreads();
+  gu_epilogue<ROUTED>(a, tid, s, hb, lrow, rsel, rselv);
+}
 
-  // epilogue: SwiGLU over the 32 outputs and their quantization (8 lanes,
-  // four elements each)
-  if (tid < 8) {
-    const int i0 = 4 * tid;
-    float hv[4];
+// The K-quant form: the same workgroup and epilogue, with the weights read
+// as K-quant units (one lane per 64-element unit, LPR lanes per row, the row
+// in one pass: k/64 == LPR) against the activation staged in LDS.
+template <int WT, int LPR, int RB, bool ROUTED>
+__global__ __launch_bounds__(1024) void moe_gate_up_k_kernel(const MoeGateUpArgs a) {
+  constexpr int WPB = 16;
+  constexpr int S = 64 / LPR;
+  constexpr int T = 64 * WPB;
+  constexpr int NWD = KQ<WT>::NWD;
+  static_assert(RB * S * WPB == 64, "a workgroup computes 32 gate + 32 up rows");
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  int8_t *lq = reinterpret_cast<int8_t *>(smem);                     // [k]
+  float *ld = reinterpret_cast<float *>(smem + a.k);                 // [nb]
+  int32_t *ls = reinterpret_cast<int32_t *>(smem + a.k + 4 * a.nb);   // [nb] code sums
+  float *lrow = reinterpret_cast<float *>(smem + a.k + 8 * a.nb);     // [64] gate | up
+
+  const int tid = static_cast<int>(threadIdx.x);
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int j = lane & (LPR - 1);   // the lane's unit of every row (single pass)
+  const int slot = lane / LPR;
+  const int p = j & 3;
+  const int hb = static_cast<int>(blockIdx.x);
+  const int s = static_cast<int>(blockIdx.y);
+
+  float xv[16];
+  gu_load_x(a, tid, xv);
+  __shared__ int32_t rsel[64];
+  __shared__ float rselv[64];
+  const int e = gu_expert<ROUTED, T>(a, tid, s, rsel, rselv);
+  if (e < 0 || e >= a.n_experts) {  // uniform over the workgroup
+    if (a.status && tid == 0) *a.status = ZQ_ERANGE;
+    return;
+  }
+  const uint8_t *wb = a.bank + static_cast<int64_t>(e) * a.expert_stride;
+
+  uint32_t v[RB][NWD];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const double gd = static_cast<double>(lrow[i0 + q]);
-      const double silu = gd / (1.0 + exp(-gd));
-      hv[q] = static_cast<float>(silu * static_cast<double>(lrow[32 + i0 + q]));
-    }
-    uint32_t packed[1];
-    float d;
-    int32_t sum;
-    quantize_block<8>(hv, packed, d, sum);
-    const int64_t hoff = static_cast<int64_t>(s) * a.d_ff + 32 * hb + i0;
-    *reinterpret_cast<uint32_t *>(a.qh + hoff) = packed[0];
-    if (tid == 0) {
-      a.dh[static_cast<int64_t>(s) * (a.d_ff / 32) + hb] = d;
-      if (a.sh) a.sh[static_cast<int64_t>(s) * (a.d_ff / 32) + hb] = sum;
-    }
-    if (a.h_out) *reinterpret_cast<float4 *>(a.h_out + hoff) = make_float4(hv[0], hv[1], hv[2], hv[3]);
-    if (a.gu_out) {
-      float *gp = a.gu_out + static_cast<int64_t>(s) * 2 * a.d_ff;
+  for (int t = 0; t < RB; ++t) {
+    const int64_t row = gu_row(a, hb, wv * (RB * S) + t * S + slot);
+    load_unit_w<WT>(wb + row * a.row_bytes + static_cast<int64_t>(j >> 2) * KQ<WT>::BYTES, p, v[t]);
+  }
+
+  gu_quantize_x<T, 1>(a, tid, xv, lq, ld, ls);
+  __syncthreads();
+
+  // the lane's unit of the activation, from LDS
+  KUnitAct act;
+  if constexpr (WT == ZQ_Q6_K) {
+    const int base = 256 * (j >> 2) + 128 * ((j >> 1) & 1) + 16 * (j & 1);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        gp[32 * hb + i0 + q] = lrow[i0 + q];
-        gp[a.d_ff + 32 * hb + i0 + q] = lrow[32 + i0 + q];
-      }
+    for (int c = 0; c < 4; ++c) {
+      const u32x4 q = *reinterpret_cast<const u32x4 *>(lq + base + 32 * c);
+      act.q[4 * c] = q.x; act.q[4 * c + 1] = q.y; act.q[4 * c + 2] = q.z; act.q[4 * c + 3] = q.w;
+      act.d[c] = ld[(base + 32 * c) >> 5];
+      act.m32[c] = -32 * code_sum(&act.q[4 * c], 4);
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const u32x4 q = *reinterpret_cast<const u32x4 *>(lq + 64 * j + 16 * c);
+      act.q[4 * c] = q.x; act.q[4 * c + 1] = q.y; act.q[4 * c + 2] = q.z; act.q[4 * c + 3] = q.w;
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      act.d[h] = ld[2 * j + h];
+      act.fs[h] = static_cast<float>(ls[2 * j + h]);
     }
   }
-  // one workgroup publishes the expert list and weights for the down pass,
-  // last, so that the fp64 softmax delays none of its loads
-  if constexpr (ROUTED) {
-    if (blockIdx.x == 0 && blockIdx.y == 0) {  // uniform over the workgroup
-      __shared__ double rsele[64];
-      route_weights(rsel, rselv, rsele, a.n_routed, a.top_k, a.shared_gate, a.ids_out, a.wts_out);
+  float acc[RB];
+#pragma unroll
+  for (int t = 0; t < RB; ++t) {
+    int32_t is[4];
+    acc[t] = unit_dot<WT>(v[t], p, act, is);
+  }
+  using R = RowReduce<LPR, RB>;
+  float res[R::NOUT];
+  R::run(acc, res);
+  if (R::writer(lane)) {
+#pragma unroll
+    for (int m = 0; m < R::NOUT; ++m) {
+      const int lr = wv * (RB * S) + R::rowstep(m, lane) * S + slot;
+      lrow[lr] = res[m];
     }
   }
+  __syncthreads();
+  gu_epilogue<ROUTED>(a, tid, s, hb, lrow, rsel, rselv);
 }
 
 // ---------------------------------------------------------------- down -----
@@ -385,6 +511,26 @@ int launch_gu_w(const MoeGateUpArgs &a, hipStream_t stream) {
   return launch_gu<WT, 64, 2, 4>(a, stream);  // nb <= 128 (moe_gate_up_fits)
 }
 
+template <int WT, int LPR, int RB>
+int launch_gu_k(const MoeGateUpArgs &a, hipStream_t stream) {
+  const size_t lds = static_cast<size_t>(a.k) + 8 * static_cast<size_t>(a.nb) + 64 * 4;
+  const dim3 grid(static_cast<unsigned>(a.d_ff / 32), static_cast<unsigned>(a.n_sel));
+  if (a.logits)
+    hipLaunchKernelGGL((moe_gate_up_k_kernel<WT, LPR, RB, true>), grid, dim3(1024), lds, stream, a);
+  else
+    hipLaunchKernelGGL((moe_gate_up_k_kernel<WT, LPR, RB, false>), grid, dim3(1024), lds, stream, a);
+  ZQ_LAUNCH_CHECK();
+  return ZQ_OK;
+}
+
+template <int WT>
+int launch_gu_k_w(const MoeGateUpArgs &a, hipStream_t stream) {
+  // one 64-element unit per lane, the row in one pass (k = 64 * LPR)
+  if (a.k == 1024) return launch_gu_k<WT, 16, 1>(a, stream);
+  if (a.k == 2048) return launch_gu_k<WT, 32, 2>(a, stream);
+  return launch_gu_k<WT, 64, 4>(a, stream);  // k == 4096 (moe_gate_up_k_fits)
+}
+
 template <int WT, int LPR, int BPL>
 int launch_dn(const MoeDownArgs &a, hipStream_t stream) {
   constexpr int WPB = 2;
@@ -423,6 +569,24 @@ int launch_moe_gate_up(int wtype, MoeGateUpArgs a, hipStream_t stream) {
   a.nb = static_cast<int32_t>(a.k / 32);
   a.row_bytes = static_cast<int64_t>(a.nb) * (wtype == ZQ_Q4_0 ? 18 : 34);
   return wtype == ZQ_Q4_0 ? launch_gu_w<ZQ_Q4_0>(a, stream) : launch_gu_w<ZQ_Q8_0>(a, stream);
+}
+
+bool moe_gate_up_k_fits(int64_t d_model) {
+  return d_model == 1024 || d_model == 2048 || d_model == 4096;
+}
+
+int launch_moe_gate_up_k(int wtype, MoeGateUpArgs a, hipStream_t stream) {
+  if (a.n_sel == 0 || a.d_ff == 0) return ZQ_OK;
+  a.nb = static_cast<int32_t>(a.k / 32);
+  switch (wtype) {
+    case ZQ_Q4_K: a.row_bytes = static_cast<int64_t>(a.k / 256) * KQ<ZQ_Q4_K>::BYTES;
+                  return launch_gu_k_w<ZQ_Q4_K>(a, stream);
+    case ZQ_Q5_K: a.row_bytes = static_cast<int64_t>(a.k / 256) * KQ<ZQ_Q5_K>::BYTES;
+                  return launch_gu_k_w<ZQ_Q5_K>(a, stream);
+    case ZQ_Q6_K: a.row_bytes = static_cast<int64_t>(a.k / 256) * KQ<ZQ_Q6_K>::BYTES;
+                  return launch_gu_k_w<ZQ_Q6_K>(a, stream);
+    default: return ZQ_EINVAL;
+  }
 }
 
 int launch_moe_down(int wtype, MoeDownArgs a, hipStream_t stream) {

@@ -35,6 +35,28 @@ inline bool al(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>
 inline bool k_ok(int64_t k) { return k > 0 && k % 32 == 0 && k / 32 <= (int64_t(1) << 30); }
 inline hipStream_t S(void *s) { return static_cast<hipStream_t>(s); }
 inline int64_t block_bytes(int wtype) { return wtype == ZQ_Q4_0 ? 18 : (wtype == ZQ_Q8_0 ? 34 : -1); }
+inline bool is_k(int wtype) { return wtype == ZQ_Q4_K || wtype == ZQ_Q5_K || wtype == ZQ_Q6_K; }
+
+// Bytes of one rows x k matrix in wtype, or -1 for an unknown type.
+inline int64_t matrix_bytes(int wtype, int64_t rows, int64_t k) {
+  if (wtype == ZQ_Q4_0 || wtype == ZQ_Q8_0) return rows * (k / 32) * block_bytes(wtype);
+  if (!is_k(wtype)) return -1;
+  const int64_t sbb = wtype == ZQ_Q4_K ? 144 : (wtype == ZQ_Q5_K ? 176 : 210);
+  return rows * (k / 256) * sbb;
+}
+
+// An expert bank's alignment: K-quant units are read with 16-byte loads.
+inline bool bank_al(int wtype, const void *p, int64_t stride) {
+  return is_k(wtype) ? (al(p, 16) && stride % 16 == 0) : (al(p, 4) && stride % 2 == 0);
+}
+
+// The fused gate/up pass (both formats) and the d_model it serves.
+inline bool gate_up_fits(int wtype, int64_t d_model) {
+  return is_k(wtype) ? zq::moe_gate_up_k_fits(d_model) : zq::moe_gate_up_fits(d_model);
+}
+inline int launch_gate_up(int wtype, const zq::MoeGateUpArgs &a, hipStream_t s) {
+  return is_k(wtype) ? zq::launch_moe_gate_up_k(wtype, a, s) : zq::launch_moe_gate_up(wtype, a, s);
+}
 
 #define ZQ_REQUIRE(cond, code) \
   do {                         \
@@ -488,16 +510,14 @@ int zq_moe_gate_up(int wtype, const void *gu_bank, int64_t gu_stride_bytes, int6
                    int64_t d_model, int64_t d_ff, const int32_t *ids, int32_t n_sel,
                    const float *x, int8_t *qh, float *dh, int32_t *sh, float *h_out,
                    float *gu_out, int32_t *dev_status, void *stream) {
-  const int64_t bb = block_bytes(wtype);
-  ZQ_REQUIRE(bb > 0, ZQ_EINVAL);
+  ZQ_REQUIRE(matrix_bytes(wtype, 1, 256) > 0, ZQ_EINVAL);
   ZQ_REQUIRE(gu_bank && ids && x && qh && dh, ZQ_ENULL);
   ZQ_REQUIRE(n_experts >= 1 && n_experts <= INT32_MAX && k_ok(d_model) && k_ok(d_ff), ZQ_EINVAL);
-  ZQ_REQUIRE(zq::moe_gate_up_fits(d_model) && d_ff <= (int64_t(1) << 30), ZQ_EINVAL);
+  ZQ_REQUIRE(gate_up_fits(wtype, d_model) && d_ff <= (int64_t(1) << 30), ZQ_EINVAL);
   ZQ_REQUIRE(n_sel >= 0 && n_sel <= 65535, ZQ_EINVAL);
-  ZQ_REQUIRE(gu_stride_bytes >= 2 * d_ff * (d_model / 32) * bb && gu_stride_bytes % 2 == 0,
-             ZQ_EINVAL);
-  ZQ_REQUIRE(al(gu_bank, 4) && al(ids, 4) && al(x, 16) && al(qh, 16) && al(dh, 4) && al(sh, 4) &&
-                 al(h_out, 16) && al(gu_out, 4) && al(dev_status, 4),
+  ZQ_REQUIRE(gu_stride_bytes >= matrix_bytes(wtype, 2 * d_ff, d_model), ZQ_EINVAL);
+  ZQ_REQUIRE(bank_al(wtype, gu_bank, gu_stride_bytes) && al(ids, 4) && al(x, 16) && al(qh, 16) &&
+                 al(dh, 4) && al(sh, 4) && al(h_out, 16) && al(gu_out, 4) && al(dev_status, 4),
              ZQ_EALIGN);
   const int dc = check_current_device();
   if (dc != ZQ_OK) return dc;
@@ -516,7 +536,7 @@ int zq_moe_gate_up(int wtype, const void *gu_bank, int64_t gu_stride_bytes, int6
   a.h_out = h_out;
   a.gu_out = gu_out;
   a.status = dev_status;
-  return zq::launch_moe_gate_up(wtype, a, S(stream));
+  return launch_gate_up(wtype, a, S(stream));
 }
 
 int zq_moe_gate_up_route(int wtype, const void *gu_bank, int64_t gu_stride_bytes,
@@ -524,20 +544,18 @@ int zq_moe_gate_up_route(int wtype, const void *gu_bank, int64_t gu_stride_bytes
                          int32_t n_routed, int32_t top_k, const float *shared_gate,
                          const float *x, int32_t *ids, float *wts, int8_t *qh, float *dh,
                          int32_t *sh, float *h_out, float *gu_out, void *stream) {
-  const int64_t bb = block_bytes(wtype);
-  ZQ_REQUIRE(bb > 0, ZQ_EINVAL);
+  ZQ_REQUIRE(matrix_bytes(wtype, 1, 256) > 0, ZQ_EINVAL);
   ZQ_REQUIRE(gu_bank && logits && ids && wts && x && qh && dh, ZQ_ENULL);
   ZQ_REQUIRE(top_k >= 1 && top_k <= 64 && n_routed >= top_k && n_routed <= 1024, ZQ_EINVAL);
   const int32_t n_sel = top_k + (shared_gate ? 1 : 0);
   ZQ_REQUIRE(n_experts >= n_sel - top_k + n_routed && n_experts <= INT32_MAX && k_ok(d_model) &&
                  k_ok(d_ff),
              ZQ_EINVAL);
-  ZQ_REQUIRE(zq::moe_gate_up_fits(d_model) && d_ff <= (int64_t(1) << 30), ZQ_EINVAL);
-  ZQ_REQUIRE(gu_stride_bytes >= 2 * d_ff * (d_model / 32) * bb && gu_stride_bytes % 2 == 0,
-             ZQ_EINVAL);
-  ZQ_REQUIRE(al(gu_bank, 4) && al(logits, 4) && al(shared_gate, 4) && al(ids, 4) && al(wts, 4) &&
-                 al(x, 16) && al(qh, 16) && al(dh, 4) && al(sh, 4) && al(h_out, 16) &&
-                 al(gu_out, 4),
+  ZQ_REQUIRE(gate_up_fits(wtype, d_model) && d_ff <= (int64_t(1) << 30), ZQ_EINVAL);
+  ZQ_REQUIRE(gu_stride_bytes >= matrix_bytes(wtype, 2 * d_ff, d_model), ZQ_EINVAL);
+  ZQ_REQUIRE(bank_al(wtype, gu_bank, gu_stride_bytes) && al(logits, 4) && al(shared_gate, 4) &&
+                 al(ids, 4) && al(wts, 4) && al(x, 16) && al(qh, 16) && al(dh, 4) && al(sh, 4) &&
+                 al(h_out, 16) && al(gu_out, 4),
              ZQ_EALIGN);
   const int dc = check_current_device();
   if (dc != ZQ_OK) return dc;
@@ -561,7 +579,7 @@ int zq_moe_gate_up_route(int wtype, const void *gu_bank, int64_t gu_stride_bytes
   a.shared_gate = shared_gate;
   a.ids_out = ids;
   a.wts_out = wts;
-  return zq::launch_moe_gate_up(wtype, a, S(stream));
+  return launch_gate_up(wtype, a, S(stream));
 }
 
 int zq_swiglu_quantize(const float *gu, int64_t n, int64_t f, int8_t *qh, float *dh, int32_t *sh,
@@ -842,16 +860,6 @@ int moe_stage(int wtype, int mode, const void *bank, int64_t stride, int64_t n_e
   return zq::launch_dmmv(wtype, mode, a, s);
 }
 
-bool is_k(int wtype) { return wtype == ZQ_Q4_K || wtype == ZQ_Q5_K || wtype == ZQ_Q6_K; }
-
-// Bytes of one rows x k matrix in wtype, or -1 for an unknown type.
-int64_t matrix_bytes(int wtype, int64_t rows, int64_t k) {
-  if (wtype == ZQ_Q4_0 || wtype == ZQ_Q8_0) return rows * (k / 32) * block_bytes(wtype);
-  if (!is_k(wtype)) return -1;
-  const int64_t sbb = wtype == ZQ_Q4_K ? 144 : (wtype == ZQ_Q5_K ? 176 : 210);
-  return rows * (k / 256) * sbb;
-}
-
 }  // namespace
 
 int zq_moe_ffn_mixed(int gu_wtype, const void *gu_bank, int64_t gu_stride_bytes, int down_wtype,
@@ -881,9 +889,6 @@ int zq_moe_ffn_mixed(int gu_wtype, const void *gu_bank, int64_t gu_stride_bytes,
   ZQ_REQUIRE((flags & ~uint32_t(ZQ_ACCUMULATE)) == 0, ZQ_EINVAL);
   const int32_t n_sel = top_k + (shared ? 1 : 0);
   ZQ_REQUIRE(workspace_bytes >= zq_moe_ffn_workspace_bytes(d_model, d_ff, n_sel), ZQ_EINVAL);
-  const auto bank_al = [](int wt, const void *p, int64_t stride) {
-    return is_k(wt) ? (al(p, 16) && stride % 16 == 0) : (al(p, 4) && stride % 2 == 0);
-  };
   ZQ_REQUIRE(bank_al(gu_wtype, gu_bank, gu_stride_bytes) &&
                  bank_al(down_wtype, down_bank, down_stride_bytes) &&
                  (!shared || (bank_al(sh_wtype, sh_gu, 0) && bank_al(sh_wtype, sh_down, 0))) &&
@@ -902,23 +907,67 @@ int zq_moe_ffn_mixed(int gu_wtype, const void *gu_bank, int64_t gu_stride_bytes,
   int8_t *qh = reinterpret_cast<int8_t *>(ws + L.qh);
   float *dh = reinterpret_cast<float *>(ws + L.dh);
   int32_t *sh = reinterpret_cast<int32_t *>(ws + L.sh);
-  int rc = zq::launch_moe_route(logits, n_routed, top_k, shared_gate, ids, wts, s);
-  if (rc != ZQ_OK) return rc;
-  rc = zq::launch_quantize_act(x, 1, d_model, d_model, qx, dx, sx, s);
-  if (rc != ZQ_OK) return rc;
-  // gate||up rows of every selected expert; the shared one (id n_routed) from
-  // its own matrix
-  rc = moe_stage(gu_wtype, zq::MODE_GATHER, gu_bank, gu_stride_bytes, n_routed, 0, 2 * d_ff,
-                 d_model, ids, nullptr, top_k, qx, dx, sx, 0, gu, 0, s);
-  if (rc != ZQ_OK) return rc;
-  if (shared) {
-    rc = moe_stage(sh_wtype, zq::MODE_GATHER, sh_gu, 0, 1, n_routed, 2 * d_ff, d_model,
-                   ids + top_k, nullptr, 1, qx, dx, sx, 0,
-                   gu + static_cast<int64_t>(top_k) * 2 * d_ff, 0, s);
+  int rc;
+  if (gate_up_fits(gu_wtype, d_model) && (!shared || gate_up_fits(sh_wtype, d_model))) {
+    // fused: the routed experts' gate/up pass ranks the logits itself and
+    // publishes ids / wts (the shared slot included); the shared expert
+    // (id n_routed) follows from its own matrix
+    zq::MoeGateUpArgs a{};
+    a.bank = static_cast<const uint8_t *>(gu_bank);
+    a.expert_stride = gu_stride_bytes;
+    a.n_experts = n_routed;
+    a.ids = ids;
+    a.n_sel = top_k;
+    a.x = x;
+    a.k = static_cast<int32_t>(d_model);
+    a.d_ff = static_cast<int32_t>(d_ff);
+    a.qh = qh;
+    a.dh = dh;
+    a.sh = sh;
+    a.logits = logits;
+    a.n_routed = n_routed;
+    a.top_k = top_k;
+    a.shared_gate = shared_gate;
+    a.ids_out = ids;
+    a.wts_out = wts;
+    rc = launch_gate_up(gu_wtype, a, s);
+    if (rc != ZQ_OK) return rc;
+    if (shared) {
+      const int64_t h0 = static_cast<int64_t>(top_k) * d_ff;
+      zq::MoeGateUpArgs b{};
+      b.bank = static_cast<const uint8_t *>(sh_gu);
+      b.n_experts = 1;
+      b.ids = ids + top_k;
+      b.id_base = n_routed;
+      b.n_sel = 1;
+      b.x = x;
+      b.k = static_cast<int32_t>(d_model);
+      b.d_ff = static_cast<int32_t>(d_ff);
+      b.qh = qh + h0;
+      b.dh = dh + h0 / 32;
+      b.sh = sh + h0 / 32;
+      rc = launch_gate_up(sh_wtype, b, s);
+      if (rc != ZQ_OK) return rc;
+    }
+  } else {
+    rc = zq::launch_moe_route(logits, n_routed, top_k, shared_gate, ids, wts, s);
+    if (rc != ZQ_OK) return rc;
+    rc = zq::launch_quantize_act(x, 1, d_model, d_model, qx, dx, sx, s);
+    if (rc != ZQ_OK) return rc;
+    // gate||up rows of every selected expert; the shared one (id n_routed)
+    // from its own matrix
+    rc = moe_stage(gu_wtype, zq::MODE_GATHER, gu_bank, gu_stride_bytes, n_routed, 0, 2 * d_ff,
+                   d_model, ids, nullptr, top_k, qx, dx, sx, 0, gu, 0, s);
+    if (rc != ZQ_OK) return rc;
+    if (shared) {
+      rc = moe_stage(sh_wtype, zq::MODE_GATHER, sh_gu, 0, 1, n_routed, 2 * d_ff, d_model,
+                     ids + top_k, nullptr, 1, qx, dx, sx, 0,
+                     gu + static_cast<int64_t>(top_k) * 2 * d_ff, 0, s);
+      if (rc != ZQ_OK) return rc;
+    }
+    rc = zq::launch_swiglu_quantize(gu, n_sel, d_ff, qh, dh, sh, nullptr, s);
     if (rc != ZQ_OK) return rc;
   }
-  rc = zq::launch_swiglu_quantize(gu, n_sel, d_ff, qh, dh, sh, nullptr, s);
-  if (rc != ZQ_OK) return rc;
   // down rows: the weighted sum over the routed experts, then the shared one
   // added onto it
   rc = moe_stage(down_wtype, zq::MODE_WEIGHTED, down_bank, down_stride_bytes, n_routed, 0,

@@ -128,6 +128,8 @@ struct MoeGateUpArgs {
   const float *shared_gate;
   int32_t *ids_out;
   float *wts_out;
+  // last, so that the fields above keep their kernel-argument offsets
+  int32_t id_base;      // without logits: expert e = ids[s] - id_base
 };
 
 // MoE down pass with the weighted sum over the selected experts fused in.
@@ -155,6 +157,10 @@ struct MoeDownArgs {
 
 int launch_moe_gate_up(int wtype, MoeGateUpArgs a, hipStream_t stream);
 int launch_moe_down(int wtype, MoeDownArgs a, hipStream_t stream);
+// The gate/up pass over K-quant experts (wtype ZQ_Q4_K / ZQ_Q5_K / ZQ_Q6_K):
+// d_model of 1024, 2048 or 4096 (one 64-element unit per lane, one pass).
+bool moe_gate_up_k_fits(int64_t d_model);
+int launch_moe_gate_up_k(int wtype, MoeGateUpArgs a, hipStream_t stream);
 size_t moe_down_lds_bytes(int64_t n_sel, int64_t k);
 bool moe_gate_up_fits(int64_t d_model);
 bool moe_down_fits(int64_t n_sel, int64_t k);

@@ -259,8 +259,13 @@ int zq_swiglu_quantize(const float *gu, int64_t n, int64_t f, int8_t *qh, float 
  * dh [n_sel][d_ff/32] fp32, sh [n_sel][d_ff/32] int32 (may be NULL).
  * Optional (may be NULL) debug outputs: h_out [n_sel][d_ff] fp32 (16-byte
  * aligned) and gu_out [n_sel][2*d_ff] fp32, the gate||up rows.
- * d_model <= 4096, d_ff % 32 == 0.  A bad id is skipped (its outputs are
- * left untouched) and reported through dev_status as in zq_dmmv_moe. */
+ * wtype: ZQ_Q4_0 / ZQ_Q8_0 with d_model <= 4096, or ZQ_Q4_K / ZQ_Q5_K /
+ * ZQ_Q6_K with d_model of 1024, 2048 or 4096 (the pages' routed experts are
+ * Q4_K gate/up: "dmmv_q4k_moe"; K-quant banks 16-byte aligned with
+ * gu_stride_bytes % 16 == 0; the row dot products are those of
+ * zq_dmmv_q4_k and its kin).  d_ff % 32 == 0.  A bad id is skipped (its
+ * outputs are left untouched) and reported through dev_status as in
+ * zq_dmmv_moe. */
 int zq_moe_gate_up(int wtype, const void *gu_bank, int64_t gu_stride_bytes, int64_t n_experts,
                    int64_t d_model, int64_t d_ff, const int32_t *ids, int32_t n_sel,
                    const float *x, int8_t *qh, float *dh, int32_t *sh, float *h_out,
@@ -271,8 +276,9 @@ int zq_moe_gate_up(int wtype, const void *gu_bank, int64_t gu_stride_bytes, int6
  * n_routed logits, slot top_k the shared expert (id n_routed) when
  * shared_gate is non-NULL; ids / wts (top_k (+1) entries) receive the
  * router's output, bit for bit, for the down pass.  Outputs as
- * zq_moe_gate_up with n_sel = top_k (+1).  1 <= top_k <= 64,
- * top_k <= n_routed <= 1024, n_experts >= n_routed (+1), d_model <= 4096. */
+ * zq_moe_gate_up with n_sel = top_k (+1), for the same weight types and
+ * d_model.  1 <= top_k <= 64, top_k <= n_routed <= 1024,
+ * n_experts >= n_routed (+1). */
 int zq_moe_gate_up_route(int wtype, const void *gu_bank, int64_t gu_stride_bytes,
                          int64_t n_experts, int64_t d_model, int64_t d_ff, const float *logits,
                          int32_t n_routed, int32_t top_k, const float *shared_gate,
@@ -327,11 +333,15 @@ int zq_moe_ffn_route(int wtype, const void *gu_bank, int64_t gu_stride_bytes,
  * n_routed experts of [d_model][d_ff]; sh_gu / sh_down: the shared expert's
  * two matrices (used when shared_gate is non-NULL).  The router is
  * zq_moe_route's (ids / wts receive top_k (+1) entries, the shared one with
- * id n_routed); then, one launch each: quantize x, gather the routed
- * gate||up rows, the shared gate||up rows, SwiGLU + re-quantize, the routed
- * weighted down sum, the shared down term added on.  y [d_model] (+)= the
- * weighted sum; workspace >= zq_moe_ffn_workspace_bytes(d_model, d_ff,
- * top_k (+1)) bytes, 256-byte aligned.  y may be x itself. */
+ * id n_routed).  When both gate/up types take the fused pass of
+ * zq_moe_gate_up at this d_model, four launches: the routed gate/up pass
+ * with the router folded in (zq_moe_gate_up_route over the routed bank),
+ * the shared expert's gate/up pass, the routed weighted down sum, the shared
+ * down term added on.  Otherwise seven: router, quantize x, the routed and
+ * the shared gate||up gathers, SwiGLU + re-quantize, the two down stages.
+ * y [d_model] (+)= the weighted sum; workspace >=
+ * zq_moe_ffn_workspace_bytes(d_model, d_ff, top_k (+1)) bytes, 256-byte
+ * aligned.  y may be x itself. */
 int zq_moe_ffn_mixed(int gu_wtype, const void *gu_bank, int64_t gu_stride_bytes, int down_wtype,
                      const void *down_bank, int64_t down_stride_bytes, int sh_wtype,
                      const void *sh_gu, const void *sh_down, int64_t d_model, int64_t d_ff,

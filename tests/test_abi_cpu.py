@@ -334,6 +334,19 @@ def test_other_argument_errors():
                             None, None, None) == zq.ZQ_ENULL
     assert L.zq_moe_gate_up(4, A, 1024 * 64 * 18, 9, 2048, 512, B, 9, C, D + 4, D + 65536, None,
                             None, None, None, None) == zq.ZQ_EALIGN
+    # K-quant gate/up: d_model off the fused pass's widths, a bank or a
+    # stride off 16 bytes, a stride short of one expert
+    kgs = 2 * 512 * (2048 // 256) * 144
+    assert L.zq_moe_gate_up(12, A, 2 * 512 * 2 * 144, 9, 512, 512, B, 9, C, D, D + 65536, None,
+                            None, None, None, None) == zq.ZQ_EINVAL
+    assert L.zq_moe_gate_up(12, A + 4, kgs, 9, 2048, 512, B, 9, C, D, D + 65536, None, None, None,
+                            None, None) == zq.ZQ_EALIGN
+    assert L.zq_moe_gate_up(12, A, kgs + 8, 9, 2048, 512, B, 9, C, D, D + 65536, None, None, None,
+                            None, None) == zq.ZQ_EALIGN
+    assert L.zq_moe_gate_up(13, A, kgs, 9, 2048, 512, B, 9, C, D, D + 65536, None, None, None,
+                            None, None) == zq.ZQ_EINVAL
+    assert L.zq_moe_gate_up(15, A, kgs, 9, 2048, 512, B, 9, C, D, D + 65536, None, None, None,
+                            None, None) == zq.ZQ_EINVAL
     # swiglu: f not a multiple of 32
     assert L.zq_swiglu_quantize(A, 9, 48, B, C, None, None, None) == zq.ZQ_EINVAL
     # moe_ffn: workspace too small

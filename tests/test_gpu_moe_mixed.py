@@ -74,6 +74,86 @@ def test_dmmv_moe_kquant_gather_and_weighted(zq, wt):
     assert np.isnan(y3h[1]).all() and not np.isnan(y3h[0]).any() and not np.isnan(y3h[2]).any()
 
 
+@pytest.mark.parametrize("wt", [Q4_K, Q5_K, Q6_K], ids=lambda t: NAME[t])
+@pytest.mark.parametrize("d_model,d_ff", [(1024, 256), (2048, 512), (4096, 96)])
+def test_moe_gate_up_kquant(zq, wt, d_model, d_ff):
+    """The fused K-quant gate/up pass, chained: gate||up rows against the
+    oracle's expert rows, h against SwiGLU of the GPU's own rows, the codes
+    bit-exact against the oracle's quantization of the GPU's h."""
+    torch = torch_cuda()
+    E = 5
+    bank, stride = gen_bank(wt, E, 2 * d_ff, d_model, 860 + wt + d_model)
+    ids = np.array([4, 0, 4, 2], np.int32)
+    n = ids.size
+    x = inputs.gen_activation(1, d_model, 861 + d_model)
+    rq, rd, _ = oracle.quantize_act(x)
+    qh = torch.full((n, d_ff), 0x55, dtype=torch.int8, device="cuda")
+    dh, sh = nan_f32(n, d_ff // 32), sentinel_i32(n, d_ff // 32)
+    h, gu = nan_f32(n, d_ff), nan_f32(n, 2 * d_ff)
+    status = sentinel_i32(1, value=0)
+    assert zq.zq_moe_gate_up(wt, dev(bank), stride, E, d_model, d_ff, dev(ids), n, dev(x), qh, dh,
+                             sh, h, gu, status) == 0
+    gu_h = host(gu)
+    for s, e in enumerate(ids):
+        y_ref, S = oracle.expert_rows_any(wt, bank, stride, 2 * d_ff, d_model, int(e), rq, rd)
+        check_rows(gu_h[s], y_ref, S, "%s gate/up slot %d, %d -> %d" % (NAME[wt], s, d_model, d_ff))
+    h_h = host(h)
+    assert np.allclose(h_h, oracle.swiglu(gu_h, d_ff), rtol=1e-6, atol=0)
+    rqh, rdh, rsh = oracle.quantize_act(h_h)
+    assert np.array_equal(host(qh), rqh)
+    assert np.array_equal(host(dh).view(np.uint32), rdh.view(np.uint32))
+    assert np.array_equal(host(sh), rsh)
+    assert int(host(status)[0]) == 0
+    # slots of one expert give the same bits; without the debug outputs too
+    assert np.array_equal(gu_h[0].view(np.uint32), gu_h[2].view(np.uint32))
+    qh2 = torch.zeros((n, d_ff), dtype=torch.int8, device="cuda")
+    dh2 = nan_f32(n, d_ff // 32)
+    zq.zq_moe_gate_up(wt, dev(bank), stride, E, d_model, d_ff, dev(ids), n, dev(x), qh2, dh2)
+    assert np.array_equal(host(qh2), host(qh))
+    assert np.array_equal(host(dh2).view(np.uint32), host(dh).view(np.uint32))
+
+
+@pytest.mark.parametrize("wt", [Q4_K, Q6_K], ids=lambda t: NAME[t])
+def test_moe_gate_up_kquant_bad_id_and_route(zq, wt):
+    """A bad expert id is skipped and reported; the routed form equals the
+    router followed by the plain pass, output by output."""
+    torch = torch_cuda()
+    d_model, d_ff, n_routed, top_k = 2048, 256, 16, 4
+    bank, stride = gen_bank(wt, n_routed + 1, 2 * d_ff, d_model, 870 + wt)
+    bank_d = dev(bank)
+    x = dev(inputs.gen_activation(1, d_model, 871))
+    status = sentinel_i32(1, value=0)
+    qh = torch.full((3, d_ff), 0x55, dtype=torch.int8, device="cuda")
+    dh = nan_f32(3, d_ff // 32)
+    zq.zq_moe_gate_up(wt, bank_d, stride, n_routed + 1, d_model, d_ff,
+                      dev(np.array([1, 17, 3], np.int32)), 3, x, qh, dh, None, None, None, status)
+    assert int(host(status)[0]) == zq.ZQ_ERANGE
+    dhh = host(dh)
+    assert np.isnan(dhh[1]).all() and not np.isnan(dhh[0]).any() and not np.isnan(dhh[2]).any()
+    assert (host(qh)[1] == 0x55).all()
+
+    logits, g = inputs.gen_router(n_routed, 872)
+    gd = dev(np.array([g], np.float32))
+    n_sel = top_k + 1
+    outs = []
+    for routed in (True, False):
+        ids, wts = sentinel_i32(n_sel), nan_f32(n_sel)
+        qh = torch.empty((n_sel, d_ff), dtype=torch.int8, device="cuda")
+        dh, sh = nan_f32(n_sel, d_ff // 32), sentinel_i32(n_sel, d_ff // 32)
+        gu = nan_f32(n_sel, 2 * d_ff)
+        if routed:
+            zq.zq_moe_gate_up_route(wt, bank_d, stride, n_routed + 1, d_model, d_ff, dev(logits),
+                                    n_routed, top_k, gd, x, ids, wts, qh, dh, sh, None, gu)
+        else:
+            zq.zq_moe_route(dev(logits), n_routed, top_k, gd, ids, wts)
+            zq.zq_moe_gate_up(wt, bank_d, stride, n_routed + 1, d_model, d_ff, ids, n_sel, x, qh,
+                              dh, sh, None, gu)
+        outs.append([host(t).copy() for t in (ids, wts, qh, dh, sh, gu)])
+    for a, b in zip(*outs):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+    assert outs[0][0][top_k] == n_routed
+
+
 def run_mixed(zq, fmt, banks, d_model, d_ff, n_routed, top_k, logits, g, x, y=None, flags=0):
     torch = torch_cuda()
     (gwt, gu_d, gs), (dwt, dn_d, ds), (swt, sgu_d, sdn_d) = banks
@@ -110,8 +190,9 @@ PAGES = (Q4_K, Q5_K, Q8_0)
 
 @pytest.mark.parametrize("fmt", [PAGES, (Q4_0, Q4_0, Q8_0), (Q6_K, Q4_K, Q4_0)],
                          ids=lambda f: "-".join(NAME[t] for t in f))
-def test_moe_ffn_mixed_small(zq, fmt):
-    d_model, d_ff, n_routed, top_k = 512, 256, 16, 4
+@pytest.mark.parametrize("d_model", [512, 1024])   # the staged path, the fused gate/up pass
+def test_moe_ffn_mixed_small(zq, fmt, d_model):
+    d_ff, n_routed, top_k = 256, 16, 4
     host_b, dev_b = make_banks(fmt, n_routed, d_model, d_ff, 830 + sum(fmt))
     logits, g = inputs.gen_router(n_routed, 831)
     x = inputs.gen_activation(1, d_model, 832)
@@ -126,12 +207,15 @@ def test_moe_ffn_mixed_small(zq, fmt):
     assert np.allclose(host(y), 2 * prev, rtol=1e-6, atol=0)
 
 
-def test_moe_ffn_mixed_equals_its_stages(zq):
+@pytest.mark.parametrize("d_model", [512, 2048])
+def test_moe_ffn_mixed_equals_its_stages(zq, d_model):
     """The composite gives the bits of the same stages run through the
-    public entry points one by one (router, quantize, routed and shared
-    gate||up gathers, SwiGLU + re-quantize, routed and shared down)."""
+    public entry points one by one.  d_model 512: router, quantize, routed
+    and shared gate||up gathers, SwiGLU + re-quantize; 2048 (the fused
+    gate/up pass): router, routed and shared zq_moe_gate_up; then the routed
+    and shared down stages."""
     torch = torch_cuda()
-    d_model, d_ff, n_routed, top_k = 512, 256, 16, 4
+    d_ff, n_routed, top_k = 256, 16, 4
     host_b, dev_b = make_banks(PAGES, n_routed, d_model, d_ff, 840)
     (gwt, gu_d, gs), (dwt, dn_d, ds), (swt, sgu_d, sdn_d) = dev_b
     logits, g = inputs.gen_router(n_routed, 841)
@@ -140,17 +224,23 @@ def test_moe_ffn_mixed_equals_its_stages(zq):
     n_sel = top_k + 1
     ids_d, wts_d = sentinel_i32(n_sel), nan_f32(n_sel)
     zq.zq_moe_route(dev(logits), n_routed, top_k, dev(np.array([g], np.float32)), ids_d, wts_d)
-    qx, dx, sx = quantize_gpu(zq, x)
-    gu = nan_f32(n_sel, 2 * d_ff)
-    zq.zq_dmmv_moe(gwt, gu_d, n_routed, gs, 2 * d_ff, d_model, ids_d, None, top_k, qx, dx, sx, 0,
-                   zq.ZQ_MOE_GATHER, gu)
     zero = dev(np.zeros(1, np.int32))
     sgu_bytes, sdn_bytes = sgu_d.numel(), sdn_d.numel()   # one expert: stride = its size
-    zq.zq_dmmv_moe(swt, sgu_d, 1, sgu_bytes, 2 * d_ff, d_model, zero, None, 1, qx, dx, sx, 0,
-                   zq.ZQ_MOE_GATHER, gu[top_k:])
     qh = torch.empty((n_sel, d_ff), dtype=torch.int8, device="cuda")
     dh, sh = nan_f32(n_sel, d_ff // 32), sentinel_i32(n_sel, d_ff // 32)
-    zq.zq_swiglu_quantize(gu, n_sel, d_ff, qh, dh, sh)
+    if d_model == 512:
+        qx, dx, sx = quantize_gpu(zq, x)
+        gu = nan_f32(n_sel, 2 * d_ff)
+        zq.zq_dmmv_moe(gwt, gu_d, n_routed, gs, 2 * d_ff, d_model, ids_d, None, top_k, qx, dx, sx,
+                       0, zq.ZQ_MOE_GATHER, gu)
+        zq.zq_dmmv_moe(swt, sgu_d, 1, sgu_bytes, 2 * d_ff, d_model, zero, None, 1, qx, dx, sx, 0,
+                       zq.ZQ_MOE_GATHER, gu[top_k:])
+        zq.zq_swiglu_quantize(gu, n_sel, d_ff, qh, dh, sh)
+    else:
+        xd = dev(x)
+        zq.zq_moe_gate_up(gwt, gu_d, gs, n_routed, d_model, d_ff, ids_d, top_k, xd, qh, dh, sh)
+        zq.zq_moe_gate_up(swt, sgu_d, sgu_bytes, 1, d_model, d_ff, zero, 1, xd, qh[top_k:],
+                          dh[top_k:], sh[top_k:])
     y2 = nan_f32(d_model)
     zq.zq_dmmv_moe(dwt, dn_d, n_routed, ds, d_model, d_ff, ids_d, wts_d, top_k, qh, dh, sh, d_ff,
                    zq.ZQ_MOE_WEIGHTED_SUM, y2)
@@ -172,3 +262,19 @@ def test_moe_ffn_mixed_pages_shape(zq):
         assert np.array_equal(ids, oracle.moe_route(logits, top_k, g)[0])
         y_ref, S = oracle_mixed(host_b, n_routed, d_model, d_ff, ids, wts, x)
         check_rows(host(y), y_ref, S, "pages-format moe", tol=1e-3)
+
+
+@pytest.mark.parametrize("fmt", [PAGES, (Q5_K, Q6_K, Q8_0)],
+                         ids=lambda f: "-".join(NAME[t] for t in f))
+def test_moe_ffn_mixed_no_shared_expert(zq, fmt):
+    """Without a shared gate: top_k routed slots only, on the fused pass."""
+    d_model, d_ff, n_routed, top_k = 4096, 256, 32, 6
+    host_b, dev_b = make_banks(fmt, n_routed, d_model, d_ff, 880 + sum(fmt))
+    logits, _ = inputs.gen_router(n_routed, 881)
+    x = inputs.gen_activation(1, d_model, 882)
+    ids, wts, y = run_mixed(zq, fmt, dev_b, d_model, d_ff, n_routed, top_k, logits, None, x)
+    rids, rw = oracle.moe_route(logits, top_k, None)
+    assert np.array_equal(ids, rids) and ids.size == top_k
+    assert np.allclose(wts, rw, rtol=1e-6, atol=0)
+    y_ref, S = oracle_mixed(host_b, n_routed, d_model, d_ff, ids, wts, x)
+    check_rows(host(y), y_ref, S, "mixed moe without shared expert", tol=1e-3)
