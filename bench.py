@@ -345,10 +345,10 @@ class DmmvTokWorkload(Workload):
 class MoeMixedWorkload(Workload):
     """Router + one token through 8 routed experts stored as the pages' model
     stores them (gate/up Q4_K, down Q5_K) and a Q8_0 shared expert, through
-    zq_moe_ffn_mixed (four launches: the routed Q4_K gate/up pass with the
-    router folded in, the shared Q8_0 gate/up pass, the routed Q5_K weighted
-    down sum, the shared down term)."""
-    dominant_name = "moe_gate_up_k_kernel (Q4_K, router folded in)"
+    zq_moe_ffn_mixed (two launches: the gate/up pass over the 8 routed Q4_K
+    experts, router folded in, and the Q8_0 shared expert; the Q5_K weighted
+    down sum with the shared Q8_0 down rows in the same reduction)."""
+    dominant_name = "moe_gate_up_mix_kernel (Q4_K routed + Q8_0 shared, router folded in)"
 
     def __init__(self, wl):
         from block_quant_matrix_amd import inputs
@@ -367,13 +367,13 @@ class MoeMixedWorkload(Workload):
         # shared expert's two matrices; plus the fp32 activation, logits, y
         self.step_bytes = (self.top_k * (self.gu_m + self.dn_m) + self.sgu_m + self.sdn_m +
                            4 * self.dm + 4 * self.E + 4 * self.dm)
-        # the routed gate/up pass: 8 experts' gate||up rows, the fp32 x and
-        # the logits in; the quantized h (codes, scales, sums) and the
-        # expert list out
-        self.gather_bytes = (self.top_k * self.gu_m + 4 * self.dm + 4 * self.E +
-                             self.top_k * self.dff + 8 * self.top_k * (self.dff // 32) +
-                             8 * self.top_k)
-        self.steps, self.warmup = 1000, 100     # four launches per step
+        # the gate/up pass: 8 routed experts' and the shared expert's
+        # gate||up rows, the fp32 x and the logits in; the quantized h
+        # (codes, scales, sums) of 9 slots and the expert list out
+        self.gather_bytes = (self.top_k * self.gu_m + self.sgu_m + 4 * self.dm + 4 * self.E +
+                             self.n_sel * self.dff + 8 * self.n_sel * (self.dff // 32) +
+                             8 * self.n_sel)
+        self.steps, self.warmup = 2000, 200     # two launches per step
 
     def setup(self, torch, zq, inputs):
         self.torch, self.zq = torch, zq
@@ -402,9 +402,9 @@ class MoeMixedWorkload(Workload):
         self.ws_bytes = zq.zq_moe_ffn_workspace_bytes(self.dm, self.dff, self.n_sel)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
         self.y = torch.empty(self.dm, dtype=torch.float32, device="cuda")
-        self.qh = torch.empty((self.top_k, self.dff), dtype=torch.int8, device="cuda")
-        self.dh = torch.empty((self.top_k, self.dff // 32), dtype=torch.float32, device="cuda")
-        self.sh = torch.empty((self.top_k, self.dff // 32), dtype=torch.int32, device="cuda")
+        self.qh = torch.empty((self.n_sel, self.dff), dtype=torch.int8, device="cuda")
+        self.dh = torch.empty((self.n_sel, self.dff // 32), dtype=torch.float32, device="cuda")
+        self.sh = torch.empty((self.n_sel, self.dff // 32), dtype=torch.int32, device="cuda")
 
     def step(self, i):
         gu, dn = self.banks[i % self.ncopy]
@@ -418,13 +418,12 @@ class MoeMixedWorkload(Workload):
         pass
 
     def dominant(self, i):
-        # the routed launch of the step, alone (the shared slot is the next
-        # launch's)
+        # the step's gate/up launch, alone
         gu, _ = self.banks[i % self.ncopy]
         j = i % self.logits.shape[0]
-        self.zq.zq_moe_gate_up_route(self.gwt, gu, self.gs, self.E, self.dm, self.dff,
-                                     self.logits[j], self.E, self.top_k, None, self.x, self.ids,
-                                     self.wts, self.qh, self.dh, self.sh)
+        self.zq.zq_moe_gate_up_mixed(self.gwt, gu, self.gs, self.swt, self.sgu, self.dm, self.dff,
+                                     self.logits[j], self.E, self.top_k, self.gates[j:j + 1],
+                                     self.x, self.ids, self.wts, self.qh, self.dh, self.sh)
 
     def value(self, ms):
         return self.step_bytes / (ms * 1e-3) / 1e9, "GB/s"

@@ -242,6 +242,167 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   }
 }
 
+// The weighted sum over experts with the experts spread over the lanes:
+// for rows of LPR units (k = 64 * LPR, one pass), a wave holds 64 / LPR
+// slots side by side, lane = (slot, unit), and reduces over all 64 lanes,
+// so the selected experts' rows are requested together instead of one
+// expert after another.  Slots beyond 64 / LPR take further rounds.  Each
+// lane folds its slot's weight into its partial; a lane whose expert id is
+// out of range contributes nothing and reports ZQ_ERANGE.
+//
+// SWT (ZQ_Q4_0 / ZQ_Q8_0, or 0 for none): the shared expert a.w2 in a
+// block format joins the same reduction: for each row step t, 64 / RB lanes
+// take the row's k / 32 blocks against slot n_sel's activation, weighted by
+// wts[n_sel].
+template <int WT, int LPR, int RB, int SWT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void dmmv_k_wsum_kernel(
+    const DmmvArgs a) {
+  constexpr int SL = 64 / LPR;
+  constexpr int NWD = KQ<WT>::NWD;
+  constexpr int LS = 64 / RB;                       // shared: lanes per row step
+  constexpr int NBK = 2 * LPR;                      // blocks per row
+  constexpr int BS = (NBK + LS - 1) / LS;           // shared: blocks per lane
+  const int lane = static_cast<int>(threadIdx.x & 63);
+  const int j = lane & (LPR - 1);
+  const int sl = lane / LPR;
+  const int p = j & 3;
+  const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
+  const int64_t n_waves = (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 6;
+  const int n_rounds = (a.n_sel + SL - 1) / SL;
+
+  KUnitAct act[1];
+  const bool hoist = n_rounds == 1;
+  if (hoist && a.n_sel > 0) {
+    load_unit_act<WT, LPR, 1>(act, a, sl < a.n_sel ? sl : a.n_sel - 1, 0, j, LPR);
+  }
+  for (int64_t gi = wave; gi < a.n_groups; gi += n_waves) {
+    const int64_t row0 = gi * RB;
+    float acc[RB];
+#pragma unroll
+    for (int t = 0; t < RB; ++t) acc[t] = 0.0f;
+    for (int r = 0; r < n_rounds; ++r) {
+      const int s = r * SL + sl;
+      const bool in = s < a.n_sel;
+      const int sc = in ? s : a.n_sel - 1;
+      const int e = a.ids[sc] - a.id_base;
+      const bool ok = in && e >= 0 && e < a.n_experts;
+      if (in && !ok && a.status) *a.status = ZQ_ERANGE;
+      const float ws = a.wts[sc];
+      const uint8_t *wb = a.w + static_cast<int64_t>(ok ? e : 0) * a.expert_stride;
+      if (!hoist) load_unit_act<WT, LPR, 1>(act, a, sc, 0, j, LPR);
+      uint32_t v[RB][NWD];
+#pragma unroll
+      for (int t = 0; t < RB; ++t) {
+        int64_t row = row0 + t;
+        row = row < a.rows ? row : a.rows - 1;
+        load_unit_w<WT>(wb + row * a.row_bytes + static_cast<int64_t>(j >> 2) * KQ<WT>::BYTES, p,
+                        v[t]);
+      }
+      finish_act<WT, LPR, 1>(act, a, 0, j, LPR);
+#pragma unroll
+      for (int t = 0; t < RB; ++t) {
+        int32_t is[4];
+        const float part = unit_dot<WT>(v[t], p, act[0], is);
+        acc[t] = ok ? __builtin_fmaf(ws, part, acc[t]) : acc[t];
+      }
+    }
+    if constexpr (SWT != 0) {
+      constexpr int NW = Blk<SWT>::NW;
+      const int st = lane / LS;  // the lane's row step
+      const int c = lane % LS;
+      int64_t row = row0 + st;
+      row = row < a.rows ? row : a.rows - 1;
+      uint32_t win[BS][NW];
+      uint32_t off[BS];
+#pragma unroll
+      for (int i = 0; i < BS; ++i) {
+        int b = c + LS * i;
+        b = b < NBK ? b : NBK - 1;
+        off[i] = load_window<SWT>(a.w2 + row * a.row_bytes2 + static_cast<int64_t>(b) * Blk<SWT>::BYTES,
+                                  win[i]);
+      }
+      const int8_t *qx = a.qx + static_cast<int64_t>(a.n_sel) * a.x_stride;
+      const float *dx = a.dx + static_cast<int64_t>(a.n_sel) * (a.x_stride / 32);
+      const int32_t *sx = a.sx ? a.sx + static_cast<int64_t>(a.n_sel) * (a.x_stride / 32) : nullptr;
+      const float wsh = a.wts[a.n_sel];
+      float part = 0.0f;
+#pragma unroll
+      for (int i = 0; i < BS; ++i) {
+        const int b = c + LS * i;
+        if (b < NBK) {
+          uint32_t xq[8];
+          const u32x4 v0 = *reinterpret_cast<const u32x4 *>(qx + 32 * b);
+          const u32x4 v1 = *reinterpret_cast<const u32x4 *>(qx + 32 * b + 16);
+          xq[0] = v0.x; xq[1] = v0.y; xq[2] = v0.z; xq[3] = v0.w;
+          xq[4] = v1.x; xq[5] = v1.y; xq[6] = v1.z; xq[7] = v1.w;
+          const float dw = window_scale(win[i][0], off[i]);
+          const uint32_t sel = quant_selector(off[i]);
+          int32_t isum;
+          if constexpr (SWT == ZQ_Q4_0) {
+            const int32_t sum = sx ? sx[b] : code_sum(xq, 8);
+            isum = q4_raw_dot(win[i], sel, xq) - 8 * sum;
+          } else {
+            isum = q8_dot(win[i], sel, xq);
+          }
+          part = __builtin_fmaf(dw * dx[b], static_cast<float>(isum), part);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < RB; ++t) acc[t] = t == st ? __builtin_fmaf(wsh, part, acc[t]) : acc[t];
+    }
+    using R = RowReduce<64, RB>;
+    float out[R::NOUT];
+    R::run(acc, out);
+    if (R::writer(lane)) {
+#pragma unroll
+      for (int m = 0; m < R::NOUT; ++m) {
+        const int64_t row = row0 + R::rowstep(m, lane);
+        if (row < a.rows) {
+          float *yp = a.y + row;
+          *yp = (a.flags & ZQ_ACCUMULATE) ? *yp + out[m] : out[m];
+        }
+      }
+    }
+  }
+}
+
+template <int WT, int LPR, int RB, int SWT>
+int launch_wsum1(DmmvArgs a, hipStream_t stream) {
+  a.n_groups = (a.rows + RB - 1) / RB;
+  const int64_t blocks = (a.n_groups + 3) / 4;
+  const unsigned grid = static_cast<unsigned>(blocks < 1048576 ? blocks : 1048576);
+  hipLaunchKernelGGL((dmmv_k_wsum_kernel<WT, LPR, RB, SWT>), dim3(grid), dim3(256), 0, stream, a);
+  ZQ_LAUNCH_CHECK();
+  return ZQ_OK;
+}
+
+// Row steps per wave: the largest of 4, 2, 1 that keeps >= 1024 waves.
+template <int WT, int LPR, int SWT>
+int launch_wsum_rb(const DmmvArgs &a, hipStream_t stream) {
+  if ((a.rows + 3) / 4 >= 1024) return launch_wsum1<WT, LPR, 4, SWT>(a, stream);
+  if ((a.rows + 1) / 2 >= 1024) return launch_wsum1<WT, LPR, 2, SWT>(a, stream);
+  return launch_wsum1<WT, LPR, 1, SWT>(a, stream);
+}
+
+// nu = k / 64 of 4, 8, 16 or 32 (wsum_fits).
+template <int WT, int SWT = 0>
+int launch_wsum(int nu, const DmmvArgs &a, hipStream_t stream) {
+  if (nu == 4) return launch_wsum_rb<WT, 4, SWT>(a, stream);
+  if (nu == 8) return launch_wsum_rb<WT, 8, SWT>(a, stream);
+  if (nu == 16) return launch_wsum_rb<WT, 16, SWT>(a, stream);
+  return launch_wsum_rb<WT, 32, SWT>(a, stream);
+}
+
+template <int WT>
+int launch_wsum_shared(int sh_wtype, int nu, DmmvArgs a, hipStream_t stream) {
+  a.row_bytes = static_cast<int64_t>(a.nb / 8) * KQ<WT>::BYTES;
+  a.row_bytes2 = static_cast<int64_t>(a.nb) * (sh_wtype == ZQ_Q4_0 ? 18 : 34);
+  if (sh_wtype == ZQ_Q4_0) return launch_wsum<WT, ZQ_Q4_0>(nu, a, stream);
+  return launch_wsum<WT, ZQ_Q8_0>(nu, a, stream);
+}
+
+bool wsum_fits(int nu) { return nu == 4 || nu == 8 || nu == 16 || nu == 32; }
+
 struct KShape {
   int lpr, bpl;
 };
@@ -333,6 +494,7 @@ int launch_kshape(const KShape &sh, int rb, const DmmvArgs &a, hipStream_t strea
 template <int WT>
 int launch_type(int mode, DmmvArgs a, hipStream_t stream) {
   a.row_bytes = static_cast<int64_t>(a.nb / 8) * KQ<WT>::BYTES;
+  if (mode == MODE_WEIGHTED && wsum_fits(a.nb / 2)) return launch_wsum<WT>(a.nb / 2, a, stream);
   const KShape sh = choose_kshape(a.nb / 2);
   const int64_t slots = mode == MODE_GATHER ? a.n_sel : 1;
   const int rb = choose_krb<WT>(sh, a.rows, mode, slots);
@@ -345,6 +507,24 @@ int launch_type(int mode, DmmvArgs a, hipStream_t stream) {
 }
 
 }  // namespace
+
+bool dmmv_k_wsum_shared_fits(int wtype, int sh_wtype, int64_t k) {
+  return (wtype == ZQ_Q4_K || wtype == ZQ_Q5_K || wtype == ZQ_Q6_K) &&
+         (sh_wtype == ZQ_Q4_0 || sh_wtype == ZQ_Q8_0) && k % 64 == 0 &&
+         wsum_fits(static_cast<int>(k / 64));
+}
+
+int launch_dmmv_k_wsum_shared(int wtype, int sh_wtype, DmmvArgs a, hipStream_t stream) {
+  if (a.rows == 0) return ZQ_OK;
+  if (!a.w2 || !dmmv_k_wsum_shared_fits(wtype, sh_wtype, static_cast<int64_t>(a.nb) * 32))
+    return ZQ_EINVAL;
+  const int nu = a.nb / 2;
+  switch (wtype) {
+    case ZQ_Q4_K: return launch_wsum_shared<ZQ_Q4_K>(sh_wtype, nu, a, stream);
+    case ZQ_Q5_K: return launch_wsum_shared<ZQ_Q5_K>(sh_wtype, nu, a, stream);
+    default: return launch_wsum_shared<ZQ_Q6_K>(sh_wtype, nu, a, stream);
+  }
+}
 
 int launch_dmmv_k(int wtype, int mode, DmmvArgs a, hipStream_t stream) {
   if (a.rows == 0) return ZQ_OK;

@@ -16,6 +16,8 @@
 // activations staged in LDS.  The per-expert weight multiplies each expert's
 // partial before the single lane reduction, so the weighted accumulate costs
 // one FMA per expert and lane.
+#include <type_traits>
+
 #include "zq_common.h"
 #include "zq_internal.h"
 #include "zq_kquant.h"
@@ -49,6 +51,9 @@ template <bool ROUTED, int T>
 __device__ __forceinline__ int gu_expert(const MoeGateUpArgs &a, int tid, int s, int32_t *rsel,
                                          float *rselv) {
   if constexpr (ROUTED) {
+    // the shared slot's workgroups need no ranking (the publication is
+    // slot 0's)
+    if (s >= a.top_k) return a.n_routed;  // uniform over the workgroup
     __shared__ float rlv[1024];
     for (int i = tid; i < a.n_routed; i += T) rlv[i] = route_key(a.logits[i]);
     __syncthreads();
@@ -137,28 +142,207 @@ __device__ __forceinline__ void gu_epilogue(const MoeGateUpArgs &a, int tid, int
   }
 }
 
-template <int WT, int LPR, int BPL, int RB, bool ROUTED>
-__global__ __launch_bounds__(1024) void moe_gate_up_kernel(const MoeGateUpArgs a) {
-  constexpr int WPB = 16;
-  constexpr int S = 64 / LPR;
-  constexpr int NW = Blk<WT>::NW;
-  constexpr int BB = Blk<WT>::BYTES;
-  constexpr int T = 64 * WPB;
-  static_assert(RB * S * WPB == 64, "a workgroup computes 32 gate + 32 up rows");
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  int8_t *lq = reinterpret_cast<int8_t *>(smem);                     // [k]
-  float *ld = reinterpret_cast<float *>(smem + a.k);                 // [nb]
-  int32_t *ls8 = reinterpret_cast<int32_t *>(smem + a.k + 4 * a.nb);  // [nb]
-  float *lrow = reinterpret_cast<float *>(smem + a.k + 8 * a.nb);     // [64] gate | up
+// The 64 rows of one gate/up workgroup in the block formats (Q4_0 / Q8_0):
+// LPR lanes per row, BPL blocks per lane, RB row steps per wave, 16 waves.
+// load() issues the weight windows; rows() takes the activation from LDS
+// (codes, scales and SUMX times the block sums) and leaves the 64 row
+// results in lrow.
+template <int WT, int LPR, int BPL, int RB>
+struct GuBlockRows {
+  static constexpr int S = 64 / LPR;
+  static constexpr int NW = Blk<WT>::NW;
+  static constexpr int BB = Blk<WT>::BYTES;
+  static constexpr int SUMX = 8;  // the Q4_0 dot subtracts 8 times the code sum
+  static_assert(RB * S * 16 == 64, "a workgroup computes 32 gate + 32 up rows");
+  uint32_t win[RB][BPL][NW];
+  uint32_t off[RB][BPL];
 
+  __device__ __forceinline__ void load(const MoeGateUpArgs &a, const uint8_t *wb,
+                                       int64_t row_bytes, int hb, int tid) {
+    const int lane = tid & 63, wv = tid >> 6;
+    const int j = lane & (LPR - 1), slot = lane / LPR;
+#pragma unroll
+    for (int t = 0; t < RB; ++t) {
+      const int64_t row = gu_row(a, hb, wv * (RB * S) + t * S + slot);
+#pragma unroll
+      for (int i = 0; i < BPL; ++i) {
+        int b = j + LPR * i;
+        b = b < a.nb ? b : a.nb - 1;
+        off[t][i] = load_window<WT>(wb + row * row_bytes + static_cast<int64_t>(b) * BB, win[t][i]);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void rows(const MoeGateUpArgs &a, const int8_t *lq, const float *ld,
+                                       const int32_t *ls, float *lrow, int tid) {
+    const int lane = tid & 63, wv = tid >> 6;
+    const int j = lane & (LPR - 1), slot = lane / LPR;
+    uint32_t xq[BPL][8];
+    float xd[BPL];
+    int32_t xs8[BPL];
+#pragma unroll
+    for (int i = 0; i < BPL; ++i) {
+      const int b = j + LPR * i;
+      if (b < a.nb) {
+        const u32x4 v0 = *reinterpret_cast<const u32x4 *>(lq + 32 * b);
+        const u32x4 v1 = *reinterpret_cast<const u32x4 *>(lq + 32 * b + 16);
+        xq[i][0] = v0.x; xq[i][1] = v0.y; xq[i][2] = v0.z; xq[i][3] = v0.w;
+        xq[i][4] = v1.x; xq[i][5] = v1.y; xq[i][6] = v1.z; xq[i][7] = v1.w;
+        xd[i] = ld[b];
+        xs8[i] = WT == ZQ_Q4_0 ? ls[b] : 0;
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) xq[i][k] = 0;
+        xd[i] = 0.0f;
+        xs8[i] = 0;
+      }
+    }
+    float acc[RB];
+#pragma unroll
+    for (int t = 0; t < RB; ++t) {
+      float p = 0.0f;
+#pragma unroll
+      for (int i = 0; i < BPL; ++i) {
+        const float dw = window_scale(win[t][i][0], off[t][i]);
+        const uint32_t sel = quant_selector(off[t][i]);
+        int32_t isum;
+        if constexpr (WT == ZQ_Q4_0) {
+          isum = q4_raw_dot(win[t][i], sel, xq[i]) - xs8[i];
+        } else {
+          isum = q8_dot(win[t][i], sel, xq[i]);
+        }
+        p = __builtin_fmaf(dw * xd[i], static_cast<float>(isum), p);
+      }
+      acc[t] = p;
+    }
+    using R = RowReduce<LPR, RB>;
+    float res[R::NOUT];
+    R::run(acc, res);
+    if (R::writer(lane)) {
+#pragma unroll
+      for (int m = 0; m < R::NOUT; ++m) lrow[wv * (RB * S) + R::rowstep(m, lane) * S + slot] = res[m];
+    }
+  }
+};
+
+// The same for the K-quants: one lane per 64-element unit, the row in one
+// pass (k = 64 * LPR), against the activation staged in LDS with plain code
+// sums.
+template <int WT, int LPR, int RB>
+struct GuKRows {
+  static constexpr int S = 64 / LPR;
+  static constexpr int NWD = KQ<WT>::NWD;
+  static constexpr int SUMX = 1;
+  static_assert(RB * S * 16 == 64, "a workgroup computes 32 gate + 32 up rows");
+  uint32_t v[RB][NWD];
+
+  __device__ __forceinline__ void load(const MoeGateUpArgs &a, const uint8_t *wb,
+                                       int64_t row_bytes, int hb, int tid) {
+    const int lane = tid & 63, wv = tid >> 6;
+    const int j = lane & (LPR - 1), slot = lane / LPR;
+#pragma unroll
+    for (int t = 0; t < RB; ++t) {
+      const int64_t row = gu_row(a, hb, wv * (RB * S) + t * S + slot);
+      load_unit_w<WT>(wb + row * row_bytes + static_cast<int64_t>(j >> 2) * KQ<WT>::BYTES, j & 3,
+                      v[t]);
+    }
+  }
+
+  __device__ __forceinline__ void rows(const MoeGateUpArgs &a, const int8_t *lq, const float *ld,
+                                       const int32_t *ls, float *lrow, int tid) {
+    (void)a;
+    const int lane = tid & 63, wv = tid >> 6;
+    const int j = lane & (LPR - 1), slot = lane / LPR;
+    KUnitAct act;
+    if constexpr (WT == ZQ_Q6_K) {
+      const int base = 256 * (j >> 2) + 128 * ((j >> 1) & 1) + 16 * (j & 1);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const u32x4 q = *reinterpret_cast<const u32x4 *>(lq + base + 32 * c);
+        act.q[4 * c] = q.x; act.q[4 * c + 1] = q.y; act.q[4 * c + 2] = q.z; act.q[4 * c + 3] = q.w;
+        act.d[c] = ld[(base + 32 * c) >> 5];
+        act.m32[c] = -32 * code_sum(&act.q[4 * c], 4);
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const u32x4 q = *reinterpret_cast<const u32x4 *>(lq + 64 * j + 16 * c);
+        act.q[4 * c] = q.x; act.q[4 * c + 1] = q.y; act.q[4 * c + 2] = q.z; act.q[4 * c + 3] = q.w;
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        act.d[h] = ld[2 * j + h];
+        act.fs[h] = static_cast<float>(ls[2 * j + h]);
+      }
+    }
+    float acc[RB];
+#pragma unroll
+    for (int t = 0; t < RB; ++t) {
+      int32_t is[4];
+      acc[t] = unit_dot<WT>(v[t], j & 3, act, is);
+    }
+    using R = RowReduce<LPR, RB>;
+    float res[R::NOUT];
+    R::run(acc, res);
+    if (R::writer(lane)) {
+#pragma unroll
+      for (int m = 0; m < R::NOUT; ++m) lrow[wv * (RB * S) + R::rowstep(m, lane) * S + slot] = res[m];
+    }
+  }
+};
+
+// The row layouts per d_model: 64 rows per 16-wave workgroup, one pass.
+template <int WT, int NB> struct GuRowsFor;
+template <int WT> struct GuRowsFor<WT, 16> { using type = GuBlockRows<WT, 16, 1, 1>; };
+template <int WT> struct GuRowsFor<WT, 32> { using type = GuBlockRows<WT, 32, 1, 2>; };
+template <int WT> struct GuRowsFor<WT, 64> { using type = GuBlockRows<WT, 64, 1, 4>; };
+template <int WT> struct GuRowsFor<WT, 128> { using type = GuBlockRows<WT, 64, 2, 4>; };
+template <int WT, int NB> struct GuKRowsFor;
+template <int WT> struct GuKRowsFor<WT, 32> { using type = GuKRows<WT, 16, 1>; };
+template <int WT> struct GuKRowsFor<WT, 64> { using type = GuKRows<WT, 32, 2>; };
+template <int WT> struct GuKRowsFor<WT, 128> { using type = GuKRows<WT, 64, 4>; };
+
+// LDS of a gate/up workgroup: x codes [k], scales [nb], sums [nb], then the
+// 64 row results.
+struct GuLds {
+  int8_t *lq;
+  float *ld;
+  int32_t *ls;
+  float *lrow;
+  __device__ __forceinline__ GuLds(uint8_t *smem, const MoeGateUpArgs &a)
+      : lq(reinterpret_cast<int8_t *>(smem)),
+        ld(reinterpret_cast<float *>(smem + a.k)),
+        ls(reinterpret_cast<int32_t *>(smem + a.k + 4 * a.nb)),
+        lrow(reinterpret_cast<float *>(smem + a.k + 8 * a.nb)) {}
+};
+
+// One workgroup of the gate/up pass after its expert is known: issue the
+// weights, quantize x into LDS meanwhile, the 64 rows, the epilogue.
+template <class Rows, bool ROUTED>
+__device__ __forceinline__ void gu_run(const MoeGateUpArgs &a, const uint8_t *wb,
+                                       int64_t row_bytes, float (&xv)[16], const GuLds &L,
+                                       int tid, int s, int hb, const int32_t *rsel,
+                                       const float *rselv) {
+  constexpr int T = 1024;
+  Rows r;
+  r.load(a, wb, row_bytes, hb, tid);
+  gu_quantize_x<T, Rows::SUMX>(a, tid, xv, L.lq, L.ld, L.ls);
+  __syncthreads();
+  r.rows(a, L.lq, L.ld, L.ls, L.lrow, tid);
+  __syncthreads();
+  gu_epilogue<ROUTED>(a, tid, s, hb, L.lrow, rsel, rselv);
+}
+
+// The gate/up pass over one bank (Rows: GuBlockRows or GuKRows): grid
+// (d_ff / 32, n_sel), 1024 threads.
+template <class Rows, bool ROUTED>
+__global__ __launch_bounds__(1024) void moe_gate_up_kernel(const MoeGateUpArgs a) {
+  constexpr int T = 1024;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const GuLds L(smem, a);
   const int tid = static_cast<int>(threadIdx.x);
-  const int lane = tid & 63;
-  const int wv = tid >> 6;
-  const int j = lane & (LPR - 1);
-  const int slot = lane / LPR;
   const int hb = static_cast<int>(blockIdx.x);  // 32-wide block of the FFN width
   const int s = static_cast<int>(blockIdx.y);   // selected-expert slot
-
   // activation loads, issued before the expert id so that they share its
   // round trip
   float xv[16];
@@ -170,164 +354,33 @@ __global__ __launch_bounds__(1024) void moe_gate_up_kernel(const MoeGateUpArgs a
     if (a.status && tid == 0) *a.status = ZQ_ERANGE;
     return;
   }
-  const uint8_t *wb = a.bank + static_cast<int64_t>(e) * a.expert_stride;
-
-  // weight windows: local rows 0..31 -> gate rows 32*hb.., 32..63 -> up rows
-  uint32_t win[RB][BPL][NW];
-  uint32_t off[RB][BPL];
-#pragma unroll
-  for (int t = 0; t < RB; ++t) {
-    const int64_t row = gu_row(a, hb, wv * (RB * S) + t * S + slot);
-#pragma unroll
-    for (int i = 0; i < BPL; ++i) {
-      int b = j + LPR * i;
-      b = b < a.nb ? b : a.nb - 1;
-      off[t][i] = load_window<WT>(wb + row * a.row_bytes + static_cast<int64_t>(b) * BB, win[t][i]);
-    }
-  }
-
-  gu_quantize_x<T, 8>(a, tid, xv, lq, ld, ls8);
-  __syncthreads();
-
-  uint32_t xq[BPL][8];
-  float xd[BPL];
-  int32_t xs8[BPL];
-#pragma unroll
-  for (int i = 0; i < BPL; ++i) {
-    const int b = j + LPR * i;
-    if (b < a.nb) {
-      const u32x4 v0 = *reinterpret_cast<const u32x4 *>(lq + 32 * b);
-      const u32x4 v1 = *reinterpret_cast<const u32x4 *>(lq + 32 * b + 16);
-      xq[i][0] = v0.x; xq[i][1] = v0.y; xq[i][2] = v0.z; xq[i][3] = v0.w;
-      xq[i][4] = v1.x; xq[i][5] = v1.y; xq[i][6] = v1.z; xq[i][7] = v1.w;
-      xd[i] = ld[b];
-      xs8[i] = WT == ZQ_Q4_0 ? ls8[b] : 0;
-    } else {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) xq[i][k] = 0;
-      xd[i] = 0.0f;
-      xs8[i] = 0;
-    }
-  }
-  float acc[RB];
-#pragma unroll
-  for (int t = 0; t < RB; ++t) {
-    float p = 0.0f;
-#pragma unroll
-    for (int i = 0; i < BPL; ++i) {
-      const float dw = window_scale(win[t][i][0], off[t][i]);
-      const uint32_t sel = quant_selector(off[t][i]);
-      int32_t isum;
-      if constexpr (WT == ZQ_Q4_0) {
-        isum = q4_raw_dot(win[t][i], sel, xq[i]) - xs8[i];
-      } else {
-        isum = q8_dot(win[t][i], sel, xq[i]);
-      }
-      p = __builtin_fmaf(dw * xd[i], static_cast<float>(isum), p);
-    }
-    acc[t] = p;
-  }
-  using R = RowReduce<LPR, RB>;
-  float res[R::NOUT];
-  R::run(acc, res);
-  if (R::writer(lane)) {
-#pragma unroll
-    for (int m = 0; m < R::NOUT; ++m) {
-      const int lr = wv * (RB * S) + R::rowstep(m, lane) * S + slot;
-      lrow[lr] = res[m];
-    }
-  }
-  __syncthreads();
-  gu_epilogue<ROUTED>(a, tid, s, hb, lrow, rsel, rselv);
+  gu_run<Rows, ROUTED>(a, a.bank + static_cast<int64_t>(e) * a.expert_stride, a.row_bytes, xv, L,
+                       tid, s, hb, rsel, rselv);
 }
 
-// The K-quant form: the same workgroup and epilogue, with the weights read
-// as K-quant units (one lane per 64-element unit, LPR lanes per row, the row
-// in one pass: k/64 == LPR) against the activation staged in LDS.
-template <int WT, int LPR, int RB, bool ROUTED>
-__global__ __launch_bounds__(1024) void moe_gate_up_k_kernel(const MoeGateUpArgs a) {
-  constexpr int WPB = 16;
-  constexpr int S = 64 / LPR;
-  constexpr int T = 64 * WPB;
-  constexpr int NWD = KQ<WT>::NWD;
-  static_assert(RB * S * WPB == 64, "a workgroup computes 32 gate + 32 up rows");
+// Routed experts and a shared expert of another format in one launch, the
+// router folded in: slots 0..top_k-1 (Rows over a.bank) take the experts
+// the workgroups rank; slot top_k (SRows over a.bank2, one matrix) is the
+// shared expert.  grid (d_ff / 32, top_k + 1).
+template <class Rows, class SRows>
+__global__ __launch_bounds__(1024) void moe_gate_up_mix_kernel(const MoeGateUpArgs a) {
+  constexpr int T = 1024;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  int8_t *lq = reinterpret_cast<int8_t *>(smem);                     // [k]
-  float *ld = reinterpret_cast<float *>(smem + a.k);                 // [nb]
-  int32_t *ls = reinterpret_cast<int32_t *>(smem + a.k + 4 * a.nb);   // [nb] code sums
-  float *lrow = reinterpret_cast<float *>(smem + a.k + 8 * a.nb);     // [64] gate | up
-
+  const GuLds L(smem, a);
   const int tid = static_cast<int>(threadIdx.x);
-  const int lane = tid & 63;
-  const int wv = tid >> 6;
-  const int j = lane & (LPR - 1);   // the lane's unit of every row (single pass)
-  const int slot = lane / LPR;
-  const int p = j & 3;
   const int hb = static_cast<int>(blockIdx.x);
   const int s = static_cast<int>(blockIdx.y);
-
   float xv[16];
   gu_load_x(a, tid, xv);
   __shared__ int32_t rsel[64];
   __shared__ float rselv[64];
-  const int e = gu_expert<ROUTED, T>(a, tid, s, rsel, rselv);
-  if (e < 0 || e >= a.n_experts) {  // uniform over the workgroup
-    if (a.status && tid == 0) *a.status = ZQ_ERANGE;
-    return;
-  }
-  const uint8_t *wb = a.bank + static_cast<int64_t>(e) * a.expert_stride;
-
-  uint32_t v[RB][NWD];
-#pragma unroll
-  for (int t = 0; t < RB; ++t) {
-    const int64_t row = gu_row(a, hb, wv * (RB * S) + t * S + slot);
-    load_unit_w<WT>(wb + row * a.row_bytes + static_cast<int64_t>(j >> 2) * KQ<WT>::BYTES, p, v[t]);
-  }
-
-  gu_quantize_x<T, 1>(a, tid, xv, lq, ld, ls);
-  __syncthreads();
-
-  // the lane's unit of the activation, from LDS
-  KUnitAct act;
-  if constexpr (WT == ZQ_Q6_K) {
-    const int base = 256 * (j >> 2) + 128 * ((j >> 1) & 1) + 16 * (j & 1);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const u32x4 q = *reinterpret_cast<const u32x4 *>(lq + base + 32 * c);
-      act.q[4 * c] = q.x; act.q[4 * c + 1] = q.y; act.q[4 * c + 2] = q.z; act.q[4 * c + 3] = q.w;
-      act.d[c] = ld[(base + 32 * c) >> 5];
-      act.m32[c] = -32 * code_sum(&act.q[4 * c], 4);
-    }
+  const int e = gu_expert<true, T>(a, tid, s, rsel, rselv);
+  if (s < a.top_k) {  // uniform over the workgroup; e in [0, n_routed)
+    gu_run<Rows, true>(a, a.bank + static_cast<int64_t>(e) * a.expert_stride, a.row_bytes, xv, L,
+                       tid, s, hb, rsel, rselv);
   } else {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const u32x4 q = *reinterpret_cast<const u32x4 *>(lq + 64 * j + 16 * c);
-      act.q[4 * c] = q.x; act.q[4 * c + 1] = q.y; act.q[4 * c + 2] = q.z; act.q[4 * c + 3] = q.w;
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      act.d[h] = ld[2 * j + h];
-      act.fs[h] = static_cast<float>(ls[2 * j + h]);
-    }
+    gu_run<SRows, true>(a, a.bank2, a.row_bytes2, xv, L, tid, s, hb, rsel, rselv);
   }
-  float acc[RB];
-#pragma unroll
-  for (int t = 0; t < RB; ++t) {
-    int32_t is[4];
-    acc[t] = unit_dot<WT>(v[t], p, act, is);
-  }
-  using R = RowReduce<LPR, RB>;
-  float res[R::NOUT];
-  R::run(acc, res);
-  if (R::writer(lane)) {
-#pragma unroll
-    for (int m = 0; m < R::NOUT; ++m) {
-      const int lr = wv * (RB * S) + R::rowstep(m, lane) * S + slot;
-      lrow[lr] = res[m];
-    }
-  }
-  __syncthreads();
-  gu_epilogue<ROUTED>(a, tid, s, hb, lrow, rsel, rselv);
 }
 
 // ---------------------------------------------------------------- down -----
@@ -490,14 +543,17 @@ __global__ __launch_bounds__(64 * WPB) void moe_down_kernel(const MoeDownArgs a)
 
 namespace {
 
-template <int WT, int LPR, int BPL, int RB>
+size_t gu_lds(const MoeGateUpArgs &a) {
+  return static_cast<size_t>(a.k) + 8 * static_cast<size_t>(a.nb) + 64 * 4;
+}
+
+template <class Rows>
 int launch_gu(const MoeGateUpArgs &a, hipStream_t stream) {
-  const size_t lds = static_cast<size_t>(a.k) + 8 * static_cast<size_t>(a.nb) + 64 * 4;
   const dim3 grid(static_cast<unsigned>(a.d_ff / 32), static_cast<unsigned>(a.n_sel));
   if (a.logits)
-    hipLaunchKernelGGL((moe_gate_up_kernel<WT, LPR, BPL, RB, true>), grid, dim3(1024), lds, stream, a);
+    hipLaunchKernelGGL((moe_gate_up_kernel<Rows, true>), grid, dim3(1024), gu_lds(a), stream, a);
   else
-    hipLaunchKernelGGL((moe_gate_up_kernel<WT, LPR, BPL, RB, false>), grid, dim3(1024), lds, stream, a);
+    hipLaunchKernelGGL((moe_gate_up_kernel<Rows, false>), grid, dim3(1024), gu_lds(a), stream, a);
   ZQ_LAUNCH_CHECK();
   return ZQ_OK;
 }
@@ -505,30 +561,68 @@ int launch_gu(const MoeGateUpArgs &a, hipStream_t stream) {
 template <int WT>
 int launch_gu_w(const MoeGateUpArgs &a, hipStream_t stream) {
   // single-pass layouts with 64 rows per 16-wave workgroup
-  if (a.nb <= 16) return launch_gu<WT, 16, 1, 1>(a, stream);
-  if (a.nb <= 32) return launch_gu<WT, 32, 1, 2>(a, stream);
-  if (a.nb <= 64) return launch_gu<WT, 64, 1, 4>(a, stream);
-  return launch_gu<WT, 64, 2, 4>(a, stream);  // nb <= 128 (moe_gate_up_fits)
-}
-
-template <int WT, int LPR, int RB>
-int launch_gu_k(const MoeGateUpArgs &a, hipStream_t stream) {
-  const size_t lds = static_cast<size_t>(a.k) + 8 * static_cast<size_t>(a.nb) + 64 * 4;
-  const dim3 grid(static_cast<unsigned>(a.d_ff / 32), static_cast<unsigned>(a.n_sel));
-  if (a.logits)
-    hipLaunchKernelGGL((moe_gate_up_k_kernel<WT, LPR, RB, true>), grid, dim3(1024), lds, stream, a);
-  else
-    hipLaunchKernelGGL((moe_gate_up_k_kernel<WT, LPR, RB, false>), grid, dim3(1024), lds, stream, a);
-  ZQ_LAUNCH_CHECK();
-  return ZQ_OK;
+  if (a.nb <= 16) return launch_gu<GuBlockRows<WT, 16, 1, 1>>(a, stream);
+  if (a.nb <= 32) return launch_gu<GuBlockRows<WT, 32, 1, 2>>(a, stream);
+  if (a.nb <= 64) return launch_gu<GuBlockRows<WT, 64, 1, 4>>(a, stream);
+  return launch_gu<GuBlockRows<WT, 64, 2, 4>>(a, stream);  // nb <= 128 (moe_gate_up_fits)
 }
 
 template <int WT>
 int launch_gu_k_w(const MoeGateUpArgs &a, hipStream_t stream) {
   // one 64-element unit per lane, the row in one pass (k = 64 * LPR)
-  if (a.k == 1024) return launch_gu_k<WT, 16, 1>(a, stream);
-  if (a.k == 2048) return launch_gu_k<WT, 32, 2>(a, stream);
-  return launch_gu_k<WT, 64, 4>(a, stream);  // k == 4096 (moe_gate_up_k_fits)
+  if (a.k == 1024) return launch_gu<GuKRows<WT, 16, 1>>(a, stream);
+  if (a.k == 2048) return launch_gu<GuKRows<WT, 32, 2>>(a, stream);
+  return launch_gu<GuKRows<WT, 64, 4>>(a, stream);  // k == 4096 (moe_gate_up_k_fits)
+}
+
+// The mixed launch: the row layouts of both formats at this d_model.
+template <int WT, int NB>
+using GuAnyRows = typename std::conditional<(WT == ZQ_Q4_0 || WT == ZQ_Q8_0), GuRowsFor<WT, NB>,
+                                            GuKRowsFor<WT, NB>>::type::type;
+
+template <class Rows, class SRows>
+int launch_gu_mix(const MoeGateUpArgs &a, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>(a.d_ff / 32), static_cast<unsigned>(a.top_k + 1));
+  hipLaunchKernelGGL((moe_gate_up_mix_kernel<Rows, SRows>), grid, dim3(1024), gu_lds(a), stream, a);
+  ZQ_LAUNCH_CHECK();
+  return ZQ_OK;
+}
+
+template <int NB, int WT>
+int gu_mix_shared(int sh_wtype, const MoeGateUpArgs &a, hipStream_t stream) {
+  using R = GuAnyRows<WT, NB>;
+  switch (sh_wtype) {
+    case ZQ_Q4_0: return launch_gu_mix<R, GuAnyRows<ZQ_Q4_0, NB>>(a, stream);
+    case ZQ_Q8_0: return launch_gu_mix<R, GuAnyRows<ZQ_Q8_0, NB>>(a, stream);
+    case ZQ_Q4_K: return launch_gu_mix<R, GuAnyRows<ZQ_Q4_K, NB>>(a, stream);
+    case ZQ_Q5_K: return launch_gu_mix<R, GuAnyRows<ZQ_Q5_K, NB>>(a, stream);
+    case ZQ_Q6_K: return launch_gu_mix<R, GuAnyRows<ZQ_Q6_K, NB>>(a, stream);
+    default: return ZQ_EINVAL;
+  }
+}
+
+template <int NB>
+int gu_mix_routed(int wtype, int sh_wtype, const MoeGateUpArgs &a, hipStream_t stream) {
+  switch (wtype) {
+    case ZQ_Q4_0: return gu_mix_shared<NB, ZQ_Q4_0>(sh_wtype, a, stream);
+    case ZQ_Q8_0: return gu_mix_shared<NB, ZQ_Q8_0>(sh_wtype, a, stream);
+    case ZQ_Q4_K: return gu_mix_shared<NB, ZQ_Q4_K>(sh_wtype, a, stream);
+    case ZQ_Q5_K: return gu_mix_shared<NB, ZQ_Q5_K>(sh_wtype, a, stream);
+    case ZQ_Q6_K: return gu_mix_shared<NB, ZQ_Q6_K>(sh_wtype, a, stream);
+    default: return ZQ_EINVAL;
+  }
+}
+
+// Bytes of one row of k elements in wtype.
+int64_t gu_row_bytes(int wtype, int64_t k) {
+  switch (wtype) {
+    case ZQ_Q4_0: return (k / 32) * 18;
+    case ZQ_Q8_0: return (k / 32) * 34;
+    case ZQ_Q4_K: return (k / 256) * KQ<ZQ_Q4_K>::BYTES;
+    case ZQ_Q5_K: return (k / 256) * KQ<ZQ_Q5_K>::BYTES;
+    case ZQ_Q6_K: return (k / 256) * KQ<ZQ_Q6_K>::BYTES;
+    default: return -1;
+  }
 }
 
 template <int WT, int LPR, int BPL>
@@ -578,15 +672,27 @@ bool moe_gate_up_k_fits(int64_t d_model) {
 int launch_moe_gate_up_k(int wtype, MoeGateUpArgs a, hipStream_t stream) {
   if (a.n_sel == 0 || a.d_ff == 0) return ZQ_OK;
   a.nb = static_cast<int32_t>(a.k / 32);
+  a.row_bytes = gu_row_bytes(wtype, a.k);
   switch (wtype) {
-    case ZQ_Q4_K: a.row_bytes = static_cast<int64_t>(a.k / 256) * KQ<ZQ_Q4_K>::BYTES;
-                  return launch_gu_k_w<ZQ_Q4_K>(a, stream);
-    case ZQ_Q5_K: a.row_bytes = static_cast<int64_t>(a.k / 256) * KQ<ZQ_Q5_K>::BYTES;
-                  return launch_gu_k_w<ZQ_Q5_K>(a, stream);
-    case ZQ_Q6_K: a.row_bytes = static_cast<int64_t>(a.k / 256) * KQ<ZQ_Q6_K>::BYTES;
-                  return launch_gu_k_w<ZQ_Q6_K>(a, stream);
+    case ZQ_Q4_K: return launch_gu_k_w<ZQ_Q4_K>(a, stream);
+    case ZQ_Q5_K: return launch_gu_k_w<ZQ_Q5_K>(a, stream);
+    case ZQ_Q6_K: return launch_gu_k_w<ZQ_Q6_K>(a, stream);
     default: return ZQ_EINVAL;
   }
+}
+
+// (at d_model 4096 the two layouts together would spill registers)
+bool moe_gate_up_mix_fits(int64_t d_model) { return d_model == 1024 || d_model == 2048; }
+
+int launch_moe_gate_up_mix(int wtype, int sh_wtype, MoeGateUpArgs a, hipStream_t stream) {
+  if (a.d_ff == 0) return ZQ_OK;
+  a.nb = static_cast<int32_t>(a.k / 32);
+  a.n_sel = a.top_k + 1;
+  a.row_bytes = gu_row_bytes(wtype, a.k);
+  a.row_bytes2 = gu_row_bytes(sh_wtype, a.k);
+  if (a.row_bytes < 0 || a.row_bytes2 < 0 || !a.logits || !a.bank2) return ZQ_EINVAL;
+  if (a.nb == 32) return gu_mix_routed<32>(wtype, sh_wtype, a, stream);
+  return gu_mix_routed<64>(wtype, sh_wtype, a, stream);  // nb == 64 (moe_gate_up_mix_fits)
 }
 
 int launch_moe_down(int wtype, MoeDownArgs a, hipStream_t stream) {

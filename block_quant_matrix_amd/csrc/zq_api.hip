@@ -582,6 +582,44 @@ int zq_moe_gate_up_route(int wtype, const void *gu_bank, int64_t gu_stride_bytes
   return launch_gate_up(wtype, a, S(stream));
 }
 
+int zq_moe_gate_up_mixed(int gu_wtype, const void *gu_bank, int64_t gu_stride_bytes,
+                         int sh_wtype, const void *sh_gu, int64_t d_model, int64_t d_ff,
+                         const float *logits, int32_t n_routed, int32_t top_k,
+                         const float *shared_gate, const float *x, int32_t *ids, float *wts,
+                         int8_t *qh, float *dh, int32_t *sh, void *stream) {
+  ZQ_REQUIRE(matrix_bytes(gu_wtype, 1, 256) > 0 && matrix_bytes(sh_wtype, 1, 256) > 0, ZQ_EINVAL);
+  ZQ_REQUIRE(gu_bank && sh_gu && logits && shared_gate && x && ids && wts && qh && dh, ZQ_ENULL);
+  ZQ_REQUIRE(top_k >= 1 && top_k <= 64 && n_routed >= top_k && n_routed <= 1024, ZQ_EINVAL);
+  ZQ_REQUIRE(zq::moe_gate_up_mix_fits(d_model) && k_ok(d_ff) && d_ff <= (int64_t(1) << 24),
+             ZQ_EINVAL);
+  ZQ_REQUIRE(gu_stride_bytes >= matrix_bytes(gu_wtype, 2 * d_ff, d_model), ZQ_EINVAL);
+  ZQ_REQUIRE(bank_al(gu_wtype, gu_bank, gu_stride_bytes) && bank_al(sh_wtype, sh_gu, 0) &&
+                 al(logits, 4) && al(shared_gate, 4) && al(x, 16) && al(ids, 4) && al(wts, 4) &&
+                 al(qh, 16) && al(dh, 4) && al(sh, 4),
+             ZQ_EALIGN);
+  const int dc = check_current_device();
+  if (dc != ZQ_OK) return dc;
+  zq::MoeGateUpArgs a{};
+  a.bank = static_cast<const uint8_t *>(gu_bank);
+  a.expert_stride = gu_stride_bytes;
+  a.n_experts = n_routed;
+  a.ids = ids;
+  a.x = x;
+  a.k = static_cast<int32_t>(d_model);
+  a.d_ff = static_cast<int32_t>(d_ff);
+  a.qh = qh;
+  a.dh = dh;
+  a.sh = sh;
+  a.logits = logits;
+  a.n_routed = n_routed;
+  a.top_k = top_k;
+  a.shared_gate = shared_gate;
+  a.ids_out = ids;
+  a.wts_out = wts;
+  a.bank2 = static_cast<const uint8_t *>(sh_gu);
+  return zq::launch_moe_gate_up_mix(gu_wtype, sh_wtype, a, S(stream));
+}
+
 int zq_swiglu_quantize(const float *gu, int64_t n, int64_t f, int8_t *qh, float *dh, int32_t *sh,
                        float *h_out, void *stream) {
   ZQ_REQUIRE(gu && qh && dh, ZQ_ENULL);
@@ -911,7 +949,8 @@ int zq_moe_ffn_mixed(int gu_wtype, const void *gu_bank, int64_t gu_stride_bytes,
   if (gate_up_fits(gu_wtype, d_model) && (!shared || gate_up_fits(sh_wtype, d_model))) {
     // fused: the routed experts' gate/up pass ranks the logits itself and
     // publishes ids / wts (the shared slot included); the shared expert
-    // (id n_routed) follows from its own matrix
+    // (id n_routed) runs in the same launch where the two row layouts fit
+    // together, else in a launch of its own
     zq::MoeGateUpArgs a{};
     a.bank = static_cast<const uint8_t *>(gu_bank);
     a.expert_stride = gu_stride_bytes;
@@ -930,9 +969,15 @@ int zq_moe_ffn_mixed(int gu_wtype, const void *gu_bank, int64_t gu_stride_bytes,
     a.shared_gate = shared_gate;
     a.ids_out = ids;
     a.wts_out = wts;
-    rc = launch_gate_up(gu_wtype, a, s);
+    if (shared && zq::moe_gate_up_mix_fits(d_model)) {
+      // both in one launch: slot top_k runs the shared matrix in its format
+      a.bank2 = static_cast<const uint8_t *>(sh_gu);
+      rc = zq::launch_moe_gate_up_mix(gu_wtype, sh_wtype, a, s);
+    } else {
+      rc = launch_gate_up(gu_wtype, a, s);
+    }
     if (rc != ZQ_OK) return rc;
-    if (shared) {
+    if (shared && !zq::moe_gate_up_mix_fits(d_model)) {
       const int64_t h0 = static_cast<int64_t>(top_k) * d_ff;
       zq::MoeGateUpArgs b{};
       b.bank = static_cast<const uint8_t *>(sh_gu);
@@ -967,6 +1012,27 @@ int zq_moe_ffn_mixed(int gu_wtype, const void *gu_bank, int64_t gu_stride_bytes,
     }
     rc = zq::launch_swiglu_quantize(gu, n_sel, d_ff, qh, dh, sh, nullptr, s);
     if (rc != ZQ_OK) return rc;
+  }
+  if (shared && zq::dmmv_k_wsum_shared_fits(down_wtype, sh_wtype, d_ff)) {
+    // K-quant routed down rows and a block-format shared expert: one launch,
+    // one reduction over every term
+    zq::DmmvArgs a{};
+    a.w = static_cast<const uint8_t *>(down_bank);
+    a.qx = qh;
+    a.dx = dh;
+    a.sx = sh;
+    a.y = y;
+    a.ids = ids;
+    a.wts = wts;
+    a.rows = d_model;
+    a.expert_stride = down_stride_bytes;
+    a.x_stride = d_ff;
+    a.nb = static_cast<int32_t>(d_ff / 32);
+    a.n_experts = n_routed;
+    a.n_sel = top_k;
+    a.flags = flags;
+    a.w2 = static_cast<const uint8_t *>(sh_down);
+    return zq::launch_dmmv_k_wsum_shared(down_wtype, sh_wtype, a, s);
   }
   // down rows: the weighted sum over the routed experts, then the shared one
   // added onto it

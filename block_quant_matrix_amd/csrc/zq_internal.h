@@ -31,6 +31,10 @@ struct DmmvArgs {
   uint32_t flags;
   // last, so that the fields above keep their kernel-argument offsets
   int32_t id_base;      // MoE: expert e = ids[s] - id_base (a bank holding experts id_base..)
+  // K-quant weighted sum with a shared expert folded in: w2 [rows][k] in a
+  // block format, taken with slot n_sel's activation and weight wts[n_sel]
+  const uint8_t *w2;
+  int64_t row_bytes2;   // filled in by the launcher
 };
 
 // The multi-token DMMV: T <= 8 activations, token t at qx + t*k,
@@ -50,6 +54,12 @@ struct DmmvTokArgs {
   uint32_t flags;
 };
 int launch_dmmv_tok(int wtype, DmmvTokArgs a, hipStream_t stream);
+
+// The K-quant weighted sum over n_sel routed slots (wtype) plus the shared
+// expert a.w2 in sh_wtype (ZQ_Q4_0 / ZQ_Q8_0) at slot n_sel, in one launch:
+// y (+)= sum_s wts[s] W[e_s] x_s + wts[n_sel] W2 x_{n_sel}.
+bool dmmv_k_wsum_shared_fits(int wtype, int sh_wtype, int64_t k);
+int launch_dmmv_k_wsum_shared(int wtype, int sh_wtype, DmmvArgs a, hipStream_t stream);
 
 // RMS normalization + quantization, one workgroup per token.
 struct RmsNormArgs {
@@ -130,6 +140,10 @@ struct MoeGateUpArgs {
   float *wts_out;
   // last, so that the fields above keep their kernel-argument offsets
   int32_t id_base;      // without logits: expert e = ids[s] - id_base
+  // the mixed launch: the shared expert's [2*d_ff][k] matrix in its own
+  // format (slot top_k)
+  const uint8_t *bank2;
+  int64_t row_bytes2;   // filled in by the launcher
 };
 
 // MoE down pass with the weighted sum over the selected experts fused in.
@@ -161,6 +175,11 @@ int launch_moe_down(int wtype, MoeDownArgs a, hipStream_t stream);
 // d_model of 1024, 2048 or 4096 (one 64-element unit per lane, one pass).
 bool moe_gate_up_k_fits(int64_t d_model);
 int launch_moe_gate_up_k(int wtype, MoeGateUpArgs a, hipStream_t stream);
+// Routed experts (wtype, a.bank, router folded in: a.logits set) and the
+// shared expert (sh_wtype, one matrix at a.bank2) in one gate/up launch of
+// top_k + 1 slots; any of the five formats each, d_model of 1024 or 2048.
+bool moe_gate_up_mix_fits(int64_t d_model);
+int launch_moe_gate_up_mix(int wtype, int sh_wtype, MoeGateUpArgs a, hipStream_t stream);
 size_t moe_down_lds_bytes(int64_t n_sel, int64_t k);
 bool moe_gate_up_fits(int64_t d_model);
 bool moe_down_fits(int64_t n_sel, int64_t k);

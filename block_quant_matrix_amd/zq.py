@@ -59,6 +59,8 @@ SIGNATURES = {
                           _P, _U32, _P, _P]),
     "zq_moe_gate_up_route": (_INT, [_INT, _P, _I64, _I64, _I64, _I64, _P, _I32, _I32, _P, _P, _P,
                                     _P, _P, _P, _P, _P, _P, _P]),
+    "zq_moe_gate_up_mixed": (_INT, [_INT, _P, _I64, _INT, _P, _I64, _I64, _P, _I32, _I32, _P, _P,
+                                    _P, _P, _P, _P, _P, _P]),
     "zq_moe_ffn_route": (_INT, [_INT, _P, _I64, _P, _I64, _I64, _I64, _I64, _P, _I32, _I32, _P, _P,
                                 _P, _P, _P, _SZ, _P, _U32, _P]),
     "zq_moe_ffn_mixed": (_INT, [_INT, _P, _I64, _INT, _P, _I64, _INT, _P, _P, _I64, _I64, _P, _I32,
@@ -233,6 +235,14 @@ def zq_moe_gate_up(wtype, gu_bank, gu_stride_bytes, n_experts, d_model, d_ff, id
     return _call("zq_moe_gate_up", wtype, ptr(gu_bank), gu_stride_bytes, n_experts, d_model, d_ff,
                  ptr(ids), n_sel, ptr(x), ptr(qh), ptr(dh), ptr(sh), ptr(h_out), ptr(gu_out),
                  ptr(dev_status), _stream(stream))
+
+
+def zq_moe_gate_up_mixed(gu_wtype, gu_bank, gu_stride_bytes, sh_wtype, sh_gu, d_model, d_ff,
+                         logits, n_routed, top_k, shared_gate, x, ids, wts, qh, dh, sh=None,
+                         stream=None):
+    return _call("zq_moe_gate_up_mixed", gu_wtype, ptr(gu_bank), gu_stride_bytes, sh_wtype,
+                 ptr(sh_gu), d_model, d_ff, ptr(logits), n_routed, top_k, ptr(shared_gate),
+                 ptr(x), ptr(ids), ptr(wts), ptr(qh), ptr(dh), ptr(sh), _stream(stream))
 
 
 def zq_moe_ffn_workspace_bytes(d_model, d_ff, n_sel) -> int:

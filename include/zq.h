@@ -285,6 +285,20 @@ int zq_moe_gate_up_route(int wtype, const void *gu_bank, int64_t gu_stride_bytes
                          const float *x, int32_t *ids, float *wts, int8_t *qh, float *dh,
                          int32_t *sh, float *h_out, float *gu_out, void *stream);
 
+/* The gate/up stage of zq_moe_ffn_mixed in one launch: the routed experts
+ * (gu_wtype, gu_bank at gu_stride_bytes) with the router folded in, as
+ * zq_moe_gate_up_route, and the shared expert's own [2*d_ff][d_model]
+ * matrix sh_gu in sh_wtype as slot top_k (id n_routed).  Any of the five
+ * weight types each; d_model of 1024 or 2048; shared_gate required.
+ * Outputs as zq_moe_gate_up_route with n_sel = top_k + 1, bit for bit
+ * those of zq_moe_gate_up run on each matrix.  ("CUDA backend for ZINC",
+ * section 5: dmmv_q4k_moe gate/up beside the Q8_0 shared expert.) */
+int zq_moe_gate_up_mixed(int gu_wtype, const void *gu_bank, int64_t gu_stride_bytes,
+                         int sh_wtype, const void *sh_gu, int64_t d_model, int64_t d_ff,
+                         const float *logits, int32_t n_routed, int32_t top_k,
+                         const float *shared_gate, const float *x, int32_t *ids, float *wts,
+                         int8_t *qh, float *dh, int32_t *sh, void *stream);
+
 /* One token through the selected experts in two launches: zq_moe_gate_up
  * (quantize x, gate||up rows, swiglu, re-quantize), then the down DMMV with
  * the weighted sum over the selected experts fused in.  gu_bank: experts of [2*d_ff][d_model]
@@ -333,12 +347,14 @@ int zq_moe_ffn_route(int wtype, const void *gu_bank, int64_t gu_stride_bytes,
  * n_routed experts of [d_model][d_ff]; sh_gu / sh_down: the shared expert's
  * two matrices (used when shared_gate is non-NULL).  The router is
  * zq_moe_route's (ids / wts receive top_k (+1) entries, the shared one with
- * id n_routed).  When both gate/up types take the fused pass of
- * zq_moe_gate_up at this d_model, four launches: the routed gate/up pass
- * with the router folded in (zq_moe_gate_up_route over the routed bank),
- * the shared expert's gate/up pass, the routed weighted down sum, the shared
- * down term added on.  Otherwise seven: router, quantize x, the routed and
- * the shared gate||up gathers, SwiGLU + re-quantize, the two down stages.
+ * id n_routed).  Gate/up: at d_model 1024 or 2048 one launch
+ * (zq_moe_gate_up_mixed); at other widths that zq_moe_gate_up takes for
+ * both types, the routed pass with the router folded in and the shared
+ * expert's pass; otherwise five launches (router, quantize x, the routed and
+ * the shared gate||up gathers, SwiGLU + re-quantize).  Down: with K-quant
+ * routed experts, a Q4_0 / Q8_0 shared expert and d_ff of 256, 512, 1024 or
+ * 2048, one launch that sums every term in one reduction; otherwise the
+ * routed weighted sum, then the shared term added on.
  * y [d_model] (+)= the weighted sum; workspace >=
  * zq_moe_ffn_workspace_bytes(d_model, d_ff, top_k (+1)) bytes, 256-byte
  * aligned.  y may be x itself. */

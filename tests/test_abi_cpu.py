@@ -347,6 +347,13 @@ def test_other_argument_errors():
                             None, None) == zq.ZQ_EINVAL
     assert L.zq_moe_gate_up(15, A, kgs, 9, 2048, 512, B, 9, C, D, D + 65536, None, None, None,
                             None, None) == zq.ZQ_EINVAL
+    # mixed gate/up stage: no shared gate, a width it does not take
+    assert L.zq_moe_gate_up_mixed(12, A, kgs, 8, B, 2048, 512, C, 16, 4, None, D, A, B, C, D, None,
+                                  None) == zq.ZQ_ENULL
+    assert L.zq_moe_gate_up_mixed(12, A, kgs, 8, B, 4096, 512, C, 16, 4, C, D, A, B, C, D, None,
+                                  None) == zq.ZQ_EINVAL
+    assert L.zq_moe_gate_up_mixed(12, A, kgs, 3, B, 2048, 512, C, 16, 4, C, D, A, B, C, D, None,
+                                  None) == zq.ZQ_EINVAL
     # swiglu: f not a multiple of 32
     assert L.zq_swiglu_quantize(A, 9, 48, B, C, None, None, None) == zq.ZQ_EINVAL
     # moe_ffn: workspace too small

@@ -74,6 +74,68 @@ def test_dmmv_moe_kquant_gather_and_weighted(zq, wt):
     assert np.isnan(y3h[1]).all() and not np.isnan(y3h[0]).any() and not np.isnan(y3h[2]).any()
 
 
+def gen_bank_padded(wt, n_experts, rows, k, seed):
+    """Experts at a stride rounded up to 16 bytes (the K-quant bank
+    alignment), padding filled with 0xFF bytes that no kernel may read."""
+    w, m = gen_bank(wt, n_experts, rows, k, seed)
+    stride = (m + 15) // 16 * 16
+    out = np.full(n_experts * stride, 0xFF, np.uint8)
+    for e in range(n_experts):
+        out[e * stride:e * stride + m] = w.reshape(-1)[e * m:(e + 1) * m]
+    return out, stride
+
+
+def weighted_ref(wt, bank, stride, rows, k, ids, wts, rqs, rds, n_experts):
+    y_ref, S = np.zeros(rows), np.zeros(rows)
+    for s, e in enumerate(ids):
+        if not 0 <= e < n_experts:
+            continue
+        ye, Se = oracle.expert_rows_any(wt, bank, stride, rows, k, int(e), rqs[s], rds[s])
+        y_ref += float(wts[s]) * ye
+        S += abs(float(wts[s])) * Se
+    return y_ref, S
+
+
+# k = 256 .. 2048 take the slots-in-lanes kernel (16 .. 2 slots per round;
+# 17 and 5 slots need a second and third round); 768 the per-slot loop.
+# rows: ragged against 1, 2 and 4 row steps per wave.
+@pytest.mark.parametrize("wt", [Q4_K, Q5_K, Q6_K], ids=lambda t: NAME[t])
+@pytest.mark.parametrize("rows,k,n_sel", [(4097, 256, 17), (2051, 512, 9), (333, 1024, 8),
+                                          (130, 2048, 5), (77, 768, 3)])
+def test_dmmv_moe_kquant_weighted_layouts(zq, wt, rows, k, n_sel):
+    E = 7
+    bank, stride = gen_bank_padded(wt, E, rows, k, 820 + wt + k)
+    bank_d = dev(bank)
+    rng = np.random.default_rng(821 + n_sel)
+    ids_h = rng.integers(0, E, n_sel).astype(np.int32)
+    wts_h = rng.standard_normal(n_sel).astype(np.float32)
+    xs = inputs.gen_activation(n_sel, k, 822 + k)
+    qxs, dxs, sxs = quantize_gpu(zq, xs)
+    rqs, rds, _ = oracle.quantize_act(xs)
+    y = nan_f32(rows)
+    zq.zq_dmmv_moe(wt, bank_d, E, stride, rows, k, dev(ids_h), dev(wts_h), n_sel, qxs, dxs, sxs, k,
+                   zq.ZQ_MOE_WEIGHTED_SUM, y)
+    y_ref, S = weighted_ref(wt, bank, stride, rows, k, ids_h, wts_h, rqs, rds, E)
+    check_rows(host(y), y_ref, S, "%s weighted %d x %d, %d slots" % (NAME[wt], rows, k, n_sel))
+    # accumulate onto y; an out-of-range id in the middle is skipped and reported
+    prev = np.random.default_rng(5).standard_normal(rows).astype(np.float32)
+    y2 = dev(prev)
+    bad = ids_h.copy()
+    bad[n_sel // 2] = E + 3
+    status = sentinel_i32(1, value=0)
+    zq.zq_dmmv_moe(wt, bank_d, E, stride, rows, k, dev(bad), dev(wts_h), n_sel, qxs, dxs, sxs, k,
+                   zq.ZQ_MOE_WEIGHTED_SUM, y2, zq.ZQ_ACCUMULATE, status)
+    assert int(host(status)[0]) == zq.ZQ_ERANGE
+    y_ref2, S2 = weighted_ref(wt, bank, stride, rows, k, bad, wts_h, rqs, rds, E)
+    check_rows(host(y2), prev.astype(np.float64) + y_ref2, S2 + np.abs(prev),
+               "%s weighted accumulate, bad id" % NAME[wt])
+    # no selected expert: zeros
+    y3 = nan_f32(rows)
+    zq.zq_dmmv_moe(wt, bank_d, E, stride, rows, k, dev(ids_h), dev(wts_h), 0, qxs, dxs, sxs, k,
+                   zq.ZQ_MOE_WEIGHTED_SUM, y3)
+    assert (host(y3) == 0).all()
+
+
 @pytest.mark.parametrize("wt", [Q4_K, Q5_K, Q6_K], ids=lambda t: NAME[t])
 @pytest.mark.parametrize("d_model,d_ff", [(1024, 256), (2048, 512), (4096, 96)])
 def test_moe_gate_up_kquant(zq, wt, d_model, d_ff):
@@ -209,11 +271,14 @@ def test_moe_ffn_mixed_small(zq, fmt, d_model):
 
 @pytest.mark.parametrize("d_model", [512, 2048])
 def test_moe_ffn_mixed_equals_its_stages(zq, d_model):
-    """The composite gives the bits of the same stages run through the
-    public entry points one by one.  d_model 512: router, quantize, routed
-    and shared gate||up gathers, SwiGLU + re-quantize; 2048 (the fused
-    gate/up pass): router, routed and shared zq_moe_gate_up; then the routed
-    and shared down stages."""
+    """The composite against the same stages run through the public entry
+    points one by one.  d_model 512: router, quantize, routed and shared
+    gate||up gathers, SwiGLU + re-quantize; 2048: router, routed and shared
+    zq_moe_gate_up (the composite runs both in one launch, with the same
+    arithmetic); then the routed and the shared down stages, which the
+    composite folds into one reduction.  The expert list and weights bit for
+    bit; y within 1e-5 of the oracle's scale S (two summation orders of the
+    same terms on the same h codes)."""
     torch = torch_cuda()
     d_ff, n_routed, top_k = 256, 16, 4
     host_b, dev_b = make_banks(PAGES, n_routed, d_model, d_ff, 840)
@@ -241,13 +306,24 @@ def test_moe_ffn_mixed_equals_its_stages(zq, d_model):
         zq.zq_moe_gate_up(gwt, gu_d, gs, n_routed, d_model, d_ff, ids_d, top_k, xd, qh, dh, sh)
         zq.zq_moe_gate_up(swt, sgu_d, sgu_bytes, 1, d_model, d_ff, zero, 1, xd, qh[top_k:],
                           dh[top_k:], sh[top_k:])
+        # the composite's one-launch stage gives the same bits
+        ids_m, wts_m = sentinel_i32(n_sel), nan_f32(n_sel)
+        qh_m = torch.empty((n_sel, d_ff), dtype=torch.int8, device="cuda")
+        dh_m, sh_m = nan_f32(n_sel, d_ff // 32), sentinel_i32(n_sel, d_ff // 32)
+        zq.zq_moe_gate_up_mixed(gwt, gu_d, gs, swt, sgu_d, d_model, d_ff, dev(logits), n_routed,
+                                top_k, dev(np.array([g], np.float32)), xd, ids_m, wts_m, qh_m,
+                                dh_m, sh_m)
+        for a_, b_ in ((ids_m, ids_d), (wts_m, wts_d), (qh_m, qh), (dh_m, dh), (sh_m, sh)):
+            assert np.array_equal(host(a_).view(np.uint8), host(b_).view(np.uint8))
     y2 = nan_f32(d_model)
     zq.zq_dmmv_moe(dwt, dn_d, n_routed, ds, d_model, d_ff, ids_d, wts_d, top_k, qh, dh, sh, d_ff,
                    zq.ZQ_MOE_WEIGHTED_SUM, y2)
     zq.zq_dmmv_moe(swt, sdn_d, 1, sdn_bytes, d_model, d_ff, zero, wts_d[top_k:], 1, qh[top_k:],
                    dh[top_k:], sh[top_k:], d_ff, zq.ZQ_MOE_WEIGHTED_SUM, y2, zq.ZQ_ACCUMULATE)
     assert np.array_equal(host(ids_d), ids)
-    assert np.array_equal(host(y2).view(np.uint32), host(y).view(np.uint32))
+    assert np.array_equal(host(wts_d).view(np.uint32), wts.view(np.uint32))
+    _, S = oracle_mixed(host_b, n_routed, d_model, d_ff, ids, wts, x)
+    check_rows(host(y), host(y2).astype(np.float64), S, "fused down vs stages", tol=1e-5)
 
 
 def test_moe_ffn_mixed_pages_shape(zq):
