@@ -97,14 +97,13 @@ __global__ __launch_bounds__(1024) void moe_route_kernel(const float *__restrict
                                                          const float *__restrict__ shared_gate,
                                                          int32_t *__restrict__ ids,
                                                          float *__restrict__ wts) {
-  __shared__ float lv[1024];
+  __shared__ __attribute__((aligned(16))) float lv[1024];
   __shared__ int32_t sel_id[64];
   __shared__ float sel_v[64];
   __shared__ double sel_e[64];
-  const int t = static_cast<int>(threadIdx.x);
-  for (int i = t; i < n_routed; i += static_cast<int>(blockDim.x)) lv[i] = route_key(logits[i]);
+  const int n_pad = route_stage<P, 1024>(lv, logits, n_routed);
   __syncthreads();
-  route_rank<P>(lv, n_routed, top_k, sel_id, sel_v);
+  route_rank<P, 1024>(lv, n_routed, n_pad, top_k, sel_id, sel_v);
   __syncthreads();
   route_weights(sel_id, sel_v, sel_e, n_routed, top_k, shared_gate, ids, wts);
 }

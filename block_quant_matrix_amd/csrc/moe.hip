@@ -31,10 +31,11 @@ namespace zq {
 
 // Loads of the fp32 activation for this thread's first 32-element block (two
 // lanes per block, 16 elements each); issued before anything is waited on.
-__device__ __forceinline__ void gu_load_x(const MoeGateUpArgs &a, int tid, float (&xv)[16]) {
+__device__ __forceinline__ void gu_load_x(const MoeGateUpArgs &a, int nb, int tid,
+                                          float (&xv)[16]) {
   const int g = tid & 1;
   const int qb = tid >> 1;
-  if (qb < a.nb) {
+  if (qb < nb) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const float4 v = *reinterpret_cast<const float4 *>(a.x + qb * 32 + g * 16 + 4 * u);
@@ -54,10 +55,10 @@ __device__ __forceinline__ int gu_expert(const MoeGateUpArgs &a, int tid, int s,
     // the shared slot's workgroups need no ranking (the publication is
     // slot 0's)
     if (s >= a.top_k) return a.n_routed;  // uniform over the workgroup
-    __shared__ float rlv[1024];
-    for (int i = tid; i < a.n_routed; i += T) rlv[i] = route_key(a.logits[i]);
+    __shared__ __attribute__((aligned(16))) float rlv[1024];
+    const int n_pad = route_stage<8, T>(rlv, a.logits, a.n_routed);
     __syncthreads();
-    route_rank<8>(rlv, a.n_routed, a.top_k, rsel, rselv);
+    route_rank<8, T>(rlv, a.n_routed, n_pad, a.top_k, rsel, rselv);
     __syncthreads();
     return s < a.top_k ? rsel[s] : a.n_routed;
   } else {
@@ -68,10 +69,11 @@ __device__ __forceinline__ int gu_expert(const MoeGateUpArgs &a, int tid, int s,
 // Quantize x into LDS (two lanes per block, the first block already in xv):
 // codes, scales and the block sums times SUMX.
 template <int T, int SUMX>
-__device__ __forceinline__ void gu_quantize_x(const MoeGateUpArgs &a, int tid, float (&xv)[16],
-                                              int8_t *lq, float *ld, int32_t *ls) {
+__device__ __forceinline__ void gu_quantize_x(const MoeGateUpArgs &a, int nb, int tid,
+                                              float (&xv)[16], int8_t *lq, float *ld,
+                                              int32_t *ls) {
   const int g = tid & 1;
-  for (int qb = tid >> 1; qb < a.nb; qb += T / 2) {
+  for (int qb = tid >> 1; qb < nb; qb += T / 2) {
     if (qb != (tid >> 1)) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -154,10 +156,11 @@ struct GuBlockRows {
   static constexpr int BB = Blk<WT>::BYTES;
   static constexpr int SUMX = 8;  // the Q4_0 dot subtracts 8 times the code sum
   static_assert(RB * S * 16 == 64, "a workgroup computes 32 gate + 32 up rows");
+  static constexpr int64_t row_bytes_for(int nb) { return static_cast<int64_t>(nb) * BB; }
   uint32_t win[RB][BPL][NW];
   uint32_t off[RB][BPL];
 
-  __device__ __forceinline__ void load(const MoeGateUpArgs &a, const uint8_t *wb,
+  __device__ __forceinline__ void load(const MoeGateUpArgs &a, int nb, const uint8_t *wb,
                                        int64_t row_bytes, int hb, int tid) {
     const int lane = tid & 63, wv = tid >> 6;
     const int j = lane & (LPR - 1), slot = lane / LPR;
@@ -167,13 +170,13 @@ struct GuBlockRows {
 #pragma unroll
       for (int i = 0; i < BPL; ++i) {
         int b = j + LPR * i;
-        b = b < a.nb ? b : a.nb - 1;
+        b = b < nb ? b : nb - 1;
         off[t][i] = load_window<WT>(wb + row * row_bytes + static_cast<int64_t>(b) * BB, win[t][i]);
       }
     }
   }
 
-  __device__ __forceinline__ void rows(const MoeGateUpArgs &a, const int8_t *lq, const float *ld,
+  __device__ __forceinline__ void rows(int nb, const int8_t *lq, const float *ld,
                                        const int32_t *ls, float *lrow, int tid) {
     const int lane = tid & 63, wv = tid >> 6;
     const int j = lane & (LPR - 1), slot = lane / LPR;
@@ -183,7 +186,7 @@ struct GuBlockRows {
 #pragma unroll
     for (int i = 0; i < BPL; ++i) {
       const int b = j + LPR * i;
-      if (b < a.nb) {
+      if (b < nb) {
         const u32x4 v0 = *reinterpret_cast<const u32x4 *>(lq + 32 * b);
         const u32x4 v1 = *reinterpret_cast<const u32x4 *>(lq + 32 * b + 16);
         xq[i][0] = v0.x; xq[i][1] = v0.y; xq[i][2] = v0.z; xq[i][3] = v0.w;
@@ -234,10 +237,14 @@ struct GuKRows {
   static constexpr int NWD = KQ<WT>::NWD;
   static constexpr int SUMX = 1;
   static_assert(RB * S * 16 == 64, "a workgroup computes 32 gate + 32 up rows");
+  static constexpr int64_t row_bytes_for(int nb) {
+    return static_cast<int64_t>(nb / 8) * KQ<WT>::BYTES;
+  }
   uint32_t v[RB][NWD];
 
-  __device__ __forceinline__ void load(const MoeGateUpArgs &a, const uint8_t *wb,
+  __device__ __forceinline__ void load(const MoeGateUpArgs &a, int nb, const uint8_t *wb,
                                        int64_t row_bytes, int hb, int tid) {
+    (void)nb;
     const int lane = tid & 63, wv = tid >> 6;
     const int j = lane & (LPR - 1), slot = lane / LPR;
 #pragma unroll
@@ -248,9 +255,9 @@ struct GuKRows {
     }
   }
 
-  __device__ __forceinline__ void rows(const MoeGateUpArgs &a, const int8_t *lq, const float *ld,
+  __device__ __forceinline__ void rows(int nb, const int8_t *lq, const float *ld,
                                        const int32_t *ls, float *lrow, int tid) {
-    (void)a;
+    (void)nb;
     const int lane = tid & 63, wv = tid >> 6;
     const int j = lane & (LPR - 1), slot = lane / LPR;
     KUnitAct act;
@@ -309,26 +316,26 @@ struct GuLds {
   float *ld;
   int32_t *ls;
   float *lrow;
-  __device__ __forceinline__ GuLds(uint8_t *smem, const MoeGateUpArgs &a)
+  __device__ __forceinline__ GuLds(uint8_t *smem, int k, int nb)
       : lq(reinterpret_cast<int8_t *>(smem)),
-        ld(reinterpret_cast<float *>(smem + a.k)),
-        ls(reinterpret_cast<int32_t *>(smem + a.k + 4 * a.nb)),
-        lrow(reinterpret_cast<float *>(smem + a.k + 8 * a.nb)) {}
+        ld(reinterpret_cast<float *>(smem + k)),
+        ls(reinterpret_cast<int32_t *>(smem + k + 4 * nb)),
+        lrow(reinterpret_cast<float *>(smem + k + 8 * nb)) {}
 };
 
 // One workgroup of the gate/up pass after its expert is known: issue the
 // weights, quantize x into LDS meanwhile, the 64 rows, the epilogue.
 template <class Rows, bool ROUTED>
-__device__ __forceinline__ void gu_run(const MoeGateUpArgs &a, const uint8_t *wb,
+__device__ __forceinline__ void gu_run(const MoeGateUpArgs &a, int nb, const uint8_t *wb,
                                        int64_t row_bytes, float (&xv)[16], const GuLds &L,
                                        int tid, int s, int hb, const int32_t *rsel,
                                        const float *rselv) {
   constexpr int T = 1024;
   Rows r;
-  r.load(a, wb, row_bytes, hb, tid);
-  gu_quantize_x<T, Rows::SUMX>(a, tid, xv, L.lq, L.ld, L.ls);
+  r.load(a, nb, wb, row_bytes, hb, tid);
+  gu_quantize_x<T, Rows::SUMX>(a, nb, tid, xv, L.lq, L.ld, L.ls);
   __syncthreads();
-  r.rows(a, L.lq, L.ld, L.ls, L.lrow, tid);
+  r.rows(nb, L.lq, L.ld, L.ls, L.lrow, tid);
   __syncthreads();
   gu_epilogue<ROUTED>(a, tid, s, hb, L.lrow, rsel, rselv);
 }
@@ -339,14 +346,14 @@ template <class Rows, bool ROUTED>
 __global__ __launch_bounds__(1024) void moe_gate_up_kernel(const MoeGateUpArgs a) {
   constexpr int T = 1024;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const GuLds L(smem, a);
+  const GuLds L(smem, a.k, a.nb);
   const int tid = static_cast<int>(threadIdx.x);
   const int hb = static_cast<int>(blockIdx.x);  // 32-wide block of the FFN width
   const int s = static_cast<int>(blockIdx.y);   // selected-expert slot
   // activation loads, issued before the expert id so that they share its
   // round trip
   float xv[16];
-  gu_load_x(a, tid, xv);
+  gu_load_x(a, a.nb, tid, xv);
   __shared__ int32_t rsel[64];
   __shared__ float rselv[64];
   const int e = gu_expert<ROUTED, T>(a, tid, s, rsel, rselv);
@@ -354,32 +361,35 @@ __global__ __launch_bounds__(1024) void moe_gate_up_kernel(const MoeGateUpArgs a
     if (a.status && tid == 0) *a.status = ZQ_ERANGE;
     return;
   }
-  gu_run<Rows, ROUTED>(a, a.bank + static_cast<int64_t>(e) * a.expert_stride, a.row_bytes, xv, L,
-                       tid, s, hb, rsel, rselv);
+  gu_run<Rows, ROUTED>(a, a.nb, a.bank + static_cast<int64_t>(e) * a.expert_stride, a.row_bytes,
+                       xv, L, tid, s, hb, rsel, rselv);
 }
 
 // Routed experts and a shared expert of another format in one launch, the
 // router folded in: slots 0..top_k-1 (Rows over a.bank) take the experts
 // the workgroups rank; slot top_k (SRows over a.bank2, one matrix) is the
-// shared expert.  grid (d_ff / 32, top_k + 1).
-template <class Rows, class SRows>
+// shared expert.  grid (d_ff / 32, top_k + 1).  The row width (NB blocks)
+// is a compile-time constant here, which keeps the scalar registers of the
+// two layouts within bounds.
+template <class Rows, class SRows, int NB>
 __global__ __launch_bounds__(1024) void moe_gate_up_mix_kernel(const MoeGateUpArgs a) {
   constexpr int T = 1024;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const GuLds L(smem, a);
+  const GuLds L(smem, 32 * NB, NB);
   const int tid = static_cast<int>(threadIdx.x);
   const int hb = static_cast<int>(blockIdx.x);
   const int s = static_cast<int>(blockIdx.y);
   float xv[16];
-  gu_load_x(a, tid, xv);
+  gu_load_x(a, NB, tid, xv);
   __shared__ int32_t rsel[64];
   __shared__ float rselv[64];
-  const int e = gu_expert<true, T>(a, tid, s, rsel, rselv);
-  if (s < a.top_k) {  // uniform over the workgroup; e in [0, n_routed)
-    gu_run<Rows, true>(a, a.bank + static_cast<int64_t>(e) * a.expert_stride, a.row_bytes, xv, L,
-                       tid, s, hb, rsel, rselv);
+  if (s < a.top_k) {  // uniform over the workgroup
+    const int e = gu_expert<true, T>(a, tid, s, rsel, rselv);  // in [0, n_routed)
+    gu_run<Rows, true>(a, NB, a.bank + static_cast<int64_t>(e) * a.expert_stride,
+                       Rows::row_bytes_for(NB), xv, L, tid, s, hb, rsel, rselv);
   } else {
-    gu_run<SRows, true>(a, a.bank2, a.row_bytes2, xv, L, tid, s, hb, rsel, rselv);
+    // (the publication is slot 0's, never this slot's)
+    gu_run<SRows, false>(a, NB, a.bank2, SRows::row_bytes_for(NB), xv, L, tid, s, hb, rsel, rselv);
   }
 }
 
@@ -580,10 +590,11 @@ template <int WT, int NB>
 using GuAnyRows = typename std::conditional<(WT == ZQ_Q4_0 || WT == ZQ_Q8_0), GuRowsFor<WT, NB>,
                                             GuKRowsFor<WT, NB>>::type::type;
 
-template <class Rows, class SRows>
+template <class Rows, class SRows, int NB>
 int launch_gu_mix(const MoeGateUpArgs &a, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(a.d_ff / 32), static_cast<unsigned>(a.top_k + 1));
-  hipLaunchKernelGGL((moe_gate_up_mix_kernel<Rows, SRows>), grid, dim3(1024), gu_lds(a), stream, a);
+  hipLaunchKernelGGL((moe_gate_up_mix_kernel<Rows, SRows, NB>), grid, dim3(1024), gu_lds(a), stream,
+                     a);
   ZQ_LAUNCH_CHECK();
   return ZQ_OK;
 }
@@ -592,11 +603,11 @@ template <int NB, int WT>
 int gu_mix_shared(int sh_wtype, const MoeGateUpArgs &a, hipStream_t stream) {
   using R = GuAnyRows<WT, NB>;
   switch (sh_wtype) {
-    case ZQ_Q4_0: return launch_gu_mix<R, GuAnyRows<ZQ_Q4_0, NB>>(a, stream);
-    case ZQ_Q8_0: return launch_gu_mix<R, GuAnyRows<ZQ_Q8_0, NB>>(a, stream);
-    case ZQ_Q4_K: return launch_gu_mix<R, GuAnyRows<ZQ_Q4_K, NB>>(a, stream);
-    case ZQ_Q5_K: return launch_gu_mix<R, GuAnyRows<ZQ_Q5_K, NB>>(a, stream);
-    case ZQ_Q6_K: return launch_gu_mix<R, GuAnyRows<ZQ_Q6_K, NB>>(a, stream);
+    case ZQ_Q4_0: return launch_gu_mix<R, GuAnyRows<ZQ_Q4_0, NB>, NB>(a, stream);
+    case ZQ_Q8_0: return launch_gu_mix<R, GuAnyRows<ZQ_Q8_0, NB>, NB>(a, stream);
+    case ZQ_Q4_K: return launch_gu_mix<R, GuAnyRows<ZQ_Q4_K, NB>, NB>(a, stream);
+    case ZQ_Q5_K: return launch_gu_mix<R, GuAnyRows<ZQ_Q5_K, NB>, NB>(a, stream);
+    case ZQ_Q6_K: return launch_gu_mix<R, GuAnyRows<ZQ_Q6_K, NB>, NB>(a, stream);
     default: return ZQ_EINVAL;
   }
 }

@@ -346,39 +346,68 @@ __device__ __forceinline__ void block_best(float &v, int32_t &i) {
 // NaN logit could otherwise leave a rank, and with it an expert slot, empty).
 __device__ __forceinline__ float route_key(float v) { return v != v ? -__builtin_inff() : v; }
 
-// Rank selection over n logits staged in LDS (lv, through route_key) by the whole workgroup, P
-// threads per logit: a logit's rank is the number of logits that beat it
-// (larger, or equal at a lower id), and the logits of rank < top_k are
-// stored at their rank (sel_id, sel_v), largest first with ties to the
-// lower id.  Counts are small integers, exact in fp32.  Every thread of the
-// workgroup must call it; the caller synchronizes before reading sel_*.
-template <int P>
-__device__ __forceinline__ void route_rank(const float *lv, int n, int top_k, int32_t *sel_id,
-                                           float *sel_v) {
+// The logits staged for ranking: lv[i] = route_key(logits[i]) for i < n,
+// -inf for n <= i < n_pad, n_pad = n rounded up to 16 * P (lv holds at
+// least that many).  Every one of the NT threads of the workgroup calls it
+// (NT a compile-time constant: reading the workgroup size would cost a
+// memory round trip before the first logit load); the caller synchronizes
+// before ranking.  Returns n_pad.
+template <int P, int NT>
+__device__ __forceinline__ int route_stage(float *lv, const float *logits, int n) {
+  const int n_pad = (n + 16 * P - 1) / (16 * P) * (16 * P);
+  for (int i = static_cast<int>(threadIdx.x); i < n_pad; i += NT)
+    lv[i] = i < n ? route_key(logits[i]) : -__builtin_inff();
+  return n_pad;
+}
+
+// Rank selection over n logits staged by route_stage (lv, 16-byte aligned,
+// n_pad entries) by the whole workgroup, P threads per logit: a logit's
+// rank is the number of logits that beat it (larger, or equal at a lower
+// id), and the logits of rank < top_k are stored at their rank (sel_id,
+// sel_v), largest first with ties to the lower id.  The -inf padding
+// beats nothing: it is not larger than any staged value, and an equal one
+// has a higher id.  Each of the P threads scans a contiguous n_pad / P
+// run, 16 values per step from four 16-byte LDS reads.  Counts are small
+// integers, exact in fp32.  Every one of the NT threads of the workgroup
+// must call it; the caller synchronizes before reading sel_*.
+template <int P, int NT>
+__device__ __forceinline__ void route_rank(const float *lv, int n, int n_pad, int top_k,
+                                           int32_t *sel_id, float *sel_v) {
   const int t = static_cast<int>(threadIdx.x);
-  const int n_groups = static_cast<int>(blockDim.x) / P;
+  constexpr int n_groups = NT / P;
   const int part = t & (P - 1);
+  const int chunk = n_pad / P;  // a multiple of 16
   for (int e0 = 0; e0 < n; e0 += n_groups) {  // uniform trip count
     const int e = e0 + t / P;
     const bool ok = e < n;
     const float v = ok ? lv[e] : 0.0f;
-    float cnt = 0.0f;
+    int cnt = 0;
     if (ok) {
-      // eight comparisons per step, their LDS reads issued together
-      for (int j0 = part; j0 < n; j0 += 8 * P) {
+      const int j0 = part * chunk;
+      for (int c = 0; c < chunk; c += 16) {
+        float u[16];
 #pragma unroll
-        for (int u8 = 0; u8 < 8; ++u8) {
-          const int j = j0 + u8 * P;
-          if (j < n) {
-            const float u = lv[j];
-            cnt += (u > v || (u == v && j < e)) ? 1.0f : 0.0f;
+        for (int q = 0; q < 4; ++q) {
+          const float4 f = *reinterpret_cast<const float4 *>(lv + j0 + c + 4 * q);
+          u[4 * q] = f.x; u[4 * q + 1] = f.y; u[4 * q + 2] = f.z; u[4 * q + 3] = f.w;
+        }
+        // four compares at a time: each leaves a lane mask in scalar
+        // registers, and sixteen in flight would exhaust them
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int m = 4 * g; m < 4 * g + 4; ++m) {
+            const int j = j0 + c + m;
+            cnt += (u[m] > v || (u[m] == v && j < e)) ? 1 : 0;
           }
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    cnt = group_sum<P>(cnt);
+    const float total = group_sum<P>(static_cast<float>(cnt));
     if (ok && part == 0) {
-      const int rank = static_cast<int>(cnt);
+      const int rank = static_cast<int>(total);
       if (rank < top_k) {
         sel_id[rank] = e;
         sel_v[rank] = v;
