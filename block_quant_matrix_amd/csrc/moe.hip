@@ -395,6 +395,120 @@ __global__ __launch_bounds__(1024) void moe_gate_up_mix_kernel(const MoeGateUpAr
 
 // ---------------------------------------------------------------- down -----
 
+// The weighted sum over experts with the experts spread over the lanes (as
+// the K-quant form in dmmv_k.hip): lane = (slot, part), LPS lanes per slot
+// and BPL blocks per lane (k = 32 * nb <= 32 * LPS * BPL), 64 / LPS slots
+// side by side, the partials reduced over the whole wave.  A wave takes RB
+// consecutive rows; every selected expert's windows for them are requested
+// at once.  Slots beyond 64 / LPS take further rounds.  A lane whose expert
+// id is out of range contributes nothing and reports ZQ_ERANGE.
+template <int WT, int LPS, int BPL, int RB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void moe_down_wsum_kernel(
+    const MoeDownArgs a) {
+  constexpr int SL = 64 / LPS;
+  constexpr int NW = Blk<WT>::NW;
+  constexpr int BB = Blk<WT>::BYTES;
+  const int lane = static_cast<int>(threadIdx.x & 63);
+  const int j = lane & (LPS - 1);
+  const int sl = lane / LPS;
+  const int64_t wave = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int64_t n_waves = static_cast<int64_t>(gridDim.x) * 4;
+  const int64_t n_groups = (a.rows + RB - 1) / RB;
+  const int n_rounds = (a.n_sel + SL - 1) / SL;
+  const int64_t xs32 = a.x_stride / 32;
+
+  uint32_t xq[BPL][8];
+  float xd[BPL];
+  int32_t xsr[BPL];  // Q4_0: the blocks' code sums as given (sx), else unused
+  // the lane's slot's activation blocks (scale 0 past the row end); loads
+  // only, the sums of a missing sx are taken once the weights are requested
+  auto load_act = [&](int sc) {
+    const int8_t *qx = a.qx + static_cast<int64_t>(sc) * a.x_stride;
+#pragma unroll
+    for (int i = 0; i < BPL; ++i) {
+      int b = j + LPS * i;
+      const bool bok = b < a.nb;
+      b = bok ? b : a.nb - 1;
+      const u32x4 v0 = *reinterpret_cast<const u32x4 *>(qx + 32 * b);
+      const u32x4 v1 = *reinterpret_cast<const u32x4 *>(qx + 32 * b + 16);
+      xq[i][0] = v0.x; xq[i][1] = v0.y; xq[i][2] = v0.z; xq[i][3] = v0.w;
+      xq[i][4] = v1.x; xq[i][5] = v1.y; xq[i][6] = v1.z; xq[i][7] = v1.w;
+      const float d = a.dx[sc * xs32 + b];
+      xd[i] = bok ? d : 0.0f;
+      xsr[i] = (WT == ZQ_Q4_0 && a.sx) ? a.sx[sc * xs32 + b] : 0;
+    }
+  };
+  const bool hoist = n_rounds == 1;
+  if (hoist && a.n_sel > 0) load_act(sl < a.n_sel ? sl : a.n_sel - 1);
+
+  for (int64_t gi = wave; gi < n_groups; gi += n_waves) {
+    const int64_t row0 = gi * RB;
+    float acc[RB];
+#pragma unroll
+    for (int t = 0; t < RB; ++t) acc[t] = 0.0f;
+    for (int r = 0; r < n_rounds; ++r) {
+      const int s = r * SL + sl;
+      const bool in = s < a.n_sel;
+      const int sc = in ? s : a.n_sel - 1;
+      const int e = a.ids[sc] - a.id_base;
+      const bool ok = in && e >= 0 && e < a.n_experts;
+      if (in && !ok && a.status) *a.status = ZQ_ERANGE;
+      const float ws = a.wts[sc];
+      const uint8_t *wb = a.bank + static_cast<int64_t>(ok ? e : 0) * a.expert_stride;
+      if (!hoist) load_act(sc);
+      uint32_t win[RB][BPL][NW];
+      uint32_t off[RB][BPL];
+#pragma unroll
+      for (int t = 0; t < RB; ++t) {
+        int64_t row = row0 + t;
+        row = row < a.rows ? row : a.rows - 1;
+#pragma unroll
+        for (int i = 0; i < BPL; ++i) {
+          int b = j + LPS * i;
+          b = b < a.nb ? b : a.nb - 1;
+          off[t][i] = load_window<WT>(wb + row * a.row_bytes + static_cast<int64_t>(b) * BB, win[t][i]);
+        }
+      }
+      int32_t xsum[BPL];
+#pragma unroll
+      for (int i = 0; i < BPL; ++i) {
+        xsum[i] = 0;
+        if constexpr (WT == ZQ_Q4_0) xsum[i] = a.sx ? xsr[i] : code_sum(xq[i], 8);
+      }
+#pragma unroll
+      for (int t = 0; t < RB; ++t) {
+        float part = 0.0f;
+#pragma unroll
+        for (int i = 0; i < BPL; ++i) {
+          const float dw = window_scale(win[t][i][0], off[t][i]);
+          const uint32_t sel = quant_selector(off[t][i]);
+          int32_t isum;
+          if constexpr (WT == ZQ_Q4_0) {
+            isum = q4_raw_dot(win[t][i], sel, xq[i]) - 8 * xsum[i];
+          } else {
+            isum = q8_dot(win[t][i], sel, xq[i]);
+          }
+          part = __builtin_fmaf(dw * xd[i], static_cast<float>(isum), part);
+        }
+        acc[t] = ok ? __builtin_fmaf(ws, part, acc[t]) : acc[t];
+      }
+    }
+    using R = RowReduce<64, RB>;
+    float out[R::NOUT];
+    R::run(acc, out);
+    if (R::writer(lane)) {
+#pragma unroll
+      for (int m = 0; m < R::NOUT; ++m) {
+        const int64_t row = row0 + R::rowstep(m, lane);
+        if (row < a.rows) {
+          float *yp = a.y + row;
+          *yp = (a.flags & ZQ_ACCUMULATE) ? *yp + out[m] : out[m];
+        }
+      }
+    }
+  }
+}
+
 constexpr int kDownMaxSel = 16;  // experts whose windows are in flight at once
 
 template <int WT, int LPR, int BPL, int WPB>
@@ -648,8 +762,41 @@ int launch_dn(const MoeDownArgs &a, hipStream_t stream) {
   return ZQ_OK;
 }
 
+template <int WT, int LPS, int BPL, int RB>
+int launch_dn_wsum1(const MoeDownArgs &a, hipStream_t stream) {
+  const int64_t n_groups = (a.rows + RB - 1) / RB;
+  const int64_t blocks = (n_groups + 3) / 4;
+  const unsigned grid = static_cast<unsigned>(blocks < 1048576 ? blocks : 1048576);
+  hipLaunchKernelGGL((moe_down_wsum_kernel<WT, LPS, BPL, RB>), dim3(grid), dim3(256), 0, stream, a);
+  ZQ_LAUNCH_CHECK();
+  return ZQ_OK;
+}
+
+// Row steps per wave: the largest of 4, 2, 1 that keeps >= 1024 waves.
+template <int WT, int LPS, int BPL>
+int launch_dn_wsum_rb(const MoeDownArgs &a, hipStream_t stream) {
+  if ((a.rows + 3) / 4 >= 1024) return launch_dn_wsum1<WT, LPS, BPL, 4>(a, stream);
+  if ((a.rows + 1) / 2 >= 1024) return launch_dn_wsum1<WT, LPS, BPL, 2>(a, stream);
+  return launch_dn_wsum1<WT, LPS, BPL, 1>(a, stream);
+}
+
+// Slots in lanes while one or two rounds take every slot: 4 lanes per slot
+// (16 slots a round) up to 16 blocks per row, 8 lanes (8 slots) up to 32.
+bool down_wsum_fits(int nb, int n_sel) { return nb <= 16 ? n_sel <= 32 : (nb <= 32 && n_sel <= 16); }
+
+template <int WT>
+int launch_dn_wsum(const MoeDownArgs &a, hipStream_t stream) {
+  if (a.nb <= 4) return launch_dn_wsum_rb<WT, 4, 1>(a, stream);
+  if (a.nb <= 8) return launch_dn_wsum_rb<WT, 4, 2>(a, stream);
+  if (a.nb <= 12) return launch_dn_wsum_rb<WT, 4, 3>(a, stream);
+  if (a.nb <= 16) return launch_dn_wsum_rb<WT, 4, 4>(a, stream);
+  if (a.nb <= 24) return launch_dn_wsum_rb<WT, 8, 3>(a, stream);
+  return launch_dn_wsum_rb<WT, 8, 4>(a, stream);  // nb <= 32 (down_wsum_fits)
+}
+
 template <int WT>
 int launch_dn_w(const MoeDownArgs &a, hipStream_t stream) {
+  if (down_wsum_fits(a.nb, a.n_sel)) return launch_dn_wsum<WT>(a, stream);
   if (a.nb <= 8) return launch_dn<WT, 8, 1>(a, stream);
   if (a.nb <= 16) return launch_dn<WT, 16, 1>(a, stream);
   if (a.nb <= 32) return launch_dn<WT, 32, 1>(a, stream);

@@ -96,13 +96,16 @@ def weighted_ref(wt, bank, stride, rows, k, ids, wts, rqs, rds, n_experts):
     return y_ref, S
 
 
-# k = 256 .. 2048 take the slots-in-lanes kernel (16 .. 2 slots per round;
-# 17 and 5 slots need a second and third round); 768 the per-slot loop.
-# rows: ragged against 1, 2 and 4 row steps per wave.
-@pytest.mark.parametrize("wt", [Q4_K, Q5_K, Q6_K], ids=lambda t: NAME[t])
+# K-quants: k = 256 .. 2048 take the slots-in-lanes kernel (16 .. 2 slots
+# per round; 17 and 5 slots need a second and third round); 768 the
+# per-slot loop.  Q4_0 / Q8_0: k = 256, 512 (4 lanes per slot, 2 and 4
+# blocks per lane; 17 slots take two rounds), 768 and 1024 (8 lanes per
+# slot, 3 and 4 blocks) take the slots-in-lanes kernel, 2048 the staged
+# kernel.  rows: ragged against 1, 2 and 4 row steps per wave.
+@pytest.mark.parametrize("wt", [Q4_0, Q8_0, Q4_K, Q5_K, Q6_K], ids=lambda t: NAME[t])
 @pytest.mark.parametrize("rows,k,n_sel", [(4097, 256, 17), (2051, 512, 9), (333, 1024, 8),
                                           (130, 2048, 5), (77, 768, 3)])
-def test_dmmv_moe_kquant_weighted_layouts(zq, wt, rows, k, n_sel):
+def test_dmmv_moe_weighted_layouts(zq, wt, rows, k, n_sel):
     E = 7
     bank, stride = gen_bank_padded(wt, E, rows, k, 820 + wt + k)
     bank_d = dev(bank)
@@ -129,6 +132,12 @@ def test_dmmv_moe_kquant_weighted_layouts(zq, wt, rows, k, n_sel):
     y_ref2, S2 = weighted_ref(wt, bank, stride, rows, k, bad, wts_h, rqs, rds, E)
     check_rows(host(y2), prev.astype(np.float64) + y_ref2, S2 + np.abs(prev),
                "%s weighted accumulate, bad id" % NAME[wt])
+    if wt == Q4_0:
+        # without block sums the kernel sums the codes itself: the same bits
+        y4 = nan_f32(rows)
+        zq.zq_dmmv_moe(wt, bank_d, E, stride, rows, k, dev(ids_h), dev(wts_h), n_sel, qxs, dxs,
+                       None, k, zq.ZQ_MOE_WEIGHTED_SUM, y4)
+        assert np.array_equal(host(y4).view(np.uint32), host(y).view(np.uint32))
     # no selected expert: zeros
     y3 = nan_f32(rows)
     zq.zq_dmmv_moe(wt, bank_d, E, stride, rows, k, dev(ids_h), dev(wts_h), 0, qxs, dxs, sxs, k,
