@@ -461,6 +461,9 @@ class DecodeChainWorkload(Workload):
     eager time of the same chain is reported beside it."""
     dominant_name = "moe_gate_up_kernel (router folded in)"
     bound = "hbm"
+    # each layer's gate/up launch is the 128-expert block's, shape for shape:
+    # its counted traffic is that workload's
+    traffic_workload = "q4_0_moe_128e_top8_shared_2048x512"
 
     def __init__(self, wl):
         from block_quant_matrix_amd import inputs
@@ -764,16 +767,17 @@ class GemmWorkload(Workload):
                            % (n_pairs, self.m * self.n, el))
 
 
-def counted_traffic(kernel_name):
-    """HBM bytes per launch from the committed counter runs (profiles/traffic.json),
-    or None when the kernel's sources have changed since they were taken."""
+def counted_traffic(kernel_name, workload):
+    """HBM bytes per launch of the kernel at this workload from the committed
+    counter runs (profiles/traffic.json, keyed by workload), or None when
+    there is none or the kernel's sources have changed since it was taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
-        rec = json.load(open(path)).get(kernel_name)
+        rec = json.load(open(path)).get(workload)
     except (OSError, ValueError):
         return None
-    if not rec:
+    if not rec or rec.get("kernel") != kernel_name:
         return None
     h = hashlib.sha256()
     for src in rec["sources"]:
@@ -915,7 +919,8 @@ def main():
     out["roofline"] = {"bound": w.bound, "kernel": w.dominant_name, "achieved": round(ach, 3),
                        "peak": peak, "unit": runit, "frac": round(ach / peak, 4),
                        "per_launch": per_launch, "ms_per_launch": round(ms_kernel, 6),
-                       "traffic": counted_traffic(w.dominant_name)}
+                       "traffic": counted_traffic(w.dominant_name,
+                                                  getattr(w, "traffic_workload", w.name))}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = w.cpu_baseline(args.cpu_seconds)
         out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 4)
