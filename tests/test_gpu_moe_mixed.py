@@ -259,9 +259,13 @@ def oracle_mixed(host_b, n_routed, d_model, d_ff, ids, wts, x):
 PAGES = (Q4_K, Q5_K, Q8_0)
 
 
-@pytest.mark.parametrize("fmt", [PAGES, (Q4_0, Q4_0, Q8_0), (Q6_K, Q4_K, Q4_0)],
+@pytest.mark.parametrize("fmt", [PAGES, (Q4_0, Q4_0, Q8_0), (Q6_K, Q4_K, Q4_0), (Q5_K, Q6_K, Q4_K),
+                                 (Q8_0, Q4_K, Q6_K)],
                          ids=lambda f: "-".join(NAME[t] for t in f))
-@pytest.mark.parametrize("d_model", [512, 1024])   # the staged path, the fused gate/up pass
+@pytest.mark.parametrize("d_model", [512, 1024, 2048, 4096])
+# 512: the staged path; 1024 / 2048: routed and shared gate/up in one launch;
+# 4096: the routed pass and the shared pass in two launches.  The down pass
+# folds a block-format shared expert into K-quant routed rows.
 def test_moe_ffn_mixed_small(zq, fmt, d_model):
     d_ff, n_routed, top_k = 256, 16, 4
     host_b, dev_b = make_banks(fmt, n_routed, d_model, d_ff, 830 + sum(fmt))
