@@ -749,7 +749,16 @@ class GemmWorkload(Workload):
         return self.ops / (ms * 1e-3) / 1e12, INT8_PEAK_TOPS, "TOP/s", self.ops
 
     def extra(self, ms):
-        return {"tokens_per_s": self.m / (ms * 1e-3)}
+        # The ceiling the fp32 rescale sets: every (token, row, block) triple
+        # needs a convert, a multiply and an FMA, unpacked, at 64 lanes per
+        # clock per CU (256 CUs, 2.4 GHz).
+        triples = self.m * self.n * (self.k // 32)
+        valu_s = 3 * triples / (256 * 64 * 2.4e9)
+        ceiling = 2 * self.m * self.n * self.k / valu_s / 1e12
+        steps_tops = 2 * self.m * self.n * self.k / (ms * 1e-3) / 1e12
+        return {"tokens_per_s": self.m / (ms * 1e-3),
+                "valu_epilogue_ceiling_TOPs": round(ceiling, 1),
+                "step_frac_of_epilogue_ceiling": round(steps_tops / ceiling, 4)}
 
     def cpu_baseline(self, seconds):
         import oracle
