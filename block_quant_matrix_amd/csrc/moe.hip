@@ -99,21 +99,26 @@ __device__ __forceinline__ int64_t gu_row(const MoeGateUpArgs &a, int hb, int lr
 }
 
 // Epilogue, after the 64 row results are in lrow: SwiGLU over the 32
-// outputs (fp64, one rounding) and their quantization (8 lanes, four
-// elements each), then the router's publication (ROUTED, one workgroup).
+// outputs (fp64, one rounding; one output per lane of wave 0, so the 32
+// exponentials run side by side) and their quantization (8 lanes, four
+// elements each, gathered by shuffles), then the router's publication
+// (ROUTED, one workgroup).
 template <bool ROUTED>
 __device__ __forceinline__ void gu_epilogue(const MoeGateUpArgs &a, int tid, int s, int hb,
                                             const float *lrow, const int32_t *rsel,
                                             const float *rselv) {
+  float h = 0.0f;
+  if (tid < 64) {
+    const int i = tid & 31;
+    const double gd = static_cast<double>(lrow[i]);
+    const double silu = gd / (1.0 + exp(-gd));
+    h = static_cast<float>(silu * static_cast<double>(lrow[32 + i]));
+  }
+  float hv[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) hv[q] = __shfl(h, 4 * (tid & 7) + q);
   if (tid < 8) {
     const int i0 = 4 * tid;
-    float hv[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const double gd = static_cast<double>(lrow[i0 + q]);
-      const double silu = gd / (1.0 + exp(-gd));
-      hv[q] = static_cast<float>(silu * static_cast<double>(lrow[32 + i0 + q]));
-    }
     uint32_t packed[1];
     float d;
     int32_t sum;
