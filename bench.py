@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11])
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -272,8 +272,9 @@ class DmmvKWorkload(Workload):
 
 
 class DmmvTokWorkload(Workload):
-    """Quantize 8 tokens + one multi-token DMMV over Q4_0 4096 x 4096 (two
-    launches): the small-M decode shape."""
+    """Quantize T tokens + one multi-token DMMV (two launches): the small-M
+    decode shapes, Q4_0 4096 x 4096 (vector units) and the 248 320-row LM
+    head (matrix cores)."""
     dominant_name = "dmmv_tok_kernel"
 
     def __init__(self, wl):
@@ -282,6 +283,8 @@ class DmmvTokWorkload(Workload):
         self.wl = wl
         self.name = cfg["name"]
         self.wtype, self.rows, self.k, self.T = cfg["wtype"], cfg["rows"], cfg["k"], cfg["n_tok"]
+        if self.rows >= 65536 and self.T >= 3:
+            self.dominant_name = "dmmv_tok_mfma_kernel (matrix cores)"
         self.nb = self.k // 32
         self.wbytes = self.rows * self.nb * inputs.BLOCK_BYTES[self.wtype]
         # the DMMV reads the weights once and every token's codes, scales and
@@ -289,7 +292,7 @@ class DmmvTokWorkload(Workload):
         # reads and its writes
         self.dmmv_bytes = self.wbytes + self.T * (self.k + 8 * self.nb) + 4 * self.T * self.rows
         self.step_bytes = self.dmmv_bytes + self.T * (4 * self.k + self.k + 8 * self.nb)
-        self.steps, self.warmup = 2000, 100
+        self.steps, self.warmup = (2000, 100) if self.rows < 65536 else (400, 20)
 
     def setup(self, torch, zq, inputs):
         self.torch, self.zq = torch, zq
@@ -805,7 +808,7 @@ def make_workload(wl):
         return MoeWorkload()
     if wl in (6, 7, 8):
         return DmmvKWorkload(wl)
-    if wl == 9:
+    if wl in (9, 12):
         return DmmvTokWorkload(wl)
     if wl == 10:
         return DecodeChainWorkload(wl)

@@ -158,6 +158,182 @@ __global__ __launch_bounds__(256) void dmmv_tok_kernel(const DmmvTokArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core form for tall matrices (the LM head): one
+// v_mfma_i32_16x16x32_i8 per (16 weight rows, block) gives the block's int32
+// sums for all tokens at once (tokens past n_tok are zero codes), instead of
+// 8 packed dot4 per (row, block, token) on the vector units.
+//
+// Each wave owns 16 consecutive rows and walks k in chunks of KC blocks.
+// Staging: the wave reads its 16 rows' chunk with the lanes on consecutive
+// blocks of a row (64/KC rows per load instruction, as the single-token
+// DMMV reads), and writes each block's codes (as stored) and scale (fp32) to
+// its own LDS region; the next chunk's windows are requested before this
+// chunk's arithmetic.  Compute: lane (n = lane % 16, g = lane / 16) takes
+// row n's codes for k = 8g..8g+7 (Q4_0: nibble - 8) and token n's codes for
+// the same k from LDS, and receives the sums of tokens 4g..4g+3 against row
+// n, which it rescales by d_x(token) * d_w(row) in fp32.  The workgroup
+// stages the tokens' codes ([n_tok][k]) and scales ([nb_pad][16], zero past
+// n_tok and past nb) once; blocks past nb in the last chunk read clamped
+// windows and take zero scales.
+constexpr int kTmWaves = 8;   // waves (16 rows each) per workgroup
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+template <int WT> struct Tm;
+// KC blocks per chunk: small chunks keep a workgroup's LDS small, and the
+// occupancy that buys hides more latency than longer chunks would (8 vs 32
+// blocks: 69 vs 101 us for 8 tokens through the Q4_0 LM head).
+template <> struct Tm<ZQ_Q4_0> { static constexpr int KC = 8; static constexpr int QB = 16; };
+template <> struct Tm<ZQ_Q8_0> { static constexpr int KC = 8; static constexpr int QB = 32; };
+
+// LDS rows (a token's codes, a weight row's chunk) are padded by 16 bytes,
+// so that the 16 rows a wave reads at once fall in different banks.
+constexpr int kTmPad = 16;
+
+// LDS bytes of one launch: tokens' codes [n_tok][k + pad], their scales
+// [nb_pad][16], and per wave a chunk of codes [16][KC*QB + pad] and scales
+// [KC][16].
+size_t tm_lds_bytes(int wtype, int32_t n_tok, int32_t k) {
+  const int kc = wtype == ZQ_Q4_0 ? Tm<ZQ_Q4_0>::KC : Tm<ZQ_Q8_0>::KC;
+  const int qb = wtype == ZQ_Q4_0 ? Tm<ZQ_Q4_0>::QB : Tm<ZQ_Q8_0>::QB;
+  const int64_t nb = k / 32, nb_pad = (nb + kc - 1) / kc * kc;
+  return static_cast<size_t>(n_tok) * (k + kTmPad) + static_cast<size_t>(nb_pad) * 64 +
+         static_cast<size_t>(kTmWaves) * (16 * (kc * qb + kTmPad) + kc * 64);
+}
+
+template <int WT>
+__global__ __launch_bounds__(64 * kTmWaves) void dmmv_tok_mfma_kernel(const DmmvTokArgs a) {
+  constexpr int NW = Blk<WT>::NW;
+  constexpr int BB = Blk<WT>::BYTES;
+  constexpr int KC = Tm<WT>::KC;
+  constexpr int QB = Tm<WT>::QB;
+  constexpr int RPI = 64 / KC;       // rows per staging load instruction
+  constexpr int NL = 16 / RPI;       // staging loads per lane per chunk
+  constexpr int WROW = KC * QB + kTmPad;   // LDS bytes per staged weight row
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int nb_pad = (a.nb + KC - 1) / KC * KC;
+  const int xrowb = a.k + kTmPad;          // LDS bytes per staged token
+  int8_t *lq = reinterpret_cast<int8_t *>(smem);                                        // [n_tok][k + pad]
+  float *ldx = reinterpret_cast<float *>(smem + static_cast<int64_t>(a.n_tok) * xrowb);  // [nb_pad][16]
+  const int tid = static_cast<int>(threadIdx.x);
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  uint8_t *wq = smem + static_cast<int64_t>(a.n_tok) * xrowb + static_cast<int64_t>(nb_pad) * 64 +
+                wv * (16 * WROW + KC * 64);                                            // [16][WROW]
+  float *wd = reinterpret_cast<float *>(wq + 16 * WROW);                               // [KC][16]
+
+  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * kTmWaves + wv) * 16;
+  // staging: lane -> (row row0 + RPI*l + lane / KC, block c0 + lane % KC)
+  const int sb = lane % KC;
+  const int sr = lane / KC;
+  uint32_t win[NL][NW];
+  uint32_t off[NL];
+  auto load_chunk = [&](int c0) {
+    int b = c0 + sb;
+    b = b < a.nb ? b : a.nb - 1;
+#pragma unroll
+    for (int l = 0; l < NL; ++l) {
+      int64_t row = row0 + RPI * l + sr;
+      row = row < a.rows ? row : a.rows - 1;
+      off[l] = load_window<WT>(a.w + row * a.row_bytes + static_cast<int64_t>(b) * BB, win[l]);
+    }
+  };
+  load_chunk(0);
+
+  // the tokens' codes (16-byte pieces) and scales
+  const int64_t nq = static_cast<int64_t>(a.n_tok) * a.k / 16;
+  const int qpr = a.k / 16;  // 16-byte pieces per token
+  for (int64_t q = tid; q < nq; q += 64 * kTmWaves) {
+    const int64_t t = q / qpr, in = q - t * qpr;
+    *reinterpret_cast<u32x4 *>(lq + t * xrowb + 16 * in) =
+        *reinterpret_cast<const u32x4 *>(a.qx + 16 * q);
+  }
+  for (int q = tid; q < nb_pad * 16; q += 64 * kTmWaves) {
+    const int b = q >> 4, t = q & 15;
+    ldx[q] = (t < a.n_tok && b < a.nb) ? a.dx[static_cast<int64_t>(t) * a.nb + b] : 0.0f;
+  }
+  __syncthreads();
+
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  const bool tok = n < a.n_tok;   // this lane's activation token exists
+  const int8_t *xrow = lq + static_cast<int64_t>(tok ? n : 0) * xrowb + 8 * g;
+  // this lane's 8 weight code bytes inside a staged block
+  const int qoff = WT == ZQ_Q4_0 ? 8 * (g & 1) : 8 * g;
+  const int sh = WT == ZQ_Q4_0 ? (g >> 1) * 4 : 0;  // Q4_0: low or high nibbles
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int c0 = 0; c0 < a.nb; c0 += KC) {
+    // the chunk's blocks into the wave's LDS region: codes as stored, scale
+    // as fp32
+#pragma unroll
+    for (int l = 0; l < NL; ++l) {
+      const uint32_t sel = quant_selector(off[l]);
+      uint8_t *dst = wq + (RPI * l + sr) * WROW + sb * QB;
+#pragma unroll
+      for (int q = 0; q < QB / 16; ++q) {
+        u32x4 v;
+        v.x = __builtin_amdgcn_perm(win[l][4 * q + 1], win[l][4 * q], sel);
+        v.y = __builtin_amdgcn_perm(win[l][4 * q + 2], win[l][4 * q + 1], sel);
+        v.z = __builtin_amdgcn_perm(win[l][4 * q + 3], win[l][4 * q + 2], sel);
+        v.w = __builtin_amdgcn_perm(win[l][4 * q + 4], win[l][4 * q + 3], sel);
+        *reinterpret_cast<u32x4 *>(dst + 16 * q) = v;
+      }
+      wd[sb * 16 + RPI * l + sr] = window_scale(win[l][0], off[l]);
+    }
+    // the next chunk's windows, in flight during this chunk's arithmetic
+    if (c0 + KC < a.nb) load_chunk(c0 + KC);  // uniform
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll 4
+    for (int bi = 0; bi < KC; ++bi) {
+      const int b = c0 + bi;
+      const uint2 wv2 = *reinterpret_cast<const uint2 *>(wq + n * WROW + bi * QB + qoff);
+      uint32_t c0w = wv2.x, c1w = wv2.y;
+      if constexpr (WT == ZQ_Q4_0) {
+        c0w = (((c0w >> sh) & 0x0F0F0F0Fu) + 0x78787878u) ^ 0x80808080u;
+        c1w = (((c1w >> sh) & 0x0F0F0F0Fu) + 0x78787878u) ^ 0x80808080u;
+      }
+      const float dw = wd[bi * 16 + n];
+      uint32_t x0 = 0, x1 = 0;
+      if (tok && b < a.nb) {
+        const uint2 xv = *reinterpret_cast<const uint2 *>(xrow + 32 * b);
+        x0 = xv.x;
+        x1 = xv.y;
+      }
+      const float4 dx4 = *reinterpret_cast<const float4 *>(ldx + 16 * b + 4 * g);
+      const int64_t av = static_cast<int64_t>((static_cast<uint64_t>(x1) << 32) | x0);
+      const int64_t bv = static_cast<int64_t>((static_cast<uint64_t>(c1w) << 32) | c0w);
+      const i32x4 z = {0, 0, 0, 0};
+      const i32x4 is = __builtin_amdgcn_mfma_i32_16x16x32_i8(av, bv, z, 0, 0, 0);
+      acc[0] = __builtin_fmaf(dx4.x * dw, static_cast<float>(is[0]), acc[0]);
+      acc[1] = __builtin_fmaf(dx4.y * dw, static_cast<float>(is[1]), acc[1]);
+      acc[2] = __builtin_fmaf(dx4.z * dw, static_cast<float>(is[2]), acc[2]);
+      acc[3] = __builtin_fmaf(dx4.w * dw, static_cast<float>(is[3]), acc[3]);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  if (row0 + n < a.rows) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 4 * g + r;
+      if (t < a.n_tok) {
+        float *yp = a.y + static_cast<int64_t>(t) * a.rows + row0 + n;
+        *yp = (a.flags & ZQ_ACCUMULATE) ? *yp + acc[r] : acc[r];
+      }
+    }
+  }
+}
+
+template <int WT>
+int launch_tm(const DmmvTokArgs &a, hipStream_t stream) {
+  const int64_t rows_per_wg = 16 * kTmWaves;
+  const unsigned grid = static_cast<unsigned>((a.rows + rows_per_wg - 1) / rows_per_wg);
+  hipLaunchKernelGGL((dmmv_tok_mfma_kernel<WT>), dim3(grid), dim3(64 * kTmWaves),
+                     tm_lds_bytes(WT, a.n_tok, a.k), stream, a);
+  ZQ_LAUNCH_CHECK();
+  return ZQ_OK;
+}
+
 struct TShape {
   int lpr, bpl;
 };
@@ -243,9 +419,18 @@ int launch_tw(DmmvTokArgs a, hipStream_t stream) {
 
 }  // namespace
 
+bool dmmv_tok_mfma_fits(int wtype, int64_t rows, int32_t k, int32_t n_tok) {
+  // tall matrices with three or more tokens (at two the vector units'
+  // dot products are faster), the LDS of a launch within 64 KB
+  return n_tok >= 3 && rows >= 65536 && tm_lds_bytes(wtype, n_tok, k) <= 64 * 1024;
+}
+
 int launch_dmmv_tok(int wtype, DmmvTokArgs a, hipStream_t stream) {
   if (a.rows == 0 || a.n_tok == 0) return ZQ_OK;
   a.row_bytes = static_cast<int64_t>(a.nb) * (wtype == ZQ_Q4_0 ? 18 : 34);
+  if (dmmv_tok_mfma_fits(wtype, a.rows, a.k, a.n_tok)) {
+    return wtype == ZQ_Q4_0 ? launch_tm<ZQ_Q4_0>(a, stream) : launch_tm<ZQ_Q8_0>(a, stream);
+  }
   if (wtype == ZQ_Q4_0) return launch_tw<ZQ_Q4_0>(a, stream);
   return launch_tw<ZQ_Q8_0>(a, stream);
 }

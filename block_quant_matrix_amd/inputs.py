@@ -137,6 +137,8 @@ WORKLOADS = {
     # Q5_K, shared expert Q8_0
     11: dict(name="moe_128e_top8_q4k_q5k_shared_q8_0_2048x512", n_routed=128, top_k=8,
              d_model=2048, d_ff=512, gu_wtype=Q4_K, down_wtype=Q5_K, sh_wtype=Q8_0),
+    # small-M at the vocabulary shape: eight tokens through the LM head
+    12: dict(name="q4_0_lmhead_8tok_248320x2048", wtype=Q4_0, rows=248320, k=2048, n_tok=8),
 }
 
 

@@ -123,7 +123,11 @@ int zq_dmmv_q6_k(const void *w, int64_t rows, int64_t k, const int8_t *qx, const
  *   y[t][r] (+)= sum_b fp32(d_w[r][b]) * dx[t][b] * isum_t[r][b].
  * wtype ZQ_Q4_0 or ZQ_Q8_0; qx [n_tok][k] int8 (16-byte aligned); dx
  * [n_tok][k/32]; sx [n_tok][k/32] for Q4_0, may be NULL (ignored for Q8_0);
- * y [n_tok][rows] fp32. */
+ * y [n_tok][rows] fp32.  Tall matrices (rows >= 65536, e.g. the LM head)
+ * with 3 or more tokens take the int8 matrix cores (one 16x16x32 MFMA per
+ * 16 rows and block, all tokens at once) when their staged tokens fit the
+ * workgroup's 64 KB of LDS (k = 2048: up to 8 tokens); the sums and the
+ * fp32 rescale are the same, only the association differs. */
 int zq_dmmv_tokens(int wtype, const void *w, int64_t rows, int64_t k, const int8_t *qx,
                    const float *dx, const int32_t *sx, int32_t n_tok, float *y, uint32_t flags,
                    void *stream);

@@ -125,3 +125,42 @@ def test_tokens_lmhead_sampled(zq):
                                     rng.integers(0, rows, 1000)])).astype(np.int64)
     for t, (y_ref, S) in enumerate(oracle_rows(Q4_0, w, rows, k, x, rows_eval=idx)):
         check_rows(y[t][idx], y_ref, S, "lm head 8 tokens, token %d" % t)
+
+
+# Tall matrices with 3+ tokens take the matrix-core form (rows >= 65536,
+# its LDS within 64 KB): rows ragged against the 128-row workgroups, k from
+# one block (less than one 8-block chunk) to 4096 (at 8 tokens the vector
+# form again), 2 tokens the vector form; every row's first and last outputs
+# and sampled ones against the oracle.
+@pytest.mark.parametrize("wt", [Q4_0, Q8_0])
+@pytest.mark.parametrize("n_tok", [2, 3, 5, 8])
+@pytest.mark.parametrize("rows,k", [(65536 + 37, 32), (70001, 2048), (65600, 4096)])
+def test_tokens_tall_matrix_cores(zq, wt, n_tok, rows, k):
+    if wt == Q8_0 and k == 4096:
+        pytest.skip("covered by Q4_0 at this width (host memory)")
+    seed = 7000 + 31 * n_tok + k + wt
+    w = inputs.gen_weights(wt, rows, k, seed)
+    x = inputs.gen_activation(n_tok, k, seed + 1).reshape(n_tok, k)
+    qx, dx, sx = quantize_gpu(zq, x)
+    y = host(run_tok(zq, wt, w, rows, k, qx, dx, sx, n_tok))
+    assert not np.isnan(y).any()
+    rng = np.random.default_rng(seed)
+    idx = np.unique(np.concatenate([np.arange(64), np.arange(rows - 64, rows),
+                                    rng.integers(0, rows, 512)])).astype(np.int64)
+    for t, (y_ref, S) in enumerate(oracle_rows(wt, w, rows, k, x, rows_eval=idx)):
+        check_rows(y[t][idx], y_ref, S, "tall %d x %d, %d tokens, token %d" % (rows, k, n_tok, t))
+
+
+def test_tokens_tall_accumulate(zq):
+    rows, k, n_tok = 65536 + 5, 2048, 4
+    w = inputs.gen_weights(Q4_0, rows, k, 7100)
+    x = inputs.gen_activation(n_tok, k, 7101)
+    qx, dx, sx = quantize_gpu(zq, x)
+    prev = np.random.default_rng(7102).standard_normal((n_tok, rows)).astype(np.float32)
+    y = dev(prev)
+    run_tok(zq, Q4_0, w, rows, k, qx, dx, sx, n_tok, y=y, flags=1)
+    yh = host(y)
+    idx = np.unique(np.concatenate([np.arange(16), np.arange(rows - 16, rows),
+                                    np.random.default_rng(3).integers(0, rows, 256)])).astype(np.int64)
+    for t, (y_ref, S) in enumerate(oracle_rows(Q4_0, w, rows, k, x, rows_eval=idx, y_prev=prev)):
+        check_rows(yh[t][idx], y_ref, S, "tall accumulate, token %d" % t)
