@@ -6,7 +6,7 @@ blocks, then the Q4_0 DMMV of a 4096 x 4096 weight matrix.  Weights rotate
 over distinct copies whose total is more than twice the 256 MB MALL, so every
 step streams its weights from HBM.  Prints ONE JSON line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1..6]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1..13]
 
 Timing: a GPU-side spin kernel is queued ahead of the timed region so that the
 K steps are enqueued before the GPU reaches them and run back to back (host
@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12])
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -99,7 +99,7 @@ class DmmvWorkload(Workload):
         self.wl = wl
         self.name = cfg["name"]
         self.wtype, self.rows, self.k = cfg["wtype"], cfg["rows"], cfg["k"]
-        self.argmax = wl == 3
+        self.argmax = wl in (3, 13)
         self.bb = inputs.BLOCK_BYTES[self.wtype]
         self.nb = self.k // 32
         self.wbytes = self.rows * self.nb * self.bb
@@ -116,8 +116,8 @@ class DmmvWorkload(Workload):
             self.dominant_name = "dmmv_f32x_kernel (LM head: quantize + DMMV + argmax partials)"
         self.step_bytes = self.dmmv_bytes
         # (one launch per step: K stays inside one hardware queue)
-        self.steps = {1: 3000, 2: 3000, 3: 200}[wl]
-        self.warmup = {1: 500, 2: 200, 3: 10}[wl]
+        self.steps = {1: 3000, 2: 3000, 3: 200, 13: 100}[wl]
+        self.warmup = {1: 500, 2: 200, 3: 10, 13: 5}[wl]
 
     def setup(self, torch, zq, inputs):
         self.torch, self.zq = torch, zq
@@ -802,7 +802,7 @@ def counted_traffic(kernel_name, workload):
 
 
 def make_workload(wl):
-    if wl in (1, 2, 3):
+    if wl in (1, 2, 3, 13):
         return DmmvWorkload(wl)
     if wl == 4:
         return MoeWorkload()
@@ -910,6 +910,21 @@ def main():
     torch.cuda.synchronize()
     ms_kernel = d_ev0.elapsed_time(d_ev1) / K
 
+    # --- the launch floor: K back-to-back launches of an empty kernel (torch's
+    # spin kernel with a zero count, one thread) on the same stream.  What a
+    # launch of any kernel costs before it reads a byte; at the 4096 x 4096
+    # size it is a large part of the DMMV's time.
+    f_ev0 = torch.cuda.Event(enable_timing=True)
+    f_ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    gpu_blocker(torch, 0.05 * K + 5)
+    f_ev0.record()
+    for i in range(K):
+        torch.cuda._sleep(0)
+    f_ev1.record()
+    torch.cuda.synchronize()
+    ms_floor = f_ev0.elapsed_time(f_ev1) / K
+
     value, unit = w.value(ms_per_step)
     ach, peak, runit, per_launch = w.achieved(ms_kernel)
     out = {
@@ -928,10 +943,14 @@ def main():
         "config": {"workload": w.name, "weight_copies": w.ncopy, "parallelism": "none"},
         "pct_of_peak": round(w.pct_of_peak(value, unit), 2),
     }
-    out.update({k: round(v, 1) for k, v in w.extra(ms_per_step).items()})
+    out.update({k: round(v, 4 if abs(v) < 10 else 1) for k, v in w.extra(ms_per_step).items()})
     out["roofline"] = {"bound": w.bound, "kernel": w.dominant_name, "achieved": round(ach, 3),
                        "peak": peak, "unit": runit, "frac": round(ach / peak, 4),
                        "per_launch": per_launch, "ms_per_launch": round(ms_kernel, 6),
+                       "empty_launch_ms": round(ms_floor, 6),
+                       "frac_after_empty_launch": (round(per_launch / ((ms_kernel - ms_floor) * 1e-3)
+                                                         / (1e9 if runit == "GB/s" else 1e12) / peak, 4)
+                                                   if ms_kernel > ms_floor else None),
                        "traffic": counted_traffic(w.dominant_name,
                                                   getattr(w, "traffic_workload", w.name))}
     if not args.no_cpu_baseline:

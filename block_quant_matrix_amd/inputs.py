@@ -139,6 +139,7 @@ WORKLOADS = {
              d_model=2048, d_ff=512, gu_wtype=Q4_K, down_wtype=Q5_K, sh_wtype=Q8_0),
     # small-M at the vocabulary shape: eight tokens through the LM head
     12: dict(name="q4_0_lmhead_8tok_248320x2048", wtype=Q4_0, rows=248320, k=2048, n_tok=8),
+    13: dict(name="q8_0_lmhead_248320x2048_argmax", wtype=Q8_0, rows=248320, k=2048),
 }
 
 

@@ -404,14 +404,15 @@ def test_lmhead_fused_ties_and_ends(zq):
         assert idx == min(rows_at), rows_at
 
 
-def test_workload_lmhead_two_launch_full(zq):
-    """248320 x 2048 Q4_0 through zq_dmmv_f32_argmax: the same logits as
-    zq_dmmv_f32, bit for bit, the oracle's within the bar, and the exact
-    argmax of them."""
-    cfg = inputs.WORKLOADS[3]
+@pytest.mark.parametrize("wl", [3, 13])
+def test_workload_lmhead_two_launch_full(zq, wl):
+    """248320 x 2048 Q4_0 and Q8_0 through zq_dmmv_f32_argmax: the same
+    logits as zq_dmmv_f32, bit for bit, the oracle's within the bar, and the
+    exact argmax of them."""
+    cfg = inputs.WORKLOADS[wl]
     wt, rows, k = cfg["wtype"], cfg["rows"], cfg["k"]
-    w = inputs.gen_weights(wt, rows, k, inputs.seed_for(3))
-    x = inputs.gen_activation(1, k, inputs.seed_for(3) + 1)
+    w = inputs.gen_weights(wt, rows, k, inputs.seed_for(wl))
+    x = inputs.gen_activation(1, k, inputs.seed_for(wl) + 1)
     wd = dev(w)
     y, idx = lmhead_gpu(zq, wt, wd, rows, k, x)
     y_f = fused_rows(zq, wt, wd, rows, k, x)

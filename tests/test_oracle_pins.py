@@ -278,7 +278,7 @@ def test_p8_bruteforce_tiny(ref, wtype, k):
     assert (np.abs(y - ybf) <= 1e-12 * S).all()
 
 
-@pytest.mark.parametrize("wl", [1, 2, 3])
+@pytest.mark.parametrize("wl", [1, 2, 3, 13])
 def test_p8_bruteforce_sampled_workloads(ref, wl):
     cfg = inputs.WORKLOADS[wl]
     w = inputs.gen_weights(cfg["wtype"], cfg["rows"], cfg["k"], inputs.seed_for(wl))
