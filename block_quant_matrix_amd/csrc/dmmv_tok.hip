@@ -161,21 +161,30 @@ __global__ __launch_bounds__(256) void dmmv_tok_kernel(const DmmvTokArgs a) {
 // ---------------------------------------------------------------------------
 // Matrix-core form for tall matrices (the LM head): one
 // v_mfma_i32_16x16x32_i8 per (16 weight rows, block) gives the block's int32
-// sums for all tokens at once (tokens past n_tok are zero codes), instead of
-// 8 packed dot4 per (row, block, token) on the vector units.
+// sums for all tokens at once (tokens past n_tok read token 0's codes and
+// take zero scales), instead of 8 packed dot4 per (row, block, token) on the
+// vector units.
 //
 // Each wave owns 16 consecutive rows and walks k in chunks of KC blocks.
 // Staging: the wave reads its 16 rows' chunk with the lanes on consecutive
 // blocks of a row (64/KC rows per load instruction, as the single-token
-// DMMV reads), and writes each block's codes (as stored) and scale (fp32) to
-// its own LDS region; the next chunk's windows are requested before this
-// chunk's arithmetic.  Compute: lane (n = lane % 16, g = lane / 16) takes
-// row n's codes for k = 8g..8g+7 (Q4_0: nibble - 8) and token n's codes for
-// the same k from LDS, and receives the sums of tokens 4g..4g+3 against row
-// n, which it rescales by d_x(token) * d_w(row) in fp32.  The workgroup
-// stages the tokens' codes ([n_tok][k]) and scales ([nb_pad][16], zero past
-// n_tok and past nb) once; blocks past nb in the last chunk read clamped
-// windows and take zero scales.
+// DMMV reads), and writes each block's codes and scale (fp32) to its own LDS
+// region; the next chunk's windows are requested before this chunk's
+// arithmetic.  Compute: lane (n = lane % 16, g = lane / 16) takes row n's
+// codes for k = 8g..8g+7 and token n's codes for the same k from LDS, and
+// receives the sums of tokens 4g..4g+3 against row n.
+//
+// Q4_0 codes are staged with every nibble's top bit flipped (q ^ 8), so a
+// nibble moved to the high half of its byte reads as the int8 16 * (q - 8):
+// lanes of low nibbles shift left by 4, lanes of high nibbles keep them in
+// place, and one AND clears the rest.  The sums come out 16 times too large,
+// exactly; the staged scale carries the 1/16.
+//
+// With at most 8 tokens only the lanes g = 0, 1 hold real tokens.  Blocks
+// are taken in pairs: v_permlane32_swap moves the second block's real half
+// into the first block's lanes 32..63, so one convert / scale / FMA pass
+// rescales both blocks (lanes 0..31 accumulate the even blocks, 32..63 the
+// odd ones), and the halves are added once at the end.
 constexpr int kTmWaves = 8;   // waves (16 rows each) per workgroup
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
@@ -183,23 +192,35 @@ typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 template <int WT> struct Tm;
 // KC blocks per chunk: small chunks keep a workgroup's LDS small, and the
 // occupancy that buys hides more latency than longer chunks would (8 vs 32
-// blocks: 69 vs 101 us for 8 tokens through the Q4_0 LM head).
+// blocks: 69 vs 101 us for 8 tokens through the Q4_0 LM head).  KC is even:
+// blocks are rescaled in pairs.
 template <> struct Tm<ZQ_Q4_0> { static constexpr int KC = 8; static constexpr int QB = 16; };
 template <> struct Tm<ZQ_Q8_0> { static constexpr int KC = 8; static constexpr int QB = 32; };
 
-// LDS rows (a token's codes, a weight row's chunk) are padded by 16 bytes,
-// so that the 16 rows a wave reads at once fall in different banks.
-constexpr int kTmPad = 16;
+// LDS row padding.  A staged weight row (KC*QB + 8 bytes, 34 dwords for
+// Q4_0) puts the 16 rows a wave reads at once 2 banks apart; a token's row
+// (k + 32 bytes, 8 banks apart for k a multiple of 256) does the same for
+// the 8 tokens x 4 k-groups of one read.  At 8 tokens and k = 2048 a Q4_0
+// launch then needs 39.1 KB, so 4 workgroups (32 waves) fit in a CU.
+constexpr int kTmPad = 8;
+constexpr int kTmXPad = 32;
 
-// LDS bytes of one launch: tokens' codes [n_tok][k + pad], their scales
-// [nb_pad][16], and per wave a chunk of codes [16][KC*QB + pad] and scales
+// LDS bytes of one launch: tokens' codes [n_tok][k + xpad], their scales
+// [nb_pad][8], and per wave a chunk of codes [16][KC*QB + pad] and scales
 // [KC][16].
 size_t tm_lds_bytes(int wtype, int32_t n_tok, int32_t k) {
   const int kc = wtype == ZQ_Q4_0 ? Tm<ZQ_Q4_0>::KC : Tm<ZQ_Q8_0>::KC;
   const int qb = wtype == ZQ_Q4_0 ? Tm<ZQ_Q4_0>::QB : Tm<ZQ_Q8_0>::QB;
   const int64_t nb = k / 32, nb_pad = (nb + kc - 1) / kc * kc;
-  return static_cast<size_t>(n_tok) * (k + kTmPad) + static_cast<size_t>(nb_pad) * 64 +
+  return static_cast<size_t>(n_tok) * (k + kTmXPad) + static_cast<size_t>(nb_pad) * 32 +
          static_cast<size_t>(kTmWaves) * (16 * (kc * qb + kTmPad) + kc * 64);
+}
+
+__device__ __forceinline__ void swap32_i(int32_t &a, int32_t &b) {
+  auto r = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(a), static_cast<uint32_t>(b),
+                                            false, false);
+  a = static_cast<int32_t>(r[0]);
+  b = static_cast<int32_t>(r[1]);
 }
 
 template <int WT>
@@ -211,15 +232,16 @@ __global__ __launch_bounds__(64 * kTmWaves) void dmmv_tok_mfma_kernel(const Dmmv
   constexpr int RPI = 64 / KC;       // rows per staging load instruction
   constexpr int NL = 16 / RPI;       // staging loads per lane per chunk
   constexpr int WROW = KC * QB + kTmPad;   // LDS bytes per staged weight row
+  static_assert(KC % 2 == 0, "blocks are rescaled in pairs");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int nb_pad = (a.nb + KC - 1) / KC * KC;
-  const int xrowb = a.k + kTmPad;          // LDS bytes per staged token
-  int8_t *lq = reinterpret_cast<int8_t *>(smem);                                        // [n_tok][k + pad]
-  float *ldx = reinterpret_cast<float *>(smem + static_cast<int64_t>(a.n_tok) * xrowb);  // [nb_pad][16]
+  const int xrowb = a.k + kTmXPad;         // LDS bytes per staged token
+  int8_t *lq = reinterpret_cast<int8_t *>(smem);                                        // [n_tok][k + xpad]
+  float *ldx = reinterpret_cast<float *>(smem + static_cast<int64_t>(a.n_tok) * xrowb);  // [nb_pad][8]
   const int tid = static_cast<int>(threadIdx.x);
   const int lane = tid & 63;
   const int wv = tid >> 6;
-  uint8_t *wq = smem + static_cast<int64_t>(a.n_tok) * xrowb + static_cast<int64_t>(nb_pad) * 64 +
+  uint8_t *wq = smem + static_cast<int64_t>(a.n_tok) * xrowb + static_cast<int64_t>(nb_pad) * 32 +
                 wv * (16 * WROW + KC * 64);                                            // [16][WROW]
   float *wd = reinterpret_cast<float *>(wq + 16 * WROW);                               // [KC][16]
 
@@ -227,45 +249,55 @@ __global__ __launch_bounds__(64 * kTmWaves) void dmmv_tok_mfma_kernel(const Dmmv
   // staging: lane -> (row row0 + RPI*l + lane / KC, block c0 + lane % KC)
   const int sb = lane % KC;
   const int sr = lane / KC;
+  const uint8_t *wrow[NL];
+#pragma unroll
+  for (int l = 0; l < NL; ++l) {
+    int64_t row = row0 + RPI * l + sr;
+    row = row < a.rows ? row : a.rows - 1;
+    wrow[l] = a.w + row * a.row_bytes;
+  }
   uint32_t win[NL][NW];
   uint32_t off[NL];
   auto load_chunk = [&](int c0) {
     int b = c0 + sb;
     b = b < a.nb ? b : a.nb - 1;
 #pragma unroll
-    for (int l = 0; l < NL; ++l) {
-      int64_t row = row0 + RPI * l + sr;
-      row = row < a.rows ? row : a.rows - 1;
-      off[l] = load_window<WT>(a.w + row * a.row_bytes + static_cast<int64_t>(b) * BB, win[l]);
-    }
+    for (int l = 0; l < NL; ++l) off[l] = load_window<WT>(wrow[l] + b * BB, win[l]);
   };
   load_chunk(0);
 
-  // the tokens' codes (16-byte pieces) and scales
-  const int64_t nq = static_cast<int64_t>(a.n_tok) * a.k / 16;
-  const int qpr = a.k / 16;  // 16-byte pieces per token
-  for (int64_t q = tid; q < nq; q += 64 * kTmWaves) {
-    const int64_t t = q / qpr, in = q - t * qpr;
+  // the tokens' codes (16-byte pieces; n_tok * k / 16 < 2^32, so the
+  // piece -> token division is a 32-bit one) and scales
+  const uint32_t nq = static_cast<uint32_t>(a.n_tok) * static_cast<uint32_t>(a.k / 16);
+  const uint32_t qpr = static_cast<uint32_t>(a.k / 16);  // 16-byte pieces per token
+  for (uint32_t q = tid; q < nq; q += 64 * kTmWaves) {
+    const uint32_t t = q / qpr, in = q - t * qpr;
     *reinterpret_cast<u32x4 *>(lq + t * xrowb + 16 * in) =
-        *reinterpret_cast<const u32x4 *>(a.qx + 16 * q);
+        *reinterpret_cast<const u32x4 *>(a.qx + 16 * static_cast<int64_t>(q));
   }
-  for (int q = tid; q < nb_pad * 16; q += 64 * kTmWaves) {
-    const int b = q >> 4, t = q & 15;
+  for (int q = tid; q < nb_pad * 8; q += 64 * kTmWaves) {
+    const int b = q >> 3, t = q & 7;
     ldx[q] = (t < a.n_tok && b < a.nb) ? a.dx[static_cast<int64_t>(t) * a.nb + b] : 0.0f;
   }
   __syncthreads();
 
   const int n = lane & 15;
   const int g = lane >> 4;
-  const bool tok = n < a.n_tok;   // this lane's activation token exists
-  const int8_t *xrow = lq + static_cast<int64_t>(tok ? n : 0) * xrowb + 8 * g;
+  const int hb = g >> 1;   // after the swap: 0 = the pair's first block, 1 = its second
+  const int tg = g & 1;    // tokens 4*tg .. 4*tg+3 of that block
+  // Token n's row (token 0's for n >= n_tok: those sums are never used).
+  // Blocks past nb read up to 32 * (nb_pad - nb) - 32 bytes past the last
+  // token's codes, into the scale table that follows; their scales are zero.
+  const int8_t *xrow = lq + static_cast<int64_t>(n < a.n_tok ? n : 0) * xrowb + 8 * g;
   // this lane's 8 weight code bytes inside a staged block
   const int qoff = WT == ZQ_Q4_0 ? 8 * (g & 1) : 8 * g;
-  const int sh = WT == ZQ_Q4_0 ? (g >> 1) * 4 : 0;  // Q4_0: low or high nibbles
+  const int shl = WT == ZQ_Q4_0 ? (1 - (g >> 1)) * 4 : 0;  // Q4_0: low nibbles move up
+  const uint8_t *wl = wq + n * WROW + qoff;
   float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int c0 = 0; c0 < a.nb; c0 += KC) {
-    // the chunk's blocks into the wave's LDS region: codes as stored, scale
-    // as fp32
+    // the chunk's blocks into the wave's LDS region: codes (Q4_0: nibbles
+    // with the top bit flipped), scale as fp32 (Q4_0: / 16; 0 for the
+    // clamped blocks past nb)
 #pragma unroll
     for (int l = 0; l < NL; ++l) {
       const uint32_t sel = quant_selector(off[l]);
@@ -277,42 +309,61 @@ __global__ __launch_bounds__(64 * kTmWaves) void dmmv_tok_mfma_kernel(const Dmmv
         v.y = __builtin_amdgcn_perm(win[l][4 * q + 2], win[l][4 * q + 1], sel);
         v.z = __builtin_amdgcn_perm(win[l][4 * q + 3], win[l][4 * q + 2], sel);
         v.w = __builtin_amdgcn_perm(win[l][4 * q + 4], win[l][4 * q + 3], sel);
-        *reinterpret_cast<u32x4 *>(dst + 16 * q) = v;
+        if constexpr (WT == ZQ_Q4_0) v ^= 0x88888888u;
+        // rows are 8-byte aligned (WROW = 8 mod 16)
+        *reinterpret_cast<uint2 *>(dst + 16 * q) = uint2{v.x, v.y};
+        *reinterpret_cast<uint2 *>(dst + 16 * q + 8) = uint2{v.z, v.w};
       }
-      wd[sb * 16 + RPI * l + sr] = window_scale(win[l][0], off[l]);
+      const float d = window_scale(win[l][0], off[l]);
+      wd[sb * 16 + RPI * l + sr] = c0 + sb >= a.nb ? 0.0f : WT == ZQ_Q4_0 ? d * 0.0625f : d;
     }
     // the next chunk's windows, in flight during this chunk's arithmetic
     if (c0 + KC < a.nb) load_chunk(c0 + KC);  // uniform
     __builtin_amdgcn_wave_barrier();
-#pragma unroll 4
-    for (int bi = 0; bi < KC; ++bi) {
+#pragma unroll
+    for (int bi = 0; bi < KC; bi += 2) {
       const int b = c0 + bi;
-      const uint2 wv2 = *reinterpret_cast<const uint2 *>(wq + n * WROW + bi * QB + qoff);
-      uint32_t c0w = wv2.x, c1w = wv2.y;
+      uint2 wa = *reinterpret_cast<const uint2 *>(wl + bi * QB);
+      uint2 wb = *reinterpret_cast<const uint2 *>(wl + (bi + 1) * QB);
       if constexpr (WT == ZQ_Q4_0) {
-        c0w = (((c0w >> sh) & 0x0F0F0F0Fu) + 0x78787878u) ^ 0x80808080u;
-        c1w = (((c1w >> sh) & 0x0F0F0F0Fu) + 0x78787878u) ^ 0x80808080u;
+        wa.x = (wa.x << shl) & 0xF0F0F0F0u;
+        wa.y = (wa.y << shl) & 0xF0F0F0F0u;
+        wb.x = (wb.x << shl) & 0xF0F0F0F0u;
+        wb.y = (wb.y << shl) & 0xF0F0F0F0u;
       }
-      const float dw = wd[bi * 16 + n];
-      uint32_t x0 = 0, x1 = 0;
-      if (tok && b < a.nb) {
-        const uint2 xv = *reinterpret_cast<const uint2 *>(xrow + 32 * b);
-        x0 = xv.x;
-        x1 = xv.y;
-      }
-      const float4 dx4 = *reinterpret_cast<const float4 *>(ldx + 16 * b + 4 * g);
-      const int64_t av = static_cast<int64_t>((static_cast<uint64_t>(x1) << 32) | x0);
-      const int64_t bv = static_cast<int64_t>((static_cast<uint64_t>(c1w) << 32) | c0w);
+      const uint2 xa = *reinterpret_cast<const uint2 *>(xrow + 32 * b);
+      const uint2 xb = *reinterpret_cast<const uint2 *>(xrow + 32 * (b + 1));
+      const float4 dx4 = *reinterpret_cast<const float4 *>(ldx + 8 * (b + hb) + 4 * tg);
+      const float dw = wd[(bi + hb) * 16 + n];
       const i32x4 z = {0, 0, 0, 0};
-      const i32x4 is = __builtin_amdgcn_mfma_i32_16x16x32_i8(av, bv, z, 0, 0, 0);
-      acc[0] = __builtin_fmaf(dx4.x * dw, static_cast<float>(is[0]), acc[0]);
-      acc[1] = __builtin_fmaf(dx4.y * dw, static_cast<float>(is[1]), acc[1]);
-      acc[2] = __builtin_fmaf(dx4.z * dw, static_cast<float>(is[2]), acc[2]);
-      acc[3] = __builtin_fmaf(dx4.w * dw, static_cast<float>(is[3]), acc[3]);
+      i32x4 sa = __builtin_amdgcn_mfma_i32_16x16x32_i8(
+          static_cast<int64_t>((static_cast<uint64_t>(xa.y) << 32) | xa.x),
+          static_cast<int64_t>((static_cast<uint64_t>(wa.y) << 32) | wa.x), z, 0, 0, 0);
+      i32x4 sb2 = __builtin_amdgcn_mfma_i32_16x16x32_i8(
+          static_cast<int64_t>((static_cast<uint64_t>(xb.y) << 32) | xb.x),
+          static_cast<int64_t>((static_cast<uint64_t>(wb.y) << 32) | wb.x), z, 0, 0, 0);
+      int32_t s[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        int32_t u = sa[r], v = sb2[r];
+        swap32_i(u, v);   // u: lanes 0..31 block b, lanes 32..63 block b + 1
+        s[r] = u;
+      }
+      acc[0] = __builtin_fmaf(dx4.x * dw, static_cast<float>(s[0]), acc[0]);
+      acc[1] = __builtin_fmaf(dx4.y * dw, static_cast<float>(s[1]), acc[1]);
+      acc[2] = __builtin_fmaf(dx4.z * dw, static_cast<float>(s[2]), acc[2]);
+      acc[3] = __builtin_fmaf(dx4.w * dw, static_cast<float>(s[3]), acc[3]);
     }
     __builtin_amdgcn_wave_barrier();
   }
-  if (row0 + n < a.rows) {
+  // lanes 0..31 add the odd blocks' sums held by lanes 32..63
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float u = acc[r], v = acc[r];
+    swap32(u, v);   // v: lanes 0..31 hold lanes 32..63 of acc
+    acc[r] += v;
+  }
+  if (g < 2 && row0 + n < a.rows) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = 4 * g + r;
@@ -420,9 +471,10 @@ int launch_tw(DmmvTokArgs a, hipStream_t stream) {
 }  // namespace
 
 bool dmmv_tok_mfma_fits(int wtype, int64_t rows, int32_t k, int32_t n_tok) {
-  // tall matrices with three or more tokens (at two the vector units'
-  // dot products are faster), the LDS of a launch within 64 KB
-  return n_tok >= 3 && rows >= 65536 && tm_lds_bytes(wtype, n_tok, k) <= 64 * 1024;
+  // tall matrices with three to eight tokens (at two the vector units'
+  // dot products are faster; the kernel keeps real tokens in lanes 0..31),
+  // the LDS of a launch within 64 KB
+  return n_tok >= 3 && n_tok <= 8 && rows >= 65536 && tm_lds_bytes(wtype, n_tok, k) <= 64 * 1024;
 }
 
 int launch_dmmv_tok(int wtype, DmmvTokArgs a, hipStream_t stream) {
