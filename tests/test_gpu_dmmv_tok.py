@@ -130,11 +130,13 @@ def test_tokens_lmhead_sampled(zq):
 # Tall matrices with 3+ tokens take the matrix-core form (rows >= 65536,
 # its LDS within 64 KB): rows ragged against the 128-row workgroups, k from
 # one block (less than one 8-block chunk) to 4096 (at 8 tokens the vector
-# form again), 2 tokens the vector form; every row's first and last outputs
-# and sampled ones against the oracle.
+# form again), block counts that end a chunk part-way and split a pair of
+# blocks (9 and 65), 2 tokens the vector form; every row's first and last
+# outputs and sampled ones against the oracle.
 @pytest.mark.parametrize("wt", [Q4_0, Q8_0])
 @pytest.mark.parametrize("n_tok", [2, 3, 5, 8])
-@pytest.mark.parametrize("rows,k", [(65536 + 37, 32), (70001, 2048), (65600, 4096)])
+@pytest.mark.parametrize("rows,k", [(65536 + 37, 32), (65536 + 1, 288), (70001, 2048),
+                                    (66000, 2080), (65600, 4096)])
 def test_tokens_tall_matrix_cores(zq, wt, n_tok, rows, k):
     if wt == Q8_0 and k == 4096:
         pytest.skip("covered by Q4_0 at this width (host memory)")
