@@ -273,8 +273,8 @@ class DmmvKWorkload(Workload):
 
 class DmmvTokWorkload(Workload):
     """Quantize T tokens + one multi-token DMMV (two launches): the small-M
-    decode shapes, Q4_0 4096 x 4096 (vector units) and the 248 320-row LM
-    head (matrix cores)."""
+    decode shapes, Q4_0 4096 x 4096 (the tile form on the matrix cores) and
+    the 248 320-row LM head (the tall form on the matrix cores)."""
     dominant_name = "dmmv_tok_kernel"
 
     def __init__(self, wl):
@@ -283,9 +283,14 @@ class DmmvTokWorkload(Workload):
         self.wl = wl
         self.name = cfg["name"]
         self.wtype, self.rows, self.k, self.T = cfg["wtype"], cfg["rows"], cfg["k"], cfg["n_tok"]
+        self.nb = self.k // 32
         if self.rows >= 65536 and self.T >= 3:
             self.dominant_name = "dmmv_tok_mfma_kernel (matrix cores)"
-        self.nb = self.k // 32
+        elif self.T >= 5 and 64 <= self.nb <= 128 and self.rows * self.k >= 8 << 20:
+            # (the library's choice for these shapes; Q8_0 rows of more than
+            # 88 blocks exceed its LDS and stay on the vector form)
+            if self.wtype == 4 or self.nb <= 88:
+                self.dominant_name = "dmmv_tok_tile_kernel (matrix cores)"
         self.wbytes = self.rows * self.nb * inputs.BLOCK_BYTES[self.wtype]
         # the DMMV reads the weights once and every token's codes, scales and
         # sums, and writes T rows of fp32; the step adds the quantizer's fp32

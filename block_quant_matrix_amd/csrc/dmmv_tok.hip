@@ -385,6 +385,199 @@ int launch_tm(const DmmvTokArgs &a, hipStream_t stream) {
   return ZQ_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Tile form on the matrix cores for matrices too short for the tall form
+// (fewer than 65 536 rows, e.g. 4096 x 4096): one workgroup of 16 waves per
+// 16 rows and rows of up to 128 blocks.  Wave w reads row w whole (the
+// lanes on consecutive blocks, as the single-token DMMV reads a row: split
+// over several waves, a row reads far slower) into the workgroup's LDS tile,
+// and with it the tokens' codes of its chunk (8 bytes per lane and block,
+// straight from global memory); after one barrier wave w takes KC-block
+// chunk w of all 16 rows on the matrix cores.  The waves' partial sums meet
+// in LDS and 128 threads add them in wave order and store.
+constexpr int kTtWaves = 16;
+
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(1))) const u32x2v g_u32x2;
+
+// Tile geometry: codes [16][nb_pad*QB + 16] (a row stride of an odd number
+// of 16-byte units puts the 16 rows of a read in different banks), scales
+// [16][nb_pad + 1] fp32, the tokens' scales [nb_pad][8], partials
+// [16][32][4].
+struct TtLayout {
+  int64_t nb_pad, crow, srow, scales, ldx, red, bytes;
+  __host__ __device__ TtLayout(int wtype, int32_t nb) {
+    const int qb = wtype == ZQ_Q4_0 ? Tm<ZQ_Q4_0>::QB : Tm<ZQ_Q8_0>::QB;
+    const int kc = Tm<ZQ_Q4_0>::KC;
+    nb_pad = (nb + kc - 1) / kc * kc;
+    crow = nb_pad * qb + 16;
+    srow = nb_pad + 1;
+    scales = 16 * crow;
+    ldx = scales + 16 * srow * 4;
+    red = ldx + nb_pad * 32;
+    bytes = red + kTtWaves * 32 * 4 * 4;
+  }
+};
+
+template <int WT, int BPL>
+__global__ __launch_bounds__(64 * kTtWaves) void dmmv_tok_tile_kernel(const DmmvTokArgs a) {
+  constexpr int NW = Blk<WT>::NW;
+  constexpr int BB = Blk<WT>::BYTES;
+  constexpr int KC = Tm<WT>::KC;
+  constexpr int QB = Tm<WT>::QB;
+  static_assert(KC % 2 == 0, "blocks are rescaled in pairs");
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const TtLayout T(WT, a.nb);
+  const int nb_pad = static_cast<int>(T.nb_pad);
+  const int n_chunks = nb_pad / KC;
+  const int W = n_chunks < kTtWaves ? n_chunks : kTtWaves;   // waves with a chunk
+  const int tid = static_cast<int>(threadIdx.x);
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  uint8_t *tq = smem;                                               // [16][crow]
+  float *ts = reinterpret_cast<float *>(smem + T.scales);           // [16][srow]
+  float *ldx = reinterpret_cast<float *>(smem + T.ldx);             // [nb_pad][8]
+  float *red = reinterpret_cast<float *>(smem + T.red);             // [16][32][4]
+  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * 16;
+  // (nb <= 128: at most 16 chunks, so wave wv has chunk wv or none)
+  const int c0 = wv * KC;
+  const bool has_chunk = wv < n_chunks;   // uniform over the wave
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  const int hb = g >> 1;
+  const int tg = g & 1;
+  // this wave's tokens' codes (token n's for k = 8g..8g+7 of each block of
+  // its chunk; token 0's for n >= n_tok, whose sums take zero scales),
+  // requested with the weights
+  const int8_t *xg = a.qx + static_cast<int64_t>(n < a.n_tok ? n : 0) * a.k + 8 * g;
+  u32x2v x[KC];
+  if (has_chunk) {
+#pragma unroll
+    for (int bi = 0; bi < KC; ++bi) {
+      const int bx = c0 + bi < a.nb ? c0 + bi : a.nb - 1;
+      x[bi] = *(const g_u32x2 *)(xg + 32 * bx);
+    }
+  }
+
+  // 1. wave wv reads row row0 + wv: lane j takes blocks j, j + 64, ...
+  {
+    int64_t row = row0 + wv;
+    row = row < a.rows ? row : a.rows - 1;
+    const uint8_t *wr = a.w + row * a.row_bytes;
+    uint32_t win[BPL][NW];
+    uint32_t off[BPL];
+#pragma unroll
+    for (int i = 0; i < BPL; ++i) {
+      int b = lane + 64 * i;
+      b = b < a.nb ? b : a.nb - 1;
+      off[i] = load_window<WT>(wr + b * BB, win[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < BPL; ++i) {
+      const int b = lane + 64 * i;
+      if (b < nb_pad) {
+        const uint32_t sel = quant_selector(off[i]);
+        uint8_t *dst = tq + wv * T.crow + b * QB;
+#pragma unroll
+        for (int q = 0; q < QB / 16; ++q) {
+          u32x4 v;
+          v.x = __builtin_amdgcn_perm(win[i][4 * q + 1], win[i][4 * q], sel);
+          v.y = __builtin_amdgcn_perm(win[i][4 * q + 2], win[i][4 * q + 1], sel);
+          v.z = __builtin_amdgcn_perm(win[i][4 * q + 3], win[i][4 * q + 2], sel);
+          v.w = __builtin_amdgcn_perm(win[i][4 * q + 4], win[i][4 * q + 3], sel);
+          if constexpr (WT == ZQ_Q4_0) v ^= 0x88888888u;
+          *reinterpret_cast<u32x4 *>(dst + 16 * q) = v;
+        }
+        const float d = window_scale(win[i][0], off[i]);
+        ts[wv * T.srow + b] = b >= a.nb ? 0.0f : WT == ZQ_Q4_0 ? d * 0.0625f : d;
+      }
+    }
+  }
+  for (int q = tid; q < nb_pad * 8; q += 64 * kTtWaves) {
+    const int b = q >> 3, t = q & 7;
+    ldx[q] = (t < a.n_tok && b < a.nb) ? a.dx[static_cast<int64_t>(t) * a.nb + b] : 0.0f;
+  }
+  __syncthreads();
+
+  // 3. wave wv: chunk wv of all 16 rows
+  const int qoff = WT == ZQ_Q4_0 ? 8 * (g & 1) : 8 * g;
+  const int shl = WT == ZQ_Q4_0 ? (1 - (g >> 1)) * 4 : 0;
+  const uint8_t *wl = tq + n * T.crow + qoff;
+  const float *wsl = ts + n * T.srow;
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (has_chunk) {
+#pragma unroll
+    for (int bi = 0; bi < KC; bi += 2) {
+      const int b = c0 + bi;
+      uint2 wa = *reinterpret_cast<const uint2 *>(wl + b * QB);
+      uint2 wb = *reinterpret_cast<const uint2 *>(wl + (b + 1) * QB);
+      if constexpr (WT == ZQ_Q4_0) {
+        wa.x = (wa.x << shl) & 0xF0F0F0F0u;
+        wa.y = (wa.y << shl) & 0xF0F0F0F0u;
+        wb.x = (wb.x << shl) & 0xF0F0F0F0u;
+        wb.y = (wb.y << shl) & 0xF0F0F0F0u;
+      }
+      const float4 dx4 = *reinterpret_cast<const float4 *>(ldx + 8 * (b + hb) + 4 * tg);
+      const float dw = wsl[b + hb];
+      const i32x4 z = {0, 0, 0, 0};
+      i32x4 sa = __builtin_amdgcn_mfma_i32_16x16x32_i8(
+          static_cast<int64_t>((static_cast<uint64_t>(x[bi].y) << 32) | x[bi].x),
+          static_cast<int64_t>((static_cast<uint64_t>(wa.y) << 32) | wa.x), z, 0, 0, 0);
+      i32x4 sb2 = __builtin_amdgcn_mfma_i32_16x16x32_i8(
+          static_cast<int64_t>((static_cast<uint64_t>(x[bi + 1].y) << 32) | x[bi + 1].x),
+          static_cast<int64_t>((static_cast<uint64_t>(wb.y) << 32) | wb.x), z, 0, 0, 0);
+      int32_t s4[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        int32_t u = sa[r], v = sb2[r];
+        swap32_i(u, v);   // u: lanes 0..31 block b, lanes 32..63 block b + 1
+        s4[r] = u;
+      }
+      acc[0] = __builtin_fmaf(dx4.x * dw, static_cast<float>(s4[0]), acc[0]);
+      acc[1] = __builtin_fmaf(dx4.y * dw, static_cast<float>(s4[1]), acc[1]);
+      acc[2] = __builtin_fmaf(dx4.z * dw, static_cast<float>(s4[2]), acc[2]);
+      acc[3] = __builtin_fmaf(dx4.w * dw, static_cast<float>(s4[3]), acc[3]);
+    }
+  }
+  // 4. this wave's partials: lanes 0..31 add the odd blocks' sums of lanes
+  // 32..63 and leave (token 4g + r, row n) in LDS; then the sum over the
+  // waves that had a chunk
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float u = acc[r], v = acc[r];
+    swap32(u, v);
+    acc[r] += v;
+  }
+  if (wv < W && lane < 32) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[(wv * 32 + lane) * 4 + r] = acc[r];
+  }
+  __syncthreads();
+  if (tid < 128) {
+    const int L = tid & 31, r = tid >> 5;
+    const int t = 4 * (L >> 4) + r;
+    const int64_t row = row0 + (L & 15);
+    float sum = 0.0f;
+    for (int w = 0; w < W; ++w) sum += red[(w * 32 + L) * 4 + r];
+    if (t < a.n_tok && row < a.rows) {
+      float *yp = a.y + static_cast<int64_t>(t) * a.rows + row;
+      *yp = (a.flags & ZQ_ACCUMULATE) ? *yp + sum : sum;
+    }
+  }
+}
+
+template <int WT>
+int launch_tt(const DmmvTokArgs &a, hipStream_t stream) {
+  const unsigned grid = static_cast<unsigned>((a.rows + 15) / 16);
+  const size_t lds = static_cast<size_t>(TtLayout(WT, a.nb).bytes);
+  if (a.nb <= 64)
+    hipLaunchKernelGGL((dmmv_tok_tile_kernel<WT, 1>), dim3(grid), dim3(64 * kTtWaves), lds, stream, a);
+  else
+    hipLaunchKernelGGL((dmmv_tok_tile_kernel<WT, 2>), dim3(grid), dim3(64 * kTtWaves), lds, stream, a);
+  ZQ_LAUNCH_CHECK();
+  return ZQ_OK;
+}
+
 struct TShape {
   int lpr, bpl;
 };
@@ -477,11 +670,25 @@ bool dmmv_tok_mfma_fits(int wtype, int64_t rows, int32_t k, int32_t n_tok) {
   return n_tok >= 3 && n_tok <= 8 && rows >= 65536 && tm_lds_bytes(wtype, n_tok, k) <= 64 * 1024;
 }
 
+// Shorter matrices: the tile form where it measured faster than the vector
+// form -- five to eight tokens, rows of 64 to 128 blocks, at least 8 M
+// weights (4096 x 4096 at 8 tokens: 6.8 against 7.4 us; at 3 tokens, or
+// 1024 x 2048, or 20000 x 1024, the vector form is faster) -- with its LDS
+// within 64 KB.
+bool dmmv_tok_tile_fits(int wtype, int64_t rows, int32_t k, int32_t n_tok) {
+  const int32_t nb = k / 32;
+  return n_tok >= 5 && n_tok <= 8 && rows < 65536 && nb >= 64 && nb <= 128 &&
+         rows * k >= (int64_t(8) << 20) && TtLayout(wtype, nb).bytes <= 64 * 1024;
+}
+
 int launch_dmmv_tok(int wtype, DmmvTokArgs a, hipStream_t stream) {
   if (a.rows == 0 || a.n_tok == 0) return ZQ_OK;
   a.row_bytes = static_cast<int64_t>(a.nb) * (wtype == ZQ_Q4_0 ? 18 : 34);
   if (dmmv_tok_mfma_fits(wtype, a.rows, a.k, a.n_tok)) {
     return wtype == ZQ_Q4_0 ? launch_tm<ZQ_Q4_0>(a, stream) : launch_tm<ZQ_Q8_0>(a, stream);
+  }
+  if (dmmv_tok_tile_fits(wtype, a.rows, a.k, a.n_tok)) {
+    return wtype == ZQ_Q4_0 ? launch_tt<ZQ_Q4_0>(a, stream) : launch_tt<ZQ_Q8_0>(a, stream);
   }
   if (wtype == ZQ_Q4_0) return launch_tw<ZQ_Q4_0>(a, stream);
   return launch_tw<ZQ_Q8_0>(a, stream);

@@ -153,6 +153,29 @@ def test_tokens_tall_matrix_cores(zq, wt, n_tok, rows, k):
         check_rows(y[t][idx], y_ref, S, "tall %d x %d, %d tokens, token %d" % (rows, k, n_tok, t))
 
 
+# Shorter matrices with 5..8 tokens, 64..128 blocks per row and at least
+# 8 M weights take the tile form: rows ragged against the 16-row tiles, a
+# last chunk that ends part-way (65 blocks) and splits a block pair.
+@pytest.mark.parametrize("wt", [Q4_0, Q8_0])
+@pytest.mark.parametrize("n_tok", [5, 8])
+@pytest.mark.parametrize("rows,k", [(4100, 2048), (4033, 2080), (4096, 4096)])
+def test_tokens_tile_form(zq, wt, n_tok, rows, k):
+    seed = 7500 + 31 * n_tok + k + wt
+    w = inputs.gen_weights(wt, rows, k, seed)
+    x = inputs.gen_activation(n_tok, k, seed + 1).reshape(n_tok, k)
+    qx, dx, sx = quantize_gpu(zq, x)
+    y = host(run_tok(zq, wt, w, rows, k, qx, dx, sx, n_tok))
+    for t, (y_ref, S) in enumerate(oracle_rows(wt, w, rows, k, x)):
+        check_rows(y[t], y_ref, S, "tile %d x %d, %d tokens, token %d" % (rows, k, n_tok, t))
+    prev = np.random.default_rng(seed).standard_normal((n_tok, rows)).astype(np.float32)
+    y2 = dev(prev)
+    run_tok(zq, wt, w, rows, k, qx, dx, sx, n_tok, y=y2, flags=1)
+    yh = host(y2)
+    idx = np.arange(0, rows, 7)
+    for t, (y_ref, S) in enumerate(oracle_rows(wt, w, rows, k, x, rows_eval=idx, y_prev=prev)):
+        check_rows(yh[t][idx], y_ref, S, "tile accumulate, token %d" % t)
+
+
 def test_tokens_tall_accumulate(zq):
     rows, k, n_tok = 65536 + 5, 2048, 4
     w = inputs.gen_weights(Q4_0, rows, k, 7100)
