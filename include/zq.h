@@ -126,8 +126,10 @@ int zq_dmmv_q6_k(const void *w, int64_t rows, int64_t k, const int8_t *qx, const
  * y [n_tok][rows] fp32.  Tall matrices (rows >= 65536, e.g. the LM head)
  * with 3 or more tokens take the int8 matrix cores (one 16x16x32 MFMA per
  * 16 rows and block, all tokens at once) when their staged tokens fit the
- * workgroup's 64 KB of LDS (k = 2048: up to 8 tokens); the sums and the
- * fp32 rescale are the same, only the association differs. */
+ * workgroup's 64 KB of LDS (k = 2048: up to 8 tokens); so do shorter
+ * matrices with 5 or more tokens, 64 to 128 blocks per row and at least 8 M
+ * weights (their rows staged whole, 16 at a time).  The sums and the fp32
+ * rescale are the same, only the association differs. */
 int zq_dmmv_tokens(int wtype, const void *w, int64_t rows, int64_t k, const int8_t *qx,
                    const float *dx, const int32_t *sx, int32_t n_tok, float *y, uint32_t flags,
                    void *stream);
