@@ -1,10 +1,14 @@
 // dmmv_tok.hip -- multi-token DMMV over Q4_0 / Q8_0 blocks (gfx950, wave64):
 // y[t][r] = sum_b d_w[r][b] * dx[t][b] * isum_t[r][b] for 2..8 tokens decoded
-// together, in one pass over the weights.
+// together, in one pass over the weights.  Three forms: the vector form
+// below (packed dot4 per token), and two on the int8 matrix cores further
+// down -- the tall form for 65 536 rows and more, the tile form for shorter
+// matrices with 5..8 tokens.  launch_dmmv_tok picks one.
 //
-// Mapping: as the single-token DMMV (dmmv.hip): a row slot of LPR lanes walks
-// one row, lane j owns blocks j, j+LPR, ... (BPL of them per pass), and each
-// wave issues the windows of RB row steps before any arithmetic.  The lane
+// Vector form.  Mapping: as the single-token DMMV (dmmv.hip): a row slot of
+// LPR lanes walks one row, lane j owns blocks j, j+LPR, ... (BPL of them per
+// pass), and each wave issues the windows of RB row steps before any
+// arithmetic.  The lane
 // holds the codes, scales and sums of its blocks for all T tokens (T*BPL <= 8
 // blocks of activation), so each weight block is unpacked once and dotted
 // with T activation blocks.  The RB*T row partials per lane are folded by
