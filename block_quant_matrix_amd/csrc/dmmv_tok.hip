@@ -8,12 +8,11 @@
 // Vector form.  Mapping: as the single-token DMMV (dmmv.hip): a row slot of
 // LPR lanes walks one row, lane j owns blocks j, j+LPR, ... (BPL of them per
 // pass), and each wave issues the windows of RB row steps before any
-// arithmetic.  The lane
-// holds the codes, scales and sums of its blocks for all T tokens (T*BPL <= 8
-// blocks of activation), so each weight block is unpacked once and dotted
-// with T activation blocks.  The RB*T row partials per lane are folded by
-// one RowReduce.  Tokens past n_tok load the last token and get zero scales;
-// their rows are not written.
+// arithmetic.  The lane holds the codes, scales and sums of its blocks for
+// all T tokens (T*BPL <= 8 blocks of activation), so each weight block is
+// unpacked once and dotted with T activation blocks.  The RB*T row partials
+// per lane are folded by one RowReduce.  Tokens past n_tok load the last
+// token and get zero scales; their rows are not written.
 #include "zq_common.h"
 #include "zq_internal.h"
 
