@@ -502,7 +502,7 @@ __global__ __launch_bounds__(64 * kTtWaves) void dmmv_tok_tile_kernel(const Dmmv
   }
   __syncthreads();
 
-  // 3. wave wv: chunk wv of all 16 rows
+  // 2. wave wv: chunk wv of all 16 rows
   const int qoff = WT == ZQ_Q4_0 ? 8 * (g & 1) : 8 * g;
   const int shl = WT == ZQ_Q4_0 ? (1 - (g >> 1)) * 4 : 0;
   const uint8_t *wl = tq + n * T.crow + qoff;
@@ -542,7 +542,7 @@ __global__ __launch_bounds__(64 * kTtWaves) void dmmv_tok_tile_kernel(const Dmmv
       acc[3] = __builtin_fmaf(dx4.w * dw, static_cast<float>(s4[3]), acc[3]);
     }
   }
-  // 4. this wave's partials: lanes 0..31 add the odd blocks' sums of lanes
+  // 3. this wave's partials: lanes 0..31 add the odd blocks' sums of lanes
   // 32..63 and leave (token 4g + r, row n) in LDS; then the sum over the
   // waves that had a chunk
 #pragma unroll
