@@ -16,9 +16,10 @@
  *     NVIDIA", section "The reassuring result: ZINC's matmuls are __dp4a, not
  *     tensor cores" (dotPacked4x8AccSatEXT / v_dot4_i32_i8 / __dp4a, and the
  *     1*5+2*6+3*7+4*8 = 70 check).
- *   - GGML block layouts, bit-for-bit: the same section ("Q8_0 ... 32-element",
- *     "identical bit-for-bit"), and "CUDA backend for ZINC", section 4
- *     "Kernel port strategy".  Q8_0 = {fp16 d; int8 q[32]} (34 bytes), value
+ *   - GGML block layouts, unchanged in every backend: the same section (it
+ *     names Q8_0 and its 32-element blocks and says the layouts match GGML's
+ *     exactly), and "CUDA backend for ZINC", section 4 "Kernel port
+ *     strategy".  Q8_0 = {fp16 d; int8 q[32]} (34 bytes), value
  *     q*d.  Q4_0 = {fp16 d; uint8 qs[16]} (18 bytes), value (nib-8)*d, element
  *     j<16 in the low nibble of qs[j], element j+16 in the high nibble.
  *   - DMMV = read quantized weights, dequantize in registers, multiply by the
@@ -28,13 +29,13 @@
  *     DMMV -> weighted accumulate, plus a sigmoid-gated shared expert:
  *     "Bringing ZINC to NVIDIA", section "The roadmap: from 70 to a coherent
  *     token", and "CUDA backend for ZINC", section 5 (milestone M1).
- *   - argmax "exact": "CUDA backend for ZINC", section 5 (M1 kernel library).
+ *   - an exact argmax: "CUDA backend for ZINC", section 5 (the M1 kernel library).
  *   - the K-quant super-blocks Q4_K / Q5_K / Q6_K (256 elements), also GGML's
- *     layouts bit for bit: "Bringing ZINC to NVIDIA", section "The reassuring
- *     result" ("Q4_K/Q5_K/Q6_K 256-element super-blocks"), and "CUDA backend
- *     for ZINC", section 5 ("canonical GGML Q4_K dequant + matvec,
- *     cross-checked vs llama.cpp get_scale_min_k4").  Layouts, as published
- *     with GGML:
+ *     layouts unchanged: "Bringing ZINC to NVIDIA", section "The reassuring
+ *     result" (the three K-quant formats and their super-blocks of 256), and
+ *     "CUDA backend for ZINC", section 5 (the Q4_K matvec there follows
+ *     GGML's dequantization, scale/min unpacking included).  Layouts, as
+ *     published with GGML:
  *       Q4_K (144 B): fp16 d, fp16 dmin, 12 bytes of 6-bit sub-block scales
  *         and mins, 128 bytes of nibbles.  Eight sub-blocks of 32; element e
  *         of 64-group g (e < 32: low nibble, else high nibble of byte

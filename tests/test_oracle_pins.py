@@ -14,6 +14,7 @@ import pytest
 from block_quant_matrix_amd import inputs
 
 Q4, Q8 = 4, 8
+Q4_K, Q5_K, Q6_K = 12, 13, 14
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
@@ -405,6 +406,103 @@ def test_p11_moe_identical_and_one_hot_experts(ref):
     assert (np.abs(ya - yb) <= 1e-12 * Sa).all()
 
 
+def _bf_expert(ref, wt, w, rows, k, qx, dx):
+    """Rows of one matrix by the element-wise brute force (fp64 dequantize
+    then dot), for block formats and K-quants alike."""
+    if wt in (Q4, Q8):
+        return ref.dmmv_bruteforce(wt, w, rows, k, qx, dx)
+    return ref.k_bruteforce(wt, w, rows, k, qx, dx)
+
+
+def _mixed_case(seed, gu_wt, down_wt, sh_wt, n_routed=6, d_model=256, d_ff=256):
+    """Routed banks of one format pair and a shared expert of its own format
+    whose matrices differ from every routed one."""
+    if gu_wt in (Q4, Q8):
+        gu, gs, _, _ = inputs.moe_banks(seed, n_routed, d_model, d_ff, gu_wt)
+    else:
+        gu, gs, _, _ = inputs.moe_banks_k(seed, n_routed, d_model, d_ff, gu_wt, Q4_K)
+    if down_wt in (Q4, Q8):
+        _, _, dn, ds = inputs.moe_banks(seed + 1, n_routed, d_model, d_ff, down_wt)
+    else:
+        _, _, dn, ds = inputs.moe_banks_k(seed + 1, n_routed, d_model, d_ff, Q4_K, down_wt)
+    if sh_wt in (Q4, Q8):
+        sgu, _, sdn, _ = inputs.moe_banks(seed + 2, 1, d_model, d_ff, sh_wt)
+    else:
+        sgu, _, sdn, _ = inputs.moe_banks_k(seed + 2, 1, d_model, d_ff, sh_wt, sh_wt)
+    return gu, gs, dn, ds, sgu, sdn
+
+
+def test_p11_mixed_reduces_to_single_format_bank(ref):
+    """moe_ffn_mixed with every matrix Q4_0 and the shared expert's matrices
+    equal to slot n_routed of the routed banks is moe_ffn over that bank of
+    n_routed + 1 experts (itself pinned above)."""
+    d_model, d_ff, n_routed = 256, 64, 7
+    bank_gu, gs, bank_d, ds = inputs.moe_banks(1300, n_routed + 1, d_model, d_ff)
+    sh_gu = bank_gu[n_routed * gs:(n_routed + 1) * gs].copy()
+    sh_dn = bank_d[n_routed * ds:(n_routed + 1) * ds].copy()
+    x = inputs.gen_activation(1, d_model, 1301)
+    logits, g = inputs.gen_router(n_routed, 1302)
+    ids, wts = ref.moe_route(logits, 3, g)
+    assert ids[-1] == n_routed
+    y0, S0 = ref.moe_ffn(Q4, bank_gu, gs, bank_d, ds, d_model, d_ff, ids, wts, x)
+    y1, S1 = ref.moe_ffn_mixed(Q4, bank_gu[:n_routed * gs], gs, Q4, bank_d[:n_routed * ds], ds, Q4,
+                               sh_gu, sh_dn, n_routed, d_model, d_ff, ids, wts, x)
+    assert np.all(np.abs(y1 - y0) <= 1e-12 * S0) and np.allclose(S1, S0, rtol=1e-12, atol=0)
+
+
+@pytest.mark.parametrize("fmts", [(Q4_K, Q5_K, Q8), (Q4, Q8, Q6_K), (Q5_K, Q6_K, Q4)])
+def test_p11_mixed_one_hot_slots_against_bruteforce(ref, fmts):
+    """One-hot weights on a slot give that expert alone, computed here by the
+    element-wise brute force from its own matrices: the shared slot (id
+    n_routed) must use the shared expert's matrices in the shared format, a
+    routed slot its bank's matrices in the routed formats."""
+    gu_wt, down_wt, sh_wt = fmts
+    d_model, d_ff, n_routed = 256, 256, 6
+    gu, gs, dn, ds, sgu, sdn = _mixed_case(1400 + gu_wt, gu_wt, down_wt, sh_wt, n_routed,
+                                           d_model, d_ff)
+    x = inputs.gen_activation(1, d_model, 1401)
+    ids = np.array([4, 1, n_routed], np.int32)
+    qx, dx, _ = ref.quantize_act(x)
+    for slot in range(3):
+        w1 = np.eye(3)[slot] * 0.625
+        y, S = ref.moe_ffn_mixed(gu_wt, gu, gs, down_wt, dn, ds, sh_wt, sgu, sdn, n_routed,
+                                 d_model, d_ff, ids, w1, x)
+        e = int(ids[slot])
+        if e == n_routed:
+            mg, md, tg, td = sgu, sdn, sh_wt, sh_wt
+        else:
+            mg, md, tg, td = gu[e * gs:(e + 1) * gs], dn[e * ds:(e + 1) * ds], gu_wt, down_wt
+        gu_rows = _bf_expert(ref, tg, mg, 2 * d_ff, d_model, qx, dx)
+        h = ref.swiglu(gu_rows.astype(np.float32).reshape(1, -1), d_ff)[0]
+        qh, dh, _ = ref.quantize_act(h)
+        expect = 0.625 * _bf_expert(ref, td, md, d_model, d_ff, qh, dh)
+        assert np.all(np.abs(y - expect) <= 1e-12 * S), (fmts, slot)
+        assert np.any(y != 0)
+
+
+def test_p11_mixed_decomposes_into_weighted_slots(ref):
+    """The block's output is the weighted sum of its slots' one-hot outputs,
+    and permuting the (id, weight) pairs changes nothing."""
+    gu_wt, down_wt, sh_wt = Q4_K, Q5_K, Q8
+    d_model, d_ff, n_routed = 256, 256, 8
+    gu, gs, dn, ds, sgu, sdn = _mixed_case(1500, gu_wt, down_wt, sh_wt, n_routed, d_model, d_ff)
+    x = inputs.gen_activation(1, d_model, 1501)
+    logits, g = inputs.gen_router(n_routed, 1502)
+    ids, wts = ref.moe_route(logits, 4, g)
+    args = (gu_wt, gu, gs, down_wt, dn, ds, sh_wt, sgu, sdn, n_routed, d_model, d_ff)
+    y, S = ref.moe_ffn_mixed(*args, ids, wts, x)
+    parts = sum(float(wts[s]) * ref.moe_ffn_mixed(*args, ids, np.eye(len(ids))[s], x)[0]
+                for s in range(len(ids)))
+    assert np.all(np.abs(y - parts) <= 1e-12 * S)
+    p = np.array([3, 0, 4, 2, 1])
+    yp, _ = ref.moe_ffn_mixed(*args, ids[p], wts[p], x)
+    assert np.all(np.abs(y - yp) <= 1e-12 * S)
+    # the shared slot's weight is the sigmoid of the gate, the routed ones
+    # sum to one
+    assert abs(wts[-1] - 1.0 / (1.0 + math.exp(-float(g)))) < 1e-7
+    assert abs(float(np.sum(wts[:-1])) - 1.0) < 1e-6
+
+
 # -------------------------------------------------------- P12: argmax -----
 
 def test_p12_argmax_cases(ref):
@@ -451,6 +549,33 @@ def test_p14_quantization_error_bound(ref, wtype):
     assert (np.abs(y - yt) <= bound * (1 + 1e-6)).all()
     # and the bound is not vacuous: the typical error is well inside it
     assert np.median(np.abs(y - yt) / bound) < 0.2
+    # the unquantized reference really uses the fp32 activation: the error is
+    # there on (almost) every row
+    assert np.median(np.abs(y - yt) / bound) > 1e-3
+    assert np.count_nonzero(y != yt) >= rows - 1
+
+
+def test_p14_unquantized_reference_closed_forms(ref):
+    """dmmv_true on cases with a known answer: (a) an activation that the
+    quantizer represents exactly gives the quantized reference's rows; (b) a
+    one-element weight against an activation element that quantizes to zero
+    gives that element itself, where the quantized reference gives 0."""
+    rng = np.random.default_rng(143)
+    rows, k = 8, 256
+    w = inputs.gen_weights(Q8, rows, k, 144)
+    x, _ = lossless_activation(rng, k)
+    qx, dx, _ = ref.quantize_act(x)
+    y, S = ref.dmmv(Q8, w, rows, k, qx, dx)
+    assert np.all(np.abs(ref.dmmv_true(Q8, w, rows, k, x) - y) <= 1e-12 * S)
+    q = np.zeros(32, np.int8)
+    q[0] = 1
+    w1 = q8_block(1.0, q)
+    xb = np.zeros(32, np.float32)
+    xb[1] = 127.0
+    xb[0] = np.float32(0.3)
+    qx1, dx1, _ = ref.quantize_act(xb)
+    assert qx1[0] == 0 and ref.dmmv(Q8, w1, 1, 32, qx1, dx1)[0][0] == 0.0
+    assert ref.dmmv_true(Q8, w1, 1, 32, xb)[0] == float(np.float32(0.3))
 
 
 # ----------------------------------------------- generators' recipe -------
@@ -487,7 +612,6 @@ def test_p3f_halfway_after_rounding(ref):
 # layouts (element index -> byte, nibble, bit), independent of the oracle's
 # decoder, which walks the other way.
 
-Q4_K, Q5_K, Q6_K = 12, 13, 14
 KBB = {Q4_K: 144, Q5_K: 176, Q6_K: 210}
 
 
