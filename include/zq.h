@@ -184,7 +184,7 @@ int zq_rms_norm_dmmv_f32_argmax(int wtype, const void *w, int64_t rows, int64_t 
 int zq_dmmv_isums(int wtype, const void *w, int64_t rows, int64_t k, const int8_t *qx,
                   const int32_t *sx, int32_t *isums, void *stream);
 
-/* Index of the largest logit, ties to the lowest index ("argmax (exact)",
+/* Index of the largest logit, ties to the lowest index (the exact argmax of the kernel library,
  * "CUDA backend for ZINC", section 5, M1 kernel library).  y [n] fp32 finite;
  * out_idx: one int32.  workspace: device scratch of at least
  * zq_argmax_workspace_bytes(n) bytes, 8-byte aligned. */
@@ -194,7 +194,7 @@ int zq_argmax_f32(const float *y, int64_t n, int32_t *out_idx, void *workspace,
 
 /* The LM-head step in two launches: y = W . Q(x) over all rows, exactly as
  * zq_dmmv_f32 computes it (same codes, same rows, bit for bit), and out_idx
- * = the argmax of y with ties to the lowest row ("argmax (exact)", "CUDA
+ * = the argmax of y with ties to the lowest row (the exact argmax of the kernel library, "CUDA
  * backend for ZINC", section 5; the vocab-output DMMV, "Как мы запустили
  * 35B LLM на видеокарте за $500", section "Утилизация полосы памяти по
  * операциям").  The DMMV launch is persistent: each workgroup quantizes the
@@ -216,8 +216,8 @@ int zq_dmmv_f32_argmax(int wtype, const void *w, int64_t rows, int64_t k, const 
  * top_k largest of n_routed logits, largest first, ties to the lower id;
  * wts = softmax over the selected logits.  If shared_gate (one device fp32)
  * is non-NULL, a shared expert with id n_routed and weight sigmoid(g) is
- * appended ("one sigmoid-gated shared expert", same page, section "The target
- * model").  ids/wts: top_k (+1) entries.  1 <= top_k <= 64,
+ * appended (the pages' model adds one shared expert whose output is scaled
+ * by a sigmoid gate: same page, section "The target model").  ids/wts: top_k (+1) entries.  1 <= top_k <= 64,
  * top_k <= n_routed <= 1024. */
 int zq_moe_route(const float *logits, int32_t n_routed, int32_t top_k,
                  const float *shared_gate, int32_t *ids, float *wts, void *stream);
@@ -307,7 +307,11 @@ int zq_moe_gate_up_mixed(int gu_wtype, const void *gu_bank, int64_t gu_stride_by
 
 /* One token through the selected experts in two launches: zq_moe_gate_up
  * (quantize x, gate||up rows, swiglu, re-quantize), then the down DMMV with
- * the weighted sum over the selected experts fused in.  gu_bank: experts of [2*d_ff][d_model]
+ * the weighted sum over the selected experts fused in.  (The expert chain of
+ * "Bringing ZINC to NVIDIA", section "The roadmap: from 70 to a coherent
+ * token": expert gate/up, swiglu, expert down, weighted accumulate; fused
+ * as the gate/up and down-accumulate kernels of "CUDA backend for ZINC",
+ * section 5, milestone M3.)  gu_bank: experts of [2*d_ff][d_model]
  * (rows 0..d_ff-1 gate, d_ff..2*d_ff-1 up); down_bank: [d_model][d_ff].
  * workspace: at least zq_moe_ffn_workspace_bytes(d_model, d_ff, n_sel) bytes,
  * 256-byte aligned.  y [d_model] (+)= sum_s wts[s] * down_s.
@@ -372,8 +376,8 @@ int zq_moe_ffn_mixed(int gu_wtype, const void *gu_bank, int64_t gu_stride_bytes,
                      void *workspace, size_t workspace_bytes, float *y, uint32_t flags,
                      void *stream);
 
-/* Batched prefill GEMM ("one register-tiled GEMM over all prompt tokens at
- * once", "RTX 5090: Batched Prefill & CUDA Graphs in ZINC", opening answer
+/* Batched prefill GEMM (all prompt tokens through one tiled GEMM rather than
+ * one matvec per token: "RTX 5090: Batched Prefill & CUDA Graphs in ZINC", opening answer
  * and section "Prefill -- a correction, and a better GEMM"; the dequant is
  * fused into the GEMM as the same page's closing paragraph recommends):
  *   Y[m][n] (+)= sum_b dx[m][b] * d_w[n][b] * isum(m, n, b),
