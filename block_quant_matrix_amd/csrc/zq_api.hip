@@ -347,6 +347,60 @@ int zq_dmmv_f32_argmax(int wtype, const void *w, int64_t rows, int64_t k, const 
   return zq::launch_dmmv_f32x(wtype, a, S(stream));
 }
 
+namespace {
+
+// The allocation-free LM-head step keeps its argmax partials (one (logit,
+// row) pair per workgroup of the persistent DMMV launch) in this array.  Each
+// GPU the library runs on holds its own copy until the process ends.  In host
+// code `scratch` names a host-side stand-in, never the device memory: the
+// launches take the address hipGetSymbolAddress returns on each device.
+constexpr size_t kScratchBytes = sizeof(zq::ValIdx) * static_cast<size_t>(zq::kArgmaxMaxParts);
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::atomic<void *> g_scratch[kMaxDevices];
+
+// The device address of `scratch` on the current device, looked up once per
+// device with that device current (two threads racing here store the same
+// address).  nullptr if the runtime cannot resolve it.
+void *scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void *p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();  // leave no error behind for the next launch check
+      return nullptr;
+    }
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+}  // namespace
+
+int zq_dmmv_f32_argmax_noalloc(int wtype, const void *w, int64_t rows, int64_t k, const float *x,
+                               float *y, int32_t *out_idx, void *stream) {
+  static_assert(sizeof(zq::ValIdx) * zq::kArgmaxMaxParts <= kScratchBytes,
+                "every partial of the persistent launch fits the scratch array");
+  ZQ_REQUIRE(block_bytes(wtype) > 0, ZQ_EINVAL);
+  ZQ_REQUIRE(w && x && y && out_idx, ZQ_ENULL);
+  ZQ_REQUIRE(rows >= 1 && rows <= INT32_MAX && k_ok(k) && k <= 16384, ZQ_EINVAL);
+  ZQ_REQUIRE(al(w, 4) && al(x, 16) && al(y, 4) && al(out_idx, 4), ZQ_EALIGN);
+  const int dc = check_current_device();
+  if (dc != ZQ_OK) return dc;
+  void *part = scratch_on_current_device();
+  if (part == nullptr) return ZQ_ELAUNCH;
+  zq::DmmvF32Args a{};
+  a.w = static_cast<const uint8_t *>(w);
+  a.x = x;
+  a.y = y;
+  a.part = part;  // every slot the final pass reads is written by this call's DMMV launch
+  a.out_idx = out_idx;
+  a.rows = rows;
+  a.k = static_cast<int32_t>(k);
+  a.nb = static_cast<int32_t>(k / 32);
+  return zq::launch_dmmv_f32x(wtype, a, S(stream));
+}
+
 inline bool eps_ok(float eps) { return eps >= 0.0f && eps <= 3.0e38f; }  // finite, not NaN
 
 int zq_rms_norm_quantize(const float *x, const float *norm_w, float eps, int64_t n_tok, int64_t k,

@@ -48,6 +48,7 @@ SIGNATURES = {
     "zq_argmax_f32": (_INT, [_P, _I64, _P, _P, _SZ, _P]),
     "zq_dmmv_f32_argmax_workspace_bytes": (_SZ, []),
     "zq_dmmv_f32_argmax": (_INT, [_INT, _P, _I64, _I64, _P, _P, _P, _P, _SZ, _P]),
+    "zq_dmmv_f32_argmax_noalloc": (_INT, [_INT, _P, _I64, _I64, _P, _P, _P, _P]),
     "zq_moe_route": (_INT, [_P, _I32, _I32, _P, _P, _P, _P]),
     "zq_dmmv_moe": (_INT, [_INT, _P, _I64, _I64, _I64, _I64, _P, _P, _I32, _P, _P, _P, _I64,
                            _INT, _P, _U32, _P, _P]),
@@ -213,6 +214,11 @@ def zq_dmmv_f32_argmax(wtype, w, rows, k, x, y, out_idx, workspace, workspace_by
                  ptr(workspace), workspace_bytes, _stream(stream))
 
 
+def zq_dmmv_f32_argmax_noalloc(wtype, w, rows, k, x, y, out_idx, stream=None):
+    return _call("zq_dmmv_f32_argmax_noalloc", wtype, ptr(w), rows, k, ptr(x), ptr(y), ptr(out_idx),
+                 _stream(stream))
+
+
 def zq_moe_route(logits, n_routed, top_k, shared_gate, ids, wts, stream=None):
     return _call("zq_moe_route", ptr(logits), n_routed, top_k, ptr(shared_gate), ptr(ids), ptr(wts),
                  _stream(stream))
@@ -291,3 +297,4 @@ def zq_moe_ffn_mixed(gu_wtype, gu_bank, gu_stride, down_wtype, down_bank, down_s
                  down_stride, sh_wtype, ptr(sh_gu), ptr(sh_down), d_model, d_ff, ptr(logits),
                  n_routed, top_k, ptr(shared_gate), ptr(x), ptr(ids), ptr(wts), ptr(workspace),
                  workspace_bytes, ptr(y), flags, _stream(stream))
+

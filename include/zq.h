@@ -211,6 +211,22 @@ size_t zq_dmmv_f32_argmax_workspace_bytes(void);
 int zq_dmmv_f32_argmax(int wtype, const void *w, int64_t rows, int64_t k, const float *x, float *y,
                        int32_t *out_idx, void *workspace, size_t workspace_bytes, void *stream);
 
+/* zq_dmmv_f32_argmax for callers that cannot allocate device memory (code
+ * under HIP graph capture, serving loops and harnesses that forbid
+ * hipMalloc): the same two launches, the same rows and index bit for bit,
+ * with no workspace argument.  The argmax partials live in a device array
+ * of 16 KiB (2048 pairs) that the library holds on each GPU it runs on,
+ * until the process ends; the call allocates and frees nothing.  Every call
+ * on one GPU shares that GPU's array, so calls that overlap on one GPU (on
+ * different streams, or from several threads) race: order them on one
+ * stream.  Nothing in the array needs to start cleared: each call writes
+ * every partial it reads.  Same arguments and limits as zq_dmmv_f32_argmax
+ * (1 <= rows <= INT32_MAX, 32 <= k <= 16384, out_idx required); larger
+ * sizes return ZQ_EINVAL, and ZQ_ELAUNCH if the runtime cannot resolve the
+ * array on the current device. */
+int zq_dmmv_f32_argmax_noalloc(int wtype, const void *w, int64_t rows, int64_t k, const float *x,
+                               float *y, int32_t *out_idx, void *stream);
+
 /* MoE router ("softmax_topk", "Bringing ZINC to NVIDIA", section "The roadmap:
  * from 70 to a coherent token"; "CUDA backend for ZINC", section 5): the
  * top_k largest of n_routed logits, largest first, ties to the lower id;

@@ -261,6 +261,25 @@ def test_lmhead_argument_errors():
     assert rc(y=C + 2) == zq.ZQ_EALIGN
 
 
+def test_lmhead_noalloc_argument_errors():
+    L = zq.lib()
+
+    def rc(wtype=4, w=A, rows=248320, k=2048, x=B, y=C, out=D):
+        return L.zq_dmmv_f32_argmax_noalloc(wtype, w, rows, k, x, y, out, None)
+
+    assert rc(wtype=5) == zq.ZQ_EINVAL
+    assert rc(rows=0) == zq.ZQ_EINVAL
+    assert rc(rows=1 << 31) == zq.ZQ_EINVAL
+    assert rc(k=2047) == zq.ZQ_EINVAL
+    assert rc(k=16384 + 32) == zq.ZQ_EINVAL
+    assert rc(x=None) == zq.ZQ_ENULL
+    assert rc(y=None) == zq.ZQ_ENULL
+    assert rc(out=None) == zq.ZQ_ENULL
+    assert rc(x=B + 4) == zq.ZQ_EALIGN
+    assert rc(y=C + 2) == zq.ZQ_EALIGN
+    assert rc(out=D + 1) == zq.ZQ_EALIGN
+
+
 def rc_dmmv_q4(**kw):
     a = dict(w=A, rows=4, k=64, qx=B, dx=C, sx=None, y=D, flags=0)
     a.update(kw)
@@ -384,6 +403,7 @@ def test_valid_arguments_without_gpu_report_no_device():
                                 L.zq_dmmv_f32_argmax_workspace_bytes(), None) == zq.ZQ_EDEVICE
     assert L.zq_dmmv_f32_argmax(4, A, 7, 64, B, C, None, A + 0x8000,
                                 L.zq_dmmv_f32_argmax_workspace_bytes(), None) == zq.ZQ_EDEVICE
+    assert L.zq_dmmv_f32_argmax_noalloc(4, A, 248320, 2048, B, C, D, None) == zq.ZQ_EDEVICE
     ws = L.zq_moe_ffn_workspace_bytes(2048, 512, 8)
     assert L.zq_moe_ffn_route(4, A, 2 * 512 * 64 * 18, B, 2048 * 16 * 18, 128, 2048, 512, B, 128,
                               8, None, D, A + 0x1000, A + 0x2000, A + 0x4000, ws, A + 0x8000, 0,
