@@ -1,25 +1,33 @@
 #!/usr/bin/env python3
 """Throughput of the block-quantized decode path on one MI355X.
 
-Default (workload 2): one step = quantize one fp32 activation of 4096 to int8
-blocks, then the Q4_0 DMMV of a 4096 x 4096 weight matrix.  Weights rotate
-over distinct copies whose total is more than twice the 256 MB MALL, so every
-step streams its weights from HBM.  Prints ONE JSON line.
+Default (workload 2): one step = the fused quantize + Q4_0 DMMV of a 4096 x
+4096 weight matrix from an fp32 activation (one launch).  Weights rotate over
+distinct copies whose total is more than twice the 256 MB MALL, so every step
+streams its weights from HBM.  Prints ONE JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1..13]
 
 Timing: a GPU-side spin kernel is queued ahead of the timed region so that the
 K steps are enqueued before the GPU reaches them and run back to back (host
 launch cost is not what is measured); HIP events on the launch stream bracket
-exactly the K steps.  A second pass times K back-to-back launches of the
-dominant kernel alone the same way (roofline.achieved).  The CPU oracle is timed on
-a bounded sample of the same workload (cpu_baseline).
+exactly the K steps.  When a step is one launch of the dominant kernel the
+roofline comes from that same timed region; otherwise a second pass times K
+back-to-back launches of the dominant kernel alone the same way.
+
+The oracle leg (cpu_baseline) runs before the timed region: it checks the
+GPU's outputs of the first step against the CPU oracle on the same inputs
+(parity_checked) and times the oracle on a bounded sample of the workload,
+on one host thread and on all of the host's cores (median of 3 runs each).
 """
 from __future__ import annotations
 
 import argparse
+import concurrent.futures as cf
 import json
 import os
+import statistics
+import subprocess
 import sys
 import time
 
@@ -31,6 +39,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA, TOP/s
 MALL_BYTES = 256 << 20
+ROW_TOL = 1e-4               # fp32 rows against the fp64 oracle (normwise and well-conditioned)
+MOE_E2E_TOL = 1e-3           # an unchained MoE block (an exp ulp may flip one re-quantized code)
+CHAIN_E2E_TOL = 1e-2         # the 40-layer chain unchained, normwise
 
 METRIC = "DMMV achieved HBM GB/s (% of MI355X peak) + rows/s, Q4_0 4096x4096"
 
@@ -40,12 +51,52 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13])
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--workload", type=int, default=2, choices=list(range(1, 14)))
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle leg (no parity check, no CPU timing)")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the LM-head measurement the default line carries")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="about how long the oracle leg's timing runs take in all")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 256 MiB device copy (counter calibration)")
     return ap.parse_args()
+
+
+# ------------------------------------------------------------ parity bars --
+
+def rows_within(y, y_ref, S, tol=ROW_TOL):
+    """The fp32 row bar: every output written; normwise |y - y_ref| <= tol*S;
+    elementwise |y - y_ref| <= tol*|y_ref| where |y_ref| >= 0.1*S.  Returns
+    (ok, worst error in units of S)."""
+    y = np.asarray(y, np.float64).ravel()
+    y_ref = np.asarray(y_ref, np.float64).ravel()
+    S = np.asarray(S, np.float64).ravel()
+    if np.isnan(y).any():
+        return False, float("nan")
+    err = np.abs(y - y_ref)
+    worst = float((err / np.maximum(S, 1e-300)).max()) if y.size else 0.0
+    ok = bool((err <= tol * S).all())
+    well = np.abs(y_ref) >= 0.1 * S
+    ok = ok and bool((err[well] <= tol * np.abs(y_ref[well])).all())
+    return ok, worst
+
+
+def first_max(y):
+    """Lowest index of the largest value."""
+    return int(np.argmax(np.asarray(y)))
+
+
+def argmax_ok(idx, y_gpu, y_ref, S, tol):
+    """The GPU's index is the argmax of its own logits (ties to the lowest
+    row), and the oracle's unless the oracle's top two are within tol of
+    each other's error scales."""
+    if idx != first_max(y_gpu):
+        return False
+    top = np.argsort(-np.asarray(y_ref), kind="stable")[:2]
+    if y_ref[top[0]] - y_ref[top[1]] >= tol * (S[top[0]] + S[top[1]]):
+        return idx == int(top[0])
+    return True
 
 
 # ------------------------------------------------------------- workloads --
@@ -56,6 +107,7 @@ class Workload:
     bound = "hbm"
     steps = 2000
     warmup = 50
+    step_is_dominant = False  # a step is exactly one launch of the dominant kernel
 
     def setup(self, torch, zq, inputs):
         raise NotImplementedError
@@ -65,11 +117,10 @@ class Workload:
 
     def prepare_dominant(self):
         """Produce the inputs the dominant kernel reads (outside any timing)."""
-        raise NotImplementedError
 
     def dominant(self, i):
         """Launch only the dominant kernel, on the inputs of step i."""
-        raise NotImplementedError
+        self.step(i)
 
     def pct_of_peak(self, value, unit):
         """The step's rate as a percentage of the chip's peak for its unit."""
@@ -82,7 +133,27 @@ class Workload:
     def achieved(self, ms_per_launch):
         raise NotImplementedError
 
-    def cpu_baseline(self, seconds):
+    def extra(self, ms):
+        return {}
+
+    # the oracle leg
+    def gpu_result(self):
+        """Run step 0 on the GPU and return its outputs on the host."""
+        raise NotImplementedError
+
+    def oracle_step(self):
+        """One step of the oracle on the inputs of step 0."""
+        raise NotImplementedError
+
+    def parity(self, gpu, ref):
+        """(ok, detail): the GPU's outputs against the oracle's."""
+        raise NotImplementedError
+
+    def cpu_value(self, s_per_step):
+        """The oracle's rate in the unit of the GPU's metric."""
+        return self.step_bytes / s_per_step / 1e9, "GB/s"
+
+    def cpu_sample(self):
         raise NotImplementedError
 
 
@@ -108,6 +179,7 @@ class DmmvWorkload(Workload):
         # quantize x once, stream many row groups and leave argmax partials,
         # then the one-block final argmax
         self.fused = wl in (1, 2)
+        self.step_is_dominant = self.fused
         # weights + fp32 activation in + fp32 rows out
         self.dmmv_bytes = self.wbytes + 4 * self.k + 4 * self.rows
         if self.fused:
@@ -143,9 +215,6 @@ class DmmvWorkload(Workload):
             self.zq.zq_dmmv_f32_argmax(self.wtype, self.w[i % self.ncopy], self.rows, self.k,
                                        self.x, self.y, self.idx, self.ws, self.ws_bytes)
 
-    def prepare_dominant(self):
-        pass
-
     def dominant(self, i):
         if self.fused:
             self.step(i)
@@ -163,23 +232,42 @@ class DmmvWorkload(Workload):
     def extra(self, ms):
         return {"rows_per_s": self.rows / (ms * 1e-3)}
 
-    def cpu_baseline(self, seconds):
+    def gpu_result(self):
+        self.y.fill_(float("nan"))
+        if self.argmax:
+            self.idx.fill_(-1)
+        self.step(0)
+        self.torch.cuda.synchronize()
+        out = {"y": self.y.cpu().numpy().copy()}
+        if self.argmax:
+            out["idx"] = int(self.idx.cpu().numpy()[0])
+        return out
+
+    def oracle_step(self, rows_eval=None):
         import oracle
-        n, t0 = 0, time.perf_counter()
-        while True:
-            qx, dx, sx = oracle.quantize_act(self.x_host)
-            y, _ = oracle.dmmv(self.wtype, self.w_host0, self.rows, self.k, qx, dx)
-            if self.argmax:
-                oracle.argmax_f32(y.astype(np.float32))
-            n += 1
-            el = time.perf_counter() - t0
-            if el >= seconds:
-                break
-        per = el / n
-        return dict(value=self.step_bytes / per / 1e9, unit="GB/s", cores=1, kind="oracle",
-                    sample="%d full steps (quantize + %d-row DMMV%s) of this workload on one "
-                           "host thread, %.1f s" % (n, self.rows, " + argmax" if self.argmax else "",
-                                                    el))
+        qx, dx, _ = oracle.quantize_act(self.x_host)
+        y, S = oracle.dmmv(self.wtype, self.w_host0, self.rows, self.k, qx, dx, rows_eval=rows_eval)
+        out = {"y": y, "S": S}
+        if self.argmax and rows_eval is None:
+            out["idx"] = oracle.argmax_f32(y.astype(np.float32))
+        return out
+
+    def parity(self, gpu, ref, rows_eval=None):
+        y = gpu["y"] if rows_eval is None else gpu["y"][rows_eval]
+        ok, worst = rows_within(y, ref["y"], ref["S"])
+        detail = "%d rows within %g*S (worst %.3g*S)" % (y.size, ROW_TOL, worst)
+        if self.argmax:
+            if "idx" in ref:
+                ok = ok and argmax_ok(gpu["idx"], gpu["y"], ref["y"], ref["S"], ROW_TOL)
+                detail += "; argmax %d = oracle's" % gpu["idx"]
+            else:
+                ok = ok and gpu["idx"] == first_max(gpu["y"])
+                detail += "; argmax %d = argmax of the GPU's logits" % gpu["idx"]
+        return ok, detail
+
+    def cpu_sample(self):
+        return "quantize + %d-row DMMV%s over this workload's first weight copy" % (
+            self.rows, " + argmax" if self.argmax else "")
 
 
 class DmmvKWorkload(Workload):
@@ -255,20 +343,25 @@ class DmmvKWorkload(Workload):
     def extra(self, ms):
         return {"rows_per_s": self.rows / (ms * 1e-3)}
 
-    def cpu_baseline(self, seconds):
+    def gpu_result(self):
+        self.y.fill_(float("nan"))
+        self.step(0)
+        self.torch.cuda.synchronize()
+        return {"y": self.y.cpu().numpy().copy()}
+
+    def oracle_step(self):
         import oracle
-        n, t0 = 0, time.perf_counter()
-        while True:
-            qx, dx, sx = oracle.quantize_act(self.x_host)
-            oracle.k_dmmv(self.wtype, self.w_host0, self.rows, self.k, qx, dx)
-            n += 1
-            el = time.perf_counter() - t0
-            if el >= seconds:
-                break
-        per = el / n
-        return dict(value=self.step_bytes / per / 1e9, unit="GB/s", cores=1, kind="oracle",
-                    sample="%d full steps (quantize + %d-row %s DMMV) of this workload on one "
-                           "host thread, %.1f s" % (n, self.rows, self.tname, el))
+        qx, dx, _ = oracle.quantize_act(self.x_host)
+        y, S = oracle.k_dmmv(self.wtype, self.w_host0, self.rows, self.k, qx, dx)
+        return {"y": y, "S": S}
+
+    def parity(self, gpu, ref):
+        ok, worst = rows_within(gpu["y"], ref["y"], ref["S"])
+        return ok, "%d rows within %g*S (worst %.3g*S)" % (self.rows, ROW_TOL, worst)
+
+    def cpu_sample(self):
+        return "quantize + %d-row %s DMMV over this workload's first weight copy" % (
+            self.rows, self.tname)
 
 
 class DmmvTokWorkload(Workload):
@@ -334,21 +427,216 @@ class DmmvTokWorkload(Workload):
     def extra(self, ms):
         return {"token_rows_per_s": self.T * self.rows / (ms * 1e-3), "us_per_token": ms * 1e3 / self.T}
 
-    def cpu_baseline(self, seconds):
+    def gpu_result(self):
+        self.y.fill_(float("nan"))
+        self.step(0)
+        self.torch.cuda.synchronize()
+        return {"y": self.y.cpu().numpy().copy()}
+
+    def oracle_step(self):
         import oracle
-        n, t0 = 0, time.perf_counter()
-        while True:
-            qx, dx, _ = oracle.quantize_act(self.x_host)
-            for t in range(self.T):
-                oracle.dmmv(self.wtype, self.w_host0, self.rows, self.k, qx[t], dx[t])
-            n += 1
-            el = time.perf_counter() - t0
-            if el >= seconds:
-                break
-        per = el / n
-        return dict(value=self.step_bytes / per / 1e9, unit="GB/s", cores=1, kind="oracle",
-                    sample="%d full steps (quantize %d tokens + %d-row DMMV per token) on one "
-                           "host thread, %.1f s" % (n, self.T, self.rows, el))
+        qx, dx, _ = oracle.quantize_act(self.x_host)
+        ys, Ss = [], []
+        for t in range(self.T):
+            y, S = oracle.dmmv(self.wtype, self.w_host0, self.rows, self.k, qx[t], dx[t])
+            ys.append(y)
+            Ss.append(S)
+        return {"y": np.stack(ys), "S": np.stack(Ss)}
+
+    def parity(self, gpu, ref):
+        ok, worst = rows_within(gpu["y"], ref["y"], ref["S"])
+        return ok, "%d tokens x %d rows within %g*S (worst %.3g*S)" % (self.T, self.rows, ROW_TOL,
+                                                                      worst)
+
+    def cpu_sample(self):
+        return "quantize %d tokens + a %d-row DMMV per token over the first weight copy" % (
+            self.T, self.rows)
+
+
+class MoeWorkload(Workload):
+    """Router + one token through 8 routed + 1 shared Q4_0 experts, in two
+    launches: gate/up with the router folded in, then down."""
+    dominant_name = "moe_gate_up_kernel (router folded in)"
+    steps = 2000
+    warmup = 100
+
+    def __init__(self):
+        from block_quant_matrix_amd import inputs
+        cfg = inputs.WORKLOADS[4]
+        self.name = cfg["name"]
+        self.E, self.top_k, self.dm, self.dff = cfg["n_routed"], cfg["top_k"], cfg["d_model"], cfg["d_ff"]
+        self.n_sel = self.top_k + 1
+        bb = 18
+        self.gu_w = self.n_sel * 2 * self.dff * (self.dm // 32) * bb
+        self.down_w = self.n_sel * self.dm * (self.dff // 32) * bb
+        self.step_bytes = self.gu_w + self.down_w + 4 * self.dm + 4 * self.dm
+        # fused gate/up pass: weights + fp32 x + router logits in, quantized h
+        # out (codes, scales, sums) + the expert list and weights
+        self.gate_up_bytes = (self.gu_w + 4 * self.dm + 4 * self.E + self.n_sel * self.dff +
+                              8 * self.n_sel * (self.dff // 32) + 8 * self.n_sel)
+
+    def setup(self, torch, zq, inputs):
+        self.torch, self.zq = torch, zq
+        bank_bytes = (self.E + 1) * (2 * self.dff * (self.dm // 32) + self.dm * (self.dff // 32)) * 18
+        self.ncopy = copies_for(bank_bytes)
+        self.banks = []
+        for c in range(self.ncopy):
+            gu, gs, down, ds = inputs.moe_banks(inputs.seed_for(4, c), self.E + 1, self.dm, self.dff)
+            self.banks.append((torch.from_numpy(gu).to("cuda"), torch.from_numpy(down).to("cuda")))
+            if c == 0:
+                self.host_bank = (gu, gs, down, ds)
+        self.gs, self.ds = gs, ds
+        nlog = 64
+        lg = [inputs.gen_router(self.E, inputs.seed_for(4, 100 + i)) for i in range(nlog)]
+        self.logits = torch.from_numpy(np.stack([l for l, _ in lg])).to("cuda")
+        self.gates = torch.from_numpy(np.array([g for _, g in lg], np.float32)).to("cuda")
+        self.host_router = lg[0]
+        self.x_host = inputs.gen_activation(1, self.dm, inputs.seed_for(4) + 7)
+        self.x = torch.from_numpy(self.x_host).to("cuda")
+        self.ids = torch.empty(self.n_sel, dtype=torch.int32, device="cuda")
+        self.wts = torch.empty(self.n_sel, dtype=torch.float32, device="cuda")
+        self.ws_bytes = zq.zq_moe_ffn_workspace_bytes(self.dm, self.dff, self.n_sel)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
+        self.y = torch.empty(self.dm, dtype=torch.float32, device="cuda")
+        # outputs of the gate/up pass when it is timed alone
+        self.qh = torch.empty((self.n_sel, self.dff), dtype=torch.int8, device="cuda")
+        self.dh = torch.empty((self.n_sel, self.dff // 32), dtype=torch.float32, device="cuda")
+        self.sh = torch.empty((self.n_sel, self.dff // 32), dtype=torch.int32, device="cuda")
+
+    def step(self, i):
+        gu, down = self.banks[i % self.ncopy]
+        j = i % self.logits.shape[0]
+        self.zq.zq_moe_ffn_route(4, gu, self.gs, down, self.ds, self.E + 1, self.dm, self.dff,
+                                 self.logits[j], self.E, self.top_k, self.gates[j:j + 1], self.x,
+                                 self.ids, self.wts, self.ws, self.ws_bytes, self.y)
+
+    def dominant(self, i):
+        gu, _ = self.banks[i % self.ncopy]
+        j = i % self.logits.shape[0]
+        self.zq.zq_moe_gate_up_route(4, gu, self.gs, self.E + 1, self.dm, self.dff, self.logits[j],
+                                     self.E, self.top_k, self.gates[j:j + 1], self.x, self.ids,
+                                     self.wts, self.qh, self.dh, self.sh)
+
+    def value(self, ms):
+        return self.step_bytes / (ms * 1e-3) / 1e9, "GB/s"
+
+    def achieved(self, ms):
+        return self.gate_up_bytes / (ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s", self.gate_up_bytes
+
+    def extra(self, ms):
+        return {"tokens_per_s": 1.0 / (ms * 1e-3)}
+
+    def gpu_result(self):
+        self.y.fill_(float("nan"))
+        self.step(0)
+        self.torch.cuda.synchronize()
+        return {"y": self.y.cpu().numpy().copy(), "ids": self.ids.cpu().numpy().copy()}
+
+    def oracle_step(self):
+        import oracle
+        gu, gs, down, ds = self.host_bank
+        logits, g = self.host_router
+        ids, wts = oracle.moe_route(logits, self.top_k, g)
+        y, S = oracle.moe_ffn(4, gu, gs, down, ds, self.dm, self.dff, ids, wts, self.x_host)
+        return {"y": y, "S": S, "ids": ids}
+
+    def parity(self, gpu, ref):
+        ok, worst = rows_within(gpu["y"], ref["y"], ref["S"], MOE_E2E_TOL)
+        ok = ok and np.array_equal(gpu["ids"], ref["ids"])
+        return ok, ("expert ids equal; %d rows within the unchained MoE bar %g*S (worst %.3g*S)"
+                    % (self.dm, MOE_E2E_TOL, worst))
+
+    def cpu_sample(self):
+        return "route + one token through 8 routed + 1 shared expert (the first bank copy)"
+
+
+class GemmWorkload(Workload):
+    dominant_name = "gemm_kernel"
+    bound = "mfma"
+    steps = 100
+    warmup = 10
+    SAMPLE = 256   # output entries per oracle step
+
+    def __init__(self):
+        from block_quant_matrix_amd import inputs
+        cfg = inputs.WORKLOADS[5]
+        self.name = cfg["name"]
+        self.m, self.n, self.k = cfg["m"], cfg["n"], cfg["k"]
+        self.ops = 2 * self.m * self.n * self.k
+
+    def setup(self, torch, zq, inputs):
+        self.torch, self.zq = torch, zq
+        wbytes = self.n * (self.k // 32) * 18
+        self.ncopy = copies_for(wbytes)
+        host = [inputs.gen_weights(4, self.n, self.k, inputs.seed_for(5, c)) for c in range(self.ncopy)]
+        self.w = [torch.from_numpy(h).to("cuda") for h in host]
+        self.w_host0 = host[0]
+        del host
+        self.x_host = inputs.gen_activation(self.m, self.k, inputs.seed_for(5) + 1)
+        self.x = torch.from_numpy(self.x_host).to("cuda")
+        self.qx = torch.empty((self.m, self.k), dtype=torch.int8, device="cuda")
+        self.dx = torch.empty((self.m, self.k // 32), dtype=torch.float32, device="cuda")
+        self.y = torch.empty((self.m, self.n), dtype=torch.float32, device="cuda")
+        rng = np.random.default_rng(55)
+        self.mi = rng.integers(0, self.m, self.SAMPLE)
+        self.ni = rng.integers(0, self.n, self.SAMPLE)
+        self._oq = None
+
+    def step(self, i):
+        self.zq.zq_quantize_act(self.x, self.m, self.k, self.k, self.qx, self.dx, None)
+        self.zq.zq_gemm_prefill(4, self.w[i % self.ncopy], self.n, self.k, self.qx, self.dx, None,
+                                self.m, self.y)
+
+    def prepare_dominant(self):
+        self.zq.zq_quantize_act(self.x, self.m, self.k, self.k, self.qx, self.dx, None)
+
+    def dominant(self, i):
+        self.zq.zq_gemm_prefill(4, self.w[i % self.ncopy], self.n, self.k, self.qx, self.dx, None,
+                                self.m, self.y)
+
+    def value(self, ms):
+        return self.ops / (ms * 1e-3) / 1e12, "TOP/s"
+
+    def achieved(self, ms):
+        return self.ops / (ms * 1e-3) / 1e12, INT8_PEAK_TOPS, "TOP/s", self.ops
+
+    def extra(self, ms):
+        # The ceiling the fp32 rescale sets: every (token, row, block) triple
+        # needs a convert, a multiply and an FMA, unpacked, at 64 lanes per
+        # clock per CU (256 CUs, 2.4 GHz).
+        triples = self.m * self.n * (self.k // 32)
+        valu_s = 3 * triples / (256 * 64 * 2.4e9)
+        ceiling = 2 * self.m * self.n * self.k / valu_s / 1e12
+        steps_tops = 2 * self.m * self.n * self.k / (ms * 1e-3) / 1e12
+        return {"tokens_per_s": self.m / (ms * 1e-3),
+                "valu_epilogue_ceiling_TOPs": round(ceiling, 1),
+                "step_frac_of_epilogue_ceiling": round(steps_tops / ceiling, 4)}
+
+    def gpu_result(self):
+        self.y.fill_(float("nan"))
+        self.step(0)
+        self.torch.cuda.synchronize()
+        return {"y": self.y.cpu().numpy()[self.mi, self.ni].copy()}
+
+    def oracle_step(self):
+        import oracle
+        if self._oq is None:  # every token's codes, once (outside the timed sample)
+            self._oq = oracle.quantize_act(self.x_host)[:2]
+        qx, dx = self._oq
+        y, S = oracle.gemm_entries(4, self.w_host0, self.n, self.k, qx, dx, self.m, self.mi,
+                                   self.ni)
+        return {"y": y, "S": S}
+
+    def parity(self, gpu, ref):
+        ok, worst = rows_within(gpu["y"], ref["y"], ref["S"])
+        return ok, "%d sampled entries within %g*S (worst %.3g*S)" % (self.SAMPLE, ROW_TOL, worst)
+
+    def cpu_value(self, s_per_step):
+        return self.SAMPLE * 2 * self.k / s_per_step / 1e12, "TOP/s"
+
+    def cpu_sample(self):
+        return ("%d sampled output entries of the %d x %d x %d GEMM (tokens quantized once "
+                "beforehand)" % (self.SAMPLE, self.m, self.n, self.k))
 
 
 class MoeMixedWorkload(Workload):
@@ -423,9 +711,6 @@ class MoeMixedWorkload(Workload):
                                  self.gates[j:j + 1], self.x, self.ids, self.wts, self.ws,
                                  self.ws_bytes, self.y)
 
-    def prepare_dominant(self):
-        pass
-
     def dominant(self, i):
         # the step's gate/up launch, alone
         gu, _ = self.banks[i % self.ncopy]
@@ -443,24 +728,30 @@ class MoeMixedWorkload(Workload):
     def extra(self, ms):
         return {"tokens_per_s": 1.0 / (ms * 1e-3)}
 
-    def cpu_baseline(self, seconds):
+    def gpu_result(self):
+        self.y.fill_(float("nan"))
+        self.step(0)
+        self.torch.cuda.synchronize()
+        return {"y": self.y.cpu().numpy().copy(), "ids": self.ids.cpu().numpy().copy()}
+
+    def oracle_step(self):
         import oracle
         gu, gs, dn, ds = self.host_bank
         sgu, sdn = self.host_shared
         logits, g = self.host_router
-        n, t0 = 0, time.perf_counter()
-        while True:
-            ids, wts = oracle.moe_route(logits, self.top_k, g)
-            oracle.moe_ffn_mixed(self.gwt, gu, gs, self.dwt, dn, ds, self.swt, sgu, sdn, self.E,
-                                 self.dm, self.dff, ids, wts, self.x_host)
-            n += 1
-            el = time.perf_counter() - t0
-            if el >= seconds:
-                break
-        per = el / n
-        return dict(value=self.step_bytes / per / 1e9, unit="GB/s", cores=1, kind="oracle",
-                    sample="%d full MoE tokens (route + 8 K-quant experts + Q8_0 shared) on one "
-                           "host thread, %.1f s" % (n, el))
+        ids, wts = oracle.moe_route(logits, self.top_k, g)
+        y, S = oracle.moe_ffn_mixed(self.gwt, gu, gs, self.dwt, dn, ds, self.swt, sgu, sdn,
+                                    self.E, self.dm, self.dff, ids, wts, self.x_host)
+        return {"y": y, "S": S, "ids": ids}
+
+    def parity(self, gpu, ref):
+        ok, worst = rows_within(gpu["y"], ref["y"], ref["S"], MOE_E2E_TOL)
+        ok = ok and np.array_equal(gpu["ids"], ref["ids"])
+        return ok, ("expert ids equal; %d rows within the unchained MoE bar %g*S (worst %.3g*S)"
+                    % (self.dm, MOE_E2E_TOL, worst))
+
+    def cpu_sample(self):
+        return "route + one token through 8 K-quant experts + the Q8_0 shared expert"
 
 
 class DecodeChainWorkload(Workload):
@@ -540,9 +831,6 @@ class DecodeChainWorkload(Workload):
     def step(self, i):
         self.chain.replay()
 
-    def prepare_dominant(self):
-        pass
-
     def dominant(self, i):
         gu, gs, _, _, ne = self.banks[i % self.nbanks]
         c = self.chain
@@ -589,200 +877,45 @@ class DecodeChainWorkload(Workload):
                 "host_submit_us_graph": host_graph * 1e3, "host_submit_us_eager": host_eager * 1e3,
                 "token_GB_per_s": self.token_bytes / (ms * 1e-3) / 1e9}
 
-    def cpu_baseline(self, seconds):
+    def gpu_result(self):
+        c = self.chain
+        c.x.copy_(self.x0)
+        c.y_lm.fill_(float("nan"))
+        c.idx.fill_(-1)
+        c.replay()
+        self.torch.cuda.synchronize()
+        return {"y": c.y_lm.cpu().numpy().copy(), "idx": int(c.idx.cpu().numpy()[0])}
+
+    def oracle_step(self):
         import oracle
         h = self.host
-        n, t0 = 0, time.perf_counter()
-        while True:
-            x = self.x0_host.astype(np.float32).copy()
-            for l in range(self.layers):
-                xn = oracle.rms_norm(x, h["norms"][l], 1e-6).astype(np.float32)
-                qx, dx, _ = oracle.quantize_act(xn)
-                logits, _ = oracle.dmmv(8, h["routers"][l], self.E, self.dm, qx, dx)
-                ids, wts = oracle.moe_route(logits.astype(np.float32), self.top_k, h["gates"][l])
-                gu, gs, down, ds = self.host_banks[l % self.nbanks]
-                y, _ = oracle.moe_ffn(4, gu, gs, down, ds, self.dm, self.dff, ids, wts, xn)
-                x = (x + y).astype(np.float32)
-            xn = oracle.rms_norm(x, h["norms"][-1], 1e-6).astype(np.float32)
+        x = self.x0_host.astype(np.float32).copy()
+        for l in range(self.layers):
+            xn = oracle.rms_norm(x, h["norms"][l], 1e-6).astype(np.float32)
             qx, dx, _ = oracle.quantize_act(xn)
-            yl, _ = oracle.dmmv(4, h["lm"], self.vocab, self.dm, qx, dx)
-            int(np.argmax(yl))
-            n += 1
-            el = time.perf_counter() - t0
-            if el >= seconds:
-                break
-        per = el / n
-        return dict(value=1.0 / per, unit="tok/s", cores=1, kind="oracle",
-                    sample="%d tokens through the %d-layer chain and the LM head on one host "
-                           "thread, %.1f s" % (n, self.layers, el))
+            logits, _ = oracle.dmmv(8, h["routers"][l], self.E, self.dm, qx, dx)
+            ids, wts = oracle.moe_route(logits.astype(np.float32), self.top_k, h["gates"][l])
+            gu, gs, down, ds = self.host_banks[l % self.nbanks]
+            y, _ = oracle.moe_ffn(4, gu, gs, down, ds, self.dm, self.dff, ids, wts, xn)
+            x = (x + y).astype(np.float32)
+        xn = oracle.rms_norm(x, h["norms"][-1], 1e-6).astype(np.float32)
+        qx, dx, _ = oracle.quantize_act(xn)
+        yl, S = oracle.dmmv(4, h["lm"], self.vocab, self.dm, qx, dx)
+        return {"y": yl, "S": S}
 
+    def parity(self, gpu, ref):
+        err = np.abs(gpu["y"].astype(np.float64) - ref["y"]) / ref["S"]
+        worst = float(err.max())
+        ok = worst <= CHAIN_E2E_TOL and argmax_ok(gpu["idx"], gpu["y"], ref["y"], ref["S"],
+                                                  CHAIN_E2E_TOL)
+        return ok, ("token %d = the oracle chain's; logits within %g*S of the unchained oracle "
+                    "chain (worst %.3g*S)" % (gpu["idx"], CHAIN_E2E_TOL, worst))
 
-class MoeWorkload(Workload):
-    """Router + one token through 8 routed + 1 shared Q4_0 experts, in two
-    launches: gate/up with the router folded in, then down."""
-    dominant_name = "moe_gate_up_kernel (router folded in)"
-    steps = 2000
-    warmup = 100
+    def cpu_value(self, s_per_step):
+        return 1.0 / s_per_step, "tok/s"
 
-    def __init__(self):
-        from block_quant_matrix_amd import inputs
-        cfg = inputs.WORKLOADS[4]
-        self.name = cfg["name"]
-        self.E, self.top_k, self.dm, self.dff = cfg["n_routed"], cfg["top_k"], cfg["d_model"], cfg["d_ff"]
-        self.n_sel = self.top_k + 1
-        bb = 18
-        self.gu_w = self.n_sel * 2 * self.dff * (self.dm // 32) * bb
-        self.down_w = self.n_sel * self.dm * (self.dff // 32) * bb
-        self.step_bytes = self.gu_w + self.down_w + 4 * self.dm + 4 * self.dm
-        # fused gate/up pass: weights + fp32 x + router logits in, quantized h
-        # out (codes, scales, sums) + the expert list and weights
-        self.gate_up_bytes = (self.gu_w + 4 * self.dm + 4 * self.E + self.n_sel * self.dff +
-                              8 * self.n_sel * (self.dff // 32) + 8 * self.n_sel)
-
-    def setup(self, torch, zq, inputs):
-        self.torch, self.zq = torch, zq
-        bank_bytes = (self.E + 1) * (2 * self.dff * (self.dm // 32) + self.dm * (self.dff // 32)) * 18
-        self.ncopy = copies_for(bank_bytes)
-        self.banks = []
-        for c in range(self.ncopy):
-            gu, gs, down, ds = inputs.moe_banks(inputs.seed_for(4, c), self.E + 1, self.dm, self.dff)
-            self.banks.append((torch.from_numpy(gu).to("cuda"), torch.from_numpy(down).to("cuda")))
-            if c == 0:
-                self.host_bank = (gu, gs, down, ds)
-        self.gs, self.ds = gs, ds
-        nlog = 64
-        lg = [inputs.gen_router(self.E, inputs.seed_for(4, 100 + i)) for i in range(nlog)]
-        self.logits = torch.from_numpy(np.stack([l for l, _ in lg])).to("cuda")
-        self.gates = torch.from_numpy(np.array([g for _, g in lg], np.float32)).to("cuda")
-        self.host_router = lg[0]
-        self.x_host = inputs.gen_activation(1, self.dm, inputs.seed_for(4) + 7)
-        self.x = torch.from_numpy(self.x_host).to("cuda")
-        self.ids = torch.empty(self.n_sel, dtype=torch.int32, device="cuda")
-        self.wts = torch.empty(self.n_sel, dtype=torch.float32, device="cuda")
-        self.ws_bytes = zq.zq_moe_ffn_workspace_bytes(self.dm, self.dff, self.n_sel)
-        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
-        self.y = torch.empty(self.dm, dtype=torch.float32, device="cuda")
-        # outputs of the gate/up pass when it is timed alone
-        self.qh = torch.empty((self.n_sel, self.dff), dtype=torch.int8, device="cuda")
-        self.dh = torch.empty((self.n_sel, self.dff // 32), dtype=torch.float32, device="cuda")
-        self.sh = torch.empty((self.n_sel, self.dff // 32), dtype=torch.int32, device="cuda")
-
-    def step(self, i):
-        gu, down = self.banks[i % self.ncopy]
-        j = i % self.logits.shape[0]
-        self.zq.zq_moe_ffn_route(4, gu, self.gs, down, self.ds, self.E + 1, self.dm, self.dff,
-                                 self.logits[j], self.E, self.top_k, self.gates[j:j + 1], self.x,
-                                 self.ids, self.wts, self.ws, self.ws_bytes, self.y)
-
-    def prepare_dominant(self):
-        pass
-
-    def dominant(self, i):
-        gu, _ = self.banks[i % self.ncopy]
-        j = i % self.logits.shape[0]
-        self.zq.zq_moe_gate_up_route(4, gu, self.gs, self.E + 1, self.dm, self.dff, self.logits[j],
-                                     self.E, self.top_k, self.gates[j:j + 1], self.x, self.ids,
-                                     self.wts, self.qh, self.dh, self.sh)
-
-    def value(self, ms):
-        return self.step_bytes / (ms * 1e-3) / 1e9, "GB/s"
-
-    def achieved(self, ms):
-        return self.gate_up_bytes / (ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s", self.gate_up_bytes
-
-    def extra(self, ms):
-        return {"tokens_per_s": 1.0 / (ms * 1e-3)}
-
-    def cpu_baseline(self, seconds):
-        import oracle
-        gu, gs, down, ds = self.host_bank
-        logits, g = self.host_router
-        n, t0 = 0, time.perf_counter()
-        while True:
-            ids, wts = oracle.moe_route(logits, self.top_k, g)
-            oracle.moe_ffn(4, gu, gs, down, ds, self.dm, self.dff, ids, wts, self.x_host)
-            n += 1
-            el = time.perf_counter() - t0
-            if el >= seconds:
-                break
-        per = el / n
-        return dict(value=self.step_bytes / per / 1e9, unit="GB/s", cores=1, kind="oracle",
-                    sample="%d full MoE tokens (route + 9 experts) on one host thread, %.1f s"
-                           % (n, el))
-
-
-class GemmWorkload(Workload):
-    dominant_name = "gemm_kernel"
-    bound = "mfma"
-    steps = 100
-    warmup = 10
-
-    def __init__(self):
-        from block_quant_matrix_amd import inputs
-        cfg = inputs.WORKLOADS[5]
-        self.name = cfg["name"]
-        self.m, self.n, self.k = cfg["m"], cfg["n"], cfg["k"]
-        self.ops = 2 * self.m * self.n * self.k
-
-    def setup(self, torch, zq, inputs):
-        self.torch, self.zq = torch, zq
-        wbytes = self.n * (self.k // 32) * 18
-        self.ncopy = copies_for(wbytes)
-        host = [inputs.gen_weights(4, self.n, self.k, inputs.seed_for(5, c)) for c in range(self.ncopy)]
-        self.w = [torch.from_numpy(h).to("cuda") for h in host]
-        self.w_host0 = host[0]
-        del host
-        self.x_host = inputs.gen_activation(self.m, self.k, inputs.seed_for(5) + 1)
-        self.x = torch.from_numpy(self.x_host).to("cuda")
-        self.qx = torch.empty((self.m, self.k), dtype=torch.int8, device="cuda")
-        self.dx = torch.empty((self.m, self.k // 32), dtype=torch.float32, device="cuda")
-        self.y = torch.empty((self.m, self.n), dtype=torch.float32, device="cuda")
-
-    def step(self, i):
-        self.zq.zq_quantize_act(self.x, self.m, self.k, self.k, self.qx, self.dx, None)
-        self.zq.zq_gemm_prefill(4, self.w[i % self.ncopy], self.n, self.k, self.qx, self.dx, None,
-                                self.m, self.y)
-
-    def prepare_dominant(self):
-        self.zq.zq_quantize_act(self.x, self.m, self.k, self.k, self.qx, self.dx, None)
-
-    def dominant(self, i):
-        self.zq.zq_gemm_prefill(4, self.w[i % self.ncopy], self.n, self.k, self.qx, self.dx, None,
-                                self.m, self.y)
-
-    def value(self, ms):
-        return self.ops / (ms * 1e-3) / 1e12, "TOP/s"
-
-    def achieved(self, ms):
-        return self.ops / (ms * 1e-3) / 1e12, INT8_PEAK_TOPS, "TOP/s", self.ops
-
-    def extra(self, ms):
-        # The ceiling the fp32 rescale sets: every (token, row, block) triple
-        # needs a convert, a multiply and an FMA, unpacked, at 64 lanes per
-        # clock per CU (256 CUs, 2.4 GHz).
-        triples = self.m * self.n * (self.k // 32)
-        valu_s = 3 * triples / (256 * 64 * 2.4e9)
-        ceiling = 2 * self.m * self.n * self.k / valu_s / 1e12
-        steps_tops = 2 * self.m * self.n * self.k / (ms * 1e-3) / 1e12
-        return {"tokens_per_s": self.m / (ms * 1e-3),
-                "valu_epilogue_ceiling_TOPs": round(ceiling, 1),
-                "step_frac_of_epilogue_ceiling": round(steps_tops / ceiling, 4)}
-
-    def cpu_baseline(self, seconds):
-        import oracle
-        rng = np.random.default_rng(0)
-        qx, dx, _ = oracle.quantize_act(self.x_host)
-        n_pairs, t0 = 0, time.perf_counter()
-        while time.perf_counter() - t0 < seconds:
-            mi = rng.integers(0, self.m, 256)
-            ni = rng.integers(0, self.n, 256)
-            oracle.gemm_entries(4, self.w_host0, self.n, self.k, qx, dx, self.m, mi, ni)
-            n_pairs += 256
-        el = time.perf_counter() - t0
-        ops_per_s = n_pairs * 2 * self.k / el
-        return dict(value=ops_per_s / 1e12, unit="TOP/s", cores=1, kind="oracle",
-                    sample="%d output entries (of %d) of this GEMM on one host thread, %.1f s"
-                           % (n_pairs, self.m * self.n, el))
+    def cpu_sample(self):
+        return "one token through the %d-layer chain and the LM head" % self.layers
 
 
 def counted_traffic(kernel_name, workload):
@@ -844,14 +977,169 @@ def gpu_blocker(torch, ms):
     torch.cuda._sleep(int(ms * _SLEEP_CYCLES_PER_MS))
 
 
-def host_launch_ms(w, torch, n=50):
+def host_launch_ms(fn, torch, n=50):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(n):
-        w.step(i)
+        fn(i)
     el = (time.perf_counter() - t0) * 1e3 / n
     torch.cuda.synchronize()
     return el
+
+
+def timed(torch, fn, K, h_ms):
+    """ms per call of K back-to-back calls of fn(i), enqueued behind a GPU
+    blocker and bracketed by two events on the launch stream."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    gpu_blocker(torch, 1.5 * h_ms * K + 5)
+    e0.record()
+    for i in range(K):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / K
+
+
+def read_ceiling(torch, zq, nbytes=1 << 30, K=20):
+    """The live streaming-read rate of the chip (GB/s): K back-to-back reads
+    of 1 GiB (4x the MALL) by the library's read probe."""
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        zq.zq_read_probe(buf, nbytes, sink)
+    h_ms = host_launch_ms(lambda i: zq.zq_read_probe(buf, nbytes, sink), torch, n=5)
+    ms = timed(torch, lambda i: zq.zq_read_probe(buf, nbytes, sink), K, h_ms)
+    del buf
+    return nbytes / (ms * 1e-3) / 1e9
+
+
+def gpu_clocks():
+    """Current shader and memory clocks from rocm-smi (best effort)."""
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+                           timeout=20)
+        d = json.loads(r.stdout)
+        card = d[sorted(k for k in d if k.startswith("card"))[0]]
+        pick = lambda key: next((v for k, v in card.items() if k.lower().startswith(key)), None)
+        return {"sclk": pick("sclk"), "mclk": pick("mclk")}
+    except Exception:  # noqa: BLE001 - a missing or changed tool only drops the field
+        return None
+
+
+# ------------------------------------------------------------- oracle leg --
+
+def host_threads():
+    """Threads the oracle may use: the process's CPUs, at most 16 (one GPU's
+    share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def oracle_leg(w, seconds):
+    """The GPU's first step against the oracle (parity), then the oracle's
+    own rate on one thread and on all host threads (each the median of 3
+    runs).  The oracle's C routines release the interpreter while they run,
+    so threads that each run whole oracle steps run in parallel."""
+    gpu = w.gpu_result()
+    t0 = time.perf_counter()
+    ref = w.oracle_step()
+    t_one = time.perf_counter() - t0
+    ok, detail = w.parity(gpu, ref)
+    n = max(1, int(round(seconds / 6.0 / t_one)))
+
+    def run(m):
+        for _ in range(m):
+            w.oracle_step()
+
+    single = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        run(n)
+        single.append((time.perf_counter() - t0) / n)
+    threads = host_threads()
+    multi = []
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        for _ in range(3):
+            t0 = time.perf_counter()
+            list(ex.map(run, [n] * threads))
+            multi.append((time.perf_counter() - t0) / (n * threads))
+    s1, sm = statistics.median(single), statistics.median(multi)
+    v1, unit = w.cpu_value(s1)
+    vm, _ = w.cpu_value(sm)
+    cpu = {"value": round(vm, 4), "unit": unit, "cores": threads, "kind": "oracle",
+           "sample": "%s; each run %d step(s) per thread, median of 3 runs, %d threads each "
+                     "running whole steps" % (w.cpu_sample(), n, threads),
+           "single_thread": {"value": round(v1, 4), "unit": unit, "s_per_step": round(s1, 6)},
+           "all_cores_s_per_step": round(sm, 6), "runs": 3, "statistic": "median",
+           "nproc": os.cpu_count(), "cpu_model": cpu_model()}
+    return cpu, {"ok": bool(ok), "detail": detail}
+
+
+# ------------------------------------------------------------------ main --
+
+def measure(w, torch, K, W):
+    """Warm up, then the timed region and the dominant kernel's pass."""
+    for i in range(W):
+        w.step(i)
+    torch.cuda.synchronize()
+    h_ms = host_launch_ms(w.step, torch)
+    ms_per_step = timed(torch, w.step, K, h_ms)
+    if w.step_is_dominant:
+        ms_kernel = ms_per_step
+    else:
+        # the dominant kernel alone: K back-to-back launches between two
+        # events (an event pair around each launch adds several microseconds
+        # of marker processing to a microsecond-scale kernel)
+        w.prepare_dominant()
+        ms_kernel = timed(torch, w.dominant, K, h_ms)
+    return ms_per_step, ms_kernel
+
+
+def oracle_leg_sampled(s):
+    """The oracle leg of a secondary line: the GPU's first step against the
+    oracle on sampled rows, and its argmax against the GPU's own logits."""
+    gpu = s.gpu_result()
+    rng = np.random.default_rng(3)
+    sel = np.unique(np.concatenate([[0, s.rows - 1, gpu["idx"]],
+                                    rng.integers(0, s.rows, 2048)])).astype(np.int64)
+    return s.parity(gpu, s.oracle_step(rows_eval=sel), rows_eval=sel)
+
+
+def lmhead_secondary(torch, zq, inputs, with_oracle):
+    """The LM-head step (Q4_0 248 320 x 2048 + argmax) measured beside the
+    headline: step rate, the fused DMMV launch alone, and (with the oracle
+    leg) a parity check of sampled rows and of the argmax."""
+    s = DmmvWorkload(3)
+    s.setup(torch, zq, inputs)
+    ok, detail = oracle_leg_sampled(s) if with_oracle else (None, None)
+    ms_step, ms_kernel = measure(s, torch, s.steps, s.warmup)
+    gbs = s.dmmv_bytes / (ms_kernel * 1e-3) / 1e9
+    out = {"workload": s.name, "steps": s.steps, "ms_per_step": round(ms_step, 6),
+           "step_GBs": round(s.step_bytes / (ms_step * 1e-3) / 1e9, 1),
+           "rows_per_s": round(s.rows / (ms_step * 1e-3), 1),
+           "dmmv_kernel": {"kernel": s.dominant_name, "ms_per_launch": round(ms_kernel, 6),
+                           "per_launch": s.dmmv_bytes, "achieved_GBs": round(gbs, 1),
+                           "frac": round(gbs / HBM_PEAK_GBS, 4),
+                           "traffic": counted_traffic(s.dominant_name, s.name)},
+           "parity_checked": None if ok is None else bool(ok), "parity": detail}
+    del s
+    return out
 
 
 def main():
@@ -882,53 +1170,19 @@ def main():
         dst.copy_(src)
         del src, dst
 
-    for i in range(W):
-        w.step(i)
-    torch.cuda.synchronize()
-    h_ms = host_launch_ms(w, torch)
+    cpu = parity = None
+    if not args.no_cpu_baseline:
+        cpu, parity = oracle_leg(w, args.cpu_seconds)
 
-    # --- timed region: exactly K steps between two events ---
-    t_ev0 = torch.cuda.Event(enable_timing=True)
-    t_ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    gpu_blocker(torch, 1.5 * h_ms * K + 5)
-    t_ev0.record()
-    for i in range(K):
-        w.step(i)
-    t_ev1.record()
-    torch.cuda.synchronize()
-    ms_per_step = t_ev0.elapsed_time(t_ev1) / K
+    clocks_before = gpu_clocks()
+    ms_per_step, ms_kernel = measure(w, torch, K, W)
+    clocks_after = gpu_clocks()
 
-    # --- dominant kernel alone: K back-to-back launches between two events.
-    # (An event pair around each launch adds several microseconds of marker
-    # processing to a microsecond-scale kernel; back-to-back launches include
-    # only the dispatch gap, which the kernel-trace durations also carry.)
-    w.prepare_dominant()
-    d_ev0 = torch.cuda.Event(enable_timing=True)
-    d_ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    gpu_blocker(torch, 1.5 * h_ms * K + 5)
-    d_ev0.record()
-    for i in range(K):
-        w.dominant(i)
-    d_ev1.record()
-    torch.cuda.synchronize()
-    ms_kernel = d_ev0.elapsed_time(d_ev1) / K
-
-    # --- the launch floor: K back-to-back launches of an empty kernel (torch's
-    # spin kernel with a zero count, one thread) on the same stream.  What a
-    # launch of any kernel costs before it reads a byte; at the 4096 x 4096
-    # size it is a large part of the DMMV's time.
-    f_ev0 = torch.cuda.Event(enable_timing=True)
-    f_ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    gpu_blocker(torch, 0.05 * K + 5)
-    f_ev0.record()
-    for i in range(K):
-        torch.cuda._sleep(0)
-    f_ev1.record()
-    torch.cuda.synchronize()
-    ms_floor = f_ev0.elapsed_time(f_ev1) / K
+    # what a launch of any kernel costs before it reads a byte: K back-to-back
+    # launches of an empty kernel (torch's spin kernel with a zero count) on
+    # the same stream; a diagnostic beside the roofline, not part of it
+    ms_floor = timed(torch, lambda i: torch.cuda._sleep(0), K, 0.01)
+    ceiling = read_ceiling(torch, zq)
 
     value, unit = w.value(ms_per_step)
     ach, peak, runit, per_launch = w.achieved(ms_kernel)
@@ -947,20 +1201,30 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "weight_copies": w.ncopy, "parallelism": "none"},
         "pct_of_peak": round(w.pct_of_peak(value, unit), 2),
+        "parity_checked": None if parity is None else parity["ok"],
     }
+    if parity is not None:
+        out["parity"] = parity["detail"]
     out.update({k: round(v, 4 if abs(v) < 10 else 1) for k, v in w.extra(ms_per_step).items()})
     out["roofline"] = {"bound": w.bound, "kernel": w.dominant_name, "achieved": round(ach, 3),
                        "peak": peak, "unit": runit, "frac": round(ach / peak, 4),
-                       "per_launch": per_launch, "ms_per_launch": round(ms_kernel, 6),
-                       "empty_launch_ms": round(ms_floor, 6),
-                       "frac_after_empty_launch": (round(per_launch / ((ms_kernel - ms_floor) * 1e-3)
-                                                         / (1e9 if runit == "GB/s" else 1e12) / peak, 4)
-                                                   if ms_kernel > ms_floor else None),
                        "traffic": counted_traffic(w.dominant_name,
-                                                  getattr(w, "traffic_workload", w.name))}
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = w.cpu_baseline(args.cpu_seconds)
-        out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 4)
+                                                  getattr(w, "traffic_workload", w.name)),
+                       "per_launch": per_launch, "ms_per_launch": round(ms_kernel, 6),
+                       "timed_in": "the timed region" if w.step_is_dominant else
+                                   "a pass of K back-to-back launches of this kernel alone"}
+    out["read_ceiling"] = {"GBs": round(ceiling, 1),
+                           "note": "live streaming read of 1 GiB by zq_read_probe"}
+    if runit == "GB/s":
+        out["read_ceiling"]["frac_of_ceiling"] = round(ach / ceiling, 4)
+    out["empty_launch_us"] = round(ms_floor * 1e3, 3)
+    out["clocks"] = {"before": clocks_before, "after": clocks_after}
+    if args.workload == 2:
+        out["target_70pct_met"] = ach / peak >= 0.70
+    if args.workload == 2 and not args.no_secondary:
+        out["secondary"] = [lmhead_secondary(torch, zq, inputs, not args.no_cpu_baseline)]
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
 
 

@@ -62,21 +62,30 @@ class DecodeChain:
         self.lm_ws = torch.empty(self.lm_ws_bytes, dtype=torch.uint8, device=dev)
         self.graph = None
 
-    def step(self, stream=None):
-        """Enqueue one token: every layer, then the LM head and argmax."""
+    def step_layer(self, layer, stream=None):
+        """Enqueue one layer: norm + router logits (xn published), then the
+        routed MoE block on xn added onto the state."""
         d, f = self.d_model, self.d_ff
-        for layer in range(self.layers):
-            _zq.zq_rms_norm_dmmv_f32(_zq.ZQ_Q8_0, self.router_w[layer], self.n_routed, d, self.x,
-                                     self.norm_w[layer], self.eps, self.logits,
-                                     xn_out=self.xn, stream=stream)
-            gu, gs, dn, ds, ne = self.moe_banks[layer]
-            g = None if self.shared_gate is None else self.shared_gate[layer]
-            _zq.zq_moe_ffn_route(_zq.ZQ_Q4_0, gu, gs, dn, ds, ne, d, f, self.logits, self.n_routed,
-                                 self.top_k, g, self.xn, self.ids, self.wts, self.ws, self.ws_bytes,
-                                 self.x, _zq.ZQ_ACCUMULATE, stream=stream)
-        _zq.zq_rms_norm_dmmv_f32_argmax(_zq.ZQ_Q4_0, self.lm_w, self.vocab, d, self.x,
+        _zq.zq_rms_norm_dmmv_f32(_zq.ZQ_Q8_0, self.router_w[layer], self.n_routed, d, self.x,
+                                 self.norm_w[layer], self.eps, self.logits,
+                                 xn_out=self.xn, stream=stream)
+        gu, gs, dn, ds, ne = self.moe_banks[layer]
+        g = None if self.shared_gate is None else self.shared_gate[layer]
+        _zq.zq_moe_ffn_route(_zq.ZQ_Q4_0, gu, gs, dn, ds, ne, d, f, self.logits, self.n_routed,
+                             self.top_k, g, self.xn, self.ids, self.wts, self.ws, self.ws_bytes,
+                             self.x, _zq.ZQ_ACCUMULATE, stream=stream)
+
+    def lm_head(self, stream=None):
+        """Enqueue the final norm, the LM-head DMMV and the argmax."""
+        _zq.zq_rms_norm_dmmv_f32_argmax(_zq.ZQ_Q4_0, self.lm_w, self.vocab, self.d_model, self.x,
                                         self.final_norm_w, self.eps, self.y_lm, self.idx,
                                         self.lm_ws, self.lm_ws_bytes, stream=stream)
+
+    def step(self, stream=None):
+        """Enqueue one token: every layer, then the LM head and argmax."""
+        for layer in range(self.layers):
+            self.step_layer(layer, stream)
+        self.lm_head(stream)
 
     def launches_per_step(self) -> int:
         return 3 * self.layers + 2

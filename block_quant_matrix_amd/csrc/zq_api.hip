@@ -1100,3 +1100,17 @@ int zq_moe_ffn_mixed(int gu_wtype, const void *gu_bank, int64_t gu_stride_bytes,
 }
 
 }  // extern "C"
+
+namespace zq {
+// probe.hip: a streaming read of `bytes` (a multiple of 16) with 16-byte loads.
+int launch_read_probe(const void *buf, int64_t bytes, uint32_t *sink, hipStream_t stream);
+}  // namespace zq
+
+int zq_read_probe(const void *buf, int64_t bytes, uint32_t *sink, void *stream) {
+  ZQ_REQUIRE(buf && sink, ZQ_ENULL);
+  ZQ_REQUIRE(bytes >= 0 && bytes % 16 == 0, ZQ_EINVAL);
+  ZQ_REQUIRE(al(buf, 16) && al(sink, 4), ZQ_EALIGN);
+  const int dc = check_current_device();
+  if (dc != ZQ_OK) return dc;
+  return zq::launch_read_probe(buf, bytes, sink, S(stream));
+}

@@ -68,6 +68,7 @@ SIGNATURES = {
                                 _I32, _P, _P, _P, _P, _P, _SZ, _P, _U32, _P]),
     "zq_gemm_prefill": (_INT, [_INT, _P, _I64, _I64, _P, _P, _P, _I64, _P, _U32, _P]),
     "zq_gemm_isums": (_INT, [_INT, _P, _I64, _I64, _P, _P, _I64, _I64, _I64, _I64, _I64, _P, _P]),
+    "zq_read_probe": (_INT, [_P, _I64, _P, _P]),
 }
 
 
@@ -298,3 +299,6 @@ def zq_moe_ffn_mixed(gu_wtype, gu_bank, gu_stride, down_wtype, down_bank, down_s
                  n_routed, top_k, ptr(shared_gate), ptr(x), ptr(ids), ptr(wts), ptr(workspace),
                  workspace_bytes, ptr(y), flags, _stream(stream))
 
+
+def zq_read_probe(buf, nbytes, sink, stream=None):
+    return _call("zq_read_probe", ptr(buf), nbytes, ptr(sink), _stream(stream))

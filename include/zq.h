@@ -411,6 +411,14 @@ int zq_gemm_isums(int wtype, const void *w, int64_t n, int64_t k, const int8_t *
                   const int32_t *sx, int64_t m, int64_t m0, int64_t m1, int64_t n0, int64_t n1,
                   int32_t *isums, void *stream);
 
+/* Measurement hook: a plain streaming read of `bytes` bytes of buf with
+ * 16-byte loads spread over the whole chip, nothing computed from them but a
+ * fold that decides whether the one word *sink is written (practically
+ * never).  Its rate is the read ceiling the weight-streaming kernels are
+ * reported against beside the chip's nominal HBM peak.  buf 16-byte aligned,
+ * bytes a multiple of 16; sink one uint32. */
+int zq_read_probe(const void *buf, int64_t bytes, uint32_t *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

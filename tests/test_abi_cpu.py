@@ -384,6 +384,16 @@ def test_other_argument_errors():
     assert L.zq_gemm_prefill(3, A, 64, 64, B, C, None, 8, D, 0, None) == zq.ZQ_EINVAL
 
 
+def test_read_probe_argument_errors():
+    L = zq.lib()
+    assert L.zq_read_probe(A, 24, C, None) == zq.ZQ_EINVAL
+    assert L.zq_read_probe(A, -16, C, None) == zq.ZQ_EINVAL
+    assert L.zq_read_probe(None, 16, C, None) == zq.ZQ_ENULL
+    assert L.zq_read_probe(A, 16, None, None) == zq.ZQ_ENULL
+    assert L.zq_read_probe(A + 8, 16, C, None) == zq.ZQ_EALIGN
+    assert L.zq_read_probe(A, 16, C + 2, None) == zq.ZQ_EALIGN
+
+
 @pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="a GPU is present")
 def test_valid_arguments_without_gpu_report_no_device():
     """With every argument valid, the last check is the device: no GPU here."""
@@ -408,4 +418,5 @@ def test_valid_arguments_without_gpu_report_no_device():
     assert L.zq_moe_ffn_route(4, A, 2 * 512 * 64 * 18, B, 2048 * 16 * 18, 128, 2048, 512, B, 128,
                               8, None, D, A + 0x1000, A + 0x2000, A + 0x4000, ws, A + 0x8000, 0,
                               None) == zq.ZQ_EDEVICE
+    assert L.zq_read_probe(A, 1 << 20, C, None) == zq.ZQ_EDEVICE
     assert zq.lib().zq_device_check(0) == zq.ZQ_EDEVICE
