@@ -15,6 +15,7 @@ Value distributions (the workloads' recipe):
     fifth bits, 6-bit sub-block scales/mins (Q4_K, Q5_K) uniform in 0..255;
     Q6_K sub-block scales int8 uniform in [-128, 127]; the super-block d and
     dmin |N(0,1)|*0.001 rounded once to fp16.
+  * F16 / F32 weights: N(0,1)*0.02 rounded once to the weight type.
   * activations: fp32 N(0,1).
   * MoE router logits: fp32 N(0,1); shared-expert gate scalar: fp32 N(0,1).
 Seeds: workload i (1-based, in the order below) uses 1000*i + s.
@@ -28,6 +29,9 @@ Q8_0 = 8
 Q4_K = 12
 Q5_K = 13
 Q6_K = 14
+F16 = 16
+F32 = 32
+FLOAT_BYTES = {F16: 2, F32: 4}
 BLOCK_BYTES = {Q4_0: 18, Q8_0: 34}
 SCALE_C = {Q8_0: 0.01, Q4_0: 0.02, Q4_K: 0.001, Q5_K: 0.001, Q6_K: 0.001}
 # K-quant super-blocks: bytes per 256 elements
@@ -100,6 +104,15 @@ def gen_weights_k(wtype: int, rows: int, k: int, seed: int) -> np.ndarray:
     return out.reshape(-1)
 
 
+def gen_weights_float(wtype: int, rows: int, k: int, seed: int, c: float = 0.02) -> np.ndarray:
+    """Random float weight matrix [rows][k] (N(0,1)*c in fp64, rounded once to
+    binary16 or binary32) as raw little-endian bytes (uint8)."""
+    rng = np.random.default_rng(seed)
+    v = rng.standard_normal((rows, k), dtype=np.float64) * c
+    dt = "<f2" if wtype == F16 else "<f4"
+    return np.ascontiguousarray(v.astype(dt)).view(np.uint8).reshape(-1)
+
+
 def gen_activation(n_tok: int, k: int, seed: int) -> np.ndarray:
     rng = np.random.default_rng(seed)
     x = rng.standard_normal((n_tok, k), dtype=np.float32)
@@ -140,6 +153,9 @@ WORKLOADS = {
     # small-M at the vocabulary shape: eight tokens through the LM head
     12: dict(name="q4_0_lmhead_8tok_248320x2048", wtype=Q4_0, rows=248320, k=2048, n_tok=8),
     13: dict(name="q8_0_lmhead_248320x2048_argmax", wtype=Q8_0, rows=248320, k=2048),
+    # the F16 member of the DMMV family: the headline shape and the LM head
+    14: dict(name="f16_dmmv_4096x4096", wtype=F16, rows=4096, k=4096),
+    15: dict(name="f16_lmhead_dmmv_248320x2048", wtype=F16, rows=248320, k=2048),
 }
 
 

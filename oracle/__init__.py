@@ -29,6 +29,9 @@ Q8_0 = 8
 Q4_K = 12
 Q5_K = 13
 Q6_K = 14
+F16 = 16
+F32 = 32
+FLOAT_BYTES = {F16: 2, F32: 4}
 BLOCK_BYTES = {Q4_0: 18, Q8_0: 34}
 K_BLOCK_BYTES = {Q4_K: 144, Q5_K: 176, Q6_K: 210}
 
@@ -83,6 +86,7 @@ def lib() -> ctypes.CDLL:
         L.zqref_k_decode.argtypes = [I, P, P, P, P, P, P]
         L.zqref_k_dmmv_rows.argtypes = [I, P, I64, I64, P, P, P, P, I64, P, P, P]
         L.zqref_k_bruteforce.argtypes = [I, P, I64, I64, P, P, P, I64, P]
+        L.zqref_float_dmmv_rows.argtypes = [I, P, I64, I64, P, P, P, I64, P, P]
         _lib = L
     return _lib
 
@@ -233,6 +237,22 @@ def k_bruteforce(wtype, w, rows, k, qx, dx, rows_eval=None):
     _check(lib().zqref_k_bruteforce(wtype, _p(w), rows, k, _p(qx), _p(dx), _p(idx), n, _p(y)),
            "k_bruteforce")
     return y
+
+
+def float_dmmv(wtype: int, w: np.ndarray, rows: int, k: int, x, rows_eval=None, y_prev=None):
+    """fp64 reference rows of a float (F16 / F32) weight matrix times the fp32
+    activation: (y_ref, S)."""
+    w = _c(w, np.uint8)
+    assert w.size >= rows * k * FLOAT_BYTES[wtype]
+    x = _c(x, np.float32)
+    idx = None if rows_eval is None else _c(rows_eval, np.int64)
+    n = rows if idx is None else idx.size
+    y = np.empty(n, np.float64)
+    S = np.empty(n, np.float64)
+    yp = None if y_prev is None else _c(y_prev, np.float32)
+    _check(lib().zqref_float_dmmv_rows(wtype, _p(w), rows, k, _p(x), _p(yp), _p(idx), n, _p(y),
+                                       _p(S)), "float_dmmv_rows")
+    return y, S
 
 
 def argmax_f32(y: np.ndarray) -> int:

@@ -287,6 +287,59 @@ int zqref_dmmv_bruteforce(int wtype, const uint8_t *w, int64_t rows, int64_t k,
     return ZQREF_OK;
 }
 
+/* ------------------------------------------------------ float weights -- */
+
+#define ZQREF_F16 16
+#define ZQREF_F32 32
+
+/* DMMV over a matrix of plain floats, the F16 / F32 members of the DMMV
+ * shader family beside the block formats (habr "Как мы запустили 35B LLM
+ * ...", section "Что такое DMMV"; the same read-dequantize-multiply-write
+ * operation with a float weight).  A float matrix has no blocks to pair with
+ * int8 codes, so the activation is the fp32 vector itself (the reading
+ * documented with the library):
+ *   y_ref[i] = sum_j (double)w[r][j] * (double)x[j]  (sequential, fp64)
+ *   S[i]     = sum_j |w[r][j] * x[j]|
+ * w: rows x k, row-major, little-endian binary16 (ZQREF_F16) or binary32
+ * (ZQREF_F32).  With y_prev (accumulate): y_ref += y_prev[r], S += |y_prev[r]|.
+ * Non-finite weights or activations are refused. */
+static double float_weight(int wtype, const uint8_t *w, int64_t idx)
+{
+    if (wtype == ZQREF_F16) return zqref_fp16_to_f64((uint16_t)(w[2 * idx] | (w[2 * idx + 1] << 8)));
+    float f;
+    memcpy(&f, w + 4 * idx, 4);
+    return (double)f;
+}
+
+int zqref_float_dmmv_rows(int wtype, const uint8_t *w, int64_t rows, int64_t k, const float *x,
+                          const float *y_prev, const int64_t *row_idx, int64_t n_eval,
+                          double *y_ref, double *S)
+{
+    if ((wtype != ZQREF_F16 && wtype != ZQREF_F32) || k <= 0 || rows < 0 || n_eval < 0)
+        return ZQREF_EINVAL;
+    for (int64_t j = 0; j < k; j++)
+        if (!isfinite(x[j])) return ZQREF_ENONFINITE;
+    for (int64_t i = 0; i < n_eval; i++) {
+        int64_t r = row_idx ? row_idx[i] : i;
+        if (r < 0 || r >= rows) return ZQREF_EINVAL;
+        double y = 0.0, s = 0.0;
+        for (int64_t j = 0; j < k; j++) {
+            double wv = float_weight(wtype, w, r * k + j);
+            if (!isfinite(wv)) return ZQREF_ENONFINITE;
+            double t = wv * (double)x[j];
+            y += t;
+            s += fabs(t);
+        }
+        if (y_prev) {
+            y += (double)y_prev[r];
+            s += fabs((double)y_prev[r]);
+        }
+        y_ref[i] = y;
+        if (S) S[i] = s;
+    }
+    return ZQREF_OK;
+}
+
 /* The unquantized-activation product sum_j w_deq[r][j] * x[j] (report only). */
 int zqref_dmmv_true(int wtype, const uint8_t *w, int64_t rows, int64_t k, const float *x,
                     const int64_t *row_idx, int64_t n_eval, double *y_true)

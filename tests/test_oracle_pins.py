@@ -864,3 +864,77 @@ def test_p16_rms_norm_invariants(ref):
     xn2 = ref.rms_norm(x2, np.ones(64, np.float32), 1e-6)
     for t in range(3):
         assert np.array_equal(xn2[t], ref.rms_norm(x2[t], np.ones(64, np.float32), 1e-6))
+
+
+# -------------------------------------------------- P17: float weights ----
+# The F16 / F32 DMMV over the fp32 activation.
+
+F16, F32 = 16, 32
+
+
+def _float_bytes(wt, vals):
+    return np.ascontiguousarray(np.asarray(vals, np.float64).astype("<f2" if wt == F16 else "<f4")
+                                ).view(np.uint8).reshape(-1)
+
+
+@pytest.mark.parametrize("wt", [F16, F32])
+def test_p17_all_ones_and_single_element(ref, wt):
+    rows, k = 5, 96
+    w = _float_bytes(wt, np.ones((rows, k)))
+    y, S = ref.float_dmmv(wt, w, rows, k, np.full(k, 0.75, np.float32))
+    assert np.all(y == 0.75 * k) and np.all(S == 0.75 * k)
+    rng = np.random.default_rng(170)
+    x = rng.standard_normal(k).astype(np.float32)
+    for r0, j0, h in [(0, 0, -1.5), (4, 95, 0.0009765625), (2, 33, 65504.0), (3, 7, 2.0 ** -24)]:
+        vals = np.zeros((rows, k))
+        vals[r0, j0] = h
+        y, S = ref.float_dmmv(wt, _float_bytes(wt, vals), rows, k, x)
+        expect = np.zeros(rows)
+        expect[r0] = h * float(x[j0])   # exact: 11 (or 24) x 24 significant bits
+        assert np.array_equal(y, expect) and np.array_equal(S, np.abs(expect))
+
+
+def test_p17_f16_byte_order_and_subnormals(ref):
+    """Little-endian binary16: bytes (0x00, 0x3C) are 1.0; (0x3C, 0x00) is
+    the subnormal 60 * 2^-24.  Subnormals decode exactly."""
+    x = np.array([1.0, 2.0, 3.0, 4.0, 5.0, 6.0, 7.0, 8.0], np.float32)
+    w = np.zeros(16, np.uint8)
+    w[1] = 0x3C
+    assert ref.float_dmmv(F16, w, 1, 8, x)[0][0] == 1.0
+    w[:] = 0
+    w[0] = 0x3C
+    assert ref.float_dmmv(F16, w, 1, 8, x)[0][0] == 60 * 2.0 ** -24
+    w = np.tile(np.array([0x01, 0x00], np.uint8), 8)   # every weight 2^-24
+    assert ref.float_dmmv(F16, w, 1, 8, x)[0][0] == 36 * 2.0 ** -24
+
+
+@pytest.mark.parametrize("wt", [F16, F32])
+def test_p17_bruteforce_against_numpy(ref, wt):
+    """Random rows against numpy's own float16/float32 decode and a float64
+    dot product, within 1e-12 of the error scale; accumulate adds y_prev."""
+    rows, k = 7, 1000
+    w = inputs.gen_weights_float(wt, rows, k, 171)
+    x = inputs.gen_activation(1, k, 172)
+    wd = w.view("<f2" if wt == F16 else "<f4").astype(np.float64).reshape(rows, k)
+    yb = wd @ x.astype(np.float64)
+    y, S = ref.float_dmmv(wt, w, rows, k, x)
+    assert np.all(np.abs(y - yb) <= 1e-12 * S)
+    assert np.allclose(S, np.abs(wd * x.astype(np.float64)).sum(1), rtol=1e-12, atol=0)
+    prev = np.arange(rows, dtype=np.float32) - 3
+    y2, S2 = ref.float_dmmv(wt, w, rows, k, x, y_prev=prev)
+    assert np.all(np.abs(y2 - (y + prev)) <= 1e-12 * S2)
+    # negating x negates y exactly; a subset of rows is those rows
+    assert np.array_equal(ref.float_dmmv(wt, w, rows, k, -x)[0], -y)
+    idx = np.array([6, 0, 3])
+    assert np.array_equal(ref.float_dmmv(wt, w, rows, k, x, rows_eval=idx)[0], y[idx])
+
+
+def test_p17_refuses_non_finite(ref):
+    w = _float_bytes(F16, np.ones((1, 8)))
+    x = np.ones(8, np.float32)
+    x[3] = np.inf
+    with pytest.raises(RuntimeError):
+        ref.float_dmmv(F16, w, 1, 8, x)
+    w = _float_bytes(F32, [[1, 1, np.nan, 1, 1, 1, 1, 1]])
+    with pytest.raises(RuntimeError):
+        ref.float_dmmv(F32, w, 1, 8, np.ones(8, np.float32))
