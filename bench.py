@@ -51,7 +51,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", type=int, default=2, choices=list(range(1, 14)))
+    ap.add_argument("--workload", type=int, default=2, choices=list(range(1, 16)))
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle leg (no parity check, no CPU timing)")
     ap.add_argument("--no-secondary", action="store_true",
@@ -108,6 +108,7 @@ class Workload:
     steps = 2000
     warmup = 50
     step_is_dominant = False  # a step is exactly one launch of the dominant kernel
+    dtype = "int8"            # the arithmetic the dominant kernel's products run in
 
     def setup(self, torch, zq, inputs):
         raise NotImplementedError
@@ -918,6 +919,70 @@ class DecodeChainWorkload(Workload):
         return "one token through the %d-layer chain and the LM head" % self.layers
 
 
+class FloatDmmvWorkload(Workload):
+    """The F16 DMMV from the fp32 activation (one launch): the headline shape
+    and the LM head."""
+    step_is_dominant = True
+    dtype = "f16 x f32 -> f32"
+
+    def __init__(self, wl):
+        from block_quant_matrix_amd import inputs
+        cfg = inputs.WORKLOADS[wl]
+        self.wl = wl
+        self.name = cfg["name"]
+        self.wtype, self.rows, self.k = cfg["wtype"], cfg["rows"], cfg["k"]
+        self.wbytes = self.rows * self.k * inputs.FLOAT_BYTES[self.wtype]
+        self.dominant_name = "dmmv_float_kernel (F16)"
+        # weights + fp32 activation in + fp32 rows out
+        self.step_bytes = self.wbytes + 4 * self.k + 4 * self.rows
+        self.steps, self.warmup = (2000, 100) if self.wbytes < (256 << 20) else (60, 5)
+
+    def setup(self, torch, zq, inputs):
+        self.torch, self.zq = torch, zq
+        self.ncopy = copies_for(self.wbytes)
+        self.w = []
+        for c in range(self.ncopy):
+            h = inputs.gen_weights_float(self.wtype, self.rows, self.k, inputs.seed_for(self.wl, c))
+            self.w.append(torch.from_numpy(h).to("cuda"))
+            if c == 0:
+                self.w_host0 = h
+            del h
+        self.x_host = inputs.gen_activation(1, self.k, inputs.seed_for(self.wl) + 1)
+        self.x = torch.from_numpy(self.x_host).to("cuda")
+        self.y = torch.empty(self.rows, dtype=torch.float32, device="cuda")
+
+    def step(self, i):
+        self.zq.zq_dmmv_float(self.wtype, self.w[i % self.ncopy], self.rows, self.k, self.x,
+                              self.y)
+
+    def value(self, ms):
+        return self.step_bytes / (ms * 1e-3) / 1e9, "GB/s"
+
+    def achieved(self, ms):
+        return self.step_bytes / (ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s", self.step_bytes
+
+    def extra(self, ms):
+        return {"rows_per_s": self.rows / (ms * 1e-3)}
+
+    def gpu_result(self):
+        self.y.fill_(float("nan"))
+        self.step(0)
+        self.torch.cuda.synchronize()
+        return {"y": self.y.cpu().numpy().copy()}
+
+    def oracle_step(self):
+        import oracle
+        y, S = oracle.float_dmmv(self.wtype, self.w_host0, self.rows, self.k, self.x_host)
+        return {"y": y, "S": S}
+
+    def parity(self, gpu, ref):
+        ok, worst = rows_within(gpu["y"], ref["y"], ref["S"])
+        return ok, "%d rows within %g*S (worst %.3g*S)" % (self.rows, ROW_TOL, worst)
+
+    def cpu_sample(self):
+        return "a %d-row F16 DMMV over this workload's first weight copy" % self.rows
+
+
 def counted_traffic(kernel_name, workload):
     """HBM bytes per launch of the kernel at this workload from the committed
     counter runs (profiles/traffic.json, keyed by workload), or None when
@@ -952,6 +1017,8 @@ def make_workload(wl):
         return DecodeChainWorkload(wl)
     if wl == 11:
         return MoeMixedWorkload(wl)
+    if wl in (14, 15):
+        return FloatDmmvWorkload(wl)
     return GemmWorkload()
 
 
@@ -1197,7 +1264,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8",
+        "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "weight_copies": w.ncopy, "parallelism": "none"},
         "pct_of_peak": round(w.pct_of_peak(value, unit), 2),

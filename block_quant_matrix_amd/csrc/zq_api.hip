@@ -5,6 +5,7 @@
 #include <cstring>
 
 #include "zq_common.h"
+#include "zq_float.h"
 #include "zq_internal.h"
 
 namespace {
@@ -307,6 +308,25 @@ int zq_dmmv_isums(int wtype, const void *w, int64_t rows, int64_t k, const int8_
   // fp32 partial.
   a.dx = reinterpret_cast<const float *>(qx);
   return zq::launch_dmmv(wtype, zq::MODE_ISUMS, a, S(stream));
+}
+
+int zq_dmmv_float(int wtype, const void *w, int64_t rows, int64_t k, const float *x, float *y,
+                  uint32_t flags, void *stream) {
+  ZQ_REQUIRE(wtype == ZQ_F16 || wtype == ZQ_F32, ZQ_EINVAL);
+  ZQ_REQUIRE(w && x && y, ZQ_ENULL);
+  ZQ_REQUIRE(rows >= 0 && k > 0 && k % 8 == 0 && k <= 16384, ZQ_EINVAL);
+  ZQ_REQUIRE((flags & ~uint32_t(ZQ_ACCUMULATE)) == 0, ZQ_EINVAL);
+  ZQ_REQUIRE(al(w, 16) && al(x, 16) && al(y, 4), ZQ_EALIGN);
+  const int dc = check_current_device();
+  if (dc != ZQ_OK) return dc;
+  zq::FloatDmmvArgs a{};
+  a.w = static_cast<const uint8_t *>(w);
+  a.x = x;
+  a.y = y;
+  a.rows = rows;
+  a.k = static_cast<int32_t>(k);
+  a.flags = flags;
+  return zq::launch_dmmv_float(wtype, a, S(stream));
 }
 
 size_t zq_argmax_workspace_bytes(int64_t n) { return zq::argmax_workspace(n); }

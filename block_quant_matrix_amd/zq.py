@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(HERE, "libzq.so")
 
 ZQ_OK, ZQ_EINVAL, ZQ_ENULL, ZQ_EALIGN, ZQ_ERANGE, ZQ_EDEVICE, ZQ_ELAUNCH = 0, -1, -2, -3, -4, -5, -6
 ZQ_ACCUMULATE = 1
-ZQ_Q4_0, ZQ_Q8_0, ZQ_Q4_K, ZQ_Q5_K, ZQ_Q6_K = 4, 8, 12, 13, 14
+ZQ_Q4_0, ZQ_Q8_0, ZQ_Q4_K, ZQ_Q5_K, ZQ_Q6_K, ZQ_F16, ZQ_F32 = 4, 8, 12, 13, 14, 16, 32
 ZQ_MOE_GATHER, ZQ_MOE_WEIGHTED_SUM = 0, 1
 
 _P = ctypes.c_void_p
@@ -43,6 +43,7 @@ SIGNATURES = {
                                            _SZ, _P]),
     "zq_dmmv_tokens": (_INT, [_INT, _P, _I64, _I64, _P, _P, _P, _I32, _P, _U32, _P]),
     "zq_dmmv_f32": (_INT, [_INT, _P, _I64, _I64, _P, _P, _U32, _P, _P, _P, _P]),
+    "zq_dmmv_float": (_INT, [_INT, _P, _I64, _I64, _P, _P, _U32, _P]),
     "zq_dmmv_isums": (_INT, [_INT, _P, _I64, _I64, _P, _P, _P, _P]),
     "zq_argmax_workspace_bytes": (_SZ, [_I64]),
     "zq_argmax_f32": (_INT, [_P, _I64, _P, _P, _SZ, _P]),
@@ -190,6 +191,10 @@ def zq_dmmv_f32(wtype, w, rows, k, x, y, flags=0, qx_out=None, dx_out=None, sx_o
                 stream=None):
     return _call("zq_dmmv_f32", wtype, ptr(w), rows, k, ptr(x), ptr(y), flags, ptr(qx_out),
                  ptr(dx_out), ptr(sx_out), _stream(stream))
+
+
+def zq_dmmv_float(wtype, w, rows, k, x, y, flags=0, stream=None):
+    return _call("zq_dmmv_float", wtype, ptr(w), rows, k, ptr(x), ptr(y), flags, _stream(stream))
 
 
 def zq_dmmv_isums(wtype, w, rows, k, qx, sx, isums, stream=None):

@@ -54,7 +54,8 @@ enum zq_status {
 };
 
 enum zq_flags { ZQ_ACCUMULATE = 1 /* y += W.x instead of y = W.x */ };
-enum zq_wtype { ZQ_Q4_0 = 4, ZQ_Q8_0 = 8, ZQ_Q4_K = 12, ZQ_Q5_K = 13, ZQ_Q6_K = 14 };
+enum zq_wtype { ZQ_Q4_0 = 4, ZQ_Q8_0 = 8, ZQ_Q4_K = 12, ZQ_Q5_K = 13, ZQ_Q6_K = 14, ZQ_F16 = 16,
+                ZQ_F32 = 32 };
 enum zq_moe_mode { ZQ_MOE_GATHER = 0, ZQ_MOE_WEIGHTED_SUM = 1 };
 
 int zq_version(void);
@@ -113,6 +114,19 @@ int zq_dmmv_q5_k(const void *w, int64_t rows, int64_t k, const int8_t *qx, const
                  const int32_t *sx, float *y, uint32_t flags, void *stream);
 int zq_dmmv_q6_k(const void *w, int64_t rows, int64_t k, const int8_t *qx, const float *dx,
                  float *y, uint32_t flags, void *stream);
+
+/* The DMMV over a plain float weight matrix, the F16 and F32 members of the
+ * DMMV shader family beside the block formats (habr "Как мы запустили 35B
+ * LLM ...", section "Что такое DMMV", which lists separate shaders for the
+ * K-quants, Q8_0, F16 and F32).  A float matrix has no blocks to pair with
+ * int8 codes, so the activation is the fp32 vector itself:
+ *   y[r] (+)= sum_j w[r][j] * x[j], accumulated in fp32.
+ * wtype ZQ_F16 (little-endian binary16) or ZQ_F32 (binary32); w: rows x k,
+ * row-major, 16-byte aligned; x [k] fp32, 16-byte aligned, finite; y [rows]
+ * fp32; k a positive multiple of 8, at most 16384; flags 0 or
+ * ZQ_ACCUMULATE. */
+int zq_dmmv_float(int wtype, const void *w, int64_t rows, int64_t k, const float *x, float *y,
+                  uint32_t flags, void *stream);
 
 /* Multi-token DMMV: the DMMV above for n_tok = 1..8 activations sharing one
  * pass over the weights: the small-M matvec ("RTX 5090: Batched Prefill &

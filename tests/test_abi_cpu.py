@@ -384,6 +384,26 @@ def test_other_argument_errors():
     assert L.zq_gemm_prefill(3, A, 64, 64, B, C, None, 8, D, 0, None) == zq.ZQ_EINVAL
 
 
+def test_float_dmmv_argument_errors():
+    L = zq.lib()
+
+    def rc(wtype=16, w=A, rows=64, k=4096, x=B, y=C, flags=0):
+        return L.zq_dmmv_float(wtype, w, rows, k, x, y, flags, None)
+
+    assert rc(wtype=4) == zq.ZQ_EINVAL
+    assert rc(k=0) == zq.ZQ_EINVAL
+    assert rc(k=4100) == zq.ZQ_EINVAL
+    assert rc(k=16384 + 8) == zq.ZQ_EINVAL
+    assert rc(rows=-1) == zq.ZQ_EINVAL
+    assert rc(flags=2) == zq.ZQ_EINVAL
+    assert rc(w=None) == zq.ZQ_ENULL
+    assert rc(x=None) == zq.ZQ_ENULL
+    assert rc(y=None) == zq.ZQ_ENULL
+    assert rc(w=A + 8) == zq.ZQ_EALIGN
+    assert rc(x=B + 4) == zq.ZQ_EALIGN
+    assert rc(y=C + 2) == zq.ZQ_EALIGN
+
+
 def test_read_probe_argument_errors():
     L = zq.lib()
     assert L.zq_read_probe(A, 24, C, None) == zq.ZQ_EINVAL
@@ -419,4 +439,6 @@ def test_valid_arguments_without_gpu_report_no_device():
                               8, None, D, A + 0x1000, A + 0x2000, A + 0x4000, ws, A + 0x8000, 0,
                               None) == zq.ZQ_EDEVICE
     assert L.zq_read_probe(A, 1 << 20, C, None) == zq.ZQ_EDEVICE
+    assert L.zq_dmmv_float(16, A, 64, 4096, B, C, 0, None) == zq.ZQ_EDEVICE
+    assert L.zq_dmmv_float(32, A, 64, 1000, B, C, 1, None) == zq.ZQ_EDEVICE
     assert zq.lib().zq_device_check(0) == zq.ZQ_EDEVICE
