@@ -51,7 +51,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", type=int, default=2, choices=list(range(1, 16)))
+    ap.add_argument("--workload", type=int, default=2, choices=list(range(1, 17)))
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle leg (no parity check, no CPU timing)")
     ap.add_argument("--no-secondary", action="store_true",
@@ -551,6 +551,107 @@ class MoeWorkload(Workload):
         return "route + one token through 8 routed + 1 shared expert (the first bank copy)"
 
 
+class MoeTokWorkload(Workload):
+    """Eight tokens, each with its own router logits, through the MoE block of
+    128 + 1 Q4_0 experts in one call (zq_moe_ffn_tokens: plan, gate/up,
+    down, weighted sums; each distinct expert's weights read once).  The
+    step's bytes are the distinct experts the step's routing touches (counted
+    from the GPU's own expert lists) plus the activations and outputs."""
+    dominant_name = "several-token MoE block (plan + gate/up + down + sum launches)"
+    step_is_dominant = True
+    steps = 1000
+    warmup = 50
+
+    def __init__(self, wl):
+        from block_quant_matrix_amd import inputs
+        cfg = inputs.WORKLOADS[wl]
+        self.wl = wl
+        self.name = cfg["name"]
+        self.E, self.top_k, self.dm, self.dff = cfg["n_routed"], cfg["top_k"], cfg["d_model"], cfg["d_ff"]
+        self.T = cfg["n_tok"]
+        self.n_sel = self.top_k + 1
+        self.expert_bytes = (2 * self.dff * (self.dm // 32) + self.dm * (self.dff // 32)) * 18
+
+    def setup(self, torch, zq, inputs):
+        self.torch, self.zq = torch, zq
+        self.ncopy = copies_for((self.E + 1) * self.expert_bytes)
+        self.banks = []
+        for c in range(self.ncopy):
+            gu, gs, down, ds = inputs.moe_banks(inputs.seed_for(self.wl, c), self.E + 1, self.dm,
+                                                self.dff)
+            self.banks.append((torch.from_numpy(gu).to("cuda"), torch.from_numpy(down).to("cuda")))
+            if c == 0:
+                self.host_bank = (gu, gs, down, ds)
+        self.gs, self.ds = gs, ds
+        self.nlog = 64
+        rng = np.random.default_rng(inputs.seed_for(self.wl, 100))
+        self.logits_host = rng.standard_normal((self.nlog, self.T, self.E)).astype(np.float32)
+        self.gates_host = rng.standard_normal((self.nlog, self.T)).astype(np.float32)
+        self.logits = torch.from_numpy(self.logits_host).to("cuda")
+        self.gates = torch.from_numpy(self.gates_host).to("cuda")
+        self.x_host = inputs.gen_activation(self.T, self.dm, inputs.seed_for(self.wl) + 7)
+        self.x = torch.from_numpy(self.x_host).to("cuda")
+        self.ids = torch.empty((self.T, self.n_sel), dtype=torch.int32, device="cuda")
+        self.wts = torch.empty((self.T, self.n_sel), dtype=torch.float32, device="cuda")
+        self.ws_bytes = zq.zq_moe_ffn_tokens_workspace_bytes(self.dm, self.dff, self.T, self.n_sel)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
+        self.y = torch.empty((self.T, self.dm), dtype=torch.float32, device="cuda")
+        # the distinct experts of each routing, from the GPU's own lists
+        distinct = []
+        for j in range(self.nlog):
+            self.step(j)
+            torch.cuda.synchronize()
+            distinct.append(len(np.unique(self.ids.cpu().numpy())))
+        self.distinct = float(np.mean(distinct))
+        self.step_bytes = (self.distinct * self.expert_bytes + 4 * self.T * self.E +
+                           8 * self.T * self.dm)
+
+    def step(self, i):
+        gu, down = self.banks[i % self.ncopy]
+        j = i % self.nlog
+        self.zq.zq_moe_ffn_tokens(4, gu, self.gs, down, self.ds, self.E + 1, self.dm, self.dff,
+                                  self.logits[j], self.E, self.top_k, self.gates[j], self.x, self.T,
+                                  self.ids, self.wts, self.ws, self.ws_bytes, self.y)
+
+    def value(self, ms):
+        return self.step_bytes / (ms * 1e-3) / 1e9, "GB/s"
+
+    def achieved(self, ms):
+        return self.step_bytes / (ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s", int(self.step_bytes)
+
+    def extra(self, ms):
+        return {"tokens_per_s": self.T / (ms * 1e-3), "us_per_token": ms * 1e3 / self.T,
+                "distinct_experts_per_step": self.distinct,
+                "expert_slots_per_step": self.T * self.n_sel}
+
+    def gpu_result(self):
+        self.y.fill_(float("nan"))
+        self.step(0)
+        self.torch.cuda.synchronize()
+        return {"y": self.y.cpu().numpy().copy(), "ids": self.ids.cpu().numpy().copy()}
+
+    def oracle_step(self):
+        import oracle
+        gu, gs, down, ds = self.host_bank
+        ys, Ss, idss = [], [], []
+        for t in range(self.T):
+            ids, wts = oracle.moe_route(self.logits_host[0, t], self.top_k, self.gates_host[0, t])
+            y, S = oracle.moe_ffn(4, gu, gs, down, ds, self.dm, self.dff, ids, wts, self.x_host[t])
+            ys.append(y)
+            Ss.append(S)
+            idss.append(ids)
+        return {"y": np.stack(ys), "S": np.stack(Ss), "ids": np.stack(idss)}
+
+    def parity(self, gpu, ref):
+        ok, worst = rows_within(gpu["y"], ref["y"], ref["S"], MOE_E2E_TOL)
+        ok = ok and np.array_equal(gpu["ids"], ref["ids"])
+        return ok, ("expert ids equal; %d tokens x %d rows within the unchained MoE bar %g*S "
+                    "(worst %.3g*S)" % (self.T, self.dm, MOE_E2E_TOL, worst))
+
+    def cpu_sample(self):
+        return "route + %d tokens through 8 routed + 1 shared expert each (first bank copy)" % self.T
+
+
 class GemmWorkload(Workload):
     dominant_name = "gemm_kernel"
     bound = "mfma"
@@ -1019,6 +1120,8 @@ def make_workload(wl):
         return MoeMixedWorkload(wl)
     if wl in (14, 15):
         return FloatDmmvWorkload(wl)
+    if wl == 16:
+        return MoeTokWorkload(wl)
     return GemmWorkload()
 
 

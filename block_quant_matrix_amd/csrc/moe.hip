@@ -21,6 +21,7 @@
 #include "zq_common.h"
 #include "zq_internal.h"
 #include "zq_kquant.h"
+#include "zq_moe_tok.h"
 
 namespace zq {
 
@@ -863,6 +864,344 @@ int launch_moe_down(int wtype, MoeDownArgs a, hipStream_t stream) {
   a.nb = static_cast<int32_t>(a.k / 32);
   a.row_bytes = static_cast<int64_t>(a.nb) * (wtype == ZQ_Q4_0 ? 18 : 34);
   return wtype == ZQ_Q4_0 ? launch_dn_w<ZQ_Q4_0>(a, stream) : launch_dn_w<ZQ_Q8_0>(a, stream);
+}
+
+// ------------------------------------------------------- several tokens ---
+// Up to kTokMax tokens, each with its own router logits (top_k routed
+// experts and an optional shared expert), through one pass over the union of
+// the experts they touch, in three launches:
+//   plan (one workgroup): route every token at once (one thread per logit
+//     ranks it among its token's logits; the weights are the router's fp64
+//     softmax, so ids and weights are those of zq_moe_route bit for bit),
+//     quantize every token's activation (the codes of zq_quantize_act), and
+//     list the distinct experts of the (token, slot) pairs in order of first
+//     use: entry u is expert plan_e[u], used by token t through the
+//     flattened slot j = t * n_sel + s (plan_slot[u][t], or -1);
+//   gate/up: a workgroup per (entry, 32-wide block of the FFN width) loads
+//     the expert's 64 gate/up rows once, stages every member token's codes in
+//     LDS, runs the 64 rows for each member, and finishes each member's
+//     SwiGLU + re-quantization on a wave of its own (the single-token stage's
+//     codes, bit for bit);
+//   down: a workgroup per 8 output rows; its 16 waves split the entries, each
+//     reads its entries' down rows once and leaves every member slot's row
+//     value in LDS; then y[t] (+)= sum_s wts[t][s] * rows[t * n_sel + s], the
+//     slots in order.
+
+// Plan layout (int32): [0] the number of entries, [1, 1 + J) plan_e,
+// [1 + J, 1 + J + kTokMax * J) plan_slot[u][kTokMax], J = n_tok * n_sel.
+__global__ __launch_bounds__(1024) void moe_tok_plan_kernel(const MoeTokArgs a) {
+  extern __shared__ __attribute__((aligned(16))) float lv[];   // [n_tok][n_pad]
+  __shared__ int32_t sel_id[kTokMax][64];
+  __shared__ float sel_v[kTokMax][64];
+  __shared__ double sel_e[kTokMax][64];
+  __shared__ int32_t jid[kTokMax * 65];      // expert of flattened slot j
+  __shared__ int32_t firstj[1025];           // per expert id: its first slot
+  __shared__ int32_t entry[kTokMax * 65];    // entry of a first use
+  const int tid = static_cast<int>(threadIdx.x);
+  if (blockIdx.x > 0) {
+    // workgroup 1 + t: token t's activation, 8 lanes per 32-element block
+    // (d_model <= 4096: at most 1024 lanes, one pass)
+    const int t = static_cast<int>(blockIdx.x) - 1;
+    const int nbx = a.d_model / 32;
+    const int b = tid >> 3, g = tid & 7;
+    if (b < nbx) {  // whole 8-lane groups
+      const int64_t o = static_cast<int64_t>(t) * a.d_model + b * 32 + g * 4;
+      const float4 v = *reinterpret_cast<const float4 *>(a.x + o);
+      const float xv[4] = {v.x, v.y, v.z, v.w};
+      float d;
+      int32_t sum;
+      const uint32_t packed = quantize_block8(xv, d, sum);
+      *reinterpret_cast<uint32_t *>(a.qx + o) = packed;
+      if (g == 0) {
+        a.dx[t * nbx + b] = d;
+        a.sx[t * nbx + b] = sum;
+      }
+    }
+    return;
+  }
+  const int n = a.n_routed, top_k = a.top_k, T = a.n_tok;
+  const int n_sel = top_k + (a.shared_gate ? 1 : 0);
+  const int J = T * n_sel;
+  const int n_pad = (n + 3) / 4 * 4;
+  int32_t *plan_e = a.plan + 1;
+  int32_t *plan_slot = a.plan + 1 + J;
+  for (int idx = tid; idx < T * n_pad; idx += 1024) {
+    const int t = idx / n_pad, i = idx - t * n_pad;
+    lv[idx] = i < n ? route_key(a.logits[static_cast<int64_t>(t) * n + i]) : -__builtin_inff();
+  }
+  for (int i = tid; i < kTokMax * J; i += 1024) plan_slot[i] = -1;
+  for (int i = tid; i <= n; i += 1024) firstj[i] = 0x7fffffff;
+  __syncthreads();
+  // rank: a logit's rank is the number of its token's logits that beat it
+  // (larger, or equal at a lower id); the -inf padding beats nothing
+  for (int idx = tid; idx < T * n; idx += 1024) {
+    const int t = idx / n, e = idx - t * n;
+    const float *row = lv + t * n_pad;
+    const float v = row[e];
+    int cnt = 0;
+    for (int j = 0; j < n_pad; j += 4) {
+      const float4 f = *reinterpret_cast<const float4 *>(row + j);
+      cnt += (f.x > v || (f.x == v && j < e)) ? 1 : 0;
+      cnt += (f.y > v || (f.y == v && j + 1 < e)) ? 1 : 0;
+      cnt += (f.z > v || (f.z == v && j + 2 < e)) ? 1 : 0;
+      cnt += (f.w > v || (f.w == v && j + 3 < e)) ? 1 : 0;
+    }
+    if (cnt < top_k) {
+      sel_id[t][cnt] = e;
+      sel_v[t][cnt] = v;
+    }
+  }
+  __syncthreads();
+  // the router's weights: softmax over the selection in fp64, the
+  // normalizer summed in rank order; the shared expert sigmoid(g)
+  for (int idx = tid; idx < T * top_k; idx += 1024) {
+    const int t = idx / top_k, r = idx - t * top_k;
+    sel_e[t][r] = exp(static_cast<double>(sel_v[t][r]) - static_cast<double>(sel_v[t][0]));
+  }
+  __syncthreads();
+  for (int idx = tid; idx < T * top_k; idx += 1024) {
+    const int t = idx / top_k, r = idx - t * top_k;
+    double z = 0.0;
+    for (int q = 0; q < top_k; ++q) z += sel_e[t][q];
+    a.ids[t * n_sel + r] = sel_id[t][r];
+    a.wts[t * n_sel + r] = static_cast<float>(sel_e[t][r] / z);
+    jid[t * n_sel + r] = sel_id[t][r];
+  }
+  if (a.shared_gate && tid < T) {
+    a.ids[tid * n_sel + top_k] = n;
+    a.wts[tid * n_sel + top_k] =
+        static_cast<float>(1.0 / (1.0 + exp(-static_cast<double>(a.shared_gate[tid]))));
+    jid[tid * n_sel + top_k] = n;
+  }
+  __syncthreads();
+  // the first slot of every expert (ids are in [0, n_routed])
+  for (int j = tid; j < J; j += 1024) atomicMin(&firstj[jid[j]], j);
+  __syncthreads();
+  // entries in order of first use: one wave counts the first uses before
+  // each slot 64 at a time
+  if (tid < 64) {
+    int before = 0;
+    for (int j0 = 0; j0 < J; j0 += 64) {
+      const int j = j0 + tid;
+      const bool f = j < J && firstj[jid[j]] == j;
+      const uint64_t m = __ballot(f);
+      if (f) {
+        const int u = before + __popcll(m & ((uint64_t(1) << tid) - 1));
+        entry[j] = u;
+        plan_e[u] = jid[j];
+      }
+      before += __popcll(m);
+    }
+    if (tid == 0) a.plan[0] = before;
+  }
+  __syncthreads();
+  // a token selects distinct experts, so (entry, token) is unique to j
+  for (int j = tid; j < J; j += 1024) plan_slot[kTokMax * entry[firstj[jid[j]]] + j / n_sel] = j;
+}
+
+// gate/up: grid (d_ff / 32, J); the workgroups past the number of entries
+// return at once.  qx / dx / sx: every token's codes from the plan.
+template <class Rows>
+__global__ __launch_bounds__(1024) void moe_gate_up_tok_kernel(const MoeGateUpArgs a,
+                                                               const int32_t *plan, int n_tok,
+                                                               const int8_t *qx, const float *dx,
+                                                               const int32_t *sx) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ int32_t mt[kTokMax], mj[kTokMax];   // member token and slot
+  const int tid = static_cast<int>(threadIdx.x);
+  const int hb = static_cast<int>(blockIdx.x);
+  const int u = static_cast<int>(blockIdx.y);
+  const int J = a.n_sel;
+  const int k = a.k, nb = a.nb;
+  if (u >= plan[0]) return;  // uniform over the workgroup
+  const int e = plan[1 + u];
+  if (e < 0 || e >= a.n_experts) {
+    if (a.status && tid == 0) *a.status = ZQ_ERANGE;
+    return;
+  }
+  Rows r;
+  r.load(a, nb, a.bank + static_cast<int64_t>(e) * a.expert_stride, a.row_bytes, hb, tid);
+  const int32_t *pslot = plan + 1 + J + kTokMax * u;
+  __shared__ int32_t raw[kTokMax];
+  if (tid < kTokMax) raw[tid] = tid < n_tok ? pslot[tid] : -1;  // one round trip
+  __syncthreads();
+  if (tid == 0) {
+    int c = 0;
+    for (int t = 0; t < kTokMax; ++t) {
+      if (raw[t] >= 0) {
+        mt[c] = t;
+        mj[c] = raw[t];
+        ++c;
+      }
+    }
+    for (; c < kTokMax; ++c) mj[c] = -1;
+  }
+  __syncthreads();
+  int c = 0;
+  while (c < kTokMax && mj[c] >= 0) ++c;  // uniform
+  // LDS: member codes [c][k], scales [c][nb], SUMX * sums [c][nb], rows [c][64]
+  int8_t *lq = reinterpret_cast<int8_t *>(smem);
+  float *ld = reinterpret_cast<float *>(smem + c * k);
+  int32_t *ls = reinterpret_cast<int32_t *>(smem + c * k + 4 * c * nb);
+  float *lrow = reinterpret_cast<float *>(smem + c * k + 8 * c * nb);
+  const int cpm = k / 16;  // 16-byte pieces of codes per member
+  for (int idx = tid; idx < c * cpm; idx += 1024) {
+    const int m = idx / cpm, p = idx - m * cpm;
+    reinterpret_cast<u32x4 *>(lq)[idx] =
+        *reinterpret_cast<const u32x4 *>(qx + static_cast<int64_t>(mt[m]) * k + 16 * p);
+  }
+  for (int idx = tid; idx < c * nb; idx += 1024) {
+    const int m = idx / nb, b = idx - m * nb;
+    ld[idx] = dx[mt[m] * nb + b];
+    ls[idx] = Rows::SUMX * sx[mt[m] * nb + b];
+  }
+  __syncthreads();
+  for (int m = 0; m < c; ++m) r.rows(nb, lq + m * k, ld + m * nb, ls + m * nb, lrow + 64 * m, tid);
+  __syncthreads();
+  const int wave = tid >> 6;
+  if (wave < c) gu_epilogue<false>(a, tid - 64 * wave, mj[wave], hb, lrow + 64 * wave, nullptr,
+                                   nullptr);
+}
+
+// down: LPR = k / 32 lanes per row (one block each), RB row steps of 64 /
+// LPR rows: 8 rows per workgroup of 16 waves; wave w takes entries w, w + 16,
+// ...  grid (rows / 8).
+template <int WT, int LPR, int RB>
+__global__ __launch_bounds__(1024) void moe_down_tok_kernel(const MoeDownTokArgs a) {
+  constexpr int S = 64 / LPR;
+  constexpr int ROWS = RB * S;
+  constexpr int NW = Blk<WT>::NW;
+  constexpr int BB = Blk<WT>::BYTES;
+  __shared__ float part[kTokMax * 65 * ROWS];   // [slot][row]
+  __shared__ int32_t lplan[1 + (1 + kTokMax) * kTokMax * 65];
+  const int tid = static_cast<int>(threadIdx.x);
+  const int lane = tid & 63, wv = tid >> 6;
+  const int jl = lane & (LPR - 1), slot = lane / LPR;
+  const int J = a.n_sel;
+  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * ROWS;
+  for (int i = tid; i < J * ROWS; i += 1024) part[i] = 0.0f;
+  for (int i = tid; i < 1 + (1 + kTokMax) * J; i += 1024) lplan[i] = a.plan[i];
+  __syncthreads();
+  const int n_union = lplan[0];
+  for (int u = wv; u < n_union; u += 16) {
+    const int e = lplan[1 + u];
+    if (e < 0 || e >= a.n_experts) {  // uniform
+      if (a.status && lane == 0) *a.status = ZQ_ERANGE;
+      continue;
+    }
+    const uint8_t *wb = a.bank + static_cast<int64_t>(e) * a.expert_stride;
+    uint32_t win[RB][NW];
+    uint32_t off[RB];
+#pragma unroll
+    for (int t2 = 0; t2 < RB; ++t2) {
+      int64_t row = row0 + t2 * S + slot;
+      row = row < a.rows ? row : a.rows - 1;
+      off[t2] = load_window<WT>(wb + row * a.row_bytes + static_cast<int64_t>(jl) * BB, win[t2]);
+    }
+    const int32_t *pslot = lplan + 1 + J + kTokMax * u;
+    for (int t = 0; t < a.n_tok; ++t) {
+      const int j = pslot[t];
+      if (j < 0) continue;  // uniform
+      const int64_t hb = static_cast<int64_t>(j) * a.nb + jl;
+      const u32x4 v0 = *reinterpret_cast<const u32x4 *>(a.qh + 32 * hb);
+      const u32x4 v1 = *reinterpret_cast<const u32x4 *>(a.qh + 32 * hb + 16);
+      const uint32_t xq[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      const float hd = a.dh[hb];
+      const int32_t hs8 = WT == ZQ_Q4_0 ? 8 * a.sh[hb] : 0;
+      float p[RB];
+#pragma unroll
+      for (int t2 = 0; t2 < RB; ++t2) {
+        const float dw = window_scale(win[t2][0], off[t2]);
+        const uint32_t sel = quant_selector(off[t2]);
+        int32_t isum;
+        if constexpr (WT == ZQ_Q4_0) {
+          isum = q4_raw_dot(win[t2], sel, xq) - hs8;
+        } else {
+          isum = q8_dot(win[t2], sel, xq);
+        }
+        p[t2] = dw * hd * static_cast<float>(isum);
+      }
+      using R = RowReduce<LPR, RB>;
+      float res[R::NOUT];
+      R::run(p, res);
+      if (R::writer(lane)) {
+#pragma unroll
+        for (int m = 0; m < R::NOUT; ++m) part[j * ROWS + R::rowstep(m, lane) * S + slot] = res[m];
+      }
+    }
+  }
+  __syncthreads();
+  const int ns = a.n_sel_tok;
+  for (int idx = tid; idx < a.n_tok * ROWS; idx += 1024) {
+    const int t = idx / ROWS, rr = idx - t * ROWS;
+    const int64_t row = row0 + rr;
+    if (row >= a.rows) continue;
+    float acc = 0.0f;
+    for (int s = 0; s < ns; ++s) acc = __builtin_fmaf(a.wts[t * ns + s], part[(t * ns + s) * ROWS + rr], acc);
+    float *yp = a.y + static_cast<int64_t>(t) * a.rows + row;
+    *yp = (a.flags & ZQ_ACCUMULATE) ? *yp + acc : acc;
+  }
+}
+
+namespace {
+
+template <class Rows>
+int launch_gu_tok(const MoeGateUpArgs &a, const MoeTokArgs &p, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>(a.d_ff / 32), static_cast<unsigned>(a.n_sel));
+  const int c = p.n_tok;  // at most this many members per entry
+  const size_t lds = static_cast<size_t>(c) * (a.k + 8 * a.nb + 64 * 4);
+  hipLaunchKernelGGL((moe_gate_up_tok_kernel<Rows>), grid, dim3(1024), lds, stream, a, p.plan,
+                     p.n_tok, p.qx, p.dx, p.sx);
+  ZQ_LAUNCH_CHECK();
+  return ZQ_OK;
+}
+
+template <int WT>
+int launch_gu_tok_w(const MoeGateUpArgs &a, const MoeTokArgs &p, hipStream_t stream) {
+  if (a.nb <= 16) return launch_gu_tok<GuBlockRows<WT, 16, 1, 1>>(a, p, stream);
+  if (a.nb <= 32) return launch_gu_tok<GuBlockRows<WT, 32, 1, 2>>(a, p, stream);
+  if (a.nb <= 64) return launch_gu_tok<GuBlockRows<WT, 64, 1, 4>>(a, p, stream);
+  return launch_gu_tok<GuBlockRows<WT, 64, 2, 4>>(a, p, stream);
+}
+
+template <int WT, int LPR, int RB>
+int launch_dn_tok(const MoeDownTokArgs &a, hipStream_t stream) {
+  constexpr int ROWS = RB * (64 / LPR);
+  const dim3 grid(static_cast<unsigned>((a.rows + ROWS - 1) / ROWS));
+  hipLaunchKernelGGL((moe_down_tok_kernel<WT, LPR, RB>), grid, dim3(1024), 0, stream, a);
+  ZQ_LAUNCH_CHECK();
+  return ZQ_OK;
+}
+
+// d_ff of 256 (8 lanes per row), 512 (16), 1024 (32) or 2048 (64 lanes): 8
+// rows per workgroup
+template <int WT>
+int launch_dn_tok_w(const MoeDownTokArgs &a, hipStream_t stream) {
+  if (a.nb == 8) return launch_dn_tok<WT, 8, 1>(a, stream);
+  if (a.nb == 16) return launch_dn_tok<WT, 16, 2>(a, stream);
+  if (a.nb == 32) return launch_dn_tok<WT, 32, 4>(a, stream);
+  return launch_dn_tok<WT, 64, 8>(a, stream);
+}
+
+}  // namespace
+
+bool moe_tok_fits(int64_t d_model, int64_t d_ff) {
+  return moe_gate_up_fits(d_model) && (d_ff == 256 || d_ff == 512 || d_ff == 1024 || d_ff == 2048);
+}
+
+int launch_moe_ffn_tok(int wtype, const MoeTokArgs &p, MoeGateUpArgs g, MoeDownTokArgs d,
+                       hipStream_t stream) {
+  const size_t lv = static_cast<size_t>(p.n_tok) * ((p.n_routed + 3) / 4 * 4) * 4;
+  hipLaunchKernelGGL(moe_tok_plan_kernel, dim3(1 + p.n_tok), dim3(1024), lv, stream, p);
+  ZQ_LAUNCH_CHECK();
+  g.nb = static_cast<int32_t>(g.k / 32);
+  g.row_bytes = static_cast<int64_t>(g.nb) * (wtype == ZQ_Q4_0 ? 18 : 34);
+  int rc = wtype == ZQ_Q4_0 ? launch_gu_tok_w<ZQ_Q4_0>(g, p, stream)
+                            : launch_gu_tok_w<ZQ_Q8_0>(g, p, stream);
+  if (rc != ZQ_OK) return rc;
+  d.nb = static_cast<int32_t>(d.k / 32);
+  d.row_bytes = static_cast<int64_t>(d.nb) * (wtype == ZQ_Q4_0 ? 18 : 34);
+  return wtype == ZQ_Q4_0 ? launch_dn_tok_w<ZQ_Q4_0>(d, stream) : launch_dn_tok_w<ZQ_Q8_0>(d, stream);
 }
 
 }  // namespace zq

@@ -7,6 +7,7 @@
 #include "zq_common.h"
 #include "zq_float.h"
 #include "zq_internal.h"
+#include "zq_moe_tok.h"
 
 namespace {
 
@@ -973,6 +974,109 @@ int moe_stage(int wtype, int mode, const void *bank, int64_t stride, int64_t n_e
 }
 
 }  // namespace
+
+namespace {
+
+struct MoeTokWorkspace {
+  size_t plan, qx, dx, sx, qh, dh, sh, total;
+};
+
+MoeTokWorkspace moe_tok_layout(int64_t d_model, int64_t d_ff, int32_t n_tok, int32_t n_sel) {
+  const size_t J = static_cast<size_t>(n_tok) * static_cast<size_t>(n_sel);
+  const size_t T = static_cast<size_t>(n_tok);
+  MoeTokWorkspace w;
+  size_t off = 0;
+  w.plan = off; off += round_up((1 + (1 + zq::kTokMax) * J) * 4);
+  w.qx = off; off += round_up(T * static_cast<size_t>(d_model));
+  w.dx = off; off += round_up(T * static_cast<size_t>(d_model / 32) * 4);
+  w.sx = off; off += round_up(T * static_cast<size_t>(d_model / 32) * 4);
+  w.qh = off; off += round_up(J * static_cast<size_t>(d_ff));
+  w.dh = off; off += round_up(J * static_cast<size_t>(d_ff / 32) * 4);
+  w.sh = off; off += round_up(J * static_cast<size_t>(d_ff / 32) * 4);
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+size_t zq_moe_ffn_tokens_workspace_bytes(int64_t d_model, int64_t d_ff, int32_t n_tok,
+                                         int32_t n_sel) {
+  if (d_model <= 0 || d_ff <= 0 || n_tok < 0 || n_sel < 0) return 0;
+  return moe_tok_layout(d_model, d_ff, n_tok, n_sel).total;
+}
+
+int zq_moe_ffn_tokens(int wtype, const void *gu_bank, int64_t gu_stride_bytes,
+                      const void *down_bank, int64_t down_stride_bytes, int64_t n_experts,
+                      int64_t d_model, int64_t d_ff, const float *logits, int32_t n_routed,
+                      int32_t top_k, const float *shared_gate, const float *x, int32_t n_tok,
+                      int32_t *ids, float *wts, void *workspace, size_t workspace_bytes, float *y,
+                      uint32_t flags, void *stream) {
+  const bool shared = shared_gate != nullptr;
+  ZQ_REQUIRE(block_bytes(wtype) > 0, ZQ_EINVAL);
+  ZQ_REQUIRE(gu_bank && down_bank && logits && x && ids && wts && workspace && y, ZQ_ENULL);
+  ZQ_REQUIRE(n_tok >= 1 && n_tok <= zq::kTokMax && top_k >= 1 && top_k <= 64 &&
+                 n_routed >= top_k && n_routed <= 1024 && n_experts >= n_routed + (shared ? 1 : 0) &&
+                 n_experts <= INT32_MAX,
+             ZQ_EINVAL);
+  ZQ_REQUIRE(k_ok(d_model) && zq::moe_tok_fits(d_model, d_ff), ZQ_EINVAL);
+  ZQ_REQUIRE(gu_stride_bytes >= matrix_bytes(wtype, 2 * d_ff, d_model) &&
+                 down_stride_bytes >= matrix_bytes(wtype, d_model, d_ff),
+             ZQ_EINVAL);
+  ZQ_REQUIRE((flags & ~uint32_t(ZQ_ACCUMULATE)) == 0, ZQ_EINVAL);
+  const int32_t n_sel = top_k + (shared ? 1 : 0);
+  const MoeTokWorkspace L = moe_tok_layout(d_model, d_ff, n_tok, n_sel);
+  ZQ_REQUIRE(workspace_bytes >= L.total, ZQ_EINVAL);
+  ZQ_REQUIRE(bank_al(wtype, gu_bank, gu_stride_bytes) &&
+                 bank_al(wtype, down_bank, down_stride_bytes) && al(logits, 4) &&
+                 al(shared_gate, 4) && al(x, 16) && al(ids, 4) && al(wts, 4) &&
+                 al(workspace, 256) && al(y, 4),
+             ZQ_EALIGN);
+  const int dc = check_current_device();
+  if (dc != ZQ_OK) return dc;
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
+  const int32_t J = n_tok * n_sel;
+  zq::MoeTokArgs p{};
+  p.logits = logits;
+  p.n_routed = n_routed;
+  p.top_k = top_k;
+  p.shared_gate = shared_gate;
+  p.n_tok = n_tok;
+  p.ids = ids;
+  p.wts = wts;
+  p.plan = reinterpret_cast<int32_t *>(ws + L.plan);
+  p.x = x;
+  p.d_model = static_cast<int32_t>(d_model);
+  p.qx = reinterpret_cast<int8_t *>(ws + L.qx);
+  p.dx = reinterpret_cast<float *>(ws + L.dx);
+  p.sx = reinterpret_cast<int32_t *>(ws + L.sx);
+  zq::MoeGateUpArgs g{};
+  g.bank = static_cast<const uint8_t *>(gu_bank);
+  g.expert_stride = gu_stride_bytes;
+  g.n_experts = static_cast<int32_t>(n_experts);
+  g.n_sel = J;
+  g.k = static_cast<int32_t>(d_model);
+  g.d_ff = static_cast<int32_t>(d_ff);
+  g.qh = reinterpret_cast<int8_t *>(ws + L.qh);
+  g.dh = reinterpret_cast<float *>(ws + L.dh);
+  g.sh = reinterpret_cast<int32_t *>(ws + L.sh);
+  zq::MoeDownTokArgs d{};
+  d.bank = static_cast<const uint8_t *>(down_bank);
+  d.expert_stride = down_stride_bytes;
+  d.n_experts = static_cast<int32_t>(n_experts);
+  d.plan = p.plan;
+  d.n_sel = J;
+  d.n_tok = n_tok;
+  d.qh = g.qh;
+  d.dh = g.dh;
+  d.sh = g.sh;
+  d.wts = wts;
+  d.n_sel_tok = n_sel;
+  d.y = y;
+  d.rows = d_model;
+  d.k = static_cast<int32_t>(d_ff);
+  d.flags = flags;
+  return zq::launch_moe_ffn_tok(wtype, p, g, d, S(stream));
+}
 
 int zq_moe_ffn_mixed(int gu_wtype, const void *gu_bank, int64_t gu_stride_bytes, int down_wtype,
                      const void *down_bank, int64_t down_stride_bytes, int sh_wtype,

@@ -156,6 +156,9 @@ WORKLOADS = {
     # the F16 member of the DMMV family: the headline shape and the LM head
     14: dict(name="f16_dmmv_4096x4096", wtype=F16, rows=4096, k=4096),
     15: dict(name="f16_lmhead_dmmv_248320x2048", wtype=F16, rows=248320, k=2048),
+    # small-M MoE: eight tokens, each with its own routing, in one call
+    16: dict(name="q4_0_moe_8tok_128e_top8_shared_2048x512", wtype=Q4_0, n_routed=128, top_k=8,
+             d_model=2048, d_ff=512, n_tok=8),
 }
 
 

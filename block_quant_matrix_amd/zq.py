@@ -67,6 +67,9 @@ SIGNATURES = {
                                 _P, _P, _P, _SZ, _P, _U32, _P]),
     "zq_moe_ffn_mixed": (_INT, [_INT, _P, _I64, _INT, _P, _I64, _INT, _P, _P, _I64, _I64, _P, _I32,
                                 _I32, _P, _P, _P, _P, _P, _SZ, _P, _U32, _P]),
+    "zq_moe_ffn_tokens_workspace_bytes": (_SZ, [_I64, _I64, _I32, _I32]),
+    "zq_moe_ffn_tokens": (_INT, [_INT, _P, _I64, _P, _I64, _I64, _I64, _I64, _P, _I32, _I32, _P, _P,
+                                 _I32, _P, _P, _P, _SZ, _P, _U32, _P]),
     "zq_gemm_prefill": (_INT, [_INT, _P, _I64, _I64, _P, _P, _P, _I64, _P, _U32, _P]),
     "zq_gemm_isums": (_INT, [_INT, _P, _I64, _I64, _P, _P, _I64, _I64, _I64, _I64, _I64, _P, _P]),
     "zq_read_probe": (_INT, [_P, _I64, _P, _P]),
@@ -283,6 +286,19 @@ def zq_moe_ffn_route(wtype, gu_bank, gu_stride, down_bank, down_stride, n_expert
     return _call("zq_moe_ffn_route", wtype, ptr(gu_bank), gu_stride, ptr(down_bank), down_stride,
                  n_experts, d_model, d_ff, ptr(logits), n_routed, top_k, ptr(shared_gate), ptr(x),
                  ptr(ids), ptr(wts), ptr(workspace), workspace_bytes, ptr(y), flags,
+                 _stream(stream))
+
+
+def zq_moe_ffn_tokens_workspace_bytes(d_model, d_ff, n_tok, n_sel) -> int:
+    return lib().zq_moe_ffn_tokens_workspace_bytes(d_model, d_ff, n_tok, n_sel)
+
+
+def zq_moe_ffn_tokens(wtype, gu_bank, gu_stride, down_bank, down_stride, n_experts, d_model, d_ff,
+                      logits, n_routed, top_k, shared_gate, x, n_tok, ids, wts, workspace,
+                      workspace_bytes, y, flags=0, stream=None):
+    return _call("zq_moe_ffn_tokens", wtype, ptr(gu_bank), gu_stride, ptr(down_bank), down_stride,
+                 n_experts, d_model, d_ff, ptr(logits), n_routed, top_k, ptr(shared_gate), ptr(x),
+                 n_tok, ptr(ids), ptr(wts), ptr(workspace), workspace_bytes, ptr(y), flags,
                  _stream(stream))
 
 

@@ -406,6 +406,39 @@ int zq_moe_ffn_mixed(int gu_wtype, const void *gu_bank, int64_t gu_stride_bytes,
                      void *workspace, size_t workspace_bytes, float *y, uint32_t flags,
                      void *stream);
 
+/* The MoE block of 1..8 tokens at once, each with its own router logits,
+ * through one pass over the union of the experts they touch: the multi-row
+ * expert kernel for the small-M matvecs of "RTX 5090: Batched Prefill & CUDA
+ * Graphs in ZINC", section "What's next", with the expert list kept on the
+ * GPU (same page, section "Prefill -- a correction, and a better GEMM").
+ * For every token t it computes what zq_moe_ffn_route computes for that
+ * token alone: the router of zq_moe_route on logits[t] (ids[t], wts[t]:
+ * top_k (+1) entries each, the shared expert id n_routed with weight
+ * sigmoid(shared_gate[t]) when shared_gate is non-NULL), then
+ *   y[t] (+)= sum_s wts[t][s] * down_{ids[t][s]}(Q(swiglu(gate||up_{ids[t][s]}(Q(x[t]))))),
+ * the gate/up codes and scales bit for bit those of the single-token stages,
+ * the weighted sum taken over the slots in order.  Three launches: a plan
+ * (every token's routing and quantized activation, and the list of distinct
+ * experts), gate/up (each distinct expert's rows read once for all tokens
+ * that selected it), and down with the per-token weighted sums (the same).
+ * wtype ZQ_Q4_0 or ZQ_Q8_0; banks as zq_moe_ffn (n_experts >= n_routed + 1
+ * with a shared expert); d_model a multiple of 32 up to 4096; d_ff 256, 512,
+ * 1024 or 2048.  logits [n_tok][n_routed]; shared_gate [n_tok] or NULL;
+ * x [n_tok][d_model] fp32 (16-byte aligned); ids [n_tok][n_sel], wts
+ * [n_tok][n_sel] receive the router's output (n_sel = top_k (+1)); y
+ * [n_tok][d_model] (may be x itself: x is read only by launches before y is
+ * written).  workspace >= zq_moe_ffn_tokens_workspace_bytes(d_model, d_ff,
+ * n_tok, n_sel) bytes, 256-byte aligned.  1 <= n_tok <= 8, 1 <= top_k <= 64,
+ * top_k <= n_routed <= 1024; flags 0 or ZQ_ACCUMULATE. */
+size_t zq_moe_ffn_tokens_workspace_bytes(int64_t d_model, int64_t d_ff, int32_t n_tok,
+                                         int32_t n_sel);
+int zq_moe_ffn_tokens(int wtype, const void *gu_bank, int64_t gu_stride_bytes,
+                      const void *down_bank, int64_t down_stride_bytes, int64_t n_experts,
+                      int64_t d_model, int64_t d_ff, const float *logits, int32_t n_routed,
+                      int32_t top_k, const float *shared_gate, const float *x, int32_t n_tok,
+                      int32_t *ids, float *wts, void *workspace, size_t workspace_bytes, float *y,
+                      uint32_t flags, void *stream);
+
 /* Batched prefill GEMM (all prompt tokens through one tiled GEMM rather than
  * one matvec per token: "RTX 5090: Batched Prefill & CUDA Graphs in ZINC", opening answer
  * and section "Prefill -- a correction, and a better GEMM"; the dequant is

@@ -384,6 +384,40 @@ def test_other_argument_errors():
     assert L.zq_gemm_prefill(3, A, 64, 64, B, C, None, 8, D, 0, None) == zq.ZQ_EINVAL
 
 
+def test_moe_ffn_tokens_argument_errors():
+    L = zq.lib()
+    ws = L.zq_moe_ffn_tokens_workspace_bytes(2048, 512, 8, 9)
+    assert ws % 256 == 0 and ws >= 8 * 2048 + 72 * 512
+    assert L.zq_moe_ffn_tokens_workspace_bytes(2048, 512, -1, 9) == 0
+    gs, ds = 2 * 512 * 64 * 18, 2048 * 16 * 18
+
+    def rc(wtype=4, n_experts=129, d_model=2048, d_ff=512, logits=B, n_routed=128, top_k=8,
+           g=C, x=D, n_tok=8, ids=A + 0x1000, wts=A + 0x2000, work=A + 0x4000, wsb=ws,
+           y=A + 0x8000, flags=0, gs=gs):
+        return L.zq_moe_ffn_tokens(wtype, A, gs, B, ds, n_experts, d_model, d_ff, logits,
+                                   n_routed, top_k, g, x, n_tok, ids, wts, work, wsb, y, flags,
+                                   None)
+
+    assert rc(wtype=12) == zq.ZQ_EINVAL
+    assert rc(n_tok=0) == zq.ZQ_EINVAL
+    assert rc(n_tok=9) == zq.ZQ_EINVAL
+    assert rc(top_k=65, n_routed=128) == zq.ZQ_EINVAL
+    assert rc(n_routed=1025, n_experts=1026) == zq.ZQ_EINVAL
+    assert rc(n_routed=7) == zq.ZQ_EINVAL              # fewer than top_k
+    assert rc(n_experts=128) == zq.ZQ_EINVAL           # no room for the shared expert
+    assert rc(d_ff=768) == zq.ZQ_EINVAL                # d_ff outside 256 / 512 / 1024 / 2048
+    assert rc(d_model=2047) == zq.ZQ_EINVAL
+    assert rc(gs=gs - 18) == zq.ZQ_EINVAL              # expert stride shorter than an expert
+    assert rc(flags=2) == zq.ZQ_EINVAL
+    assert rc(wsb=ws - 1) == zq.ZQ_EINVAL
+    assert rc(logits=None) == zq.ZQ_ENULL
+    assert rc(work=None) == zq.ZQ_ENULL
+    assert rc(x=D + 4) == zq.ZQ_EALIGN
+    assert rc(work=A + 0x4010) == zq.ZQ_EALIGN
+    if not os.path.exists("/dev/kfd"):
+        assert rc(g=None, n_experts=128) == zq.ZQ_EDEVICE   # valid: the device check is last
+
+
 def test_float_dmmv_argument_errors():
     L = zq.lib()
 
