@@ -870,38 +870,36 @@ int launch_moe_down(int wtype, MoeDownArgs a, hipStream_t stream) {
 // Up to kTokMax tokens, each with its own router logits (top_k routed
 // experts and an optional shared expert), through one pass over the union of
 // the experts they touch, in three launches:
-//   plan (one workgroup): route every token at once (one thread per logit
-//     ranks it among its token's logits; the weights are the router's fp64
-//     softmax, so ids and weights are those of zq_moe_route bit for bit),
-//     quantize every token's activation (the codes of zq_quantize_act), and
-//     list the distinct experts of the (token, slot) pairs in order of first
-//     use: entry u is expert plan_e[u], used by token t through the
-//     flattened slot j = t * n_sel + s (plan_slot[u][t], or -1);
-//   gate/up: a workgroup per (entry, 32-wide block of the FFN width) loads
-//     the expert's 64 gate/up rows once, stages every member token's codes in
-//     LDS, runs the 64 rows for each member, and finishes each member's
-//     SwiGLU + re-quantization on a wave of its own (the single-token stage's
-//     codes, bit for bit);
-//   down: a workgroup per 8 output rows; its 16 waves split the entries, each
-//     reads its entries' down rows once and leaves every member slot's row
-//     value in LDS; then y[t] (+)= sum_s wts[t][s] * rows[t * n_sel + s], the
-//     slots in order.
+//   route: a workgroup per token runs the single-token router on its logits
+//     (rank selection and fp64 softmax, so ids and weights are those of
+//     zq_moe_route bit for bit), and another per token quantizes its
+//     activation (the codes of zq_quantize_act);
+//   gate/up: a workgroup per (flattened slot j = t * n_sel + s, 32-wide block
+//     of the FFN width) reads every token's expert ids; unless an earlier
+//     slot holds the same expert it loads the expert's 64 gate/up rows once,
+//     stages the codes of every token that selected that expert (its
+//     members) in LDS, runs the 64 rows for each member, and finishes each
+//     member's SwiGLU + re-quantization on a wave of its own (the
+//     single-token stage's codes, bit for bit).  The workgroups of block 0
+//     record every slot's members for the down pass (none for a slot whose
+//     expert an earlier slot holds);
+//   down: a workgroup per 8 output rows lists the first-use slots (the
+//     distinct experts), requests the first ones' down rows, stages every
+//     slot's hidden codes in LDS (when they fit), and its 16 waves take the
+//     experts (the first 16 in order, the rest claimed from an LDS counter
+//     so that a wave slowed by an expert with many members takes fewer),
+//     each reading its experts' down rows once (the next one's requested
+//     before the current one's members are computed) and leaving every
+//     member slot's row value in LDS; then
+//     y[t] (+)= sum_s wts[t][s] * rows[t * n_sel + s], the slots in order.
 
-// Plan layout (int32): [0] the number of entries, [1, 1 + J) plan_e,
-// [1 + J, 1 + J + kTokMax * J) plan_slot[u][kTokMax], J = n_tok * n_sel.
-__global__ __launch_bounds__(1024) void moe_tok_plan_kernel(const MoeTokArgs a) {
-  extern __shared__ __attribute__((aligned(16))) float lv[];   // [n_tok][n_pad]
-  __shared__ int32_t sel_id[kTokMax][64];
-  __shared__ float sel_v[kTokMax][64];
-  __shared__ double sel_e[kTokMax][64];
-  __shared__ int32_t jid[kTokMax * 65];      // expert of flattened slot j
-  __shared__ int32_t firstj[1025];           // per expert id: its first slot
-  __shared__ int32_t entry[kTokMax * 65];    // entry of a first use
+// Route (blockIdx.y 0) and quantize (blockIdx.y 1) token blockIdx.x.
+template <int P>
+__global__ __launch_bounds__(1024) void moe_tok_route_kernel(const MoeTokArgs a) {
+  const int t = static_cast<int>(blockIdx.x);
   const int tid = static_cast<int>(threadIdx.x);
-  if (blockIdx.x > 0) {
-    // workgroup 1 + t: token t's activation, 8 lanes per 32-element block
-    // (d_model <= 4096: at most 1024 lanes, one pass)
-    const int t = static_cast<int>(blockIdx.x) - 1;
+  if (blockIdx.y == 1) {
+    // 8 lanes per 32-element block (d_model <= 4096: one pass)
     const int nbx = a.d_model / 32;
     const int b = tid >> 3, g = tid & 7;
     if (b < nbx) {  // whole 8-lane groups
@@ -919,126 +917,74 @@ __global__ __launch_bounds__(1024) void moe_tok_plan_kernel(const MoeTokArgs a) 
     }
     return;
   }
-  const int n = a.n_routed, top_k = a.top_k, T = a.n_tok;
-  const int n_sel = top_k + (a.shared_gate ? 1 : 0);
-  const int J = T * n_sel;
-  const int n_pad = (n + 3) / 4 * 4;
-  int32_t *plan_e = a.plan + 1;
-  int32_t *plan_slot = a.plan + 1 + J;
-  for (int idx = tid; idx < T * n_pad; idx += 1024) {
-    const int t = idx / n_pad, i = idx - t * n_pad;
-    lv[idx] = i < n ? route_key(a.logits[static_cast<int64_t>(t) * n + i]) : -__builtin_inff();
-  }
-  for (int i = tid; i < kTokMax * J; i += 1024) plan_slot[i] = -1;
-  for (int i = tid; i <= n; i += 1024) firstj[i] = 0x7fffffff;
+  __shared__ __attribute__((aligned(16))) float lv[1024];
+  __shared__ int32_t sel_id[64];
+  __shared__ float sel_v[64];
+  __shared__ double sel_e[64];
+  const int n = a.n_routed;
+  const int n_sel = a.top_k + (a.shared_gate ? 1 : 0);
+  const int n_pad = route_stage<P, 1024>(lv, a.logits + static_cast<int64_t>(t) * n, n);
   __syncthreads();
-  // rank: a logit's rank is the number of its token's logits that beat it
-  // (larger, or equal at a lower id); the -inf padding beats nothing
-  for (int idx = tid; idx < T * n; idx += 1024) {
-    const int t = idx / n, e = idx - t * n;
-    const float *row = lv + t * n_pad;
-    const float v = row[e];
-    int cnt = 0;
-    for (int j = 0; j < n_pad; j += 4) {
-      const float4 f = *reinterpret_cast<const float4 *>(row + j);
-      cnt += (f.x > v || (f.x == v && j < e)) ? 1 : 0;
-      cnt += (f.y > v || (f.y == v && j + 1 < e)) ? 1 : 0;
-      cnt += (f.z > v || (f.z == v && j + 2 < e)) ? 1 : 0;
-      cnt += (f.w > v || (f.w == v && j + 3 < e)) ? 1 : 0;
-    }
-    if (cnt < top_k) {
-      sel_id[t][cnt] = e;
-      sel_v[t][cnt] = v;
-    }
-  }
+  route_rank<P, 1024>(lv, n, n_pad, a.top_k, sel_id, sel_v);
   __syncthreads();
-  // the router's weights: softmax over the selection in fp64, the
-  // normalizer summed in rank order; the shared expert sigmoid(g)
-  for (int idx = tid; idx < T * top_k; idx += 1024) {
-    const int t = idx / top_k, r = idx - t * top_k;
-    sel_e[t][r] = exp(static_cast<double>(sel_v[t][r]) - static_cast<double>(sel_v[t][0]));
-  }
-  __syncthreads();
-  for (int idx = tid; idx < T * top_k; idx += 1024) {
-    const int t = idx / top_k, r = idx - t * top_k;
-    double z = 0.0;
-    for (int q = 0; q < top_k; ++q) z += sel_e[t][q];
-    a.ids[t * n_sel + r] = sel_id[t][r];
-    a.wts[t * n_sel + r] = static_cast<float>(sel_e[t][r] / z);
-    jid[t * n_sel + r] = sel_id[t][r];
-  }
-  if (a.shared_gate && tid < T) {
-    a.ids[tid * n_sel + top_k] = n;
-    a.wts[tid * n_sel + top_k] =
-        static_cast<float>(1.0 / (1.0 + exp(-static_cast<double>(a.shared_gate[tid]))));
-    jid[tid * n_sel + top_k] = n;
-  }
-  __syncthreads();
-  // the first slot of every expert (ids are in [0, n_routed])
-  for (int j = tid; j < J; j += 1024) atomicMin(&firstj[jid[j]], j);
-  __syncthreads();
-  // entries in order of first use: one wave counts the first uses before
-  // each slot 64 at a time
-  if (tid < 64) {
-    int before = 0;
-    for (int j0 = 0; j0 < J; j0 += 64) {
-      const int j = j0 + tid;
-      const bool f = j < J && firstj[jid[j]] == j;
-      const uint64_t m = __ballot(f);
-      if (f) {
-        const int u = before + __popcll(m & ((uint64_t(1) << tid) - 1));
-        entry[j] = u;
-        plan_e[u] = jid[j];
-      }
-      before += __popcll(m);
-    }
-    if (tid == 0) a.plan[0] = before;
-  }
-  __syncthreads();
-  // a token selects distinct experts, so (entry, token) is unique to j
-  for (int j = tid; j < J; j += 1024) plan_slot[kTokMax * entry[firstj[jid[j]]] + j / n_sel] = j;
+  route_weights(sel_id, sel_v, sel_e, n, a.top_k, a.shared_gate ? a.shared_gate + t : nullptr,
+                a.ids + t * n_sel, a.wts + t * n_sel);
 }
 
-// gate/up: grid (d_ff / 32, J); the workgroups past the number of entries
-// return at once.  qx / dx / sx: every token's codes from the plan.
+// gate/up: grid (d_ff / 32, J).  a.ids: every token's expert ids [J];
+// mem: the member table [J][kTokMax] (written by the workgroups of block
+// 0): the member slots of first-use slot j in token order, then -1; all -1
+// for a slot that is not a first use.
 template <class Rows>
-__global__ __launch_bounds__(1024) void moe_gate_up_tok_kernel(const MoeGateUpArgs a,
-                                                               const int32_t *plan, int n_tok,
+__global__ __launch_bounds__(1024) void moe_gate_up_tok_kernel(const MoeGateUpArgs a, int32_t *mem,
+                                                               int n_tok, int n_sel_tok,
                                                                const int8_t *qx, const float *dx,
                                                                const int32_t *sx) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  __shared__ int32_t mt[kTokMax], mj[kTokMax];   // member token and slot
+  __shared__ int32_t lid[kTokMax * 65];
+  __shared__ int32_t mslot[kTokMax];
+  __shared__ int32_t mt[kTokMax], mj[kTokMax];   // member token and slot, compacted
+  __shared__ int32_t dup, n_mem;
   const int tid = static_cast<int>(threadIdx.x);
   const int hb = static_cast<int>(blockIdx.x);
-  const int u = static_cast<int>(blockIdx.y);
-  const int J = a.n_sel;
+  const int j = static_cast<int>(blockIdx.y);
+  const int J = a.n_sel;  // <= kTokMax * 65 < 1024
   const int k = a.k, nb = a.nb;
-  if (u >= plan[0]) return;  // uniform over the workgroup
-  const int e = plan[1 + u];
-  if (e < 0 || e >= a.n_experts) {
+  if (tid < J) lid[tid] = a.ids[tid];
+  if (tid < kTokMax) mslot[tid] = -1;
+  if (tid == 0) dup = 0;
+  __syncthreads();
+  const int e = lid[j];
+  // an earlier slot with the same expert makes this one a duplicate; a token
+  // selects distinct experts, so each token holds e in at most one slot
+  if (tid < J && lid[tid] == e) {
+    if (tid < j) dup = 1;
+    mslot[tid / n_sel_tok] = tid;
+  }
+  __syncthreads();
+  const bool bad = e < 0 || e >= a.n_experts;
+  if (tid < 64) {  // the members in token order; block 0 records them for the down pass
+    const int v = tid < kTokMax && !dup && !bad ? mslot[tid] : -1;
+    const uint64_t m = __ballot(v >= 0);
+    const int cnt = __popcll(m);
+    if (v >= 0) {
+      const int pos = __popcll(m & ((uint64_t(1) << tid) - 1));
+      mt[pos] = tid;
+      mj[pos] = v;
+      if (hb == 0) mem[kTokMax * j + pos] = v;
+    }
+    if (hb == 0 && tid >= cnt && tid < kTokMax) mem[kTokMax * j + tid] = -1;
+    if (tid == 0) n_mem = cnt;
+  }
+  if (dup) return;  // uniform over the workgroup
+  if (bad) {
     if (a.status && tid == 0) *a.status = ZQ_ERANGE;
     return;
   }
   Rows r;
   r.load(a, nb, a.bank + static_cast<int64_t>(e) * a.expert_stride, a.row_bytes, hb, tid);
-  const int32_t *pslot = plan + 1 + J + kTokMax * u;
-  __shared__ int32_t raw[kTokMax];
-  if (tid < kTokMax) raw[tid] = tid < n_tok ? pslot[tid] : -1;  // one round trip
   __syncthreads();
-  if (tid == 0) {
-    int c = 0;
-    for (int t = 0; t < kTokMax; ++t) {
-      if (raw[t] >= 0) {
-        mt[c] = t;
-        mj[c] = raw[t];
-        ++c;
-      }
-    }
-    for (; c < kTokMax; ++c) mj[c] = -1;
-  }
-  __syncthreads();
-  int c = 0;
-  while (c < kTokMax && mj[c] >= 0) ++c;  // uniform
+  const int c = n_mem;
   // LDS: member codes [c][k], scales [c][nb], SUMX * sums [c][nb], rows [c][64]
   int8_t *lq = reinterpret_cast<int8_t *>(smem);
   float *ld = reinterpret_cast<float *>(smem + c * k);
@@ -1063,61 +1009,123 @@ __global__ __launch_bounds__(1024) void moe_gate_up_tok_kernel(const MoeGateUpAr
                                    nullptr);
 }
 
+// The LDS of a down workgroup (byte offsets), with the hidden codes staged
+// when STAGE.
+struct DnTokLds {
+  int part, mem, ent, lid, wts, q, d, s, total;
+  __host__ __device__ DnTokLds(int J, int k, int rows, bool stage) {
+    const int nb = k / 32;
+    part = 0;
+    mem = part + 4 * J * rows;
+    ent = mem + 4 * kTokMax * J;
+    lid = ent + 4 * J;
+    wts = lid + 4 * J;
+    q = (wts + 4 * J + 15) / 16 * 16;
+    d = q + (stage ? J * k : 0);
+    s = d + (stage ? 4 * J * nb : 0);
+    total = s + (stage ? 4 * J * nb : 0);
+  }
+};
+
+constexpr int kDnTokLdsMax = 60 * 1024;
+
 // down: LPR = k / 32 lanes per row (one block each), RB row steps of 64 /
-// LPR rows: 8 rows per workgroup of 16 waves; wave w takes entries w, w + 16,
-// ...  grid (rows / 8).
-template <int WT, int LPR, int RB>
+// LPR rows: 8 rows per workgroup of 16 waves.  grid (rows / 8).
+template <int WT, int LPR, int RB, bool STAGE>
 __global__ __launch_bounds__(1024) void moe_down_tok_kernel(const MoeDownTokArgs a) {
   constexpr int S = 64 / LPR;
   constexpr int ROWS = RB * S;
   constexpr int NW = Blk<WT>::NW;
   constexpr int BB = Blk<WT>::BYTES;
-  __shared__ float part[kTokMax * 65 * ROWS];   // [slot][row]
-  __shared__ int32_t lplan[1 + (1 + kTokMax) * kTokMax * 65];
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ int32_t n_ent, dctr;
   const int tid = static_cast<int>(threadIdx.x);
   const int lane = tid & 63, wv = tid >> 6;
   const int jl = lane & (LPR - 1), slot = lane / LPR;
-  const int J = a.n_sel;
+  const int J = a.n_sel, k = a.k, nb = a.nb;
+  const DnTokLds L(J, k, ROWS, STAGE);
+  float *part = reinterpret_cast<float *>(smem + L.part);
+  int32_t *mem = reinterpret_cast<int32_t *>(smem + L.mem);
+  int32_t *ent = reinterpret_cast<int32_t *>(smem + L.ent);
+  int32_t *lid = reinterpret_cast<int32_t *>(smem + L.lid);
+  float *lw = reinterpret_cast<float *>(smem + L.wts);
   const int64_t row0 = static_cast<int64_t>(blockIdx.x) * ROWS;
+  for (int i = tid; i < kTokMax * J; i += 1024) mem[i] = a.mem[i];
+  for (int i = tid; i < J; i += 1024) {
+    lid[i] = a.ids[i];
+    lw[i] = a.wts[i];
+  }
   for (int i = tid; i < J * ROWS; i += 1024) part[i] = 0.0f;
-  for (int i = tid; i < 1 + (1 + kTokMax) * J; i += 1024) lplan[i] = a.plan[i];
+  if (tid == 0) dctr = 0;
   __syncthreads();
-  const int n_union = lplan[0];
-  for (int u = wv; u < n_union; u += 16) {
-    const int e = lplan[1 + u];
-    if (e < 0 || e >= a.n_experts) {  // uniform
-      if (a.status && lane == 0) *a.status = ZQ_ERANGE;
-      continue;
+  // the first-use slots in order: the slots whose member row is not empty
+  if (tid < 64) {
+    int before = 0;
+    for (int j0 = 0; j0 < J; j0 += 64) {
+      const int j = j0 + tid;
+      const bool f = j < J && mem[kTokMax * j] >= 0;
+      const uint64_t m = __ballot(f);
+      if (f) ent[before + __popcll(m & ((uint64_t(1) << tid) - 1))] = j;
+      before += __popcll(m);
     }
+    if (tid == 0) n_ent = before;
+  }
+  __syncthreads();
+  const int ne = n_ent;
+
+  constexpr int NBUF = RB > 4 ? 1 : 2;
+  uint32_t win[NBUF][RB][NW];
+  uint32_t off[NBUF][RB];
+  auto load = [&](int u, int buf) {
+    u = u < ne ? u : ne - 1;  // past the last entry: the last one again
+    int e = lid[ent[u]];
+    e = e < 0 ? 0 : (e >= a.n_experts ? a.n_experts - 1 : e);  // reported below
     const uint8_t *wb = a.bank + static_cast<int64_t>(e) * a.expert_stride;
-    uint32_t win[RB][NW];
-    uint32_t off[RB];
 #pragma unroll
     for (int t2 = 0; t2 < RB; ++t2) {
       int64_t row = row0 + t2 * S + slot;
       row = row < a.rows ? row : a.rows - 1;
-      off[t2] = load_window<WT>(wb + row * a.row_bytes + static_cast<int64_t>(jl) * BB, win[t2]);
+      off[buf][t2] = load_window<WT>(wb + row * a.row_bytes + static_cast<int64_t>(jl) * BB,
+                                     win[buf][t2]);
     }
-    const int32_t *pslot = lplan + 1 + J + kTokMax * u;
-    for (int t = 0; t < a.n_tok; ++t) {
-      const int j = pslot[t];
-      if (j < 0) continue;  // uniform
-      const int64_t hb = static_cast<int64_t>(j) * a.nb + jl;
-      const u32x4 v0 = *reinterpret_cast<const u32x4 *>(a.qh + 32 * hb);
-      const u32x4 v1 = *reinterpret_cast<const u32x4 *>(a.qh + 32 * hb + 16);
+  };
+  auto run = [&](int u, int buf) {
+    const int j = ent[u];
+    const int e = lid[j];
+    if (e < 0 || e >= a.n_experts) {  // uniform
+      if (a.status && lane == 0) *a.status = ZQ_ERANGE;
+      return;
+    }
+    for (int m = 0; m < kTokMax; ++m) {
+      const int js = mem[kTokMax * j + m];
+      if (js < 0) break;  // uniform
+      const int hb = js * nb + jl;
+      u32x4 v0, v1;
+      float hd;
+      int32_t hsum;
+      if constexpr (STAGE) {
+        v0 = *reinterpret_cast<const u32x4 *>(smem + L.q + 32 * hb);
+        v1 = *reinterpret_cast<const u32x4 *>(smem + L.q + 32 * hb + 16);
+        hd = reinterpret_cast<const float *>(smem + L.d)[hb];
+        hsum = reinterpret_cast<const int32_t *>(smem + L.s)[hb];
+      } else {
+        v0 = *reinterpret_cast<const u32x4 *>(a.qh + 32 * static_cast<int64_t>(hb));
+        v1 = *reinterpret_cast<const u32x4 *>(a.qh + 32 * static_cast<int64_t>(hb) + 16);
+        hd = a.dh[hb];
+        hsum = a.sh[hb];
+      }
       const uint32_t xq[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-      const float hd = a.dh[hb];
-      const int32_t hs8 = WT == ZQ_Q4_0 ? 8 * a.sh[hb] : 0;
+      const int32_t hs8 = WT == ZQ_Q4_0 ? 8 * hsum : 0;
       float p[RB];
 #pragma unroll
       for (int t2 = 0; t2 < RB; ++t2) {
-        const float dw = window_scale(win[t2][0], off[t2]);
-        const uint32_t sel = quant_selector(off[t2]);
+        const float dw = window_scale(win[buf][t2][0], off[buf][t2]);
+        const uint32_t sel = quant_selector(off[buf][t2]);
         int32_t isum;
         if constexpr (WT == ZQ_Q4_0) {
-          isum = q4_raw_dot(win[t2], sel, xq) - hs8;
+          isum = q4_raw_dot(win[buf][t2], sel, xq) - hs8;
         } else {
-          isum = q8_dot(win[t2], sel, xq);
+          isum = q8_dot(win[buf][t2], sel, xq);
         }
         p[t2] = dw * hd * static_cast<float>(isum);
       }
@@ -1126,8 +1134,56 @@ __global__ __launch_bounds__(1024) void moe_down_tok_kernel(const MoeDownTokArgs
       R::run(p, res);
       if (R::writer(lane)) {
 #pragma unroll
-        for (int m = 0; m < R::NOUT; ++m) part[j * ROWS + R::rowstep(m, lane) * S + slot] = res[m];
+        for (int m = 0; m < R::NOUT; ++m) part[js * ROWS + R::rowstep(m, lane) * S + slot] = res[m];
       }
+    }
+  };
+  // the first entries' rows are requested before the hidden codes are
+  // staged (with two window sets)
+  // entries past a wave's first are claimed from an LDS counter, so that a
+  // wave slowed by an expert with many members takes fewer entries
+  auto claim = [&]() {
+    int c = 0;
+    if (lane == 0) c = atomicAdd(&dctr, 1);
+    return 16 + __shfl(c, 0);
+  };
+  int u = wv, un = 0;
+  if constexpr (NBUF == 2) {
+    if (wv < ne) {
+      un = claim();
+      load(u, 0);
+      load(un, 1);
+    }
+  }
+  if constexpr (STAGE) {
+    const int pieces = J * k / 16;
+    for (int i = tid; i < pieces; i += 1024)
+      reinterpret_cast<u32x4 *>(smem + L.q)[i] = reinterpret_cast<const u32x4 *>(a.qh)[i];
+    for (int i = tid; i < J * nb; i += 1024) {
+      reinterpret_cast<float *>(smem + L.d)[i] = a.dh[i];
+      reinterpret_cast<int32_t *>(smem + L.s)[i] = a.sh[i];
+    }
+    __syncthreads();
+  }
+  // two window sets (up to 4 row steps): entry u + 16 is requested before
+  // entry u is computed; 8 row steps keep one set, within the registers
+  if constexpr (RB > 4) {
+    while (u < ne) {
+      load(u, 0);
+      run(u, 0);
+      u = claim();
+    }
+  } else if (wv < ne) {
+    // buffer 0 holds entry u, buffer 1 entry un
+    for (;;) {
+      run(u, 0);
+      if (un >= ne) break;
+      u = claim();
+      load(u, 0);
+      run(un, 1);
+      if (u >= ne) break;
+      un = claim();
+      load(un, 1);
     }
   }
   __syncthreads();
@@ -1137,7 +1193,7 @@ __global__ __launch_bounds__(1024) void moe_down_tok_kernel(const MoeDownTokArgs
     const int64_t row = row0 + rr;
     if (row >= a.rows) continue;
     float acc = 0.0f;
-    for (int s = 0; s < ns; ++s) acc = __builtin_fmaf(a.wts[t * ns + s], part[(t * ns + s) * ROWS + rr], acc);
+    for (int s = 0; s < ns; ++s) acc = __builtin_fmaf(lw[t * ns + s], part[(t * ns + s) * ROWS + rr], acc);
     float *yp = a.y + static_cast<int64_t>(t) * a.rows + row;
     *yp = (a.flags & ZQ_ACCUMULATE) ? *yp + acc : acc;
   }
@@ -1145,30 +1201,46 @@ __global__ __launch_bounds__(1024) void moe_down_tok_kernel(const MoeDownTokArgs
 
 namespace {
 
+template <int P>
+void launch_tok_route(const MoeTokArgs &p, hipStream_t stream) {
+  hipLaunchKernelGGL((moe_tok_route_kernel<P>), dim3(static_cast<unsigned>(p.n_tok), 2),
+                     dim3(1024), 0, stream, p);
+}
+
 template <class Rows>
-int launch_gu_tok(const MoeGateUpArgs &a, const MoeTokArgs &p, hipStream_t stream) {
+int launch_gu_tok(const MoeGateUpArgs &a, int32_t *mem, const MoeTokArgs &p, int n_sel_tok,
+                  hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(a.d_ff / 32), static_cast<unsigned>(a.n_sel));
-  const int c = p.n_tok;  // at most this many members per entry
+  const int c = p.n_tok;  // at most this many members per expert
   const size_t lds = static_cast<size_t>(c) * (a.k + 8 * a.nb + 64 * 4);
-  hipLaunchKernelGGL((moe_gate_up_tok_kernel<Rows>), grid, dim3(1024), lds, stream, a, p.plan,
-                     p.n_tok, p.qx, p.dx, p.sx);
+  hipLaunchKernelGGL((moe_gate_up_tok_kernel<Rows>), grid, dim3(1024), lds, stream, a, mem,
+                     p.n_tok, n_sel_tok, p.qx, p.dx, p.sx);
   ZQ_LAUNCH_CHECK();
   return ZQ_OK;
 }
 
 template <int WT>
-int launch_gu_tok_w(const MoeGateUpArgs &a, const MoeTokArgs &p, hipStream_t stream) {
-  if (a.nb <= 16) return launch_gu_tok<GuBlockRows<WT, 16, 1, 1>>(a, p, stream);
-  if (a.nb <= 32) return launch_gu_tok<GuBlockRows<WT, 32, 1, 2>>(a, p, stream);
-  if (a.nb <= 64) return launch_gu_tok<GuBlockRows<WT, 64, 1, 4>>(a, p, stream);
-  return launch_gu_tok<GuBlockRows<WT, 64, 2, 4>>(a, p, stream);
+int launch_gu_tok_w(const MoeGateUpArgs &a, int32_t *mem, const MoeTokArgs &p, int n_sel_tok,
+                    hipStream_t stream) {
+  if (a.nb <= 16) return launch_gu_tok<GuBlockRows<WT, 16, 1, 1>>(a, mem, p, n_sel_tok, stream);
+  if (a.nb <= 32) return launch_gu_tok<GuBlockRows<WT, 32, 1, 2>>(a, mem, p, n_sel_tok, stream);
+  if (a.nb <= 64) return launch_gu_tok<GuBlockRows<WT, 64, 1, 4>>(a, mem, p, n_sel_tok, stream);
+  return launch_gu_tok<GuBlockRows<WT, 64, 2, 4>>(a, mem, p, n_sel_tok, stream);
 }
 
 template <int WT, int LPR, int RB>
 int launch_dn_tok(const MoeDownTokArgs &a, hipStream_t stream) {
   constexpr int ROWS = RB * (64 / LPR);
   const dim3 grid(static_cast<unsigned>((a.rows + ROWS - 1) / ROWS));
-  hipLaunchKernelGGL((moe_down_tok_kernel<WT, LPR, RB>), grid, dim3(1024), 0, stream, a);
+  const DnTokLds staged(a.n_sel, a.k, ROWS, true);
+  if (staged.total <= kDnTokLdsMax) {
+    hipLaunchKernelGGL((moe_down_tok_kernel<WT, LPR, RB, true>), grid, dim3(1024),
+                       static_cast<size_t>(staged.total), stream, a);
+  } else {
+    const DnTokLds plain(a.n_sel, a.k, ROWS, false);
+    hipLaunchKernelGGL((moe_down_tok_kernel<WT, LPR, RB, false>), grid, dim3(1024),
+                       static_cast<size_t>(plain.total), stream, a);
+  }
   ZQ_LAUNCH_CHECK();
   return ZQ_OK;
 }
@@ -1191,14 +1263,26 @@ bool moe_tok_fits(int64_t d_model, int64_t d_ff) {
 
 int launch_moe_ffn_tok(int wtype, const MoeTokArgs &p, MoeGateUpArgs g, MoeDownTokArgs d,
                        hipStream_t stream) {
-  const size_t lv = static_cast<size_t>(p.n_tok) * ((p.n_routed + 3) / 4 * 4) * 4;
-  hipLaunchKernelGGL(moe_tok_plan_kernel, dim3(1 + p.n_tok), dim3(1024), lv, stream, p);
+  // P threads per logit while n_routed * P fits the 1024 threads (P <= 16),
+  // as the single-token router
+  int pp = 1;
+  while (pp < 16 && p.n_routed * (pp * 2) <= 1024) pp *= 2;
+  switch (pp) {
+    case 16: launch_tok_route<16>(p, stream); break;
+    case 8: launch_tok_route<8>(p, stream); break;
+    case 4: launch_tok_route<4>(p, stream); break;
+    case 2: launch_tok_route<2>(p, stream); break;
+    default: launch_tok_route<1>(p, stream); break;
+  }
   ZQ_LAUNCH_CHECK();
+  const int n_sel_tok = d.n_sel_tok;
+  g.ids = p.ids;
   g.nb = static_cast<int32_t>(g.k / 32);
   g.row_bytes = static_cast<int64_t>(g.nb) * (wtype == ZQ_Q4_0 ? 18 : 34);
-  int rc = wtype == ZQ_Q4_0 ? launch_gu_tok_w<ZQ_Q4_0>(g, p, stream)
-                            : launch_gu_tok_w<ZQ_Q8_0>(g, p, stream);
+  int rc = wtype == ZQ_Q4_0 ? launch_gu_tok_w<ZQ_Q4_0>(g, d.mem, p, n_sel_tok, stream)
+                            : launch_gu_tok_w<ZQ_Q8_0>(g, d.mem, p, n_sel_tok, stream);
   if (rc != ZQ_OK) return rc;
+  d.ids = p.ids;
   d.nb = static_cast<int32_t>(d.k / 32);
   d.row_bytes = static_cast<int64_t>(d.nb) * (wtype == ZQ_Q4_0 ? 18 : 34);
   return wtype == ZQ_Q4_0 ? launch_dn_tok_w<ZQ_Q4_0>(d, stream) : launch_dn_tok_w<ZQ_Q8_0>(d, stream);

@@ -978,7 +978,7 @@ int moe_stage(int wtype, int mode, const void *bank, int64_t stride, int64_t n_e
 namespace {
 
 struct MoeTokWorkspace {
-  size_t plan, qx, dx, sx, qh, dh, sh, total;
+  size_t mem, qx, dx, sx, qh, dh, sh, total;
 };
 
 MoeTokWorkspace moe_tok_layout(int64_t d_model, int64_t d_ff, int32_t n_tok, int32_t n_sel) {
@@ -986,7 +986,7 @@ MoeTokWorkspace moe_tok_layout(int64_t d_model, int64_t d_ff, int32_t n_tok, int
   const size_t T = static_cast<size_t>(n_tok);
   MoeTokWorkspace w;
   size_t off = 0;
-  w.plan = off; off += round_up((1 + (1 + zq::kTokMax) * J) * 4);
+  w.mem = off; off += round_up(zq::kTokMax * J * 4);
   w.qx = off; off += round_up(T * static_cast<size_t>(d_model));
   w.dx = off; off += round_up(T * static_cast<size_t>(d_model / 32) * 4);
   w.sx = off; off += round_up(T * static_cast<size_t>(d_model / 32) * 4);
@@ -1043,7 +1043,6 @@ int zq_moe_ffn_tokens(int wtype, const void *gu_bank, int64_t gu_stride_bytes,
   p.n_tok = n_tok;
   p.ids = ids;
   p.wts = wts;
-  p.plan = reinterpret_cast<int32_t *>(ws + L.plan);
   p.x = x;
   p.d_model = static_cast<int32_t>(d_model);
   p.qx = reinterpret_cast<int8_t *>(ws + L.qx);
@@ -1063,7 +1062,7 @@ int zq_moe_ffn_tokens(int wtype, const void *gu_bank, int64_t gu_stride_bytes,
   d.bank = static_cast<const uint8_t *>(down_bank);
   d.expert_stride = down_stride_bytes;
   d.n_experts = static_cast<int32_t>(n_experts);
-  d.plan = p.plan;
+  d.mem = reinterpret_cast<int32_t *>(ws + L.mem);
   d.n_sel = J;
   d.n_tok = n_tok;
   d.qh = g.qh;

@@ -11,7 +11,7 @@ namespace zq {
 
 constexpr int kTokMax = 8;  // tokens per several-token MoE call
 
-// The plan launch: routing of every token and the union of their experts.
+// The route launch: every token's router and activation codes.
 struct MoeTokArgs {
   const float *logits;        // [n_tok][n_routed]
   int32_t n_routed;
@@ -20,7 +20,6 @@ struct MoeTokArgs {
   int32_t n_tok;
   int32_t *ids;               // [n_tok][n_sel]
   float *wts;                 // [n_tok][n_sel]
-  int32_t *plan;              // 1 + (1 + kTokMax) * n_tok * n_sel int32
   const float *x;             // [n_tok][d_model], 16-byte aligned
   int32_t d_model;
   int8_t *qx;                 // [n_tok][d_model]: every token's codes
@@ -33,7 +32,11 @@ struct MoeDownTokArgs {
   const uint8_t *bank;        // experts of [rows][k]
   int64_t expert_stride;
   int32_t n_experts;
-  const int32_t *plan;
+  int32_t *mem;               // [J][kTokMax]: when slot j is the first use of its
+                              // expert, the slots of every token that selected that
+                              // expert in token order, then -1; all -1 otherwise
+                              // (written by the gate/up launch)
+  const int32_t *ids;         // [J]: the router's expert ids (filled in by the launcher)
   int32_t n_sel;              // J = n_tok * (top_k (+1)): flattened slots
   int32_t n_tok;
   const int8_t *qh;           // [J][k]
@@ -51,7 +54,7 @@ struct MoeDownTokArgs {
 };
 
 bool moe_tok_fits(int64_t d_model, int64_t d_ff);
-// plan, gate/up (g: bank, stride, n_experts, k = d_model, d_ff, qh / dh /
+// route, gate/up (g: bank, stride, n_experts, k = d_model, d_ff, qh / dh /
 // sh of J slots, n_sel = J), down with the weighted sums.
 int launch_moe_ffn_tok(int wtype, const MoeTokArgs &p, MoeGateUpArgs g, MoeDownTokArgs d,
                        hipStream_t stream);

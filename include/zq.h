@@ -417,10 +417,11 @@ int zq_moe_ffn_mixed(int gu_wtype, const void *gu_bank, int64_t gu_stride_bytes,
  * sigmoid(shared_gate[t]) when shared_gate is non-NULL), then
  *   y[t] (+)= sum_s wts[t][s] * down_{ids[t][s]}(Q(swiglu(gate||up_{ids[t][s]}(Q(x[t]))))),
  * the gate/up codes and scales bit for bit those of the single-token stages,
- * the weighted sum taken over the slots in order.  Three launches: a plan
- * (every token's routing and quantized activation, and the list of distinct
- * experts), gate/up (each distinct expert's rows read once for all tokens
- * that selected it), and down with the per-token weighted sums (the same).
+ * the weighted sum taken over the slots in order.  Three launches: route
+ * (every token's router and quantized activation), gate/up (each distinct
+ * expert's rows read once for all tokens that selected it; it also records
+ * which tokens share each expert), and down with the per-token weighted sums
+ * (each distinct expert's rows read once).
  * wtype ZQ_Q4_0 or ZQ_Q8_0; banks as zq_moe_ffn (n_experts >= n_routed + 1
  * with a shared expert); d_model a multiple of 32 up to 4096; d_ff 256, 512,
  * 1024 or 2048.  logits [n_tok][n_routed]; shared_gate [n_tok] or NULL;

@@ -133,13 +133,20 @@ def test_tokens_shared_experts_and_accumulate(zq):
     assert np.array_equal(y2.view(np.uint32), (x + y).astype(np.float32).view(np.uint32))
 
 
-# Q8_0 experts, every d_ff the call takes, no shared expert, top 1 and a
-# wide router.
+# Q8_0 experts, every d_ff the call takes, no shared expert, top 1, a wide
+# router, slots whose hidden codes are too many for the down pass to stage
+# in LDS (8 x 17 slots of 1024, and the most slots a call takes: 8 tokens x
+# 65), and activations wider than 64 blocks (two blocks per lane in gate/up,
+# the second partly past the row at 3072).
 @pytest.mark.parametrize("wt,n_routed,top_k,d_model,d_ff,n_tok,shared", [
     (Q8_0, 16, 4, 1024, 256, 3, True),
     (Q8_0, 32, 2, 512, 1024, 8, False),
     (Q4_0, 20, 1, 2048, 2048, 6, True),
     (Q4_0, 1024, 64, 256, 256, 2, True),
+    (Q4_0, 64, 16, 512, 1024, 8, True),
+    (Q8_0, 256, 64, 256, 256, 8, True),
+    (Q4_0, 8, 2, 4096, 512, 3, True),
+    (Q8_0, 8, 2, 3072, 256, 2, False),
 ])
 def test_tokens_shapes(zq, wt, n_routed, top_k, d_model, d_ff, n_tok, shared):
     n_exp = n_routed + (1 if shared else 0)
