@@ -272,9 +272,10 @@ class DmmvWorkload(Workload):
 
 
 class DmmvKWorkload(Workload):
-    """Quantize + DMMV over K-quant super-blocks (Q4_K / Q5_K / Q6_K; two
-    launches)."""
-    dominant_name = "dmmv_k_kernel"
+    """DMMV over K-quant super-blocks (Q4_K / Q5_K / Q6_K) from the fp32
+    activation: one launch of zq_dmmv_k_f32, the quantization inside it."""
+    dominant_name = "dmmv_k_f32_kernel"
+    step_is_dominant = True
 
     def __init__(self, wl):
         from block_quant_matrix_amd import inputs
@@ -283,23 +284,17 @@ class DmmvKWorkload(Workload):
         self.name = cfg["name"]
         self.wtype, self.rows, self.k = cfg["wtype"], cfg["rows"], cfg["k"]
         self.tname = {inputs.Q4_K: "Q4_K", inputs.Q5_K: "Q5_K", inputs.Q6_K: "Q6_K"}[self.wtype]
-        self.dominant_name = "dmmv_k_kernel (%s)" % self.tname
+        self.dominant_name = "dmmv_k_f32_kernel (%s, quantize + DMMV)" % self.tname
         self.nb = self.k // 32
         self.wbytes = self.rows * (self.k // 256) * inputs.K_BLOCK_BYTES[self.wtype]
-        # the DMMV reads the weights, the int8 codes, scales (and for Q4_K /
-        # Q5_K the block sums), and writes fp32 rows; the step adds the fp32
-        # activation the quantizer reads and the codes, scales and sums it
-        # writes
-        sums = 4 * self.nb if self.wtype != inputs.Q6_K else 0
-        self.dmmv_bytes = self.wbytes + self.k + 4 * self.nb + sums + 4 * self.rows
-        self.step_bytes = self.dmmv_bytes + 4 * self.k + self.k + 8 * self.nb
-        # two launches per step: at most 2000 steps keep the timed region's
-        # launches within one hardware queue, so all of them are enqueued
-        # ahead of the GPU
+        # the step reads the weights and the fp32 activation and writes fp32
+        # rows (the codes live in each workgroup's LDS)
+        self.dmmv_bytes = self.wbytes + 4 * self.k + 4 * self.rows
+        self.step_bytes = self.dmmv_bytes
         if self.wbytes > (64 << 20):
             self.steps, self.warmup = 300, 20
         else:
-            self.steps, self.warmup = 2000, 100
+            self.steps, self.warmup = 3000, 100
 
     def setup(self, torch, zq, inputs):
         self.torch, self.zq = torch, zq
@@ -316,24 +311,9 @@ class DmmvKWorkload(Workload):
         self.sx = torch.empty(self.nb, dtype=torch.int32, device="cuda")
         self.y = torch.empty(self.rows, dtype=torch.float32, device="cuda")
 
-    def _dmmv(self, i):
-        w = self.w[i % self.ncopy]
-        if self.tname == "Q4_K":
-            self.zq.zq_dmmv_q4_k(w, self.rows, self.k, self.qx, self.dx, self.sx, self.y)
-        elif self.tname == "Q5_K":
-            self.zq.zq_dmmv_q5_k(w, self.rows, self.k, self.qx, self.dx, self.sx, self.y)
-        else:
-            self.zq.zq_dmmv_q6_k(w, self.rows, self.k, self.qx, self.dx, self.y)
-
     def step(self, i):
-        self.zq.zq_quantize_act(self.x, 1, self.k, self.k, self.qx, self.dx, self.sx)
-        self._dmmv(i)
-
-    def prepare_dominant(self):
-        self.zq.zq_quantize_act(self.x, 1, self.k, self.k, self.qx, self.dx, self.sx)
-
-    def dominant(self, i):
-        self._dmmv(i)
+        self.zq.zq_dmmv_k_f32(self.wtype, self.w[i % self.ncopy], self.rows, self.k, self.x,
+                              self.y)
 
     def value(self, ms):
         return self.step_bytes / (ms * 1e-3) / 1e9, "GB/s"
@@ -346,19 +326,26 @@ class DmmvKWorkload(Workload):
 
     def gpu_result(self):
         self.y.fill_(float("nan"))
-        self.step(0)
+        self.qx.fill_(0)
+        self.zq.zq_dmmv_k_f32(self.wtype, self.w[0], self.rows, self.k, self.x, self.y, 0,
+                              self.qx, self.dx, self.sx)
         self.torch.cuda.synchronize()
-        return {"y": self.y.cpu().numpy().copy()}
+        return {"y": self.y.cpu().numpy().copy(), "qx": self.qx.cpu().numpy().copy(),
+                "dx": self.dx.cpu().numpy().copy(), "sx": self.sx.cpu().numpy().copy()}
 
     def oracle_step(self):
         import oracle
-        qx, dx, _ = oracle.quantize_act(self.x_host)
+        qx, dx, sx = oracle.quantize_act(self.x_host)
         y, S = oracle.k_dmmv(self.wtype, self.w_host0, self.rows, self.k, qx, dx)
-        return {"y": y, "S": S}
+        return {"y": y, "S": S, "qx": qx, "dx": dx, "sx": sx}
 
     def parity(self, gpu, ref):
+        codes = (np.array_equal(gpu["qx"], ref["qx"]) and np.array_equal(gpu["sx"], ref["sx"])
+                 and np.array_equal(gpu["dx"].view(np.uint32),
+                                    np.asarray(ref["dx"], np.float32).view(np.uint32)))
         ok, worst = rows_within(gpu["y"], ref["y"], ref["S"])
-        return ok, "%d rows within %g*S (worst %.3g*S)" % (self.rows, ROW_TOL, worst)
+        return ok and codes, "stored codes %s; %d rows within %g*S (worst %.3g*S)" % (
+            "bit-exact" if codes else "DIFFER", self.rows, ROW_TOL, worst)
 
     def cpu_sample(self):
         return "quantize + %d-row %s DMMV over this workload's first weight copy" % (
@@ -366,9 +353,10 @@ class DmmvKWorkload(Workload):
 
 
 class DmmvTokWorkload(Workload):
-    """Quantize T tokens + one multi-token DMMV (two launches): the small-M
-    decode shapes, Q4_0 4096 x 4096 (the tile form on the matrix cores) and
-    the 248 320-row LM head (the tall form on the matrix cores)."""
+    """T fp32 tokens through zq_dmmv_tokens_f32 (two launches: the quantizer,
+    then one multi-token DMMV): the small-M decode shapes, Q4_0 4096 x 4096
+    (the tile form on the matrix cores) and the 248 320-row LM head (the tall
+    form on the matrix cores)."""
     dominant_name = "dmmv_tok_kernel"
 
     def __init__(self, wl):
@@ -409,8 +397,8 @@ class DmmvTokWorkload(Workload):
         self.y = torch.empty((self.T, self.rows), dtype=torch.float32, device="cuda")
 
     def step(self, i):
-        self.zq.zq_quantize_act(self.x, self.T, self.k, self.k, self.qx, self.dx, self.sx)
-        self.dominant(i)
+        self.zq.zq_dmmv_tokens_f32(self.wtype, self.w[i % self.ncopy], self.rows, self.k, self.x,
+                                   self.T, self.qx, self.dx, self.sx, self.y)
 
     def prepare_dominant(self):
         self.zq.zq_quantize_act(self.x, self.T, self.k, self.k, self.qx, self.dx, self.sx)

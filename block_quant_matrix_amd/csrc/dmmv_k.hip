@@ -39,6 +39,7 @@
 // registers, the loads of RB row steps are issued before any arithmetic, and
 // row partials are folded across lanes by RowReduce.
 #include "zq_common.h"
+#include "zq_f32in.h"
 #include "zq_internal.h"
 #include "zq_kquant.h"
 
@@ -366,6 +367,165 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   }
 }
 
+// ---------------------------------------------------------------------------
+// fp32-input form: y (+)= W . Q(x) in one launch, Q the activation quantizer
+// of quantize.hip.  Each workgroup (4 waves) issues its loads of x (two lanes
+// per 32-element block), then every lane issues its first row group's weight
+// units, then x is quantized into LDS (codes, scales, code sums) while the
+// weights stream in; after one barrier each lane takes its units' codes from
+// LDS and the row groups proceed as in dmmv_k_kernel (one pass over the
+// units: k <= 64 * LPR * BPL).  Workgroup 0 can also store the quantized
+// activation.
+template <int WT, int LPR, int BPL, int RB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void dmmv_k_f32_kernel(
+    const DmmvKF32Args a) {
+  constexpr int S = 64 / LPR;
+  constexpr int NWD = KQ<WT>::NWD;
+  constexpr int T = 256;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  int8_t *lq = reinterpret_cast<int8_t *>(smem);                       // [k]
+  float *ld = reinterpret_cast<float *>(smem + a.k);                   // [nb]
+  int32_t *ls = reinterpret_cast<int32_t *>(smem + a.k + 4 * a.nb);    // [nb]
+  const int tid = static_cast<int>(threadIdx.x);
+  const int lane = tid & 63;
+  const int j = lane & (LPR - 1);
+  const int slot = lane / LPR;
+  const int64_t wave = (static_cast<int64_t>(blockIdx.x) * T + tid) >> 6;
+  const int64_t n_waves = (static_cast<int64_t>(gridDim.x) * T) >> 6;
+  const int nu = a.nb / 2;  // 64-element units per row
+  const int p = j & 3;
+
+  // 1. x: this thread's first block half (16 elements)
+  const int g = tid & 1;
+  int qb = tid >> 1;
+  float xv[16];
+  if (qb < a.nb) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float4 f = *reinterpret_cast<const float4 *>(a.x + qb * 32 + g * 16 + 4 * u);
+      xv[4 * u] = f.x; xv[4 * u + 1] = f.y; xv[4 * u + 2] = f.z; xv[4 * u + 3] = f.w;
+    }
+  }
+
+  // 2. the first row group's weight units
+  uint32_t v[RB][BPL][NWD];
+  auto load_group = [&](int64_t gi) {
+    const int64_t row0 = gi * (RB * S);
+#pragma unroll
+    for (int t = 0; t < RB; ++t) {
+      int64_t row = row0 + t * S + slot;
+      row = row < a.rows ? row : a.rows - 1;
+#pragma unroll
+      for (int i = 0; i < BPL; ++i) {
+        int u = j + LPR * i;
+        u = u < nu ? u : nu - 1;
+        load_unit_w<WT>(a.w + row * a.row_bytes + static_cast<int64_t>(u >> 2) * KQ<WT>::BYTES, p,
+                        v[t][i]);
+      }
+    }
+  };
+  // (unconditional, past the last group the last one again: a load under a
+  // branch would make the activation's quantization below wait for every
+  // weight load, the wait counts being merged over both paths)
+  int64_t gi = wave;
+  load_group(gi < a.n_groups ? gi : a.n_groups - 1);
+
+  // 3. quantize x into LDS
+  const bool out = blockIdx.x == 0 && a.qx_out != nullptr;
+  for (; qb < a.nb; qb += T / 2) {
+    if (qb != (tid >> 1)) {  // further blocks when k > 4096
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float4 f = *reinterpret_cast<const float4 *>(a.x + qb * 32 + g * 16 + 4 * u);
+        xv[4 * u] = f.x; xv[4 * u + 1] = f.y; xv[4 * u + 2] = f.z; xv[4 * u + 3] = f.w;
+      }
+    }
+    uint32_t pk[4];
+    float d;
+    int32_t sum;
+    quantize_block<2>(xv, pk, d, sum);
+    *reinterpret_cast<u32x4 *>(lq + qb * 32 + g * 16) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+    if (g == 0) {
+      ld[qb] = d;
+      ls[qb] = sum;
+    }
+    if (out) {
+      uint32_t *qo = reinterpret_cast<uint32_t *>(a.qx_out + qb * 32 + g * 16);
+      qo[0] = pk[0]; qo[1] = pk[1]; qo[2] = pk[2]; qo[3] = pk[3];
+      if (g == 0) {
+        if (a.dx_out) a.dx_out[qb] = d;
+        if (a.sx_out) a.sx_out[qb] = sum;
+      }
+    }
+  }
+  __syncthreads();
+
+  // 4. this lane's units' activation; units past the row end take the last
+  //    unit's codes and zero scales
+  KUnitAct act[BPL];
+#pragma unroll
+  for (int i = 0; i < BPL; ++i) {
+    const int u0 = j + LPR * i;
+    const bool ok = u0 < nu;
+    const int u = ok ? u0 : nu - 1;
+    KUnitAct &A = act[i];
+    if constexpr (WT == ZQ_Q6_K) {
+      const int base = 256 * (u >> 2) + 128 * ((u >> 1) & 1) + 16 * (u & 1);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int e0 = base + 32 * c;
+        const u32x4 q = *reinterpret_cast<const u32x4 *>(lq + e0);
+        A.q[4 * c] = q.x; A.q[4 * c + 1] = q.y; A.q[4 * c + 2] = q.z; A.q[4 * c + 3] = q.w;
+        A.d[c] = ok ? ld[e0 >> 5] : 0.0f;
+        A.m32[c] = -32 * code_sum(&A.q[4 * c], 4);
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int b = 2 * u + h;
+        const u32x4 q0 = *reinterpret_cast<const u32x4 *>(lq + 32 * b);
+        const u32x4 q1 = *reinterpret_cast<const u32x4 *>(lq + 32 * b + 16);
+        uint32_t *q = &A.q[8 * h];
+        q[0] = q0.x; q[1] = q0.y; q[2] = q0.z; q[3] = q0.w;
+        q[4] = q1.x; q[5] = q1.y; q[6] = q1.z; q[7] = q1.w;
+        A.d[h] = ok ? ld[b] : 0.0f;
+        A.fs[h] = static_cast<float>(ls[b]);  // |sum| <= 32*127: exact
+      }
+    }
+  }
+
+  // 5. the row groups: dots, reduction, store; then the next group's units
+  while (gi < a.n_groups) {
+    const int64_t row0 = gi * (RB * S);
+    float acc[RB];
+#pragma unroll
+    for (int t = 0; t < RB; ++t) {
+      float part = 0.0f;
+#pragma unroll
+      for (int i = 0; i < BPL; ++i) {
+        int32_t is[4];
+        part += unit_dot<WT>(v[t][i], p, act[i], is);
+      }
+      acc[t] = part;
+    }
+    using R = RowReduce<LPR, RB>;
+    float res[R::NOUT];
+    R::run(acc, res);
+    if (R::writer(lane)) {
+#pragma unroll
+      for (int m = 0; m < R::NOUT; ++m) {
+        const int64_t row = row0 + static_cast<int64_t>(R::rowstep(m, lane)) * S + slot;
+        if (row < a.rows) {
+          float *yp = a.y + row;
+          *yp = (a.flags & ZQ_ACCUMULATE) ? *yp + res[m] : res[m];
+        }
+      }
+    }
+    gi += n_waves;
+    if (gi < a.n_groups) load_group(gi);
+  }
+}
+
 template <int WT, int LPR, int RB, int SWT>
 int launch_wsum1(DmmvArgs a, hipStream_t stream) {
   a.n_groups = (a.rows + RB - 1) / RB;
@@ -506,7 +666,62 @@ int launch_type(int mode, DmmvArgs a, hipStream_t stream) {
   }
 }
 
+// The fp32-input form: the plain layout and row steps, a workgroup's
+// activation staged once (grids beyond 4096 workgroups loop over groups).
+template <int WT, int LPR, int BPL, int RB>
+int launch_kf1(DmmvKF32Args a, hipStream_t stream) {
+  constexpr int S = 64 / LPR;
+  a.n_groups = (a.rows + RB * S - 1) / (RB * S);
+  const int64_t blocks = (a.n_groups + 3) / 4;
+  const unsigned grid = static_cast<unsigned>(blocks < 4096 ? blocks : 4096);
+  const size_t lds = static_cast<size_t>(a.k) + 8 * static_cast<size_t>(a.nb);
+  hipLaunchKernelGGL((dmmv_k_f32_kernel<WT, LPR, BPL, RB>), dim3(grid), dim3(256), lds, stream, a);
+  ZQ_LAUNCH_CHECK();
+  return ZQ_OK;
+}
+
+template <int WT, int LPR, int BPL>
+int launch_kfrb(int rb, const DmmvKF32Args &a, hipStream_t stream) {
+  constexpr int CAP = 96 / (KQ<WT>::NWD * BPL);
+  if constexpr (CAP >= 8) {
+    if (rb >= 8) return launch_kf1<WT, LPR, BPL, 8>(a, stream);
+  }
+  if constexpr (CAP >= 4) {
+    if (rb >= 4) return launch_kf1<WT, LPR, BPL, 4>(a, stream);
+  }
+  if constexpr (CAP >= 2) {
+    if (rb >= 2) return launch_kf1<WT, LPR, BPL, 2>(a, stream);
+  }
+  return launch_kf1<WT, LPR, BPL, 1>(a, stream);
+}
+
+template <int WT>
+int launch_kf_type(DmmvKF32Args a, hipStream_t stream) {
+  a.row_bytes = static_cast<int64_t>(a.nb / 8) * KQ<WT>::BYTES;
+  const int nu = a.nb / 2;
+  const KShape sh = choose_kshape(nu);
+  if (static_cast<int64_t>(sh.lpr) * sh.bpl < nu) return ZQ_EINVAL;  // one pass only
+  const int rb = choose_krb<WT>(sh, a.rows, MODE_PLAIN, 1);
+  if (sh.lpr == 8) return launch_kfrb<WT, 8, 1>(rb, a, stream);
+  if (sh.lpr == 16 && sh.bpl == 1) return launch_kfrb<WT, 16, 1>(rb, a, stream);
+  if (sh.lpr == 16) return launch_kfrb<WT, 16, 5>(rb, a, stream);
+  if (sh.lpr == 32) return launch_kfrb<WT, 32, 1>(rb, a, stream);
+  if (sh.bpl == 1) return launch_kfrb<WT, 64, 1>(rb, a, stream);
+  if (sh.bpl == 2) return launch_kfrb<WT, 64, 2>(rb, a, stream);
+  return launch_kfrb<WT, 64, 4>(rb, a, stream);
+}
+
 }  // namespace
+
+int launch_dmmv_k_f32(int wtype, DmmvKF32Args a, hipStream_t stream) {
+  if (a.rows == 0) return ZQ_OK;
+  switch (wtype) {
+    case ZQ_Q4_K: return launch_kf_type<ZQ_Q4_K>(a, stream);
+    case ZQ_Q5_K: return launch_kf_type<ZQ_Q5_K>(a, stream);
+    case ZQ_Q6_K: return launch_kf_type<ZQ_Q6_K>(a, stream);
+    default: return ZQ_EINVAL;
+  }
+}
 
 bool dmmv_k_wsum_shared_fits(int wtype, int sh_wtype, int64_t k) {
   return (wtype == ZQ_Q4_K || wtype == ZQ_Q5_K || wtype == ZQ_Q6_K) &&

@@ -5,6 +5,7 @@
 #include <cstring>
 
 #include "zq_common.h"
+#include "zq_f32in.h"
 #include "zq_float.h"
 #include "zq_internal.h"
 #include "zq_moe_tok.h"
@@ -285,6 +286,63 @@ int zq_dmmv_f32(int wtype, const void *w, int64_t rows, int64_t k, const float *
   a.nb = static_cast<int32_t>(k / 32);
   a.flags = flags;
   return zq::launch_dmmv_f32x(wtype, a, S(stream));
+}
+
+int zq_dmmv_k_f32(int wtype, const void *w, int64_t rows, int64_t k, const float *x, float *y,
+                  uint32_t flags, int8_t *qx_out, float *dx_out, int32_t *sx_out, void *stream) {
+  ZQ_REQUIRE(is_k(wtype), ZQ_EINVAL);
+  ZQ_REQUIRE(w && x && y, ZQ_ENULL);
+  ZQ_REQUIRE(rows >= 0 && k >= 256 && k % 256 == 0 && k <= 16384, ZQ_EINVAL);
+  ZQ_REQUIRE((flags & ~uint32_t(ZQ_ACCUMULATE)) == 0, ZQ_EINVAL);
+  ZQ_REQUIRE(al(w, 16) && al(x, 16) && al(y, 4) && al(qx_out, 4) && al(dx_out, 4) &&
+                 al(sx_out, 4),
+             ZQ_EALIGN);
+  const int dc = check_current_device();
+  if (dc != ZQ_OK) return dc;
+  zq::DmmvKF32Args a{};
+  a.w = static_cast<const uint8_t *>(w);
+  a.x = x;
+  a.y = y;
+  a.qx_out = qx_out;
+  a.dx_out = dx_out;
+  a.sx_out = sx_out;
+  a.rows = rows;
+  a.k = static_cast<int32_t>(k);
+  a.nb = static_cast<int32_t>(k / 32);
+  a.flags = flags;
+  return zq::launch_dmmv_k_f32(wtype, a, S(stream));
+}
+
+int zq_dmmv_tokens_f32(int wtype, const void *w, int64_t rows, int64_t k, const float *x,
+                       int32_t n_tok, int8_t *qx, float *dx, int32_t *sx, float *y, uint32_t flags,
+                       void *stream) {
+  ZQ_REQUIRE(block_bytes(wtype) > 0, ZQ_EINVAL);
+  ZQ_REQUIRE(w && x && qx && dx && sx && y, ZQ_ENULL);
+  ZQ_REQUIRE(rows >= 0 && k_ok(k) && k <= (int64_t(1) << 30), ZQ_EINVAL);
+  ZQ_REQUIRE(n_tok >= 1 && n_tok <= 8, ZQ_EINVAL);
+  ZQ_REQUIRE(int64_t(n_tok) * (k / 32) <= (int64_t(1) << 31), ZQ_EINVAL);
+  ZQ_REQUIRE((flags & ~uint32_t(ZQ_ACCUMULATE)) == 0, ZQ_EINVAL);
+  ZQ_REQUIRE(al(w, 4) && al(x, 16) && al(qx, 16) && al(dx, 4) && al(sx, 4) && al(y, 4),
+             ZQ_EALIGN);
+  const int dc = check_current_device();
+  if (dc != ZQ_OK) return dc;
+  // every workgroup of every multi-token form needs all the tokens' codes:
+  // quantizing inside the product's launch would redo the whole
+  // quantization in each workgroup, so the quantizer runs first
+  const int rc = zq::launch_quantize_act(x, n_tok, k, k, qx, dx, sx, S(stream));
+  if (rc != ZQ_OK) return rc;
+  zq::DmmvTokArgs a{};
+  a.w = static_cast<const uint8_t *>(w);
+  a.qx = qx;
+  a.dx = dx;
+  a.sx = wtype == ZQ_Q4_0 ? sx : nullptr;
+  a.y = y;
+  a.rows = rows;
+  a.k = static_cast<int32_t>(k);
+  a.nb = static_cast<int32_t>(k / 32);
+  a.n_tok = n_tok;
+  a.flags = flags;
+  return zq::launch_dmmv_tok(wtype, a, S(stream));
 }
 
 int zq_dmmv_isums(int wtype, const void *w, int64_t rows, int64_t k, const int8_t *qx,

@@ -44,6 +44,8 @@ SIGNATURES = {
     "zq_dmmv_tokens": (_INT, [_INT, _P, _I64, _I64, _P, _P, _P, _I32, _P, _U32, _P]),
     "zq_dmmv_f32": (_INT, [_INT, _P, _I64, _I64, _P, _P, _U32, _P, _P, _P, _P]),
     "zq_dmmv_float": (_INT, [_INT, _P, _I64, _I64, _P, _P, _U32, _P]),
+    "zq_dmmv_k_f32": (_INT, [_INT, _P, _I64, _I64, _P, _P, _U32, _P, _P, _P, _P]),
+    "zq_dmmv_tokens_f32": (_INT, [_INT, _P, _I64, _I64, _P, _I32, _P, _P, _P, _P, _U32, _P]),
     "zq_dmmv_isums": (_INT, [_INT, _P, _I64, _I64, _P, _P, _P, _P]),
     "zq_argmax_workspace_bytes": (_SZ, [_I64]),
     "zq_argmax_f32": (_INT, [_P, _I64, _P, _P, _SZ, _P]),
@@ -194,6 +196,17 @@ def zq_dmmv_f32(wtype, w, rows, k, x, y, flags=0, qx_out=None, dx_out=None, sx_o
                 stream=None):
     return _call("zq_dmmv_f32", wtype, ptr(w), rows, k, ptr(x), ptr(y), flags, ptr(qx_out),
                  ptr(dx_out), ptr(sx_out), _stream(stream))
+
+
+def zq_dmmv_k_f32(wtype, w, rows, k, x, y, flags=0, qx_out=None, dx_out=None, sx_out=None,
+                  stream=None):
+    return _call("zq_dmmv_k_f32", wtype, ptr(w), rows, k, ptr(x), ptr(y), flags, ptr(qx_out),
+                 ptr(dx_out), ptr(sx_out), _stream(stream))
+
+
+def zq_dmmv_tokens_f32(wtype, w, rows, k, x, n_tok, qx, dx, sx, y, flags=0, stream=None):
+    return _call("zq_dmmv_tokens_f32", wtype, ptr(w), rows, k, ptr(x), n_tok, ptr(qx), ptr(dx),
+                 ptr(sx), ptr(y), flags, _stream(stream))
 
 
 def zq_dmmv_float(wtype, w, rows, k, x, y, flags=0, stream=None):

@@ -163,6 +163,40 @@ int zq_dmmv_tokens(int wtype, const void *w, int64_t rows, int64_t k, const int8
 int zq_dmmv_f32(int wtype, const void *w, int64_t rows, int64_t k, const float *x, float *y,
                 uint32_t flags, int8_t *qx_out, float *dx_out, int32_t *sx_out, void *stream);
 
+/* The K-quant DMMV from the fp32 activation in one launch: y (+)= W . Q(x),
+ * Q exactly the quantization of zq_quantize_act, over Q4_K / Q5_K / Q6_K
+ * super-blocks as zq_dmmv_q4_k / zq_dmmv_q5_k / zq_dmmv_q6_k read them.  The
+ * fp32-input ABI of the direct DMMV slice ("The first ZINC_RT model slices
+ * that actually count", section "The one-wave workaround"), with the
+ * activation's quantization fused into the matvec kernel ("Как мы запустили
+ * 35B LLM...", section "Фьюженные ядра"): each workgroup quantizes x into LDS
+ * while its first weight loads are in flight.
+ * wtype ZQ_Q4_K, ZQ_Q5_K or ZQ_Q6_K; w rows x k/256 super-blocks (16-byte
+ * aligned); x [k] fp32 (16-byte aligned, finite); y [rows] fp32; flags 0 or
+ * ZQ_ACCUMULATE; k a multiple of 256, 256 <= k <= 16384.  qx_out [k] int8
+ * (4-byte aligned), dx_out [k/32], sx_out [k/32]: as for zq_dmmv_f32. */
+int zq_dmmv_k_f32(int wtype, const void *w, int64_t rows, int64_t k, const float *x, float *y,
+                  uint32_t flags, int8_t *qx_out, float *dx_out, int32_t *sx_out, void *stream);
+
+/* The multi-token DMMV from fp32 tokens: for t < n_tok,
+ *   y[t] (+)= W . Q(x[t]),
+ * the products of zq_dmmv_tokens on the codes of zq_quantize_act, which are
+ * also stored in qx / dx / sx (always written; they may feed later products
+ * against the same tokens).  The fp32-input ABI of the same slice ("The first
+ * ZINC_RT model slices that actually count", section "The one-wave
+ * workaround") for the multi-row matvec of "RTX 5090: Batched Prefill & CUDA
+ * Graphs in ZINC", section "What's next".  Two launches: zq_quantize_act,
+ * then zq_dmmv_tokens (every workgroup of the product needs every token's
+ * codes, so quantizing inside it would repeat the whole quantization in each
+ * workgroup; a producer that emits the codes, as zq_rms_norm_quantize does,
+ * saves the first launch).  wtype ZQ_Q4_0 or ZQ_Q8_0; w rows x k blocks;
+ * x [n_tok][k] fp32 (16-byte aligned, finite); qx [n_tok][k] int8 (16-byte
+ * aligned); dx, sx [n_tok][k/32]; y [n_tok][rows]; 1 <= n_tok <= 8; flags 0
+ * or ZQ_ACCUMULATE. */
+int zq_dmmv_tokens_f32(int wtype, const void *w, int64_t rows, int64_t k, const float *x,
+                       int32_t n_tok, int8_t *qx, float *dx, int32_t *sx, float *y, uint32_t flags,
+                       void *stream);
+
 /* RMS normalization fused with the activation quantization (the
  * rms_norm_mul stage of "Bringing ZINC to NVIDIA: a CUDA backend, because
  * WSL2 only speaks CUDA", section "The roadmap: from 70 to a coherent

@@ -438,6 +438,42 @@ def test_float_dmmv_argument_errors():
     assert rc(y=C + 2) == zq.ZQ_EALIGN
 
 
+def test_f32_input_forms_argument_errors():
+    L = zq.lib()
+
+    def rk(wtype=12, w=A, rows=64, k=4096, x=B, y=C, flags=0, qx=None, dx=None, sx=None):
+        return L.zq_dmmv_k_f32(wtype, w, rows, k, x, y, flags, qx, dx, sx, None)
+
+    assert rk(wtype=4) == zq.ZQ_EINVAL                  # block formats take zq_dmmv_f32
+    assert rk(k=4096 + 32) == zq.ZQ_EINVAL             # not whole super-blocks
+    assert rk(k=16384 + 256) == zq.ZQ_EINVAL
+    assert rk(k=0) == zq.ZQ_EINVAL
+    assert rk(rows=-1) == zq.ZQ_EINVAL
+    assert rk(flags=2) == zq.ZQ_EINVAL
+    assert rk(w=None) == zq.ZQ_ENULL
+    assert rk(x=None) == zq.ZQ_ENULL
+    assert rk(w=A + 4) == zq.ZQ_EALIGN
+    assert rk(x=B + 4) == zq.ZQ_EALIGN
+    assert rk(qx=D + 2) == zq.ZQ_EALIGN
+
+    def rt(wtype=4, w=A, rows=4096, k=4096, x=B, n_tok=8, qx=C, dx=D, sx=D + 0x1000,
+           y=D + 0x2000, flags=0):
+        return L.zq_dmmv_tokens_f32(wtype, w, rows, k, x, n_tok, qx, dx, sx, y, flags, None)
+
+    assert rt(wtype=12) == zq.ZQ_EINVAL
+    assert rt(n_tok=0) == zq.ZQ_EINVAL
+    assert rt(n_tok=9) == zq.ZQ_EINVAL
+    assert rt(k=4100) == zq.ZQ_EINVAL
+    assert rt(flags=2) == zq.ZQ_EINVAL
+    assert rt(qx=None) == zq.ZQ_ENULL                  # the codes are always stored
+    assert rt(sx=None) == zq.ZQ_ENULL
+    assert rt(x=B + 8) == zq.ZQ_EALIGN
+    assert rt(qx=C + 4) == zq.ZQ_EALIGN
+    if not os.path.exists("/dev/kfd"):
+        assert rk() == zq.ZQ_EDEVICE
+        assert rt() == zq.ZQ_EDEVICE
+
+
 def test_read_probe_argument_errors():
     L = zq.lib()
     assert L.zq_read_probe(A, 24, C, None) == zq.ZQ_EINVAL
