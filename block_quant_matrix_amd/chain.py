@@ -2,11 +2,11 @@
 replay.
 
 One token passes through `layers` copies of the hot path and the LM head:
-  per layer: RMS-normalize the fp32 state and take the router logits as a
-    Q8_0 DMMV of it (one launch; the normalized state xn is published for
-    the experts), then the routed MoE block on xn (router top-k + softmax
-    folded into the gate/up pass, SwiGLU + requantize, down with the
-    weighted sum) added onto the state (two launches, ZQ_ACCUMULATE);
+  per layer, zq_moe_ffn_norm_route: RMS-normalize the fp32 state and take
+    the Q8_0 router DMMV of it (one launch; xn and the logits published),
+    then the routed MoE block on xn (router top-k + softmax folded into the
+    gate/up pass, SwiGLU + requantize, down with the weighted sum) added
+    onto the state (two launches, ZQ_ACCUMULATE);
   then the LM head: final RMS norm, Q4_0 DMMV + argmax (two launches).
 The layer order and the residual add follow the decode forward order of
 "Bringing ZINC to NVIDIA: a CUDA backend, because WSL2 only speaks CUDA",
@@ -63,17 +63,15 @@ class DecodeChain:
         self.graph = None
 
     def step_layer(self, layer, stream=None):
-        """Enqueue one layer: norm + router logits (xn published), then the
-        routed MoE block on xn added onto the state."""
+        """Enqueue one layer: norm, router, the routed MoE block added onto
+        the state (xn and the logits published)."""
         d, f = self.d_model, self.d_ff
-        _zq.zq_rms_norm_dmmv_f32(_zq.ZQ_Q8_0, self.router_w[layer], self.n_routed, d, self.x,
-                                 self.norm_w[layer], self.eps, self.logits,
-                                 xn_out=self.xn, stream=stream)
         gu, gs, dn, ds, ne = self.moe_banks[layer]
         g = None if self.shared_gate is None else self.shared_gate[layer]
-        _zq.zq_moe_ffn_route(_zq.ZQ_Q4_0, gu, gs, dn, ds, ne, d, f, self.logits, self.n_routed,
-                             self.top_k, g, self.xn, self.ids, self.wts, self.ws, self.ws_bytes,
-                             self.x, _zq.ZQ_ACCUMULATE, stream=stream)
+        _zq.zq_moe_ffn_norm_route(_zq.ZQ_Q4_0, gu, gs, dn, ds, ne, d, f, self.router_w[layer],
+                                  self.norm_w[layer], self.eps, self.x, self.n_routed, self.top_k,
+                                  g, self.xn, self.logits, self.ids, self.wts, self.ws,
+                                  self.ws_bytes, self.x, _zq.ZQ_ACCUMULATE, stream=stream)
 
     def lm_head(self, stream=None):
         """Enqueue the final norm, the LM-head DMMV and the argmax."""

@@ -30,32 +30,83 @@ __global__ __launch_bounds__(kArgmaxThreads) void argmax_partial_kernel(const fl
   if (threadIdx.x == 0) part[blockIdx.x] = ValIdx{v, i};
 }
 
-// Stage 2: one block reduces the partial pairs.  Each thread issues the
-// loads of up to kFinalPer pairs before comparing any, so the pass costs one
-// memory latency rather than one per pair.
-constexpr int kFinalPer = 8;
+// Stage 2: one workgroup of 1024 threads reduces the partial pairs.  Each
+// thread requests its pairs (two per round, 2048 per round over the
+// workgroup) before comparing any, so a round costs one memory latency; the
+// pairs meet within each wave through DPP moves inside 16-lane rows and the
+// permlane swaps across rows (a few cycles each, against a round trip
+// through LDS per step for lane shuffles), then across the 16 waves through
+// LDS and the same wave reduction once more.
+constexpr int kFinalThreads = 1024;
 
-__global__ __launch_bounds__(kArgmaxThreads) void argmax_final_kernel(const ValIdx *__restrict__ part,
-                                                                      int nparts,
-                                                                      int32_t *__restrict__ out) {
+template <int CTRL>
+__device__ __forceinline__ int32_t dpp_i(int32_t v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ void take_best(float &v, int32_t &i, float ov, int32_t oi) {
+  if (beats(ov, oi, v, i)) {
+    v = ov;
+    i = oi;
+  }
+}
+
+// The best pair of the wave, in every lane.  "beats" is a total order on
+// the pairs (ties go to the lower index), so the order of the steps does not
+// change the result.
+__device__ __forceinline__ void wave_best_dpp(float &v, int32_t &i) {
+  take_best(v, i, dpp<DPP_QUAD_XOR1>(v), dpp_i<DPP_QUAD_XOR1>(i));
+  take_best(v, i, dpp<DPP_QUAD_XOR2>(v), dpp_i<DPP_QUAD_XOR2>(i));
+  take_best(v, i, dpp<DPP_ROW_HALF_MIRROR>(v), dpp_i<DPP_ROW_HALF_MIRROR>(i));
+  take_best(v, i, dpp<DPP_ROW_MIRROR>(v), dpp_i<DPP_ROW_MIRROR>(i));
+  // rows 0/1 and 2/3: each lane sees both rows of its 32-lane half
+  {
+    float a = v, b = v;
+    swap16(a, b);
+    float ai = __builtin_bit_cast(float, i), bi = ai;
+    swap16(ai, bi);
+    take_best(v, i, a, __builtin_bit_cast(int32_t, ai));
+    take_best(v, i, b, __builtin_bit_cast(int32_t, bi));
+  }
+  // the two halves
+  {
+    float a = v, b = v;
+    swap32(a, b);
+    float ai = __builtin_bit_cast(float, i), bi = ai;
+    swap32(ai, bi);
+    take_best(v, i, a, __builtin_bit_cast(int32_t, ai));
+    take_best(v, i, b, __builtin_bit_cast(int32_t, bi));
+  }
+}
+
+__global__ __launch_bounds__(kFinalThreads) void argmax_final_kernel(const ValIdx *__restrict__ part,
+                                                                     int nparts,
+                                                                     int32_t *__restrict__ out) {
+  __shared__ float sv[kFinalThreads / 64];
+  __shared__ int32_t si[kFinalThreads / 64];
+  const int tid = static_cast<int>(threadIdx.x);
   float v = -__builtin_inff();
   int32_t i = 0x7fffffff;
-  for (int base = 0; base < nparts; base += kArgmaxThreads * kFinalPer) {
-    ValIdx p[kFinalPer];
-#pragma unroll
-    for (int u = 0; u < kFinalPer; ++u) {
-      const int k = base + u * kArgmaxThreads + static_cast<int>(threadIdx.x);
-      p[u] = k < nparts ? part[k] : ValIdx{-__builtin_inff(), 0x7fffffff};
-    }
-#pragma unroll
-    for (int u = 0; u < kFinalPer; ++u)
-      if (beats(p[u].v, p[u].i, v, i)) {
-        v = p[u].v;
-        i = p[u].i;
-      }
+  for (int base = 0; base < nparts; base += 2 * kFinalThreads) {
+    const int k0 = base + tid, k1 = base + kFinalThreads + tid;
+    const ValIdx p0 = k0 < nparts ? part[k0] : ValIdx{-__builtin_inff(), 0x7fffffff};
+    const ValIdx p1 = k1 < nparts ? part[k1] : ValIdx{-__builtin_inff(), 0x7fffffff};
+    take_best(v, i, p0.v, p0.i);
+    take_best(v, i, p1.v, p1.i);
   }
-  block_best<kArgmaxThreads / 64>(v, i);
-  if (threadIdx.x == 0) *out = i;
+  wave_best_dpp(v, i);
+  const int w = tid >> 6;
+  if ((tid & 63) == 0) {
+    sv[w] = v;
+    si[w] = i;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    v = tid < kFinalThreads / 64 ? sv[tid] : -__builtin_inff();
+    i = tid < kFinalThreads / 64 ? si[tid] : 0x7fffffff;
+    wave_best_dpp(v, i);
+    if (tid == 0) *out = i;
+  }
 }
 
 static int argmax_blocks(int64_t n) {
@@ -68,7 +119,7 @@ static int argmax_blocks(int64_t n) {
 size_t argmax_workspace(int64_t n) { return sizeof(ValIdx) * static_cast<size_t>(argmax_blocks(n)); }
 
 int launch_argmax_final(const void *part, int nparts, int32_t *out_idx, hipStream_t stream) {
-  hipLaunchKernelGGL(argmax_final_kernel, dim3(1), dim3(kArgmaxThreads), 0, stream,
+  hipLaunchKernelGGL(argmax_final_kernel, dim3(1), dim3(kFinalThreads), 0, stream,
                      static_cast<const ValIdx *>(part), nparts, out_idx);
   ZQ_LAUNCH_CHECK();
   return ZQ_OK;
@@ -81,7 +132,7 @@ int launch_argmax(const float *y, int64_t n, int32_t *out_idx, void *ws, hipStre
   hipLaunchKernelGGL(argmax_partial_kernel, dim3(nb), dim3(kArgmaxThreads), 0, stream, y, n, chunk,
                      part);
   ZQ_LAUNCH_CHECK();
-  hipLaunchKernelGGL(argmax_final_kernel, dim3(1), dim3(kArgmaxThreads), 0, stream, part, nb,
+  hipLaunchKernelGGL(argmax_final_kernel, dim3(1), dim3(kFinalThreads), 0, stream, part, nb,
                      out_idx);
   ZQ_LAUNCH_CHECK();
   return ZQ_OK;

@@ -950,6 +950,55 @@ int zq_moe_ffn_route(int wtype, const void *gu_bank, int64_t gu_stride_bytes,
                      S(stream));
 }
 
+int zq_moe_ffn_norm_route(int wtype, const void *gu_bank, int64_t gu_stride_bytes,
+                          const void *down_bank, int64_t down_stride_bytes, int64_t n_experts,
+                          int64_t d_model, int64_t d_ff, const void *router_w,
+                          const float *norm_w, float eps, const float *x, int32_t n_routed,
+                          int32_t top_k, const float *shared_gate, float *xn_out,
+                          float *logits_out, int32_t *ids, float *wts, void *workspace,
+                          size_t workspace_bytes, float *y, uint32_t flags, void *stream) {
+  const int64_t bb = block_bytes(wtype);
+  ZQ_REQUIRE(bb > 0, ZQ_EINVAL);
+  ZQ_REQUIRE(gu_bank && down_bank && router_w && norm_w && x && xn_out && logits_out && ids &&
+                 wts && workspace && y,
+             ZQ_ENULL);
+  ZQ_REQUIRE(top_k >= 1 && top_k <= 64 && n_routed >= top_k && n_routed <= 1024, ZQ_EINVAL);
+  const int32_t n_sel = top_k + (shared_gate ? 1 : 0);
+  ZQ_REQUIRE(n_experts >= n_sel - top_k + n_routed && n_experts <= INT32_MAX && k_ok(d_model) &&
+                 d_model <= 16384 && k_ok(d_ff) && eps_ok(eps),
+             ZQ_EINVAL);
+  ZQ_REQUIRE(gu_stride_bytes >= 2 * d_ff * (d_model / 32) * bb && gu_stride_bytes % 2 == 0,
+             ZQ_EINVAL);
+  ZQ_REQUIRE(down_stride_bytes >= d_model * (d_ff / 32) * bb && down_stride_bytes % 2 == 0,
+             ZQ_EINVAL);
+  ZQ_REQUIRE((flags & ~uint32_t(ZQ_ACCUMULATE)) == 0, ZQ_EINVAL);
+  ZQ_REQUIRE(workspace_bytes >= moe_layout(d_model, d_ff, n_sel).total, ZQ_EINVAL);
+  ZQ_REQUIRE(al(gu_bank, 4) && al(down_bank, 4) && al(router_w, 4) && al(norm_w, 16) &&
+                 al(x, 16) && al(shared_gate, 4) && al(xn_out, 16) && al(logits_out, 4) &&
+                 al(ids, 4) && al(wts, 4) && al(workspace, kAlign) && al(y, 4),
+             ZQ_EALIGN);
+  const int dc = check_current_device();
+  if (dc != ZQ_OK) return dc;
+  const hipStream_t s = S(stream);
+  const MoeRoute route{logits_out, n_routed, top_k, shared_gate};
+  // the fused norm + router DMMV launch, then the block on xn
+  zq::DmmvF32Args r{};
+  r.w = static_cast<const uint8_t *>(router_w);
+  r.x = x;
+  r.y = logits_out;
+  r.norm_w = norm_w;
+  r.eps = eps;
+  r.xn_out = xn_out;
+  r.rows = n_routed;
+  r.k = static_cast<int32_t>(d_model);
+  r.nb = static_cast<int32_t>(d_model / 32);
+  const int rc = zq::launch_dmmv_f32x(ZQ_Q8_0, r, s);
+  if (rc != ZQ_OK) return rc;
+  return moe_ffn_run(wtype, gu_bank, gu_stride_bytes, down_bank, down_stride_bytes, n_experts,
+                     d_model, d_ff, ids, wts, n_sel, xn_out, workspace, y, flags, nullptr, &route,
+                     s);
+}
+
 int zq_gemm_prefill(int wtype, const void *w, int64_t n, int64_t k, const int8_t *qx,
                     const float *dx, const int32_t *sx, int64_t m, float *y, uint32_t flags,
                     void *stream) {

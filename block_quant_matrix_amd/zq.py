@@ -44,6 +44,8 @@ SIGNATURES = {
     "zq_dmmv_tokens": (_INT, [_INT, _P, _I64, _I64, _P, _P, _P, _I32, _P, _U32, _P]),
     "zq_dmmv_f32": (_INT, [_INT, _P, _I64, _I64, _P, _P, _U32, _P, _P, _P, _P]),
     "zq_dmmv_float": (_INT, [_INT, _P, _I64, _I64, _P, _P, _U32, _P]),
+    "zq_moe_ffn_norm_route": (_INT, [_INT, _P, _I64, _P, _I64, _I64, _I64, _I64, _P, _P, ctypes.c_float, _P,
+                                     _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P, _U32, _P]),
     "zq_dmmv_k_f32": (_INT, [_INT, _P, _I64, _I64, _P, _P, _U32, _P, _P, _P, _P]),
     "zq_dmmv_tokens_f32": (_INT, [_INT, _P, _I64, _I64, _P, _I32, _P, _P, _P, _P, _U32, _P]),
     "zq_dmmv_isums": (_INT, [_INT, _P, _I64, _I64, _P, _P, _P, _P]),
@@ -196,6 +198,16 @@ def zq_dmmv_f32(wtype, w, rows, k, x, y, flags=0, qx_out=None, dx_out=None, sx_o
                 stream=None):
     return _call("zq_dmmv_f32", wtype, ptr(w), rows, k, ptr(x), ptr(y), flags, ptr(qx_out),
                  ptr(dx_out), ptr(sx_out), _stream(stream))
+
+
+def zq_moe_ffn_norm_route(wtype, gu_bank, gu_stride, down_bank, down_stride, n_experts, d_model,
+                          d_ff, router_w, norm_w, eps, x, n_routed, top_k, shared_gate, xn_out,
+                          logits_out, ids, wts, workspace, workspace_bytes, y, flags=0,
+                          stream=None):
+    return _call("zq_moe_ffn_norm_route", wtype, ptr(gu_bank), gu_stride, ptr(down_bank),
+                 down_stride, n_experts, d_model, d_ff, ptr(router_w), ptr(norm_w), eps, ptr(x),
+                 n_routed, top_k, ptr(shared_gate), ptr(xn_out), ptr(logits_out), ptr(ids),
+                 ptr(wts), ptr(workspace), workspace_bytes, ptr(y), flags, _stream(stream))
 
 
 def zq_dmmv_k_f32(wtype, w, rows, k, x, y, flags=0, qx_out=None, dx_out=None, sx_out=None,

@@ -474,6 +474,32 @@ int zq_moe_ffn_tokens(int wtype, const void *gu_bank, int64_t gu_stride_bytes,
                       int32_t *ids, float *wts, void *workspace, size_t workspace_bytes, float *y,
                       uint32_t flags, void *stream);
 
+/* One decode layer's MoE block from the un-normalized state, the layer's
+ * RMS norm and router matvec included:
+ *   xn = rms_norm(x) * norm_w, as zq_rms_norm_dmmv_f32 computes it,
+ *   logits = R . Q(xn), R the Q8_0 router matrix [n_routed][d_model],
+ *   then the routed MoE block of zq_moe_ffn_route on xn and those logits:
+ *   y (+)= sum_s wts[s] * down_{ids[s]}(Q(swiglu(gate||up_{ids[s]}(Q(xn))))).
+ * The per-token order of "Bringing ZINC to NVIDIA: a CUDA backend, because
+ * WSL2 only speaks CUDA", section "The roadmap: from 70 to a coherent token"
+ * (router DMMV, softmax_topk, expert gate/up, swiglu, expert down with the
+ * weighted accumulate, residual accumulate), in three launches:
+ * zq_rms_norm_dmmv_f32, then zq_moe_ffn_route.  (Running the norm and the
+ * router inside every gate/up workgroup instead, two launches, measured
+ * slower at the pages' widths: each of the 144 workgroups then reads the
+ * whole 278 KB router.)  xn_out [d_model] (16-byte aligned) and logits_out
+ * [n_routed] receive xn and the logits (always written); xn_out must not
+ * overlap x.  Other arguments as zq_moe_ffn_route; norm_w [d_model] 16-byte
+ * aligned, eps finite and >= 0, d_model <= 16384; y may be x itself (the
+ * residual add, with ZQ_ACCUMULATE). */
+int zq_moe_ffn_norm_route(int wtype, const void *gu_bank, int64_t gu_stride_bytes,
+                          const void *down_bank, int64_t down_stride_bytes, int64_t n_experts,
+                          int64_t d_model, int64_t d_ff, const void *router_w,
+                          const float *norm_w, float eps, const float *x, int32_t n_routed,
+                          int32_t top_k, const float *shared_gate, float *xn_out,
+                          float *logits_out, int32_t *ids, float *wts, void *workspace,
+                          size_t workspace_bytes, float *y, uint32_t flags, void *stream);
+
 /* Batched prefill GEMM (all prompt tokens through one tiled GEMM rather than
  * one matvec per token: "RTX 5090: Batched Prefill & CUDA Graphs in ZINC", opening answer
  * and section "Prefill -- a correction, and a better GEMM"; the dequant is

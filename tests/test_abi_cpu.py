@@ -418,6 +418,38 @@ def test_moe_ffn_tokens_argument_errors():
         assert rc(g=None, n_experts=128) == zq.ZQ_EDEVICE   # valid: the device check is last
 
 
+def test_moe_ffn_norm_route_argument_errors():
+    L = zq.lib()
+    ws = L.zq_moe_ffn_workspace_bytes(2048, 512, 9)
+    gs, ds = 2 * 512 * 64 * 18, 2048 * 16 * 18
+
+    def rc(wtype=4, n_experts=129, d_model=2048, d_ff=512, router=B, norm=C, eps=1e-6, x=D,
+           n_routed=128, top_k=8, g=C + 0x1000, xn=A + 0x1000, lg=A + 0x2000, ids=A + 0x3000,
+           wts=A + 0x4000, work=A + 0x8000, wsb=ws, y=D, flags=1):
+        return L.zq_moe_ffn_norm_route(wtype, A, gs, B, ds, n_experts, d_model, d_ff, router, norm,
+                                       eps, x, n_routed, top_k, g, xn, lg, ids, wts, work, wsb, y,
+                                       flags, None)
+
+    assert rc(wtype=13) == zq.ZQ_EINVAL
+    assert rc(top_k=0) == zq.ZQ_EINVAL
+    assert rc(n_routed=7) == zq.ZQ_EINVAL
+    assert rc(n_experts=128) == zq.ZQ_EINVAL           # no room for the shared expert
+    assert rc(eps=float("nan")) == zq.ZQ_EINVAL
+    assert rc(eps=-1.0) == zq.ZQ_EINVAL
+    assert rc(d_model=16384 + 32) == zq.ZQ_EINVAL
+    assert rc(wsb=ws - 1) == zq.ZQ_EINVAL
+    assert rc(flags=2) == zq.ZQ_EINVAL
+    assert rc(router=None) == zq.ZQ_ENULL
+    assert rc(norm=None) == zq.ZQ_ENULL
+    assert rc(xn=None) == zq.ZQ_ENULL                  # xn and the logits are always written
+    assert rc(lg=None) == zq.ZQ_ENULL
+    assert rc(norm=C + 4) == zq.ZQ_EALIGN
+    assert rc(xn=A + 0x1004) == zq.ZQ_EALIGN
+    assert rc(x=D + 4, y=D + 4) == zq.ZQ_EALIGN
+    if not os.path.exists("/dev/kfd"):
+        assert rc() == zq.ZQ_EDEVICE
+
+
 def test_float_dmmv_argument_errors():
     L = zq.lib()
 
