@@ -541,11 +541,12 @@ class MoeWorkload(Workload):
 
 class MoeTokWorkload(Workload):
     """Eight tokens, each with its own router logits, through the MoE block of
-    128 + 1 Q4_0 experts in one call (zq_moe_ffn_tokens: plan, gate/up,
-    down, weighted sums; each distinct expert's weights read once).  The
-    step's bytes are the distinct experts the step's routing touches (counted
-    from the GPU's own expert lists) plus the activations and outputs."""
-    dominant_name = "several-token MoE block (plan + gate/up + down + sum launches)"
+    128 + 1 Q4_0 experts in one call (zq_moe_ffn_tokens: route, gate/up,
+    down with the weighted sums; each distinct expert's weights read once).
+    The step's bytes are the distinct experts the step's routing touches
+    (counted from the GPU's own expert lists) plus the activations and
+    outputs."""
+    dominant_name = "several-token MoE block (route + gate/up + down launches)"
     step_is_dominant = True
     steps = 1000
     warmup = 50
