@@ -1175,6 +1175,25 @@ def read_ceiling(torch, zq, nbytes=1 << 30, K=20):
     return nbytes / (ms * 1e-3) / 1e9
 
 
+def read_floor(torch, zq, nbytes, ncopy, K):
+    """The same-size read floor (ms per launch): K back-to-back launches of the
+    library's read probe over nbytes, rotating over ncopy distinct buffers as
+    the workload's weights rotate, so that each launch reads from HBM; the
+    time any kernel needs to read that many bytes, its launch included."""
+    n16 = nbytes // 16 * 16
+    buf = torch.empty(ncopy * n16, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    base = buf.data_ptr()
+    fn = lambda i: zq.zq_read_probe(base + (i % ncopy) * n16, n16, sink)
+    for i in range(3):
+        fn(i)
+    h_ms = host_launch_ms(fn, torch, n=5)
+    ms = timed(torch, fn, K, h_ms)
+    del buf
+    return n16, ms
+
+
 def gpu_clocks():
     """Current shader and memory clocks from rocm-smi (best effort)."""
     try:
@@ -1376,6 +1395,16 @@ def main():
                            "note": "live streaming read of 1 GiB by zq_read_probe"}
     if runit == "GB/s":
         out["read_ceiling"]["frac_of_ceiling"] = round(ach / ceiling, 4)
+    if runit == "GB/s" and per_launch <= (64 << 20):
+        # at sizes where a launch's fixed cost weighs, the time a read-only
+        # kernel needs for the same bytes, measured the same way
+        nf, ms_rf = read_floor(torch, zq, per_launch, w.ncopy, min(K, 2000))
+        out["read_floor"] = {"bytes": nf, "us_per_launch": round(ms_rf * 1e3, 3),
+                             "GBs": round(nf / (ms_rf * 1e-3) / 1e9, 1),
+                             "kernel_us_per_launch": round(ms_kernel * 1e3, 3),
+                             "frac_of_floor_rate": round(ms_rf / ms_kernel, 4),
+                             "note": "zq_read_probe over the dominant kernel's algorithmic "
+                                     "bytes, rotating over the workload's weight copies"}
     out["empty_launch_us"] = round(ms_floor * 1e3, 3)
     out["clocks"] = {"before": clocks_before, "after": clocks_after}
     if args.workload == 2:

@@ -15,8 +15,8 @@ constexpr int kProbeMaxBlocks = 8192;
 
 }  // namespace
 
-// Each workgroup reads one contiguous chunk with 16-byte loads, kProbeUnroll
-// per lane in flight, and folds them with XOR.  The one store is taken only
+// Each workgroup reads one contiguous chunk with 16-byte loads (kProbeUnroll
+// per lane in flight on large buffers) and folds them with XOR.  The one store is taken only
 // when the fold equals a fixed word, which the compiler cannot rule out, so
 // every load stays and (almost) nothing is written.
 __global__ __launch_bounds__(kProbeThreads) void read_probe_kernel(const uint4 *__restrict__ p,
@@ -44,8 +44,10 @@ __global__ __launch_bounds__(kProbeThreads) void read_probe_kernel(const uint4 *
 int launch_read_probe(const void *buf, int64_t bytes, uint32_t *sink, hipStream_t stream) {
   const int64_t n16 = bytes / 16;
   if (n16 == 0) return ZQ_OK;
-  const int64_t per_block = static_cast<int64_t>(kProbeThreads) * kProbeUnroll;
-  int64_t blocks = (n16 + per_block - 1) / per_block;
+  // a load per lane per workgroup where that keeps the grid within
+  // kProbeMaxBlocks (small buffers: as many waves as the DMMV launches
+  // over the same bytes), else kProbeUnroll loads per lane in flight
+  int64_t blocks = (n16 + kProbeThreads - 1) / kProbeThreads;
   if (blocks > kProbeMaxBlocks) blocks = kProbeMaxBlocks;
   const int64_t chunk = (n16 + blocks - 1) / blocks;
   blocks = (n16 + chunk - 1) / chunk;
