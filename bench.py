@@ -108,6 +108,7 @@ class Workload:
     steps = 2000
     warmup = 50
     step_is_dominant = False  # a step is exactly one launch of the dominant kernel
+    step_is_graph = False     # a step is itself one graph replay (timed eagerly)
     dtype = "int8"            # the arithmetic the dominant kernel's products run in
 
     def setup(self, torch, zq, inputs):
@@ -852,6 +853,7 @@ class DecodeChainWorkload(Workload):
     eager time of the same chain is reported beside it."""
     dominant_name = "moe_gate_up_kernel (router folded in)"
     bound = "hbm"
+    step_is_graph = True
     # each layer's gate/up launch is the 128-expert block's, shape for shape:
     # its counted traffic is that workload's
     traffic_workload = "q4_0_moe_128e_top8_shared_2048x512"
@@ -1146,18 +1148,44 @@ def host_launch_ms(fn, torch, n=50):
     return el
 
 
-def timed(torch, fn, K, h_ms):
-    """ms per call of K back-to-back calls of fn(i), enqueued behind a GPU
-    blocker and bracketed by two events on the launch stream."""
+def timed(torch, fn, K, h_ms, graph=True):
+    """ms per call of K back-to-back calls of fn(i) between two events on the
+    launch stream.
+
+    With graph (the default) the K calls are captured once as a HIP graph and
+    the timed region is one replay of it: the host then submits a node in well
+    under a microsecond, so a kernel shorter than a Python-level call is not
+    paced by the host.  The replay waits behind a GPU blocker longer than its
+    own submission.  Without graph the K calls are made eagerly behind a
+    blocker sized from h_ms (for steps that are themselves graph replays)."""
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    gpu_blocker(torch, 1.5 * h_ms * K + 5)
+    if not graph:
+        gpu_blocker(torch, 1.5 * h_ms * K + 5)
+        e0.record()
+        for i in range(K):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(g, stream=side):
+        for i in range(K):
+            fn(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g.replay()  # untimed: the replay's own host cost sizes the blocker
+    h_replay = (time.perf_counter() - t0) * 1e3
+    torch.cuda.synchronize()
+    gpu_blocker(torch, 1.5 * h_replay + 5)
     e0.record()
-    for i in range(K):
-        fn(i)
+    g.replay()
     e1.record()
     torch.cuda.synchronize()
+    del g
     return e0.elapsed_time(e1) / K
 
 
@@ -1277,7 +1305,7 @@ def measure(w, torch, K, W):
         w.step(i)
     torch.cuda.synchronize()
     h_ms = host_launch_ms(w.step, torch)
-    ms_per_step = timed(torch, w.step, K, h_ms)
+    ms_per_step = timed(torch, w.step, K, h_ms, graph=not w.step_is_graph)
     if w.step_is_dominant:
         ms_kernel = ms_per_step
     else:

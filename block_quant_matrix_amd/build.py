@@ -29,6 +29,11 @@ FLAGS = [
     "-Wno-unused-command-line-argument",
     # no packed fp32 instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # kernel-argument preloading: a kernel's leading scalar arguments (up to
+    # 14 SGPRs) arrive in SGPRs at wave start instead of one memory round
+    # trip later; each kernel passes the fields its first loads need that way
+    # (headline 4096 x 4096 Q4_0 DMMV: 3.74 -> 3.43 us per launch)
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
 ]
 
 # Per-source extra flags.  The GEMM's MFMA results feed VALU code right away;

@@ -131,7 +131,12 @@ __device__ __forceinline__ void block_pass(const DmmvArgs &a, const uint8_t *wb,
 }
 
 template <int WT, int LPR, int BPL, int RB, int MODE>
-__global__ __launch_bounds__(256) void dmmv_kernel(const DmmvArgs a) {
+__global__ __launch_bounds__(256) void dmmv_kernel(const uint8_t *w, const int8_t *qx,
+                                                   const float *dx, int64_t rows,
+                                                   int64_t row_bytes, int64_t n_groups, int32_t nb,
+                                                   int32_t id_base, const DmmvArgs a_in) {
+  DmmvArgs a = a_in;
+  dmmv_hot(a, w, qx, dx, rows, row_bytes, n_groups, nb, id_base);
   constexpr int S = 64 / LPR;
   const int lane = static_cast<int>(threadIdx.x & 63);
   const int j = lane & (LPR - 1);
@@ -264,7 +269,7 @@ int launch_one(const DmmvArgs &a, hipStream_t stream, unsigned grid_y) {
   const int64_t blocks = (b.n_groups + 3) / 4;  // 4 waves per 256-thread block
   const unsigned grid_x = static_cast<unsigned>(blocks < 1048576 ? blocks : 1048576);
   hipLaunchKernelGGL((dmmv_kernel<WT, LPR, BPL, RB, MODE>), dim3(grid_x, grid_y), dim3(256), 0,
-                     stream, b);
+                     stream, ZQ_DMMV_HOT(b), b);
   ZQ_LAUNCH_CHECK();
   return ZQ_OK;
 }

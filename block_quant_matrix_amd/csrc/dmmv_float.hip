@@ -37,7 +37,17 @@ typedef __attribute__((address_space(1))) const u32x4 g_u32x4;
 }  // namespace
 
 template <int WT, int RB, int U>
-__global__ __launch_bounds__(kFloatThreads) void dmmv_float_kernel(const FloatDmmvArgs a) {
+__global__ __launch_bounds__(kFloatThreads) void dmmv_float_kernel(const uint8_t *w, const float *x,
+                                                                   int64_t rows, int64_t row_bytes,
+                                                                   int32_t k,
+                                                                   const FloatDmmvArgs a_in) {
+  // leading scalars: preloaded kernel arguments (as dmmv_hot in zq_internal.h)
+  FloatDmmvArgs a = a_in;
+  a.w = w;
+  a.x = x;
+  a.rows = rows;
+  a.row_bytes = row_bytes;
+  a.k = k;
   extern __shared__ __attribute__((aligned(16))) float xs[];
   constexpr int EPC = WT == ZQ_F16 ? 8 : 4;   // weights per 16-byte chunk
   const int nch = a.k / EPC;
@@ -141,7 +151,7 @@ int launch_fl(const FloatDmmvArgs &a, hipStream_t stream) {
   if (grid > kFloatMaxGrid) grid = kFloatMaxGrid;
   const size_t lds = static_cast<size_t>(a.k) * 4;
   hipLaunchKernelGGL((dmmv_float_kernel<WT, RB, U>), dim3(static_cast<unsigned>(grid)),
-                     dim3(kFloatThreads), lds, stream, a);
+                     dim3(kFloatThreads), lds, stream, a.w, a.x, a.rows, a.row_bytes, a.k, a);
   ZQ_LAUNCH_CHECK();
   return ZQ_OK;
 }

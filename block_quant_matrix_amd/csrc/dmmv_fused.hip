@@ -28,22 +28,24 @@
 namespace zq {
 
 template <int WT, int LPR, int BPL, int RB, int WPB, bool ARGMAX, bool NORM>
-__global__ __launch_bounds__(64 * WPB) void dmmv_f32x_kernel(const DmmvF32Args a) {
+__global__ __launch_bounds__(64 * WPB) void dmmv_f32x_kernel(const uint8_t *__restrict__ w, const float *__restrict__ x,
+                                                        int64_t rows, int64_t row_bytes, int32_t k,
+                                                        int32_t nb, const DmmvF32Args a) {
   constexpr int S = 64 / LPR;
   constexpr int NW = Blk<WT>::NW;
   constexpr int BB = Blk<WT>::BYTES;
   constexpr int T = 64 * WPB;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   int8_t *lq = reinterpret_cast<int8_t *>(smem);                   // [k]
-  float *ld = reinterpret_cast<float *>(smem + a.k);               // [nb]
-  int32_t *ls8 = reinterpret_cast<int32_t *>(smem + a.k + 4 * a.nb);  // [nb]
+  float *ld = reinterpret_cast<float *>(smem + k);               // [nb]
+  int32_t *ls8 = reinterpret_cast<int32_t *>(smem + k + 4 * nb);  // [nb]
 
   const int tid = static_cast<int>(threadIdx.x);
   const int lane = tid & 63;
   const int wv = tid >> 6;
   const int j = lane & (LPR - 1);
   const int slot = lane / LPR;
-  const int64_t n_groups = (a.rows + RB * S - 1) / (RB * S);
+  const int64_t n_groups = (rows + RB * S - 1) / (RB * S);
   const int64_t gstride = static_cast<int64_t>(gridDim.x) * WPB;
   int64_t grp = static_cast<int64_t>(blockIdx.x) * WPB + wv;   // first row group of this wave
   int64_t row0 = grp * (RB * S);
@@ -54,10 +56,10 @@ __global__ __launch_bounds__(64 * WPB) void dmmv_f32x_kernel(const DmmvF32Args a
   int qb = tid >> 1;
   float xv[16];
   float nw[16];  // the norm weights of the same elements (NORM)
-  if (qb < a.nb) {
+  if (qb < nb) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const float4 v = *reinterpret_cast<const float4 *>(a.x + qb * 32 + g * 16 + 4 * u);
+      const float4 v = *reinterpret_cast<const float4 *>(x + qb * 32 + g * 16 + 4 * u);
       xv[4 * u] = v.x; xv[4 * u + 1] = v.y; xv[4 * u + 2] = v.z; xv[4 * u + 3] = v.w;
       if constexpr (NORM) {
         const float4 q = *reinterpret_cast<const float4 *>(a.norm_w + qb * 32 + g * 16 + 4 * u);
@@ -72,12 +74,12 @@ __global__ __launch_bounds__(64 * WPB) void dmmv_f32x_kernel(const DmmvF32Args a
 #pragma unroll
   for (int t = 0; t < RB; ++t) {
     int64_t row = row0 + t * S + slot;
-    row = row < a.rows ? row : a.rows - 1;
+    row = row < rows ? row : rows - 1;
 #pragma unroll
     for (int i = 0; i < BPL; ++i) {
       int b = j + LPR * i;
-      b = b < a.nb ? b : a.nb - 1;
-      off[t][i] = load_window<WT>(a.w + row * a.row_bytes + static_cast<int64_t>(b) * BB, win[t][i]);
+      b = b < nb ? b : nb - 1;
+      off[t][i] = load_window<WT>(w + row * row_bytes + static_cast<int64_t>(b) * BB, win[t][i]);
     }
   }
 
@@ -86,14 +88,14 @@ __global__ __launch_bounds__(64 * WPB) void dmmv_f32x_kernel(const DmmvF32Args a
   float inv = 1.0f;
   if constexpr (NORM) {
     float ss = 0.0f;
-    for (int b = tid >> 1; b < a.nb; b += T / 2) {
+    for (int b = tid >> 1; b < nb; b += T / 2) {
       if (b == (tid >> 1)) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) ss = __builtin_fmaf(xv[e], xv[e], ss);
       } else {  // further blocks when k > 16*T
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const float4 v = *reinterpret_cast<const float4 *>(a.x + b * 32 + g * 16 + 4 * u);
+          const float4 v = *reinterpret_cast<const float4 *>(x + b * 32 + g * 16 + 4 * u);
           ss = __builtin_fmaf(v.x, v.x, ss);
           ss = __builtin_fmaf(v.y, v.y, ss);
           ss = __builtin_fmaf(v.z, v.z, ss);
@@ -102,18 +104,18 @@ __global__ __launch_bounds__(64 * WPB) void dmmv_f32x_kernel(const DmmvF32Args a
       }
     }
     ss = block_sum_all<WPB>(ss);
-    inv = rms_inv(ss, a.k, a.eps);
+    inv = rms_inv(ss, k, a.eps);
   }
 
   // 3. quantize the activation into LDS.  Two lanes per block keep the
   //    per-block work (the two IEEE divisions) on as few waves as possible.
   const bool out = (blockIdx.x == 0) && (a.qx_out != nullptr);
   const bool xn_out = NORM && (blockIdx.x == 0) && (a.xn_out != nullptr);
-  for (; qb < a.nb; qb += T / 2) {
+  for (; qb < nb; qb += T / 2) {
     if (qb != (tid >> 1)) {  // further blocks when k > 16*T (not for k <= 16384)
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const float4 v = *reinterpret_cast<const float4 *>(a.x + qb * 32 + g * 16 + 4 * u);
+        const float4 v = *reinterpret_cast<const float4 *>(x + qb * 32 + g * 16 + 4 * u);
         xv[4 * u] = v.x; xv[4 * u + 1] = v.y; xv[4 * u + 2] = v.z; xv[4 * u + 3] = v.w;
         if constexpr (NORM) {
           const float4 q = *reinterpret_cast<const float4 *>(a.norm_w + qb * 32 + g * 16 + 4 * u);
@@ -159,7 +161,7 @@ __global__ __launch_bounds__(64 * WPB) void dmmv_f32x_kernel(const DmmvF32Args a
 #pragma unroll
   for (int i = 0; i < BPL; ++i) {
     const int b = j + LPR * i;
-    if (b < a.nb) {
+    if (b < nb) {
       const u32x4 v0 = *reinterpret_cast<const u32x4 *>(lq + 32 * b);
       const u32x4 v1 = *reinterpret_cast<const u32x4 *>(lq + 32 * b + 16);
       xq[i][0] = v0.x; xq[i][1] = v0.y; xq[i][2] = v0.z; xq[i][3] = v0.w;
@@ -203,7 +205,7 @@ __global__ __launch_bounds__(64 * WPB) void dmmv_f32x_kernel(const DmmvF32Args a
 #pragma unroll
       for (int m = 0; m < R::NOUT; ++m) {
         const int64_t row = row0 + static_cast<int64_t>(R::rowstep(m, lane)) * S + slot;
-        if (row < a.rows) {
+        if (row < rows) {
           float *yp = a.y + row;
           const float v = (a.flags & ZQ_ACCUMULATE) ? *yp + res[m] : res[m];
           *yp = v;
@@ -222,12 +224,12 @@ __global__ __launch_bounds__(64 * WPB) void dmmv_f32x_kernel(const DmmvF32Args a
 #pragma unroll
     for (int t = 0; t < RB; ++t) {
       int64_t row = row0 + t * S + slot;
-      row = row < a.rows ? row : a.rows - 1;
+      row = row < rows ? row : rows - 1;
 #pragma unroll
       for (int i = 0; i < BPL; ++i) {
         int b = j + LPR * i;
-        b = b < a.nb ? b : a.nb - 1;
-        off[t][i] = load_window<WT>(a.w + row * a.row_bytes + static_cast<int64_t>(b) * BB, win[t][i]);
+        b = b < nb ? b : nb - 1;
+        off[t][i] = load_window<WT>(w + row * row_bytes + static_cast<int64_t>(b) * BB, win[t][i]);
       }
     }
   }
@@ -255,20 +257,20 @@ int launch_f(const DmmvF32Args &a, hipStream_t stream) {
   if (a.part) {
     if (a.norm_w)
       hipLaunchKernelGGL((dmmv_f32x_kernel<WT, LPR, BPL, RB, WPB, true, true>), gd, dim3(64 * WPB),
-                         lds, stream, a);
+                         lds, stream, a.w, a.x, a.rows, a.row_bytes, a.k, a.nb, a);
     else
       hipLaunchKernelGGL((dmmv_f32x_kernel<WT, LPR, BPL, RB, WPB, true, false>), gd, dim3(64 * WPB),
-                         lds, stream, a);
+                         lds, stream, a.w, a.x, a.rows, a.row_bytes, a.k, a.nb, a);
     ZQ_LAUNCH_CHECK();
     if (a.out_idx) return launch_argmax_final(a.part, static_cast<int>(gd.x), a.out_idx, stream);
     return ZQ_OK;
   }
   if (a.norm_w)
     hipLaunchKernelGGL((dmmv_f32x_kernel<WT, LPR, BPL, RB, WPB, false, true>), gd, dim3(64 * WPB),
-                       lds, stream, a);
+                       lds, stream, a.w, a.x, a.rows, a.row_bytes, a.k, a.nb, a);
   else
     hipLaunchKernelGGL((dmmv_f32x_kernel<WT, LPR, BPL, RB, WPB, false, false>), gd, dim3(64 * WPB),
-                       lds, stream, a);
+                       lds, stream, a.w, a.x, a.rows, a.row_bytes, a.k, a.nb, a);
   ZQ_LAUNCH_CHECK();
   return ZQ_OK;
 }

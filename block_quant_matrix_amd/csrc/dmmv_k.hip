@@ -124,7 +124,10 @@ __device__ __forceinline__ void finish_act(KUnitAct (&act)[BPL], const DmmvArgs 
 // e_s = ids[s] - id_base, skipped (and reported) outside [0, n_experts).
 template <int WT, int LPR, int BPL, int RB, int MODE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void dmmv_k_kernel(
-    const DmmvArgs a) {
+    const uint8_t *w, const int8_t *qx, const float *dx, int64_t rows, int64_t row_bytes,
+    int64_t n_groups, int32_t nb, int32_t id_base, const DmmvArgs a_in) {
+  DmmvArgs a = a_in;
+  dmmv_hot(a, w, qx, dx, rows, row_bytes, n_groups, nb, id_base);
   constexpr bool ISUMS = MODE == MODE_ISUMS;
   constexpr int S = 64 / LPR;
   constexpr int NWD = KQ<WT>::NWD;
@@ -257,7 +260,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 // wts[n_sel].
 template <int WT, int LPR, int RB, int SWT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void dmmv_k_wsum_kernel(
-    const DmmvArgs a) {
+    const int32_t *ids, const float *wts, const int8_t *qx, const float *dx, int64_t n_groups,
+    int32_t n_sel, int32_t nb, int32_t id_base, const DmmvArgs a_in) {
+  // leading scalars: preloaded kernel arguments (as dmmv_hot)
+  DmmvArgs a = a_in;
+  a.ids = ids;
+  a.wts = wts;
+  a.qx = qx;
+  a.dx = dx;
+  a.n_groups = n_groups;
+  a.n_sel = n_sel;
+  a.nb = nb;
+  a.id_base = id_base;
   constexpr int SL = 64 / LPR;
   constexpr int NWD = KQ<WT>::NWD;
   constexpr int LS = 64 / RB;                       // shared: lanes per row step
@@ -378,7 +392,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 // activation.
 template <int WT, int LPR, int BPL, int RB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void dmmv_k_f32_kernel(
-    const DmmvKF32Args a) {
+    const uint8_t *w, const float *x, int64_t rows, int64_t row_bytes, int64_t n_groups,
+    int32_t k, int32_t nb, const DmmvKF32Args a_in) {
+  // leading scalars: preloaded kernel arguments (as dmmv_hot)
+  DmmvKF32Args a = a_in;
+  a.w = w;
+  a.x = x;
+  a.rows = rows;
+  a.row_bytes = row_bytes;
+  a.n_groups = n_groups;
+  a.k = k;
+  a.nb = nb;
   constexpr int S = 64 / LPR;
   constexpr int NWD = KQ<WT>::NWD;
   constexpr int T = 256;
@@ -531,7 +555,8 @@ int launch_wsum1(DmmvArgs a, hipStream_t stream) {
   a.n_groups = (a.rows + RB - 1) / RB;
   const int64_t blocks = (a.n_groups + 3) / 4;
   const unsigned grid = static_cast<unsigned>(blocks < 1048576 ? blocks : 1048576);
-  hipLaunchKernelGGL((dmmv_k_wsum_kernel<WT, LPR, RB, SWT>), dim3(grid), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((dmmv_k_wsum_kernel<WT, LPR, RB, SWT>), dim3(grid), dim3(256), 0, stream, a.ids,
+                     a.wts, a.qx, a.dx, a.n_groups, a.n_sel, a.nb, a.id_base, a);
   ZQ_LAUNCH_CHECK();
   return ZQ_OK;
 }
@@ -614,7 +639,7 @@ int launch_k1(DmmvArgs a, hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>(blocks < 1048576 ? blocks : 1048576);
   const unsigned gy = MODE == MODE_GATHER ? static_cast<unsigned>(a.n_sel) : 1u;
   hipLaunchKernelGGL((dmmv_k_kernel<WT, LPR, BPL, RB, MODE>), dim3(grid, gy), dim3(256), 0, stream,
-                     a);
+                     ZQ_DMMV_HOT(a), a);
   ZQ_LAUNCH_CHECK();
   return ZQ_OK;
 }
@@ -675,7 +700,8 @@ int launch_kf1(DmmvKF32Args a, hipStream_t stream) {
   const int64_t blocks = (a.n_groups + 3) / 4;
   const unsigned grid = static_cast<unsigned>(blocks < 4096 ? blocks : 4096);
   const size_t lds = static_cast<size_t>(a.k) + 8 * static_cast<size_t>(a.nb);
-  hipLaunchKernelGGL((dmmv_k_f32_kernel<WT, LPR, BPL, RB>), dim3(grid), dim3(256), lds, stream, a);
+  hipLaunchKernelGGL((dmmv_k_f32_kernel<WT, LPR, BPL, RB>), dim3(grid), dim3(256), lds, stream, a.w,
+                     a.x, a.rows, a.row_bytes, a.n_groups, a.k, a.nb, a);
   ZQ_LAUNCH_CHECK();
   return ZQ_OK;
 }

@@ -78,7 +78,21 @@ __device__ __forceinline__ void tok_finish_act(TokAct<T, BPL> &A, const DmmvTokA
 }
 
 template <int WT, int LPR, int BPL, int RB, int T>
-__global__ __launch_bounds__(256) void dmmv_tok_kernel(const DmmvTokArgs a) {
+__global__ __launch_bounds__(256) void dmmv_tok_kernel(const uint8_t *w, const int8_t *qx,
+                                                       const float *dx, int64_t rows,
+                                                       int64_t row_bytes, int64_t n_groups,
+                                                       int32_t k, int32_t nb,
+                                                       const DmmvTokArgs a_in) {
+  // leading scalars: preloaded kernel arguments (as dmmv_hot in zq_internal.h)
+  DmmvTokArgs a = a_in;
+  a.w = w;
+  a.qx = qx;
+  a.dx = dx;
+  a.rows = rows;
+  a.row_bytes = row_bytes;
+  a.n_groups = n_groups;
+  a.k = k;
+  a.nb = nb;
   constexpr int S = 64 / LPR;
   constexpr int NW = Blk<WT>::NW;
   constexpr int BB = Blk<WT>::BYTES;
@@ -226,8 +240,30 @@ __device__ __forceinline__ void swap32_i(int32_t &a, int32_t &b) {
   b = static_cast<int32_t>(r[1]);
 }
 
+// The matrix-core and tile kernels' leading scalars: preloaded kernel
+// arguments (as dmmv_hot in zq_internal.h).
+__device__ __forceinline__ void tok_tile_hot(DmmvTokArgs &a, const uint8_t *w, const int8_t *qx,
+                                             const float *dx, int64_t rows, int64_t row_bytes,
+                                             int32_t k, int32_t nb, int32_t n_tok) {
+  a.w = w;
+  a.qx = qx;
+  a.dx = dx;
+  a.rows = rows;
+  a.row_bytes = row_bytes;
+  a.k = k;
+  a.nb = nb;
+  a.n_tok = n_tok;
+}
+
 template <int WT>
-__global__ __launch_bounds__(64 * kTmWaves) void dmmv_tok_mfma_kernel(const DmmvTokArgs a) {
+__global__ __launch_bounds__(64 * kTmWaves) void dmmv_tok_mfma_kernel(const uint8_t *w,
+                                                                     const int8_t *qx,
+                                                                     const float *dx, int64_t rows,
+                                                                     int64_t row_bytes, int32_t k,
+                                                                     int32_t nb, int32_t n_tok,
+                                                                     const DmmvTokArgs a_in) {
+  DmmvTokArgs a = a_in;
+  tok_tile_hot(a, w, qx, dx, rows, row_bytes, k, nb, n_tok);
   constexpr int NW = Blk<WT>::NW;
   constexpr int BB = Blk<WT>::BYTES;
   constexpr int KC = Tm<WT>::KC;
@@ -383,7 +419,8 @@ int launch_tm(const DmmvTokArgs &a, hipStream_t stream) {
   const int64_t rows_per_wg = 16 * kTmWaves;
   const unsigned grid = static_cast<unsigned>((a.rows + rows_per_wg - 1) / rows_per_wg);
   hipLaunchKernelGGL((dmmv_tok_mfma_kernel<WT>), dim3(grid), dim3(64 * kTmWaves),
-                     tm_lds_bytes(WT, a.n_tok, a.k), stream, a);
+                     tm_lds_bytes(WT, a.n_tok, a.k), stream, a.w, a.qx, a.dx, a.rows, a.row_bytes,
+                     a.k, a.nb, a.n_tok, a);
   ZQ_LAUNCH_CHECK();
   return ZQ_OK;
 }
@@ -423,7 +460,14 @@ struct TtLayout {
 };
 
 template <int WT, int BPL>
-__global__ __launch_bounds__(64 * kTtWaves) void dmmv_tok_tile_kernel(const DmmvTokArgs a) {
+__global__ __launch_bounds__(64 * kTtWaves) void dmmv_tok_tile_kernel(const uint8_t *w,
+                                                                     const int8_t *qx,
+                                                                     const float *dx, int64_t rows,
+                                                                     int64_t row_bytes, int32_t k,
+                                                                     int32_t nb, int32_t n_tok,
+                                                                     const DmmvTokArgs a_in) {
+  DmmvTokArgs a = a_in;
+  tok_tile_hot(a, w, qx, dx, rows, row_bytes, k, nb, n_tok);
   constexpr int NW = Blk<WT>::NW;
   constexpr int BB = Blk<WT>::BYTES;
   constexpr int KC = Tm<WT>::KC;
@@ -574,9 +618,11 @@ int launch_tt(const DmmvTokArgs &a, hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>((a.rows + 15) / 16);
   const size_t lds = static_cast<size_t>(TtLayout(WT, a.nb).bytes);
   if (a.nb <= 64)
-    hipLaunchKernelGGL((dmmv_tok_tile_kernel<WT, 1>), dim3(grid), dim3(64 * kTtWaves), lds, stream, a);
+    hipLaunchKernelGGL((dmmv_tok_tile_kernel<WT, 1>), dim3(grid), dim3(64 * kTtWaves), lds, stream,
+                       a.w, a.qx, a.dx, a.rows, a.row_bytes, a.k, a.nb, a.n_tok, a);
   else
-    hipLaunchKernelGGL((dmmv_tok_tile_kernel<WT, 2>), dim3(grid), dim3(64 * kTtWaves), lds, stream, a);
+    hipLaunchKernelGGL((dmmv_tok_tile_kernel<WT, 2>), dim3(grid), dim3(64 * kTtWaves), lds, stream,
+                       a.w, a.qx, a.dx, a.rows, a.row_bytes, a.k, a.nb, a.n_tok, a);
   ZQ_LAUNCH_CHECK();
   return ZQ_OK;
 }
@@ -613,7 +659,8 @@ int launch_t1(DmmvTokArgs a, hipStream_t stream) {
   a.n_groups = (a.rows + RB * S - 1) / (RB * S);
   const int64_t blocks = (a.n_groups + 3) / 4;
   const unsigned grid = static_cast<unsigned>(blocks < 1048576 ? blocks : 1048576);
-  hipLaunchKernelGGL((dmmv_tok_kernel<WT, LPR, BPL, RB, T>), dim3(grid), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((dmmv_tok_kernel<WT, LPR, BPL, RB, T>), dim3(grid), dim3(256), 0, stream, a.w,
+                     a.qx, a.dx, a.rows, a.row_bytes, a.n_groups, a.k, a.nb, a);
   ZQ_LAUNCH_CHECK();
   return ZQ_OK;
 }

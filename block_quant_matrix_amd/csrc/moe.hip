@@ -30,6 +30,21 @@ namespace zq {
 // workgroup of T threads per (selected expert, 32-wide block of the FFN
 // width), computing 32 gate rows and the 32 matching up rows.
 
+// The gate/up kernels' leading scalars: the fields their first loads need,
+// as preloaded kernel arguments (see dmmv_hot in zq_internal.h).
+__device__ __forceinline__ void gu_hot(MoeGateUpArgs &a, const float *x, const float *logits,
+                                       const int32_t *ids, int32_t nb, int32_t k, int32_t n_routed,
+                                       int32_t top_k, int32_t id_base) {
+  a.x = x;
+  a.logits = logits;
+  a.ids = ids;
+  a.nb = nb;
+  a.k = k;
+  a.n_routed = n_routed;
+  a.top_k = top_k;
+  a.id_base = id_base;
+}
+
 // Loads of the fp32 activation for this thread's first 32-element block (two
 // lanes per block, 16 elements each); issued before anything is waited on.
 __device__ __forceinline__ void gu_load_x(const MoeGateUpArgs &a, int nb, int tid,
@@ -349,7 +364,12 @@ __device__ __forceinline__ void gu_run(const MoeGateUpArgs &a, int nb, const uin
 // The gate/up pass over one bank (Rows: GuBlockRows or GuKRows): grid
 // (d_ff / 32, n_sel), 1024 threads.
 template <class Rows, bool ROUTED>
-__global__ __launch_bounds__(1024) void moe_gate_up_kernel(const MoeGateUpArgs a) {
+__global__ __launch_bounds__(1024) void moe_gate_up_kernel(const float *x, const float *logits,
+                                                           const int32_t *ids, int32_t nb, int32_t k,
+                                                           int32_t n_routed, int32_t top_k,
+                                                           int32_t id_base, const MoeGateUpArgs a_in) {
+  MoeGateUpArgs a = a_in;
+  gu_hot(a, x, logits, ids, nb, k, n_routed, top_k, id_base);
   constexpr int T = 1024;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const GuLds L(smem, a.k, a.nb);
@@ -378,7 +398,13 @@ __global__ __launch_bounds__(1024) void moe_gate_up_kernel(const MoeGateUpArgs a
 // is a compile-time constant here, which keeps the scalar registers of the
 // two layouts within bounds.
 template <class Rows, class SRows, int NB>
-__global__ __launch_bounds__(1024) void moe_gate_up_mix_kernel(const MoeGateUpArgs a) {
+__global__ __launch_bounds__(1024) void moe_gate_up_mix_kernel(const float *x, const float *logits,
+                                                               const int32_t *ids, int32_t nb,
+                                                               int32_t k, int32_t n_routed,
+                                                               int32_t top_k, int32_t id_base,
+                                                               const MoeGateUpArgs a_in) {
+  MoeGateUpArgs a = a_in;
+  gu_hot(a, x, logits, ids, nb, k, n_routed, top_k, id_base);
   constexpr int T = 1024;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const GuLds L(smem, 32 * NB, NB);
@@ -401,6 +427,20 @@ __global__ __launch_bounds__(1024) void moe_gate_up_mix_kernel(const MoeGateUpAr
 
 // ---------------------------------------------------------------- down -----
 
+// The down kernels' leading scalars (preloaded kernel arguments, as dmmv_hot).
+__device__ __forceinline__ void dn_hot(MoeDownArgs &a, const int32_t *ids, const int8_t *qx,
+                                       const float *dx, int64_t x_stride, int64_t rows,
+                                       int32_t n_sel, int32_t nb, int32_t id_base) {
+  a.ids = ids;
+  a.qx = qx;
+  a.dx = dx;
+  a.x_stride = x_stride;
+  a.rows = rows;
+  a.n_sel = n_sel;
+  a.nb = nb;
+  a.id_base = id_base;
+}
+
 // The weighted sum over experts with the experts spread over the lanes (as
 // the K-quant form in dmmv_k.hip): lane = (slot, part), LPS lanes per slot
 // and BPL blocks per lane (k = 32 * nb <= 32 * LPS * BPL), 64 / LPS slots
@@ -410,7 +450,10 @@ __global__ __launch_bounds__(1024) void moe_gate_up_mix_kernel(const MoeGateUpAr
 // id is out of range contributes nothing and reports ZQ_ERANGE.
 template <int WT, int LPS, int BPL, int RB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void moe_down_wsum_kernel(
-    const MoeDownArgs a) {
+    const int32_t *ids, const int8_t *qx, const float *dx, int64_t x_stride, int64_t rows,
+    int32_t n_sel, int32_t nb, int32_t id_base, const MoeDownArgs a_in) {
+  MoeDownArgs a = a_in;
+  dn_hot(a, ids, qx, dx, x_stride, rows, n_sel, nb, id_base);
   constexpr int SL = 64 / LPS;
   constexpr int NW = Blk<WT>::NW;
   constexpr int BB = Blk<WT>::BYTES;
@@ -518,7 +561,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 constexpr int kDownMaxSel = 16;  // experts whose windows are in flight at once
 
 template <int WT, int LPR, int BPL, int WPB>
-__global__ __launch_bounds__(64 * WPB) void moe_down_kernel(const MoeDownArgs a) {
+__global__ __launch_bounds__(64 * WPB) void moe_down_kernel(const int32_t *ids, const int8_t *qx,
+                                                           const float *dx, int64_t x_stride,
+                                                           int64_t rows, int32_t n_sel, int32_t nb,
+                                                           int32_t id_base, const MoeDownArgs a_in) {
+  MoeDownArgs a = a_in;
+  dn_hot(a, ids, qx, dx, x_stride, rows, n_sel, nb, id_base);
   constexpr int S = 64 / LPR;
   constexpr int NW = Blk<WT>::NW;
   constexpr int BB = Blk<WT>::BYTES;
@@ -681,9 +729,11 @@ template <class Rows>
 int launch_gu(const MoeGateUpArgs &a, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(a.d_ff / 32), static_cast<unsigned>(a.n_sel));
   if (a.logits)
-    hipLaunchKernelGGL((moe_gate_up_kernel<Rows, true>), grid, dim3(1024), gu_lds(a), stream, a);
+    hipLaunchKernelGGL((moe_gate_up_kernel<Rows, true>), grid, dim3(1024), gu_lds(a), stream,
+                       a.x, a.logits, a.ids, a.nb, a.k, a.n_routed, a.top_k, a.id_base, a);
   else
-    hipLaunchKernelGGL((moe_gate_up_kernel<Rows, false>), grid, dim3(1024), gu_lds(a), stream, a);
+    hipLaunchKernelGGL((moe_gate_up_kernel<Rows, false>), grid, dim3(1024), gu_lds(a), stream,
+                       a.x, a.logits, a.ids, a.nb, a.k, a.n_routed, a.top_k, a.id_base, a);
   ZQ_LAUNCH_CHECK();
   return ZQ_OK;
 }
@@ -714,7 +764,7 @@ template <class Rows, class SRows, int NB>
 int launch_gu_mix(const MoeGateUpArgs &a, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(a.d_ff / 32), static_cast<unsigned>(a.top_k + 1));
   hipLaunchKernelGGL((moe_gate_up_mix_kernel<Rows, SRows, NB>), grid, dim3(1024), gu_lds(a), stream,
-                     a);
+                     a.x, a.logits, a.ids, a.nb, a.k, a.n_routed, a.top_k, a.id_base, a);
   ZQ_LAUNCH_CHECK();
   return ZQ_OK;
 }
@@ -763,7 +813,8 @@ int launch_dn(const MoeDownArgs &a, hipStream_t stream) {
   const int64_t rows_per_wg = WPB * S;
   const unsigned grid = static_cast<unsigned>((a.rows + rows_per_wg - 1) / rows_per_wg);
   hipLaunchKernelGGL((moe_down_kernel<WT, LPR, BPL, WPB>), dim3(grid), dim3(64 * WPB),
-                     moe_down_lds_bytes(a.n_sel, a.k), stream, a);
+                     moe_down_lds_bytes(a.n_sel, a.k), stream, a.ids, a.qx, a.dx, a.x_stride, a.rows,
+                     a.n_sel, a.nb, a.id_base, a);
   ZQ_LAUNCH_CHECK();
   return ZQ_OK;
 }
@@ -773,7 +824,8 @@ int launch_dn_wsum1(const MoeDownArgs &a, hipStream_t stream) {
   const int64_t n_groups = (a.rows + RB - 1) / RB;
   const int64_t blocks = (n_groups + 3) / 4;
   const unsigned grid = static_cast<unsigned>(blocks < 1048576 ? blocks : 1048576);
-  hipLaunchKernelGGL((moe_down_wsum_kernel<WT, LPS, BPL, RB>), dim3(grid), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((moe_down_wsum_kernel<WT, LPS, BPL, RB>), dim3(grid), dim3(256), 0, stream,
+                     a.ids, a.qx, a.dx, a.x_stride, a.rows, a.n_sel, a.nb, a.id_base, a);
   ZQ_LAUNCH_CHECK();
   return ZQ_OK;
 }
@@ -895,7 +947,21 @@ int launch_moe_down(int wtype, MoeDownArgs a, hipStream_t stream) {
 
 // Route (blockIdx.y 0) and quantize (blockIdx.y 1) token blockIdx.x.
 template <int P>
-__global__ __launch_bounds__(1024) void moe_tok_route_kernel(const MoeTokArgs a) {
+__global__ __launch_bounds__(1024) void moe_tok_route_kernel(const float *logits, const float *x,
+                                                             const float *shared_gate, int8_t *qx,
+                                                             float *dx, int32_t n_routed,
+                                                             int32_t top_k, int32_t d_model,
+                                                             const MoeTokArgs a_in) {
+  // leading scalars: preloaded kernel arguments (as dmmv_hot)
+  MoeTokArgs a = a_in;
+  a.logits = logits;
+  a.x = x;
+  a.shared_gate = shared_gate;
+  a.qx = qx;
+  a.dx = dx;
+  a.n_routed = n_routed;
+  a.top_k = top_k;
+  a.d_model = d_model;
   const int t = static_cast<int>(blockIdx.x);
   const int tid = static_cast<int>(threadIdx.x);
   if (blockIdx.y == 1) {
@@ -936,10 +1002,19 @@ __global__ __launch_bounds__(1024) void moe_tok_route_kernel(const MoeTokArgs a)
 // 0): the member slots of first-use slot j in token order, then -1; all -1
 // for a slot that is not a first use.
 template <class Rows>
-__global__ __launch_bounds__(1024) void moe_gate_up_tok_kernel(const MoeGateUpArgs a, int32_t *mem,
-                                                               int n_tok, int n_sel_tok,
+__global__ __launch_bounds__(1024) void moe_gate_up_tok_kernel(const int32_t *ids, int32_t *mem,
                                                                const int8_t *qx, const float *dx,
+                                                               int32_t n_sel, int32_t k_in,
+                                                               int32_t nb_in, int n_tok,
+                                                               int n_sel_tok,
+                                                               const MoeGateUpArgs a_in,
                                                                const int32_t *sx) {
+  // leading scalars: preloaded kernel arguments (as dmmv_hot)
+  MoeGateUpArgs a = a_in;
+  a.ids = ids;
+  a.n_sel = n_sel;
+  a.k = k_in;
+  a.nb = nb_in;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int32_t lid[kTokMax * 65];
   __shared__ int32_t mslot[kTokMax];
@@ -1032,7 +1107,20 @@ constexpr int kDnTokLdsMax = 60 * 1024;
 // down: LPR = k / 32 lanes per row (one block each), RB row steps of 64 /
 // LPR rows: 8 rows per workgroup of 16 waves.  grid (rows / 8).
 template <int WT, int LPR, int RB, bool STAGE>
-__global__ __launch_bounds__(1024) void moe_down_tok_kernel(const MoeDownTokArgs a) {
+__global__ __launch_bounds__(1024) void moe_down_tok_kernel(int32_t *mem_in, const int32_t *ids,
+                                                            const float *wts, int64_t rows,
+                                                            int32_t n_sel, int32_t k_in,
+                                                            int32_t nb_in,
+                                                            const MoeDownTokArgs a_in) {
+  // leading scalars: preloaded kernel arguments (as dmmv_hot)
+  MoeDownTokArgs a = a_in;
+  a.mem = mem_in;
+  a.ids = ids;
+  a.wts = wts;
+  a.rows = rows;
+  a.n_sel = n_sel;
+  a.k = k_in;
+  a.nb = nb_in;
   constexpr int S = 64 / LPR;
   constexpr int ROWS = RB * S;
   constexpr int NW = Blk<WT>::NW;
@@ -1204,7 +1292,8 @@ namespace {
 template <int P>
 void launch_tok_route(const MoeTokArgs &p, hipStream_t stream) {
   hipLaunchKernelGGL((moe_tok_route_kernel<P>), dim3(static_cast<unsigned>(p.n_tok), 2),
-                     dim3(1024), 0, stream, p);
+                     dim3(1024), 0, stream, p.logits, p.x, p.shared_gate, p.qx, p.dx, p.n_routed,
+                     p.top_k, p.d_model, p);
 }
 
 template <class Rows>
@@ -1213,8 +1302,8 @@ int launch_gu_tok(const MoeGateUpArgs &a, int32_t *mem, const MoeTokArgs &p, int
   const dim3 grid(static_cast<unsigned>(a.d_ff / 32), static_cast<unsigned>(a.n_sel));
   const int c = p.n_tok;  // at most this many members per expert
   const size_t lds = static_cast<size_t>(c) * (a.k + 8 * a.nb + 64 * 4);
-  hipLaunchKernelGGL((moe_gate_up_tok_kernel<Rows>), grid, dim3(1024), lds, stream, a, mem,
-                     p.n_tok, n_sel_tok, p.qx, p.dx, p.sx);
+  hipLaunchKernelGGL((moe_gate_up_tok_kernel<Rows>), grid, dim3(1024), lds, stream, a.ids, mem,
+                     p.qx, p.dx, a.n_sel, a.k, a.nb, p.n_tok, n_sel_tok, a, p.sx);
   ZQ_LAUNCH_CHECK();
   return ZQ_OK;
 }
@@ -1235,11 +1324,13 @@ int launch_dn_tok(const MoeDownTokArgs &a, hipStream_t stream) {
   const DnTokLds staged(a.n_sel, a.k, ROWS, true);
   if (staged.total <= kDnTokLdsMax) {
     hipLaunchKernelGGL((moe_down_tok_kernel<WT, LPR, RB, true>), grid, dim3(1024),
-                       static_cast<size_t>(staged.total), stream, a);
+                       static_cast<size_t>(staged.total), stream, a.mem, a.ids, a.wts, a.rows,
+                       a.n_sel, a.k, a.nb, a);
   } else {
     const DnTokLds plain(a.n_sel, a.k, ROWS, false);
     hipLaunchKernelGGL((moe_down_tok_kernel<WT, LPR, RB, false>), grid, dim3(1024),
-                       static_cast<size_t>(plain.total), stream, a);
+                       static_cast<size_t>(plain.total), stream, a.mem, a.ids, a.wts, a.rows,
+                       a.n_sel, a.k, a.nb, a);
   }
   ZQ_LAUNCH_CHECK();
   return ZQ_OK;

@@ -13,8 +13,16 @@
 
 namespace zq {
 
-__global__ __launch_bounds__(256) void rms_norm_quantize_kernel(const RmsNormArgs a) {
+__global__ __launch_bounds__(256) void rms_norm_quantize_kernel(const float *x_in, const float *w,
+                                                                int64_t x_stride, int32_t k,
+                                                                const RmsNormArgs a_in) {
 #pragma clang fp contract(off)
+  // leading scalars: preloaded kernel arguments (as dmmv_hot in zq_internal.h)
+  RmsNormArgs a = a_in;
+  a.x = x_in;
+  a.w = w;
+  a.x_stride = x_stride;
+  a.k = k;
   const int64_t t = blockIdx.x;
   const int tid = static_cast<int>(threadIdx.x);
   const float *x = a.x + t * a.x_stride;
@@ -53,7 +61,7 @@ __global__ __launch_bounds__(256) void rms_norm_quantize_kernel(const RmsNormArg
 int launch_rms_norm_quantize(RmsNormArgs a, hipStream_t stream) {
   if (a.n_tok == 0) return ZQ_OK;
   hipLaunchKernelGGL(rms_norm_quantize_kernel, dim3(static_cast<unsigned>(a.n_tok)), dim3(256), 0,
-                     stream, a);
+                     stream, a.x, a.w, a.x_stride, a.k, a);
   ZQ_LAUNCH_CHECK();
   return ZQ_OK;
 }

@@ -37,6 +37,32 @@ struct DmmvArgs {
   int64_t row_bytes2;   // filled in by the launcher
 };
 
+// Kernel arguments in SGPRs.  The library is built with kernel-argument
+// preloading: a kernel's leading scalar arguments (up to 14 SGPRs' worth)
+// are in SGPRs when its waves start, while a struct argument stays in the
+// argument segment in memory, a round trip away, and every load whose
+// address needs one of its fields waits for that round trip.  So a kernel
+// takes the fields its first loads need as leading scalars and the whole
+// struct after them, and puts the scalars back into its local copy of the
+// struct, so the rest of its code reads one struct.  Pointers come first and
+// 32-bit fields last, so that no SGPR is lost to alignment.
+//
+// DmmvArgs for the single-matrix and gathered forms: the weights, the
+// activation and the row groups.
+__device__ __forceinline__ void dmmv_hot(DmmvArgs &a, const uint8_t *w, const int8_t *qx,
+                                         const float *dx, int64_t rows, int64_t row_bytes,
+                                         int64_t n_groups, int32_t nb, int32_t id_base) {
+  a.w = w;
+  a.qx = qx;
+  a.dx = dx;
+  a.rows = rows;
+  a.row_bytes = row_bytes;
+  a.n_groups = n_groups;
+  a.nb = nb;
+  a.id_base = id_base;
+}
+#define ZQ_DMMV_HOT(a) (a).w, (a).qx, (a).dx, (a).rows, (a).row_bytes, (a).n_groups, (a).nb, (a).id_base
+
 // The multi-token DMMV: T <= 8 activations, token t at qx + t*k,
 // dx / sx + t*nb, output rows at y + t*rows.
 struct DmmvTokArgs {
