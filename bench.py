@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--workload", type=int, default=2, choices=list(range(1, 17)))
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle leg (no parity check, no CPU timing)")
+    ap.add_argument("--no-clocks", action="store_true",
+                    help="skip the rocm-smi clock readings (a child process; for profiler runs)")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the LM-head measurement the default line carries")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -1380,9 +1382,9 @@ def main():
     if not args.no_cpu_baseline:
         cpu, parity = oracle_leg(w, args.cpu_seconds)
 
-    clocks_before = gpu_clocks()
+    clocks_before = None if args.no_clocks else gpu_clocks()
     ms_per_step, ms_kernel = measure(w, torch, K, W)
-    clocks_after = gpu_clocks()
+    clocks_after = None if args.no_clocks else gpu_clocks()
 
     # what a launch of any kernel costs before it reads a byte: K back-to-back
     # launches of an empty kernel (torch's spin kernel with a zero count) on
