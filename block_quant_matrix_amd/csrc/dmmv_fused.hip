@@ -275,15 +275,26 @@ int launch_f(const DmmvF32Args &a, hipStream_t stream) {
   return ZQ_OK;
 }
 
-// Small matrices (decode): 16 waves per workgroup, one row step per wave, so
-// the activation is quantized once per 16*S rows and every SIMD holds four
-// waves.  Large matrices: four waves per workgroup, several row steps each.
+// Small matrices (decode, up to 256 workgroups): one workgroup quantizes the
+// activation for all of its rows.  With one or two blocks per lane, 8 waves
+// of two row steps each (16 rows of 4096, 3.33 us against 3.40 for 16 waves
+// of one row and 3.47 for 4 waves of four; 2048 x 2048: 2.38 against 2.56),
+// except for a few hundred rows without the norm, which keep 16 waves of one
+// row step (64 x 2048 Q8_0: 2.28 against 2.37 us; with the norm, whose sum
+// of squares is reduced over the workgroup, 8 waves are faster there too:
+// the 128-row router of a 40-layer chain, 685 against 703 us per token).
+// With more blocks per lane, 8 waves of one row step (2048 x 8192: 4.28
+// against 4.83 for two).  Large matrices: four waves per workgroup, several
+// row steps each.
 template <int WT, int LPR, int BPL>
 int launch_fs(const DmmvF32Args &a, hipStream_t stream) {
   constexpr int S = 64 / LPR;
-  // 1024-thread groups leave 128 VGPRs per wave: wide layouts use 8 waves.
-  constexpr int WPB = BPL <= 2 ? 16 : 8;
-  if (a.rows <= static_cast<int64_t>(256) * WPB * S) return launch_f<WT, LPR, BPL, 1, WPB>(a, stream);
+  constexpr int RBS = BPL <= 2 ? 2 : 1;
+  if constexpr (BPL <= 2) {
+    if (a.rows <= 256 && a.norm_w == nullptr) return launch_f<WT, LPR, BPL, 1, 16>(a, stream);
+  }
+  if (a.rows <= static_cast<int64_t>(256) * 8 * RBS * S)
+    return launch_f<WT, LPR, BPL, RBS, 8>(a, stream);
   // windows held per lane: RB * BPL
   if constexpr (BPL == 1) return launch_f<WT, LPR, BPL, 8, 4>(a, stream);
   if constexpr (BPL == 2) return launch_f<WT, LPR, BPL, 4, 4>(a, stream);
