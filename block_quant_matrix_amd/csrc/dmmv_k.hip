@@ -383,15 +383,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 
 // ---------------------------------------------------------------------------
 // fp32-input form: y (+)= W . Q(x) in one launch, Q the activation quantizer
-// of quantize.hip.  Each workgroup (4 waves) issues its loads of x (two lanes
+// of quantize.hip.  Each workgroup (WPB waves) issues its loads of x (two lanes
 // per 32-element block), then every lane issues its first row group's weight
 // units, then x is quantized into LDS (codes, scales, code sums) while the
 // weights stream in; after one barrier each lane takes its units' codes from
 // LDS and the row groups proceed as in dmmv_k_kernel (one pass over the
 // units: k <= 64 * LPR * BPL).  Workgroup 0 can also store the quantized
 // activation.
-template <int WT, int LPR, int BPL, int RB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void dmmv_k_f32_kernel(
+template <int WT, int LPR, int BPL, int RB, int WPB>
+__global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(1, 2))) void dmmv_k_f32_kernel(
     const uint8_t *w, const float *x, int64_t rows, int64_t row_bytes, int64_t n_groups,
     int32_t k, int32_t nb, const DmmvKF32Args a_in) {
   // leading scalars: preloaded kernel arguments (as dmmv_hot)
@@ -405,7 +405,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   a.nb = nb;
   constexpr int S = 64 / LPR;
   constexpr int NWD = KQ<WT>::NWD;
-  constexpr int T = 256;
+  constexpr int T = 64 * WPB;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   int8_t *lq = reinterpret_cast<int8_t *>(smem);                       // [k]
   float *ld = reinterpret_cast<float *>(smem + a.k);                   // [nb]
@@ -457,7 +457,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   // 3. quantize x into LDS
   const bool out = blockIdx.x == 0 && a.qx_out != nullptr;
   for (; qb < a.nb; qb += T / 2) {
-    if (qb != (tid >> 1)) {  // further blocks when k > 4096
+    if (qb != (tid >> 1)) {  // further blocks when k > 16 * T
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const float4 f = *reinterpret_cast<const float4 *>(a.x + qb * 32 + g * 16 + 4 * u);
@@ -693,32 +693,43 @@ int launch_type(int mode, DmmvArgs a, hipStream_t stream) {
 
 // The fp32-input form: the plain layout and row steps, a workgroup's
 // activation staged once (grids beyond 4096 workgroups loop over groups).
-template <int WT, int LPR, int BPL, int RB>
+template <int WT, int LPR, int BPL, int RB, int WPB = 4>
 int launch_kf1(DmmvKF32Args a, hipStream_t stream) {
   constexpr int S = 64 / LPR;
   a.n_groups = (a.rows + RB * S - 1) / (RB * S);
-  const int64_t blocks = (a.n_groups + 3) / 4;
+  const int64_t blocks = (a.n_groups + WPB - 1) / WPB;
   const unsigned grid = static_cast<unsigned>(blocks < 4096 ? blocks : 4096);
   const size_t lds = static_cast<size_t>(a.k) + 8 * static_cast<size_t>(a.nb);
-  hipLaunchKernelGGL((dmmv_k_f32_kernel<WT, LPR, BPL, RB>), dim3(grid), dim3(256), lds, stream, a.w,
-                     a.x, a.rows, a.row_bytes, a.n_groups, a.k, a.nb, a);
+  hipLaunchKernelGGL((dmmv_k_f32_kernel<WT, LPR, BPL, RB, WPB>), dim3(grid), dim3(64 * WPB), lds,
+                     stream, a.w, a.x, a.rows, a.row_bytes, a.n_groups, a.k, a.nb, a);
   ZQ_LAUNCH_CHECK();
   return ZQ_OK;
 }
 
-template <int WT, int LPR, int BPL>
+template <int WT, int LPR, int BPL, int WPB>
 int launch_kfrb(int rb, const DmmvKF32Args &a, hipStream_t stream) {
   constexpr int CAP = 96 / (KQ<WT>::NWD * BPL);
   if constexpr (CAP >= 8) {
-    if (rb >= 8) return launch_kf1<WT, LPR, BPL, 8>(a, stream);
+    if (rb >= 8) return launch_kf1<WT, LPR, BPL, 8, WPB>(a, stream);
   }
   if constexpr (CAP >= 4) {
-    if (rb >= 4) return launch_kf1<WT, LPR, BPL, 4>(a, stream);
+    if (rb >= 4) return launch_kf1<WT, LPR, BPL, 4, WPB>(a, stream);
   }
   if constexpr (CAP >= 2) {
-    if (rb >= 2) return launch_kf1<WT, LPR, BPL, 2>(a, stream);
+    if (rb >= 2) return launch_kf1<WT, LPR, BPL, 2, WPB>(a, stream);
   }
-  return launch_kf1<WT, LPR, BPL, 1>(a, stream);
+  return launch_kf1<WT, LPR, BPL, 1, WPB>(a, stream);
+}
+
+template <int WT, int WPB>
+int launch_kf_shape(const KShape &sh, int rb, const DmmvKF32Args &a, hipStream_t stream) {
+  if (sh.lpr == 8) return launch_kfrb<WT, 8, 1, WPB>(rb, a, stream);
+  if (sh.lpr == 16 && sh.bpl == 1) return launch_kfrb<WT, 16, 1, WPB>(rb, a, stream);
+  if (sh.lpr == 16) return launch_kfrb<WT, 16, 5, WPB>(rb, a, stream);
+  if (sh.lpr == 32) return launch_kfrb<WT, 32, 1, WPB>(rb, a, stream);
+  if (sh.bpl == 1) return launch_kfrb<WT, 64, 1, WPB>(rb, a, stream);
+  if (sh.bpl == 2) return launch_kfrb<WT, 64, 2, WPB>(rb, a, stream);
+  return launch_kfrb<WT, 64, 4, WPB>(rb, a, stream);
 }
 
 template <int WT>
@@ -728,13 +739,16 @@ int launch_kf_type(DmmvKF32Args a, hipStream_t stream) {
   const KShape sh = choose_kshape(nu);
   if (static_cast<int64_t>(sh.lpr) * sh.bpl < nu) return ZQ_EINVAL;  // one pass only
   const int rb = choose_krb<WT>(sh, a.rows, MODE_PLAIN, 1);
-  if (sh.lpr == 8) return launch_kfrb<WT, 8, 1>(rb, a, stream);
-  if (sh.lpr == 16 && sh.bpl == 1) return launch_kfrb<WT, 16, 1>(rb, a, stream);
-  if (sh.lpr == 16) return launch_kfrb<WT, 16, 5>(rb, a, stream);
-  if (sh.lpr == 32) return launch_kfrb<WT, 32, 1>(rb, a, stream);
-  if (sh.bpl == 1) return launch_kfrb<WT, 64, 1>(rb, a, stream);
-  if (sh.bpl == 2) return launch_kfrb<WT, 64, 2>(rb, a, stream);
-  return launch_kfrb<WT, 64, 4>(rb, a, stream);
+  // 8 waves per workgroup where the row groups still fill 256 workgroups
+  // (fewer workgroups quantize x, each stages it for twice the rows):
+  // 4096 x 4096 Q4_K / Q5_K / Q6_K 3.57 / 4.30 / 5.01 us against 4.08 /
+  // 4.51 / 5.44 with 4 waves, 4096 x 14336 Q4_K 11.1 against 12.9;
+  // below that (2048 x 2048: 128 workgroups) 4 waves (2.41 against 2.64).
+  // The LM-head shapes keep 4.
+  const int64_t groups = (a.rows + static_cast<int64_t>(rb) * (64 / sh.lpr) - 1) /
+                         (static_cast<int64_t>(rb) * (64 / sh.lpr));
+  if (a.rows <= 16384 && groups >= 8 * 256) return launch_kf_shape<WT, 8>(sh, rb, a, stream);
+  return launch_kf_shape<WT, 4>(sh, rb, a, stream);
 }
 
 }  // namespace
