@@ -284,8 +284,7 @@ int launch_f(const DmmvF32Args &a, hipStream_t stream) {
 // of squares is reduced over the workgroup, 8 waves are faster there too:
 // the 128-row router of a 40-layer chain, 685 against 703 us per token).
 // With more blocks per lane, 8 waves of one row step (2048 x 8192: 4.28
-// against 4.83 for two).  Large matrices: four waves per workgroup, several
-// row steps each.
+// against 4.83 for two).
 template <int WT, int LPR, int BPL>
 int launch_fs(const DmmvF32Args &a, hipStream_t stream) {
   constexpr int S = 64 / LPR;
@@ -295,8 +294,27 @@ int launch_fs(const DmmvF32Args &a, hipStream_t stream) {
   }
   if (a.rows <= static_cast<int64_t>(256) * 8 * RBS * S)
     return launch_f<WT, LPR, BPL, RBS, 8>(a, stream);
-  // windows held per lane: RB * BPL
-  if constexpr (BPL == 1) return launch_f<WT, LPR, BPL, 8, 4>(a, stream);
+  if (a.rows <= 16384) {
+    // Mid-size matrices: 8 waves per workgroup, row steps by blocks per lane
+    // (a sweep of 1/2/4/8 row steps x 4/8 waves; us per launch):
+    //   one block per lane, 4 row steps: 6144 x 2048 3.01 (4 waves of 8
+    //     steps: 3.35), 16384 x 2048 4.79 (5.05), 11008 x 2048 4.53 (4.78);
+    //   two blocks, 2 row steps up to 8192 rows, else 4: 8192 x 4096 4.94
+    //     (4 waves of 4: 5.14), 14336 x 4096 7.36 (8.16);
+    //   four or more, 2 row steps: 4096 x 8192 5.66 (4 waves: 6.82),
+    //     5120 x 5120 5.47 (6.78), 4096 x 14336 10.64 (12.46).
+    if constexpr (BPL == 1) return launch_f<WT, LPR, BPL, 4, 8>(a, stream);
+    if constexpr (BPL == 2) {
+      if (a.rows <= static_cast<int64_t>(8192) * S) return launch_f<WT, LPR, BPL, 2, 8>(a, stream);
+      return launch_f<WT, LPR, BPL, 4, 8>(a, stream);
+    }
+    return launch_f<WT, LPR, BPL, 2, 8>(a, stream);
+  }
+  // Large matrices (the LM head), windows held per lane RB * BPL.  One
+  // block per lane: 8 waves of 4 row steps (the 248 320 x 2048 LM head with
+  // argmax, Q4_0 50.3 us against 50.9 for 4 waves of 8, Q8_0 89.3 against
+  // 93.0); otherwise four waves of several row steps.
+  if constexpr (BPL == 1) return launch_f<WT, LPR, BPL, 4, 8>(a, stream);
   if constexpr (BPL == 2) return launch_f<WT, LPR, BPL, 4, 4>(a, stream);
   return launch_f<WT, LPR, BPL, 2, 4>(a, stream);
 }
