@@ -26,8 +26,6 @@ namespace zq {
 
 namespace {
 
-constexpr int kFloatThreads = 256;   // 4 waves per workgroup
-constexpr int kFloatWaves = kFloatThreads / 64;
 constexpr int kFloatMaxGrid = 4096;  // workgroups of a persistent launch
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
@@ -36,8 +34,8 @@ typedef __attribute__((address_space(1))) const u32x4 g_u32x4;
 
 }  // namespace
 
-template <int WT, int RB, int U>
-__global__ __launch_bounds__(kFloatThreads) void dmmv_float_kernel(const uint8_t *w, const float *x,
+template <int WT, int RB, int U, int WPB>
+__global__ __launch_bounds__(64 * WPB) void dmmv_float_kernel(const uint8_t *w, const float *x,
                                                                    int64_t rows, int64_t row_bytes,
                                                                    int32_t k,
                                                                    const FloatDmmvArgs a_in) {
@@ -54,8 +52,8 @@ __global__ __launch_bounds__(kFloatThreads) void dmmv_float_kernel(const uint8_t
   const int lane = static_cast<int>(threadIdx.x & 63);
   const int wave = static_cast<int>(threadIdx.x >> 6);
   const int64_t n_groups = (a.rows + RB - 1) / RB;
-  const int64_t wstride = static_cast<int64_t>(gridDim.x) * kFloatWaves;
-  int64_t grp = static_cast<int64_t>(blockIdx.x) * kFloatWaves + wave;
+  const int64_t wstride = static_cast<int64_t>(gridDim.x) * WPB;
+  int64_t grp = static_cast<int64_t>(blockIdx.x) * WPB + wave;
 
   // Request the first row group's weights before staging the activation.
   u32x4 wv[RB][U];
@@ -74,7 +72,7 @@ __global__ __launch_bounds__(kFloatThreads) void dmmv_float_kernel(const uint8_t
     }
   };
   if (grp < n_groups) load_group(grp, 0);
-  for (int i = static_cast<int>(threadIdx.x) * 4; i < a.k; i += kFloatThreads * 4)
+  for (int i = static_cast<int>(threadIdx.x) * 4; i < a.k; i += 64 * WPB * 4)
     *reinterpret_cast<u32x4 *>(xs + i) = *(const g_u32x4 *)(a.x + i);
   __syncthreads();
 
@@ -144,29 +142,39 @@ __global__ __launch_bounds__(kFloatThreads) void dmmv_float_kernel(const uint8_t
 
 namespace {
 
-template <int WT, int RB, int U>
+template <int WT, int RB, int U, int WPB = 4>
 int launch_fl(const FloatDmmvArgs &a, hipStream_t stream) {
   const int64_t n_groups = (a.rows + RB - 1) / RB;
-  int64_t grid = (n_groups + kFloatWaves - 1) / kFloatWaves;
+  int64_t grid = (n_groups + WPB - 1) / WPB;
   if (grid > kFloatMaxGrid) grid = kFloatMaxGrid;
   const size_t lds = static_cast<size_t>(a.k) * 4;
-  hipLaunchKernelGGL((dmmv_float_kernel<WT, RB, U>), dim3(static_cast<unsigned>(grid)),
-                     dim3(kFloatThreads), lds, stream, a.w, a.x, a.rows, a.row_bytes, a.k, a);
+  hipLaunchKernelGGL((dmmv_float_kernel<WT, RB, U, WPB>), dim3(static_cast<unsigned>(grid)),
+                     dim3(64 * WPB), lds, stream, a.w, a.x, a.rows, a.row_bytes, a.k, a);
   ZQ_LAUNCH_CHECK();
   return ZQ_OK;
 }
 
 // U 16-byte chunks per lane and step (at most 8, enough for one pass over
 // rows of up to 512 chunks) and RB rows per wave, RB * U <= 16 loads in
-// flight per lane.
+// flight per lane; 8 waves per workgroup, so each workgroup's staged
+// activation serves twice the rows of 4 waves.  From a sweep of 1/2/4 rows
+// x 4/8/16 waves (F16, us per launch):
+//   8 or more chunks per lane: one row per step, 4096 x 4096 8.02 (2 rows,
+//     4 waves: 8.35), 14336 x 4096 22.99 (23.84), 4096 x 14336 23.77
+//     (25.16), F32 4096 x 4096 13.27 (14.13);
+//   4 chunks per lane: 4 rows per step on the LM head, 248 320 x 2048
+//     156.6 (4 waves: 170.2), one row elsewhere, 2048 x 2048 3.94 (4.21).
 template <int WT>
 int launch_fw(const FloatDmmvArgs &a, hipStream_t stream) {
   constexpr int EPC = WT == ZQ_F16 ? 8 : 4;
   const int cpl = (a.k / EPC + 63) / 64;
   if (cpl <= 1) return launch_fl<WT, 4, 1>(a, stream);
   if (cpl <= 2) return launch_fl<WT, 4, 2>(a, stream);
-  if (cpl <= 4) return launch_fl<WT, 4, 4>(a, stream);
-  return launch_fl<WT, 2, 8>(a, stream);
+  if (cpl <= 4) {
+    if (a.rows >= 65536) return launch_fl<WT, 4, 4, 8>(a, stream);
+    return launch_fl<WT, 1, 4, 8>(a, stream);
+  }
+  return launch_fl<WT, 1, 8, 8>(a, stream);
 }
 
 }  // namespace
