@@ -27,17 +27,22 @@
 
 namespace zq {
 
+// w, x, rows, row_bytes, k and nb (the fields the first loads need) arrive
+// as leading scalars, preloaded into SGPRs (dmmv_hot in zq_internal.h); a
+// holds the rest.
 template <int WT, int LPR, int BPL, int RB, int WPB, bool ARGMAX, bool NORM>
-__global__ __launch_bounds__(64 * WPB) void dmmv_f32x_kernel(const uint8_t *__restrict__ w, const float *__restrict__ x,
-                                                        int64_t rows, int64_t row_bytes, int32_t k,
-                                                        int32_t nb, const DmmvF32Args a) {
+__global__ __launch_bounds__(64 * WPB) void dmmv_f32x_kernel(const uint8_t *__restrict__ w,
+                                                             const float *__restrict__ x,
+                                                             int64_t rows, int64_t row_bytes,
+                                                             int32_t k, int32_t nb,
+                                                             const DmmvF32Args a) {
   constexpr int S = 64 / LPR;
   constexpr int NW = Blk<WT>::NW;
   constexpr int BB = Blk<WT>::BYTES;
   constexpr int T = 64 * WPB;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  int8_t *lq = reinterpret_cast<int8_t *>(smem);                   // [k]
-  float *ld = reinterpret_cast<float *>(smem + k);               // [nb]
+  int8_t *lq = reinterpret_cast<int8_t *>(smem);                  // [k]
+  float *ld = reinterpret_cast<float *>(smem + k);                // [nb]
   int32_t *ls8 = reinterpret_cast<int32_t *>(smem + k + 4 * nb);  // [nb]
 
   const int tid = static_cast<int>(threadIdx.x);
