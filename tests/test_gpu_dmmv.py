@@ -372,6 +372,28 @@ def test_lmhead_fused_small(zq, wtype, rows, k):
     assert idx == oracle.argmax_f32(y)
 
 
+# Every branch of the fused DMMV's launch table: two blocks per lane past
+# 8192 rows (4 row steps), four and five blocks per lane at mid size (2 row
+# steps), and past 16384 rows two blocks (4 waves of 4 row steps) and eight
+# (4 waves of 2).  The rows against the oracle; the argmax form's rows equal
+# the plain form's bit for bit and its index is their exact argmax.
+@pytest.mark.parametrize("wtype", [Q4, Q8])
+@pytest.mark.parametrize("rows,k", [(10001, 4096), (3000, 8192), (5000, 5120), (20000, 4096),
+                                    (17000, 8192)])
+def test_dmmv_f32_launch_table(zq, wtype, rows, k):
+    seed = 91 + rows + k + wtype
+    w = inputs.gen_weights(wtype, rows, k, seed)
+    x = inputs.gen_activation(1, k, seed + 1)
+    wd = dev(w)
+    y_f = fused_rows(zq, wtype, wd, rows, k, x)
+    rq, rd, _ = oracle.quantize_act(x)
+    y_ref, S = oracle.dmmv(wtype, w, rows, k, rq, rd)
+    check_rows(y_f, y_ref, S, "launch table %d x %d" % (rows, k))
+    y, idx = lmhead_gpu(zq, wtype, wd, rows, k, x)
+    assert np.array_equal(y.view(np.uint32), y_f.view(np.uint32))
+    assert idx == oracle.argmax_f32(y)
+
+
 def test_lmhead_fused_ties_and_ends(zq):
     """Equal logits resolve to the lowest row, across workgroups too; the
     maximum at the first and at the last row is found."""

@@ -53,9 +53,11 @@ def check_codes(qx, dx, sx, x, what):
 
 
 # one pass of every lane layout (k = 256 .. 16384), ragged and single rows,
-# and the decode shape
+# the decode shape and both workgroup sizes (2048 x 2048 takes 4 waves per
+# workgroup, 4096 x 4096 and 8193 x 4096 take 8, the latter with a ragged
+# last row group)
 K_SHAPES = [(1, 256), (7, 512), (33, 2048), (300, 4096), (130, 5120), (9, 16384), (4099, 1024),
-            (4096, 4096)]
+            (4096, 4096), (2048, 2048), (8193, 4096)]
 
 
 @pytest.mark.parametrize("wt", KTYPES, ids=lambda t: NAME[t])

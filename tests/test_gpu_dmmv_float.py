@@ -24,10 +24,12 @@ def zq():
 
 # k from one 16-byte chunk to 16384, with chunk counts that end a pass of
 # 64 lanes part-way (4104 F16 = 513 chunks, 1000 F32 = 250 chunks); rows
-# ragged against the 2- and 4-row groups and the 4-wave workgroups.
+# ragged against the 1-, 2- and 4-row groups and the 4- and 8-wave
+# workgroups (70001 x 2048 takes the 4-row LM-head launch).
 @pytest.mark.parametrize("wt", [F16, F32])
 @pytest.mark.parametrize("rows,k", [(1, 8), (37, 64), (130, 512), (300, 2048), (4096, 4096),
-                                    (65, 4104), (7, 1000), (5, 16384), (4099, 1024)])
+                                    (65, 4104), (7, 1000), (5, 16384), (4099, 1024),
+                                    (70001, 2048)])
 def test_float_rows(zq, wt, rows, k):
     seed = 8000 + rows + k + wt
     w = inputs.gen_weights_float(wt, rows, k, seed)
