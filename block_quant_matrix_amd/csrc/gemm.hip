@@ -7,10 +7,10 @@
 // 16 (tokens) x 16 (weight rows) tile, so every block's integer sum leaves
 // the matrix core on its own and is rescaled in fp32 (convert, d_x*d_w,
 // FMA) before the next block; a K=64 form would add two blocks with
-// different scales.  The matrix cores finish a tile's block in about 20
-// cycles, the 12 VALU operations of its rescale take longer: the epilogue,
-// not the MFMA, bounds this kernel, so the layout below is chosen to keep
-// every other cost (LDS traffic, staging, idle CUs) under it.
+// different scales.  The matrix cores finish a tile's block in 16 cycles,
+// the 12 VALU operations of its rescale take 48: the epilogue, not the
+// MFMA, bounds this kernel, so the layout below is chosen to keep every
+// other cost (LDS traffic, staging, idle CUs) under it.
 //
 // Workgroup tile: 128 tokens x 80 weight rows, 8 waves.  For the prefill
 // shape (512 x 5120) that is 4 x 64 = 256 tiles, one per CU of the chip, so
@@ -20,7 +20,7 @@
 // through LDS at the end.
 //
 // Staging: every stage (4 blocks) is loaded from global memory into
-// registers one stage ahead and written to LDS double-buffered.  Activation
+// registers two stages ahead and written to LDS double-buffered.  Activation
 // codes are copied as they are; weight blocks are unpacked once per tile to
 // signed int8 (Q4_0: nib - 8 via (nib + 0x78) ^ 0x80 per byte).  In LDS a
 // row is laid out [lane group g][block][8 bytes], so one 16-byte read gives
@@ -52,7 +52,6 @@ constexpr int STAGE_BYTES = DW_OFF + BM * KB * 4;
 static_assert(BM * KB == NT, "one activation (row, block) per thread");
 static_assert(BN <= BM, "weight rows fit the staging grid");
 constexpr int RING = 2;                 // stages of global loads in flight
-constexpr bool kInterleave = false;     // MFMA / rescale interleaving hints
 static_assert(RING % 2 == 0, "the LDS double buffer alternates with the unrolled ring");
 // More than half of the CU's 160 KB, so a CU never holds two tiles while
 // another CU idles.
@@ -204,17 +203,6 @@ __device__ __forceinline__ void compute_stage(const GemmArgs &g, const uint8_t *
       for (int r = 0; r < 4; ++r)
         acc[ms][j][r] = __builtin_fmaf(dxs[r] * dw, static_cast<float>(is[t][r]), acc[ms][j][r]);
     }
-  }
-  if constexpr (!ISUMS && kInterleave) {
-    // Keep the matrix pipe busy while the VALU rescales older tiles: two
-    // MFMAs ahead, then one MFMA per tile's 12-op rescale.
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-#pragma unroll
-    for (int t = 0; t < NTILE - 2; ++t) {
-      __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);
   }
 }
 
