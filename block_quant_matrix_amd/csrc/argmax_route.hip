@@ -39,46 +39,6 @@ __global__ __launch_bounds__(kArgmaxThreads) void argmax_partial_kernel(const fl
 // LDS and the same wave reduction once more.
 constexpr int kFinalThreads = 1024;
 
-template <int CTRL>
-__device__ __forceinline__ int32_t dpp_i(int32_t v) {
-  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
-}
-
-__device__ __forceinline__ void take_best(float &v, int32_t &i, float ov, int32_t oi) {
-  if (beats(ov, oi, v, i)) {
-    v = ov;
-    i = oi;
-  }
-}
-
-// The best pair of the wave, in every lane.  "beats" is a total order on
-// the pairs (ties go to the lower index), so the order of the steps does not
-// change the result.
-__device__ __forceinline__ void wave_best_dpp(float &v, int32_t &i) {
-  take_best(v, i, dpp<DPP_QUAD_XOR1>(v), dpp_i<DPP_QUAD_XOR1>(i));
-  take_best(v, i, dpp<DPP_QUAD_XOR2>(v), dpp_i<DPP_QUAD_XOR2>(i));
-  take_best(v, i, dpp<DPP_ROW_HALF_MIRROR>(v), dpp_i<DPP_ROW_HALF_MIRROR>(i));
-  take_best(v, i, dpp<DPP_ROW_MIRROR>(v), dpp_i<DPP_ROW_MIRROR>(i));
-  // rows 0/1 and 2/3: each lane sees both rows of its 32-lane half
-  {
-    float a = v, b = v;
-    swap16(a, b);
-    float ai = __builtin_bit_cast(float, i), bi = ai;
-    swap16(ai, bi);
-    take_best(v, i, a, __builtin_bit_cast(int32_t, ai));
-    take_best(v, i, b, __builtin_bit_cast(int32_t, bi));
-  }
-  // the two halves
-  {
-    float a = v, b = v;
-    swap32(a, b);
-    float ai = __builtin_bit_cast(float, i), bi = ai;
-    swap32(ai, bi);
-    take_best(v, i, a, __builtin_bit_cast(int32_t, ai));
-    take_best(v, i, b, __builtin_bit_cast(int32_t, bi));
-  }
-}
-
 __global__ __launch_bounds__(kFinalThreads) void argmax_final_kernel(const ValIdx *__restrict__ part,
                                                                      int nparts,
                                                                      int32_t *__restrict__ out) {
@@ -94,7 +54,7 @@ __global__ __launch_bounds__(kFinalThreads) void argmax_final_kernel(const ValId
     take_best(v, i, p0.v, p0.i);
     take_best(v, i, p1.v, p1.i);
   }
-  wave_best_dpp(v, i);
+  wave_best(v, i);
   const int w = tid >> 6;
   if ((tid & 63) == 0) {
     sv[w] = v;
@@ -104,7 +64,7 @@ __global__ __launch_bounds__(kFinalThreads) void argmax_final_kernel(const ValId
   if (tid < 64) {
     v = tid < kFinalThreads / 64 ? sv[tid] : -__builtin_inff();
     i = tid < kFinalThreads / 64 ? si[tid] : 0x7fffffff;
-    wave_best_dpp(v, i);
+    wave_best(v, i);
     if (tid == 0) *out = i;
   }
 }

@@ -304,16 +304,45 @@ __device__ __forceinline__ bool beats(float av, int32_t ai, float bv, int32_t bi
   return av > bv || (av == bv && ai < bi);
 }
 
-// Best pair of the wave, valid in every lane.
+template <int CTRL>
+__device__ __forceinline__ int32_t dpp_i(int32_t v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ void take_best(float &v, int32_t &i, float ov, int32_t oi) {
+  if (beats(ov, oi, v, i)) {
+    v = ov;
+    i = oi;
+  }
+}
+
+// The best pair of the wave, in every lane: DPP moves inside 16-lane rows,
+// then the permlane swaps across rows (a few cycles each; lane shuffles
+// would cost a round trip through LDS per step).  "beats" is a total order
+// on the pairs (ties go to the lower index), so the order of the steps does
+// not change the result.
 __device__ __forceinline__ void wave_best(float &v, int32_t &i) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const float ov = __shfl_xor(v, m);
-    const int32_t oi = __shfl_xor(i, m);
-    if (beats(ov, oi, v, i)) {
-      v = ov;
-      i = oi;
-    }
+  take_best(v, i, dpp<DPP_QUAD_XOR1>(v), dpp_i<DPP_QUAD_XOR1>(i));
+  take_best(v, i, dpp<DPP_QUAD_XOR2>(v), dpp_i<DPP_QUAD_XOR2>(i));
+  take_best(v, i, dpp<DPP_ROW_HALF_MIRROR>(v), dpp_i<DPP_ROW_HALF_MIRROR>(i));
+  take_best(v, i, dpp<DPP_ROW_MIRROR>(v), dpp_i<DPP_ROW_MIRROR>(i));
+  // rows 0/1 and 2/3: each lane sees both rows of its 32-lane half
+  {
+    float a = v, b = v;
+    swap16(a, b);
+    float ai = __builtin_bit_cast(float, i), bi = ai;
+    swap16(ai, bi);
+    take_best(v, i, a, __builtin_bit_cast(int32_t, ai));
+    take_best(v, i, b, __builtin_bit_cast(int32_t, bi));
+  }
+  // the two halves
+  {
+    float a = v, b = v;
+    swap32(a, b);
+    float ai = __builtin_bit_cast(float, i), bi = ai;
+    swap32(ai, bi);
+    take_best(v, i, a, __builtin_bit_cast(int32_t, ai));
+    take_best(v, i, b, __builtin_bit_cast(int32_t, bi));
   }
 }
 
