@@ -389,8 +389,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 // weights stream in; after one barrier each lane takes its units' codes from
 // LDS and the row groups proceed as in dmmv_k_kernel (one pass over the
 // units: k <= 64 * LPR * BPL).  Workgroup 0 can also store the quantized
-// activation.
-template <int WT, int LPR, int BPL, int RB, int WPB>
+// activation.  PIPE: the grid is persistent and each wave walks many groups,
+// requesting the next group's units before the current group's arithmetic.
+template <int WT, int LPR, int BPL, int RB, int WPB, bool PIPE>
 __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(1, 2))) void dmmv_k_f32_kernel(
     const uint8_t *w, const float *x, int64_t rows, int64_t row_bytes, int64_t n_groups,
     int32_t k, int32_t nb, const DmmvKF32Args a_in) {
@@ -433,7 +434,7 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(1, 2))
 
   // 2. the first row group's weight units
   uint32_t v[RB][BPL][NWD];
-  auto load_group = [&](int64_t gi) {
+  auto load_group_into = [&](uint32_t (&v)[RB][BPL][NWD], int64_t gi) {
     const int64_t row0 = gi * (RB * S);
 #pragma unroll
     for (int t = 0; t < RB; ++t) {
@@ -452,7 +453,7 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(1, 2))
   // branch would make the activation's quantization below wait for every
   // weight load, the wait counts being merged over both paths)
   int64_t gi = wave;
-  load_group(gi < a.n_groups ? gi : a.n_groups - 1);
+  load_group_into(v, gi < a.n_groups ? gi : a.n_groups - 1);
 
   // 3. quantize x into LDS
   const bool out = blockIdx.x == 0 && a.qx_out != nullptr;
@@ -518,8 +519,8 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(1, 2))
     }
   }
 
-  // 5. the row groups: dots, reduction, store; then the next group's units
-  while (gi < a.n_groups) {
+  // 5. the row groups: dots, reduction, store
+  auto run_group = [&](const uint32_t (&v)[RB][BPL][NWD], int64_t gi) {
     const int64_t row0 = gi * (RB * S);
     float acc[RB];
 #pragma unroll
@@ -545,8 +546,38 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(1, 2))
         }
       }
     }
-    gi += n_waves;
-    if (gi < a.n_groups) load_group(gi);
+  };
+  if constexpr (PIPE) {
+    // A wave that walks several groups requests the next group's units
+    // before it computes the current one, in a second register set; the
+    // last group is peeled off so that every load sits on a straight path
+    // (a load under a branch would merge the wait counts of both paths).
+    uint32_t v2[RB][BPL][NWD];
+    while (gi < a.n_groups) {
+      const int64_t g1 = gi + n_waves;
+      if (g1 >= a.n_groups) {
+        run_group(v, gi);
+        break;
+      }
+      load_group_into(v2, g1);
+      run_group(v, gi);
+      gi = g1;
+      const int64_t g2 = gi + n_waves;
+      if (g2 >= a.n_groups) {
+        run_group(v2, gi);
+        break;
+      }
+      load_group_into(v, g2);
+      run_group(v2, gi);
+      gi = g2;
+    }
+  } else {
+    // then the next group's units, after this one's arithmetic
+    while (gi < a.n_groups) {
+      run_group(v, gi);
+      gi += n_waves;
+      if (gi < a.n_groups) load_group_into(v, gi);
+    }
   }
 }
 
@@ -692,16 +723,40 @@ int launch_type(int mode, DmmvArgs a, hipStream_t stream) {
 }
 
 // The fp32-input form: the plain layout and row steps, a workgroup's
-// activation staged once (grids beyond 4096 workgroups loop over groups).
+// activation staged once, one row group per wave.  Row groups beyond what kKF32Walk workgroups take in one pass (the LM-head
+// shapes) go to a persistent grid of one workgroup per CU whose waves walk
+// the groups, each requesting the next group's units before it computes the
+// current one.  Q6_K LM head (248 320 x 2048), one box, alternating: 72.3-
+// 72.7 us with 256 such workgroups, against 81.3-81.9 us for a grid capped
+// at 4096 workgroups that walked without the second register set
+// (1024: 74.5-75.0 us, 512: 73.4-73.5 us; the second register set at 512
+// workgroups, two waves per SIMD: 74.8-75.2 us).
+constexpr int64_t kKF32Walk = 4096;
+constexpr int kKF32WalkGrid = 256;
+constexpr int kKF32WalkWpb = 4;
+
+inline bool kf_walks(int64_t n_groups) { return n_groups > 4 * kKF32Walk; }
+
 template <int WT, int LPR, int BPL, int RB, int WPB = 4>
 int launch_kf1(DmmvKF32Args a, hipStream_t stream) {
   constexpr int S = 64 / LPR;
   a.n_groups = (a.rows + RB * S - 1) / (RB * S);
   const int64_t blocks = (a.n_groups + WPB - 1) / WPB;
-  const unsigned grid = static_cast<unsigned>(blocks < 4096 ? blocks : 4096);
   const size_t lds = static_cast<size_t>(a.k) + 8 * static_cast<size_t>(a.nb);
-  hipLaunchKernelGGL((dmmv_k_f32_kernel<WT, LPR, BPL, RB, WPB>), dim3(grid), dim3(64 * WPB), lds,
-                     stream, a.w, a.x, a.rows, a.row_bytes, a.n_groups, a.k, a.nb, a);
+  if constexpr (WPB == kKF32WalkWpb) {
+    if (kf_walks(a.n_groups)) {
+      hipLaunchKernelGGL((dmmv_k_f32_kernel<WT, LPR, BPL, RB, WPB, true>), dim3(kKF32WalkGrid),
+                         dim3(64 * WPB), lds, stream, a.w, a.x, a.rows, a.row_bytes, a.n_groups, a.k,
+                         a.nb, a);
+      ZQ_LAUNCH_CHECK();
+      return ZQ_OK;
+    }
+  }
+  {
+    hipLaunchKernelGGL((dmmv_k_f32_kernel<WT, LPR, BPL, RB, WPB, false>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(64 * WPB), lds, stream, a.w, a.x, a.rows, a.row_bytes, a.n_groups, a.k,
+                       a.nb, a);
+  }
   ZQ_LAUNCH_CHECK();
   return ZQ_OK;
 }
@@ -747,6 +802,7 @@ int launch_kf_type(DmmvKF32Args a, hipStream_t stream) {
   // The LM-head shapes keep 4.
   const int64_t groups = (a.rows + static_cast<int64_t>(rb) * (64 / sh.lpr) - 1) /
                          (static_cast<int64_t>(rb) * (64 / sh.lpr));
+  if (kf_walks(groups)) return launch_kf_shape<WT, kKF32WalkWpb>(sh, rb, a, stream);
   if (a.rows <= 16384 && groups >= 8 * 256) return launch_kf_shape<WT, 8>(sh, rb, a, stream);
   return launch_kf_shape<WT, 4>(sh, rb, a, stream);
 }

@@ -85,6 +85,35 @@ def test_k_f32(zq, wt, rows, k):
 
 
 @pytest.mark.parametrize("wt", KTYPES, ids=lambda t: NAME[t])
+@pytest.mark.parametrize("rows", [248320, 200003])
+def test_k_f32_walking_groups(zq, wt, rows):
+    """Row counts past the capped grid (the LM head's 248 320 and a ragged
+    200 003 at k = 2048), where every wave walks several row groups with the
+    next group's units requested before the current one's arithmetic: every
+    row bit-identical to the two-launch path, sampled rows (both ends and
+    across the grid) against the oracle."""
+    torch = torch_cuda()
+    k = 2048
+    seed = 6300 + wt + rows
+    w = inputs.gen_weights_k(wt, rows, k, seed)
+    x = inputs.gen_activation(1, k, seed + 1)
+    wd = dev(w)
+    y = nan_f32(rows)
+    assert zq.zq_dmmv_k_f32(wt, wd, rows, k, dev(x), y, 0) == 0
+    torch.cuda.synchronize()
+    yh = host(y)
+    what = "%s %d x %d" % (NAME[wt], rows, k)
+    assert np.array_equal(yh.view(np.uint32), two_launch_k(zq, wt, wd, rows, k, x).view(np.uint32)), \
+        what + " against the two-launch path"
+    rng = np.random.default_rng(seed)
+    idx = np.unique(np.concatenate([np.arange(64), np.arange(rows - 64, rows),
+                                    rng.integers(0, rows, 1500)])).astype(np.int64)
+    rq, rd, _ = oracle.quantize_act(x)
+    y_ref, S = oracle.k_dmmv(wt, w, rows, k, rq, rd, rows_eval=idx)
+    check_rows(yh[idx], y_ref, S, what + " sampled")
+
+
+@pytest.mark.parametrize("wt", KTYPES, ids=lambda t: NAME[t])
 def test_k_f32_accumulate_without_outputs(zq, wt):
     torch = torch_cuda()
     rows, k = 1000, 2048
