@@ -285,9 +285,8 @@ int launch_f(const DmmvF32Args &a, hipStream_t stream) {
 // of two row steps each (16 rows of 4096, 3.33 us against 3.40 for 16 waves
 // of one row and 3.47 for 4 waves of four; 2048 x 2048: 2.38 against 2.56),
 // except for a few hundred rows without the norm, which keep 16 waves of one
-// row step (64 x 2048 Q8_0: 2.28 against 2.37 us; with the norm, whose sum
-// of squares is reduced over the workgroup, 8 waves are faster there too:
-// the 128-row router of a 40-layer chain, 685 against 703 us per token).
+// row step (64 x 2048 Q8_0: 2.28 against 2.37 us), and with the norm, whose
+// sum of squares is reduced over the workgroup, fewer waves (below).
 // With more blocks per lane, 8 waves of one row step (2048 x 8192: 4.28
 // against 4.83 for two).
 template <int WT, int LPR, int BPL>
@@ -297,6 +296,11 @@ int launch_fs(const DmmvF32Args &a, hipStream_t stream) {
   if constexpr (BPL <= 2) {
     if (a.rows <= 256 && a.norm_w == nullptr) return launch_f<WT, LPR, BPL, 1, 16>(a, stream);
   }
+  // A few hundred rows with the norm: 4 waves of one row step.  The 128-row
+  // router of a 40-layer chain (32 workgroups), alternating on one box:
+  // 673-674 us per token against 689-690 with 8 waves of two row steps
+  // (4 x 2: 675; 2 x 2: 672-674; 2 x 1: 676; 1 x 2: 732).
+  if (a.norm_w && a.rows <= 256) return launch_f<WT, LPR, BPL, 1, 4>(a, stream);
   if (a.rows <= static_cast<int64_t>(256) * 8 * RBS * S)
     return launch_f<WT, LPR, BPL, RBS, 8>(a, stream);
   if (a.rows <= 16384) {
