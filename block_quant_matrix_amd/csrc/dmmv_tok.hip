@@ -187,15 +187,17 @@ __global__ __launch_bounds__(256) void dmmv_tok_kernel(const uint8_t *w, const i
 // blocks of a row (64/KC rows per load instruction, as the single-token
 // DMMV reads), and writes each block's codes and scale (fp32) to its own LDS
 // region; the next chunk's windows are requested before this chunk's
-// arithmetic.  Compute: lane (n = lane % 16, g = lane / 16) takes row n's
-// codes for k = 8g..8g+7 and token n's codes for the same k from LDS, and
-// receives the sums of tokens 4g..4g+3 against row n.
+// arithmetic.  Compute: lane (n = lane % 16, g = lane / 16) takes 8 of row
+// n's codes and token n's codes for the same 8 k from LDS, and receives the
+// sums of tokens 4g..4g+3 against row n.  Q8_0: k = 8g..8g+7.
 //
-// Q4_0 codes are staged with every nibble's top bit flipped (q ^ 8), so a
-// nibble moved to the high half of its byte reads as the int8 16 * (q - 8):
-// lanes of low nibbles shift left by 4, lanes of high nibbles keep them in
-// place, and one AND clears the rest.  The sums come out 16 times too large,
-// exactly; the staged scale carries the 1/16.
+// Q4_0: a lane's 8 codes are the nibbles of one dword of the block's 16 code
+// bytes, dword g: its low nibbles (k = 4g..4g+3), then its high nibbles
+// (k = 16+4g..16+4g+3); the tokens' codes are staged in that k order.  The
+// codes are staged with every nibble's top bit flipped (q ^ 8), so a nibble
+// in the high half of its byte reads as the int8 16 * (q - 8): the low
+// nibbles shift left by 4, and one AND each clears the rest.  The sums come
+// out 16 times too large, exactly; the staged scale carries the 1/16.
 //
 // With at most 8 tokens only the lanes g = 0, 1 hold real tokens.  Blocks
 // are taken in pairs: v_permlane32_swap moves the second block's real half
@@ -307,12 +309,30 @@ __global__ __launch_bounds__(64 * kTmWaves) void dmmv_tok_mfma_kernel(const uint
 
   // the tokens' codes (16-byte pieces; n_tok * k / 16 < 2^32, so the
   // piece -> token division is a 32-bit one) and scales
-  const uint32_t nq = static_cast<uint32_t>(a.n_tok) * static_cast<uint32_t>(a.k / 16);
-  const uint32_t qpr = static_cast<uint32_t>(a.k / 16);  // 16-byte pieces per token
-  for (uint32_t q = tid; q < nq; q += 64 * kTmWaves) {
-    const uint32_t t = q / qpr, in = q - t * qpr;
-    *reinterpret_cast<u32x4 *>(lq + t * xrowb + 16 * in) =
-        *reinterpret_cast<const u32x4 *>(a.qx + 16 * static_cast<int64_t>(q));
+  if constexpr (WT == ZQ_Q4_0) {
+    // Q4_0 takes k in the order of the codes' dwords: a lane's 8 codes are
+    // the low nibbles of one dword of a block (k = 4j..4j+3) and then its
+    // high nibbles (k = 16+4j..16+4j+3), so each token block is staged with
+    // its dwords in the order 0 4 1 5 2 6 3 7.  The int32 sum of the block
+    // is the same in any k order.
+    const uint32_t nbq = static_cast<uint32_t>(a.n_tok) * static_cast<uint32_t>(a.nb);
+    const uint32_t bpr = static_cast<uint32_t>(a.nb);     // blocks per token
+    for (uint32_t q = tid; q < nbq; q += 64 * kTmWaves) {
+      const uint32_t t = q / bpr, in = q - t * bpr;
+      const u32x4 lo = *reinterpret_cast<const u32x4 *>(a.qx + 32 * static_cast<int64_t>(q));
+      const u32x4 hi = *reinterpret_cast<const u32x4 *>(a.qx + 32 * static_cast<int64_t>(q) + 16);
+      int8_t *dst = lq + t * xrowb + 32 * in;
+      *reinterpret_cast<u32x4 *>(dst) = u32x4{lo.x, hi.x, lo.y, hi.y};
+      *reinterpret_cast<u32x4 *>(dst + 16) = u32x4{lo.z, hi.z, lo.w, hi.w};
+    }
+  } else {
+    const uint32_t nq = static_cast<uint32_t>(a.n_tok) * static_cast<uint32_t>(a.k / 16);
+    const uint32_t qpr = static_cast<uint32_t>(a.k / 16);  // 16-byte pieces per token
+    for (uint32_t q = tid; q < nq; q += 64 * kTmWaves) {
+      const uint32_t t = q / qpr, in = q - t * qpr;
+      *reinterpret_cast<u32x4 *>(lq + t * xrowb + 16 * in) =
+          *reinterpret_cast<const u32x4 *>(a.qx + 16 * static_cast<int64_t>(q));
+    }
   }
   for (int q = tid; q < nb_pad * 8; q += 64 * kTmWaves) {
     const int b = q >> 3, t = q & 7;
@@ -328,10 +348,9 @@ __global__ __launch_bounds__(64 * kTmWaves) void dmmv_tok_mfma_kernel(const uint
   // Blocks past nb read up to 32 * (nb_pad - nb) - 32 bytes past the last
   // token's codes, into the scale table that follows; their scales are zero.
   const int8_t *xrow = lq + static_cast<int64_t>(n < a.n_tok ? n : 0) * xrowb + 8 * g;
-  // this lane's 8 weight code bytes inside a staged block
-  const int qoff = WT == ZQ_Q4_0 ? 8 * (g & 1) : 8 * g;
-  const int shl = WT == ZQ_Q4_0 ? (1 - (g >> 1)) * 4 : 0;  // Q4_0: low nibbles move up
-  const uint8_t *wl = wq + n * WROW + qoff;
+  // this lane's weight codes inside a staged block: Q8_0 8 bytes, Q4_0 one
+  // dword (its low nibbles, then its high nibbles)
+  const uint8_t *wl = wq + n * WROW + (WT == ZQ_Q4_0 ? 4 * g : 8 * g);
   float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int c0 = 0; c0 < a.nb; c0 += KC) {
     // the chunk's blocks into the wave's LDS region: codes (Q4_0: nibbles
@@ -362,13 +381,15 @@ __global__ __launch_bounds__(64 * kTmWaves) void dmmv_tok_mfma_kernel(const uint
 #pragma unroll
     for (int bi = 0; bi < KC; bi += 2) {
       const int b = c0 + bi;
-      uint2 wa = *reinterpret_cast<const uint2 *>(wl + bi * QB);
-      uint2 wb = *reinterpret_cast<const uint2 *>(wl + (bi + 1) * QB);
+      uint2 wa, wb;
       if constexpr (WT == ZQ_Q4_0) {
-        wa.x = (wa.x << shl) & 0xF0F0F0F0u;
-        wa.y = (wa.y << shl) & 0xF0F0F0F0u;
-        wb.x = (wb.x << shl) & 0xF0F0F0F0u;
-        wb.y = (wb.y << shl) & 0xF0F0F0F0u;
+        const uint32_t da = *reinterpret_cast<const uint32_t *>(wl + bi * QB);
+        const uint32_t db = *reinterpret_cast<const uint32_t *>(wl + (bi + 1) * QB);
+        wa = uint2{(da << 4) & 0xF0F0F0F0u, da & 0xF0F0F0F0u};
+        wb = uint2{(db << 4) & 0xF0F0F0F0u, db & 0xF0F0F0F0u};
+      } else {
+        wa = *reinterpret_cast<const uint2 *>(wl + bi * QB);
+        wb = *reinterpret_cast<const uint2 *>(wl + (bi + 1) * QB);
       }
       const uint2 xa = *reinterpret_cast<const uint2 *>(xrow + 32 * b);
       const uint2 xb = *reinterpret_cast<const uint2 *>(xrow + 32 * (b + 1));
